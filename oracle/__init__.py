@@ -1,0 +1,315 @@
+"""CPU oracle of the hybrid W4 decode step (TEST INFRASTRUCTURE ONLY).
+
+Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may use
+this package.  It shares no code with the HIP library: the C model in
+aw4_oracle.c is compiled with gcc and driven through ctypes here; brute.py is
+an independent numpy implementation for tiny shapes; accept.py holds the
+speculative-decoding acceptance rule.
+
+Precision and formats are described in aw4_oracle.c.  Parity status per
+function is recorded in DESIGN.md ("parity pins").
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SO = os.path.join(_HERE, "liboracle.so")
+
+_vp, _i32, _i64, _f32, _f64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_double
+
+
+def build():
+    src = os.path.join(_HERE, "aw4_oracle.c")
+    subprocess.check_call(["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared",
+                           "-o", SO + ".tmp", src, "-lm"])
+    os.replace(SO + ".tmp", SO)
+    global _lib
+    _lib = None
+
+
+class Cfg(ctypes.Structure):
+    _fields_ = [("hidden", _i32), ("ffn", _i32), ("vocab", _i32), ("n_layers", _i32),
+                ("gdn_qk_heads", _i32), ("gdn_v_heads", _i32), ("gdn_head_dim", _i32),
+                ("attn_q_heads", _i32), ("attn_kv_heads", _i32), ("attn_head_dim", _i32),
+                ("group", _i32), ("max_ctx", _i32), ("rms_eps", _f64), ("pattern", ctypes.c_char * 128)]
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(SO):
+            raise RuntimeError(f"{SO} missing: run __graft_entry__.build()")
+        L = ctypes.CDLL(SO)
+        sig = {
+            "or_f32_to_f16": ([_f32], ctypes.c_uint16),
+            "or_f16_to_f64": ([ctypes.c_uint16], _f64),
+            "or_quant_group": ([_vp, ctypes.c_int, ctypes.c_int, _vp, _vp], None),
+            "or_quant_w4_rows": ([_vp, _i64, _i64, _vp, _vp], None),
+            "or_quant_i8_rows": ([_vp, _i64, _i64, _vp, _vp], None),
+            "or_rht_forward": ([_vp, _vp, ctypes.c_int, _vp], None),
+            "or_rht_inverse": ([_vp, _vp, ctypes.c_int, _vp], None),
+            "or_create": ([ctypes.POINTER(Cfg)], _vp),
+            "or_destroy": ([_vp], None),
+            "or_load_w4": ([_vp, ctypes.c_int, ctypes.c_int, _vp, _vp], ctypes.c_int),
+            "or_quant_w4_into": ([_vp, ctypes.c_int, ctypes.c_int, _i64, _i64, _vp], ctypes.c_int),
+            "or_quant_lm_into": ([_vp, _i64, _i64, _vp], ctypes.c_int),
+            "or_load_i8": ([_vp, _vp, _vp], ctypes.c_int),
+            "or_load_vec": ([_vp, ctypes.c_int, ctypes.c_int, _vp, ctypes.c_int], ctypes.c_int),
+            "or_load_signs": ([_vp, _vp, ctypes.c_int], ctypes.c_int),
+            "or_gdn_head_step": ([_vp, _vp, _vp, _vp, _f64, _f64, ctypes.c_int, ctypes.c_int, _vp], None),
+            "or_attend_head": ([_vp, _vp, _vp, _vp, _vp, _i64, _i64, ctypes.c_int, _vp, _vp], None),
+            "or_kv_encode": ([_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp], None),
+            "or_forward_layers": ([_vp, _vp, _vp], ctypes.c_int),
+            "or_embed": ([_vp, _i32, _vp], ctypes.c_int),
+            "or_head": ([_vp, _vp, _vp, _vp], ctypes.c_int),
+            "or_decode_token": ([_vp, _i32, _vp, _vp, _vp], ctypes.c_int),
+            "or_get_pos": ([_vp], _i32),
+            "or_set_pos": ([_vp, _i32], ctypes.c_int),
+            "or_set_state_gdn": ([_vp, ctypes.c_int, _vp], ctypes.c_int),
+            "or_get_state_gdn": ([_vp, ctypes.c_int, _vp], ctypes.c_int),
+            "or_set_state_kv": ([_vp, ctypes.c_int, _i32, _vp, _vp, _vp, _vp], ctypes.c_int),
+            "or_get_state_kv": ([_vp, ctypes.c_int, _i32, _vp, _vp, _vp, _vp], ctypes.c_int),
+        }
+        for name, (a, r) in sig.items():
+            f = getattr(L, name)
+            f.argtypes = a
+            f.restype = r
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+# ------------------------------------------------------------------ codec helpers
+def f32_to_f16_bits(x):
+    return np.array([lib().or_f32_to_f16(float(v)) for v in np.asarray(x, np.float32).ravel()],
+                    dtype=np.uint16).reshape(np.shape(x))
+
+
+def f16_bits_to_f64(h):
+    return np.array([lib().or_f16_to_f64(int(v)) for v in np.asarray(h, np.uint16).ravel()],
+                    dtype=np.float64).reshape(np.shape(h))
+
+
+def quant_group(x, qmax):
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    s = np.zeros(1, np.uint16)
+    c = np.zeros(len(x), np.int8)
+    lib().or_quant_group(_p(x), len(x), qmax, _p(s), _p(c))
+    return int(s[0]), c
+
+
+def quant_w4(w):
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    rows, cols = w.shape
+    codes = np.zeros((rows, cols // 2), np.uint8)
+    scales = np.zeros((rows, cols // 32), np.uint16)
+    lib().or_quant_w4_rows(_p(w), rows, cols, _p(codes), _p(scales))
+    return codes, scales
+
+
+def quant_i8(w):
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    rows, cols = w.shape
+    codes = np.zeros((rows, cols), np.int8)
+    scales = np.zeros((rows, cols // 32), np.uint16)
+    lib().or_quant_i8_rows(_p(w), rows, cols, _p(codes), _p(scales))
+    return codes, scales
+
+
+def rht_forward(v, signs):
+    v = np.ascontiguousarray(v, np.float64)
+    s = np.ascontiguousarray(signs, np.int8)
+    out = np.zeros_like(v)
+    lib().or_rht_forward(_p(v), _p(s), len(v), _p(out))
+    return out
+
+
+def rht_inverse(v, signs):
+    v = np.ascontiguousarray(v, np.float64)
+    s = np.ascontiguousarray(signs, np.int8)
+    out = np.zeros_like(v)
+    lib().or_rht_inverse(_p(v), _p(s), len(v), _p(out))
+    return out
+
+
+def gdn_head_step(S, k, v, q, alpha, beta):
+    """One head: returns (new S, o).  S is [dv][dk]."""
+    S = np.array(S, np.float64, order="C")
+    dv, dk = S.shape
+    k, v, q = (np.ascontiguousarray(a, np.float64) for a in (k, v, q))
+    o = np.zeros(dv)
+    lib().or_gdn_head_step(_p(S), _p(k), _p(v), _p(q), alpha, beta, dv, dk, _p(o))
+    return S, o
+
+
+def attend_head(q, kc, ks, vc, vs, signs):
+    """q [d]; kc/vc int8 [npos][d]; ks/vs fp16 bits [npos][d/32]."""
+    q = np.ascontiguousarray(q, np.float64)
+    kc, vc = np.ascontiguousarray(kc, np.int8), np.ascontiguousarray(vc, np.int8)
+    ks, vs = np.ascontiguousarray(ks, np.uint16), np.ascontiguousarray(vs, np.uint16)
+    sg = np.ascontiguousarray(signs, np.int8)
+    npos, d = kc.shape
+    out = np.zeros(d)
+    lib().or_attend_head(_p(q), _p(kc), _p(ks), _p(vc), _p(vs), npos, d, d, _p(sg), _p(out))
+    return out
+
+
+def kv_encode(k, v, signs):
+    d = len(k)
+    k, v = np.ascontiguousarray(k, np.float64), np.ascontiguousarray(v, np.float64)
+    sg = np.ascontiguousarray(signs, np.int8)
+    kc, vc = np.zeros(d, np.int8), np.zeros(d, np.int8)
+    ks, vs = np.zeros(d // 32, np.uint16), np.zeros(d // 32, np.uint16)
+    lib().or_kv_encode(_p(k), _p(v), _p(sg), d, _p(kc), _p(ks), _p(vc), _p(vs))
+    return kc, ks, vc, vs
+
+
+# ------------------------------------------------------------------ model
+T_MIX_IN, T_MIX_OUT, T_FFN_GATE, T_FFN_UP, T_FFN_DOWN, T_LM_HEAD = 0, 1, 2, 3, 4, 5
+T_NORM_MIX, T_NORM_FFN, T_NORM_GATED, T_A_BIAS, T_NORM_FINAL, T_RHT_SIGNS = 6, 7, 8, 9, 10, 11
+
+
+class Model:
+    """The oracle model.  shape: any object with the fields of synth.workloads.Shape."""
+
+    def __init__(self, shape):
+        self.shape = shape
+        c = Cfg()
+        for f in ("hidden", "ffn", "vocab", "gdn_qk_heads", "gdn_v_heads", "gdn_head_dim",
+                  "attn_q_heads", "attn_kv_heads", "attn_head_dim", "group", "max_ctx"):
+            setattr(c, f, int(getattr(shape, f)))
+        c.n_layers = len(shape.pattern)
+        c.rms_eps = float(shape.rms_eps)
+        c.pattern = shape.pattern.encode()
+        self._cfg = c
+        self.h = lib().or_create(ctypes.byref(c))
+        if not self.h:
+            raise MemoryError("oracle allocation failed")
+
+    def __del__(self):
+        if getattr(self, "h", None):
+            lib().or_destroy(self.h)
+            self.h = None
+
+    def _rc(self, rc, what):
+        if rc != 0:
+            raise ValueError(f"oracle {what} failed ({rc})")
+
+    # -- weights
+    def load_w4(self, layer, kind, codes, scales):
+        codes = np.ascontiguousarray(codes, np.uint8)
+        scales = np.ascontiguousarray(scales, np.uint16)
+        self._rc(lib().or_load_w4(self.h, layer, kind, _p(codes), _p(scales)), "load_w4")
+
+    def quant_w4_into(self, layer, kind, row0, w):
+        w = np.ascontiguousarray(w, np.float32)
+        self._rc(lib().or_quant_w4_into(self.h, layer, kind, row0, w.shape[0], _p(w)), "quant_w4_into")
+
+    def quant_lm_into(self, row0, w):
+        w = np.ascontiguousarray(w, np.float32)
+        self._rc(lib().or_quant_lm_into(self.h, row0, w.shape[0], _p(w)), "quant_lm_into")
+
+    def load_i8(self, codes, scales):
+        codes = np.ascontiguousarray(codes, np.int8)
+        scales = np.ascontiguousarray(scales, np.uint16)
+        self._rc(lib().or_load_i8(self.h, _p(codes), _p(scales)), "load_i8")
+
+    def load_vec(self, layer, kind, v):
+        v = np.ascontiguousarray(v, np.float32)
+        self._rc(lib().or_load_vec(self.h, layer, kind, _p(v), len(v)), "load_vec")
+
+    def load_signs(self, s):
+        s = np.ascontiguousarray(s, np.int8)
+        self._rc(lib().or_load_signs(self.h, _p(s), len(s)), "load_signs")
+
+    # -- steps
+    @property
+    def pos(self):
+        return lib().or_get_pos(self.h)
+
+    def set_pos(self, p):
+        self._rc(lib().or_set_pos(self.h, p), "set_pos")
+
+    def forward_layers(self, x, trace=False):
+        x = np.array(x, np.float64)
+        tr = np.zeros((len(self.shape.pattern), self.shape.hidden)) if trace else None
+        self._rc(lib().or_forward_layers(self.h, _p(x), _p(tr) if trace else None), "forward_layers")
+        return (x, tr) if trace else x
+
+    def embed(self, token):
+        x = np.zeros(self.shape.hidden)
+        self._rc(lib().or_embed(self.h, int(token), _p(x)), "embed")
+        return x
+
+    def head(self, x):
+        x = np.ascontiguousarray(x, np.float64)
+        logits = np.zeros(self.shape.vocab)
+        am = np.zeros(1, np.int32)
+        self._rc(lib().or_head(self.h, _p(x), _p(logits), _p(am)), "head")
+        return logits, int(am[0])
+
+    def decode_token(self, token):
+        """-> (final residual, logits, argmax)"""
+        x = np.zeros(self.shape.hidden)
+        logits = np.zeros(self.shape.vocab)
+        am = np.zeros(1, np.int32)
+        self._rc(lib().or_decode_token(self.h, int(token), _p(x), _p(logits), _p(am)), "decode_token")
+        return x, logits, int(am[0])
+
+    # -- state
+    def set_gdn_state(self, layer, S):
+        S = np.ascontiguousarray(S, np.float32)
+        self._rc(lib().or_set_state_gdn(self.h, layer, _p(S)), "set_gdn_state")
+
+    def get_gdn_state(self, layer):
+        s = self.shape
+        S = np.zeros((s.gdn_v_heads, s.gdn_head_dim, s.gdn_head_dim))
+        self._rc(lib().or_get_state_gdn(self.h, layer, _p(S)), "get_gdn_state")
+        return S
+
+    def set_kv(self, layer, kc, ks, vc, vs):
+        npos = kc.shape[0]
+        arrs = [np.ascontiguousarray(a) for a in (kc, ks, vc, vs)]
+        self._rc(lib().or_set_state_kv(self.h, layer, npos, *[_p(a) for a in arrs]), "set_kv")
+
+    def get_kv(self, layer, npos):
+        s = self.shape
+        d, nkv = s.attn_head_dim, s.attn_kv_heads
+        kc = np.zeros((npos, nkv, d), np.int8)
+        vc = np.zeros((npos, nkv, d), np.int8)
+        ks = np.zeros((npos, nkv, d // 32), np.uint16)
+        vs = np.zeros((npos, nkv, d // 32), np.uint16)
+        self._rc(lib().or_get_state_kv(self.h, layer, npos, _p(kc), _p(ks), _p(vc), _p(vs)), "get_kv")
+        return kc, ks, vc, vs
+
+
+def from_recipe(shape, seed, norm_jitter=0.0, chunk_rows=None):
+    """Build an oracle model whose fp32 weights come from the seeded recipe
+    (synth.workloads.tensor_specs) and are quantised by the oracle's codec."""
+    import synth
+    from synth import workloads as W
+    m = Model(shape)
+    for spec in W.tensor_specs(shape, norm_jitter):
+        if spec.fmt in (W.W4, W.I8):
+            step = chunk_rows or max(1, (1 << 24) // spec.cols)
+            for r0 in range(0, spec.rows, step):
+                n = min(step, spec.rows - r0)
+                w = synth.matrix_rows(spec, seed, r0, n)
+                if spec.fmt == W.W4:
+                    m.quant_w4_into(spec.layer, spec.kind, r0, w)
+                else:
+                    m.quant_lm_into(r0, w)
+        elif spec.fmt == W.VEC:
+            m.load_vec(spec.layer, spec.kind, synth.vector(spec, seed))
+        elif spec.fmt == W.SIGNS:
+            m.load_signs(synth.signs(spec.cols, seed, spec.stream))
+    return m
