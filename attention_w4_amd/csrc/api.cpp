@@ -1,0 +1,958 @@
+// Host runtime behind the C ABI in include/aw4.h: config validation, arena
+// planning, weight packing/export, the per-token launch sequence and its HIP
+// graph, and state import/export.  All device memory comes from the caller's
+// arena; nothing here allocates device memory.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/aw4.h"
+#include "aw4_internal.h"
+
+using namespace aw4;
+
+namespace {
+
+struct LayerBufs {
+    char type = 'G';
+    int64_t in_rows = 0, out_cols = 0;
+    uint32_t* w_in = nullptr;
+    uint16_t* s_in = nullptr;
+    uint32_t* w_out = nullptr;
+    uint16_t* s_out = nullptr;
+    uint32_t* w_gu = nullptr;   // gate/up interleaved: row 2i gate i, row 2i+1 up i
+    uint16_t* s_gu = nullptr;
+    uint32_t* w_down = nullptr;
+    uint16_t* s_down = nullptr;
+    float* norm_mix = nullptr;
+    float* norm_ffn = nullptr;
+    float* norm_gated = nullptr;
+    float* a_bias = nullptr;
+    float* S = nullptr;
+    int8_t* kc = nullptr;
+    uint16_t* ks = nullptr;
+    uint32_t* vc = nullptr;
+    uint16_t* vs = nullptr;
+};
+
+struct Plan {
+    uint64_t off = 0;
+    uint8_t* base = nullptr;   // null while only sizing
+    template <class T>
+    T* take(uint64_t bytes) {
+        off = (off + 255) & ~uint64_t(255);
+        T* p = base ? (T*)(base + off) : nullptr;
+        off += bytes;
+        return p;
+    }
+};
+
+}  // namespace
+
+struct aw4_model {
+    aw4_config cfg{};
+    uint8_t* arena = nullptr;
+    uint64_t arena_bytes = 0;
+    hipStream_t stream = nullptr;
+    std::vector<LayerBufs> L;
+    int8_t* lm_codes = nullptr;
+    uint16_t* lm_scales = nullptr;
+    float* norm_final = nullptr;
+    float* signs = nullptr;
+    Ctl* ctl = nullptr;
+    float* x = nullptr;
+    float* proj = nullptr;
+    float* obuf = nullptr;
+    _Float16* hbuf = nullptr;
+    _Float16* abuf = nullptr;
+    float* part = nullptr;
+    float* logits = nullptr;
+    float* pv = nullptr;
+    int32_t* pi = nullptr;
+    int32_t* ring = nullptr;
+    int ring_cap = 0;
+    int nhead_blocks = 0;
+    int nsplit = 1;
+    int32_t host_pos = 0;
+    uint64_t state_off = 0, state_bytes = 0;   // recurrent states + caches
+    bool use_graph = true;
+    hipGraphExec_t g_head = nullptr;
+    hipGraphExec_t g_nohead = nullptr;
+    std::string err;
+};
+
+namespace {
+
+const int kRingCap = 1 << 16;
+
+int fail(aw4_model* m, int code, const std::string& msg) {
+    if (m) m->err = msg;
+    return code;
+}
+
+#define HIPCHK(m, expr)                                                                        \
+    do {                                                                                       \
+        hipError_t e_ = (expr);                                                                \
+        if (e_ != hipSuccess)                                                                  \
+            return fail((m), AW4_E_HIP, std::string(#expr) + ": " + hipGetErrorString(e_));    \
+    } while (0)
+
+int64_t mix_in_rows(const aw4_config* c, char t) {
+    if (t == 'G')
+        return 2LL * c->gdn_qk_heads * c->gdn_head_dim + 2LL * c->gdn_v_heads * c->gdn_head_dim +
+               2LL * c->gdn_v_heads;
+    return 2LL * c->attn_q_heads * c->attn_head_dim + 2LL * c->attn_kv_heads * c->attn_head_dim;
+}
+
+int64_t mix_out_cols(const aw4_config* c, char t) {
+    return t == 'G' ? (int64_t)c->gdn_v_heads * c->gdn_head_dim : (int64_t)c->attn_q_heads * c->attn_head_dim;
+}
+
+int nsplit_for(int max_ctx) {
+    int n = max_ctx / 256;
+    if (n < 1) n = 1;
+    if (n > 128) n = 128;
+    return n;
+}
+
+// Lays out every buffer in the arena (base null: sizing only).
+uint64_t plan_layout(const aw4_config* c, aw4_model* m, uint8_t* base) {
+    Plan p;
+    p.base = base;
+    const int64_t H = c->hidden, F = c->ffn;
+    auto w4 = [&](int64_t rows, int64_t cols, uint32_t** w, uint16_t** s) {
+        *w = p.take<uint32_t>((uint64_t)rows * cols / 2);
+        *s = p.take<uint16_t>((uint64_t)rows * (cols / 32) * 2);
+    };
+    std::vector<LayerBufs> L(c->n_layers);
+    int64_t max_in = 0;
+    bool has_g = false, has_a = false;
+    for (int l = 0; l < c->n_layers; ++l) {
+        LayerBufs& b = L[l];
+        b.type = c->layer_pattern[l];
+        b.in_rows = mix_in_rows(c, b.type);
+        b.out_cols = mix_out_cols(c, b.type);
+        if (b.in_rows > max_in) max_in = b.in_rows;
+        w4(b.in_rows, H, &b.w_in, &b.s_in);
+        w4(H, b.out_cols, &b.w_out, &b.s_out);
+        w4(2 * F, H, &b.w_gu, &b.s_gu);
+        w4(H, F, &b.w_down, &b.s_down);
+        b.norm_mix = p.take<float>(H * 4);
+        b.norm_ffn = p.take<float>(H * 4);
+        if (b.type == 'G') {
+            has_g = true;
+            b.norm_gated = p.take<float>((uint64_t)c->gdn_head_dim * 4);
+            b.a_bias = p.take<float>((uint64_t)c->gdn_v_heads * 4);
+        } else {
+            has_a = true;
+        }
+    }
+    int8_t* lm_codes = nullptr;
+    uint16_t* lm_scales = nullptr;
+    float* norm_final = nullptr;
+    if (c->vocab > 0) {
+        lm_codes = p.take<int8_t>((uint64_t)c->vocab * H);
+        lm_scales = p.take<uint16_t>((uint64_t)c->vocab * (H / 32) * 2);
+        norm_final = p.take<float>(H * 4);
+    }
+    float* signs = p.take<float>((uint64_t)(has_a ? c->attn_head_dim : 1) * 4);
+    // recurrent states and caches: one contiguous region, cleared by reset
+    p.off = (p.off + 255) & ~uint64_t(255);
+    const uint64_t state_off = p.off;
+    for (int l = 0; l < c->n_layers; ++l) {
+        LayerBufs& b = L[l];
+        if (b.type == 'G') {
+            b.S = p.take<float>((uint64_t)c->gdn_v_heads * c->gdn_head_dim * c->gdn_head_dim * 4);
+        } else {
+            const uint64_t n = (uint64_t)c->attn_kv_heads * c->max_ctx * c->attn_head_dim;
+            b.kc = p.take<int8_t>(n);
+            b.ks = p.take<uint16_t>(n / 32 * 2);
+            b.vc = p.take<uint32_t>(n / 32 * 12);
+            b.vs = p.take<uint16_t>(n / 32 * 2);
+        }
+    }
+    p.off = (p.off + 255) & ~uint64_t(255);
+    const uint64_t state_bytes = p.off - state_off;
+    Ctl* ctl = p.take<Ctl>(sizeof(Ctl));
+    float* x = p.take<float>(H * 4);
+    float* proj = p.take<float>((uint64_t)max_in * 4);
+    float* obuf = p.take<float>((uint64_t)(has_g ? c->gdn_v_heads * c->gdn_head_dim : 1) * 4);
+    const int64_t hlen = F > (int64_t)c->attn_q_heads * c->attn_head_dim ? F : (int64_t)c->attn_q_heads * c->attn_head_dim;
+    _Float16* hbuf = p.take<_Float16>((uint64_t)hlen * 2);
+    _Float16* abuf = p.take<_Float16>((uint64_t)(has_a ? c->attn_q_heads * c->attn_head_dim : 1) * 2);
+    const int nsplit = nsplit_for(c->max_ctx);
+    float* part = p.take<float>((uint64_t)(has_a ? c->attn_q_heads : 1) * nsplit * (c->attn_head_dim + 2) * 4);
+    float* logits = nullptr;
+    float* pv = nullptr;
+    int32_t* pi = nullptr;
+    int nhb = 0;
+    if (c->vocab > 0) {
+        logits = p.take<float>((uint64_t)c->vocab * 4);
+        nhb = head_blocks(c->vocab);
+        pv = p.take<float>((uint64_t)nhb * 4);
+        pi = p.take<int32_t>((uint64_t)nhb * 4);
+    }
+    int32_t* ring = p.take<int32_t>((uint64_t)kRingCap * 4);
+    p.off = (p.off + 255) & ~uint64_t(255);
+    if (m) {
+        m->L = L;
+        m->lm_codes = lm_codes;
+        m->lm_scales = lm_scales;
+        m->norm_final = norm_final;
+        m->signs = signs;
+        m->ctl = ctl;
+        m->x = x;
+        m->proj = proj;
+        m->obuf = obuf;
+        m->hbuf = hbuf;
+        m->abuf = abuf;
+        m->part = part;
+        m->logits = logits;
+        m->pv = pv;
+        m->pi = pi;
+        m->ring = ring;
+        m->ring_cap = kRingCap;
+        m->nhead_blocks = nhb;
+        m->nsplit = nsplit;
+        m->state_off = state_off;
+        m->state_bytes = state_bytes;
+    }
+    return p.off;
+}
+
+const char* check_config(const aw4_config* c) {
+    if (!c) return "null config";
+    if (c->hidden <= 0 || c->hidden % 64) return "hidden must be a positive multiple of 64";
+    if (c->ffn <= 0 || c->ffn % 64) return "ffn must be a positive multiple of 64";
+    if (c->group != 32) return "group must be 32";
+    if (c->n_layers < 1 || c->n_layers > 127) return "n_layers must be in [1, 127]";
+    if ((int)strnlen(c->layer_pattern, 128) != c->n_layers) return "layer_pattern length must equal n_layers";
+    bool g = false, a = false;
+    for (int i = 0; i < c->n_layers; ++i) {
+        if (c->layer_pattern[i] == 'G') g = true;
+        else if (c->layer_pattern[i] == 'A') a = true;
+        else return "layer_pattern letters must be 'G' or 'A'";
+    }
+    if (g) {
+        if (c->gdn_head_dim != 64 && c->gdn_head_dim != 128) return "gdn_head_dim must be 64 or 128";
+        if (c->gdn_qk_heads < 1 || c->gdn_v_heads < 1 || c->gdn_v_heads % c->gdn_qk_heads)
+            return "gdn_v_heads must be a positive multiple of gdn_qk_heads";
+        if (((int64_t)c->gdn_v_heads * c->gdn_head_dim) % 64) return "gdn_v_heads * gdn_head_dim must be a multiple of 64";
+    }
+    if (a) {
+        if (c->attn_head_dim != 64 && c->attn_head_dim != 256) return "attn_head_dim must be 64 or 256";
+        if (c->attn_kv_heads < 1 || c->attn_q_heads < 1 || c->attn_q_heads % c->attn_kv_heads)
+            return "attn_q_heads must be a positive multiple of attn_kv_heads";
+        const int G = c->attn_q_heads / c->attn_kv_heads;
+        if (!(G == 1 || G == 2 || G == 4 || G == 6 || G == 8)) return "attn_q_heads / attn_kv_heads must be 1, 2, 4, 6 or 8";
+    }
+    if (c->vocab < 0) return "vocab must be >= 0";
+    if (c->max_ctx < 1) return "max_ctx must be >= 1";
+    if (c->max_verify < 1 || c->max_verify > 4) return "max_verify must be in [1, 4]";
+    if (!(c->rms_eps > 0.f) || !std::isfinite(c->rms_eps)) return "rms_eps must be positive";
+    return nullptr;
+}
+
+// host-side nibble permutation between the logical W4 format and the GPU layout
+void w4_logical_to_gpu(const uint8_t* src, int64_t cols, uint32_t* dst) {
+    for (int64_t d = 0; d < cols / 8; ++d) {
+        uint32_t w = 0;
+        for (int e = 0; e < 8; ++e) {
+            const int64_t k = d * 8 + e;
+            const uint32_t nib = (k & 1) ? (src[k >> 1] >> 4) : (src[k >> 1] & 15);
+            w |= nib << (4 * w4_slot(e));
+        }
+        dst[d] = w;
+    }
+}
+
+void w4_gpu_to_logical(const uint32_t* src, int64_t cols, uint8_t* dst) {
+    memset(dst, 0, (size_t)(cols / 2));
+    for (int64_t d = 0; d < cols / 8; ++d)
+        for (int e = 0; e < 8; ++e) {
+            const int64_t k = d * 8 + e;
+            const uint8_t nib = (uint8_t)((src[d] >> (4 * w4_slot(e))) & 15);
+            dst[k >> 1] |= (k & 1) ? (uint8_t)(nib << 4) : nib;
+        }
+}
+
+struct MatRef {
+    uint32_t* w4 = nullptr;
+    int8_t* i8 = nullptr;
+    uint16_t* scales = nullptr;
+    int64_t rows = 0, cols = 0;
+    int64_t row_stride = 1;   // GPU rows between consecutive logical rows (2 for gate/up)
+};
+
+int mat_ref(aw4_model* m, int layer, int kind, MatRef* r) {
+    const aw4_config* c = &m->cfg;
+    if (kind == AW4_T_LM_HEAD) {
+        if (layer != -1 || c->vocab <= 0) return fail(m, AW4_E_INVAL, "lm_head needs layer -1 and vocab > 0");
+        r->i8 = m->lm_codes;
+        r->scales = m->lm_scales;
+        r->rows = c->vocab;
+        r->cols = c->hidden;
+        return AW4_OK;
+    }
+    if (kind < 0 || kind > 4 || layer < 0 || layer >= c->n_layers) return fail(m, AW4_E_INVAL, "bad layer/kind");
+    LayerBufs& b = m->L[layer];
+    const int64_t H = c->hidden, F = c->ffn;
+    switch (kind) {
+        case AW4_T_MIX_IN: *r = {b.w_in, nullptr, b.s_in, b.in_rows, H, 1}; break;
+        case AW4_T_MIX_OUT: *r = {b.w_out, nullptr, b.s_out, H, b.out_cols, 1}; break;
+        case AW4_T_FFN_GATE: *r = {b.w_gu, nullptr, b.s_gu, F, H, 2}; break;
+        case AW4_T_FFN_UP: *r = {b.w_gu + H / 8, nullptr, b.s_gu + H / 32, F, H, 2}; break;
+        case AW4_T_FFN_DOWN: *r = {b.w_down, nullptr, b.s_down, H, F, 1}; break;
+    }
+    return AW4_OK;
+}
+
+// ---------------------------------------------------------------- step sequence
+int enqueue_layers(aw4_model* m) {
+    const aw4_config* c = &m->cfg;
+    hipStream_t s = m->stream;
+    const int H = c->hidden, F = c->ffn;
+    for (int l = 0; l < c->n_layers; ++l) {
+        LayerBufs& b = m->L[l];
+        GemvArgs gi{};
+        gi.codes = b.w_in;
+        gi.scales = b.s_in;
+        gi.rows = (int)b.in_rows;
+        gi.K = H;
+        gi.x = m->x;
+        gi.nw = b.norm_mix;
+        gi.eps = c->rms_eps;
+        gi.y = m->proj;
+        HIPCHK(m, launch_gemv(PRO_NORM, EPI_STORE, gi, s));
+        if (b.type == 'G') {
+            GdnArgs ga{m->proj, b.a_bias, b.S, m->obuf, c->gdn_qk_heads, c->gdn_v_heads, c->gdn_head_dim, c->rms_eps};
+            HIPCHK(m, launch_gdn(ga, s));
+            GemvArgs go{};
+            go.codes = b.w_out;
+            go.scales = b.s_out;
+            go.rows = H;
+            go.K = (int)b.out_cols;
+            go.x = m->obuf;
+            go.nw = b.norm_gated;
+            go.z = m->proj + 2LL * c->gdn_qk_heads * c->gdn_head_dim + (int64_t)c->gdn_v_heads * c->gdn_head_dim;
+            go.gated_d = c->gdn_head_dim;
+            go.eps = c->rms_eps;
+            go.y = m->x;
+            HIPCHK(m, launch_gemv(PRO_GATED, EPI_RESID, go, s));
+        } else {
+            AttnArgs aa{};
+            aa.proj = m->proj;
+            aa.kc = b.kc;
+            aa.ks = b.ks;
+            aa.vc = b.vc;
+            aa.vs = b.vs;
+            aa.signs = m->signs;
+            aa.ctl = m->ctl;
+            aa.part = m->part;
+            aa.max_ctx = c->max_ctx;
+            aa.nq = c->attn_q_heads;
+            aa.nkv = c->attn_kv_heads;
+            aa.d = c->attn_head_dim;
+            aa.nsplit = m->nsplit;
+            HIPCHK(m, launch_attn(aa, s));
+            CombineArgs ca{m->part, m->proj, m->signs, m->ctl, m->abuf, c->attn_q_heads, c->attn_kv_heads,
+                           c->attn_head_dim, m->nsplit};
+            HIPCHK(m, launch_combine(ca, s));
+            GemvArgs go{};
+            go.codes = b.w_out;
+            go.scales = b.s_out;
+            go.rows = H;
+            go.K = (int)b.out_cols;
+            go.h = m->abuf;
+            go.y = m->x;
+            HIPCHK(m, launch_gemv(PRO_LOADH, EPI_RESID, go, s));
+        }
+        GemvArgs gf{};
+        gf.codes = b.w_gu;
+        gf.scales = b.s_gu;
+        gf.rows = 2 * F;
+        gf.K = H;
+        gf.x = m->x;
+        gf.nw = b.norm_ffn;
+        gf.eps = c->rms_eps;
+        gf.hout = m->hbuf;
+        HIPCHK(m, launch_gemv(PRO_NORM, EPI_SWIGLU, gf, s));
+        GemvArgs gd{};
+        gd.codes = b.w_down;
+        gd.scales = b.s_down;
+        gd.rows = H;
+        gd.K = F;
+        gd.h = m->hbuf;
+        gd.y = m->x;
+        HIPCHK(m, launch_gemv(PRO_LOADH, EPI_RESID, gd, s));
+    }
+    return AW4_OK;
+}
+
+// one launch of a phase for layer l (timing); returns its algorithmic bytes
+int enqueue_phase(aw4_model* m, int phase, int l, uint64_t* bytes) {
+    const aw4_config* c = &m->cfg;
+    hipStream_t s = m->stream;
+    const int H = c->hidden, F = c->ffn;
+    LayerBufs& b = m->L[l];
+    auto w4b = [](int64_t rows, int64_t cols) { return (uint64_t)(rows * cols / 2 + rows * (cols / 32) * 2); };
+    GemvArgs g{};
+    g.eps = c->rms_eps;
+    switch (phase) {
+        case AW4_PHASE_FFN_GATE_UP:
+            g.codes = b.w_gu; g.scales = b.s_gu; g.rows = 2 * F; g.K = H; g.x = m->x; g.nw = b.norm_ffn;
+            g.hout = m->hbuf;
+            *bytes = w4b(2LL * F, H) + (uint64_t)H * 8 + (uint64_t)F * 2;
+            HIPCHK(m, launch_gemv(PRO_NORM, EPI_SWIGLU, g, s));
+            break;
+        case AW4_PHASE_FFN_DOWN:
+            g.codes = b.w_down; g.scales = b.s_down; g.rows = H; g.K = F; g.h = m->hbuf; g.y = m->x;
+            *bytes = w4b(H, F) + (uint64_t)F * 2 + (uint64_t)H * 8;
+            HIPCHK(m, launch_gemv(PRO_LOADH, EPI_RESID, g, s));
+            break;
+        case AW4_PHASE_MIX_IN:
+            g.codes = b.w_in; g.scales = b.s_in; g.rows = (int)b.in_rows; g.K = H; g.x = m->x; g.nw = b.norm_mix;
+            g.y = m->proj;
+            *bytes = w4b(b.in_rows, H) + (uint64_t)H * 8 + (uint64_t)b.in_rows * 4;
+            HIPCHK(m, launch_gemv(PRO_NORM, EPI_STORE, g, s));
+            break;
+        default:
+            return fail(m, AW4_E_INVAL, "unknown phase");
+    }
+    return AW4_OK;
+}
+
+// embed ctl->token, run the layers, then either the head (argmax -> ctl->token,
+// pos += 1) or just pos += 1
+int enqueue_step(aw4_model* m, bool head) {
+    const aw4_config* c = &m->cfg;
+    hipStream_t s = m->stream;
+    HIPCHK(m, launch_embed(m->lm_codes, m->lm_scales, c->hidden, m->ctl, m->x, s));
+    int rc = enqueue_layers(m);
+    if (rc) return rc;
+    if (head) {
+        HeadArgs ha{m->lm_codes, m->lm_scales, c->vocab, c->hidden, m->x, m->norm_final, c->rms_eps,
+                    m->logits, m->pv, m->pi};
+        HIPCHK(m, launch_head(ha, s));
+        HIPCHK(m, launch_head_final(m->pv, m->pi, m->nhead_blocks, m->ctl, m->ring, m->ring_cap, s));
+    } else {
+        HIPCHK(m, launch_advance(m->ctl, s));
+    }
+    return AW4_OK;
+}
+
+int run_step(aw4_model* m, bool head) {
+    if (!m->use_graph) return enqueue_step(m, head);
+    hipGraphExec_t* ge = head ? &m->g_head : &m->g_nohead;
+    if (!*ge) {
+        hipGraph_t g = nullptr;
+        HIPCHK(m, hipStreamBeginCapture(m->stream, hipStreamCaptureModeThreadLocal));
+        int rc = enqueue_step(m, head);
+        hipError_t e = hipStreamEndCapture(m->stream, &g);
+        if (rc) {
+            if (g) (void)hipGraphDestroy(g);
+            return rc;
+        }
+        if (e != hipSuccess) return fail(m, AW4_E_HIP, std::string("hipStreamEndCapture: ") + hipGetErrorString(e));
+        e = hipGraphInstantiate(ge, g, nullptr, nullptr, 0);
+        (void)hipGraphDestroy(g);
+        if (e != hipSuccess) {
+            *ge = nullptr;
+            return fail(m, AW4_E_HIP, std::string("hipGraphInstantiate: ") + hipGetErrorString(e));
+        }
+    }
+    HIPCHK(m, hipGraphLaunch(*ge, m->stream));
+    return AW4_OK;
+}
+
+void drop_graphs(aw4_model* m) {
+    if (m->g_head) (void)hipGraphExecDestroy(m->g_head);
+    if (m->g_nohead) (void)hipGraphExecDestroy(m->g_nohead);
+    m->g_head = m->g_nohead = nullptr;
+}
+
+int check_model(aw4_model* m) {
+    if (!m) return AW4_E_INVAL;
+    return AW4_OK;
+}
+
+}  // namespace
+
+// ==================================================================== C ABI
+extern "C" {
+
+const char* aw4_status_string(int st) {
+    switch (st) {
+        case AW4_OK: return "ok";
+        case AW4_E_INVAL: return "invalid argument";
+        case AW4_E_ARENA: return "arena missing, misaligned or too small";
+        case AW4_E_NODEVICE: return "no gfx950 HIP device";
+        case AW4_E_HIP: return "HIP runtime error";
+        case AW4_E_FORMAT: return "weight blob format error";
+        case AW4_E_CTX_FULL: return "context full";
+        case AW4_E_TOKEN: return "token out of range";
+        case AW4_E_STATE: return "call not valid in the current state";
+        default: return "unknown status";
+    }
+}
+
+const char* aw4_last_error(const aw4_model* m) { return m ? m->err.c_str() : "null model"; }
+
+int aw4_validate_config(const aw4_config* cfg) { return check_config(cfg) ? AW4_E_INVAL : AW4_OK; }
+
+int aw4_workspace_bytes(const aw4_config* cfg, uint64_t* out) {
+    if (check_config(cfg) || !out) return AW4_E_INVAL;
+    *out = plan_layout(cfg, nullptr, nullptr);
+    return AW4_OK;
+}
+
+int aw4_create(const aw4_config* cfg, void* dev_arena, uint64_t arena_bytes, void* hip_stream, aw4_model** out) {
+    if (!out) return AW4_E_INVAL;
+    *out = nullptr;
+    if (check_config(cfg)) return AW4_E_INVAL;
+    const uint64_t need = plan_layout(cfg, nullptr, nullptr);
+    if (!dev_arena || ((uintptr_t)dev_arena & 255) || arena_bytes < need) return AW4_E_ARENA;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return AW4_E_NODEVICE;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return AW4_E_NODEVICE;
+    if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) return AW4_E_NODEVICE;
+    hipPointerAttribute_t attr;
+    if (hipPointerGetAttributes(&attr, dev_arena) != hipSuccess || attr.type != hipMemoryTypeDevice)
+        return AW4_E_ARENA;
+    aw4_model* m = new aw4_model();
+    m->cfg = *cfg;
+    m->arena = (uint8_t*)dev_arena;
+    m->arena_bytes = arena_bytes;
+    m->stream = (hipStream_t)hip_stream;
+    plan_layout(cfg, m, m->arena);
+    // zero everything once (weights included) so unused tensors are defined
+    if (launch_fill_zero(m->arena, need & ~uint64_t(3), m->stream) != hipSuccess) {
+        delete m;
+        return AW4_E_HIP;
+    }
+    *out = m;
+    return AW4_OK;
+}
+
+void aw4_destroy(aw4_model* m) {
+    if (!m) return;
+    drop_graphs(m);
+    delete m;
+}
+
+int aw4_tensor_shape(const aw4_model* mc, int32_t layer, int32_t kind, int64_t* rows, int64_t* cols) {
+    aw4_model* m = const_cast<aw4_model*>(mc);
+    if (check_model(m) || !rows || !cols) return AW4_E_INVAL;
+    const aw4_config* c = &m->cfg;
+    if (kind >= 0 && kind <= 5) {
+        MatRef r;
+        int rc = mat_ref(m, layer, kind, &r);
+        if (rc) return rc;
+        *rows = r.rows;
+        *cols = r.cols;
+        return AW4_OK;
+    }
+    int64_t n = -1;
+    if (kind == AW4_T_NORM_FINAL && layer == -1 && c->vocab > 0) n = c->hidden;
+    if (kind == AW4_T_RHT_SIGNS && layer == -1 && strchr(c->layer_pattern, 'A')) n = c->attn_head_dim;
+    if (layer >= 0 && layer < c->n_layers) {
+        const char t = c->layer_pattern[layer];
+        if (kind == AW4_T_NORM_MIX || kind == AW4_T_NORM_FFN) n = c->hidden;
+        if (kind == AW4_T_NORM_GATED && t == 'G') n = c->gdn_head_dim;
+        if (kind == AW4_T_A_BIAS && t == 'G') n = c->gdn_v_heads;
+    }
+    if (n < 0) return fail(m, AW4_E_INVAL, "no such tensor");
+    *rows = 1;
+    *cols = n;
+    return AW4_OK;
+}
+
+int aw4_quantize_tensor(aw4_model* m, int32_t layer, int32_t kind, int64_t row0, int64_t nrows, const float* src) {
+    if (check_model(m) || !src || nrows < 0) return AW4_E_INVAL;
+    MatRef r;
+    int rc = mat_ref(m, layer, kind, &r);
+    if (rc) return rc;
+    if (row0 < 0 || row0 + nrows > r.rows) return fail(m, AW4_E_INVAL, "row range outside the tensor");
+    if (nrows == 0) return AW4_OK;
+    if (r.i8) {
+        HIPCHK(m, launch_quant_i8(src, nrows, r.cols, r.i8 + row0 * r.cols, r.scales + row0 * (r.cols / 32), m->stream));
+    } else {
+        HIPCHK(m, launch_quant_w4(src, nrows, r.cols, r.w4 + row0 * r.row_stride * (r.cols / 8),
+                                  r.scales + row0 * r.row_stride * (r.cols / 32), r.row_stride, m->stream));
+    }
+    drop_graphs(m);
+    return AW4_OK;
+}
+
+int aw4_load_tensor(aw4_model* m, int32_t layer, int32_t kind, const void* host_codes, const uint16_t* host_scales) {
+    if (check_model(m) || !host_codes || !host_scales) return AW4_E_INVAL;
+    MatRef r;
+    int rc = mat_ref(m, layer, kind, &r);
+    if (rc) return rc;
+    const int64_t G = r.cols / 32;
+    HIPCHK(m, hipStreamSynchronize(m->stream));
+    if (r.i8) {
+        HIPCHK(m, hipMemcpy(r.i8, host_codes, (size_t)(r.rows * r.cols), hipMemcpyHostToDevice));
+        HIPCHK(m, hipMemcpy(r.scales, host_scales, (size_t)(r.rows * G * 2), hipMemcpyHostToDevice));
+        return AW4_OK;
+    }
+    std::vector<uint32_t> row(r.cols / 8);
+    const uint8_t* src = (const uint8_t*)host_codes;
+    // pack on the host, copy row by row into the (possibly interleaved) GPU rows
+    std::vector<uint32_t> buf((size_t)(r.rows * (r.cols / 8)));
+    for (int64_t i = 0; i < r.rows; ++i) w4_logical_to_gpu(src + i * (r.cols / 2), r.cols, buf.data() + i * (r.cols / 8));
+    HIPCHK(m, hipMemcpy2D(r.w4, (size_t)(r.row_stride * r.cols / 2), buf.data(), (size_t)(r.cols / 2),
+                          (size_t)(r.cols / 2), (size_t)r.rows, hipMemcpyHostToDevice));
+    HIPCHK(m, hipMemcpy2D(r.scales, (size_t)(r.row_stride * G * 2), host_scales, (size_t)(G * 2), (size_t)(G * 2),
+                          (size_t)r.rows, hipMemcpyHostToDevice));
+    drop_graphs(m);
+    return AW4_OK;
+}
+
+int aw4_export_tensor(aw4_model* m, int32_t layer, int32_t kind, void* host_codes, uint16_t* host_scales) {
+    if (check_model(m) || !host_codes || !host_scales) return AW4_E_INVAL;
+    MatRef r;
+    int rc = mat_ref(m, layer, kind, &r);
+    if (rc) return rc;
+    const int64_t G = r.cols / 32;
+    HIPCHK(m, hipStreamSynchronize(m->stream));
+    if (r.i8) {
+        HIPCHK(m, hipMemcpy(host_codes, r.i8, (size_t)(r.rows * r.cols), hipMemcpyDeviceToHost));
+        HIPCHK(m, hipMemcpy(host_scales, r.scales, (size_t)(r.rows * G * 2), hipMemcpyDeviceToHost));
+        return AW4_OK;
+    }
+    std::vector<uint32_t> buf((size_t)(r.rows * (r.cols / 8)));
+    HIPCHK(m, hipMemcpy2D(buf.data(), (size_t)(r.cols / 2), r.w4, (size_t)(r.row_stride * r.cols / 2),
+                          (size_t)(r.cols / 2), (size_t)r.rows, hipMemcpyDeviceToHost));
+    HIPCHK(m, hipMemcpy2D(host_scales, (size_t)(G * 2), r.scales, (size_t)(r.row_stride * G * 2), (size_t)(G * 2),
+                          (size_t)r.rows, hipMemcpyDeviceToHost));
+    uint8_t* dst = (uint8_t*)host_codes;
+    for (int64_t i = 0; i < r.rows; ++i) w4_gpu_to_logical(buf.data() + i * (r.cols / 8), r.cols, dst + i * (r.cols / 2));
+    return AW4_OK;
+}
+
+int aw4_set_vector(aw4_model* m, int32_t layer, int32_t kind, const float* vals, int32_t n) {
+    if (check_model(m) || !vals) return AW4_E_INVAL;
+    int64_t rows = 0, cols = 0;
+    int rc = aw4_tensor_shape(m, layer, kind, &rows, &cols);
+    if (rc) return rc;
+    if (kind < 6 || n != cols) return fail(m, AW4_E_INVAL, "vector length mismatch");
+    float* dst = nullptr;
+    if (kind == AW4_T_NORM_FINAL) dst = m->norm_final;
+    else if (kind == AW4_T_RHT_SIGNS) {
+        for (int i = 0; i < n; ++i)
+            if (vals[i] != 1.0f && vals[i] != -1.0f) return fail(m, AW4_E_INVAL, "rotation signs must be +-1");
+        dst = m->signs;
+    } else {
+        LayerBufs& b = m->L[layer];
+        dst = kind == AW4_T_NORM_MIX ? b.norm_mix : kind == AW4_T_NORM_FFN ? b.norm_ffn
+              : kind == AW4_T_NORM_GATED ? b.norm_gated : b.a_bias;
+    }
+    HIPCHK(m, hipStreamSynchronize(m->stream));
+    HIPCHK(m, hipMemcpy(dst, vals, (size_t)n * 4, hipMemcpyHostToDevice));
+    return AW4_OK;
+}
+
+int aw4_load_weights(aw4_model* m, const void* blob, uint64_t bytes) {
+    if (check_model(m) || !blob) return AW4_E_INVAL;
+    const uint8_t* p = (const uint8_t*)blob;
+    const uint8_t* end = p + bytes;
+    auto need = [&](uint64_t n) { return (uint64_t)(end - p) >= n; };
+    if (!need(4 + 4 + sizeof(aw4_config) + 4) || memcmp(p, "AW4W", 4) != 0)
+        return fail(m, AW4_E_FORMAT, "bad magic or truncated header");
+    p += 4;
+    uint32_t ver;
+    memcpy(&ver, p, 4);
+    p += 4;
+    if (ver != 1) return fail(m, AW4_E_FORMAT, "unsupported blob version");
+    aw4_config bc;
+    memcpy(&bc, p, sizeof(bc));
+    p += sizeof(bc);
+    const aw4_config* c = &m->cfg;
+    if (bc.hidden != c->hidden || bc.ffn != c->ffn || bc.vocab != c->vocab || bc.n_layers != c->n_layers ||
+        bc.gdn_qk_heads != c->gdn_qk_heads || bc.gdn_v_heads != c->gdn_v_heads || bc.gdn_head_dim != c->gdn_head_dim ||
+        bc.attn_q_heads != c->attn_q_heads || bc.attn_kv_heads != c->attn_kv_heads ||
+        bc.attn_head_dim != c->attn_head_dim || bc.group != c->group ||
+        strncmp(bc.layer_pattern, c->layer_pattern, 128) != 0)
+        return fail(m, AW4_E_FORMAT, "blob was made for another config");
+    uint32_t count;
+    memcpy(&count, p, 4);
+    p += 4;
+    for (uint32_t t = 0; t < count; ++t) {
+        if (!need(32)) return fail(m, AW4_E_FORMAT, "truncated tensor header");
+        int32_t layer, kind;
+        int64_t rows, cols;
+        uint64_t nb;
+        memcpy(&layer, p, 4);
+        memcpy(&kind, p + 4, 4);
+        memcpy(&rows, p + 8, 8);
+        memcpy(&cols, p + 16, 8);
+        memcpy(&nb, p + 24, 8);
+        p += 32;
+        if (!need(nb)) return fail(m, AW4_E_FORMAT, "truncated tensor payload");
+        int64_t er = 0, ec = 0;
+        if (aw4_tensor_shape(m, layer, kind, &er, &ec) || er != rows || ec != cols)
+            return fail(m, AW4_E_FORMAT, "tensor shape does not match the config");
+        int rc;
+        if (kind <= 5) {
+            const uint64_t cb = kind == AW4_T_LM_HEAD ? (uint64_t)rows * cols : (uint64_t)rows * cols / 2;
+            const uint64_t sb = (uint64_t)rows * (cols / 32) * 2;
+            if (nb != cb + sb) return fail(m, AW4_E_FORMAT, "tensor payload size mismatch");
+            std::vector<uint16_t> sc((size_t)(sb / 2));
+            memcpy(sc.data(), p + cb, (size_t)sb);
+            rc = aw4_load_tensor(m, layer, kind, p, sc.data());
+        } else {
+            if (nb != (uint64_t)cols * 4) return fail(m, AW4_E_FORMAT, "vector payload size mismatch");
+            std::vector<float> v((size_t)cols);
+            memcpy(v.data(), p, (size_t)nb);
+            rc = aw4_set_vector(m, layer, kind, v.data(), (int32_t)cols);
+        }
+        if (rc) return rc == AW4_E_INVAL ? fail(m, AW4_E_FORMAT, "bad tensor: " + m->err) : rc;
+        p += nb;
+    }
+    if (p != end) return fail(m, AW4_E_FORMAT, "trailing bytes after the last tensor");
+    return AW4_OK;
+}
+
+int aw4_reset(aw4_model* m) {
+    if (check_model(m)) return AW4_E_INVAL;
+    HIPCHK(m, launch_fill_zero(m->arena + m->state_off, m->state_bytes, m->stream));
+    HIPCHK(m, launch_set_ctl(m->ctl, 0, 0, 0, m->stream));
+    m->host_pos = 0;
+    return AW4_OK;
+}
+
+int aw4_set_graph(aw4_model* m, int32_t enable) {
+    if (check_model(m)) return AW4_E_INVAL;
+    m->use_graph = enable != 0;
+    if (!m->use_graph) drop_graphs(m);
+    return AW4_OK;
+}
+
+int aw4_get_pos(aw4_model* m, int32_t* pos) {
+    if (check_model(m) || !pos) return AW4_E_INVAL;
+    *pos = m->host_pos;
+    return AW4_OK;
+}
+
+int aw4_set_pos(aw4_model* m, int32_t pos) {
+    if (check_model(m)) return AW4_E_INVAL;
+    if (pos < 0 || pos > m->cfg.max_ctx) return fail(m, AW4_E_CTX_FULL, "position outside [0, max_ctx]");
+    HIPCHK(m, launch_set_ctl(m->ctl, pos, -1, -1, m->stream));
+    m->host_pos = pos;
+    return AW4_OK;
+}
+
+int aw4_prefill(aw4_model* m, const int32_t* tokens, int32_t n, float* dev_logits) {
+    if (check_model(m) || (!tokens && n > 0) || n < 0) return AW4_E_INVAL;
+    if (m->cfg.vocab <= 0) return fail(m, AW4_E_STATE, "prefill needs a vocabulary");
+    if ((int64_t)m->host_pos + n > m->cfg.max_ctx) return fail(m, AW4_E_CTX_FULL, "prompt exceeds max_ctx");
+    for (int i = 0; i < n; ++i)
+        if (tokens[i] < 0 || tokens[i] >= m->cfg.vocab) return fail(m, AW4_E_TOKEN, "prompt token out of range");
+    for (int i = 0; i < n; ++i) {
+        HIPCHK(m, launch_set_token(m->ctl, tokens[i], m->stream));
+        const bool last = i == n - 1;
+        int rc = run_step(m, last && dev_logits != nullptr);
+        if (rc) return rc;
+        m->host_pos += 1;
+    }
+    if (n > 0 && dev_logits)
+        HIPCHK(m, hipMemcpyAsync(dev_logits, m->logits, (size_t)m->cfg.vocab * 4, hipMemcpyDeviceToDevice, m->stream));
+    return AW4_OK;
+}
+
+int aw4_decode_step(aw4_model* m, int32_t token, float* dev_logits, int32_t* host_argmax) {
+    if (check_model(m)) return AW4_E_INVAL;
+    if (m->cfg.vocab <= 0) return fail(m, AW4_E_STATE, "decode_step needs a vocabulary");
+    if (token < 0 || token >= m->cfg.vocab) return fail(m, AW4_E_TOKEN, "token out of range");
+    if (m->host_pos + 1 > m->cfg.max_ctx) return fail(m, AW4_E_CTX_FULL, "context full");
+    HIPCHK(m, launch_set_token(m->ctl, token, m->stream));
+    int rc = run_step(m, true);
+    if (rc) return rc;
+    m->host_pos += 1;
+    if (dev_logits)
+        HIPCHK(m, hipMemcpyAsync(dev_logits, m->logits, (size_t)m->cfg.vocab * 4, hipMemcpyDeviceToDevice, m->stream));
+    if (host_argmax) {
+        HIPCHK(m, hipMemcpyAsync(host_argmax, &m->ctl->argmax, 4, hipMemcpyDeviceToHost, m->stream));
+        HIPCHK(m, hipStreamSynchronize(m->stream));
+    }
+    return AW4_OK;
+}
+
+int aw4_decode_greedy(aw4_model* m, int32_t first_token, int32_t n_steps, int32_t* host_out) {
+    if (check_model(m) || n_steps < 0 || (!host_out && n_steps > 0)) return AW4_E_INVAL;
+    if (m->cfg.vocab <= 0) return fail(m, AW4_E_STATE, "decode_greedy needs a vocabulary");
+    if (first_token < 0 || first_token >= m->cfg.vocab) return fail(m, AW4_E_TOKEN, "token out of range");
+    if ((int64_t)m->host_pos + n_steps > m->cfg.max_ctx) return fail(m, AW4_E_CTX_FULL, "context full");
+    int done = 0;
+    int32_t tok = first_token;
+    while (done < n_steps) {
+        const int chunk = n_steps - done < m->ring_cap ? n_steps - done : m->ring_cap;
+        HIPCHK(m, launch_set_ctl(m->ctl, -1, tok, 0, m->stream));
+        for (int i = 0; i < chunk; ++i) {
+            int rc = run_step(m, true);
+            if (rc) return rc;
+            m->host_pos += 1;
+        }
+        HIPCHK(m, hipMemcpyAsync(host_out + done, m->ring, (size_t)chunk * 4, hipMemcpyDeviceToHost, m->stream));
+        HIPCHK(m, hipStreamSynchronize(m->stream));
+        done += chunk;
+        tok = host_out[done - 1];
+    }
+    return AW4_OK;
+}
+
+int aw4_decode_hidden(aw4_model* m, const float* dev_in, float* dev_out) {
+    if (check_model(m) || !dev_in || !dev_out) return AW4_E_INVAL;
+    if (m->host_pos + 1 > m->cfg.max_ctx) return fail(m, AW4_E_CTX_FULL, "context full");
+    if (dev_in != m->x) HIPCHK(m, launch_copy_f32(m->x, dev_in, m->cfg.hidden, m->stream));
+    int rc = enqueue_layers(m);
+    if (rc) return rc;
+    HIPCHK(m, launch_advance(m->ctl, m->stream));
+    if (dev_out != m->x) HIPCHK(m, launch_copy_f32(dev_out, m->x, m->cfg.hidden, m->stream));
+    m->host_pos += 1;
+    return AW4_OK;
+}
+
+int aw4_read_hidden(aw4_model* m, float* host_x) {
+    if (check_model(m) || !host_x) return AW4_E_INVAL;
+    HIPCHK(m, hipMemcpyAsync(host_x, m->x, (size_t)m->cfg.hidden * 4, hipMemcpyDeviceToHost, m->stream));
+    HIPCHK(m, hipStreamSynchronize(m->stream));
+    return AW4_OK;
+}
+
+int aw4_time_phase(aw4_model* m, int32_t phase, int32_t reps, float* avg_us, uint64_t* bytes_per_launch) {
+    if (check_model(m) || reps < 1 || !avg_us || !bytes_per_launch) return AW4_E_INVAL;
+    if (phase < 0 || phase > AW4_PHASE_MIX_IN) return fail(m, AW4_E_INVAL, "unknown phase");
+    hipEvent_t e0, e1;
+    HIPCHK(m, hipEventCreate(&e0));
+    HIPCHK(m, hipEventCreate(&e1));
+    uint64_t bytes = 0;
+    const int L = m->cfg.n_layers;
+    // round robin over the layers so that consecutive launches stream different
+    // weights (a single layer's matrices would stay in the 256 MB last-level cache)
+    for (int i = 0; i < L && i < reps; ++i) {
+        int rc = enqueue_phase(m, phase, i % L, &bytes);
+        if (rc) return rc;
+    }
+    HIPCHK(m, hipEventRecord(e0, m->stream));
+    for (int i = 0; i < reps; ++i) {
+        int rc = enqueue_phase(m, phase, i % L, &bytes);
+        if (rc) return rc;
+    }
+    HIPCHK(m, hipEventRecord(e1, m->stream));
+    HIPCHK(m, hipEventSynchronize(e1));
+    float ms = 0.f;
+    HIPCHK(m, hipEventElapsedTime(&ms, e0, e1));
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    *avg_us = ms * 1000.f / (float)reps;
+    *bytes_per_launch = bytes;
+    return AW4_OK;
+}
+
+int aw4_export_state_gdn(aw4_model* m, int32_t layer, float* host_S) {
+    if (check_model(m) || !host_S || layer < 0 || layer >= m->cfg.n_layers || m->L[layer].type != 'G')
+        return fail(m, AW4_E_INVAL, "not a GDN layer");
+    const aw4_config* c = &m->cfg;
+    const size_t n = (size_t)c->gdn_v_heads * c->gdn_head_dim * c->gdn_head_dim;
+    HIPCHK(m, hipStreamSynchronize(m->stream));
+    HIPCHK(m, hipMemcpy(host_S, m->L[layer].S, n * 4, hipMemcpyDeviceToHost));
+    return AW4_OK;
+}
+
+int aw4_import_state_gdn(aw4_model* m, int32_t layer, const float* host_S) {
+    if (check_model(m) || !host_S || layer < 0 || layer >= m->cfg.n_layers || m->L[layer].type != 'G')
+        return fail(m, AW4_E_INVAL, "not a GDN layer");
+    const aw4_config* c = &m->cfg;
+    const size_t n = (size_t)c->gdn_v_heads * c->gdn_head_dim * c->gdn_head_dim;
+    HIPCHK(m, hipStreamSynchronize(m->stream));
+    HIPCHK(m, hipMemcpy(m->L[layer].S, host_S, n * 4, hipMemcpyHostToDevice));
+    return AW4_OK;
+}
+
+int aw4_export_state_kv(aw4_model* m, int32_t layer, int32_t npos, int8_t* kc, uint16_t* ks, int8_t* vc,
+                        uint16_t* vs) {
+    if (check_model(m) || !kc || !ks || !vc || !vs || layer < 0 || layer >= m->cfg.n_layers ||
+        m->L[layer].type != 'A')
+        return fail(m, AW4_E_INVAL, "not an attention layer");
+    const aw4_config* c = &m->cfg;
+    if (npos < 0 || npos > c->max_ctx) return fail(m, AW4_E_INVAL, "npos outside [0, max_ctx]");
+    const int nkv = c->attn_kv_heads, d = c->attn_head_dim, NG = d / 32;
+    LayerBufs& b = m->L[layer];
+    HIPCHK(m, hipStreamSynchronize(m->stream));
+    std::vector<int8_t> k((size_t)npos * d);
+    std::vector<uint16_t> s1((size_t)npos * NG), s2((size_t)npos * NG);
+    std::vector<uint32_t> v((size_t)npos * NG * 3);
+    for (int j = 0; j < nkv; ++j) {
+        const int64_t hb = (int64_t)j * c->max_ctx;
+        if (npos == 0) break;
+        HIPCHK(m, hipMemcpy(k.data(), b.kc + hb * d, k.size(), hipMemcpyDeviceToHost));
+        HIPCHK(m, hipMemcpy(s1.data(), b.ks + hb * NG, s1.size() * 2, hipMemcpyDeviceToHost));
+        HIPCHK(m, hipMemcpy(s2.data(), b.vs + hb * NG, s2.size() * 2, hipMemcpyDeviceToHost));
+        HIPCHK(m, hipMemcpy(v.data(), b.vc + hb * NG * 3, v.size() * 4, hipMemcpyDeviceToHost));
+        for (int t = 0; t < npos; ++t) {
+            const int64_t lo = ((int64_t)t * nkv + j);
+            memcpy(kc + lo * d, k.data() + (size_t)t * d, (size_t)d);
+            memcpy(ks + lo * NG, s1.data() + (size_t)t * NG, (size_t)NG * 2);
+            memcpy(vs + lo * NG, s2.data() + (size_t)t * NG, (size_t)NG * 2);
+            for (int g = 0; g < NG; ++g) {
+                const uint32_t* w = v.data() + ((size_t)t * NG + g) * 3;
+                for (int i = 0; i < 32; ++i) {
+                    const int bit = 3 * i, wi = bit >> 5, off = bit & 31;
+                    uint64_t bits = (uint64_t)w[wi] | (wi < 2 ? (uint64_t)w[wi + 1] << 32 : 0ull);
+                    vc[lo * d + g * 32 + i] = (int8_t)((int)((bits >> off) & 7u) - 4);
+                }
+            }
+        }
+    }
+    return AW4_OK;
+}
+
+int aw4_import_state_kv(aw4_model* m, int32_t layer, int32_t npos, const int8_t* kc, const uint16_t* ks,
+                        const int8_t* vc, const uint16_t* vs) {
+    if (check_model(m) || !kc || !ks || !vc || !vs || layer < 0 || layer >= m->cfg.n_layers ||
+        m->L[layer].type != 'A')
+        return fail(m, AW4_E_INVAL, "not an attention layer");
+    const aw4_config* c = &m->cfg;
+    if (npos < 0 || npos > c->max_ctx) return fail(m, AW4_E_INVAL, "npos outside [0, max_ctx]");
+    const int nkv = c->attn_kv_heads, d = c->attn_head_dim, NG = d / 32;
+    for (int64_t i = 0; i < (int64_t)npos * nkv * d; ++i)
+        if (vc[i] < -3 || vc[i] > 3) return fail(m, AW4_E_INVAL, "V codes must be in -3..3");
+    LayerBufs& b = m->L[layer];
+    HIPCHK(m, hipStreamSynchronize(m->stream));
+    std::vector<int8_t> k((size_t)npos * d);
+    std::vector<uint16_t> s1((size_t)npos * NG), s2((size_t)npos * NG);
+    std::vector<uint32_t> v((size_t)npos * NG * 3);
+    for (int j = 0; j < nkv && npos > 0; ++j) {
+        for (int t = 0; t < npos; ++t) {
+            const int64_t lo = ((int64_t)t * nkv + j);
+            memcpy(k.data() + (size_t)t * d, kc + lo * d, (size_t)d);
+            memcpy(s1.data() + (size_t)t * NG, ks + lo * NG, (size_t)NG * 2);
+            memcpy(s2.data() + (size_t)t * NG, vs + lo * NG, (size_t)NG * 2);
+            for (int g = 0; g < NG; ++g) {
+                uint32_t w[3] = {0, 0, 0};
+                for (int i = 0; i < 32; ++i) {
+                    const uint32_t n = (uint32_t)(vc[lo * d + g * 32 + i] + 4) & 7u;
+                    const int bit = 3 * i, wi = bit >> 5, off = bit & 31;
+                    w[wi] |= n << off;
+                    if (off > 29) w[wi + 1] |= n >> (32 - off);
+                }
+                memcpy(v.data() + ((size_t)t * NG + g) * 3, w, 12);
+            }
+        }
+        const int64_t hb = (int64_t)j * c->max_ctx;
+        HIPCHK(m, hipMemcpy(b.kc + hb * d, k.data(), k.size(), hipMemcpyHostToDevice));
+        HIPCHK(m, hipMemcpy(b.ks + hb * NG, s1.data(), s1.size() * 2, hipMemcpyHostToDevice));
+        HIPCHK(m, hipMemcpy(b.vs + hb * NG, s2.data(), s2.size() * 2, hipMemcpyHostToDevice));
+        HIPCHK(m, hipMemcpy(b.vc + hb * NG * 3, v.data(), v.size() * 4, hipMemcpyHostToDevice));
+    }
+    return AW4_OK;
+}
+
+}  // extern "C"

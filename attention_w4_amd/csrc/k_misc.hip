@@ -1,0 +1,147 @@
+// Small kernels: embedding, control-block updates, fills, and the group codec
+// that packs fp32 weights into the GPU layouts.
+//
+// Codec (4-bit weights per page 1, dcwnkz.com "27B x 4 bit" estimate, and page
+// 4, jdon.com W4A16; the int8 head follows the same recipe with qmax 127):
+// per 32 consecutive inputs of a row, s = fp16(amax / qmax) with the quotient
+// in fp32 and round-to-nearest-even, codes clamp(rint(w / s), -qmax, qmax),
+// all codes 0 when s rounds to 0.
+#include "aw4_internal.h"
+
+namespace aw4 {
+namespace {
+
+__global__ void k_embed(const int8_t* __restrict__ codes, const uint16_t* __restrict__ scales, int H,
+                        const Ctl* ctl, float* __restrict__ x) {
+    const int64_t tok = ctl->token;
+    for (int k = blockIdx.x * blockDim.x + threadIdx.x; k < H; k += gridDim.x * blockDim.x) {
+        const float s = (float)__builtin_bit_cast(_Float16, scales[tok * (H / 32) + k / 32]);
+        x[k] = (float)codes[tok * H + k] * s;
+    }
+}
+
+__global__ void k_set_token(Ctl* ctl, int32_t token) { ctl->token = token; }
+
+__global__ void k_advance(Ctl* ctl) { ctl->pos += 1; }
+
+__global__ void k_set_ctl(Ctl* ctl, int32_t pos, int32_t token, int32_t nstep) {
+    if (pos >= 0) ctl->pos = pos;
+    if (token >= 0) ctl->token = token;
+    if (nstep >= 0) ctl->nstep = nstep;
+}
+
+__global__ void k_fill_zero(uint32_t* p, uint64_t n) {
+    for (uint64_t i = blockIdx.x * (uint64_t)blockDim.x + threadIdx.x; i < n; i += (uint64_t)gridDim.x * blockDim.x)
+        p[i] = 0u;
+}
+
+__global__ void k_copy_f32(float* dst, const float* src, int64_t n) {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        dst[i] = src[i];
+}
+
+__device__ __forceinline__ void quant_group32(const float* w, int qmax, int* c, uint16_t* sbits) {
+    float amax = 0.f;
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(w[i]));
+    const _Float16 sh = (_Float16)(amax / (float)qmax);
+    const float s = (float)sh;
+    for (int i = 0; i < 32; ++i) {
+        float q = s == 0.f ? 0.f : rintf(w[i] / s);
+        q = fminf(fmaxf(q, -(float)qmax), (float)qmax);
+        c[i] = (int)q;
+    }
+    *sbits = __builtin_bit_cast(uint16_t, sh);
+}
+
+// one thread per (row, group of 32); dst rows are row_stride apart
+__global__ void k_quant_w4(const float* __restrict__ src, int64_t nrows, int64_t cols, uint32_t* __restrict__ codes,
+                           uint16_t* __restrict__ scales, int64_t row_stride) {
+    const int64_t G = cols / 32;
+    for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < nrows * G;
+         t += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t r = t / G, g = t % G;
+        int c[32];
+        uint16_t sb;
+        quant_group32(src + r * cols + g * 32, 7, c, &sb);
+        uint32_t* dst = codes + r * row_stride * (cols / 8) + g * 4;
+        for (int m = 0; m < 4; ++m) {
+            uint32_t w = 0;
+            for (int e = 0; e < 8; ++e) w |= (uint32_t)((c[8 * m + e] + 8) & 15) << (4 * w4_slot(e));
+            dst[m] = w;
+        }
+        scales[r * row_stride * G + g] = sb;
+    }
+}
+
+__global__ void k_quant_i8(const float* __restrict__ src, int64_t nrows, int64_t cols, int8_t* __restrict__ codes,
+                           uint16_t* __restrict__ scales) {
+    const int64_t G = cols / 32;
+    for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < nrows * G;
+         t += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t r = t / G, g = t % G;
+        int c[32];
+        uint16_t sb;
+        quant_group32(src + r * cols + g * 32, 127, c, &sb);
+        for (int i = 0; i < 32; ++i) codes[r * cols + g * 32 + i] = (int8_t)c[i];
+        scales[r * G + g] = sb;
+    }
+}
+
+int grid_for(int64_t n, int per_block = 256) {
+    int64_t g = (n + per_block - 1) / per_block;
+    if (g > 8192) g = 8192;
+    if (g < 1) g = 1;
+    return (int)g;
+}
+
+}  // namespace
+
+hipError_t launch_embed(const int8_t* codes, const uint16_t* scales, int H, const Ctl* ctl, float* x,
+                        hipStream_t s) {
+    hipLaunchKernelGGL(k_embed, dim3(grid_for(H)), dim3(256), 0, s, codes, scales, H, ctl, x);
+    return hipGetLastError();
+}
+
+hipError_t launch_set_token(Ctl* ctl, int32_t token, hipStream_t s) {
+    hipLaunchKernelGGL(k_set_token, dim3(1), dim3(1), 0, s, ctl, token);
+    return hipGetLastError();
+}
+
+hipError_t launch_advance(Ctl* ctl, hipStream_t s) {
+    hipLaunchKernelGGL(k_advance, dim3(1), dim3(1), 0, s, ctl);
+    return hipGetLastError();
+}
+
+hipError_t launch_set_ctl(Ctl* ctl, int32_t pos, int32_t token, int32_t nstep, hipStream_t s) {
+    hipLaunchKernelGGL(k_set_ctl, dim3(1), dim3(1), 0, s, ctl, pos, token, nstep);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(void* p, uint64_t bytes, hipStream_t s) {
+    if (bytes % 4) return hipErrorInvalidValue;
+    const uint64_t n = bytes / 4;
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_fill_zero, dim3(grid_for((int64_t)n)), dim3(256), 0, s, (uint32_t*)p, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_copy_f32(float* dst, const float* src, int64_t n, hipStream_t s) {
+    hipLaunchKernelGGL(k_copy_f32, dim3(grid_for(n)), dim3(256), 0, s, dst, src, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_w4(const float* src, int64_t nrows, int64_t cols, uint32_t* codes, uint16_t* scales,
+                           int64_t row_stride, hipStream_t s) {
+    hipLaunchKernelGGL(k_quant_w4, dim3(grid_for(nrows * (cols / 32))), dim3(256), 0, s, src, nrows, cols, codes,
+                       scales, row_stride);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_i8(const float* src, int64_t nrows, int64_t cols, int8_t* codes, uint16_t* scales,
+                           hipStream_t s) {
+    hipLaunchKernelGGL(k_quant_i8, dim3(grid_for(nrows * (cols / 32))), dim3(256), 0, s, src, nrows, cols, codes,
+                       scales);
+    return hipGetLastError();
+}
+
+}  // namespace aw4

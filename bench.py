@@ -1,0 +1,203 @@
+#!/usr/bin/env python3
+"""Batch-1 decode benchmark of the 27B-shape hybrid W4 stack on one MI355X.
+
+Workload (the full synthetic stack): 64 layers (48 Gated DeltaNet + 16 gated
+attention, 3:1), W4A16 group-32 random weights (~14.2 GB), int8 lm_head with
+vocab 248320, an 8192-token random prompt, then greedy decode.  The pages the
+method comes from measure single-user decode speed of this model class in
+tok/s and attribute it to weight streaming (page 5, bs178.com llamAmpere
+article, "为什么它真能这么快" point 二); the metric here is decode tok/s plus
+the fraction of the HBM roofline (algorithmic bytes per token / 8 TB/s).
+
+Timed region: `--steps` greedy steps through aw4_decode_greedy (one captured
+HIP graph per token, argmax fed back on the device), after `--warmup` steps,
+with weights, prompt state and caches already resident in HBM.
+
+Prints one JSON line.
+"""
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def step_bytes(shape, pos):
+    """Algorithmic HBM bytes of one decode step at position pos (the token
+    attends to pos + 1 cached positions)."""
+    from synth import workloads as W
+    H, F = shape.hidden, shape.ffn
+    w4 = lambda r, c: r * c // 2 + r * (c // 32) * 2
+    b = 0
+    for t in shape.pattern:
+        b += w4(W.mixer_in_rows(shape, t), H) + w4(H, W.mixer_out_cols(shape, t))
+        b += 2 * w4(F, H) + w4(H, F)
+    if shape.vocab:
+        b += shape.vocab * H + shape.vocab * (H // 32) * 2      # int8 head
+        b += shape.vocab * 4                                    # logits
+    ng = shape.pattern.count("G")
+    na = shape.pattern.count("A")
+    b += ng * shape.gdn_v_heads * shape.gdn_head_dim ** 2 * 4 * 2   # state read + write
+    d = shape.attn_head_dim
+    kv_pos = shape.attn_kv_heads * (d + d * 3 // 8 + 2 * (d // 32) * 2)
+    b += na * kv_pos * (pos + 1)                                # cache read incl. the new entry
+    return b
+
+
+def cpu_baseline(ctx, seed):
+    """Oracle on a bounded sample: one GDN layer step and one attention layer
+    step at `ctx` cached positions (synthetic state), and the int8 head over a
+    1/8 slice of the vocabulary; scaled to one full token."""
+    import numpy as np
+    import oracle
+    import synth
+    from synth import state as SS
+    from synth import workloads as W
+    full = W.FULL_27B
+    g = W.with_(full, pattern="G", vocab=0, max_ctx=ctx + 8)
+    a = W.with_(full, pattern="A", vocab=full.vocab // 8, max_ctx=ctx + 8)
+    og = oracle.from_recipe(g, seed)
+    oa = oracle.from_recipe(a, seed)
+    SS.fill(og, g, ctx, seed)
+    SS.fill(oa, a, ctx, seed)
+    x = synth.normal(1, full.hidden, 1.0, seed, W.STREAM_HIDDEN)[0].astype(np.float64)
+
+    def med(f, n=3):
+        f()
+        ts = []
+        for _ in range(n):
+            t0 = time.perf_counter()
+            f()
+            ts.append(time.perf_counter() - t0)
+        return statistics.median(ts)
+
+    def step_g():
+        og.set_pos(ctx)
+        og.forward_layers(x)
+
+    def step_a():
+        oa.set_pos(ctx)
+        oa.forward_layers(x)
+
+    tg, ta = med(step_g), med(step_a)
+    th = med(lambda: oa.head(x)) * 8
+    per_token = full.pattern.count("G") * tg + full.pattern.count("A") * ta + th
+    cores = len(os.sched_getaffinity(0))
+    threads = int(os.environ.get("OMP_NUM_THREADS", cores))
+    return {"value": round(1.0 / per_token, 4), "unit": "tok/s", "cores": min(cores, threads), "kind": "oracle",
+            "sample": (f"fp64 C oracle: 1 GDN layer step ({tg:.3f} s) and 1 attention layer step ({ta:.3f} s) at "
+                       f"{ctx} cached positions, int8 head over vocab/8 ({th / 8:.3f} s); median of 3; "
+                       f"scaled to 48 + 16 layers + full head = {per_token:.2f} s/token")}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1024)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--ctx", type=int, default=8192, help="prompt length before the timed steps")
+    ap.add_argument("--prompt", choices=["decode", "synthetic"], default="decode",
+                    help="decode: run the random prompt through the model; synthetic: import a seeded "
+                         "cache/state of ctx positions")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--phase-reps", type=int, default=128)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU: the batch-1 decode path is built "
+                                   "and measured on a single MI355X; --gpus must be 1"}))
+        sys.exit(2)
+
+    import torch
+    import attention_w4_amd as A
+    import synth
+    from synth import workloads as W
+    from synth import state as SS
+    from synth.gpu_load import load_recipe
+
+    shape = W.with_(W.FULL_27B, max_ctx=args.ctx + args.warmup + args.steps + 8)
+    t0 = time.time()
+    m = A.Model(shape)
+    load_recipe(m, shape, args.seed)
+    t_load = time.time() - t0
+    prompt = synth.tokens(args.ctx, shape.vocab, args.seed)
+    t0 = time.time()
+    if args.prompt == "decode":
+        m.prefill(prompt[:-1])
+    else:
+        SS.fill(m, shape, args.ctx - 1, args.seed)
+    m.sync()
+    t_prompt = time.time() - t0
+    first = int(prompt[-1])
+    warm = m.decode_greedy(first, args.warmup) if args.warmup else [first]
+    tok = int(warm[-1])
+    pos0 = m.pos
+
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(m.stream)
+    t0 = time.perf_counter()
+    toks = m.decode_greedy(tok, args.steps)
+    ev1.record(m.stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall = t1 - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    tok_s = args.steps / wall
+    ms_step = wall * 1e3 / args.steps
+    total_bytes = sum(step_bytes(shape, p) for p in range(pos0, pos0 + args.steps))
+    gbs = total_bytes / wall / 1e9
+
+    # dominant kernel: the fused RMSNorm + gate/up W4 GEMV + SwiGLU (66% of the
+    # weight bytes are FFN, gate/up alone 46% of the step)
+    us, nbytes = m.time_phase(A.PHASE_FFN_GATE_UP, args.phase_reps)
+    ach = nbytes / (us * 1e-6) / 1e9
+    others = {}
+    for name, ph in (("ffn_down", A.PHASE_FFN_DOWN), ("mixer_in", A.PHASE_MIX_IN)):
+        u, b = m.time_phase(ph, args.phase_reps)
+        others[name] = {"avg_us": round(u, 2), "bytes": b, "GB/s": round(b / (u * 1e-6) / 1e9, 1)}
+
+    out = {
+        "metric": "batch-1 decode tok/s (27B-shape W4) + % of HBM roofline, 8K and 262K ctx",
+        "value": round(tok_s, 2),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "w4a16 (int4 codes x fp16 scales, fp16 activations, fp32 accumulate)",
+        "data": "synthetic (seeded random weights, random prompt)",
+        "config": {"workload": f"27B-shape hybrid stack, 64 layers (48 GDN + 16 gated attention), "
+                               f"{args.ctx}-token random prompt then greedy decode, batch 1",
+                   "ctx_start": int(pos0), "prompt": args.prompt, "global_batch": 1},
+        "hbm": {"algorithmic_GB_per_step": round(total_bytes / args.steps / 1e9, 4),
+                "achieved_GB/s": round(gbs, 1), "frac_of_8TB/s": round(gbs / HBM_PEAK_GBS, 4),
+                "gpu_event_ms": round(gpu_ms, 3)},
+        "roofline": {"kernel": "k_gemv_stream (RMSNorm + FFN gate/up W4 GEMV + SwiGLU), K=5120, 34816 rows",
+                     "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                     "avg_launch_us": round(us, 3), "bytes_per_launch": nbytes, "other_kernels": others},
+        "setup_s": {"load": round(t_load, 1), "prompt": round(t_prompt, 1)},
+        "first_tokens": [int(t) for t in toks[:8]],
+    }
+    m.close()
+    del m
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.ctx, args.seed)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,233 @@
+/*
+ * aw4.h - C ABI of the MI355X (gfx950) batch-1 decode library for a hybrid
+ * Gated DeltaNet / gated-attention language model with 4-bit weights.
+ *
+ * What the library computes (readings of the pages are listed in the design doc):
+ *  - Decode is bandwidth-bound: every token streams all weights from memory
+ *    (page 5, bs178.com llamAmpere article, "为什么它真能这么快" point 二;
+ *    page 3 "Qwen3.8-27B 實測", section "部署前必知").
+ *  - The stack interleaves Gated DeltaNet recurrent layers with full-attention
+ *    layers, 48 + 16 in the 27B model (page 3, "部署前必知"; page 5 point 一).
+ *  - Weights are 4-bit (W4A16: 4-bit weights, 16-bit activations; page 4,
+ *    jdon.com, section on quantisation schools; page 1, the "27B x 4 bit"
+ *    estimate), here symmetric codes in groups of 32 with an fp16 scale; the
+ *    output head is int8 and doubles as the embedding table.
+ *  - The KV cache stores keys at 8 bits and values rotated and compressed to
+ *    about 3 bits (page 5, point 三): keys int8 per 32 with an fp16 scale, values
+ *    multiplied by a random-sign Walsh-Hadamard matrix then 3-bit per 32.
+ *  - verify_k checks draft tokens with acceptance probability min(1, p/q) and
+ *    residual resampling (page 5, point 四).
+ *
+ * Conventions for every entry point:
+ *  - Returns AW4_OK (0) or a negative AW4_E_* code; no exception crosses the
+ *    ABI.  aw4_last_error() gives a message for the last failure on a model.
+ *  - "dev_" pointers are device (HIP) addresses, "host_" pointers are host
+ *    memory.  The library never frees caller memory.
+ *  - One model is bound to one device and one HIP stream; calls on one model
+ *    must not overlap (not thread-safe).  Host buffers are read or written only
+ *    during the call.
+ *  - Entry points that only enqueue work return before it finishes; those that
+ *    return data on the host synchronise the stream first.
+ */
+#ifndef AW4_H
+#define AW4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define AW4_OK 0
+#define AW4_E_INVAL (-1)       /* bad argument or unsupported shape */
+#define AW4_E_ARENA (-2)       /* arena missing, misaligned or too small */
+#define AW4_E_NODEVICE (-3)    /* no HIP device / not gfx950 */
+#define AW4_E_HIP (-4)         /* a HIP runtime call failed */
+#define AW4_E_FORMAT (-5)      /* weight blob: bad magic, version, size or config echo */
+#define AW4_E_CTX_FULL (-6)    /* position would exceed max_ctx */
+#define AW4_E_TOKEN (-7)       /* token id outside [0, vocab) */
+#define AW4_E_STATE (-8)       /* call not valid in the model's current state */
+
+/* Model shape.  Requirements (else AW4_E_INVAL): hidden, ffn multiples of 64;
+ * group == 32; n_layers in [1, 128], layer_pattern holds n_layers letters
+ * 'G' (Gated DeltaNet) or 'A' (gated attention); GDN: gdn_head_dim in {64, 128},
+ * gdn_v_heads a multiple of gdn_qk_heads; attention: attn_head_dim in {64, 256},
+ * attn_q_heads a multiple of attn_kv_heads, attn_q_heads/attn_kv_heads <= 8;
+ * vocab >= 0 (0: no embedding or output head, only aw4_decode_hidden works);
+ * max_ctx >= 1; max_verify in [1, 4]; rms_eps > 0. */
+typedef struct aw4_config {
+    int32_t hidden;
+    int32_t ffn;
+    int32_t vocab;
+    int32_t n_layers;
+    int32_t gdn_qk_heads;
+    int32_t gdn_v_heads;
+    int32_t gdn_head_dim;
+    int32_t attn_q_heads;
+    int32_t attn_kv_heads;
+    int32_t attn_head_dim;
+    int32_t group;
+    int32_t max_ctx;
+    int32_t max_verify;
+    float rms_eps;
+    char layer_pattern[128];
+} aw4_config;
+
+typedef struct aw4_model aw4_model;
+
+/* Tensor kinds.  Per-layer W4 matrices [rows x cols], y = W x:
+ *   MIX_IN   GDN: rows [q | k | v | z | a | b] = 2*nqk*d + 2*nv*d + 2*nv;
+ *            attention: rows [q | g | k | v] = 2*nq*dh + 2*nkv*dh; cols hidden.
+ *   MIX_OUT  [hidden x nv*d] (GDN) or [hidden x nq*dh] (attention).
+ *   FFN_GATE, FFN_UP [ffn x hidden]; FFN_DOWN [hidden x ffn].
+ * Global: LM_HEAD int8 [vocab x hidden] (also the embedding table).
+ * Vectors (fp32): NORM_MIX, NORM_FFN [hidden]; NORM_GATED [gdn_head_dim];
+ * A_BIAS [gdn_v_heads]; NORM_FINAL [hidden]; RHT_SIGNS [attn_head_dim] (+1/-1). */
+enum {
+    AW4_T_MIX_IN = 0,
+    AW4_T_MIX_OUT = 1,
+    AW4_T_FFN_GATE = 2,
+    AW4_T_FFN_UP = 3,
+    AW4_T_FFN_DOWN = 4,
+    AW4_T_LM_HEAD = 5,
+    AW4_T_NORM_MIX = 6,
+    AW4_T_NORM_FFN = 7,
+    AW4_T_NORM_GATED = 8,
+    AW4_T_A_BIAS = 9,
+    AW4_T_NORM_FINAL = 10,
+    AW4_T_RHT_SIGNS = 11
+};
+
+/* ----------------------------------------------------------- lifetime */
+
+/* Pure host check of a config; enqueues nothing. */
+int aw4_validate_config(const aw4_config* cfg);
+
+/* Bytes of device memory the model needs (weights, caches, states, scratch),
+ * written to *out_bytes.  Pure host computation. */
+int aw4_workspace_bytes(const aw4_config* cfg, uint64_t* out_bytes);
+
+/* Bind a model to a caller-owned device arena of at least
+ * aw4_workspace_bytes() bytes, 256-byte aligned, on the current HIP device,
+ * and to hip_stream (a hipStream_t; NULL = the null stream).  The arena stays
+ * owned by the caller and must outlive the model.  The library allocates no
+ * device memory.  Zeroes states and caches (enqueued on the stream).
+ * Errors: AW4_E_INVAL, AW4_E_ARENA, AW4_E_NODEVICE, AW4_E_HIP. */
+int aw4_create(const aw4_config* cfg, void* dev_arena, uint64_t arena_bytes, void* hip_stream,
+               aw4_model** out_model);
+
+/* Release host-side resources (captured graphs included).  NULL is a no-op. */
+void aw4_destroy(aw4_model* model);
+
+const char* aw4_status_string(int status);
+const char* aw4_last_error(const aw4_model* model);
+
+/* ----------------------------------------------------------- weights */
+
+/* Shape of a tensor kind (layer -1 for the global ones). */
+int aw4_tensor_shape(const aw4_model* model, int32_t layer, int32_t kind, int64_t* rows, int64_t* cols);
+
+/* Quantise fp32 rows [row0, row0+nrows) of a matrix (kinds 0..5) held at
+ * dev_src ([nrows x cols], row-major, device) into the model with the group
+ * codec: per 32 consecutive inputs of a row s = fp16(amax / qmax) (qmax 7 for
+ * W4, 127 for LM_HEAD, quotient in fp32, round to nearest even), codes
+ * clamp(rint(w / s), -qmax, qmax), 0 where s == 0.  Enqueued on the stream. */
+int aw4_quantize_tensor(aw4_model* model, int32_t layer, int32_t kind, int64_t row0, int64_t nrows,
+                        const float* dev_src);
+
+/* Load an already-quantised matrix from host memory in the logical format:
+ * W4: codes uint8 [rows][cols/2], element k in the low nibble of byte k/2 when
+ * k is even and the high nibble when odd, nibble = code + 8; LM_HEAD: codes
+ * int8 [rows][cols]; scales fp16 bits [rows][cols/32].  Synchronous. */
+int aw4_load_tensor(aw4_model* model, int32_t layer, int32_t kind, const void* host_codes,
+                    const uint16_t* host_scales);
+
+/* Read a matrix back in the logical format above (test and export use).
+ * Synchronous. */
+int aw4_export_tensor(aw4_model* model, int32_t layer, int32_t kind, void* host_codes, uint16_t* host_scales);
+
+/* Set a vector kind (6..11) from n host floats.  Synchronous. */
+int aw4_set_vector(aw4_model* model, int32_t layer, int32_t kind, const float* host_vals, int32_t n);
+
+/* Load every tensor from one host blob: "AW4W" magic, uint32 version 1, the
+ * aw4_config it was made for, uint32 tensor count, then per tensor
+ * {int32 layer, int32 kind, int64 rows, int64 cols, uint64 bytes} followed by
+ * the payload (logical codes then scales, or n fp32 values for vectors).
+ * Errors: AW4_E_FORMAT on magic, version, size or config mismatch. */
+int aw4_load_weights(aw4_model* model, const void* host_blob, uint64_t bytes);
+
+/* ----------------------------------------------------------- decode */
+
+/* Clear recurrent states and caches; position 0.  Enqueued. */
+int aw4_reset(aw4_model* model);
+
+/* Append n prompt tokens (positions pos..pos+n-1) through every layer.  If
+ * dev_logits is not NULL it receives the fp32 logits [vocab] after the last
+ * token.  Errors: AW4_E_CTX_FULL, AW4_E_TOKEN, AW4_E_STATE (vocab 0). */
+int aw4_prefill(aw4_model* model, const int32_t* host_tokens, int32_t n, float* dev_logits);
+
+/* One decode step on `token` at the current position: embed, all layers
+ * (appending this position to the caches), final norm, output head, argmax
+ * (lowest index on ties).  dev_logits (optional) receives fp32 [vocab];
+ * host_argmax (optional) receives the argmax after a stream sync; without it
+ * the call only enqueues. */
+int aw4_decode_step(aw4_model* model, int32_t token, float* dev_logits, int32_t* host_argmax);
+
+/* n greedy steps starting from first_token; each step's argmax feeds the next
+ * on the device.  host_tokens_out receives the n generated tokens (one sync at
+ * the end).  This is the measured decode loop. */
+int aw4_decode_greedy(aw4_model* model, int32_t first_token, int32_t n_steps, int32_t* host_tokens_out);
+
+/* Layers only, at the current position: dev_x_out = stack(dev_x_in), both
+ * fp32 [hidden] device vectors (may alias).  For models without a vocabulary
+ * (single-layer workloads) and for hidden-state checks.  Enqueued. */
+int aw4_decode_hidden(aw4_model* model, const float* dev_x_in, float* dev_x_out);
+
+/* Copy the residual vector after the last step's layers (fp32 [hidden]) to the
+ * host.  Synchronous. */
+int aw4_read_hidden(aw4_model* model, float* host_x);
+
+/* Use (1) or not (0) a captured HIP graph for the per-token launch sequence
+ * of decode_step / decode_greedy (default 1). */
+int aw4_set_graph(aw4_model* model, int32_t enable);
+
+/* Kernel timing for roofline reports.  Launches one phase of the step `reps`
+ * times, cycling through the layers so that consecutive launches stream
+ * different weights, between two HIP events on the model's stream, and
+ * returns the average launch-to-launch duration (microseconds) and the
+ * algorithmic bytes one launch moves (weights + scales + activations read and
+ * written).  Synchronous.  Leaves activations scratch overwritten. */
+enum {
+    AW4_PHASE_FFN_GATE_UP = 0,   /* RMSNorm + gate/up W4 GEMV + SwiGLU  */
+    AW4_PHASE_FFN_DOWN = 1,      /* down W4 GEMV + residual add          */
+    AW4_PHASE_MIX_IN = 2         /* RMSNorm + mixer input W4 GEMV         */
+};
+int aw4_time_phase(aw4_model* model, int32_t phase, int32_t reps, float* avg_us, uint64_t* bytes_per_launch);
+
+/* ----------------------------------------------------------- state */
+
+int aw4_get_pos(aw4_model* model, int32_t* pos);
+
+/* Set the position without touching the caches (state import). */
+int aw4_set_pos(aw4_model* model, int32_t pos);
+
+/* GDN recurrent state of one 'G' layer, fp32 [v_heads][head_dim][head_dim]
+ * (row i of a head's matrix maps keys to value dim i).  Synchronous. */
+int aw4_export_state_gdn(aw4_model* model, int32_t layer, float* host_S);
+int aw4_import_state_gdn(aw4_model* model, int32_t layer, const float* host_S);
+
+/* Cache of one 'A' layer, positions [0, npos), logical layout: K codes int8
+ * [npos][kv_heads][head_dim], K scales fp16 [npos][kv_heads][head_dim/32],
+ * V codes int8 in -3..3 (rotated domain) [npos][kv_heads][head_dim], V scales
+ * fp16 [npos][kv_heads][head_dim/32].  Synchronous. */
+int aw4_export_state_kv(aw4_model* model, int32_t layer, int32_t npos, int8_t* host_kc, uint16_t* host_ks,
+                        int8_t* host_vc, uint16_t* host_vs);
+int aw4_import_state_kv(aw4_model* model, int32_t layer, int32_t npos, const int8_t* host_kc,
+                        const uint16_t* host_ks, const int8_t* host_vc, const uint16_t* host_vs);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AW4_H */

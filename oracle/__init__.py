@@ -71,6 +71,7 @@ def lib():
             "or_decode_token": ([_vp, _i32, _vp, _vp, _vp], ctypes.c_int),
             "or_get_pos": ([_vp], _i32),
             "or_set_pos": ([_vp, _i32], ctypes.c_int),
+            "or_get_last_kv": ([_vp, ctypes.c_int, _vp, _vp], ctypes.c_int),
             "or_set_state_gdn": ([_vp, ctypes.c_int, _vp], ctypes.c_int),
             "or_get_state_gdn": ([_vp, ctypes.c_int, _vp], ctypes.c_int),
             "or_set_state_kv": ([_vp, ctypes.c_int, _i32, _vp, _vp, _vp, _vp], ctypes.c_int),
@@ -196,8 +197,8 @@ class Model:
             raise MemoryError("oracle allocation failed")
 
     def __del__(self):
-        if getattr(self, "h", None):
-            lib().or_destroy(self.h)
+        if getattr(self, "h", None) and _lib is not None:
+            _lib.or_destroy(self.h)
             self.h = None
 
     def _rc(self, rc, what):
@@ -280,6 +281,14 @@ class Model:
         npos = kc.shape[0]
         arrs = [np.ascontiguousarray(a) for a in (kc, ks, vc, vs)]
         self._rc(lib().or_set_state_kv(self.h, layer, npos, *[_p(a) for a in arrs]), "set_kv")
+
+    def last_kv(self, layer):
+        """fp32 keys and rotated values [nkv][dh] the last append quantised"""
+        s = self.shape
+        k = np.zeros((s.attn_kv_heads, s.attn_head_dim), np.float32)
+        v = np.zeros_like(k)
+        self._rc(lib().or_get_last_kv(self.h, layer, _p(k), _p(v)), "last_kv")
+        return k, v
 
     def get_kv(self, layer, npos):
         s = self.shape

@@ -161,6 +161,8 @@ typedef struct {
     uint16_t* ks;           /* A: [max_ctx][nkv][dh/32] */
     int8_t* vc;             /* A: rotated-domain codes in -3..3 */
     uint16_t* vs;
+    float* klast;           /* A: fp32 keys of the last appended position [nkv][dh] */
+    float* vlast;           /* A: fp32 rotated values of the last appended position */
 } or_layer;
 
 typedef struct {
@@ -222,6 +224,8 @@ or_model* or_create(const or_cfg* cfg) {
             L->vc = (int8_t*)zalloc(n);
             L->ks = (uint16_t*)zalloc(n / 32 * 2);
             L->vs = (uint16_t*)zalloc(n / 32 * 2);
+            L->klast = (float*)zalloc(sizeof(float) * c->attn_kv_heads * c->attn_head_dim);
+            L->vlast = (float*)zalloc(sizeof(float) * c->attn_kv_heads * c->attn_head_dim);
         }
     }
     if (c->vocab > 0) {
@@ -241,7 +245,7 @@ void or_destroy(or_model* m) {
         or_layer* L = &m->L[l];
         for (int i = 0; i < 5; ++i) { free(L->w[i].codes); free(L->w[i].scales); }
         free(L->norm_mix); free(L->norm_ffn); free(L->norm_gated); free(L->a_bias); free(L->S);
-        free(L->kc); free(L->ks); free(L->vc); free(L->vs);
+        free(L->kc); free(L->ks); free(L->vc); free(L->vs); free(L->klast); free(L->vlast);
     }
     free(m->L);
     free(m->lm.codes); free(m->lm.scales); free(m->norm_final); free(m->signs);
@@ -461,6 +465,15 @@ void or_kv_encode(const double* k, const double* v, const int8_t* signs, int d, 
     free(vr);
 }
 
+/* the fp32 key and rotated value the last append quantised (for tie checks) */
+static void kv_record(const double* k, const double* v, const int8_t* signs, int d, float* kl, float* vl) {
+    double* vr = (double*)malloc(sizeof(double) * d);
+    for (int i = 0; i < d; ++i) kl[i] = (float)k[i];
+    or_rht_forward(v, signs, d, vr);
+    for (int i = 0; i < d; ++i) vl[i] = (float)vr[i];
+    free(vr);
+}
+
 /* gated attention: append the current token, attend over positions 0..pos,
  * gate each head output by sigmoid(g), project back */
 static void attn_mixer(or_model* m, or_layer* L, const double* xh, double* delta) {
@@ -478,6 +491,8 @@ static void attn_mixer(or_model* m, or_layer* L, const double* xh, double* delta
         int64_t base = (t * nkv + j) * d;
         or_kv_encode(k + (int64_t)j * d, v + (int64_t)j * d, m->signs, d, L->kc + base, L->ks + base / 32,
                      L->vc + base, L->vs + base / 32);
+        kv_record(k + (int64_t)j * d, v + (int64_t)j * d, m->signs, d, L->klast + (int64_t)j * d,
+                  L->vlast + (int64_t)j * d);
     }
     double* o = (double*)malloc(sizeof(double) * nq * d);
     int ratio = nq / nkv;
@@ -609,6 +624,14 @@ int or_get_state_kv(const or_model* m, int layer, int32_t npos, int8_t* kc, uint
     memcpy(vc, L->vc, n);
     memcpy(ks, L->ks, n / 32 * 2);
     memcpy(vs, L->vs, n / 32 * 2);
+    return 0;
+}
+
+int or_get_last_kv(const or_model* m, int layer, float* k, float* vrot) {
+    if (layer < 0 || layer >= m->c.n_layers || m->L[layer].type != 'A') return -1;
+    int64_t n = (int64_t)m->c.attn_kv_heads * m->c.attn_head_dim;
+    memcpy(k, m->L[layer].klast, sizeof(float) * n);
+    memcpy(vrot, m->L[layer].vlast, sizeof(float) * n);
     return 0;
 }
 

@@ -69,6 +69,7 @@ def dev():
     if _dev is None:
         if not os.path.exists(DEV_SO):
             raise RuntimeError(f"{DEV_SO} missing: run __graft_entry__.build()")
+        import torch  # noqa: F401  (one HIP runtime: torch's, see attention_w4_amd.lib)
         L = ctypes.CDLL(DEV_SO)
         for n, a in [("aw4s_dev_normal_f32", [_vp, _i64, _i64, _i64, _f32, _u64, _u32, _vp]),
                      ("aw4s_dev_codes_i8", [_vp, _i64, _i64, _i32, _i32, _u64, _u32, _vp]),

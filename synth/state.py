@@ -1,0 +1,53 @@
+"""Synthetic decode state (recurrent states and compressed KV cache), seeded.
+
+Used where a long context has to exist without prefilling it token by token
+(8K-262K positions): both the oracle and the GPU model import the same arrays.
+Codes and scales are drawn directly (discretised normals, fp16 bit patterns),
+so no quantiser is involved.  Magnitudes mimic what the decode step writes:
+keys ~ N(0, 1.4^2) stored as int8 codes x 0.035, rotated values ~ 1.4 in
+3-bit codes x ~1, recurrent state entries ~ N(0, 0.1^2).
+"""
+import numpy as np
+
+from . import codes, normal, scale_bits
+from .workloads import STREAM_STATE
+
+K_SPREAD256 = 40 * 256          # code std ~ 40 (keys of std 1.4 at scale 0.035)
+V_SPREAD256 = 358               # code std ~ 1.4
+K_SCALE_BITS = 0x287B           # fp16 0.0350
+V_SCALE_BITS = 0x3C00           # fp16 1.0
+S_STD = 0.1
+
+
+def _stream(layer, part):
+    return STREAM_STATE + layer * 8 + part
+
+
+def gdn_state(shape, layer, seed):
+    n = shape.gdn_v_heads * shape.gdn_head_dim
+    return normal(n, shape.gdn_head_dim, S_STD, seed, _stream(layer, 0)).reshape(
+        shape.gdn_v_heads, shape.gdn_head_dim, shape.gdn_head_dim)
+
+
+def kv_state(shape, layer, npos, seed):
+    d, nkv = shape.attn_head_dim, shape.attn_kv_heads
+    n = npos * nkv * d
+    kc = codes(n, K_SPREAD256, 127, seed, _stream(layer, 1)).reshape(npos, nkv, d)
+    vc = codes(n, V_SPREAD256, 3, seed, _stream(layer, 2)).reshape(npos, nkv, d)
+    ks = scale_bits(n // 32, K_SCALE_BITS, seed, _stream(layer, 3)).reshape(npos, nkv, d // 32)
+    vs = scale_bits(n // 32, V_SCALE_BITS, seed, _stream(layer, 4)).reshape(npos, nkv, d // 32)
+    return kc, ks, vc, vs
+
+
+def fill(model, shape, npos, seed, gdn=True):
+    """Import a synthetic state of npos positions into a model exposing
+    import_gdn / import_kv / set_pos (the GPU binding) or set_gdn_state /
+    set_kv / set_pos (the oracle)."""
+    for l, t in enumerate(shape.pattern):
+        if t == "G" and gdn:
+            S = gdn_state(shape, l, seed)
+            (model.import_gdn if hasattr(model, "import_gdn") else model.set_gdn_state)(l, S)
+        elif t == "A":
+            kv = kv_state(shape, l, npos, seed)
+            (model.import_kv if hasattr(model, "import_kv") else model.set_kv)(l, *kv)
+    model.set_pos(npos)

@@ -6,8 +6,8 @@ import synth
 from synth import workloads as W
 
 # a tiny hybrid with grouped heads on both mixer types, for brute-force pins
-TINY = W.Shape(hidden=64, ffn=96, vocab=128, pattern="GAGA", gdn_qk_heads=2, gdn_v_heads=4,
-               gdn_head_dim=32, attn_q_heads=4, attn_kv_heads=2, attn_head_dim=64, max_ctx=64)
+TINY = W.Shape(hidden=128, ffn=192, vocab=160, pattern="GAGA", gdn_qk_heads=2, gdn_v_heads=4,
+               gdn_head_dim=64, attn_q_heads=4, attn_kv_heads=2, attn_head_dim=64, max_ctx=64)
 
 
 def logical_weights(shape, seed, norm_jitter=0.0):
