@@ -266,7 +266,7 @@ struct Prologue<K, PRO_LOADH> {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int idx = threadIdx.x + 256 * i;
-            if (N8 % 256 == 0 || idx < N8) v[i] = src[idx];
+            v[i] = src[idx < N8 ? idx : N8 - 1];   // clamped: straight-line loads, stores guarded
         }
     }
     __device__ __forceinline__ void finish(const GemvArgs&, _Float16* xs, float*) {
@@ -308,7 +308,7 @@ __device__ __forceinline__ void load_block(RowBlock<R, NF>& b, const uint32_t* _
 }
 
 template <int R, int NF, int PRO, int EPI>
-__global__ __launch_bounds__(256, 3) void k_gemv_stream(GemvArgs a) {
+__global__ __launch_bounds__(256, 2) void k_gemv_stream(GemvArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     float* red = (float*)smem;
     _Float16* xs = (_Float16*)(smem + 64);
@@ -335,6 +335,15 @@ __global__ __launch_bounds__(256, 3) void k_gemv_stream(GemvArgs a) {
         grp_of[i] = f % G;
     }
     const uint4* xv = (const uint4*)xs;   // group g: xv[4g .. 4g+3]
+    // short rows: this lane's slices of the input stay in registers for every
+    // row block (the lane -> group map is the same for all of them)
+    uint4 xr[kPipe ? NF : 1][4];
+    if (kPipe) {
+#pragma unroll
+        for (int i = 0; i < NF; ++i)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) xr[kPipe ? i : 0][k] = xv[4 * grp_of[i] + k];
+    }
     for (; rb < nrb; rb += nw) {
         const bool more = rb + nw < nrb;
         if (kPipe && more) load_block<R, NF>(nxt, a.codes, a.scales, rb + nw, G, lane);
@@ -343,8 +352,14 @@ __global__ __launch_bounds__(256, 3) void k_gemv_stream(GemvArgs a) {
         for (int r = 0; r < R; ++r) acc[r] = 0.f;
 #pragma unroll
         for (int i = 0; i < NF; ++i) {
-            const int g = grp_of[i];
-            const uint4 x0 = xv[4 * g], x1 = xv[4 * g + 1], x2 = xv[4 * g + 2], x3 = xv[4 * g + 3];
+            uint4 x0, x1, x2, x3;
+            if (kPipe) {
+                x0 = xr[kPipe ? i : 0][0]; x1 = xr[kPipe ? i : 0][1];
+                x2 = xr[kPipe ? i : 0][2]; x3 = xr[kPipe ? i : 0][3];
+            } else {
+                const int g = grp_of[i];
+                x0 = xv[4 * g]; x1 = xv[4 * g + 1]; x2 = xv[4 * g + 2]; x3 = xv[4 * g + 3];
+            }
             float ea = 0.f, eb = 0.f;
             dq_dot8(cur.c[i][0], x0, ea, eb);
             dq_dot8(cur.c[i][1], x1, ea, eb);
@@ -353,9 +368,9 @@ __global__ __launch_bounds__(256, 3) void k_gemv_stream(GemvArgs a) {
             const float part = half_bits_to_float(cur.s[i]) * (ea + 0.0625f * eb);
 #pragma unroll
             for (int r = 0; r < R; ++r) acc[r] += row_of[i] == r ? part : 0.f;
-            // long rows: keep the compiler from hoisting every group's LDS reads
-            // (16 registers each) above the first dot products
-            if (!kPipe) asm volatile("" ::: "memory");
+            // long rows: split the group loop in two so that the compiler hoists
+            // at most half of the LDS reads (16 registers per group)
+            if (!kPipe && i == NF / 2) asm volatile("" ::: "memory");
         }
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[r] = wave_sum_fast(acc[r]);
