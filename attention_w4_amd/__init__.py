@@ -64,6 +64,7 @@ _SIGS = {
     "aw4_decode_step": [_vp, _i32, _vp, _vp],
     "aw4_decode_greedy": [_vp, _i32, _i32, _vp],
     "aw4_decode_hidden": [_vp, _vp, _vp],
+    "aw4_verify_k": [_vp, _vp, _i32, _vp, _vp, _f32, _vp, _vp],
     "aw4_read_hidden": [_vp, _vp],
     "aw4_set_graph": [_vp, _i32],
     "aw4_get_pos": [_vp, ctypes.POINTER(_i32)],
@@ -228,6 +229,20 @@ class Model:
         out = np.zeros(max(n, 1), np.int32)
         self._rc(lib().aw4_decode_greedy(self.h, int(first_token), n, _ptr(out)), "decode_greedy")
         return out[:n]
+
+    def verify_k(self, tokens, q=None, u=None, temperature=0.0):
+        """tokens: [t0, d1..dk]; q: device fp32 tensor [k, V] (sampling); u: k+1 uniforms.
+        Returns the emitted tokens (accepted drafts + the drawn token)."""
+        import numpy as np
+        t = np.ascontiguousarray(tokens, np.int32)
+        k = len(t) - 1
+        uu = np.ascontiguousarray(u, np.float32) if u is not None else None
+        out = np.zeros(4, np.int32)
+        n = _i32()
+        self._rc(lib().aw4_verify_k(self.h, _ptr(t), k, q.data_ptr() if q is not None else None,
+                                    _ptr(uu) if uu is not None else None, float(temperature), _ptr(out),
+                                    ctypes.byref(n)), "verify_k")
+        return [int(v) for v in out[:n.value]]
 
     def decode_hidden(self, x_in, x_out):
         self._rc(lib().aw4_decode_hidden(self.h, x_in.data_ptr(), x_out.data_ptr()), "decode_hidden")

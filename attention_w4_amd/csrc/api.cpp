@@ -75,6 +75,19 @@ struct aw4_model {
     int32_t* pi = nullptr;
     int32_t* ring = nullptr;
     int ring_cap = 0;
+    // draft verification (M = k + 1 tokens)
+    float* vx = nullptr;            // [max_verify][H] residuals
+    std::vector<float*> vproj_g;    // per GDN layer [max_verify][in_rows] (kept for the replay)
+    float* vproj_a = nullptr;       // [max_verify][attn in_rows]
+    float* vo = nullptr;            // [max_verify][nv*d]
+    _Float16* vh = nullptr;         // [max_verify][hlen]
+    _Float16* va = nullptr;         // [max_verify][nq*dh]
+    float* vlogits = nullptr;       // [max_verify][V]
+    float* vpv = nullptr;           // [max_verify][nhb]
+    int32_t* vpi = nullptr;
+    float* vzpart = nullptr;        // [max_verify][accept blocks]
+    float* vwpart = nullptr;
+    int64_t hlen = 0;
     int nhead_blocks = 0;
     int nsplit = 1;
     int32_t host_pos = 0;
@@ -182,6 +195,7 @@ uint64_t plan_layout(const aw4_config* c, aw4_model* m, uint8_t* base) {
     float* proj = p.take<float>((uint64_t)max_in * 4);
     float* obuf = p.take<float>((uint64_t)(has_g ? c->gdn_v_heads * c->gdn_head_dim : 1) * 4);
     const int64_t hlen = F > (int64_t)c->attn_q_heads * c->attn_head_dim ? F : (int64_t)c->attn_q_heads * c->attn_head_dim;
+    // (hlen also sizes the per-token FFN buffers of the verify pass)
     _Float16* hbuf = p.take<_Float16>((uint64_t)hlen * 2);
     _Float16* abuf = p.take<_Float16>((uint64_t)(has_a ? c->attn_q_heads * c->attn_head_dim : 1) * 2);
     const int nsplit = nsplit_for(c->max_ctx);
@@ -197,8 +211,39 @@ uint64_t plan_layout(const aw4_config* c, aw4_model* m, uint8_t* base) {
         pi = p.take<int32_t>((uint64_t)nhb * 4);
     }
     int32_t* ring = p.take<int32_t>((uint64_t)kRingCap * 4);
+    const int MV = c->max_verify;
+    float* vx = p.take<float>((uint64_t)MV * H * 4);
+    std::vector<float*> vproj_g;
+    float* vproj_a = nullptr;
+    for (int l = 0; l < c->n_layers; ++l)
+        if (L[l].type == 'G') vproj_g.push_back(p.take<float>((uint64_t)MV * L[l].in_rows * 4));
+    if (has_a) vproj_a = p.take<float>((uint64_t)MV * mix_in_rows(c, 'A') * 4);
+    float* vo = p.take<float>((uint64_t)MV * (has_g ? c->gdn_v_heads * c->gdn_head_dim : 1) * 4);
+    _Float16* vh = p.take<_Float16>((uint64_t)MV * hlen * 2);
+    _Float16* va = p.take<_Float16>((uint64_t)MV * (has_a ? c->attn_q_heads * c->attn_head_dim : 1) * 2);
+    float *vlogits = nullptr, *vpv = nullptr, *vzpart = nullptr, *vwpart = nullptr;
+    int32_t* vpi = nullptr;
+    if (c->vocab > 0) {
+        vlogits = p.take<float>((uint64_t)MV * c->vocab * 4);
+        vpv = p.take<float>((uint64_t)MV * nhb * 4);
+        vpi = p.take<int32_t>((uint64_t)MV * nhb * 4);
+        vzpart = p.take<float>((uint64_t)MV * accept_blocks(c->vocab) * 4);
+        vwpart = p.take<float>((uint64_t)MV * accept_blocks(c->vocab) * 4);
+    }
     p.off = (p.off + 255) & ~uint64_t(255);
     if (m) {
+        m->vx = vx;
+        m->vproj_g = vproj_g;
+        m->vproj_a = vproj_a;
+        m->vo = vo;
+        m->vh = vh;
+        m->va = va;
+        m->vlogits = vlogits;
+        m->vpv = vpv;
+        m->vpi = vpi;
+        m->vzpart = vzpart;
+        m->vwpart = vwpart;
+        m->hlen = hlen;
         m->L = L;
         m->lm_codes = lm_codes;
         m->lm_scales = lm_scales;
@@ -359,7 +404,7 @@ int enqueue_layers(aw4_model* m) {
             aa.d = c->attn_head_dim;
             aa.nsplit = m->nsplit;
             HIPCHK(m, launch_attn(aa, s));
-            CombineArgs ca{m->part, m->proj, m->signs, m->ctl, m->abuf, c->attn_q_heads, c->attn_kv_heads,
+            CombineArgs ca{0, m->part, m->proj, m->signs, m->ctl, m->abuf, c->attn_q_heads, c->attn_kv_heads,
                            c->attn_head_dim, m->nsplit};
             HIPCHK(m, launch_combine(ca, s));
             GemvArgs go{};
@@ -423,6 +468,87 @@ int enqueue_phase(aw4_model* m, int phase, int l, uint64_t* bytes) {
         default:
             return fail(m, AW4_E_INVAL, "unknown phase");
     }
+    return AW4_OK;
+}
+
+// The verify pass: M tokens (ctl->vtok) at positions pos .. pos+M-1 through
+// every layer with one sweep over the weights, the head over the M residuals,
+// acceptance, then the commit (GDN replay of the accepted prefix, pos advance).
+int enqueue_verify(aw4_model* m, int M, int k, const float* dev_q, float temperature) {
+    const aw4_config* c = &m->cfg;
+    hipStream_t s = m->stream;
+    const int H = c->hidden, F = c->ffn;
+    HIPCHK(m, launch_embed_multi(m->lm_codes, m->lm_scales, H, m->ctl, M, m->vx, s));
+    int gi_layer = 0;
+    for (int l = 0; l < c->n_layers; ++l) {
+        LayerBufs& b = m->L[l];
+        float* proj = b.type == 'G' ? m->vproj_g[gi_layer] : m->vproj_a;
+        GemvMultiArgs gi{};
+        gi.codes = b.w_in; gi.scales = b.s_in; gi.rows = (int)b.in_rows; gi.K = H; gi.M = M;
+        gi.x = m->vx; gi.sx = H; gi.nw = b.norm_mix; gi.eps = c->rms_eps; gi.y = proj; gi.sy = b.in_rows;
+        HIPCHK(m, launch_gemv_multi(PRO_NORM, EPI_STORE, gi, s));
+        if (b.type == 'G') {
+            GdnMultiArgs ga{};
+            ga.proj = proj; ga.sproj = b.in_rows; ga.a_bias = b.a_bias; ga.S = b.S; ga.o = m->vo;
+            ga.so = (int64_t)c->gdn_v_heads * c->gdn_head_dim; ga.nqk = c->gdn_qk_heads; ga.nv = c->gdn_v_heads;
+            ga.d = c->gdn_head_dim; ga.M = M; ga.eps = c->rms_eps; ga.replay = 0; ga.commit_n = nullptr;
+            HIPCHK(m, launch_gdn_multi(ga, s));
+            GemvMultiArgs go{};
+            go.codes = b.w_out; go.scales = b.s_out; go.rows = H; go.K = (int)b.out_cols; go.M = M;
+            go.x = m->vo; go.sx = ga.so; go.nw = b.norm_gated;
+            go.z = proj + 2LL * c->gdn_qk_heads * c->gdn_head_dim + (int64_t)c->gdn_v_heads * c->gdn_head_dim;
+            go.sz = b.in_rows; go.gated_d = c->gdn_head_dim; go.eps = c->rms_eps; go.y = m->vx; go.sy = H;
+            HIPCHK(m, launch_gemv_multi(PRO_GATED, EPI_RESID, go, s));
+            ++gi_layer;
+        } else {
+            const int64_t od = (int64_t)c->attn_q_heads * c->attn_head_dim;
+            for (int t = 0; t < M; ++t) {
+                AttnArgs aa{};
+                aa.pos_offset = t;
+                aa.proj = proj + (int64_t)t * b.in_rows;
+                aa.kc = b.kc; aa.ks = b.ks; aa.vc = b.vc; aa.vs = b.vs;
+                aa.signs = m->signs; aa.ctl = m->ctl; aa.part = m->part;
+                aa.max_ctx = c->max_ctx; aa.nq = c->attn_q_heads; aa.nkv = c->attn_kv_heads;
+                aa.d = c->attn_head_dim; aa.nsplit = m->nsplit;
+                HIPCHK(m, launch_attn(aa, s));
+                CombineArgs ca{t, m->part, aa.proj, m->signs, m->ctl, m->va + t * od, c->attn_q_heads,
+                               c->attn_kv_heads, c->attn_head_dim, m->nsplit};
+                HIPCHK(m, launch_combine(ca, s));
+            }
+            GemvMultiArgs go{};
+            go.codes = b.w_out; go.scales = b.s_out; go.rows = H; go.K = (int)b.out_cols; go.M = M;
+            go.h = m->va; go.sh = od; go.y = m->vx; go.sy = H;
+            HIPCHK(m, launch_gemv_multi(PRO_LOADH, EPI_RESID, go, s));
+        }
+        GemvMultiArgs gf{};
+        gf.codes = b.w_gu; gf.scales = b.s_gu; gf.rows = 2 * F; gf.K = H; gf.M = M;
+        gf.x = m->vx; gf.sx = H; gf.nw = b.norm_ffn; gf.eps = c->rms_eps; gf.hout = m->vh; gf.so = m->hlen;
+        HIPCHK(m, launch_gemv_multi(PRO_NORM, EPI_SWIGLU, gf, s));
+        GemvMultiArgs gd{};
+        gd.codes = b.w_down; gd.scales = b.s_down; gd.rows = H; gd.K = F; gd.M = M;
+        gd.h = m->vh; gd.sh = m->hlen; gd.y = m->vx; gd.sy = H;
+        HIPCHK(m, launch_gemv_multi(PRO_LOADH, EPI_RESID, gd, s));
+    }
+    HeadMultiArgs ha{m->lm_codes, m->lm_scales, c->vocab, c->hidden, M, m->vx, m->norm_final, c->rms_eps,
+                     m->vlogits, m->vpv, m->vpi};
+    HIPCHK(m, launch_head_multi(ha, s));
+    AcceptArgs ac{};
+    ac.ctl = m->ctl; ac.logits = m->vlogits; ac.q = dev_q; ac.V = c->vocab; ac.k = k;
+    ac.greedy = temperature == 0.f; ac.inv_t = temperature == 0.f ? 1.f : 1.f / temperature;
+    ac.zpart = m->vzpart; ac.wpart = m->vwpart;
+    HIPCHK(m, launch_accept(ac, m->vpv, m->vpi, m->nhead_blocks, s));
+    // commit: replay the accepted prefix into the GDN states, advance the position
+    gi_layer = 0;
+    for (int l = 0; l < c->n_layers; ++l) {
+        LayerBufs& b = m->L[l];
+        if (b.type != 'G') continue;
+        GdnMultiArgs ga{};
+        ga.proj = m->vproj_g[gi_layer++]; ga.sproj = b.in_rows; ga.a_bias = b.a_bias; ga.S = b.S; ga.o = nullptr;
+        ga.so = 0; ga.nqk = c->gdn_qk_heads; ga.nv = c->gdn_v_heads; ga.d = c->gdn_head_dim; ga.M = M;
+        ga.eps = c->rms_eps; ga.replay = 1; ga.commit_n = &m->ctl->vcommit;
+        HIPCHK(m, launch_gdn_multi(ga, s));
+    }
+    HIPCHK(m, launch_commit_pos(m->ctl, s));
     return AW4_OK;
 }
 
@@ -804,6 +930,43 @@ int aw4_decode_greedy(aw4_model* m, int32_t first_token, int32_t n_steps, int32_
         done += chunk;
         tok = host_out[done - 1];
     }
+    return AW4_OK;
+}
+
+int aw4_verify_k(aw4_model* m, const int32_t* host_tokens, int32_t k, const float* dev_q, const float* host_u,
+                 float temperature, int32_t* host_out, int32_t* host_n_out) {
+    if (check_model(m) || !host_tokens || !host_out || !host_n_out) return AW4_E_INVAL;
+    const aw4_config* c = &m->cfg;
+    if (c->vocab <= 0) return fail(m, AW4_E_STATE, "verify_k needs a vocabulary");
+    if (k < 0 || k + 1 > c->max_verify) return fail(m, AW4_E_INVAL, "k must be in [0, max_verify - 1]");
+    if (!(temperature >= 0.f) || !std::isfinite(temperature)) return fail(m, AW4_E_INVAL, "temperature must be >= 0");
+    if (temperature > 0.f && (!host_u || (k > 0 && !dev_q)))
+        return fail(m, AW4_E_INVAL, "sampling needs uniforms and draft probabilities");
+    for (int i = 0; i <= k; ++i)
+        if (host_tokens[i] < 0 || host_tokens[i] >= c->vocab) return fail(m, AW4_E_TOKEN, "token out of range");
+    if (host_u)
+        for (int i = 0; i <= k; ++i)
+            if (!(host_u[i] >= 0.f && host_u[i] < 1.f)) return fail(m, AW4_E_INVAL, "uniforms must lie in [0, 1)");
+    if ((int64_t)m->host_pos + k + 1 > c->max_ctx) return fail(m, AW4_E_CTX_FULL, "context full");
+    int32_t tok[4] = {0, 0, 0, 0};
+    float u[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i <= k; ++i) {
+        tok[i] = host_tokens[i];
+        if (host_u) u[i] = host_u[i];
+    }
+    // the uniform of the final draw is u[k]
+    HIPCHK(m, launch_set_verify(m->ctl, tok, u, m->stream));
+    int rc = enqueue_verify(m, k + 1, k, dev_q, temperature);
+    if (rc) return rc;
+    int32_t res[8];
+    HIPCHK(m, hipMemcpyAsync(res, &m->ctl->vout[0], 4 * sizeof(int32_t), hipMemcpyDeviceToHost, m->stream));
+    HIPCHK(m, hipMemcpyAsync(res + 4, &m->ctl->vn_acc, 4 * sizeof(int32_t), hipMemcpyDeviceToHost, m->stream));
+    HIPCHK(m, hipStreamSynchronize(m->stream));
+    const int n_out = res[5];
+    if (n_out < 1 || n_out > k + 1) return fail(m, AW4_E_HIP, "verify produced an invalid token count");
+    for (int i = 0; i < n_out; ++i) host_out[i] = res[i];
+    *host_n_out = n_out;
+    m->host_pos += res[6];
     return AW4_OK;
 }
 

@@ -12,7 +12,18 @@ struct Ctl {
     int32_t token;      // token fed to the next embedding
     int32_t argmax;     // last argmax
     int32_t nstep;      // index into the greedy output ring
-    int32_t pad[60];
+    // draft verification
+    int32_t vtok[4];    // t0 (last emitted) and the drafts
+    float vu[4];        // uniforms: one per draft, the last for the draw
+    float vmax[4];      // max logit per verified position
+    float vz[4];        // softmax normaliser per verified position
+    int32_t vargmax[4];
+    int32_t vout[4];    // emitted tokens
+    int32_t vn_acc;     // drafts accepted
+    int32_t vn_out;     // tokens emitted (vn_acc + 1)
+    int32_t vcommit;    // positions committed (vn_acc + 1)
+    int32_t vresid_p;   // 1 when the residual was all zero and p was used
+    int32_t pad[28];
 };
 
 // W4 GPU layout: codes as dwords [rows][cols/8]; within each dword the eight
@@ -40,6 +51,28 @@ struct GemvArgs {
     _Float16* hout;       // SWIGLU: fp16 out [rows/2]; rows interleave gate/up
 };
 
+// M input vectors (M <= 4, one per verified token), vectors at fixed strides
+struct GemvMultiArgs {
+    const uint32_t* codes;
+    const uint16_t* scales;
+    int32_t rows;
+    int32_t K;
+    int32_t M;
+    const float* x;        // NORM / GATED input, vector m at x + m * sx
+    int64_t sx;
+    const float* nw;
+    const float* z;        // GATED gate input, vector m at z + m * sz
+    int64_t sz;
+    const _Float16* h;     // LOADH input, vector m at h + m * sh
+    int64_t sh;
+    int32_t gated_d;
+    float eps;
+    float* y;              // STORE / RESID output, vector m at y + m * sy
+    int64_t sy;
+    _Float16* hout;        // SWIGLU output, vector m at hout + m * so
+    int64_t so;
+};
+
 struct HeadArgs {
     const int8_t* codes;      // [V][H]
     const uint16_t* scales;   // [V][H/32]
@@ -63,6 +96,7 @@ struct GdnArgs {
 };
 
 struct AttnArgs {
+    int32_t pos_offset;       // the token sits at ctl->pos + pos_offset
     const float* proj;        // [q nq*d | g nq*d | k nkv*d | v nkv*d]
     int8_t* kc;               // [nkv][max_ctx][d]
     uint16_t* ks;             // [nkv][max_ctx][d/32]
@@ -75,6 +109,7 @@ struct AttnArgs {
 };
 
 struct CombineArgs {
+    int32_t pos_offset;
     const float* part;
     const float* proj;        // for the gate g
     const float* signs;
@@ -83,14 +118,59 @@ struct CombineArgs {
     int32_t nq, nkv, d, nsplit;
 };
 
+struct GdnMultiArgs {
+    const float* proj;        // token m's projections at proj + m * sproj
+    int64_t sproj;
+    const float* a_bias;
+    float* S;
+    float* o;                 // token m's readout at o + m * so
+    int64_t so;
+    int32_t nqk, nv, d, M;
+    float eps;
+    int32_t replay;           // 1: apply *commit_n steps and write S back
+    const int32_t* commit_n;
+};
+
+struct AcceptArgs {
+    Ctl* ctl;
+    const float* logits;      // [k+1][V]
+    const float* q;           // [k][V] draft probabilities (unused when greedy)
+    int32_t V, k, greedy;
+    float inv_t;
+    float* zpart;             // [k+1][nb]
+    float* wpart;             // [k+1][nb]
+};
+
 // ---------------------------------------------------------------- launches
 hipError_t launch_gemv(int pro, int epi, const GemvArgs& a, hipStream_t s);
 int gemv_blocks(int rows);
 hipError_t launch_head(const HeadArgs& a, hipStream_t s);
+hipError_t launch_gemv_multi(int pro, int epi, const GemvMultiArgs& a, hipStream_t s);
+// int8 head over M vectors: logits [M][V], per-block best per vector [M][nblocks]
+struct HeadMultiArgs {
+    const int8_t* codes;
+    const uint16_t* scales;
+    int32_t V, H, M;
+    const float* x;        // residuals, vector m at x + m * H
+    const float* nw;
+    float eps;
+    float* logits;         // [M][V]
+    float* part_val;       // [M][nblocks]
+    int32_t* part_idx;
+};
+hipError_t launch_head_multi(const HeadMultiArgs& a, hipStream_t s);
 int head_blocks(int V);
 hipError_t launch_head_final(const float* pv, const int32_t* pi, int n, Ctl* ctl, int32_t* ring, int ring_cap,
                              hipStream_t s);
 hipError_t launch_gdn(const GdnArgs& a, hipStream_t s);
+hipError_t launch_gdn_multi(const GdnMultiArgs& a, hipStream_t s);
+int accept_blocks(int V);
+hipError_t launch_accept(const AcceptArgs& a, const float* head_pv, const int32_t* head_pi, int head_nb,
+                         hipStream_t s);
+hipError_t launch_commit_pos(Ctl* ctl, hipStream_t s);
+hipError_t launch_embed_multi(const int8_t* codes, const uint16_t* scales, int H, const Ctl* ctl, int M, float* x,
+                              hipStream_t s);
+hipError_t launch_set_verify(Ctl* ctl, const int32_t* tok, const float* u, hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_embed(const int8_t* codes, const uint16_t* scales, int H, const Ctl* ctl, float* x,

@@ -92,7 +92,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
     const int split = blockIdx.x, j = blockIdx.y, tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int row = lane >> 4, jl = lane & 15;
-    const int pos = a.ctl->pos;
+    const int pos = a.ctl->pos + a.pos_offset;
     const int npos = pos + 1;
     int pps, used;
     split_range(npos, a.nsplit, pps, used);
@@ -303,7 +303,7 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
     __shared__ float wsum[256];
     __shared__ float red[8];
     const int i = blockIdx.x, tid = threadIdx.x;
-    const int pos = a.ctl->pos;
+    const int pos = a.ctl->pos + a.pos_offset;
     int pps, used;
     split_range(pos + 1, a.nsplit, pps, used);
     const float* base = a.part + (int64_t)i * a.nsplit * (D + 2);

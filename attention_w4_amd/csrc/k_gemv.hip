@@ -486,6 +486,230 @@ __global__ __launch_bounds__(256) void k_head_i8(HeadArgs a) {
     }
 }
 
+// ------------------------------------------------------------------ M-vector W4 GEMV
+// The verify pass of draft tokens runs M <= 4 tokens through every layer in
+// one sweep over the weights: each group of codes is loaded and dequantised
+// once and dotted with the M input vectors held in LDS.
+template <int MAXM>
+__device__ __forceinline__ void multi_prologue(int pro, const GemvMultiArgs& a, _Float16* xs, float* red) {
+    const int K = a.K, M = a.M;
+    if (pro == PRO_LOADH) {
+        for (int m = 0; m < M; ++m) {
+            const uint4* src = (const uint4*)(a.h + m * a.sh);
+            uint4* dst = (uint4*)(xs + m * K);
+            for (int i = threadIdx.x; i < K / 8; i += 256) dst[i] = src[i];
+        }
+        return;
+    }
+    if (pro == PRO_NORM) {
+        float ss[MAXM];
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m) {
+            ss[m] = 0.f;
+            if (m < M)
+                for (int k = threadIdx.x; k < K; k += 256) {
+                    const float v = a.x[m * a.sx + k];
+                    ss[m] += v * v;
+                }
+            ss[m] = wave_sum(ss[m]);
+        }
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        if (lane == 0)
+#pragma unroll
+            for (int m = 0; m < MAXM; ++m) red[m * 4 + wave] = ss[m];
+        __syncthreads();
+        for (int m = 0; m < M; ++m) {
+            const float t = red[m * 4] + red[m * 4 + 1] + red[m * 4 + 2] + red[m * 4 + 3];
+            const float r = 1.0f / sqrtf(t / (float)K + a.eps);
+            for (int k = threadIdx.x; k < K; k += 256) xs[m * K + k] = (_Float16)(a.x[m * a.sx + k] * r * a.nw[k]);
+        }
+        return;
+    }
+    // gated: per head of d values RMSNorm(o) * w * SiLU(z), one wave per head
+    const int d = a.gated_d, nh = K / d;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int m = 0; m < M; ++m)
+        for (int hh = wave; hh < nh; hh += 4) {
+            const float* o = a.x + m * a.sx + (int64_t)hh * d;
+            const float* z = a.z + m * a.sz + (int64_t)hh * d;
+            float ss = 0.f;
+            for (int i = lane; i < d; i += 64) ss += o[i] * o[i];
+            ss = wave_sum(ss);
+            const float r = 1.0f / sqrtf(ss / (float)d + a.eps);
+            for (int i = lane; i < d; i += 64)
+                xs[m * K + hh * d + i] = (_Float16)(o[i] * r * a.nw[i] * (z[i] * sigmoidf_(z[i])));
+        }
+}
+
+template <int R, int NF, int PRO, int EPI>
+__global__ __launch_bounds__(256, 2) void k_gemv_multi(GemvMultiArgs a) {
+    constexpr int MAXM = 4;
+    extern __shared__ __align__(16) unsigned char smem[];
+    float* red = (float*)smem;                       // 16 floats
+    _Float16* xs = (_Float16*)(smem + 64);           // [M][K]
+    constexpr int G = 64 * NF / R;
+    constexpr int K = 32 * G;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nrb = (a.rows + R - 1) / R;            // the last row block may be partial
+    const int nw = gridDim.x * 4;
+    const int M = a.M;
+    int row_of[NF], grp_of[NF];
+#pragma unroll
+    for (int i = 0; i < NF; ++i) {
+        const int f = lane + 64 * i;
+        row_of[i] = f / G;
+        grp_of[i] = f % G;
+    }
+    auto load = [&](RowBlock<R, NF>& b, int rbk) {
+        const u32x4* cb = (const u32x4*)(a.codes + (int64_t)rbk * R * G * 4);
+        const uint16_t* sb = a.scales + (int64_t)rbk * R * G;
+#pragma unroll
+        for (int i = 0; i < NF; ++i) {
+            if (rbk * R + row_of[i] < a.rows) {
+                b.c[i] = __builtin_nontemporal_load(cb + lane + 64 * i);
+                b.s[i] = sb[lane + 64 * i];
+            } else {
+                b.c[i] = u32x4{0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
+                b.s[i] = 0;
+            }
+        }
+    };
+    int rb = blockIdx.x * 4 + wave;
+    RowBlock<R, NF> cur;
+    if (rb < nrb) load(cur, rb);
+    multi_prologue<MAXM>(PRO, a, xs, red);
+    __syncthreads();
+    for (; rb < nrb; rb += nw) {
+        float acc[MAXM][R];
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m)
+#pragma unroll
+            for (int r = 0; r < R; ++r) acc[m][r] = 0.f;
+#pragma unroll
+        for (int i = 0; i < NF; ++i) {
+            const int g = grp_of[i];
+            const float sc = half_bits_to_float(cur.s[i]);
+#pragma unroll
+            for (int m = 0; m < MAXM; ++m) {
+                if (m < M) {
+                    const uint4* xv = (const uint4*)(xs + m * K);
+                    float ea = 0.f, eb = 0.f;
+                    dq_dot8(cur.c[i][0], xv[4 * g], ea, eb);
+                    dq_dot8(cur.c[i][1], xv[4 * g + 1], ea, eb);
+                    dq_dot8(cur.c[i][2], xv[4 * g + 2], ea, eb);
+                    dq_dot8(cur.c[i][3], xv[4 * g + 3], ea, eb);
+                    const float part = sc * (ea + 0.0625f * eb);
+#pragma unroll
+                    for (int r = 0; r < R; ++r) acc[m][r] += row_of[i] == r ? part : 0.f;
+                }
+            }
+            if (NF > 8 && i == NF / 2) asm volatile("" ::: "memory");
+        }
+        const int r0 = rb * R;
+        if (rb + nw < nrb) load(cur, rb + nw);
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m) {
+            if (m < M) {
+#pragma unroll
+                for (int r = 0; r < R; ++r) acc[m][r] = wave_sum_fast(acc[m][r]);
+                if (lane == 0) {
+                    if (EPI == EPI_STORE) {
+#pragma unroll
+                        for (int r = 0; r < R; ++r)
+                            if (r0 + r < a.rows) a.y[m * a.sy + r0 + r] = acc[m][r];
+                    } else if (EPI == EPI_RESID) {
+#pragma unroll
+                        for (int r = 0; r < R; ++r)
+                            if (r0 + r < a.rows) a.y[m * a.sy + r0 + r] += acc[m][r];
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < R; r += 2) {
+                            if (r0 + r + 1 < a.rows) {
+                                const float gg = acc[m][r];
+                                a.hout[m * a.so + ((r0 + r) >> 1)] = (_Float16)(gg * sigmoidf_(gg) * acc[m][r + 1]);
+                            }
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
+// int8 head over M vectors (per-vector logits and per-block argmax partials)
+__global__ __launch_bounds__(256) void k_head_multi(HeadMultiArgs a) {
+    constexpr int MAXM = 4;
+    extern __shared__ __align__(16) unsigned char smem[];
+    float* red = (float*)smem;
+    _Float16* xs = (_Float16*)(smem + 64);   // [M][H]
+    __shared__ float bv_s[MAXM][4];
+    __shared__ int bi_s[MAXM][4];
+    {
+        GemvMultiArgs g{};
+        g.K = a.H;
+        g.M = a.M;
+        g.x = a.x;
+        g.sx = a.H;
+        g.nw = a.nw;
+        g.eps = a.eps;
+        multi_prologue<MAXM>(PRO_NORM, g, xs, red);
+    }
+    __syncthreads();
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int H = a.H, M = a.M;
+    const int nchunk = H >> 4;
+    const int g_row = H >> 5;
+    float best[MAXM];
+    int besti[MAXM];
+#pragma unroll
+    for (int m = 0; m < MAXM; ++m) { best[m] = -INFINITY; besti[m] = 0x7fffffff; }
+    for (int r = blockIdx.x * 4 + wave; r < a.V; r += gridDim.x * 4) {
+        const uint4* c0 = (const uint4*)(a.codes + (int64_t)r * H);
+        const uint16_t* s0 = a.scales + (int64_t)r * g_row;
+        float acc[MAXM];
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m) acc[m] = 0.f;
+        for (int c = lane; c < nchunk; c += 64) {
+            const uint4 w = c0[c];
+            const float sc = half_bits_to_float(s0[c >> 1]);
+#pragma unroll
+            for (int m = 0; m < MAXM; ++m) {
+                if (m < M) {
+                    const uint4* xv = (const uint4*)(xs + m * H);
+                    const uint4 xa = xv[2 * c], xb = xv[2 * c + 1];
+                    float p = 0.f;
+                    i8_dot4(w.x, xa.x, xa.y, p);
+                    i8_dot4(w.y, xa.z, xa.w, p);
+                    i8_dot4(w.z, xb.x, xb.y, p);
+                    i8_dot4(w.w, xb.z, xb.w, p);
+                    acc[m] += sc * p;
+                }
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m) {
+            if (m < M) {
+                const float v = wave_sum_fast(acc[m]);
+                if (lane == 0) a.logits[(int64_t)m * a.V + r] = v;
+                if (better(v, r, best[m], besti[m])) { best[m] = v; besti[m] = r; }
+            }
+        }
+    }
+    if (lane == 0)
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m) { bv_s[m][wave] = best[m]; bi_s[m][wave] = besti[m]; }
+    __syncthreads();
+    if (threadIdx.x < M) {
+        const int m = threadIdx.x;
+        float b = bv_s[m][0];
+        int bi = bi_s[m][0];
+        for (int w = 1; w < 4; ++w)
+            if (better(bv_s[m][w], bi_s[m][w], b, bi)) { b = bv_s[m][w]; bi = bi_s[m][w]; }
+        a.part_val[m * gridDim.x + blockIdx.x] = b;
+        a.part_idx[m * gridDim.x + blockIdx.x] = bi;
+    }
+}
+
 // final argmax over the per-block results; feeds the next embedding and the
 // greedy output ring, and advances the position
 __global__ __launch_bounds__(256) void k_head_final(const float* pv, const int32_t* pi, int n, Ctl* ctl,
@@ -609,6 +833,61 @@ hipError_t launch_gemv(int pro, int epi, const GemvArgs& a, hipStream_t s) {
 #undef AW4_SHAPE
     }
     return launch_generic(pro, epi, a, s);
+}
+
+namespace {
+template <int R, int NF>
+hipError_t launch_multi_rnf(int pro, int epi, const GemvMultiArgs& a, hipStream_t s) {
+    const size_t shm = 64 + (size_t)a.K * 2 * (size_t)a.M;
+    const dim3 grid(stream_blocks(a.rows + R - 1, R, NF)), block(256);
+#define AW4_MULTI_CASE(P, E)                                                                        \
+    if (pro == P && epi == E) {                                                                     \
+        if (shm > 65536) {                                                                          \
+            hipError_t e = hipFuncSetAttribute((const void*)k_gemv_multi<R, NF, P, E>,              \
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm); \
+            if (e != hipSuccess) return e;                                                          \
+        }                                                                                           \
+        hipLaunchKernelGGL((k_gemv_multi<R, NF, P, E>), grid, block, shm, s, a);                    \
+        return hipGetLastError();                                                                   \
+    }
+    AW4_MULTI_CASE(PRO_NORM, EPI_STORE)
+    AW4_MULTI_CASE(PRO_NORM, EPI_SWIGLU)
+    AW4_MULTI_CASE(PRO_GATED, EPI_RESID)
+    AW4_MULTI_CASE(PRO_LOADH, EPI_RESID)
+#undef AW4_MULTI_CASE
+    return hipErrorInvalidValue;
+}
+}  // namespace
+
+hipError_t launch_gemv_multi(int pro, int epi, const GemvMultiArgs& a, hipStream_t s) {
+    if (a.M < 1 || a.M > 4) return hipErrorInvalidValue;
+    int R, NF;
+    stream_shape(a.K, R, NF);
+    if (pro == PRO_GATED && (a.gated_d <= 0 || a.K % a.gated_d)) return hipErrorInvalidValue;
+#define AW4_SHAPE(RR, FF) \
+    if (R == RR && NF == FF) return launch_multi_rnf<RR, FF>(pro, epi, a, s);
+    AW4_SHAPE(2, 5)
+    AW4_SHAPE(2, 4)
+    AW4_SHAPE(2, 6)
+    AW4_SHAPE(2, 17)
+    AW4_SHAPE(4, 1)
+    AW4_SHAPE(4, 3)
+    AW4_SHAPE(8, 1)
+    AW4_SHAPE(16, 1)
+    AW4_SHAPE(32, 3)
+#undef AW4_SHAPE
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_head_multi(const HeadMultiArgs& a, hipStream_t s) {
+    if (a.M < 1 || a.M > 4) return hipErrorInvalidValue;
+    const size_t shm = 64 + (size_t)a.H * 2 * (size_t)a.M;
+    if (shm > 65536) {
+        hipError_t e = hipFuncSetAttribute((const void*)k_head_multi, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(k_head_multi, dim3(head_blocks(a.V)), dim3(256), shm, s, a);
+    return hipGetLastError();
 }
 
 hipError_t launch_head(const HeadArgs& a, hipStream_t s) {

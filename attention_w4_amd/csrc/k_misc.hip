@@ -22,6 +22,31 @@ __global__ void k_embed(const int8_t* __restrict__ codes, const uint16_t* __rest
 
 __global__ void k_set_token(Ctl* ctl, int32_t token) { ctl->token = token; }
 
+__global__ void k_embed_multi(const int8_t* __restrict__ codes, const uint16_t* __restrict__ scales, int H,
+                              const Ctl* ctl, int M, float* __restrict__ x) {
+    for (int m = 0; m < M; ++m) {
+        const int64_t tok = ctl->vtok[m];
+        for (int k = blockIdx.x * blockDim.x + threadIdx.x; k < H; k += gridDim.x * blockDim.x) {
+            const float s = (float)__builtin_bit_cast(_Float16, scales[tok * (H / 32) + k / 32]);
+            x[(int64_t)m * H + k] = (float)codes[tok * H + k] * s;
+        }
+    }
+}
+
+struct VerifyIn {
+    int32_t tok[4];
+    float u[4];
+};
+
+__global__ void k_set_verify(Ctl* ctl, VerifyIn in) {
+    for (int i = 0; i < 4; ++i) {
+        ctl->vtok[i] = in.tok[i];
+        ctl->vu[i] = in.u[i];
+        ctl->vout[i] = 0;
+    }
+    ctl->vn_acc = ctl->vn_out = ctl->vcommit = ctl->vresid_p = 0;
+}
+
 __global__ void k_advance(Ctl* ctl) { ctl->pos += 1; }
 
 __global__ void k_set_ctl(Ctl* ctl, int32_t pos, int32_t token, int32_t nstep) {
@@ -99,6 +124,22 @@ int grid_for(int64_t n, int per_block = 256) {
 hipError_t launch_embed(const int8_t* codes, const uint16_t* scales, int H, const Ctl* ctl, float* x,
                         hipStream_t s) {
     hipLaunchKernelGGL(k_embed, dim3(grid_for(H)), dim3(256), 0, s, codes, scales, H, ctl, x);
+    return hipGetLastError();
+}
+
+hipError_t launch_embed_multi(const int8_t* codes, const uint16_t* scales, int H, const Ctl* ctl, int M, float* x,
+                              hipStream_t s) {
+    hipLaunchKernelGGL(k_embed_multi, dim3(grid_for(H)), dim3(256), 0, s, codes, scales, H, ctl, M, x);
+    return hipGetLastError();
+}
+
+hipError_t launch_set_verify(Ctl* ctl, const int32_t* tok, const float* u, hipStream_t s) {
+    VerifyIn in;
+    for (int i = 0; i < 4; ++i) {
+        in.tok[i] = tok[i];
+        in.u[i] = u[i];
+    }
+    hipLaunchKernelGGL(k_set_verify, dim3(1), dim3(1), 0, s, ctl, in);
     return hipGetLastError();
 }
 

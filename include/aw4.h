@@ -179,6 +179,27 @@ int aw4_decode_step(aw4_model* model, int32_t token, float* dev_logits, int32_t*
  * the end).  This is the measured decode loop. */
 int aw4_decode_greedy(aw4_model* model, int32_t first_token, int32_t n_steps, int32_t* host_tokens_out);
 
+/* Draft verification (page 5, bs178.com llamAmpere article, point 四: the
+ * model's draft head proposes k tokens, the target checks them in one pass and
+ * keeps each with probability min(1, p/q), which leaves the output distribution
+ * equal to the target's).  host_tokens holds k + 1 ids: the last emitted token
+ * t0 (not yet run through the model) and k drafts, 0 <= k <= max_verify - 1.
+ * The pass runs the k + 1 tokens at positions pos .. pos + k with one sweep
+ * over the weights.  With temperature > 0, p_j = softmax(L_j / T) where L_j is
+ * the output at position pos + j; draft j+1 is kept when host_u[j] <
+ * min(1, p_j(d) / q_j(d)) (dev_q: k rows of V fp32 draft probabilities on the
+ * device; a draft with q = 0 is rejected); at the first rejection one token is
+ * drawn from max(0, p_j - q_j) renormalised (from p_j if that is all zero), and
+ * when every draft is kept a bonus token from p_k, both by inverse CDF in index
+ * order with host_u[k].  temperature == 0 is exact-match greedy (dev_q, host_u
+ * unused).  host_out receives the accepted drafts followed by the drawn token
+ * (*host_n_out = accepted + 1 <= k + 1); the model commits positions pos ..
+ * pos + accepted (recurrent states replayed from the committed state, the
+ * cache length set), and the last emitted token becomes the next pass's t0.
+ * Synchronous.  Errors: AW4_E_INVAL, AW4_E_TOKEN, AW4_E_CTX_FULL, AW4_E_STATE. */
+int aw4_verify_k(aw4_model* model, const int32_t* host_tokens, int32_t k, const float* dev_q, const float* host_u,
+                 float temperature, int32_t* host_out, int32_t* host_n_out);
+
 /* Layers only, at the current position: dev_x_out = stack(dev_x_in), both
  * fp32 [hidden] device vectors (may alias).  For models without a vocabulary
  * (single-layer workloads) and for hidden-state checks.  Enqueued. */

@@ -290,6 +290,21 @@ class Model:
         self._rc(lib().or_get_last_kv(self.h, layer, _p(k), _p(v)), "last_kv")
         return k, v
 
+    def snapshot(self):
+        """recurrent states, caches and position"""
+        st = {"pos": self.pos}
+        for l, t in enumerate(self.shape.pattern):
+            st[l] = self.get_gdn_state(l) if t == "G" else self.get_kv(l, self.pos)
+        return st
+
+    def restore(self, st):
+        for l, t in enumerate(self.shape.pattern):
+            if t == "G":
+                self.set_gdn_state(l, st[l].astype(np.float32))
+            else:
+                self.set_kv(l, *st[l])
+        self.set_pos(st["pos"])
+
     def get_kv(self, layer, npos):
         s = self.shape
         d, nkv = s.attn_head_dim, s.attn_kv_heads

@@ -54,9 +54,9 @@ def accept(logits, drafts, q, u, temperature):
         p = softmax_t(logits[j], temperature)
         d = int(drafts[j])
         qd = float(q[j][d])
-        if qd <= 0:
-            raise ValueError("draft token has zero draft probability")
-        if u[j] < min(1.0, p[d] / qd):
+        # a draft the draft distribution gives probability 0 is rejected
+        ratio = p[d] / qd if qd > 0 else 0.0
+        if u[j] < min(1.0, ratio):
             out.append(d)
             continue
         resid = np.maximum(p - np.asarray(q[j], np.float64), 0.0)
@@ -66,3 +66,21 @@ def accept(logits, drafts, q, u, temperature):
         return out, j
     out.append(inverse_cdf(softmax_t(logits[k], temperature), u[k]))
     return out, k
+
+
+def verify(model, tokens, q, u, temperature):
+    """Oracle of draft verification on an oracle.Model: run tokens [t0, d1..dk]
+    from the model's state, apply the acceptance rule, then restore the state
+    and commit t0 .. d_a (the accepted prefix).  Returns (emitted, accepted,
+    logits [k+1][V])."""
+    snap = model.snapshot()
+    logits = []
+    for t in tokens:
+        _, L, _ = model.decode_token(int(t))
+        logits.append(L)
+    logits = np.stack(logits)
+    out, a = accept(logits, list(tokens[1:]), q, u, temperature)
+    model.restore(snap)
+    for t in tokens[:a + 1]:
+        model.decode_token(int(t))
+    return out, a, logits

@@ -1,0 +1,189 @@
+"""GPU parity of draft verification (aw4_verify_k) against the oracle.
+
+The oracle runs the k + 1 tokens one by one, applies the acceptance rule of
+oracle/accept.py and commits the accepted prefix (oracle.accept.verify).  Each
+pass starts from the oracle's state on both sides (teacher forcing), so the
+comparison covers one pass: emitted tokens, committed position, recurrent
+states after the replay and the committed cache entries.  With temperature 0
+the rule is exact-match greedy and the emitted tokens must equal plain greedy
+decoding; with sampling a decision may only differ where the oracle's own
+quantity sits at the decision boundary (u against min(1, p/q), or the inverse
+CDF crossing), since the two sides round p differently.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from oracle.accept import verify as oracle_verify, softmax_t, inverse_cdf
+from synth import workloads as W
+from tests.helpers import TINY, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def aw4():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import attention_w4_amd as A
+    A.lib()
+    return A
+
+
+def _pair(A, shape, seed, n_prompt, jitter=0.0):
+    from synth.gpu_load import load_recipe
+    om = oracle.from_recipe(shape, seed, jitter)
+    gm = A.Model(shape)
+    load_recipe(gm, shape, seed, jitter)
+    prompt = synth.tokens(n_prompt, shape.vocab, seed)
+    # the last prompt token is the first pass's t0 (emitted, not yet run)
+    for t in prompt[:-1]:
+        om.decode_token(int(t))
+    return om, gm, prompt
+
+
+def _import(gm, om, shape):
+    for l, t in enumerate(shape.pattern):
+        if t == "G":
+            gm.import_gdn(l, om.get_gdn_state(l).astype(np.float32))
+        else:
+            gm.import_kv(l, *om.get_kv(l, om.pos))
+    gm.set_pos(om.pos)
+
+
+def _check_commit(gm, om, shape, pos0):
+    assert gm.pos == om.pos
+    for l, t in enumerate(shape.pattern):
+        if t == "G":
+            assert rel_l2(gm.export_gdn(l), om.get_gdn_state(l)) < 1e-3, l
+        else:
+            gk, ok = gm.export_kv(l, om.pos), om.get_kv(l, om.pos)
+            for a, b in ((gk[0], ok[0]), (gk[2], ok[2])):
+                d = a[pos0:].astype(int) - b[pos0:].astype(int)
+                assert np.abs(d).max() <= 1 and (d != 0).mean() < 6e-2
+
+
+@pytest.mark.parametrize("shape_name", ["TINY", "TOY"])
+def test_verify_greedy_equals_greedy_decode(aw4, shape_name):
+    shape = TINY if shape_name == "TINY" else W.TOY
+    _say("case: verify_k greedy", shape_name)
+    om, gm, prompt = _pair(aw4, shape, 2, 24, 0.1 if shape_name == "TINY" else 0.0)
+    rng = np.random.default_rng(0)
+    t0 = int(prompt[-1])
+    total_acc = 0
+    for p in range(10):
+        k = [3, 2, 1, 0, 3, 3, 2, 3, 1, 3][p]
+        # drafts: the oracle's own greedy continuation, with one wrong token on some passes
+        snap = om.snapshot()
+        chain, t = [], t0
+        for _ in range(k):
+            _, _, t = om.decode_token(t)
+            chain.append(t)
+        om.restore(snap)
+        if k and p % 3 == 1:
+            j = int(rng.integers(0, k))
+            chain[j] = (chain[j] + 1) % shape.vocab
+        tokens = [t0] + chain
+        _import(gm, om, shape)
+        pos0 = om.pos
+        ref, a, _ = oracle_verify(om, tokens, None, None, 0.0)
+        got = gm.verify_k(tokens, temperature=0.0)
+        assert got == ref, (p, tokens, got, ref)
+        _check_commit(gm, om, shape, pos0)
+        total_acc += a
+        t0 = ref[-1]
+    _say("accepted drafts", total_acc)
+    assert total_acc > 5
+    gm.close()
+
+
+def _synthetic_q(V, k, seed, pass_id):
+    """draft distributions q_j = softmax of N(0, 1.43^2) logits, drafts d_j ~ q_j"""
+    logits = synth.normal(k, V, W.DRAFT_LOGIT_STD, seed, W.STREAM_DRAFT + pass_id).astype(np.float64)
+    q = np.stack([softmax_t(logits[j], 1.0) for j in range(k)]).astype(np.float32)
+    du = synth.uniform(k, seed, W.STREAM_UNIFORM, i0=1000 + 8 * pass_id)
+    drafts = [inverse_cdf(q[j], du[j]) for j in range(k)]
+    return q, drafts
+
+
+def test_verify_sampling_matches_oracle(aw4):
+    import torch
+    shape = W.TOY
+    _say("case: verify_k sampling T=1")
+    om, gm, prompt = _pair(aw4, shape, 4, 20)
+    t0 = int(prompt[-1])
+    agree = near = 0
+    for p in range(12):
+        k = 3
+        q, drafts = _synthetic_q(shape.vocab, k, 4, p)
+        u = synth.uniform(k + 1, 4, W.STREAM_UNIFORM, i0=8 * p)
+        tokens = [t0] + drafts
+        _import(gm, om, shape)
+        pos0 = om.pos
+        qd = torch.from_numpy(q).cuda()
+        ref, a, L = oracle_verify(om, tokens, q.astype(np.float64), u, 1.0)
+        got = gm.verify_k(tokens, qd, u, 1.0)
+        if got == ref:
+            agree += 1
+            _check_commit(gm, om, shape, pos0)
+        else:
+            # only a decision at the oracle's own boundary may differ
+            ok = False
+            for j in range(min(len(got), len(ref))):
+                if got[j] == ref[j]:
+                    continue
+                if j < k:
+                    pj = softmax_t(L[j], 1.0)
+                    thr = min(1.0, pj[drafts[j]] / q[j][drafts[j]])
+                    ok = abs(u[j] - thr) < 1e-4
+                break
+            assert ok, (p, got, ref)
+            near += 1
+            # resynchronise both sides on the oracle's committed state
+        t0 = ref[-1]
+    _say(f"passes agreeing {agree}, at a decision boundary {near}")
+    assert agree >= 10
+    gm.close()
+
+
+def test_verify_acceptance_distribution_chi2(aw4):
+    """The first emitted token of a k=1 pass, over many passes from the same
+    state with fresh uniforms and drafts d ~ q, follows the target p (the
+    equivalence the pages state for the min(1, p/q) rule)."""
+    import torch
+    from scipy.stats import chisquare
+    shape = TINY
+    _say("case: chi-square of GPU acceptance")
+    om, gm, prompt = _pair(aw4, shape, 6, 8)
+    t0 = int(prompt[-1])
+    snap = om.snapshot()
+    _, L0, _ = om.decode_token(t0)
+    om.restore(snap)
+    p = softmax_t(L0, 1.0)
+    # a draft distribution that differs from p: flattened logits
+    q = softmax_t(L0 * 0.3, 1.0).astype(np.float32)
+    qd = torch.from_numpy(q[None, :]).cuda()
+    n = 3000
+    du = synth.uniform(n, 8, W.STREAM_UNIFORM, i0=50_000)
+    uu = synth.uniform(2 * n, 9, W.STREAM_UNIFORM, i0=90_000).reshape(n, 2)
+    counts = np.zeros(shape.vocab)
+    for i in range(n):
+        _import(gm, om, shape)
+        d = inverse_cdf(q, du[i])
+        got = gm.verify_k([t0, d], qd, uu[i], 1.0)
+        counts[got[0]] += 1
+    top = np.argsort(p)[::-1][:12]
+    obs = np.append(counts[top], n - counts[top].sum())
+    exp = np.append(p[top] * n, n * (1 - p[top].sum()))
+    stat = chisquare(obs, exp)
+    _say(f"chi2 p-value {stat.pvalue:.3f}")
+    assert stat.pvalue > 1e-3
+    gm.close()
