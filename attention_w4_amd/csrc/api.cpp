@@ -125,10 +125,12 @@ int64_t mix_out_cols(const aw4_config* c, char t) {
     return t == 'G' ? (int64_t)c->gdn_v_heads * c->gdn_head_dim : (int64_t)c->attn_q_heads * c->attn_head_dim;
 }
 
+// splits of the attention grid: enough workgroups at long context, and a
+// split never shorter than 64 positions (one load batch per row-group)
 int nsplit_for(int max_ctx) {
-    int n = max_ctx / 256;
+    int n = max_ctx / 64;
     if (n < 1) n = 1;
-    if (n > 128) n = 128;
+    if (n > 256) n = 256;
     return n;
 }
 

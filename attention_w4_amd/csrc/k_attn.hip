@@ -197,39 +197,49 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
     const int wi = bit0 >> 5, woff = bit0 & 31;
     const int rg = wave * 4 + row;   // row-group 0..15
 
-    // load one position's K and V slice of this lane (from the LDS copy for
-    // the current token, whose global entry split 0 may still be writing)
-    auto load = [&](int t, float* kf, float* vf) {
-        if (t == pos) {
+    // Raw cache words of one position for this lane; dequantised at use so
+    // that the loads of a whole batch stay in flight together (the current
+    // token comes from the LDS copy: split 0 may still be writing its entry).
+    struct Raw {
+        uint32_t k[DL / 4];
+        uint32_t vlo, vhi;
+        uint16_t ks, vs;
+        bool cur;
+    };
+    auto load_raw = [&](int t, Raw& r) {
+        r.cur = (t == pos);
+        if (r.cur) return;
+        const int64_t prow = hbase + t;
+        r.ks = a.ks[prow * NG + grp];
+        r.vs = a.vs[prow * NG + grp];
+        const int8_t* kr = a.kc + prow * D + e0;
+        if (DL == 16) {
+            const uint4 kw = *(const uint4*)kr;
+            r.k[0] = kw.x; r.k[1] = kw.y; r.k[2] = kw.z; r.k[3] = kw.w;
+        } else {
+            r.k[0] = *(const uint32_t*)kr;
+        }
+        const uint32_t* vg = a.vc + (prow * NG + grp) * 3;
+        r.vlo = vg[wi];
+        r.vhi = wi < 2 ? vg[wi + 1] : 0u;
+    };
+    auto update = [&](const Raw& r) {
+        float kf[DL], vf[DL];
+        if (r.cur) {
 #pragma unroll
             for (int e = 0; e < DL; ++e) {
                 kf[e] = (float)kcur[e0 + e] * kscur[grp];
                 vf[e] = (float)vcur[e0 + e] * vscur[grp];
             }
         } else {
-            const int64_t prow = hbase + t;
-            const float ksc = (float)__builtin_bit_cast(_Float16, a.ks[prow * NG + grp]);
-            const float vsc = (float)__builtin_bit_cast(_Float16, a.vs[prow * NG + grp]);
-            const int8_t* kr = a.kc + prow * D + e0;
-            if (DL == 16) {
-                const uint4 kw = *(const uint4*)kr;
-                const uint32_t kk[4] = {kw.x, kw.y, kw.z, kw.w};
+            const float ksc = (float)__builtin_bit_cast(_Float16, r.ks);
+            const float vsc = (float)__builtin_bit_cast(_Float16, r.vs);
 #pragma unroll
-                for (int e = 0; e < DL; ++e) kf[e] = (float)(int8_t)(kk[e >> 2] >> (8 * (e & 3))) * ksc;
-            } else {
-                const uint32_t kw = *(const uint32_t*)kr;
-#pragma unroll
-                for (int e = 0; e < DL; ++e) kf[e] = (float)(int8_t)(kw >> (8 * e)) * ksc;
-            }
-            const uint32_t* vg = a.vc + (prow * NG + grp) * 3;
-            const uint32_t lo = vg[wi];
-            const uint32_t hi = wi < 2 ? vg[wi + 1] : 0u;
-            const uint64_t bits = (((uint64_t)hi << 32) | lo) >> woff;
+            for (int e = 0; e < DL; ++e) kf[e] = (float)(int8_t)(r.k[e >> 2] >> (8 * (e & 3))) * ksc;
+            const uint64_t bits = (((uint64_t)r.vhi << 32) | r.vlo) >> woff;
 #pragma unroll
             for (int e = 0; e < DL; ++e) vf[e] = (float)((int)((bits >> (3 * e)) & 7u) - 4) * vsc;
         }
-    };
-    auto update = [&](const float* kf, const float* vf) {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             float p = 0.f;
@@ -245,15 +255,27 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
             m[g] = mn;
         }
     };
-    // positions t0 + rg + 16 k, two in flight per row; a wave runs while any of
-    // its rows has work (rows with none skip, all lanes of a row agree)
-    for (int t = t0 + rg; t - row < t1; t += 32) {
-        float ka[DL], va[DL], kb[DL], vb[DL];
-        const bool ha = t < t1, hb = t + 16 < t1;
-        if (ha) load(t, ka, va);
-        if (hb) load(t + 16, kb, vb);
-        if (ha) update(ka, va);
-        if (hb) update(kb, vb);
+    // positions t0 + rg + 16 k, in batches of NB per row-group with the next
+    // batch's loads issued before the current one is used; a wave runs while any
+    // of its rows has work (rows without skip, all lanes of a row agree)
+    constexpr int NB = 4;
+    Raw ra[NB] = {}, rn[NB] = {};
+    int t = t0 + rg;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+        if (t + 16 * b < t1) load_raw(t + 16 * b, ra[b]);
+    for (; t - row < t1; t += 16 * NB) {
+        const int tn = t + 16 * NB;
+        if (tn - row < t1) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+                if (tn + 16 * b < t1) load_raw(tn + 16 * b, rn[b]);
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+            if (t + 16 * b < t1) update(ra[b]);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) ra[b] = rn[b];
     }
 
     // merge the four rows of each wave (lanes jl, jl+16, jl+32, jl+48 hold the same dims)

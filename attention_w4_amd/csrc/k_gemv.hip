@@ -324,6 +324,10 @@ __global__ __launch_bounds__(256, 2) void k_gemv_stream(GemvArgs a) {
     pro.load(a);
     RowBlock<R, NF> cur, nxt;
     if (rb < nrb) load_block<R, NF>(cur, a.codes, a.scales, rb, G, lane);
+    // residual epilogue: the wave's old values, loaded now (lane r holds row r)
+    // so the epilogue is a plain store instead of a dependent read-modify-write
+    float yold = 0.f, ynext = 0.f;
+    if (EPI == EPI_RESID && rb < nrb && lane < R) yold = a.y[rb * R + lane];
     pro.finish(a, xs, red);
     __syncthreads();
 
@@ -347,6 +351,7 @@ __global__ __launch_bounds__(256, 2) void k_gemv_stream(GemvArgs a) {
     for (; rb < nrb; rb += nw) {
         const bool more = rb + nw < nrb;
         if (kPipe && more) load_block<R, NF>(nxt, a.codes, a.scales, rb + nw, G, lane);
+        if (EPI == EPI_RESID && more && lane < R) ynext = a.y[(rb + nw) * R + lane];
         float acc[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[r] = 0.f;
@@ -374,14 +379,18 @@ __global__ __launch_bounds__(256, 2) void k_gemv_stream(GemvArgs a) {
         }
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[r] = wave_sum_fast(acc[r]);
-        if (lane == 0) {
-            const int r0 = rb * R;
+        const int r0 = rb * R;
+        if (EPI == EPI_RESID) {
+            // lane r adds row r's dot product (acc is uniform across the wave)
+            float mine = 0.f;
+#pragma unroll
+            for (int r = 0; r < R; ++r) mine = lane == r ? acc[r] : mine;
+            if (lane < R) a.y[r0 + lane] = yold + mine;
+            yold = ynext;
+        } else if (lane == 0) {
             if (EPI == EPI_STORE) {
 #pragma unroll
                 for (int r = 0; r < R; ++r) a.y[r0 + r] = acc[r];
-            } else if (EPI == EPI_RESID) {
-#pragma unroll
-                for (int r = 0; r < R; ++r) a.y[r0 + r] += acc[r];
             } else {
 #pragma unroll
                 for (int r = 0; r < R; r += 2) {
