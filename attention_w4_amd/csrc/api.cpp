@@ -4,6 +4,7 @@
 // arena; nothing here allocates device memory.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -125,12 +126,28 @@ int64_t mix_out_cols(const aw4_config* c, char t) {
     return t == 'G' ? (int64_t)c->gdn_v_heads * c->gdn_head_dim : (int64_t)c->attn_q_heads * c->attn_head_dim;
 }
 
-// splits of the attention grid: enough workgroups at long context, and a
-// split never shorter than 64 positions (one load batch per row-group)
-int nsplit_for(int max_ctx) {
-    int n = max_ctx / 64;
-    if (n < 1) n = 1;
+// Cache row layouts written and read by k_attn.hip: the key code + 128 of
+// logical dim e of a row of d bytes sits at byte kv_key_byte(e, d); the 3-bit
+// field (code + 4) of logical value dim e starts at bit kv_value_bit(e, d) of the
+// position's record.
+int kv_key_byte(int e, int d) { return 8 * (d / 32) * ((e & 31) >> 3) + 8 * (e >> 5) + (e & 7); }
+int kv_value_bit(int e, int d) { return 3 * ((d / 16) * (e & 15) + (e >> 4)); }
+uint32_t kv_value_field(const uint32_t* rec, int words, int bit) {
+    const int wi = bit >> 5, off = bit & 31;
+    uint64_t x = rec[wi];
+    if (wi + 1 < words) x |= (uint64_t)rec[wi + 1] << 32;
+    return (uint32_t)(x >> off) & 7u;
+}
+
+// Splits of the attention grid per kv head: one workgroup per compute unit in
+// one round (256 units on gfx950; aw4_create lowers it to the device's count),
+// never more than there are 16-position tiles of capacity.
+int nsplit_for(int max_ctx, int nkv, int cus = 256) {
+    int n = cus / (nkv > 0 ? nkv : 1);
+    const int tiles = (max_ctx + 15) / 16;
+    if (n > tiles) n = tiles;
     if (n > 256) n = 256;
+    if (n < 1) n = 1;
     return n;
 }
 
@@ -200,7 +217,7 @@ uint64_t plan_layout(const aw4_config* c, aw4_model* m, uint8_t* base) {
     // (hlen also sizes the per-token FFN buffers of the verify pass)
     _Float16* hbuf = p.take<_Float16>((uint64_t)hlen * 2);
     _Float16* abuf = p.take<_Float16>((uint64_t)(has_a ? c->attn_q_heads * c->attn_head_dim : 1) * 2);
-    const int nsplit = nsplit_for(c->max_ctx);
+    const int nsplit = nsplit_for(c->max_ctx, c->attn_kv_heads);
     float* part = p.take<float>((uint64_t)(has_a ? c->attn_q_heads : 1) * nsplit * (c->attn_head_dim + 2) * 4);
     float* logits = nullptr;
     float* pv = nullptr;
@@ -658,6 +675,7 @@ int aw4_create(const aw4_config* cfg, void* dev_arena, uint64_t arena_bytes, voi
     m->arena_bytes = arena_bytes;
     m->stream = (hipStream_t)hip_stream;
     plan_layout(cfg, m, m->arena);
+    m->nsplit = nsplit_for(cfg->max_ctx, cfg->attn_kv_heads, prop.multiProcessorCount < 256 ? prop.multiProcessorCount : 256);
     // zero everything once (weights included) so unused tensors are defined
     if (launch_fill_zero(m->arena, need & ~uint64_t(3), m->stream) != hipSuccess) {
         delete m;
@@ -1048,32 +1066,28 @@ int aw4_export_state_kv(aw4_model* m, int32_t layer, int32_t npos, int8_t* kc, u
         return fail(m, AW4_E_INVAL, "not an attention layer");
     const aw4_config* c = &m->cfg;
     if (npos < 0 || npos > c->max_ctx) return fail(m, AW4_E_INVAL, "npos outside [0, max_ctx]");
-    const int nkv = c->attn_kv_heads, d = c->attn_head_dim, NG = d / 32;
+    const int nkv = c->attn_kv_heads, d = c->attn_head_dim, NG = d / 32, VW = 3 * NG;
     LayerBufs& b = m->L[layer];
     HIPCHK(m, hipStreamSynchronize(m->stream));
     std::vector<int8_t> k((size_t)npos * d);
     std::vector<uint16_t> s1((size_t)npos * NG), s2((size_t)npos * NG);
-    std::vector<uint32_t> v((size_t)npos * NG * 3);
-    for (int j = 0; j < nkv; ++j) {
+    std::vector<uint32_t> v((size_t)npos * VW + 1);
+    for (int j = 0; j < nkv && npos > 0; ++j) {
         const int64_t hb = (int64_t)j * c->max_ctx;
-        if (npos == 0) break;
-        HIPCHK(m, hipMemcpy(k.data(), b.kc + hb * d, k.size(), hipMemcpyDeviceToHost));
+        HIPCHK(m, hipMemcpy(k.data(), b.kc + hb * d, (size_t)npos * d, hipMemcpyDeviceToHost));
         HIPCHK(m, hipMemcpy(s1.data(), b.ks + hb * NG, s1.size() * 2, hipMemcpyDeviceToHost));
         HIPCHK(m, hipMemcpy(s2.data(), b.vs + hb * NG, s2.size() * 2, hipMemcpyDeviceToHost));
-        HIPCHK(m, hipMemcpy(v.data(), b.vc + hb * NG * 3, v.size() * 4, hipMemcpyDeviceToHost));
+        HIPCHK(m, hipMemcpy(v.data(), b.vc + hb * VW, (size_t)npos * VW * 4, hipMemcpyDeviceToHost));
         for (int t = 0; t < npos; ++t) {
             const int64_t lo = ((int64_t)t * nkv + j);
-            memcpy(kc + lo * d, k.data() + (size_t)t * d, (size_t)d);
+            const int8_t* kr = k.data() + (size_t)t * d;
+            const uint32_t* rec = v.data() + (size_t)t * VW;
+            for (int e = 0; e < d; ++e) {
+                kc[lo * d + e] = (int8_t)((int)(uint8_t)kr[kv_key_byte(e, d)] - 128);
+                vc[lo * d + e] = (int8_t)((int)kv_value_field(rec, VW, kv_value_bit(e, d)) - 4);
+            }
             memcpy(ks + lo * NG, s1.data() + (size_t)t * NG, (size_t)NG * 2);
             memcpy(vs + lo * NG, s2.data() + (size_t)t * NG, (size_t)NG * 2);
-            for (int g = 0; g < NG; ++g) {
-                const uint32_t* w = v.data() + ((size_t)t * NG + g) * 3;
-                for (int i = 0; i < 32; ++i) {
-                    const int bit = 3 * i, wi = bit >> 5, off = bit & 31;
-                    uint64_t bits = (uint64_t)w[wi] | (wi < 2 ? (uint64_t)w[wi + 1] << 32 : 0ull);
-                    vc[lo * d + g * 32 + i] = (int8_t)((int)((bits >> off) & 7u) - 4);
-                }
-            }
         }
     }
     return AW4_OK;
@@ -1086,36 +1100,35 @@ int aw4_import_state_kv(aw4_model* m, int32_t layer, int32_t npos, const int8_t*
         return fail(m, AW4_E_INVAL, "not an attention layer");
     const aw4_config* c = &m->cfg;
     if (npos < 0 || npos > c->max_ctx) return fail(m, AW4_E_INVAL, "npos outside [0, max_ctx]");
-    const int nkv = c->attn_kv_heads, d = c->attn_head_dim, NG = d / 32;
+    const int nkv = c->attn_kv_heads, d = c->attn_head_dim, NG = d / 32, VW = 3 * NG;
     for (int64_t i = 0; i < (int64_t)npos * nkv * d; ++i)
         if (vc[i] < -3 || vc[i] > 3) return fail(m, AW4_E_INVAL, "V codes must be in -3..3");
     LayerBufs& b = m->L[layer];
     HIPCHK(m, hipStreamSynchronize(m->stream));
     std::vector<int8_t> k((size_t)npos * d);
     std::vector<uint16_t> s1((size_t)npos * NG), s2((size_t)npos * NG);
-    std::vector<uint32_t> v((size_t)npos * NG * 3);
+    std::vector<uint32_t> v((size_t)npos * VW);
     for (int j = 0; j < nkv && npos > 0; ++j) {
+        std::fill(v.begin(), v.end(), 0u);
         for (int t = 0; t < npos; ++t) {
             const int64_t lo = ((int64_t)t * nkv + j);
-            memcpy(k.data() + (size_t)t * d, kc + lo * d, (size_t)d);
+            int8_t* kr = k.data() + (size_t)t * d;
+            uint32_t* rec = v.data() + (size_t)t * VW;
+            for (int e = 0; e < d; ++e) {
+                kr[kv_key_byte(e, d)] = (int8_t)(uint8_t)((int)kc[lo * d + e] + 128);
+                const uint32_t n = (uint32_t)(vc[lo * d + e] + 4) & 7u;
+                const int bit = kv_value_bit(e, d), wi = bit >> 5, off = bit & 31;
+                rec[wi] |= n << off;
+                if (off > 29) rec[wi + 1] |= n >> (32 - off);
+            }
             memcpy(s1.data() + (size_t)t * NG, ks + lo * NG, (size_t)NG * 2);
             memcpy(s2.data() + (size_t)t * NG, vs + lo * NG, (size_t)NG * 2);
-            for (int g = 0; g < NG; ++g) {
-                uint32_t w[3] = {0, 0, 0};
-                for (int i = 0; i < 32; ++i) {
-                    const uint32_t n = (uint32_t)(vc[lo * d + g * 32 + i] + 4) & 7u;
-                    const int bit = 3 * i, wi = bit >> 5, off = bit & 31;
-                    w[wi] |= n << off;
-                    if (off > 29) w[wi + 1] |= n >> (32 - off);
-                }
-                memcpy(v.data() + ((size_t)t * NG + g) * 3, w, 12);
-            }
         }
         const int64_t hb = (int64_t)j * c->max_ctx;
         HIPCHK(m, hipMemcpy(b.kc + hb * d, k.data(), k.size(), hipMemcpyHostToDevice));
         HIPCHK(m, hipMemcpy(b.ks + hb * NG, s1.data(), s1.size() * 2, hipMemcpyHostToDevice));
         HIPCHK(m, hipMemcpy(b.vs + hb * NG, s2.data(), s2.size() * 2, hipMemcpyHostToDevice));
-        HIPCHK(m, hipMemcpy(b.vc + hb * NG * 3, v.data(), v.size() * 4, hipMemcpyHostToDevice));
+        HIPCHK(m, hipMemcpy(b.vc + hb * VW, v.data(), v.size() * 4, hipMemcpyHostToDevice));
     }
     return AW4_OK;
 }

@@ -98,13 +98,13 @@ struct GdnArgs {
 struct AttnArgs {
     int32_t pos_offset;       // the token sits at ctl->pos + pos_offset
     const float* proj;        // [q nq*d | g nq*d | k nkv*d | v nkv*d]
-    int8_t* kc;               // [nkv][max_ctx][d]
+    int8_t* kc;               // [nkv][max_ctx][d] code + 128, dims permuted for the MFMA operand (k_attn.hip)
     uint16_t* ks;             // [nkv][max_ctx][d/32]
-    uint32_t* vc;             // [nkv][max_ctx][d/32][3] packed 3-bit (value i of a group at bits 3i..3i+2)
+    uint32_t* vc;             // [nkv][max_ctx][3 d/32] 3-bit codes + 4, dims permuted (k_attn.hip)
     uint16_t* vs;             // [nkv][max_ctx][d/32]
     const float* signs;       // [d] +-1
     const Ctl* ctl;
-    float* part;              // [nq][nsplit][d + 2]: acc[d], m, l
+    float* part;              // [nq][nsplit][d] acc, then [nq][nsplit][2] (m, l)
     int32_t max_ctx, nq, nkv, d, nsplit;
 };
 

@@ -6,19 +6,43 @@
 // fp16 scale; values v' = H D v / sqrt(d) (Sylvester Hadamard H, random signs
 // D) then 3-bit codes -3..3 per 32 with an fp16 scale.  The same passage says
 // the old dequant path of that cache reached only ~10% of usable bandwidth;
-// here the cache is streamed position-major per kv head by many workgroups.
+// here the cache is streamed position-major per kv head by many workgroups and
+// both products run on the matrix cores.
 //
-// k_attn: grid (split, kv head).  Every workgroup that needs the current token
-// encodes its K and V (quantise K; sign flip, fast Walsh-Hadamard transform,
-// quantise V); split 0 appends them to the cache.  Each workgroup then runs an
-// online softmax over its range of positions for the q heads that share the kv
-// head, accumulating values in the rotated domain, and writes (acc, m, l).
+// Physical layout of one cached position (kv head j, position t):
+//   key row, D bytes of code + 128: logical dim d = 32 g + 8 q + e (scale
+//     group g, lane quarter q, e < 8) sits at byte 8 (D/32) q + 8 g + e, so the
+//     8 keys a lane feeds to one 16x16x32 MFMA for each group are contiguous;
+//   value record, 3 D / 8 bytes as 32-bit words: code + 4 of logical dim d in
+//     bits 3 ((D/16) (d % 16) + d / 16) .. +2, so lane c of a 16x16x16 MFMA
+//     finds the dims c, c + 16, c + 32, ... it needs as one 3 D / 16-bit field;
+//   key and value scales: D/32 fp16 each, by group.
+//
+// k_attn: grid (split, kv head), 8 waves.  The workgroup whose range ends at
+// the current token encodes its K and V (quantise K; sign flip, fast
+// Walsh-Hadamard transform, quantise V) and appends them before anything reads
+// the range.  Each wave takes 16-position tiles: scores S^T (16 positions x 16
+// query-head slots) = sum over groups of key scale x (K_g Q_g^T), on
+// 16x16x32 f16 MFMAs with exact int8 keys and q split into fp16 hi + lo parts;
+// an online softmax per head; then O^T += V^T P'^T on 16x16x16 f16 MFMAs with
+// exact codes and the value scale folded into P' (fp16 hi + lo again).  The
+// score layout a lane holds (one head, four positions) is the B-operand layout
+// of the second product, so P never leaves registers.  Waves merge through
+// LDS; each split writes (acc, m, l) per query head.
 // k_combine: per q head, merges the splits (log-sum-exp), undoes the rotation
 // once (D H acc / sqrt(d)), applies the output gate sigmoid(g) and emits fp16.
 #include "aw4_internal.h"
 
 namespace aw4 {
 namespace {
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 8;                    // waves per attention workgroup
+constexpr int kTile = 16;                    // positions per wave tile; split lengths are multiples
 
 __device__ __forceinline__ float sigmoidf_(float v) { return 1.0f / (1.0f + __expf(-v)); }
 
@@ -30,9 +54,14 @@ __device__ __forceinline__ float seg32_max(float v) {
 }
 
 __device__ __forceinline__ void split_range(int npos, int nsplit, int& pps, int& used) {
-    int p = (npos + nsplit - 1) / nsplit;
-    pps = p < 64 ? 64 : p;
+    const int p = (npos + nsplit - 1) / nsplit;
+    pps = (p + kTile - 1) / kTile * kTile;
     used = (npos + pps - 1) / pps;
+}
+
+template <int D>
+__device__ __forceinline__ int k_byte(int d) {
+    return 8 * (D / 32) * ((d & 31) >> 3) + 8 * (d >> 5) + (d & 7);
 }
 
 // in-place Sylvester fast Walsh-Hadamard transform of v[0..D) by D/2 threads
@@ -50,48 +79,36 @@ __device__ void fwht(float* v) {
     }
 }
 
-// DPP sum inside each 16-lane row (every lane of the row gets the row sum)
-#define AW4_DPP_ADD(v, ctrl)                                                                        \
-    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), ctrl, \
-                                                               0xF, 0xF, true))
-__device__ __forceinline__ float row16_sum(float v) {
-    AW4_DPP_ADD(v, 0xB1);    // quad_perm [1,0,3,2]
-    AW4_DPP_ADD(v, 0x4E);    // quad_perm [2,3,0,1]
-    AW4_DPP_ADD(v, 0x141);   // row_half_mirror
-    AW4_DPP_ADD(v, 0x140);   // row_mirror
-    return v;
+// eight offset-binary bytes u = b + 128 (little endian in x0, x1) -> the eight
+// exact fp16 values b: 0x6400 | u is the half 1024 + u
+__device__ __forceinline__ h8 u8x8_to_h8(uint32_t x0, uint32_t x1) {
+    const h2 bias = {(_Float16)-1152.f, (_Float16)-1152.f};
+    const h2 a = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, x0, 0x04010400u)) + bias;
+    const h2 b = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, x0, 0x04030402u)) + bias;
+    const h2 c = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, x1, 0x04010400u)) + bias;
+    const h2 d = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, x1, 0x04030402u)) + bias;
+    const h8 r = {a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+    return r;
 }
 
-// merge online-softmax states (m, l, acc) b into a
-__device__ __forceinline__ float merge_scale(float& m, float mb, float& fa) {
-    const float M = fmaxf(m, mb);
-    fa = m == -INFINITY ? 0.f : __expf(m - M);
-    const float fb = mb == -INFINITY ? 0.f : __expf(mb - M);
-    m = M;
-    return fb;
-}
-
-// Lane layout: a 16-lane row of a wave owns one cached position at a time,
-// lane j of the row holds dims [DL*j, DL*j + DL) (DL = D/16).  The 16 rows of a
-// workgroup (4 waves x 4 rows) walk the split's positions round robin, two
-// positions per row in flight; each keeps its own online softmax state for the
-// G query heads; rows and waves are merged at the end.
 template <int D, int G>
-__global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
-    constexpr int NG = D / 32;    // scale groups
-    constexpr int DL = D / 16;    // dims per lane: 16 (D=256) or 4 (D=64)
-    __shared__ float qs[G][D];
+__global__ __launch_bounds__(512, 1) void k_attn(AttnArgs a) {
+    constexpr int NG = D / 32;          // scale groups
+    constexpr int NB = D / 16;          // 16-dim blocks of the value product
+    constexpr int VW = 3 * NG;          // 32-bit words per value record
+    constexpr int VB = 3 * NB;          // value bits per lane slot
+    constexpr int HPL = NG / 2;         // staged scale halves per lane (NG >= 2)
+    static_assert(G >= 1 && G <= 16 && NG >= 2, "shape");
+
     __shared__ float vt[D];
-    __shared__ int8_t kcur[D];
-    __shared__ int8_t vcur[D];
-    __shared__ float kscur[NG], vscur[NG];
-    __shared__ uint16_t ksb[NG], vsb[NG];
-    __shared__ float mm[4][G], ll[4][G];
-    __shared__ float aa[4][G][D];
+    __shared__ uint8_t vq[D];
+    __shared__ float stile[kWaves][2][NG][kTile];      // per wave: key / value scales [group][position]
+    __shared__ float mo[kWaves][G][D];                  // wave results
+    __shared__ float mm[kWaves][G], ll[kWaves][G];
 
     const int split = blockIdx.x, j = blockIdx.y, tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int row = lane >> 4, jl = lane & 15;
+    const int lane = tid & 63, w = tid >> 6;
+    const int c = lane & 15, q = lane >> 4;
     const int pos = a.ctl->pos + a.pos_offset;
     const int npos = pos + 1;
     int pps, used;
@@ -99,269 +116,344 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
     if (split >= used) return;
     const int t0 = split * pps;
     const int t1 = min(npos, t0 + pps);
-    const bool has_cur = (t1 == npos);
     const int64_t hbase = (int64_t)j * a.max_ctx;
-
-    // queries of the G heads sharing kv head j, pre-scaled by 1/sqrt(D)
     const float qscale = 1.0f / sqrtf((float)D);
-    {
-        constexpr int N4 = G * D / 4;
-        const float4* src = (const float4*)(a.proj + (int64_t)(j * G) * D);
-#pragma unroll
-        for (int i = 0; i < (N4 + 255) / 256; ++i) {
-            const int idx = tid + 256 * i;
-            if (idx < N4) {
-                float4 q = src[idx];
-                float* dst = &qs[0][0] + 4 * idx;
-                dst[0] = q.x * qscale;
-                dst[1] = q.y * qscale;
-                dst[2] = q.z * qscale;
-                dst[3] = q.w * qscale;
-            }
-        }
-    }
 
-    if (split == 0 || has_cur) {
+    if (t1 == npos) {
+        // append the current token (this workgroup is the only one whose range holds it)
         const float* kp = a.proj + 2LL * a.nq * D + (int64_t)j * D;
         const float* vp = kp + (int64_t)a.nkv * D;
-        // K: int8 per 32
-        {
-            const float kv = tid < D ? kp[tid] : 0.f;
+        const int64_t prow = hbase + pos;
+        if (tid < D) {
+            const float kv = kp[tid];
             const float am = seg32_max(fabsf(kv));
             const _Float16 sh = (_Float16)(am / 127.0f);
             const float sc = (float)sh;
-            float c = sc == 0.f ? 0.f : rintf(kv / sc);
-            c = fminf(fmaxf(c, -127.f), 127.f);
-            if (tid < D) {
-                kcur[tid] = (int8_t)c;
-                if ((tid & 31) == 0) { kscur[tid >> 5] = sc; ksb[tid >> 5] = __builtin_bit_cast(uint16_t, sh); }
-                vt[tid] = vp[tid] * a.signs[tid];
-            }
+            float cd = sc == 0.f ? 0.f : rintf(kv / sc);
+            cd = fminf(fmaxf(cd, -127.f), 127.f);
+            a.kc[prow * D + k_byte<D>(tid)] = (int8_t)(uint8_t)((int)cd + 128);
+            if ((tid & 31) == 0) a.ks[prow * NG + (tid >> 5)] = __builtin_bit_cast(uint16_t, sh);
+            vt[tid] = vp[tid] * a.signs[tid];
         }
         __syncthreads();
         fwht<D>(vt);
-        {
-            const float vr = tid < D ? vt[tid] * qscale : 0.f;   // 1/sqrt(D): exact power of two here
+        if (tid < D) {
+            const float vr = vt[tid] * qscale;   // 1/sqrt(D): a power of two for D = 64, 256
             const float am = seg32_max(fabsf(vr));
             const _Float16 sh = (_Float16)(am / 3.0f);
             const float sc = (float)sh;
-            float c = sc == 0.f ? 0.f : rintf(vr / sc);
-            c = fminf(fmaxf(c, -3.f), 3.f);
-            if (tid < D) {
-                vcur[tid] = (int8_t)c;
-                if ((tid & 31) == 0) { vscur[tid >> 5] = sc; vsb[tid >> 5] = __builtin_bit_cast(uint16_t, sh); }
-            }
+            float cd = sc == 0.f ? 0.f : rintf(vr / sc);
+            cd = fminf(fmaxf(cd, -3.f), 3.f);
+            vq[tid] = (uint8_t)((int)cd + 4);
+            if ((tid & 31) == 0) a.vs[prow * NG + (tid >> 5)] = __builtin_bit_cast(uint16_t, sh);
         }
         __syncthreads();
-        if (split == 0) {
-            const int64_t prow = hbase + pos;
-            if (tid < D) a.kc[prow * D + tid] = kcur[tid];
-            if (tid < NG) {
-                a.ks[prow * NG + tid] = ksb[tid];
-                a.vs[prow * NG + tid] = vsb[tid];
-                uint32_t w[3] = {0u, 0u, 0u};
-                for (int i = 0; i < 32; ++i) {
-                    const uint32_t n = (uint32_t)(vcur[tid * 32 + i] + 4) & 7u;
-                    const int bit = 3 * i, wi = bit >> 5, off = bit & 31;
-                    w[wi] |= n << off;
-                    if (off > 29) w[wi + 1] |= n >> (32 - off);
-                }
-                uint32_t* dst = a.vc + (prow * NG + tid) * 3;
-                dst[0] = w[0];
-                dst[1] = w[1];
-                dst[2] = w[2];
+        if (tid < VW) {
+            // word tid of the record: 3-bit slots f = NB (d % 16) + d / 16 overlapping its bits
+            uint32_t word = 0;
+            const int lo = 32 * tid;
+            const int f0 = lo / 3 > 0 ? lo / 3 - 1 : 0;
+            const int f1 = min(D - 1, (lo + 31) / 3);
+            for (int f = f0; f <= f1; ++f) {
+                const int d = 16 * (f % NB) + f / NB;
+                const uint32_t n = vq[d];
+                const int s = 3 * f - lo;
+                if (s >= 32 || s <= -3) continue;
+                word |= s >= 0 ? n << s : n >> (-s);
             }
+            a.vc[prow * VW + tid] = word;
         }
+        __threadfence_block();
+        __syncthreads();
     }
-    __syncthreads();
 
-    // this lane's query slices
-    const int e0 = jl * DL;
-    const int grp = e0 >> 5;
-    float q[G][DL];
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int e = 0; e < DL; ++e) q[g][e] = qs[g][e0 + e];
-
-    float m[G], l[G], acc[G][DL];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        m[g] = -INFINITY;
-        l[g] = 0.f;
-#pragma unroll
-        for (int e = 0; e < DL; ++e) acc[g][e] = 0.f;
-    }
-    // 3-bit fields of this lane's dims: group grp, values (e0 & 31) .. +DL-1
-    const int bit0 = 3 * (e0 & 31);
-    const int wi = bit0 >> 5, woff = bit0 & 31;
-    const int rg = wave * 4 + row;   // row-group 0..15
-
-    // Raw cache words of one position for this lane; dequantised at use so
-    // that the loads of a whole batch stay in flight together (the current
-    // token comes from the LDS copy: split 0 may still be writing its entry).
+    // raw words of one tile for this lane
     struct Raw {
-        uint32_t k[DL / 4];
-        uint32_t vlo, vhi;
-        uint16_t ks, vs;
-        bool cur;
+        uint4 k[NG / 2];           // key bytes of position tile0 + c, quarter q
+        uint32_t vlo[4], vhi[4];   // value words of positions tile0 + 4 q + r
+        uint32_t sc[2];            // HPL staged scale halves
+        bool sv;                   // their position is inside the range
     };
-    auto load_raw = [&](int t, Raw& r) {
-        r.cur = (t == pos);
-        if (r.cur) return;
-        const int64_t prow = hbase + t;
-        r.ks = a.ks[prow * NG + grp];
-        r.vs = a.vs[prow * NG + grp];
-        const int8_t* kr = a.kc + prow * D + e0;
-        if (DL == 16) {
-            const uint4 kw = *(const uint4*)kr;
-            r.k[0] = kw.x; r.k[1] = kw.y; r.k[2] = kw.z; r.k[3] = kw.w;
-        } else {
-            r.k[0] = *(const uint32_t*)kr;
-        }
-        const uint32_t* vg = a.vc + (prow * NG + grp) * 3;
-        r.vlo = vg[wi];
-        r.vhi = wi < 2 ? vg[wi + 1] : 0u;
-    };
-    auto update = [&](const Raw& r) {
-        float kf[DL], vf[DL];
-        if (r.cur) {
+    const int vbit0 = VB * c;
+    const int vw0 = vbit0 >> 5, vsh = vbit0 & 31;
+    const int vw1 = vw0 + 1 < VW ? vw0 + 1 : VW - 1;
+    // scale staging: lanes 0..31 key scales, 32..63 value scales; HPL halves each
+    const int ssel = lane >> 5;
+    const int sidx = (lane & 31) * HPL;
+    const int spp = sidx / NG, sg0 = sidx % NG;
+    const uint16_t* sbase = ssel ? a.vs : a.ks;
+
+    // per-head bases; offsets inside a head fit 32 bits (max_ctx * D < 2^31)
+    const int8_t* khead = a.kc + hbase * D;
+    const uint32_t* vhead = a.vc + hbase * VW;
+    const uint16_t* shead = sbase + hbase * NG;
+    auto load = [&](int tile0, Raw& r) {
+        {
+            const int p = min(tile0 + c, t1 - 1);
+            const uint4* kp = (const uint4*)(khead + (p * D + 8 * NG * q));
 #pragma unroll
-            for (int e = 0; e < DL; ++e) {
-                kf[e] = (float)kcur[e0 + e] * kscur[grp];
-                vf[e] = (float)vcur[e0 + e] * vscur[grp];
+            for (int i = 0; i < NG / 2; ++i) r.k[i] = kp[i];
+        }
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const uint32_t* rec = vhead + min(tile0 + 4 * q + rr, t1 - 1) * VW;
+            r.vlo[rr] = rec[vw0];
+            r.vhi[rr] = rec[vw1];
+        }
+        {
+            const int p = tile0 + spp;
+            const uint16_t* sp = shead + (min(p, t1 - 1) * NG + sg0);
+            if (HPL == 4) {
+                const uint2 v = *(const uint2*)sp;
+                r.sc[0] = v.x;
+                r.sc[1] = v.y;
+            } else if (HPL == 2) {
+                r.sc[0] = *(const uint32_t*)sp;
+                r.sc[1] = 0u;
+            } else {
+                r.sc[0] = *sp;
+                r.sc[1] = 0u;
             }
-        } else {
-            const float ksc = (float)__builtin_bit_cast(_Float16, r.ks);
-            const float vsc = (float)__builtin_bit_cast(_Float16, r.vs);
-#pragma unroll
-            for (int e = 0; e < DL; ++e) kf[e] = (float)(int8_t)(r.k[e >> 2] >> (8 * (e & 3))) * ksc;
-            const uint64_t bits = (((uint64_t)r.vhi << 32) | r.vlo) >> woff;
-#pragma unroll
-            for (int e = 0; e < DL; ++e) vf[e] = (float)((int)((bits >> (3 * e)) & 7u) - 4) * vsc;
-        }
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            float p = 0.f;
-#pragma unroll
-            for (int e = 0; e < DL; ++e) p += q[g][e] * kf[e];
-            const float sc = row16_sum(p);
-            const float mn = fmaxf(m[g], sc);
-            const float corr = __expf(m[g] - mn);
-            const float pe = __expf(sc - mn);
-            l[g] = l[g] * corr + pe;
-#pragma unroll
-            for (int e = 0; e < DL; ++e) acc[g][e] = acc[g][e] * corr + pe * vf[e];
-            m[g] = mn;
+            r.sv = p < t1;
         }
     };
-    // positions t0 + rg + 16 k, in batches of NB per row-group with the next
-    // batch's loads issued before the current one is used; a wave runs while any
-    // of its rows has work (rows without skip, all lanes of a row agree)
-    constexpr int NB = 4;
-    Raw ra[NB] = {}, rn[NB] = {};
-    int t = t0 + rg;
+
+    const int ntiles = (t1 - t0 + kTile - 1) / kTile;
+    Raw cur = {}, nxt = {};
+    if (w < ntiles) load(t0 + w * kTile, cur);   // in flight while q is read
+
+    // query fragments (B operand of the score product): head c, dims 32 g + 8 q + e,
+    // pre-scaled by 1/sqrt(D), as fp16 hi + lo so the scores keep fp32 accuracy
+    h8 qh[NG], ql[NG];
+    {
+        const float* qp = a.proj + (int64_t)(j * G + (c < G ? c : 0)) * D + 8 * q;
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
-        if (t + 16 * b < t1) load_raw(t + 16 * b, ra[b]);
-    for (; t - row < t1; t += 16 * NB) {
-        const int tn = t + 16 * NB;
-        if (tn - row < t1) {
+        for (int g = 0; g < NG; ++g) {
+            float4 x0 = make_float4(0.f, 0.f, 0.f, 0.f), x1 = x0;
+            if (c < G) {
+                x0 = *(const float4*)(qp + 32 * g);
+                x1 = *(const float4*)(qp + 32 * g + 4);
+            }
+            const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
-            for (int b = 0; b < NB; ++b)
-                if (tn + 16 * b < t1) load_raw(tn + 16 * b, rn[b]);
+            for (int e = 0; e < 8; ++e) {
+                const float v = xs[e] * qscale;
+                const _Float16 hi = (_Float16)v;
+                qh[g][e] = hi;
+                ql[g][e] = (_Float16)(v - (float)hi);
+            }
         }
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-            if (t + 16 * b < t1) update(ra[b]);
-#pragma unroll
-        for (int b = 0; b < NB; ++b) ra[b] = rn[b];
     }
 
-    // merge the four rows of each wave (lanes jl, jl+16, jl+32, jl+48 hold the same dims)
+    float m = -INFINITY, l = 0.f;
+    f4 o[NB];
 #pragma unroll
-    for (int sh = 16; sh <= 32; sh <<= 1) {
+    for (int b = 0; b < NB; ++b) o[b] = f4{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](int tile0, const Raw& r) {
+        // stage this tile's scales, transposed to [group][position]; positions
+        // past the range get zero scales
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            const float mb = __shfl_xor(m[g], sh, 64);
-            const float lb = __shfl_xor(l[g], sh, 64);
-            float fa;
-            const float fb = merge_scale(m[g], mb, fa);
-            l[g] = l[g] * fa + lb * fb;
+        for (int h = 0; h < HPL; ++h)
+            stile[w][ssel][sg0 + h][spp] =
+                r.sv ? (float)__builtin_bit_cast(_Float16, (uint16_t)(r.sc[h >> 1] >> (16 * (h & 1)))) : 0.f;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+        // scores of head c at positions tile0 + 4 q + rr
+        float s[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int e = 0; e < DL; ++e) acc[g][e] = acc[g][e] * fa + __shfl_xor(acc[g][e], sh, 64) * fb;
+        for (int g = 0; g < NG; ++g) {
+            const uint4 kw = r.k[g >> 1];
+            const h8 kf = (g & 1) ? u8x8_to_h8(kw.z, kw.w) : u8x8_to_h8(kw.x, kw.y);
+            f4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qh[g], (f4{0.f, 0.f, 0.f, 0.f}), 0, 0, 0);
+            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, ql[g], d, 0, 0, 0);
+            const f4 ks = *(const f4*)&stile[w][0][g][4 * q];
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) s[rr] += ks[rr] * d[rr];
+        }
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+            if (tile0 + 4 * q + rr >= t1) s[rr] = -INFINITY;
+
+        // online softmax for head c (the four quarters hold the tile's 16 positions)
+        float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float mn = fmaxf(m, mx);
+        const float corr = __expf(m - mn);
+        float p[4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) p[rr] = __expf(s[rr] - mn);
+        l = l * corr + ((p[0] + p[1]) + (p[2] + p[3]));
+        m = mn;
+        if (__builtin_amdgcn_ballot_w64(corr != 1.0f)) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) o[b] *= corr;
+        }
+
+        // O^T += V^T P'^T, 16 dims per MFMA, with P' = p x value scale of the
+        // position's group in fp32, split into fp16 hi + lo (round toward zero;
+        // the lo part carries the residual) so that the product keeps fp32
+        // accuracy; the codes themselves are exact halves.  The lane's value slot
+        // of position rr holds dims c + 16 b at bits 3 b.
+        uint32_t lo32[4], mid[4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const uint64_t win = ((((uint64_t)r.vhi[rr]) << 32) | r.vlo[rr]) >> vsh;
+            lo32[rr] = (uint32_t)win;
+            mid[rr] = (uint32_t)(win >> 16);
+        }
+        // fields of positions (0, 1) and (2, 3) five at a time: the low 16 bits
+        // of each position's shifted slot side by side in one word
+        uint32_t zc[2][4];
+#pragma unroll
+        for (int pr = 0; pr < 2; ++pr) {
+            const int ra = 2 * pr, rb = 2 * pr + 1;
+            zc[pr][0] = __builtin_amdgcn_perm(lo32[rb], lo32[ra], 0x05040100u);               // fields 0..4
+            if (NB > 5) zc[pr][1] = __builtin_amdgcn_perm(lo32[rb] >> 15, lo32[ra] >> 15, 0x05040100u);  // 5..9
+            if (NB > 10) zc[pr][2] = __builtin_amdgcn_perm(mid[rb] >> 14, mid[ra] >> 14, 0x05040100u);  // 10..14
+            if (NB > 15) zc[pr][3] = __builtin_amdgcn_perm(mid[rb] >> 29, mid[ra] >> 29, 0x05040100u);  // 15
+        }
+        const h2 bias = {(_Float16)-1028.f, (_Float16)-1028.f};
+        // (x & mask) | 0x6400 halves in one v_and_or_b32: the mask in an SGPR and
+        // the constant in a VGPR (a gfx9 VOP3 takes no literal operands)
+        uint32_t m7, h64;
+        asm volatile("s_mov_b32 %0, 0x70007" : "=s"(m7));
+        asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(h64));
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            const f4 vs = *(const f4*)&stile[w][1][g][4 * q];
+            float pg[4];
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) pg[rr] = p[rr] * vs[rr];
+            const h2 hi01 = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(pg[0], pg[1]));
+            const h2 hi23 = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(pg[2], pg[3]));
+            const h2 lo01 = __builtin_bit_cast(
+                h2, __builtin_amdgcn_cvt_pkrtz(pg[0] - (float)hi01[0], pg[1] - (float)hi01[1]));
+            const h2 lo23 = __builtin_bit_cast(
+                h2, __builtin_amdgcn_cvt_pkrtz(pg[2] - (float)hi23[0], pg[3] - (float)hi23[1]));
+            const h4 phi = {hi01[0], hi01[1], hi23[0], hi23[1]};
+            const h4 plo = {lo01[0], lo01[1], lo23[0], lo23[1]};
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb) {
+                const int b = 2 * g + bb;
+                const int ch = b / 5, sh3 = 3 * (b % 5);
+                const h2 v01 = __builtin_bit_cast(h2, ((zc[0][ch] >> sh3) & m7) | h64) + bias;
+                const h2 v23 = __builtin_bit_cast(h2, ((zc[1][ch] >> sh3) & m7) | h64) + bias;
+                const h4 va = {v01[0], v01[1], v23[0], v23[1]};
+                o[b] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, phi, o[b], 0, 0, 0);
+                o[b] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, plo, o[b], 0, 0, 0);
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+    };
+
+    {
+        // the next tile's loads are issued before the current tile is used; the
+        // last round re-reads the final tile so every round issues the same loads
+        // two register sets used in turn (no copies between rounds)
+        for (int tt = w; tt < ntiles; tt += 2 * kWaves) {
+            load(t0 + min(tt + kWaves, ntiles - 1) * kTile, nxt);
+            compute(t0 + tt * kTile, cur);
+            if (tt + kWaves >= ntiles) break;
+            load(t0 + min(tt + 2 * kWaves, ntiles - 1) * kTile, cur);
+            compute(t0 + (tt + kWaves) * kTile, nxt);
         }
     }
-    if (row == 0) {
+    // the four quarters hold partial sums of l for head c
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+
+    // every wave posts (m, l, acc) of its heads; lane (c, q) holds head c,
+    // dims 16 b + 4 q + rr; then one pass merges the waves per output
+    if (c < G) {
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            if (jl == 0) { mm[wave][g] = m[g]; ll[wave][g] = l[g]; }
-#pragma unroll
-            for (int e = 0; e < DL; ++e) aa[wave][g][e0 + e] = acc[g][e];
+        for (int b = 0; b < NB; ++b) *(f4*)&mo[w][c][16 * b + 4 * q] = o[b];
+        if (q == 0) {
+            mm[w][c] = m;
+            ll[w][c] = l;
         }
     }
     __syncthreads();
-    for (int idx = tid; idx < G * D; idx += 256) {
+    float* mlp = a.part + (int64_t)a.nq * a.nsplit * D;
+    for (int idx = tid; idx < G * D; idx += 64 * kWaves) {
         const int g = idx / D, e = idx % D;
-        const float M = fmaxf(fmaxf(mm[0][g], mm[1][g]), fmaxf(mm[2][g], mm[3][g]));
-        float L = 0.f, A = 0.f;
-        if (M != -INFINITY) {
+        float M = mm[0][g];
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const float f = mm[w][g] == -INFINITY ? 0.f : __expf(mm[w][g] - M);
-                L += ll[w][g] * f;
-                A += aa[w][g][e] * f;
-            }
+        for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, mm[ww][g]);
+        float L = 0.f, A = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) {
+            const float f = mm[ww][g] == -INFINITY ? 0.f : __expf(mm[ww][g] - M);
+            L += ll[ww][g] * f;
+            A += mo[ww][g][e] * f;
         }
-        float* dst = a.part + ((int64_t)(j * G + g) * a.nsplit + split) * (D + 2);
-        dst[e] = A;
-        if (e == 0) { dst[D] = M; dst[D + 1] = L; }
+        const int64_t row = (int64_t)(j * G + g) * a.nsplit + split;
+        a.part[row * D + e] = A;
+        if (e == 0) {
+            mlp[2 * row] = M;
+            mlp[2 * row + 1] = L;
+        }
     }
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
+__global__ __launch_bounds__(1024) void k_combine(CombineArgs a) {
+    constexpr int LR = D / 4;            // lanes per split row, a float4 each
+    constexpr int ROWS = 1024 / LR;      // split rows in flight
+    __shared__ float wts[256];
+    __shared__ float red[ROWS][D];
     __shared__ float v[D];
-    __shared__ float wsum[256];
-    __shared__ float red[8];
+    __shared__ float rmax[16], rsum[16];
     const int i = blockIdx.x, tid = threadIdx.x;
     const int pos = a.ctl->pos + a.pos_offset;
     int pps, used;
     split_range(pos + 1, a.nsplit, pps, used);
-    const float* base = a.part + (int64_t)i * a.nsplit * (D + 2);
+    const float* base = a.part + (int64_t)i * a.nsplit * D;
+    const float* mlp = a.part + (int64_t)a.nq * a.nsplit * D + 2LL * i * a.nsplit;
     // split weights exp(m_s - M) and the normaliser, one split per thread
     float ms = -INFINITY, ls = 0.f;
     if (tid < used) {
-        ms = base[(int64_t)tid * (D + 2) + D];
-        ls = base[(int64_t)tid * (D + 2) + D + 1];
+        ms = mlp[2 * tid];
+        ls = mlp[2 * tid + 1];
     }
     float M = ms;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-    if ((tid & 63) == 0) red[tid >> 6] = M;
+    if ((tid & 63) == 0) rmax[tid >> 6] = M;
     __syncthreads();
-    M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    const float w = (tid < used && ms != -INFINITY) ? __expf(ms - M) : 0.f;
-    wsum[tid] = w;
-    float L = w * ls;
+    M = rmax[0];
+#pragma unroll
+    for (int k = 1; k < 16; ++k) M = fmaxf(M, rmax[k]);
+    const float wgt = tid < used ? __expf(ms - M) : 0.f;
+    if (tid < 256) wts[tid] = wgt;
+    float L = wgt * ls;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o, 64);
+    if ((tid & 63) == 0) rsum[tid >> 6] = L;
     __syncthreads();
-    if ((tid & 63) == 0) red[4 + (tid >> 6)] = L;
-    __syncthreads();
-    L = red[4] + red[5] + red[6] + red[7];
-    if (tid < D) {
-        float A = 0.f;
-        int s = 0;
-        for (; s + 4 <= used; s += 4) {
-            const float p0 = base[(int64_t)(s + 0) * (D + 2) + tid];
-            const float p1 = base[(int64_t)(s + 1) * (D + 2) + tid];
-            const float p2 = base[(int64_t)(s + 2) * (D + 2) + tid];
-            const float p3 = base[(int64_t)(s + 3) * (D + 2) + tid];
-            A += p0 * wsum[s] + p1 * wsum[s + 1] + p2 * wsum[s + 2] + p3 * wsum[s + 3];
+    L = 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) L += rsum[k];
+    {
+        const int row = tid / LR, e4 = tid % LR;
+        f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < 256 / ROWS; ++k) {
+            const int s = row + k * ROWS;
+            if (s < used) acc += wts[s] * *(const f4*)(base + (int64_t)s * D + 4 * e4);
         }
-        for (; s < used; ++s) A += base[(int64_t)s * (D + 2) + tid] * wsum[s];
-        v[tid] = A / L;
+        *(f4*)&red[row][4 * e4] = acc;
+    }
+    __syncthreads();
+    if (tid < D) {
+        float t = 0.f;
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) t += red[r][tid];
+        v[tid] = t / L;
     }
     __syncthreads();
     fwht<D>(v);
@@ -376,7 +468,8 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
     const int G = a.nq / a.nkv;
-    const dim3 grid(a.nsplit, a.nkv), block(256);
+    if (a.nsplit < 1 || a.nsplit > 256) return hipErrorInvalidValue;
+    const dim3 grid(a.nsplit, a.nkv), block(64 * kWaves);
 #define AW4_ATTN_CASE(DD, GG)                                                   \
     if (a.d == DD && G == GG) {                                                 \
         hipLaunchKernelGGL((k_attn<DD, GG>), grid, block, 0, s, a);             \
@@ -397,9 +490,9 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
-    if (a.nsplit > 256) return hipErrorInvalidValue;
-    if (a.d == 256) hipLaunchKernelGGL(k_combine<256>, dim3(a.nq), dim3(256), 0, s, a);
-    else if (a.d == 64) hipLaunchKernelGGL(k_combine<64>, dim3(a.nq), dim3(256), 0, s, a);
+    if (a.nsplit < 1 || a.nsplit > 256) return hipErrorInvalidValue;
+    if (a.d == 256) hipLaunchKernelGGL(k_combine<256>, dim3(a.nq), dim3(1024), 0, s, a);
+    else if (a.d == 64) hipLaunchKernelGGL(k_combine<64>, dim3(a.nq), dim3(1024), 0, s, a);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }
