@@ -40,6 +40,31 @@ __device__ __forceinline__ void dq_dot8(uint32_t w, uint4 xv, float& ea, float& 
     eb = __builtin_amdgcn_fdot2(p3, as_h2(xv.w), eb, false);
 }
 
+// The same with the constants where a VOP3 can read them (gfx9 VOP3 encodings
+// take no literals): masks in SGPRs and the exponent pattern in a VGPR, so each
+// (w & mask) | 0x6400 pair is one v_and_or_b32 instead of an and plus an or.
+struct NibK {
+    uint32_t lo, hi, e;
+    __device__ __forceinline__ NibK() {
+        asm volatile("s_mov_b32 %0, 0xf000f" : "=s"(lo));
+        asm volatile("s_mov_b32 %0, 0xf000f0" : "=s"(hi));
+        asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(e));
+    }
+};
+__device__ __forceinline__ void dq_dot8(uint32_t w, uint4 xv, float& ea, float& eb, const NibK& k) {
+    const h2 off_lo = {(_Float16)1032.0f, (_Float16)1032.0f};
+    const h2 off_hi = {(_Float16)1152.0f, (_Float16)1152.0f};
+    const uint32_t w8 = w >> 8;
+    const h2 p0 = as_h2((w & k.lo) | k.e) - off_lo;
+    const h2 p1 = as_h2((w & k.hi) | k.e) - off_hi;
+    const h2 p2 = as_h2((w8 & k.lo) | k.e) - off_lo;
+    const h2 p3 = as_h2((w8 & k.hi) | k.e) - off_hi;
+    ea = __builtin_amdgcn_fdot2(p0, as_h2(xv.x), ea, false);
+    eb = __builtin_amdgcn_fdot2(p1, as_h2(xv.y), eb, false);
+    ea = __builtin_amdgcn_fdot2(p2, as_h2(xv.z), ea, false);
+    eb = __builtin_amdgcn_fdot2(p3, as_h2(xv.w), eb, false);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
@@ -226,14 +251,29 @@ struct Prologue<K, PRO_NORM> {
 template <int K>
 struct Prologue<K, PRO_GATED> {
     static constexpr int E = K >= 256 ? K / 256 : 1;
-    float ov[E], zv[E];
+    static constexpr int V4 = E % 4 == 0 ? E / 4 : 0;   // float4 loads per array when E allows
+    float ov[E], zv[E], wv[E];
     __device__ __forceinline__ void load(const GemvArgs& a) {
         const int base = threadIdx.x * E;
         const bool live = base < K;   // K < 256: threads past K idle (whole waves)
+        const int c0 = live ? base % a.gated_d : 0;
+        if (V4) {
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            ov[e] = live ? a.x[base + e] : 0.f;
-            zv[e] = live ? a.z[base + e] : 0.f;
+            for (int i = 0; i < V4; ++i) {
+                const float4 o = ((const float4*)(a.x + base))[i];
+                const float4 z = ((const float4*)(a.z + base))[i];
+                const float4 w = ((const float4*)(a.nw + c0))[i];
+                ov[4 * i] = o.x; ov[4 * i + 1] = o.y; ov[4 * i + 2] = o.z; ov[4 * i + 3] = o.w;
+                zv[4 * i] = z.x; zv[4 * i + 1] = z.y; zv[4 * i + 2] = z.z; zv[4 * i + 3] = z.w;
+                wv[4 * i] = w.x; wv[4 * i + 1] = w.y; wv[4 * i + 2] = w.z; wv[4 * i + 3] = w.w;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                ov[e] = live ? a.x[base + e] : 0.f;
+                zv[e] = live ? a.z[base + e] : 0.f;
+                wv[e] = live ? a.nw[c0 + e] : 0.f;
+            }
         }
     }
     __device__ __forceinline__ void finish(const GemvArgs& a, _Float16* xs, float*) {
@@ -245,12 +285,11 @@ struct Prologue<K, PRO_GATED> {
         const int tph = d / E;   // threads per head (power of two, <= 64)
         for (int m = tph >> 1; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
         const float r = 1.0f / sqrtf(ss / (float)d + a.eps);
-        const int c0 = base % d;
         if (base < K) {
 #pragma unroll
             for (int e = 0; e < E; ++e) {
                 const float silu = zv[e] * sigmoidf_(zv[e]);
-                xs[base + e] = (_Float16)(ov[e] * r * a.nw[c0 + e] * silu);
+                xs[base + e] = (_Float16)(ov[e] * r * wv[e] * silu);
             }
         }
     }
@@ -289,6 +328,8 @@ struct Prologue<K, PRO_LOADH> {
 // overlaps the input normalisation and the cross-lane reductions.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+constexpr int kStreamMaxPer = 10;   // row blocks per wave the pipelined path unrolls
+
 template <int R, int NF>
 struct RowBlock {
     u32x4 c[NF];
@@ -313,23 +354,28 @@ __global__ __launch_bounds__(256, 2) void k_gemv_stream(GemvArgs a) {
     float* red = (float*)smem;
     _Float16* xs = (_Float16*)(smem + 64);
     constexpr int G = 64 * NF / R;
-    // double-buffer the codes across row blocks only while the buffers stay small
+    // pipeline the codes across row blocks only while the buffers stay small
     constexpr bool kPipe = NF <= 8;
+    constexpr int kDepth = 3;
+    constexpr int kMaxPer = kStreamMaxPer;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nrb = a.rows / R;
     const int nw = gridDim.x * 4;
     int rb = blockIdx.x * 4 + wave;
 
+    // The input vector first, then the weights: issued together, the input's
+    // short cache reads queue behind the chip-wide flood of weight requests
+    // and every block waits several microseconds for its prologue.
     Prologue<32 * G, PRO> pro;
     pro.load(a);
-    RowBlock<R, NF> cur, nxt;
-    if (rb < nrb) load_block<R, NF>(cur, a.codes, a.scales, rb, G, lane);
-    // residual epilogue: the wave's old values, loaded now (lane r holds row r)
-    // so the epilogue is a plain store instead of a dependent read-modify-write
-    float yold = 0.f, ynext = 0.f;
-    if (EPI == EPI_RESID && rb < nrb && lane < R) yold = a.y[rb * R + lane];
     pro.finish(a, xs, red);
     __syncthreads();
+    RowBlock<R, NF> ring[kPipe ? kDepth : 1];   // ring[0]: the wave's first block
+    if (rb < nrb) load_block<R, NF>(ring[0], a.codes, a.scales, rb, G, lane);
+    // residual epilogue: the wave's old values, loaded ahead (lane r holds row
+    // r) so the epilogue is a plain store instead of a dependent read-modify-write
+    float yold = 0.f;
+    if (EPI == EPI_RESID && rb < nrb && lane < R) yold = a.y[rb * R + lane];
 
     int row_of[NF], grp_of[NF];
 #pragma unroll
@@ -348,10 +394,11 @@ __global__ __launch_bounds__(256, 2) void k_gemv_stream(GemvArgs a) {
 #pragma unroll
             for (int k = 0; k < 4; ++k) xr[kPipe ? i : 0][k] = xv[4 * grp_of[i] + k];
     }
-    for (; rb < nrb; rb += nw) {
-        const bool more = rb + nw < nrb;
-        if (kPipe && more) load_block<R, NF>(nxt, a.codes, a.scales, rb + nw, G, lane);
-        if (EPI == EPI_RESID && more && lane < R) ynext = a.y[(rb + nw) * R + lane];
+    const NibK nk;
+
+    // dot products of one row block and the epilogue (yo: the lane's old
+    // residual value, lane r holding row r)
+    auto body = [&](const RowBlock<R, NF>& b, int rbb, float yo) {
         float acc[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[r] = 0.f;
@@ -366,11 +413,11 @@ __global__ __launch_bounds__(256, 2) void k_gemv_stream(GemvArgs a) {
                 x0 = xv[4 * g]; x1 = xv[4 * g + 1]; x2 = xv[4 * g + 2]; x3 = xv[4 * g + 3];
             }
             float ea = 0.f, eb = 0.f;
-            dq_dot8(cur.c[i][0], x0, ea, eb);
-            dq_dot8(cur.c[i][1], x1, ea, eb);
-            dq_dot8(cur.c[i][2], x2, ea, eb);
-            dq_dot8(cur.c[i][3], x3, ea, eb);
-            const float part = half_bits_to_float(cur.s[i]) * (ea + 0.0625f * eb);
+            dq_dot8(b.c[i][0], x0, ea, eb, nk);
+            dq_dot8(b.c[i][1], x1, ea, eb, nk);
+            dq_dot8(b.c[i][2], x2, ea, eb, nk);
+            dq_dot8(b.c[i][3], x3, ea, eb, nk);
+            const float part = half_bits_to_float(b.s[i]) * (ea + 0.0625f * eb);
 #pragma unroll
             for (int r = 0; r < R; ++r) acc[r] += row_of[i] == r ? part : 0.f;
             // long rows: split the group loop in two so that the compiler hoists
@@ -379,14 +426,13 @@ __global__ __launch_bounds__(256, 2) void k_gemv_stream(GemvArgs a) {
         }
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[r] = wave_sum_fast(acc[r]);
-        const int r0 = rb * R;
+        const int r0 = rbb * R;
         if (EPI == EPI_RESID) {
             // lane r adds row r's dot product (acc is uniform across the wave)
             float mine = 0.f;
 #pragma unroll
             for (int r = 0; r < R; ++r) mine = lane == r ? acc[r] : mine;
-            if (lane < R) a.y[r0 + lane] = yold + mine;
-            yold = ynext;
+            if (lane < R) a.y[r0 + lane] = yo + mine;
         } else if (lane == 0) {
             if (EPI == EPI_STORE) {
 #pragma unroll
@@ -399,9 +445,47 @@ __global__ __launch_bounds__(256, 2) void k_gemv_stream(GemvArgs a) {
                 }
             }
         }
-        if (more) {
-            if (kPipe) cur = nxt;
-            else load_block<R, NF>(cur, a.codes, a.scales, rb + nw, G, lane);
+    };
+
+    if (rb >= nrb) return;
+    if (kPipe) {
+        // a ring of PD register sets, each filled PD - 1 row blocks ahead of its
+        // use (fully unrolled: no copies between sets); past the wave's last
+        // block the prefetch re-reads that block (cache hits), so every step
+        // issues the same loads and no wait ever drains the ring
+        constexpr int PD = kDepth;
+        float yr[PD];
+        const int last = rb + ((nrb - 1 - rb) / nw) * nw;   // this wave's last block
+        yr[0] = yold;
+#pragma unroll
+        for (int k = 1; k < PD - 1; ++k) {
+            const int bk = min(rb + k * nw, last);
+            load_block<R, NF>(ring[k], a.codes, a.scales, bk, G, lane);
+            if (EPI == EPI_RESID && lane < R) yr[k] = a.y[bk * R + lane];
+        }
+        // straight-line steps (no loop header, so the wait counts stay exact);
+        // the launch keeps every wave within kMaxPer blocks, the tail loop
+        // below only keeps other launches correct
+#pragma unroll
+        for (int j = 0; j < kMaxPer; ++j) {
+            const int bl = min(rb + (j + PD - 1) * nw, last);
+            load_block<R, NF>(ring[(j + PD - 1) % PD], a.codes, a.scales, bl, G, lane);
+            if (EPI == EPI_RESID && lane < R) yr[(j + PD - 1) % PD] = a.y[bl * R + lane];
+            asm volatile("" ::: "memory");   // issue the prefetch before this block's math
+            body(ring[j % PD], rb + j * nw, yr[j % PD]);
+            if (rb + (j + 1) * nw >= nrb) break;
+        }
+        for (int rx = rb + kMaxPer * nw; rx < nrb; rx += nw) {
+            load_block<R, NF>(ring[0], a.codes, a.scales, rx, G, lane);
+            body(ring[0], rx, EPI == EPI_RESID && lane < R ? a.y[rx * R + lane] : 0.f);
+        }
+    } else {
+        for (; rb < nrb; rb += nw) {
+            body(ring[0], rb, yold);
+            if (rb + nw < nrb) {
+                load_block<R, NF>(ring[0], a.codes, a.scales, rb + nw, G, lane);
+                if (EPI == EPI_RESID && lane < R) yold = a.y[(rb + nw) * R + lane];
+            }
         }
     }
 }
@@ -775,7 +859,8 @@ void stream_shape(int K, int& R, int& NF) {
 
 int stream_blocks(int rows, int R, int NF) {
     const int nrb = rows / R;
-    const int max_waves = NF <= 8 ? 2048 : 4096;
+    int max_waves = NF <= 8 ? 2048 : 4096;
+    if (nrb > max_waves * kStreamMaxPer) max_waves = (nrb + kStreamMaxPer - 1) / kStreamMaxPer;
     const int per = (nrb + max_waves - 1) / max_waves;
     const int waves = (nrb + per - 1) / per;
     return (waves + 3) / 4;
