@@ -96,6 +96,80 @@ def cpu_baseline(ctx, seed):
                        f"scaled to 48 + 16 layers + full head = {per_token:.2f} s/token")}
 
 
+def long_leg(args, torch, A, W, SS, synth):
+    """Greedy decode and draft verification at a long cached context.  The
+    cache and the recurrent states are a seeded synthetic state (prefilling
+    262K positions token by token would take about 20 minutes); drafts come
+    from a synthetic draft distribution q (softmax of N(0, 1.43^2) logits,
+    fixed per draft slot), so the acceptance rate is that of an unrelated
+    draft model and says nothing about a trained one."""
+    import numpy as np
+    from synth.gpu_load import load_recipe
+    ctx = args.long_ctx
+    k = 3
+    shape = W.with_(W.FULL_27B, max_ctx=ctx + 16 + args.long_steps + (k + 1) * args.verify_passes + 16)
+    m = A.Model(shape)
+    load_recipe(m, shape, args.seed)
+    t0 = time.time()
+    # the seeded state, generated a few layers at a time on host threads
+    from concurrent.futures import ThreadPoolExecutor
+    SS.fill(m, shape, ctx - 1, args.seed, kv=False)
+    alayers = [l for l, t in enumerate(shape.pattern) if t == "A"]
+    with ThreadPoolExecutor(4) as ex:
+        for l, kv in zip(alayers, ex.map(lambda l: SS.kv_state(shape, l, ctx - 1, args.seed), alayers)):
+            m.import_kv(l, *kv)
+    m.set_pos(ctx - 1)
+    m.sync()
+    t_fill = time.time() - t0
+    first = int(synth.tokens(1, shape.vocab, args.seed + 1)[0])
+    warm = m.decode_greedy(first, 8)
+    tok = int(warm[-1])
+    pos0 = m.pos
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    toks = m.decode_greedy(tok, args.long_steps)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    nbytes = sum(step_bytes(shape, p) for p in range(pos0, pos0 + args.long_steps))
+    res = {"tok/s": round(args.long_steps / wall, 2), "ms_per_step": round(wall * 1e3 / args.long_steps, 4),
+           "steps": args.long_steps, "ctx_start": int(pos0),
+           "algorithmic_GB_per_step": round(nbytes / args.long_steps / 1e9, 4),
+           "achieved_GB/s": round(nbytes / wall / 1e9, 1), "frac_of_8TB/s": round(nbytes / wall / 1e9 / HBM_PEAK_GBS, 4),
+           "state": "seeded synthetic cache and recurrent states", "setup_fill_s": round(t_fill, 1)}
+    if args.verify_passes:
+        V = shape.vocab
+        logits = synth.normal(k, V, W.DRAFT_LOGIT_STD, args.seed, W.STREAM_DRAFT).astype(np.float64)
+        z = np.exp(logits - logits.max(axis=1, keepdims=True))
+        q = (z / z.sum(axis=1, keepdims=True)).astype(np.float32)
+        cq = np.cumsum(q.astype(np.float64), axis=1)
+        qd = torch.from_numpy(q).cuda()
+        du = synth.uniform(k * args.verify_passes, args.seed, W.STREAM_UNIFORM, i0=1 << 20).reshape(-1, k)
+        uu = synth.uniform((k + 1) * args.verify_passes, args.seed, W.STREAM_UNIFORM, i0=1 << 22).reshape(-1, k + 1)
+        t = int(toks[-1])
+        emitted = accepted = 0
+        m.verify_k([t] + [int(np.searchsorted(cq[j], du[0, j] * cq[j, -1], side="right")) for j in range(k)],
+                   qd, uu[0], 1.0)   # warm-up pass (graph-free path, first-use costs)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for p in range(args.verify_passes):
+            drafts = [min(V - 1, int(np.searchsorted(cq[j], du[p, j] * cq[j, -1], side="right"))) for j in range(k)]
+            out = m.verify_k([t] + drafts, qd, uu[p], 1.0)
+            emitted += len(out)
+            accepted += len(out) - 1
+            t = out[-1]
+        wall = time.perf_counter() - t0
+        res["verify"] = {"drafts_per_pass": k, "passes": args.verify_passes,
+                         "passes/s": round(args.verify_passes / wall, 2),
+                         "ms_per_pass": round(wall * 1e3 / args.verify_passes, 3),
+                         "emitted_tok/s": round(emitted / wall, 2),
+                         "accepted_per_pass": round(accepted / args.verify_passes, 3),
+                         "temperature": 1.0, "draft_q": "softmax of N(0, 1.43^2) logits per slot (synthetic)"}
+    m.close()
+    del m
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -108,6 +182,10 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--phase-reps", type=int, default=128)
+    ap.add_argument("--long-ctx", type=int, default=262144,
+                    help="second leg: cached positions of the long-context decode and verify runs (0: skip)")
+    ap.add_argument("--long-steps", type=int, default=128, help="timed greedy steps at --long-ctx")
+    ap.add_argument("--verify-passes", type=int, default=64, help="timed verify_k passes at --long-ctx (3 drafts)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -194,6 +272,9 @@ def main():
     }
     m.close()
     del m
+    torch.cuda.empty_cache()
+    if args.long_ctx:
+        out["ctx_262k" if args.long_ctx == 262144 else f"ctx_{args.long_ctx}"] = long_leg(args, torch, A, W, SS, synth)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.ctx, args.seed)
     print(json.dumps(out), flush=True)

@@ -39,7 +39,7 @@ def kv_state(shape, layer, npos, seed):
     return kc, ks, vc, vs
 
 
-def fill(model, shape, npos, seed, gdn=True):
+def fill(model, shape, npos, seed, gdn=True, kv=True):
     """Import a synthetic state of npos positions into a model exposing
     import_gdn / import_kv / set_pos (the GPU binding) or set_gdn_state /
     set_kv / set_pos (the oracle)."""
@@ -47,7 +47,7 @@ def fill(model, shape, npos, seed, gdn=True):
         if t == "G" and gdn:
             S = gdn_state(shape, l, seed)
             (model.import_gdn if hasattr(model, "import_gdn") else model.set_gdn_state)(l, S)
-        elif t == "A":
+        elif t == "A" and kv:
             kv = kv_state(shape, l, npos, seed)
             (model.import_kv if hasattr(model, "import_kv") else model.set_kv)(l, *kv)
     model.set_pos(npos)
