@@ -583,14 +583,21 @@ __global__ __launch_bounds__(256) void k_head_i8(HeadArgs a) {
 // The verify pass of draft tokens runs M <= 4 tokens through every layer in
 // one sweep over the weights: each group of codes is loaded and dequantised
 // once and dotted with the M input vectors held in LDS.
-template <int MAXM>
+// LDS image of the M input vectors: flat [M][K], or with each 32-value group
+// padded to 40 halves (80 bytes), so that lanes reading consecutive groups hit
+// distinct banks
+template <bool PAD>
+__device__ __forceinline__ int xs_index(int k) { return PAD ? (k >> 5) * 40 + (k & 31) : k; }
+template <bool PAD>
+__device__ __forceinline__ int xs_stride(int K) { return PAD ? (K >> 5) * 40 : K; }
+
+template <int MAXM, bool PAD = false>
 __device__ __forceinline__ void multi_prologue(int pro, const GemvMultiArgs& a, _Float16* xs, float* red) {
-    const int K = a.K, M = a.M;
+    const int K = a.K, M = a.M, KP = xs_stride<PAD>(K);
     if (pro == PRO_LOADH) {
         for (int m = 0; m < M; ++m) {
             const uint4* src = (const uint4*)(a.h + m * a.sh);
-            uint4* dst = (uint4*)(xs + m * K);
-            for (int i = threadIdx.x; i < K / 8; i += 256) dst[i] = src[i];
+            for (int i = threadIdx.x; i < K / 8; i += 256) *(uint4*)(xs + m * KP + xs_index<PAD>(8 * i)) = src[i];
         }
         return;
     }
@@ -614,12 +621,50 @@ __device__ __forceinline__ void multi_prologue(int pro, const GemvMultiArgs& a, 
         for (int m = 0; m < M; ++m) {
             const float t = red[m * 4] + red[m * 4 + 1] + red[m * 4 + 2] + red[m * 4 + 3];
             const float r = 1.0f / sqrtf(t / (float)K + a.eps);
-            for (int k = threadIdx.x; k < K; k += 256) xs[m * K + k] = (_Float16)(a.x[m * a.sx + k] * r * a.nw[k]);
+            for (int k = threadIdx.x; k < K; k += 256)
+                xs[m * KP + xs_index<PAD>(k)] = (_Float16)(a.x[m * a.sx + k] * r * a.nw[k]);
         }
         return;
     }
-    // gated: per head of d values RMSNorm(o) * w * SiLU(z), one wave per head
-    const int d = a.gated_d, nh = K / d;
+    // gated: per head of d values RMSNorm(o) * w * SiLU(z).  Thread t takes E
+    // consecutive values (E = K/256 when that divides a head, as in the
+    // single-vector prologue); the d/E threads of a head reduce with shuffles.
+    const int d = a.gated_d;
+    const int E = K >= 256 && K % 256 == 0 && d % (K / 256) == 0 && d / (K / 256) <= 64 ? K / 256 : 0;
+    if (E == 16) {
+        const int base = threadIdx.x * 16, c0 = base % d;
+        float wv[16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float4 w = ((const float4*)(a.nw + c0))[i];
+            wv[4 * i] = w.x; wv[4 * i + 1] = w.y; wv[4 * i + 2] = w.z; wv[4 * i + 3] = w.w;
+        }
+        const int tph = d / 16;
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m) {
+            if (m < M) {
+                float ov[16], zv[16];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float4 o = ((const float4*)(a.x + m * a.sx + base))[i];
+                    const float4 z = ((const float4*)(a.z + m * a.sz + base))[i];
+                    ov[4 * i] = o.x; ov[4 * i + 1] = o.y; ov[4 * i + 2] = o.z; ov[4 * i + 3] = o.w;
+                    zv[4 * i] = z.x; zv[4 * i + 1] = z.y; zv[4 * i + 2] = z.z; zv[4 * i + 3] = z.w;
+                }
+                float ss = 0.f;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) ss += ov[e] * ov[e];
+                for (int mm = tph >> 1; mm >= 1; mm >>= 1) ss += __shfl_xor(ss, mm, 64);
+                const float r = 1.0f / sqrtf(ss / (float)d + a.eps);
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    xs[m * KP + xs_index<PAD>(base + e)] = (_Float16)(ov[e] * r * wv[e] * (zv[e] * sigmoidf_(zv[e])));
+            }
+        }
+        return;
+    }
+    // other shapes: one wave per head
+    const int nh = K / d;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     for (int m = 0; m < M; ++m)
         for (int hh = wave; hh < nh; hh += 4) {
@@ -630,7 +675,7 @@ __device__ __forceinline__ void multi_prologue(int pro, const GemvMultiArgs& a, 
             ss = wave_sum(ss);
             const float r = 1.0f / sqrtf(ss / (float)d + a.eps);
             for (int i = lane; i < d; i += 64)
-                xs[m * K + hh * d + i] = (_Float16)(o[i] * r * a.nw[i] * (z[i] * sigmoidf_(z[i])));
+                xs[m * KP + xs_index<PAD>(hh * d + i)] = (_Float16)(o[i] * r * a.nw[i] * (z[i] * sigmoidf_(z[i])));
         }
 }
 
@@ -639,9 +684,11 @@ __global__ __launch_bounds__(256, 2) void k_gemv_multi(GemvMultiArgs a) {
     constexpr int MAXM = 4;
     extern __shared__ __align__(16) unsigned char smem[];
     float* red = (float*)smem;                       // 16 floats
-    _Float16* xs = (_Float16*)(smem + 64);           // [M][K]
+    _Float16* xs = (_Float16*)(smem + 64);           // [M][KP]
     constexpr int G = 64 * NF / R;
     constexpr int K = 32 * G;
+    constexpr bool kPad = NF <= 8;                   // padded image fits LDS for M = 4
+    constexpr int KP = kPad ? G * 40 : K;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nrb = (a.rows + R - 1) / R;            // the last row block may be partial
     const int nw = gridDim.x * 4;
@@ -667,12 +714,20 @@ __global__ __launch_bounds__(256, 2) void k_gemv_multi(GemvMultiArgs a) {
             }
         }
     };
-    int rb = blockIdx.x * 4 + wave;
-    RowBlock<R, NF> cur;
-    if (rb < nrb) load(cur, rb);
-    multi_prologue<MAXM>(PRO, a, xs, red);
+    // the input vectors first (see k_gemv_stream), then the weights
+    multi_prologue<MAXM, kPad>(PRO, a, xs, red);
     __syncthreads();
-    for (; rb < nrb; rb += nw) {
+    int rb = blockIdx.x * 4 + wave;
+    if (rb >= nrb) return;
+    RowBlock<R, NF> cur;
+    load(cur, rb);
+    const NibK nk;
+    const h2 off_lo = {(_Float16)1032.0f, (_Float16)1032.0f};
+    const h2 off_hi = {(_Float16)1152.0f, (_Float16)1152.0f};
+
+    // one row block: each code dword is dequantised once and dotted with the
+    // M inputs (read from LDS)
+    auto body = [&](const RowBlock<R, NF>& b, int rbb) {
         float acc[MAXM][R];
 #pragma unroll
         for (int m = 0; m < MAXM; ++m)
@@ -681,16 +736,29 @@ __global__ __launch_bounds__(256, 2) void k_gemv_multi(GemvMultiArgs a) {
 #pragma unroll
         for (int i = 0; i < NF; ++i) {
             const int g = grp_of[i];
-            const float sc = half_bits_to_float(cur.s[i]);
+            const float sc = half_bits_to_float(b.s[i]);
+            h2 p[4][4];
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const uint32_t w = b.c[i][d], w8 = w >> 8;
+                p[d][0] = as_h2((w & nk.lo) | nk.e) - off_lo;
+                p[d][1] = as_h2((w & nk.hi) | nk.e) - off_hi;
+                p[d][2] = as_h2((w8 & nk.lo) | nk.e) - off_lo;
+                p[d][3] = as_h2((w8 & nk.hi) | nk.e) - off_hi;
+            }
 #pragma unroll
             for (int m = 0; m < MAXM; ++m) {
                 if (m < M) {
-                    const uint4* xv = (const uint4*)(xs + m * K);
+                    const uint4* xv = (const uint4*)(xs + m * KP + (kPad ? 40 : 32) * g);
                     float ea = 0.f, eb = 0.f;
-                    dq_dot8(cur.c[i][0], xv[4 * g], ea, eb);
-                    dq_dot8(cur.c[i][1], xv[4 * g + 1], ea, eb);
-                    dq_dot8(cur.c[i][2], xv[4 * g + 2], ea, eb);
-                    dq_dot8(cur.c[i][3], xv[4 * g + 3], ea, eb);
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        const uint4 x = xv[d];
+                        ea = __builtin_amdgcn_fdot2(p[d][0], as_h2(x.x), ea, false);
+                        eb = __builtin_amdgcn_fdot2(p[d][1], as_h2(x.y), eb, false);
+                        ea = __builtin_amdgcn_fdot2(p[d][2], as_h2(x.z), ea, false);
+                        eb = __builtin_amdgcn_fdot2(p[d][3], as_h2(x.w), eb, false);
+                    }
                     const float part = sc * (ea + 0.0625f * eb);
 #pragma unroll
                     for (int r = 0; r < R; ++r) acc[m][r] += row_of[i] == r ? part : 0.f;
@@ -698,8 +766,7 @@ __global__ __launch_bounds__(256, 2) void k_gemv_multi(GemvMultiArgs a) {
             }
             if (NF > 8 && i == NF / 2) asm volatile("" ::: "memory");
         }
-        const int r0 = rb * R;
-        if (rb + nw < nrb) load(cur, rb + nw);
+        const int r0 = rbb * R;
 #pragma unroll
         for (int m = 0; m < MAXM; ++m) {
             if (m < M) {
@@ -726,6 +793,13 @@ __global__ __launch_bounds__(256, 2) void k_gemv_multi(GemvMultiArgs a) {
                 }
             }
         }
+    };
+
+    // at M = 4 the LDS reads of the inputs bound this kernel, not HBM: a plain
+    // loop with the next block's loads issued before the epilogue
+    for (; rb < nrb; rb += nw) {
+        body(cur, rb);
+        if (rb + nw < nrb) load(cur, rb + nw);
     }
 }
 
@@ -932,7 +1006,8 @@ hipError_t launch_gemv(int pro, int epi, const GemvArgs& a, hipStream_t s) {
 namespace {
 template <int R, int NF>
 hipError_t launch_multi_rnf(int pro, int epi, const GemvMultiArgs& a, hipStream_t s) {
-    const size_t shm = 64 + (size_t)a.K * 2 * (size_t)a.M;
+    const size_t kp = NF <= 8 ? (size_t)(a.K / 32) * 40 : (size_t)a.K;   // the kernel's kPad
+    const size_t shm = 64 + kp * 2 * (size_t)a.M;
     const dim3 grid(stream_blocks(a.rows + R - 1, R, NF)), block(256);
 #define AW4_MULTI_CASE(P, E)                                                                        \
     if (pro == P && epi == E) {                                                                     \
