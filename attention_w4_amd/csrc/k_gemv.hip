@@ -450,16 +450,17 @@ __global__ __launch_bounds__(256, 2) void k_gemv_stream(GemvArgs a) {
     if (rb >= nrb) return;
     if (kPipe) {
         // a ring of PD register sets, each filled PD - 1 row blocks ahead of its
-        // use (fully unrolled: no copies between sets); past the wave's last
-        // block the prefetch re-reads that block (cache hits), so every step
-        // issues the same loads and no wait ever drains the ring
+        // use (fully unrolled: no copies between sets); every step issues the
+        // same loads, so no wait ever drains the ring
         constexpr int PD = kDepth;
         float yr[PD];
-        const int last = rb + ((nrb - 1 - rb) / nw) * nw;   // this wave's last block
+        // a prefetch past the wave's last block reads block 0 instead: one
+        // small region every such wave shares, so it stays in L2 and costs no
+        // HBM traffic (the data is never used)
         yr[0] = yold;
 #pragma unroll
         for (int k = 1; k < PD - 1; ++k) {
-            const int bk = min(rb + k * nw, last);
+            const int bk = rb + k * nw < nrb ? rb + k * nw : 0;
             load_block<R, NF>(ring[k], a.codes, a.scales, bk, G, lane);
             if (EPI == EPI_RESID && lane < R) yr[k] = a.y[bk * R + lane];
         }
@@ -468,7 +469,7 @@ __global__ __launch_bounds__(256, 2) void k_gemv_stream(GemvArgs a) {
         // below only keeps other launches correct
 #pragma unroll
         for (int j = 0; j < kMaxPer; ++j) {
-            const int bl = min(rb + (j + PD - 1) * nw, last);
+            const int bl = rb + (j + PD - 1) * nw < nrb ? rb + (j + PD - 1) * nw : 0;
             load_block<R, NF>(ring[(j + PD - 1) % PD], a.codes, a.scales, bl, G, lane);
             if (EPI == EPI_RESID && lane < R) yr[(j + PD - 1) % PD] = a.y[bl * R + lane];
             asm volatile("" ::: "memory");   // issue the prefetch before this block's math

@@ -28,6 +28,22 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 
 
+# HBM bytes per launch of the gate/up GEMV from the FETCH_SIZE / WRITE_SIZE
+# counter runs recorded in profiles/hbm_traffic_8k_decode.md, valid only for
+# the kernel source whose sha256 prefix is recorded with them.
+GATEUP_TRAFFIC = {"k_gemv_sha256": "561bb64232a8bdff", "bytes": 101222420}
+
+
+def gateup_traffic():
+    import hashlib
+    src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "attention_w4_amd", "csrc", "k_gemv.hip")
+    try:
+        h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    except OSError:
+        return None
+    return GATEUP_TRAFFIC["bytes"] if h == GATEUP_TRAFFIC["k_gemv_sha256"] else None
+
+
 def step_bytes(shape, pos):
     """Algorithmic HBM bytes of one decode step at position pos (the token
     attends to pos + 1 cached positions)."""
@@ -186,6 +202,8 @@ def main():
                     help="second leg: cached positions of the long-context decode and verify runs (0: skip)")
     ap.add_argument("--long-steps", type=int, default=128, help="timed greedy steps at --long-ctx")
     ap.add_argument("--verify-passes", type=int, default=64, help="timed verify_k passes at --long-ctx (3 drafts)")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="run one plain device copy of this many MiB first (a known-size kernel for counter runs)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -201,6 +219,13 @@ def main():
     from synth import state as SS
     from synth.gpu_load import load_recipe
 
+    if args.calib_copy_mb:
+        n = args.calib_copy_mb << 18   # fp32 elements
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     shape = W.with_(W.FULL_27B, max_ctx=args.ctx + args.warmup + args.steps + 8)
     t0 = time.time()
     m = A.Model(shape)
@@ -265,7 +290,7 @@ def main():
                 "gpu_event_ms": round(gpu_ms, 3)},
         "roofline": {"kernel": "k_gemv_stream (RMSNorm + FFN gate/up W4 GEMV + SwiGLU), K=5120, 34816 rows",
                      "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": gateup_traffic(),
                      "avg_launch_us": round(us, 3), "bytes_per_launch": nbytes, "other_kernels": others},
         "setup_s": {"load": round(t_load, 1), "prompt": round(t_prompt, 1)},
         "first_tokens": [int(t) for t in toks[:8]],
