@@ -200,7 +200,7 @@ def main():
     ap.add_argument("--phase-reps", type=int, default=128)
     ap.add_argument("--long-ctx", type=int, default=262144,
                     help="second leg: cached positions of the long-context decode and verify runs (0: skip)")
-    ap.add_argument("--long-steps", type=int, default=128, help="timed greedy steps at --long-ctx")
+    ap.add_argument("--long-steps", type=int, default=256, help="timed greedy steps at --long-ctx")
     ap.add_argument("--verify-passes", type=int, default=64, help="timed verify_k passes at --long-ctx (3 drafts)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run one plain device copy of this many MiB first (a known-size kernel for counter runs)")
