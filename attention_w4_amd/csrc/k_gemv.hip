@@ -92,7 +92,8 @@ __device__ __forceinline__ float half_bits_to_float(uint16_t b) {
     return (float)__builtin_bit_cast(_Float16, b);
 }
 
-__device__ __forceinline__ float sigmoidf_(float v) { return 1.0f / (1.0f + __expf(-v)); }
+// logistic function with the hardware reciprocal (about 1 ulp, like __expf)
+__device__ __forceinline__ float sigmoidf_(float v) { return __builtin_amdgcn_rcpf(1.0f + __expf(-v)); }
 
 // block-wide sum over 256 threads; red must hold 4 floats
 __device__ __forceinline__ float block_sum256(float v, float* red) {
