@@ -36,6 +36,16 @@ __global__ __launch_bounds__(256) void k_gdn(GdnArgs a) {
     const float* av = a.proj + 2LL * a.nqk * D + 2LL * a.nv * D;
     const float* bv = av + a.nv;
 
+    // this thread's slice of the state row, its v and the gate inputs are
+    // requested first: their HBM latency then overlaps the norm reductions
+    const int r = row0 + tid / TPR;
+    const int c0 = (tid % TPR) * EPT;
+    float* Srow = a.S + ((int64_t)h * D + r) * D + c0;
+    const float4 s0 = *(const float4*)Srow;
+    const float4 s1 = *(const float4*)(Srow + 4);
+    const float vr = v[r];
+    const float araw = av[h] + a.a_bias[h], braw = bv[h];
+
     // L2 norms of k and q (threads [0, D) take k, [D, 2D) take q)
     float val = 0.f;
     if (tid < 2 * D) val = tid < D ? k[tid] : q[tid - D];
@@ -56,21 +66,16 @@ __global__ __launch_bounds__(256) void k_gdn(GdnArgs a) {
     }
     __syncthreads();
 
-    const float alpha = sigmoidf_(av[h] + a.a_bias[h]);
-    const float beta = sigmoidf_(bv[h]);
+    const float alpha = sigmoidf_(araw);
+    const float beta = sigmoidf_(braw);
 
-    const int r = row0 + tid / TPR;
-    const int c0 = (tid % TPR) * EPT;
-    float* Srow = a.S + ((int64_t)h * D + r) * D + c0;
-    float4 s0 = *(const float4*)Srow;
-    float4 s1 = *(const float4*)(Srow + 4);
     float s[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
     float u = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) u += s[e] * kq[0][c0 + e];
 #pragma unroll
     for (int o = TPR / 2; o >= 1; o >>= 1) u += __shfl_xor(u, o, 64);
-    const float delta = beta * (v[r] - alpha * u);
+    const float delta = beta * (vr - alpha * u);
     float oo = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {

@@ -581,6 +581,108 @@ __global__ __launch_bounds__(256) void k_head_i8(HeadArgs a) {
     }
 }
 
+// Streaming int8 head for rows of H = 1024 k bytes: lane l takes the NC = H/1024
+// 16-byte chunks l + 64 i of every row (one 1 KB wave load per chunk index),
+// keeps its slices of the normalised input in registers, and streams rows
+// through a ring of three register sets filled two rows ahead.  The loop is
+// unrolled by three with the same loads in flight at its entry and at its
+// back edge, so the compiler's wait counts stay exact; a prefetch past the
+// wave's last row reads row 0 instead (an L2 hit, the data is never used).
+template <int H>
+__global__ __launch_bounds__(256, 2) void k_head_stream(HeadArgs a) {
+    constexpr int NC = H / 1024;
+    constexpr int GR = H / 32;
+    extern __shared__ __align__(16) unsigned char smem[];
+    float* red = (float*)smem;
+    _Float16* xs = (_Float16*)(smem + 64);
+    __shared__ float bv_s[4];
+    __shared__ int bi_s[4];
+    {
+        GemvArgs g{};
+        g.K = H;
+        g.x = a.x;
+        g.nw = a.nw;
+        g.eps = a.eps;
+        Prologue<H, PRO_NORM> pro;
+        pro.load(g);
+        pro.finish(g, xs, red);
+    }
+    __syncthreads();
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nw = gridDim.x * 4;
+    const int r0 = blockIdx.x * 4 + wave;
+    const uint4* xv = (const uint4*)xs;
+    uint4 xa[NC], xb[NC];
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+        xa[i] = xv[2 * (lane + 64 * i)];
+        xb[i] = xv[2 * (lane + 64 * i) + 1];
+    }
+    struct Row {
+        u32x4 c[NC];
+        uint16_t s[NC];
+    };
+    auto load = [&](Row& b, int row) {
+        const u32x4* cp = (const u32x4*)(a.codes + (int64_t)row * H);
+        const uint16_t* sp = a.scales + (int64_t)row * GR;
+#pragma unroll
+        for (int i = 0; i < NC; ++i) {
+            b.c[i] = __builtin_nontemporal_load(cp + lane + 64 * i);
+            b.s[i] = sp[(lane + 64 * i) >> 1];
+        }
+    };
+    float best = -INFINITY;
+    int besti = 0x7fffffff;
+    auto body = [&](const Row& b, int row) {
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < NC; ++i) {
+            float p = 0.f;
+            i8_dot4(b.c[i][0], xa[i].x, xa[i].y, p);
+            i8_dot4(b.c[i][1], xa[i].z, xa[i].w, p);
+            i8_dot4(b.c[i][2], xb[i].x, xb[i].y, p);
+            i8_dot4(b.c[i][3], xb[i].z, xb[i].w, p);
+            acc += half_bits_to_float(b.s[i]) * p;
+        }
+        acc = wave_sum_fast(acc);
+        if (lane == 0 && a.logits) a.logits[row] = acc;
+        if (better(acc, row, best, besti)) { best = acc; besti = row; }
+    };
+    if (r0 < a.V) {
+        Row ring[3];
+        auto clampr = [&](int row) { return row < a.V ? row : 0; };
+        load(ring[0], r0);
+        load(ring[1], clampr(r0 + nw));
+        for (int row = r0;; row += 3 * nw) {
+            load(ring[2], clampr(row + 2 * nw));
+            asm volatile("" ::: "memory");
+            body(ring[0], row);
+            if (row + nw >= a.V) break;
+            load(ring[0], clampr(row + 3 * nw));
+            asm volatile("" ::: "memory");
+            body(ring[1], row + nw);
+            if (row + 2 * nw >= a.V) break;
+            load(ring[1], clampr(row + 4 * nw));
+            asm volatile("" ::: "memory");
+            body(ring[2], row + 2 * nw);
+            if (row + 3 * nw >= a.V) break;
+        }
+    }
+    if (lane == 0) {
+        bv_s[wave] = best;
+        bi_s[wave] = besti;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float b = bv_s[0];
+        int bi = bi_s[0];
+        for (int w = 1; w < 4; ++w)
+            if (better(bv_s[w], bi_s[w], b, bi)) { b = bv_s[w]; bi = bi_s[w]; }
+        a.part_val[blockIdx.x] = b;
+        a.part_idx[blockIdx.x] = bi;
+    }
+}
+
 // ------------------------------------------------------------------ M-vector W4 GEMV
 // The verify pass of draft tokens runs M <= 4 tokens through every layer in
 // one sweep over the weights: each group of codes is loaded and dequantised
@@ -1063,7 +1165,10 @@ hipError_t launch_head_multi(const HeadMultiArgs& a, hipStream_t s) {
 
 hipError_t launch_head(const HeadArgs& a, hipStream_t s) {
     const size_t shm = 64 + (size_t)a.H * 2;
-    hipLaunchKernelGGL(k_head_i8, dim3(head_blocks(a.V)), dim3(256), shm, s, a);
+    if (a.H == 5120)
+        hipLaunchKernelGGL(k_head_stream<5120>, dim3(head_blocks(a.V)), dim3(256), shm, s, a);
+    else
+        hipLaunchKernelGGL(k_head_i8, dim3(head_blocks(a.V)), dim3(256), shm, s, a);
     return hipGetLastError();
 }
 
