@@ -100,7 +100,6 @@ __global__ __launch_bounds__(512, 1) void k_attn(AttnArgs a) {
     constexpr int HPL = NG / 2;         // staged scale halves per lane (NG >= 2)
     static_assert(G >= 1 && G <= 16 && NG >= 2, "shape");
 
-    __shared__ float vt[D];
     __shared__ uint8_t vq[D];
     __shared__ float stile[kWaves][2][NG][kTile];      // per wave: key / value scales [group][position]
     __shared__ float mo[kWaves][G][D];                  // wave results
@@ -118,54 +117,6 @@ __global__ __launch_bounds__(512, 1) void k_attn(AttnArgs a) {
     const int t1 = min(npos, t0 + pps);
     const int64_t hbase = (int64_t)j * a.max_ctx;
     const float qscale = 1.0f / sqrtf((float)D);
-
-    if (t1 == npos) {
-        // append the current token (this workgroup is the only one whose range holds it)
-        const float* kp = a.proj + 2LL * a.nq * D + (int64_t)j * D;
-        const float* vp = kp + (int64_t)a.nkv * D;
-        const int64_t prow = hbase + pos;
-        if (tid < D) {
-            const float kv = kp[tid];
-            const float am = seg32_max(fabsf(kv));
-            const _Float16 sh = (_Float16)(am / 127.0f);
-            const float sc = (float)sh;
-            float cd = sc == 0.f ? 0.f : rintf(kv / sc);
-            cd = fminf(fmaxf(cd, -127.f), 127.f);
-            a.kc[prow * D + k_byte<D>(tid)] = (int8_t)(uint8_t)((int)cd + 128);
-            if ((tid & 31) == 0) a.ks[prow * NG + (tid >> 5)] = __builtin_bit_cast(uint16_t, sh);
-            vt[tid] = vp[tid] * a.signs[tid];
-        }
-        __syncthreads();
-        fwht<D>(vt);
-        if (tid < D) {
-            const float vr = vt[tid] * qscale;   // 1/sqrt(D): a power of two for D = 64, 256
-            const float am = seg32_max(fabsf(vr));
-            const _Float16 sh = (_Float16)(am / 3.0f);
-            const float sc = (float)sh;
-            float cd = sc == 0.f ? 0.f : rintf(vr / sc);
-            cd = fminf(fmaxf(cd, -3.f), 3.f);
-            vq[tid] = (uint8_t)((int)cd + 4);
-            if ((tid & 31) == 0) a.vs[prow * NG + (tid >> 5)] = __builtin_bit_cast(uint16_t, sh);
-        }
-        __syncthreads();
-        if (tid < VW) {
-            // word tid of the record: 3-bit slots f = NB (d % 16) + d / 16 overlapping its bits
-            uint32_t word = 0;
-            const int lo = 32 * tid;
-            const int f0 = lo / 3 > 0 ? lo / 3 - 1 : 0;
-            const int f1 = min(D - 1, (lo + 31) / 3);
-            for (int f = f0; f <= f1; ++f) {
-                const int d = 16 * (f % NB) + f / NB;
-                const uint32_t n = vq[d];
-                const int s = 3 * f - lo;
-                if (s >= 32 || s <= -3) continue;
-                word |= s >= 0 ? n << s : n >> (-s);
-            }
-            a.vc[prow * VW + tid] = word;
-        }
-        __threadfence_block();
-        __syncthreads();
-    }
 
     // raw words of one tile for this lane
     struct Raw {
@@ -218,9 +169,114 @@ __global__ __launch_bounds__(512, 1) void k_attn(AttnArgs a) {
         }
     };
 
+    // The current token is encoded (quantise K; sign flip, fast Walsh-Hadamard
+    // transform, quantise V) and appended by one wave: the one that owns the
+    // final tile of the range that ends at it.  Only that tile holds the new
+    // position, so no other wave waits; the writer's own loads of that tile
+    // come after its stores in program order.
+    auto encode = [&]() {
+        constexpr int P = D / 64;                 // dims per lane: d = P lane + i
+        constexpr int GL = 32 / P;                // lanes per scale group
+        const float* kp = a.proj + 2LL * a.nq * D + (int64_t)j * D;
+        const float* vp = kp + (int64_t)a.nkv * D;
+        const int64_t prow = hbase + pos;
+        float kv[P], v[P];
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            kv[i] = kp[P * lane + i];
+            v[i] = vp[P * lane + i] * a.signs[P * lane + i];
+        }
+        float am = 0.f;
+#pragma unroll
+        for (int i = 0; i < P; ++i) am = fmaxf(am, fabsf(kv[i]));
+#pragma unroll
+        for (int o = 1; o < GL; o <<= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
+        {
+            const _Float16 sh = (_Float16)(am / 127.0f);
+            const float sc = (float)sh;
+            uint32_t packed = 0;
+#pragma unroll
+            for (int i = 0; i < P; ++i) {
+                float cd = sc == 0.f ? 0.f : rintf(kv[i] / sc);
+                cd = fminf(fmaxf(cd, -127.f), 127.f);
+                packed |= (uint32_t)((int)cd + 128) << (8 * i);
+            }
+            // P consecutive dims stay consecutive bytes of the permuted row
+            if (P == 4) *(uint32_t*)(a.kc + prow * D + k_byte<D>(P * lane)) = packed;
+            else a.kc[prow * D + k_byte<D>(lane)] = (int8_t)(uint8_t)packed;
+            if (lane % GL == 0) a.ks[prow * NG + lane / GL] = __builtin_bit_cast(uint16_t, sh);
+        }
+        // Sylvester transform, stage by stage in the order of the index bits
+#pragma unroll
+        for (int hh = 1; hh < D; hh <<= 1) {
+            if (hh < P) {
+#pragma unroll
+                for (int i = 0; i < P; ++i)
+                    if ((i & hh) == 0) {
+                        const float x = v[i], y = v[i + hh];
+                        v[i] = x + y;
+                        v[i + hh] = x - y;
+                    }
+            } else {
+                const int lm = hh / P;
+#pragma unroll
+                for (int i = 0; i < P; ++i) {
+                    const float o = __shfl_xor(v[i], lm, 64);
+                    v[i] = (lane & lm) ? o - v[i] : v[i] + o;
+                }
+            }
+        }
+        am = 0.f;
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            v[i] *= qscale;   // 1/sqrt(D): a power of two for D = 64, 256
+            am = fmaxf(am, fabsf(v[i]));
+        }
+#pragma unroll
+        for (int o = 1; o < GL; o <<= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
+        {
+            const _Float16 sh = (_Float16)(am / 3.0f);
+            const float sc = (float)sh;
+#pragma unroll
+            for (int i = 0; i < P; ++i) {
+                float cd = sc == 0.f ? 0.f : rintf(v[i] / sc);
+                cd = fminf(fmaxf(cd, -3.f), 3.f);
+                vq[P * lane + i] = (uint8_t)((int)cd + 4);
+            }
+            if (lane % GL == 0) a.vs[prow * NG + lane / GL] = __builtin_bit_cast(uint16_t, sh);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (lane < VW) {
+            // word lane of the record: 3-bit slots f = NB (d % 16) + d / 16 overlapping its bits
+            uint32_t word = 0;
+            const int lo = 32 * lane;
+            const int f0 = lo / 3 > 0 ? lo / 3 - 1 : 0;
+            const int f1 = min(D - 1, (lo + 31) / 3);
+            for (int f = f0; f <= f1; ++f) {
+                const int d = 16 * (f % NB) + f / NB;
+                const uint32_t n = vq[d];
+                const int sft = 3 * f - lo;
+                if (sft >= 32 || sft <= -3) continue;
+                word |= sft >= 0 ? n << sft : n >> (-sft);
+            }
+            a.vc[prow * VW + lane] = word;
+        }
+        __threadfence_block();
+    };
+
     const int ntiles = (t1 - t0 + kTile - 1) / kTile;
+    const bool writer = t1 == npos && w == (ntiles - 1) % kWaves;
+    const bool first_final = w == ntiles - 1;
     Raw cur = {}, nxt = {};
-    if (w < ntiles) load(t0 + w * kTile, cur);   // in flight while q is read
+    // the first tile is in flight while q is read; the writer requests the
+    // final tile only after appending the token
+    if (w < ntiles && !(writer && first_final)) load(t0 + w * kTile, cur);
+    if (writer) {
+        encode();
+        if (first_final) load(t0 + w * kTile, cur);
+    }
 
     // query fragments (B operand of the score product): head c, dims 32 g + 8 q + e,
     // pre-scaled by 1/sqrt(D), as fp16 hi + lo so the scores keep fp32 accuracy
