@@ -1037,7 +1037,10 @@ void stream_shape(int K, int& R, int& NF) {
 
 int stream_blocks(int rows, int R, int NF) {
     const int nrb = rows / R;
-    int max_waves = NF <= 8 ? 2048 : 4096;
+    // pipelined shapes: about one 4-wave workgroup per CU while the ring covers
+    // the rows in at most kStreamMaxPer steps (measured faster than two per CU
+    // for 5-18k rows); the FFN gate/up (17k row blocks) keeps two per CU
+    int max_waves = NF > 8 ? 4096 : nrb <= 1024 * kStreamMaxPer ? 1024 : 2048;
     if (nrb > max_waves * kStreamMaxPer) max_waves = (nrb + kStreamMaxPer - 1) / kStreamMaxPer;
     const int per = (nrb + max_waves - 1) / max_waves;
     const int waves = (nrb + per - 1) / per;

@@ -205,6 +205,8 @@ def main():
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run one plain device copy of this many MiB first (a known-size kernel for counter runs)")
     args = ap.parse_args()
+    if args.phase_reps < 1:
+        ap.error("--phase-reps must be at least 1 (the roofline figure times the dominant kernel)")
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
