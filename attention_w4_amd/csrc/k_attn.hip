@@ -64,21 +64,6 @@ __device__ __forceinline__ int k_byte(int d) {
     return 8 * (D / 32) * ((d & 31) >> 3) + 8 * (d >> 5) + (d & 7);
 }
 
-// in-place Sylvester fast Walsh-Hadamard transform of v[0..D) by D/2 threads
-template <int D>
-__device__ void fwht(float* v) {
-    for (int hh = 1; hh < D; hh <<= 1) {
-        if (threadIdx.x < D / 2) {
-            const int t = threadIdx.x;
-            const int i = (t / hh) * 2 * hh + (t % hh);
-            const float x = v[i], y = v[i + hh];
-            v[i] = x + y;
-            v[i + hh] = x - y;
-        }
-        __syncthreads();
-    }
-}
-
 // eight offset-binary bytes u = b + 128 (little endian in x0, x1) -> the eight
 // exact fp16 values b: 0x6400 | u is the half 1024 + u
 __device__ __forceinline__ h8 u8x8_to_h8(uint32_t x0, uint32_t x1) {
@@ -460,6 +445,8 @@ template <int D>
 __global__ __launch_bounds__(1024) void k_combine(CombineArgs a) {
     constexpr int LR = D / 4;            // lanes per split row, a float4 each
     constexpr int ROWS = 1024 / LR;      // split rows in flight
+    constexpr int KMAX = 256 / ROWS;     // rows per thread at the largest split count
+    constexpr int P = D / 64;            // values per lane in the final transform
     __shared__ float wts[256];
     __shared__ float red[ROWS][D];
     __shared__ float v[D];
@@ -470,12 +457,21 @@ __global__ __launch_bounds__(1024) void k_combine(CombineArgs a) {
     split_range(pos + 1, a.nsplit, pps, used);
     const float* base = a.part + (int64_t)i * a.nsplit * D;
     const float* mlp = a.part + (int64_t)a.nq * a.nsplit * D + 2LL * i * a.nsplit;
-    // split weights exp(m_s - M) and the normaliser, one split per thread
+    // every load is issued before any is used: (m, l) of one split per
+    // thread, then this thread's slices of the split rows
     float ms = -INFINITY, ls = 0.f;
     if (tid < used) {
         ms = mlp[2 * tid];
         ls = mlp[2 * tid + 1];
     }
+    const int row = tid / LR, e4 = tid % LR;
+    f4 pv[KMAX];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        const int sp = row + k * ROWS;
+        pv[k] = sp < used ? *(const f4*)(base + (int64_t)sp * D + 4 * e4) : f4{0.f, 0.f, 0.f, 0.f};
+    }
+    // split weights exp(m_s - M) and the normaliser
     float M = ms;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
@@ -495,12 +491,11 @@ __global__ __launch_bounds__(1024) void k_combine(CombineArgs a) {
 #pragma unroll
     for (int k = 0; k < 16; ++k) L += rsum[k];
     {
-        const int row = tid / LR, e4 = tid % LR;
         f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int k = 0; k < 256 / ROWS; ++k) {
-            const int s = row + k * ROWS;
-            if (s < used) acc += wts[s] * *(const f4*)(base + (int64_t)s * D + 4 * e4);
+        for (int k = 0; k < KMAX; ++k) {
+            const int sp = row + k * ROWS;
+            if (sp < used) acc += wts[sp] * pv[k];
         }
         *(f4*)&red[row][4 * e4] = acc;
     }
@@ -512,11 +507,39 @@ __global__ __launch_bounds__(1024) void k_combine(CombineArgs a) {
         v[tid] = t / L;
     }
     __syncthreads();
-    fwht<D>(v);
-    if (tid < D) {
-        const float o = v[tid] * (1.0f / sqrtf((float)D)) * a.signs[tid];
-        const float g = a.proj[(int64_t)a.nq * D + (int64_t)i * D + tid];
-        a.out[(int64_t)i * D + tid] = (_Float16)(o * sigmoidf_(g));
+    if (tid < 64) {
+        // undo the rotation in one wave: Sylvester transform stage by stage in
+        // the order of the index bits, lane holds d = P lane + j
+        const int lane = tid;
+        float x[P];
+#pragma unroll
+        for (int j = 0; j < P; ++j) x[j] = v[P * lane + j];
+#pragma unroll
+        for (int hh = 1; hh < D; hh <<= 1) {
+            if (hh < P) {
+#pragma unroll
+                for (int j = 0; j < P; ++j)
+                    if ((j & hh) == 0) {
+                        const float p0 = x[j], p1 = x[j + hh];
+                        x[j] = p0 + p1;
+                        x[j + hh] = p0 - p1;
+                    }
+            } else {
+                const int lm = hh / P;
+#pragma unroll
+                for (int j = 0; j < P; ++j) {
+                    const float o = __shfl_xor(x[j], lm, 64);
+                    x[j] = (lane & lm) ? o - x[j] : x[j] + o;
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+            const int d = P * lane + j;
+            const float o = x[j] * (1.0f / sqrtf((float)D)) * a.signs[d];
+            const float g = a.proj[(int64_t)a.nq * D + (int64_t)i * D + d];
+            a.out[(int64_t)i * D + d] = (_Float16)(o * sigmoidf_(g));
+        }
     }
 }
 

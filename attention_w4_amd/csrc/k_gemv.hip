@@ -1035,17 +1035,26 @@ void stream_shape(int K, int& R, int& NF) {
     NF = R * G / 64;
 }
 
-int stream_blocks(int rows, int R, int NF) {
-    const int nrb = rows / R;
-    // pipelined shapes: about one 4-wave workgroup per CU while the ring covers
-    // the rows in at most kStreamMaxPer steps (measured faster than two per CU
-    // for 5-18k rows); the FFN gate/up (17k row blocks) keeps two per CU
-    int max_waves = NF > 8 ? 4096 : nrb <= 1024 * kStreamMaxPer ? 1024 : 2048;
+// 4-wave workgroups of a streaming launch over nrb row blocks with at most
+// max_waves waves, unless that would take more than kStreamMaxPer blocks per wave
+int stream_grid(int nrb, int max_waves) {
     if (nrb > max_waves * kStreamMaxPer) max_waves = (nrb + kStreamMaxPer - 1) / kStreamMaxPer;
     const int per = (nrb + max_waves - 1) / max_waves;
     const int waves = (nrb + per - 1) / per;
     return (waves + 3) / 4;
 }
+
+int stream_blocks(int rows, int R, int NF) {
+    const int nrb = rows / R;
+    // pipelined shapes: about one workgroup per CU while the ring covers the
+    // rows in at most kStreamMaxPer steps (measured faster than two per CU for
+    // 5-18k rows, and than 8-wave workgroups); the FFN gate/up (17k row
+    // blocks) keeps two per CU
+    return stream_grid(nrb, NF > 8 ? 4096 : nrb <= 1024 * kStreamMaxPer ? 1024 : 2048);
+}
+
+// the multi-input kernel: two workgroups per CU for short rows
+int multi_blocks(int rows, int R, int NF) { return stream_grid(rows / R, NF <= 8 ? 2048 : 4096); }
 
 template <int R, int NF>
 hipError_t launch_stream(int pro, int epi, const GemvArgs& a, hipStream_t s) {
@@ -1115,7 +1124,7 @@ template <int R, int NF>
 hipError_t launch_multi_rnf(int pro, int epi, const GemvMultiArgs& a, hipStream_t s) {
     const size_t kp = NF <= 8 ? (size_t)(a.K / 32) * 40 : (size_t)a.K;   // the kernel's kPad
     const size_t shm = 64 + kp * 2 * (size_t)a.M;
-    const dim3 grid(stream_blocks(a.rows + R - 1, R, NF)), block(256);
+    const dim3 grid(multi_blocks(a.rows + R - 1, R, NF)), block(256);
 #define AW4_MULTI_CASE(P, E)                                                                        \
     if (pro == P && epi == E) {                                                                     \
         if (shm > 65536) {                                                                          \
