@@ -907,6 +907,292 @@ __global__ __launch_bounds__(256, 2) void k_gemv_multi(GemvMultiArgs a) {
     }
 }
 
+// ------------------------------------------------------------------ multi-input W4 GEMM on MFMA
+// M <= 4 input vectors against one W4 matrix on the matrix cores.  A block of
+// 16 rows takes one v_mfma_f32_16x16x32_f16 per 32-value group: the A operand
+// holds the 16 rows' exact codes (lane (r, q): row r, values 8q..8q+7 of the
+// group, i.e. one code dword), the B operand the inputs as columns (lane
+// (m, q): input m, the same 8 values, from LDS), so lane (m, q) of the result
+// holds the group's unscaled dot products of rows 4q..4q+3 with input m; the
+// fp16 group scale is then applied row by row with a mixed-precision FMA.
+// Products are exact (small integers times fp16) and accumulate in fp32, as in
+// the single-vector kernel.  KS waves of a workgroup share one row block and
+// split its groups, adding their partial sums through LDS.  Loads run two
+// stages of kStage groups ahead in a ring of three register sets.
+constexpr int kStage = 8;
+
+// The M input vectors as fp16 [M][K] in LDS for a compile-time K: every load
+// of every input is issued before any is used (one memory round trip), and the
+// norms need one barrier.  NORM: RMSNorm(x_m) * w.  LOADH: fp16 copy (two
+// inputs per round, to bound the registers).  GATED: per head of d values
+// RMSNorm(o) * w * SiLU(z), thread t taking E = K/256 consecutive values.
+template <int K, int PRO>
+__device__ __forceinline__ void mfma_prologue(const GemvMultiArgs& a, _Float16* xs, float* red) {
+    constexpr int MAXM = 4;
+    const int M = a.M, tid = threadIdx.x;
+    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+    if (PRO == PRO_NORM) {
+        constexpr int N4 = K / 4, PER = (N4 + 255) / 256;
+        float4 v[MAXM][PER], w[PER];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int idx = tid + 256 * i;
+            const bool in = N4 % 256 == 0 || idx < N4;
+            w[i] = in ? ((const float4*)a.nw)[idx] : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int m = 0; m < MAXM; ++m)
+                v[m][i] = in && m < M ? ((const float4*)(a.x + m * a.sx))[idx] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        float ss[MAXM];
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m) {
+            ss[m] = 0.f;
+#pragma unroll
+            for (int i = 0; i < PER; ++i)
+                ss[m] += v[m][i].x * v[m][i].x + v[m][i].y * v[m][i].y + v[m][i].z * v[m][i].z + v[m][i].w * v[m][i].w;
+            ss[m] = wave_sum_fast(ss[m]);
+        }
+        const int wave = tid >> 6;
+        if ((tid & 63) == 0)
+#pragma unroll
+            for (int m = 0; m < MAXM; ++m) red[m * 4 + wave] = ss[m];
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m) {
+            if (m >= M) break;
+            const float r = 1.0f / sqrtf((red[m * 4] + red[m * 4 + 1] + red[m * 4 + 2] + red[m * 4 + 3]) / (float)K + a.eps);
+#pragma unroll
+            for (int i = 0; i < PER; ++i) {
+                const int idx = tid + 256 * i;
+                if (N4 % 256 == 0 || idx < N4) {
+                    const h4 o = {(_Float16)(v[m][i].x * r * w[i].x), (_Float16)(v[m][i].y * r * w[i].y),
+                                  (_Float16)(v[m][i].z * r * w[i].z), (_Float16)(v[m][i].w * r * w[i].w)};
+                    ((h4*)(xs + m * K))[idx] = o;
+                }
+            }
+        }
+    } else if (PRO == PRO_LOADH) {
+        constexpr int N8 = K / 8, PER = (N8 + 255) / 256;
+#pragma unroll
+        for (int m0 = 0; m0 < MAXM; m0 += 2) {
+            if (m0 >= M) break;
+            uint4 v[2][PER];
+#pragma unroll
+            for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+                for (int i = 0; i < PER; ++i) {
+                    const int idx = tid + 256 * i;
+                    const int m = m0 + mm < M ? m0 + mm : m0;
+                    v[mm][i] = ((const uint4*)(a.h + m * a.sh))[idx < N8 ? idx : N8 - 1];
+                }
+#pragma unroll
+            for (int mm = 0; mm < 2; ++mm)
+                if (m0 + mm < M)
+#pragma unroll
+                    for (int i = 0; i < PER; ++i) {
+                        const int idx = tid + 256 * i;
+                        if (N8 % 256 == 0 || idx < N8) ((uint4*)(xs + (m0 + mm) * K))[idx] = v[mm][i];
+                    }
+        }
+    } else {
+        constexpr int E = K >= 256 ? K / 256 : 1;
+        const int base = tid * E;
+        const bool live = base < K;
+        const int d = a.gated_d, c0 = live ? base % d : 0;
+        const int tph = d / E;   // threads per head (power of two, <= 64)
+        // 16-byte loads when a thread's values come in fours (the 27B shape)
+        constexpr bool V4 = E % 4 == 0;
+        float wv[E];
+        if (V4) {
+#pragma unroll
+            for (int i = 0; i < E / 4; ++i) {
+                const float4 w = ((const float4*)(a.nw + c0))[i];
+                wv[4 * i] = w.x; wv[4 * i + 1] = w.y; wv[4 * i + 2] = w.z; wv[4 * i + 3] = w.w;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e) wv[e] = live ? a.nw[c0 + e] : 0.f;
+        }
+#pragma unroll
+        for (int m0 = 0; m0 < MAXM; m0 += 2) {
+            if (m0 >= M) break;
+            float ov[2][E], zv[2][E];
+#pragma unroll
+            for (int mm = 0; mm < 2; ++mm) {
+                const int m = m0 + mm < M ? m0 + mm : m0;
+                if (V4) {
+#pragma unroll
+                    for (int i = 0; i < E / 4; ++i) {
+                        const float4 o = ((const float4*)(a.x + m * a.sx + base))[i];
+                        const float4 z = ((const float4*)(a.z + m * a.sz + base))[i];
+                        ov[mm][4 * i] = o.x; ov[mm][4 * i + 1] = o.y; ov[mm][4 * i + 2] = o.z; ov[mm][4 * i + 3] = o.w;
+                        zv[mm][4 * i] = z.x; zv[mm][4 * i + 1] = z.y; zv[mm][4 * i + 2] = z.z; zv[mm][4 * i + 3] = z.w;
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        ov[mm][e] = live ? a.x[m * a.sx + base + e] : 0.f;
+                        zv[mm][e] = live ? a.z[m * a.sz + base + e] : 0.f;
+                    }
+                }
+            }
+#pragma unroll
+            for (int mm = 0; mm < 2; ++mm) {
+                float ss = 0.f;
+#pragma unroll
+                for (int e = 0; e < E; ++e) ss += ov[mm][e] * ov[mm][e];
+                for (int o = tph >> 1; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
+                const float r = 1.0f / sqrtf(ss / (float)d + a.eps);
+                if (live && m0 + mm < M)
+#pragma unroll
+                    for (int e = 0; e < E; ++e)
+                        xs[(m0 + mm) * K + base + e] =
+                            (_Float16)(ov[mm][e] * r * wv[e] * (zv[mm][e] * sigmoidf_(zv[mm][e])));
+            }
+        }
+    }
+}
+
+template <int PRO, int EPI, int KS, int NST>
+__global__ __launch_bounds__(256, 2) void k_gemv_mfma(GemvMultiArgs a) {
+    constexpr int MAXM = 4, U = kStage, NB = 4 / KS;   // NB row blocks per workgroup
+    typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    extern __shared__ __align__(16) unsigned char smem[];
+    float* red = (float*)smem;                        // 16 floats
+    _Float16* xs = (_Float16*)(smem + 64);            // [M][K]
+    const int K = a.K, G = K / 32, M = a.M, rows = a.rows;
+    f4* part = (f4*)(smem + 64 + (size_t)4 * M * (K / 2));   // [4 waves][64 lanes], KS > 1
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar branches
+    const int c = lane & 15, q = lane >> 4;
+
+    mfma_prologue<32 * KS * NST * U, PRO>(a, xs, red);
+    __syncthreads();
+
+    const int nrb = (rows + 15) / 16;
+    const int blk = blockIdx.x * NB + wave / KS;
+    const bool live = blk < nrb;                       // uniform over the KS waves of a block
+    const int gbeg = (wave % KS) * (NST * U);   // NST stages of U groups per wave
+    const int r0 = blk * 16;
+    // codes: lane (c, q) loads row c's group g + q whole (16 bytes) and four
+    // lane-row swaps hand each lane its dword of every group (see compute);
+    // the four result rows, clamped into the matrix
+    const u32x4* arow = (const u32x4*)(a.codes + (int64_t)min(r0 + c, rows - 1) * G * 4) + q;
+    const uint16_t* srow[4];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) srow[rr] = a.scales + (int64_t)min(r0 + 4 * q + rr, rows - 1) * G;
+    // B operand: input min(c, M - 1) (columns past M are computed and dropped)
+    const _Float16* xrow = xs + min(c, M - 1) * K + 8 * q;
+
+    struct Stage {
+        u32x4 w[U / 4];     // row c, groups g0 + 4h + q (h < U/4), all four dwords
+        uint4 s[4];         // fp16 scales of groups g0 .. g0 + U - 1, rows 4q .. 4q + 3
+    };
+    auto load = [&](Stage& st, int sidx) {
+        const int g0 = gbeg + sidx * U;
+#pragma unroll
+        for (int h = 0; h < U / 4; ++h) st.w[h] = __builtin_nontemporal_load(arow + g0 + 4 * h);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) st.s[rr] = *(const uint4*)(srow[rr] + g0);
+    };
+    const NibK nk;
+    const h2 off_lo = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+    const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+    const h2 off_hi = {(_Float16)-72.0f, (_Float16)-72.0f};
+    const f4 zero = {0.f, 0.f, 0.f, 0.f};
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](const Stage& st, int sidx) {
+        const int g0 = gbeg + sidx * U;
+        // the stage's input fragments first (LDS latency once per stage), then
+        // the products back to back, then the scales
+        uint4 xb[U];
+#pragma unroll
+        for (int j = 0; j < U; ++j) xb[j] = *(const uint4*)(xrow + 32 * (g0 + j));
+        // 4 x 4 transpose across the lane rows (16 lanes each): lane row t
+        // holds dwords 0..3 of group g0 + 4h + t; after two 32-lane and two
+        // 16-lane swaps, word j of lane row q is dword q of group g0 + 4h + j
+        uint32_t wd[U];
+#pragma unroll
+        for (int h = 0; h < U / 4; ++h) {
+            const auto ab = __builtin_amdgcn_permlane32_swap(st.w[h][0], st.w[h][2], false, false);
+            const auto cd = __builtin_amdgcn_permlane32_swap(st.w[h][1], st.w[h][3], false, false);
+            const auto t01 = __builtin_amdgcn_permlane16_swap(ab[0], cd[0], false, false);
+            const auto t23 = __builtin_amdgcn_permlane16_swap(ab[1], cd[1], false, false);
+            wd[4 * h] = t01[0];
+            wd[4 * h + 1] = t01[1];
+            wd[4 * h + 2] = t23[0];
+            wd[4 * h + 3] = t23[1];
+        }
+        f4 d[U];
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            // exact codes: lo slots 1024 + n - 1032, hi slots (1024 + 16 n) / 16 - 72
+            const uint32_t w = wd[j], w8 = w >> 8;
+            const h2 p0 = as_h2((w & nk.lo) | nk.e) + off_lo;
+            const h2 p1 = __builtin_elementwise_fma(as_h2((w & nk.hi) | nk.e), sixteenth, off_hi);
+            const h2 p2 = as_h2((w8 & nk.lo) | nk.e) + off_lo;
+            const h2 p3 = __builtin_elementwise_fma(as_h2((w8 & nk.hi) | nk.e), sixteenth, off_hi);
+            const h8 av = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+            d[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(h8, xb[j]), zero, 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < U; ++j)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const uint32_t sw = (j >> 1) == 0 ? st.s[rr].x : (j >> 1) == 1 ? st.s[rr].y
+                                  : (j >> 1) == 2 ? st.s[rr].z : st.s[rr].w;
+                acc[rr] += (float)as_h2(sw)[j & 1] * d[j][rr];
+            }
+    };
+    if (live) {
+        // three register sets used in turn, each refilled right after use, in
+        // straight-line code (a loop header would merge the wait counts); loads
+        // past the last stage re-read it so every step issues the same ones
+        Stage ring[3];
+        load(ring[0], 0);
+        load(ring[1], NST > 1 ? 1 : 0);
+#pragma unroll
+        for (int sidx = 0; sidx < NST; ++sidx) {
+            load(ring[(sidx + 2) % 3], sidx + 2 < NST ? sidx + 2 : NST - 1);
+            asm volatile("" ::: "memory");   // keep each stage's loads in their place
+            compute(ring[sidx % 3], sidx);
+        }
+    }
+    if (KS > 1) {
+        part[wave * 64 + lane] = f4{acc[0], acc[1], acc[2], acc[3]};
+        __syncthreads();
+        if (wave % KS != 0) return;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) acc[rr] = 0.f;
+#pragma unroll
+        for (int t = 0; t < KS; ++t) {
+            const f4 v = part[(wave + t) * 64 + lane];
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) acc[rr] += v[rr];
+        }
+    }
+    if (!live || c >= M) return;
+    const int rb = r0 + 4 * q;
+    if (EPI == EPI_STORE) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+            if (rb + rr < rows) a.y[c * a.sy + rb + rr] = acc[rr];
+    } else if (EPI == EPI_RESID) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+            if (rb + rr < rows) a.y[c * a.sy + rb + rr] += acc[rr];
+    } else {
+        // interleaved gate/up rows: (4q, 4q + 1) and (4q + 2, 4q + 3)
+#pragma unroll
+        for (int rr = 0; rr < 4; rr += 2)
+            if (rb + rr + 1 < rows) {
+                const float gg = acc[rr];
+                a.hout[c * a.so + ((rb + rr) >> 1)] = (_Float16)(gg * sigmoidf_(gg) * acc[rr + 1]);
+            }
+    }
+}
+
 // int8 head over M vectors (per-vector logits and per-block argmax partials)
 __global__ __launch_bounds__(256) void k_head_multi(HeadMultiArgs a) {
     constexpr int MAXM = 4;
@@ -1144,11 +1430,62 @@ hipError_t launch_multi_rnf(int pro, int epi, const GemvMultiArgs& a, hipStream_
 }
 }  // namespace
 
+namespace {
+template <int P, int E, int KS, int NST>
+hipError_t launch_mfma(const GemvMultiArgs& a, hipStream_t s) {
+    const int nrb = (a.rows + 15) / 16;
+    const dim3 grid((nrb + 4 / KS - 1) / (4 / KS)), block(256);
+    const size_t shm = 64 + (size_t)2 * a.M * a.K + (KS > 1 ? 4 * 64 * 16 : 0);
+    if (shm > 65536) {
+        hipError_t e = hipFuncSetAttribute((const void*)k_gemv_mfma<P, E, KS, NST>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((k_gemv_mfma<P, E, KS, NST>), grid, block, shm, s, a);
+    return hipGetLastError();
+}
+
+// the instantiated (prologue, epilogue, waves per block, stages per wave):
+// the 27B-shape matrices and the small test stack; true if launched
+bool try_mfma(int pro, int epi, int ks, int nst, const GemvMultiArgs& a, hipStream_t s, hipError_t& err) {
+#define AW4_MFMA(P, E, KS, NST)                              \
+    if (pro == P && epi == E && ks == KS && nst == NST) {    \
+        err = launch_mfma<P, E, KS, NST>(a, s);              \
+        return true;                                         \
+    }
+    AW4_MFMA(PRO_NORM, EPI_SWIGLU, 2, 10)   // FFN gate/up, K 5120
+    AW4_MFMA(PRO_NORM, EPI_STORE, 2, 10)    // mixer in-projections, K 5120
+    AW4_MFMA(PRO_GATED, EPI_RESID, 4, 4)    // GDN out-projection, K 4096
+    AW4_MFMA(PRO_LOADH, EPI_RESID, 4, 6)    // attention o-projection, K 6144
+    AW4_MFMA(PRO_LOADH, EPI_RESID, 4, 17)   // FFN down, K 17408
+    AW4_MFMA(PRO_NORM, EPI_SWIGLU, 2, 1)    // small stack (K 512, 1536, 256)
+    AW4_MFMA(PRO_NORM, EPI_STORE, 2, 1)
+    AW4_MFMA(PRO_LOADH, EPI_RESID, 2, 3)
+    AW4_MFMA(PRO_GATED, EPI_RESID, 1, 1)
+    AW4_MFMA(PRO_LOADH, EPI_RESID, 1, 1)
+#undef AW4_MFMA
+    return false;
+}
+}  // namespace
+
+// M <= 4 vectors: on the matrix cores when the groups split into whole stages
+// (every 27B-shape matrix), else the dot-product kernel.  Row blocks that
+// would leave the chip short of waves split their groups over 2 or 4 waves.
 hipError_t launch_gemv_multi(int pro, int epi, const GemvMultiArgs& a, hipStream_t s) {
     if (a.M < 1 || a.M > 4) return hipErrorInvalidValue;
     int R, NF;
     stream_shape(a.K, R, NF);
     if (pro == PRO_GATED && (a.gated_d <= 0 || a.K % a.gated_d)) return hipErrorInvalidValue;
+    const int G = a.K / 32;
+    if (a.K % 32 == 0 && G % kStage == 0 && a.rows >= 1) {
+        const int nrb = (a.rows + 15) / 16;
+        // at least two waves per row block: with one, the stage offsets are
+        // compile-time constants and the compiler merges the ring's loads
+        // until the registers spill
+        const int ks = nrb <= 512 && G % (4 * kStage) == 0 ? 4 : G % (2 * kStage) == 0 ? 2 : 1;
+        hipError_t err;
+        if (try_mfma(pro, epi, ks, G / (ks * kStage), a, s, err)) return err;
+    }
 #define AW4_SHAPE(RR, FF) \
     if (R == RR && NF == FF) return launch_multi_rnf<RR, FF>(pro, epi, a, s);
     AW4_SHAPE(2, 5)

@@ -43,6 +43,13 @@ def test_full_27b_greedy_from_8k_state():
     first = int(synth.tokens(1, shape.vocab, 0, i0=CTX)[0])
     got = gm.decode_greedy(first, STEPS)
     xg = gm.read_hidden()
+    # the same state again through one verify pass of three drafts at
+    # temperature 0, which runs the multi-token (M = 4) projections at every
+    # 27B shape: the greedy drafts are all accepted and the bonus token is the
+    # fourth greedy token
+    SS.fill(gm, shape, CTX, 0)
+    emitted = gm.verify_k([first] + [int(t) for t in got[:3]], temperature=0.0)
+    vpos = gm.pos
     gm.close()
     del gm
     torch.cuda.empty_cache()
@@ -62,5 +69,7 @@ def test_full_27b_greedy_from_8k_state():
          f"final hidden rel-L2 {rel_l2(xg, x):.2e}")
     _say("gpu   ", list(got))
     _say("oracle", ref)
+    _say("verify", emitted, "position", vpos)
     assert list(got) == ref
+    assert emitted == ref[:4] and vpos == CTX + 4
     assert rel_l2(xg, x) < 1e-2
