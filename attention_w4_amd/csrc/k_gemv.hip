@@ -1109,6 +1109,7 @@ __global__ __launch_bounds__(256, 2) void k_gemv_mfma(GemvMultiArgs a) {
         uint4 xb[U];
 #pragma unroll
         for (int j = 0; j < U; ++j) xb[j] = *(const uint4*)(xrow + 32 * (g0 + j));
+        asm volatile("" ::: "memory");   // issued together, before the products
         // 4 x 4 transpose across the lane rows (16 lanes each): lane row t
         // holds dwords 0..3 of group g0 + 4h + t; after two 32-lane and two
         // 16-lane swaps, word j of lane row q is dword q of group g0 + 4h + j
@@ -1458,6 +1459,7 @@ bool try_mfma(int pro, int epi, int ks, int nst, const GemvMultiArgs& a, hipStre
     AW4_MFMA(PRO_GATED, EPI_RESID, 4, 4)    // GDN out-projection, K 4096
     AW4_MFMA(PRO_LOADH, EPI_RESID, 4, 6)    // attention o-projection, K 6144
     AW4_MFMA(PRO_LOADH, EPI_RESID, 4, 17)   // FFN down, K 17408
+    AW4_MFMA(PRO_LOADH, EPI_RESID, 2, 34)   // FFN down when one workgroup fills a CU's LDS
     AW4_MFMA(PRO_NORM, EPI_SWIGLU, 2, 1)    // small stack (K 512, 1536, 256)
     AW4_MFMA(PRO_NORM, EPI_STORE, 2, 1)
     AW4_MFMA(PRO_LOADH, EPI_RESID, 2, 3)
@@ -1482,7 +1484,10 @@ hipError_t launch_gemv_multi(int pro, int epi, const GemvMultiArgs& a, hipStream
         // at least two waves per row block: with one, the stage offsets are
         // compile-time constants and the compiler merges the ring's loads
         // until the registers spill
-        const int ks = nrb <= 512 && G % (4 * kStage) == 0 ? 4 : G % (2 * kStage) == 0 ? 2 : 1;
+        int ks = nrb <= 512 && G % (4 * kStage) == 0 ? 4 : G % (2 * kStage) == 0 ? 2 : 1;
+        // an input image above half the LDS leaves one workgroup per CU: then
+        // two waves per row block keep the grid within one round of CUs
+        if (ks == 4 && (size_t)2 * a.M * a.K > 80 * 1024) ks = 2;
         hipError_t err;
         if (try_mfma(pro, epi, ks, G / (ks * kStage), a, s, err)) return err;
     }
