@@ -40,6 +40,8 @@ struct LayerBufs {
     uint16_t* vs = nullptr;
 };
 
+constexpr int kSweepRows = 4;   // most tokens one attention sweep takes (verify_k has at most 4)
+
 struct Plan {
     uint64_t off = 0;
     uint8_t* base = nullptr;   // null while only sizing
@@ -218,7 +220,8 @@ uint64_t plan_layout(const aw4_config* c, aw4_model* m, uint8_t* base) {
     _Float16* hbuf = p.take<_Float16>((uint64_t)hlen * 2);
     _Float16* abuf = p.take<_Float16>((uint64_t)(has_a ? c->attn_q_heads * c->attn_head_dim : 1) * 2);
     const int nsplit = nsplit_for(c->max_ctx, c->attn_kv_heads);
-    float* part = p.take<float>((uint64_t)(has_a ? c->attn_q_heads : 1) * nsplit * (c->attn_head_dim + 2) * 4);
+    // split partials: one row per (token of a sweep, q head), up to 4 tokens
+    float* part = p.take<float>((uint64_t)(has_a ? kSweepRows * c->attn_q_heads : 1) * nsplit * (c->attn_head_dim + 2) * 4);
     float* logits = nullptr;
     float* pv = nullptr;
     int32_t* pi = nullptr;
@@ -409,6 +412,8 @@ int enqueue_layers(aw4_model* m) {
             HIPCHK(m, launch_gemv(PRO_GATED, EPI_RESID, go, s));
         } else {
             AttnArgs aa{};
+            aa.nt = 1;
+            aa.append = 1;
             aa.proj = m->proj;
             aa.kc = b.kc;
             aa.ks = b.ks;
@@ -417,14 +422,15 @@ int enqueue_layers(aw4_model* m) {
             aa.signs = m->signs;
             aa.ctl = m->ctl;
             aa.part = m->part;
+            aa.prow = kSweepRows * c->attn_q_heads;
             aa.max_ctx = c->max_ctx;
             aa.nq = c->attn_q_heads;
             aa.nkv = c->attn_kv_heads;
             aa.d = c->attn_head_dim;
             aa.nsplit = m->nsplit;
             HIPCHK(m, launch_attn(aa, s));
-            CombineArgs ca{0, m->part, m->proj, m->signs, m->ctl, m->abuf, c->attn_q_heads, c->attn_kv_heads,
-                           c->attn_head_dim, m->nsplit};
+            CombineArgs ca{0, 1, 0, m->part, m->proj, m->signs, m->ctl, m->abuf, aa.prow, c->attn_q_heads,
+                           c->attn_kv_heads, c->attn_head_dim, m->nsplit};
             HIPCHK(m, launch_combine(ca, s));
             GemvArgs go{};
             go.codes = b.w_out;
@@ -520,18 +526,26 @@ int enqueue_verify(aw4_model* m, int M, int k, const float* dev_q, float tempera
             HIPCHK(m, launch_gemv_multi(PRO_GATED, EPI_RESID, go, s));
             ++gi_layer;
         } else {
+            // all M tokens' K and V first, then sweeps of up to tps tokens over
+            // the cache (each token masked to its own position)
             const int64_t od = (int64_t)c->attn_q_heads * c->attn_head_dim;
-            for (int t = 0; t < M; ++t) {
-                AttnArgs aa{};
+            AttnArgs aa{};
+            aa.nt = M;
+            aa.sproj = b.in_rows;
+            aa.proj = proj;
+            aa.kc = b.kc; aa.ks = b.ks; aa.vc = b.vc; aa.vs = b.vs;
+            aa.signs = m->signs; aa.ctl = m->ctl; aa.part = m->part; aa.prow = kSweepRows * c->attn_q_heads;
+            aa.max_ctx = c->max_ctx; aa.nq = c->attn_q_heads; aa.nkv = c->attn_kv_heads;
+            aa.d = c->attn_head_dim; aa.nsplit = m->nsplit;
+            HIPCHK(m, launch_append(aa, s));
+            const int tps = attn_tokens_per_sweep(c->attn_head_dim, c->attn_q_heads, c->attn_kv_heads);
+            for (int t = 0; t < M; t += tps) {
                 aa.pos_offset = t;
+                aa.nt = std::min(tps, M - t);
                 aa.proj = proj + (int64_t)t * b.in_rows;
-                aa.kc = b.kc; aa.ks = b.ks; aa.vc = b.vc; aa.vs = b.vs;
-                aa.signs = m->signs; aa.ctl = m->ctl; aa.part = m->part;
-                aa.max_ctx = c->max_ctx; aa.nq = c->attn_q_heads; aa.nkv = c->attn_kv_heads;
-                aa.d = c->attn_head_dim; aa.nsplit = m->nsplit;
                 HIPCHK(m, launch_attn(aa, s));
-                CombineArgs ca{t, m->part, aa.proj, m->signs, m->ctl, m->va + t * od, c->attn_q_heads,
-                               c->attn_kv_heads, c->attn_head_dim, m->nsplit};
+                CombineArgs ca{t, aa.nt, b.in_rows, m->part, aa.proj, m->signs, m->ctl, m->va + t * od, aa.prow,
+                               c->attn_q_heads, c->attn_kv_heads, c->attn_head_dim, m->nsplit};
                 HIPCHK(m, launch_combine(ca, s));
             }
             GemvMultiArgs go{};

@@ -96,7 +96,10 @@ struct GdnArgs {
 };
 
 struct AttnArgs {
-    int32_t pos_offset;       // the token sits at ctl->pos + pos_offset
+    int32_t pos_offset;       // the first token sits at ctl->pos + pos_offset
+    int32_t nt;               // tokens in this sweep, at consecutive positions
+    int32_t append;           // encode and append the (single) token first
+    int64_t sproj;            // token m's projections at proj + m * sproj
     const float* proj;        // [q nq*d | g nq*d | k nkv*d | v nkv*d]
     int8_t* kc;               // [nkv][max_ctx][d] code + 128, dims permuted for the MFMA operand (k_attn.hip)
     uint16_t* ks;             // [nkv][max_ctx][d/32]
@@ -104,17 +107,21 @@ struct AttnArgs {
     uint16_t* vs;             // [nkv][max_ctx][d/32]
     const float* signs;       // [d] +-1
     const Ctl* ctl;
-    float* part;              // [nq][nsplit][d] acc, then [nq][nsplit][2] (m, l)
+    float* part;              // [prow][nsplit][d] acc, then [prow][nsplit][2] (m, l); row m nq + head
+    int32_t prow;             // rows of part: nq times the most tokens per sweep
     int32_t max_ctx, nq, nkv, d, nsplit;
 };
 
 struct CombineArgs {
     int32_t pos_offset;
+    int32_t nt;               // tokens of the sweep (rows m nq + head of part)
+    int64_t sproj;            // token m's projections (for the gate g) at proj + m * sproj
     const float* part;
-    const float* proj;        // for the gate g
+    const float* proj;
     const float* signs;
     const Ctl* ctl;
-    _Float16* out;            // [nq*d]
+    _Float16* out;            // token m, head h at out + (m nq + h) d
+    int32_t prow;
     int32_t nq, nkv, d, nsplit;
 };
 
@@ -172,6 +179,8 @@ hipError_t launch_embed_multi(const int8_t* codes, const uint16_t* scales, int H
                               hipStream_t s);
 hipError_t launch_set_verify(Ctl* ctl, const int32_t* tok, const float* u, hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
+hipError_t launch_append(const AttnArgs& a, hipStream_t s);
+int attn_tokens_per_sweep(int d, int nq, int nkv);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_embed(const int8_t* codes, const uint16_t* scales, int H, const Ctl* ctl, float* x,
                         hipStream_t s);

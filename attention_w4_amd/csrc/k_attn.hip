@@ -76,25 +76,128 @@ __device__ __forceinline__ h8 u8x8_to_h8(uint32_t x0, uint32_t x1) {
     return r;
 }
 
-template <int D, int G>
+// Encode one token (quantise K; sign flip, fast Walsh-Hadamard transform,
+// quantise V) and write it at cache row prow (kv-head base + position): one
+// wave, lane holding dims P lane .. P lane + P - 1; vq is D bytes of LDS.
+template <int D>
+__device__ void encode_append(const float* kp, const float* vp, const float* signs, int8_t* kc, uint16_t* ks,
+                              uint32_t* vc, uint16_t* vs, int64_t prow, uint8_t* vq, int lane) {
+    constexpr int NG = D / 32, NB = D / 16, VW = 3 * NG;
+    const float qscale = 1.0f / sqrtf((float)D);
+    constexpr int P = D / 64;                 // dims per lane: d = P lane + i
+    constexpr int GL = 32 / P;                // lanes per scale group
+    float kv[P], v[P];
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+        kv[i] = kp[P * lane + i];
+        v[i] = vp[P * lane + i] * signs[P * lane + i];
+    }
+    float am = 0.f;
+#pragma unroll
+    for (int i = 0; i < P; ++i) am = fmaxf(am, fabsf(kv[i]));
+#pragma unroll
+    for (int o = 1; o < GL; o <<= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
+    {
+        const _Float16 sh = (_Float16)(am / 127.0f);
+        const float sc = (float)sh;
+        uint32_t packed = 0;
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            float cd = sc == 0.f ? 0.f : rintf(kv[i] / sc);
+            cd = fminf(fmaxf(cd, -127.f), 127.f);
+            packed |= (uint32_t)((int)cd + 128) << (8 * i);
+        }
+        // P consecutive dims stay consecutive bytes of the permuted row
+        if (P == 4) *(uint32_t*)(kc + prow * D + k_byte<D>(P * lane)) = packed;
+        else kc[prow * D + k_byte<D>(lane)] = (int8_t)(uint8_t)packed;
+        if (lane % GL == 0) ks[prow * NG + lane / GL] = __builtin_bit_cast(uint16_t, sh);
+    }
+    // Sylvester transform, stage by stage in the order of the index bits
+#pragma unroll
+    for (int hh = 1; hh < D; hh <<= 1) {
+        if (hh < P) {
+#pragma unroll
+            for (int i = 0; i < P; ++i)
+                if ((i & hh) == 0) {
+                    const float x = v[i], y = v[i + hh];
+                    v[i] = x + y;
+                    v[i + hh] = x - y;
+                }
+        } else {
+            const int lm = hh / P;
+#pragma unroll
+            for (int i = 0; i < P; ++i) {
+                const float o = __shfl_xor(v[i], lm, 64);
+                v[i] = (lane & lm) ? o - v[i] : v[i] + o;
+            }
+        }
+    }
+    am = 0.f;
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+        v[i] *= qscale;   // 1/sqrt(D): a power of two for D = 64, 256
+        am = fmaxf(am, fabsf(v[i]));
+    }
+#pragma unroll
+    for (int o = 1; o < GL; o <<= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
+    {
+        const _Float16 sh = (_Float16)(am / 3.0f);
+        const float sc = (float)sh;
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            float cd = sc == 0.f ? 0.f : rintf(v[i] / sc);
+            cd = fminf(fmaxf(cd, -3.f), 3.f);
+            vq[P * lane + i] = (uint8_t)((int)cd + 4);
+        }
+        if (lane % GL == 0) vs[prow * NG + lane / GL] = __builtin_bit_cast(uint16_t, sh);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (lane < VW) {
+        // word lane of the record: 3-bit slots f = NB (d % 16) + d / 16 overlapping its bits
+        uint32_t word = 0;
+        const int lo = 32 * lane;
+        const int f0 = lo / 3 > 0 ? lo / 3 - 1 : 0;
+        const int f1 = min(D - 1, (lo + 31) / 3);
+        for (int f = f0; f <= f1; ++f) {
+            const int d = 16 * (f % NB) + f / NB;
+            const uint32_t n = vq[d];
+            const int sft = 3 * f - lo;
+            if (sft >= 32 || sft <= -3) continue;
+            word |= sft >= 0 ? n << sft : n >> (-sft);
+        }
+        vc[prow * VW + lane] = word;
+    }
+    __threadfence_block();
+}
+
+// NT tokens at consecutive positions share one sweep over the cache: query
+// column c of the score product is token c / G, head c % G (QC = G NT <= 16
+// columns), and token m sees positions up to its own.
+template <int D, int G, int NT>
 __global__ __launch_bounds__(512, 1) void k_attn(AttnArgs a) {
     constexpr int NG = D / 32;          // scale groups
     constexpr int NB = D / 16;          // 16-dim blocks of the value product
     constexpr int VW = 3 * NG;          // 32-bit words per value record
     constexpr int VB = 3 * NB;          // value bits per lane slot
     constexpr int HPL = NG / 2;         // staged scale halves per lane (NG >= 2)
-    static_assert(G >= 1 && G <= 16 && NG >= 2, "shape");
+    constexpr int QC = G * NT;          // query columns
+    static_assert(G >= 1 && QC <= 16 && NG >= 2, "shape");
+    // wave results merge in one pass when all fit 48 KB, else through 4 slots
+    constexpr bool kOnePass = kWaves * QC * D <= 12288;
 
     __shared__ uint8_t vq[D];
     __shared__ float stile[kWaves][2][NG][kTile];      // per wave: key / value scales [group][position]
-    __shared__ float mo[kWaves][G][D];                  // wave results
-    __shared__ float mm[kWaves][G], ll[kWaves][G];
+    __shared__ float mo[kOnePass ? kWaves : 4][QC][D];  // wave results
+    __shared__ float mm[kWaves][QC], ll[kWaves][QC];
 
     const int split = blockIdx.x, j = blockIdx.y, tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
     const int c = lane & 15, q = lane >> 4;
-    const int pos = a.ctl->pos + a.pos_offset;
-    const int npos = pos + 1;
+    const int pos = a.ctl->pos + a.pos_offset;   // the first token's position
+    const int nt = NT == 1 ? 1 : a.nt;
+    const int npos = pos + nt;
     int pps, used;
     split_range(npos, a.nsplit, pps, used);
     if (split >= used) return;
@@ -159,100 +262,17 @@ __global__ __launch_bounds__(512, 1) void k_attn(AttnArgs a) {
     // final tile of the range that ends at it.  Only that tile holds the new
     // position, so no other wave waits; the writer's own loads of that tile
     // come after its stores in program order.
+    // The current token is encoded and appended by one wave: the one that
+    // owns the final tile of the range that ends at it.  Only that tile holds
+    // the new position, so no other wave waits; the writer's own loads of that
+    // tile come after its stores in program order.
     auto encode = [&]() {
-        constexpr int P = D / 64;                 // dims per lane: d = P lane + i
-        constexpr int GL = 32 / P;                // lanes per scale group
         const float* kp = a.proj + 2LL * a.nq * D + (int64_t)j * D;
-        const float* vp = kp + (int64_t)a.nkv * D;
-        const int64_t prow = hbase + pos;
-        float kv[P], v[P];
-#pragma unroll
-        for (int i = 0; i < P; ++i) {
-            kv[i] = kp[P * lane + i];
-            v[i] = vp[P * lane + i] * a.signs[P * lane + i];
-        }
-        float am = 0.f;
-#pragma unroll
-        for (int i = 0; i < P; ++i) am = fmaxf(am, fabsf(kv[i]));
-#pragma unroll
-        for (int o = 1; o < GL; o <<= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
-        {
-            const _Float16 sh = (_Float16)(am / 127.0f);
-            const float sc = (float)sh;
-            uint32_t packed = 0;
-#pragma unroll
-            for (int i = 0; i < P; ++i) {
-                float cd = sc == 0.f ? 0.f : rintf(kv[i] / sc);
-                cd = fminf(fmaxf(cd, -127.f), 127.f);
-                packed |= (uint32_t)((int)cd + 128) << (8 * i);
-            }
-            // P consecutive dims stay consecutive bytes of the permuted row
-            if (P == 4) *(uint32_t*)(a.kc + prow * D + k_byte<D>(P * lane)) = packed;
-            else a.kc[prow * D + k_byte<D>(lane)] = (int8_t)(uint8_t)packed;
-            if (lane % GL == 0) a.ks[prow * NG + lane / GL] = __builtin_bit_cast(uint16_t, sh);
-        }
-        // Sylvester transform, stage by stage in the order of the index bits
-#pragma unroll
-        for (int hh = 1; hh < D; hh <<= 1) {
-            if (hh < P) {
-#pragma unroll
-                for (int i = 0; i < P; ++i)
-                    if ((i & hh) == 0) {
-                        const float x = v[i], y = v[i + hh];
-                        v[i] = x + y;
-                        v[i + hh] = x - y;
-                    }
-            } else {
-                const int lm = hh / P;
-#pragma unroll
-                for (int i = 0; i < P; ++i) {
-                    const float o = __shfl_xor(v[i], lm, 64);
-                    v[i] = (lane & lm) ? o - v[i] : v[i] + o;
-                }
-            }
-        }
-        am = 0.f;
-#pragma unroll
-        for (int i = 0; i < P; ++i) {
-            v[i] *= qscale;   // 1/sqrt(D): a power of two for D = 64, 256
-            am = fmaxf(am, fabsf(v[i]));
-        }
-#pragma unroll
-        for (int o = 1; o < GL; o <<= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
-        {
-            const _Float16 sh = (_Float16)(am / 3.0f);
-            const float sc = (float)sh;
-#pragma unroll
-            for (int i = 0; i < P; ++i) {
-                float cd = sc == 0.f ? 0.f : rintf(v[i] / sc);
-                cd = fminf(fmaxf(cd, -3.f), 3.f);
-                vq[P * lane + i] = (uint8_t)((int)cd + 4);
-            }
-            if (lane % GL == 0) a.vs[prow * NG + lane / GL] = __builtin_bit_cast(uint16_t, sh);
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        if (lane < VW) {
-            // word lane of the record: 3-bit slots f = NB (d % 16) + d / 16 overlapping its bits
-            uint32_t word = 0;
-            const int lo = 32 * lane;
-            const int f0 = lo / 3 > 0 ? lo / 3 - 1 : 0;
-            const int f1 = min(D - 1, (lo + 31) / 3);
-            for (int f = f0; f <= f1; ++f) {
-                const int d = 16 * (f % NB) + f / NB;
-                const uint32_t n = vq[d];
-                const int sft = 3 * f - lo;
-                if (sft >= 32 || sft <= -3) continue;
-                word |= sft >= 0 ? n << sft : n >> (-sft);
-            }
-            a.vc[prow * VW + lane] = word;
-        }
-        __threadfence_block();
+        encode_append<D>(kp, kp + (int64_t)a.nkv * D, a.signs, a.kc, a.ks, a.vc, a.vs, hbase + pos, vq, lane);
     };
 
     const int ntiles = (t1 - t0 + kTile - 1) / kTile;
-    const bool writer = t1 == npos && w == (ntiles - 1) % kWaves;
+    const bool writer = NT == 1 && a.append && t1 == npos && w == (ntiles - 1) % kWaves;
     const bool first_final = w == ntiles - 1;
     Raw cur = {}, nxt = {};
     // the first tile is in flight while q is read; the writer requests the
@@ -265,13 +285,16 @@ __global__ __launch_bounds__(512, 1) void k_attn(AttnArgs a) {
 
     // query fragments (B operand of the score product): head c, dims 32 g + 8 q + e,
     // pre-scaled by 1/sqrt(D), as fp16 hi + lo so the scores keep fp32 accuracy
+    const bool qv = c < G * nt;                        // a live query column
+    const int cm = qv ? c / G : 0, cg = qv ? c % G : 0;
+    const int lim = pos + cm;                          // last position column c sees
     h8 qh[NG], ql[NG];
     {
-        const float* qp = a.proj + (int64_t)(j * G + (c < G ? c : 0)) * D + 8 * q;
+        const float* qp = a.proj + (int64_t)cm * a.sproj + (int64_t)(j * G + cg) * D + 8 * q;
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
             float4 x0 = make_float4(0.f, 0.f, 0.f, 0.f), x1 = x0;
-            if (c < G) {
+            if (qv) {
                 x0 = *(const float4*)(qp + 32 * g);
                 x1 = *(const float4*)(qp + 32 * g + 4);
             }
@@ -316,17 +339,19 @@ __global__ __launch_bounds__(512, 1) void k_attn(AttnArgs a) {
         }
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr)
-            if (tile0 + 4 * q + rr >= t1) s[rr] = -INFINITY;
+            if (tile0 + 4 * q + rr >= t1 || (NT > 1 && tile0 + 4 * q + rr > lim)) s[rr] = -INFINITY;
 
-        // online softmax for head c (the four quarters hold the tile's 16 positions)
+        // online softmax for column c (the four quarters hold the tile's 16
+        // positions); with several tokens a column can see none of a tile
         float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
         mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
         const float mn = fmaxf(m, mx);
-        const float corr = __expf(m - mn);
+        const bool none = NT > 1 && mn == -INFINITY;
+        const float corr = none ? 1.f : __expf(m - mn);
         float p[4];
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) p[rr] = __expf(s[rr] - mn);
+        for (int rr = 0; rr < 4; ++rr) p[rr] = none ? 0.f : __expf(s[rr] - mn);
         l = l * corr + ((p[0] + p[1]) + (p[2] + p[3]));
         m = mn;
         if (__builtin_amdgcn_ballot_w64(corr != 1.0f)) {
@@ -408,35 +433,83 @@ __global__ __launch_bounds__(512, 1) void k_attn(AttnArgs a) {
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
 
-    // every wave posts (m, l, acc) of its heads; lane (c, q) holds head c,
-    // dims 16 b + 4 q + rr; then one pass merges the waves per output
-    if (c < G) {
+    // partial rows: column c of kv head j is slot (c / G) nq + j G + c % G
+    float* mlp = a.part + (int64_t)a.prow * a.nsplit * D;
+    auto slot_row = [&](int cc) { return (int64_t)((cc / G) * a.nq + j * G + cc % G) * a.nsplit + split; };
+    if (kOnePass) {
+        // every wave posts (m, l, acc) of its columns; lane (c, q) holds column c,
+        // dims 16 b + 4 q + rr; then one pass merges the waves per output
+        if (c < QC) {
 #pragma unroll
-        for (int b = 0; b < NB; ++b) *(f4*)&mo[w][c][16 * b + 4 * q] = o[b];
-        if (q == 0) {
+            for (int b = 0; b < NB; ++b) *(f4*)&mo[w][c][16 * b + 4 * q] = o[b];
+            if (q == 0) {
+                mm[w][c] = m;
+                ll[w][c] = l;
+            }
+        }
+        __syncthreads();
+        for (int idx = tid; idx < G * nt * D; idx += 64 * kWaves) {
+            const int g = idx / D, e = idx % D;
+            float M = mm[0][g];
+#pragma unroll
+            for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, mm[ww][g]);
+            float L = 0.f, A = 0.f;
+#pragma unroll
+            for (int ww = 0; ww < kWaves; ++ww) {
+                const float f = mm[ww][g] == -INFINITY ? 0.f : __expf(mm[ww][g] - M);
+                L += ll[ww][g] * f;
+                A += mo[ww][g][e] * f;
+            }
+            const int64_t row = slot_row(g);
+            a.part[row * D + e] = A;
+            if (e == 0) {
+                mlp[2 * row] = M;
+                mlp[2 * row + 1] = L;
+            }
+        }
+    } else {
+        // the waves first agree on each column's maximum and rescale to it,
+        // then add their accumulators through four LDS slots
+        if (c < QC && q == 0) {
             mm[w][c] = m;
             ll[w][c] = l;
         }
-    }
-    __syncthreads();
-    float* mlp = a.part + (int64_t)a.nq * a.nsplit * D;
-    for (int idx = tid; idx < G * D; idx += 64 * kWaves) {
-        const int g = idx / D, e = idx % D;
-        float M = mm[0][g];
+        __syncthreads();
+        {
+            float M = -INFINITY;
+            if (c < QC)
 #pragma unroll
-        for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, mm[ww][g]);
-        float L = 0.f, A = 0.f;
+                for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, mm[ww][c]);
+            const float f = m == -INFINITY ? 0.f : __expf(m - M);
 #pragma unroll
-        for (int ww = 0; ww < kWaves; ++ww) {
-            const float f = mm[ww][g] == -INFINITY ? 0.f : __expf(mm[ww][g] - M);
-            L += ll[ww][g] * f;
-            A += mo[ww][g][e] * f;
+            for (int b = 0; b < NB; ++b) o[b] *= f;
         }
-        const int64_t row = (int64_t)(j * G + g) * a.nsplit + split;
-        a.part[row * D + e] = A;
-        if (e == 0) {
-            mlp[2 * row] = M;
-            mlp[2 * row + 1] = L;
+        if (w >= 4 && c < QC)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) *(f4*)&mo[w - 4][c][16 * b + 4 * q] = o[b];
+        __syncthreads();
+        if (w < 4 && c < QC)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                f4* slot = (f4*)&mo[w][c][16 * b + 4 * q];
+                *slot = o[b] + *slot;
+            }
+        __syncthreads();
+        for (int idx = tid; idx < G * nt * D; idx += 64 * kWaves) {
+            const int g = idx / D, e = idx % D;
+            float M = mm[0][g];
+#pragma unroll
+            for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, mm[ww][g]);
+            float L = 0.f;
+#pragma unroll
+            for (int ww = 0; ww < kWaves; ++ww) L += ll[ww][g] * (mm[ww][g] == -INFINITY ? 0.f : __expf(mm[ww][g] - M));
+            const float A = (mo[0][g][e] + mo[1][g][e]) + (mo[2][g][e] + mo[3][g][e]);
+            const int64_t row = slot_row(g);
+            a.part[row * D + e] = A;
+            if (e == 0) {
+                mlp[2 * row] = M;
+                mlp[2 * row + 1] = L;
+            }
         }
     }
 }
@@ -451,12 +524,14 @@ __global__ __launch_bounds__(1024) void k_combine(CombineArgs a) {
     __shared__ float red[ROWS][D];
     __shared__ float v[D];
     __shared__ float rmax[16], rsum[16];
+    // block i: token i / nq, head i % nq (its slot in the partial rows)
     const int i = blockIdx.x, tid = threadIdx.x;
+    const int tm = i / a.nq, hq = i % a.nq;
     const int pos = a.ctl->pos + a.pos_offset;
     int pps, used;
-    split_range(pos + 1, a.nsplit, pps, used);
+    split_range(pos + a.nt, a.nsplit, pps, used);
     const float* base = a.part + (int64_t)i * a.nsplit * D;
-    const float* mlp = a.part + (int64_t)a.nq * a.nsplit * D + 2LL * i * a.nsplit;
+    const float* mlp = a.part + (int64_t)a.prow * a.nsplit * D + 2LL * i * a.nsplit;
     // every load is issued before any is used: (m, l) of one split per
     // thread, then this thread's slices of the split rows
     float ms = -INFINITY, ls = 0.f;
@@ -537,41 +612,75 @@ __global__ __launch_bounds__(1024) void k_combine(CombineArgs a) {
         for (int j = 0; j < P; ++j) {
             const int d = P * lane + j;
             const float o = x[j] * (1.0f / sqrtf((float)D)) * a.signs[d];
-            const float g = a.proj[(int64_t)a.nq * D + (int64_t)i * D + d];
+            const float g = a.proj[(int64_t)tm * a.sproj + (int64_t)a.nq * D + (int64_t)hq * D + d];
             a.out[(int64_t)i * D + d] = (_Float16)(o * sigmoidf_(g));
         }
     }
 }
 
+// The nt tokens' K and V at positions ctl->pos + pos_offset + m, one wave per
+// (kv head, token), before a multi-token sweep reads them.
+template <int D>
+__global__ __launch_bounds__(64) void k_append(AttnArgs a) {
+    __shared__ uint8_t vq[D];
+    const int j = blockIdx.x, tm = blockIdx.y;
+    const int pos = a.ctl->pos + a.pos_offset + tm;
+    const float* kp = a.proj + (int64_t)tm * a.sproj + 2LL * a.nq * D + (int64_t)j * D;
+    encode_append<D>(kp, kp + (int64_t)a.nkv * D, a.signs, a.kc, a.ks, a.vc, a.vs, (int64_t)j * a.max_ctx + pos, vq,
+                     threadIdx.x);
+}
+
 }  // namespace
+
+int attn_tokens_per_sweep(int d, int nq, int nkv) {
+    const int G = nq / nkv;
+    if (d == 256 && G == 6) return 2;
+    if (d == 64 && (G == 4 || G == 2)) return 4;
+    return 1;
+}
+
+hipError_t launch_append(const AttnArgs& a, hipStream_t s) {
+    if (a.nt < 1) return hipErrorInvalidValue;
+    const dim3 grid(a.nkv, a.nt), block(64);
+    if (a.d == 256) hipLaunchKernelGGL(k_append<256>, grid, block, 0, s, a);
+    else if (a.d == 64) hipLaunchKernelGGL(k_append<64>, grid, block, 0, s, a);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
     const int G = a.nq / a.nkv;
-    if (a.nsplit < 1 || a.nsplit > 256) return hipErrorInvalidValue;
+    if (a.nsplit < 1 || a.nsplit > 256 || a.nt < 1 || a.nt > attn_tokens_per_sweep(a.d, a.nq, a.nkv) ||
+        (a.nt > 1 && a.append) || a.nq * a.nt > a.prow)
+        return hipErrorInvalidValue;
     const dim3 grid(a.nsplit, a.nkv), block(64 * kWaves);
-#define AW4_ATTN_CASE(DD, GG)                                                   \
-    if (a.d == DD && G == GG) {                                                 \
-        hipLaunchKernelGGL((k_attn<DD, GG>), grid, block, 0, s, a);             \
+#define AW4_ATTN_CASE(DD, GG, NN)                                               \
+    if (a.d == DD && G == GG && (NN == 1 ? a.nt == 1 : a.nt > 1)) {            \
+        hipLaunchKernelGGL((k_attn<DD, GG, NN>), grid, block, 0, s, a);         \
         return hipGetLastError();                                               \
     }
-    AW4_ATTN_CASE(256, 6)
-    AW4_ATTN_CASE(256, 4)
-    AW4_ATTN_CASE(256, 8)
-    AW4_ATTN_CASE(256, 2)
-    AW4_ATTN_CASE(256, 1)
-    AW4_ATTN_CASE(64, 4)
-    AW4_ATTN_CASE(64, 2)
-    AW4_ATTN_CASE(64, 1)
-    AW4_ATTN_CASE(64, 6)
-    AW4_ATTN_CASE(64, 8)
+    AW4_ATTN_CASE(256, 6, 1)
+    AW4_ATTN_CASE(256, 6, 2)
+    AW4_ATTN_CASE(256, 4, 1)
+    AW4_ATTN_CASE(256, 8, 1)
+    AW4_ATTN_CASE(256, 2, 1)
+    AW4_ATTN_CASE(256, 1, 1)
+    AW4_ATTN_CASE(64, 4, 1)
+    AW4_ATTN_CASE(64, 4, 4)
+    AW4_ATTN_CASE(64, 2, 1)
+    AW4_ATTN_CASE(64, 2, 4)
+    AW4_ATTN_CASE(64, 1, 1)
+    AW4_ATTN_CASE(64, 6, 1)
+    AW4_ATTN_CASE(64, 8, 1)
 #undef AW4_ATTN_CASE
     return hipErrorInvalidValue;
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
     if (a.nsplit < 1 || a.nsplit > 256) return hipErrorInvalidValue;
-    if (a.d == 256) hipLaunchKernelGGL(k_combine<256>, dim3(a.nq), dim3(1024), 0, s, a);
-    else if (a.d == 64) hipLaunchKernelGGL(k_combine<64>, dim3(a.nq), dim3(1024), 0, s, a);
+    if (a.nt < 1 || a.nq * a.nt > a.prow) return hipErrorInvalidValue;
+    if (a.d == 256) hipLaunchKernelGGL(k_combine<256>, dim3(a.nq * a.nt), dim3(1024), 0, s, a);
+    else if (a.d == 64) hipLaunchKernelGGL(k_combine<64>, dim3(a.nq * a.nt), dim3(1024), 0, s, a);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }
