@@ -31,7 +31,7 @@ HBM_PEAK_GBS = 8000.0
 # HBM bytes per launch of the gate/up GEMV from the FETCH_SIZE / WRITE_SIZE
 # counter runs recorded in profiles/hbm_traffic_8k_decode.md, valid only for
 # the kernel source whose sha256 prefix is recorded with them.
-GATEUP_TRAFFIC = {"k_gemv_sha256": "d0c7ce92e3016793", "bytes": 101202715}
+GATEUP_TRAFFIC = {"k_gemv_sha256": "e005bcccc8ed1190", "bytes": 101213227}
 
 
 def gateup_traffic():
