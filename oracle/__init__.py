@@ -34,7 +34,8 @@ class Cfg(ctypes.Structure):
     _fields_ = [("hidden", _i32), ("ffn", _i32), ("vocab", _i32), ("n_layers", _i32),
                 ("gdn_qk_heads", _i32), ("gdn_v_heads", _i32), ("gdn_head_dim", _i32),
                 ("attn_q_heads", _i32), ("attn_kv_heads", _i32), ("attn_head_dim", _i32),
-                ("group", _i32), ("max_ctx", _i32), ("rms_eps", _f64), ("pattern", ctypes.c_char * 128)]
+                ("group", _i32), ("max_ctx", _i32), ("rms_eps", _f64), ("pattern", ctypes.c_char * 128),
+                ("draft_vocab", _i32)]
 
 
 _lib = None
@@ -75,6 +76,11 @@ def lib():
             "or_set_state_gdn": ([_vp, ctypes.c_int, _vp], ctypes.c_int),
             "or_get_state_gdn": ([_vp, ctypes.c_int, _vp], ctypes.c_int),
             "or_set_state_kv": ([_vp, ctypes.c_int, _i32, _vp, _vp, _vp, _vp], ctypes.c_int),
+            "or_set_draft_map": ([_vp, _vp, _i32], ctypes.c_int),
+            "or_get_draft_map": ([_vp, _vp], ctypes.c_int),
+            "or_draft_step": ([_vp, _i32, _vp, _i32, _vp, _vp], ctypes.c_int),
+            "or_get_dpos": ([_vp], _i32),
+            "or_set_dpos": ([_vp, _i32], ctypes.c_int),
             "or_get_state_kv": ([_vp, ctypes.c_int, _i32, _vp, _vp, _vp, _vp], ctypes.c_int),
         }
         for name, (a, r) in sig.items():
@@ -177,6 +183,7 @@ def kv_encode(k, v, signs):
 # ------------------------------------------------------------------ model
 T_MIX_IN, T_MIX_OUT, T_FFN_GATE, T_FFN_UP, T_FFN_DOWN, T_LM_HEAD = 0, 1, 2, 3, 4, 5
 T_NORM_MIX, T_NORM_FFN, T_NORM_GATED, T_A_BIAS, T_NORM_FINAL, T_RHT_SIGNS = 6, 7, 8, 9, 10, 11
+T_DRAFT_FUSE, T_DRAFT_NORM_EMB, T_DRAFT_NORM_HID, T_DRAFT_NORM_OUT = 12, 13, 14, 15
 
 
 class Model:
@@ -191,6 +198,7 @@ class Model:
         c.n_layers = len(shape.pattern)
         c.rms_eps = float(shape.rms_eps)
         c.pattern = shape.pattern.encode()
+        c.draft_vocab = int(getattr(shape, "draft_vocab", 0))
         self._cfg = c
         self.h = lib().or_create(ctypes.byref(c))
         if not self.h:
@@ -266,6 +274,32 @@ class Model:
         self._rc(lib().or_decode_token(self.h, int(token), _p(x), _p(logits), _p(am)), "decode_token")
         return x, logits, int(am[0])
 
+    # -- draft head (layer index n_layers holds its weights)
+    def set_draft_map(self, ids):
+        ids = np.ascontiguousarray(ids, np.int32)
+        self._rc(lib().or_set_draft_map(self.h, _p(ids), len(ids)), "set_draft_map")
+
+    def draft_map(self):
+        ids = np.zeros(self.shape.draft_vocab, np.int32)
+        self._rc(lib().or_get_draft_map(self.h, _p(ids)), "draft_map")
+        return ids
+
+    @property
+    def dpos(self):
+        return lib().or_get_dpos(self.h)
+
+    def set_dpos(self, p):
+        self._rc(lib().or_set_dpos(self.h, p), "set_dpos")
+
+    def draft_step(self, token, h, slot=0):
+        """-> (output hidden [H], mapped logits [draft_vocab]); writes draft cache
+        entry dpos + slot, leaves dpos unchanged"""
+        h = np.ascontiguousarray(h, np.float64)
+        x = np.zeros(self.shape.hidden)
+        z = np.zeros(self.shape.draft_vocab)
+        self._rc(lib().or_draft_step(self.h, int(token), _p(h), int(slot), _p(x), _p(z)), "draft_step")
+        return x, z
+
     # -- state
     def set_gdn_state(self, layer, S):
         S = np.ascontiguousarray(S, np.float32)
@@ -336,4 +370,6 @@ def from_recipe(shape, seed, norm_jitter=0.0, chunk_rows=None):
             m.load_vec(spec.layer, spec.kind, synth.vector(spec, seed))
         elif spec.fmt == W.SIGNS:
             m.load_signs(synth.signs(spec.cols, seed, spec.stream))
+        elif spec.fmt == W.MAP:
+            m.set_draft_map(synth.draft_map(shape, seed))
     return m

@@ -12,7 +12,9 @@
  *    page 5, bs178.com llamAmpere article, "为什么它真能这么快" point 一);
  *  - 4-bit weights (page 1, the "27B x 4 bit" estimate; page 4, jdon.com,
  *    section on quantisation schools, W4A16);
- *  - KV cache with 8-bit keys and rotated ~3-bit values (page 5, point 三).
+ *  - KV cache with 8-bit keys and rotated ~3-bit values (page 5, point 三);
+ *  - a built-in draft head whose output projection covers only a mapped subset
+ *    of the vocabulary (page 5, point 四); its block structure is a reading.
  * Formats (group 32, fp16 scales, round-to-nearest-even) follow the readings.
  *
  * Precision: every continuous quantity is computed in fp64.  Where the method
@@ -144,6 +146,7 @@ typedef struct {
     int32_t group, max_ctx;
     double rms_eps;
     char pattern[128];
+    int32_t draft_vocab;    /* rows of the draft head's vocabulary map, 0 = no draft head */
 } or_cfg;
 
 typedef struct { int64_t rows, cols; uint8_t* codes; uint16_t* scales; } or_w4;
@@ -172,6 +175,16 @@ typedef struct {
     double* norm_final;
     int8_t* signs;
     int32_t pos;
+    /* draft head (draft_vocab > 0): fuse [H][2H] over [norm(embedding); norm(hidden)],
+     * one gated-attention layer with its own cache of dpos entries, a final norm and
+     * the int8 table rows listed in dmap (ascending ids) */
+    or_layer D;
+    or_w4 fuse;
+    double* dn_emb;
+    double* dn_hid;
+    double* dn_out;
+    int32_t* dmap;
+    int32_t dpos;
 } or_model;
 
 static void* zalloc(size_t n) {
@@ -197,15 +210,10 @@ static void w4_alloc(or_w4* w, int64_t rows, int64_t cols) {
     w->scales = (uint16_t*)zalloc((size_t)(rows * (cols / 32) * 2));
 }
 
-or_model* or_create(const or_cfg* cfg) {
-    or_model* m = (or_model*)zalloc(sizeof(or_model));
-    m->c = *cfg;
-    const or_cfg* c = &m->c;
+static void layer_alloc(const or_cfg* c, or_layer* L, char type) {
     int64_t H = c->hidden;
-    m->L = (or_layer*)zalloc(sizeof(or_layer) * (size_t)c->n_layers);
-    for (int l = 0; l < c->n_layers; ++l) {
-        or_layer* L = &m->L[l];
-        L->type = c->pattern[l];
+    {
+        L->type = type;
         w4_alloc(&L->w[0], mix_in_rows(c, L->type), H);
         w4_alloc(&L->w[1], H, mix_out_cols(c, L->type));
         w4_alloc(&L->w[2], c->ffn, H);
@@ -228,6 +236,34 @@ or_model* or_create(const or_cfg* cfg) {
             L->vlast = (float*)zalloc(sizeof(float) * c->attn_kv_heads * c->attn_head_dim);
         }
     }
+}
+
+static void layer_free(or_layer* L) {
+    for (int i = 0; i < 5; ++i) { free(L->w[i].codes); free(L->w[i].scales); }
+    free(L->norm_mix); free(L->norm_ffn); free(L->norm_gated); free(L->a_bias); free(L->S);
+    free(L->kc); free(L->ks); free(L->vc); free(L->vs); free(L->klast); free(L->vlast);
+}
+
+or_model* or_create(const or_cfg* cfg) {
+    or_model* m = (or_model*)zalloc(sizeof(or_model));
+    m->c = *cfg;
+    const or_cfg* c = &m->c;
+    int64_t H = c->hidden;
+    if (c->draft_vocab < 0 || (c->draft_vocab > 0 && (c->vocab <= 0 || c->draft_vocab > c->vocab))) {
+        free(m);
+        return NULL;
+    }
+    m->L = (or_layer*)zalloc(sizeof(or_layer) * (size_t)c->n_layers);
+    for (int l = 0; l < c->n_layers; ++l) layer_alloc(c, &m->L[l], c->pattern[l]);
+    if (c->draft_vocab > 0) {
+        layer_alloc(c, &m->D, 'A');
+        w4_alloc(&m->fuse, H, 2 * H);
+        m->dn_emb = (double*)zalloc(sizeof(double) * H);
+        m->dn_hid = (double*)zalloc(sizeof(double) * H);
+        m->dn_out = (double*)zalloc(sizeof(double) * H);
+        m->dmap = (int32_t*)zalloc(sizeof(int32_t) * (size_t)c->draft_vocab);
+        for (int32_t i = 0; i < c->draft_vocab; ++i) m->dmap[i] = i;
+    }
     if (c->vocab > 0) {
         m->lm.rows = c->vocab;
         m->lm.cols = H;
@@ -241,23 +277,39 @@ or_model* or_create(const or_cfg* cfg) {
 
 void or_destroy(or_model* m) {
     if (!m) return;
-    for (int l = 0; l < m->c.n_layers; ++l) {
-        or_layer* L = &m->L[l];
-        for (int i = 0; i < 5; ++i) { free(L->w[i].codes); free(L->w[i].scales); }
-        free(L->norm_mix); free(L->norm_ffn); free(L->norm_gated); free(L->a_bias); free(L->S);
-        free(L->kc); free(L->ks); free(L->vc); free(L->vs); free(L->klast); free(L->vlast);
-    }
+    for (int l = 0; l < m->c.n_layers; ++l) layer_free(&m->L[l]);
     free(m->L);
+    if (m->c.draft_vocab > 0) {
+        layer_free(&m->D);
+        free(m->fuse.codes); free(m->fuse.scales);
+        free(m->dn_emb); free(m->dn_hid); free(m->dn_out); free(m->dmap);
+    }
     free(m->lm.codes); free(m->lm.scales); free(m->norm_final); free(m->signs);
     free(m);
 }
 
 /* tensor kinds: 0 mixer in, 1 mixer out, 2 ffn gate, 3 ffn up, 4 ffn down (W4);
  * 5 lm_head (int8); 6 mixer norm, 7 ffn norm, 8 gated norm, 9 a bias,
- * 10 final norm (vectors); 11 rotation signs. */
+ * 10 final norm (vectors); 11 rotation signs.  Layer n_layers is the draft
+ * head's gated-attention layer (kinds 0-4, 6, 7) and holds its fuse matrix
+ * (12, W4 [hidden][2 hidden]) and its norms of the embedding (13), of the
+ * hidden state (14) and of the output (15). */
+static or_layer* layer_ref(or_model* m, int layer) {
+    if (layer >= 0 && layer < m->c.n_layers) return &m->L[layer];
+    if (layer == m->c.n_layers && m->c.draft_vocab > 0) return &m->D;
+    return NULL;
+}
+
+static or_w4* w4_ref(or_model* m, int layer, int kind) {
+    if (kind == 12) return layer == m->c.n_layers && m->c.draft_vocab > 0 ? &m->fuse : NULL;
+    or_layer* L = layer_ref(m, layer);
+    if (!L || kind < 0 || kind > 4) return NULL;
+    return &L->w[kind];
+}
+
 int or_load_w4(or_model* m, int layer, int kind, const uint8_t* codes, const uint16_t* scales) {
-    if (layer < 0 || layer >= m->c.n_layers || kind < 0 || kind > 4) return -1;
-    or_w4* w = &m->L[layer].w[kind];
+    or_w4* w = w4_ref(m, layer, kind);
+    if (!w) return -1;
     memcpy(w->codes, codes, (size_t)(w->rows * w->cols / 2));
     memcpy(w->scales, scales, (size_t)(w->rows * (w->cols / 32) * 2));
     return 0;
@@ -265,8 +317,8 @@ int or_load_w4(or_model* m, int layer, int kind, const uint8_t* codes, const uin
 
 /* quantise fp32 rows [row0, row0+nrows) of a W4 tensor straight into the model */
 int or_quant_w4_into(or_model* m, int layer, int kind, int64_t row0, int64_t nrows, const float* w) {
-    if (layer < 0 || layer >= m->c.n_layers || kind < 0 || kind > 4) return -1;
-    or_w4* W = &m->L[layer].w[kind];
+    or_w4* W = w4_ref(m, layer, kind);
+    if (!W) return -1;
     if (row0 < 0 || row0 + nrows > W->rows) return -1;
     or_quant_w4_rows(w, nrows, W->cols, W->codes + row0 * (W->cols / 2), W->scales + row0 * (W->cols / 32));
     return 0;
@@ -290,9 +342,13 @@ int or_load_vec(or_model* m, int layer, int kind, const float* v, int n) {
     double* dst = NULL;
     int want = 0;
     if (kind == 10) { dst = m->norm_final; want = m->c.hidden; }
-    else {
-        if (layer < 0 || layer >= m->c.n_layers) return -1;
-        or_layer* L = &m->L[layer];
+    else if (kind >= 13 && kind <= 15) {
+        if (layer != m->c.n_layers || m->c.draft_vocab <= 0) return -1;
+        dst = kind == 13 ? m->dn_emb : kind == 14 ? m->dn_hid : m->dn_out;
+        want = m->c.hidden;
+    } else {
+        or_layer* L = layer_ref(m, layer);
+        if (!L) return -1;
         if (kind == 6) { dst = L->norm_mix; want = m->c.hidden; }
         if (kind == 7) { dst = L->norm_ffn; want = m->c.hidden; }
         if (kind == 8) { dst = L->norm_gated; want = m->c.gdn_head_dim; }
@@ -474,9 +530,9 @@ static void kv_record(const double* k, const double* v, const int8_t* signs, int
     free(vr);
 }
 
-/* gated attention: append the current token, attend over positions 0..pos,
+/* gated attention: append the token at cache entry t, attend over entries 0..t,
  * gate each head output by sigmoid(g), project back */
-static void attn_mixer(or_model* m, or_layer* L, const double* xh, double* delta) {
+static void attn_mixer(or_model* m, or_layer* L, int64_t t, const double* xh, double* delta) {
     const or_cfg* c = &m->c;
     int nq = c->attn_q_heads, nkv = c->attn_kv_heads, d = c->attn_head_dim;
     int64_t rows = L->w[0].rows;
@@ -486,7 +542,6 @@ static void attn_mixer(or_model* m, or_layer* L, const double* xh, double* delta
     double* g = q + (int64_t)nq * d;
     double* k = g + (int64_t)nq * d;
     double* v = k + (int64_t)nkv * d;
-    int64_t t = m->pos;
     for (int j = 0; j < nkv; ++j) {
         int64_t base = (t * nkv + j) * d;
         or_kv_encode(k + (int64_t)j * d, v + (int64_t)j * d, m->signs, d, L->kc + base, L->ks + base / 32,
@@ -524,6 +579,20 @@ static void ffn(or_model* m, or_layer* L, const double* xh, double* delta) {
 /* Run every layer at the current position on residual x (in place); append
  * the cache entry, update the recurrent states and advance the position.
  * trace (optional) receives the residual after each layer, [n_layers][H]. */
+/* one pre-norm residual block: x += mixer(norm(x)); x += ffn(norm(x)); an
+ * attention mixer writes cache entry t (xh, dl: scratch of H doubles) */
+static void layer_forward(or_model* m, or_layer* L, int64_t t, double* x, double* xh, double* dl) {
+    const or_cfg* c = &m->c;
+    int64_t H = c->hidden;
+    rmsnorm_a16(x, L->norm_mix, H, c->rms_eps, xh);
+    if (L->type == 'G') gdn_mixer(m, L, xh, dl);
+    else attn_mixer(m, L, t, xh, dl);
+    for (int64_t i = 0; i < H; ++i) x[i] += dl[i];
+    rmsnorm_a16(x, L->norm_ffn, H, c->rms_eps, xh);
+    ffn(m, L, xh, dl);
+    for (int64_t i = 0; i < H; ++i) x[i] += dl[i];
+}
+
 int or_forward_layers(or_model* m, double* x, double* trace) {
     const or_cfg* c = &m->c;
     if (m->pos >= c->max_ctx) return -2;
@@ -531,14 +600,7 @@ int or_forward_layers(or_model* m, double* x, double* trace) {
     double* xh = (double*)malloc(sizeof(double) * H);
     double* dl = (double*)malloc(sizeof(double) * H);
     for (int l = 0; l < c->n_layers; ++l) {
-        or_layer* L = &m->L[l];
-        rmsnorm_a16(x, L->norm_mix, H, c->rms_eps, xh);
-        if (L->type == 'G') gdn_mixer(m, L, xh, dl);
-        else attn_mixer(m, L, xh, dl);
-        for (int64_t i = 0; i < H; ++i) x[i] += dl[i];
-        rmsnorm_a16(x, L->norm_ffn, H, c->rms_eps, xh);
-        ffn(m, L, xh, dl);
-        for (int64_t i = 0; i < H; ++i) x[i] += dl[i];
+        layer_forward(m, &m->L[l], m->pos, x, xh, dl);
         if (trace) memcpy(trace + (int64_t)l * H, x, sizeof(double) * H);
     }
     m->pos++;
@@ -583,6 +645,88 @@ int or_decode_token(or_model* m, int32_t token, double* x_out, double* logits, i
 
 int32_t or_get_pos(const or_model* m) { return m->pos; }
 
+/* ------------------------------------------------------------ draft head
+ * The pages' draft head (page 5, bs178.com llamAmpere article, "为什么它真能这么快"
+ * point 四) proposes tokens from the target's last hidden state and scores them
+ * with a projection restricted to a list of token ids (the vocabulary map);
+ * the target still chooses from the full vocabulary.  Readings: the block
+ * combines the normalised embedding of the current token with the normalised
+ * hidden state through one W4 matrix, runs one gated-attention layer of the
+ * target's shape with its own cache, and scores the normalised result with the
+ * tied int8 table rows of the mapped ids. */
+
+static int cmp_i32(const void* a, const void* b) {
+    int32_t x = *(const int32_t*)a, y = *(const int32_t*)b;
+    return x < y ? -1 : x > y;
+}
+
+/* the map as distinct ids in [0, vocab), stored ascending */
+int or_set_draft_map(or_model* m, const int32_t* ids, int32_t n) {
+    if (m->c.draft_vocab <= 0 || n != m->c.draft_vocab) return -1;
+    int32_t* t = (int32_t*)malloc(sizeof(int32_t) * (size_t)n);
+    memcpy(t, ids, sizeof(int32_t) * (size_t)n);
+    qsort(t, (size_t)n, sizeof(int32_t), cmp_i32);
+    for (int32_t i = 0; i < n; ++i)
+        if (t[i] < 0 || t[i] >= m->c.vocab || (i > 0 && t[i] == t[i - 1])) { free(t); return -1; }
+    memcpy(m->dmap, t, sizeof(int32_t) * (size_t)n);
+    free(t);
+    return 0;
+}
+
+int or_get_draft_map(const or_model* m, int32_t* ids) {
+    if (m->c.draft_vocab <= 0) return -1;
+    memcpy(ids, m->dmap, sizeof(int32_t) * (size_t)m->c.draft_vocab);
+    return 0;
+}
+
+/* One step of the draft head on (token, h): writes cache entry dpos + slot and
+ * attends over entries 0 .. dpos + slot; the entry count dpos is left alone.
+ * x_out (optional): the block's output hidden state [H]; logits (optional):
+ * the mapped scores [draft_vocab] in ascending-id order. */
+int or_draft_step(or_model* m, int32_t token, const double* h, int32_t slot, double* x_out, double* logits) {
+    const or_cfg* c = &m->c;
+    if (c->draft_vocab <= 0 || token < 0 || token >= c->vocab || slot < 0) return -1;
+    int64_t t = (int64_t)m->dpos + slot;
+    if (t >= c->max_ctx) return -2;
+    int64_t H = c->hidden;
+    double* e = (double*)malloc(sizeof(double) * H);
+    double* u = (double*)malloc(sizeof(double) * 2 * H);
+    double* x = (double*)malloc(sizeof(double) * H);
+    double* xh = (double*)malloc(sizeof(double) * H);
+    double* dl = (double*)malloc(sizeof(double) * H);
+    or_embed(m, token, e);
+    rmsnorm_a16(e, m->dn_emb, H, c->rms_eps, u);
+    rmsnorm_a16(h, m->dn_hid, H, c->rms_eps, u + H);
+    gemv_w4(&m->fuse, u, x);
+    layer_forward(m, &m->D, t, x, xh, dl);
+    if (x_out) memcpy(x_out, x, sizeof(double) * H);
+    if (logits) {
+        rmsnorm_a16(x, m->dn_out, H, c->rms_eps, xh);
+        int64_t G = H / 32;
+#pragma omp parallel for schedule(static)
+        for (int32_t i = 0; i < c->draft_vocab; ++i) {
+            const int8_t* cr = m->lm.codes + (int64_t)m->dmap[i] * H;
+            const uint16_t* sr = m->lm.scales + (int64_t)m->dmap[i] * G;
+            double acc = 0.0;
+            for (int64_t g = 0; g < G; ++g) {
+                double sc = or_f16_to_f64(sr[g]);
+                for (int64_t k = 32 * g; k < 32 * g + 32; ++k) acc += ((double)cr[k] * sc) * xh[k];
+            }
+            logits[i] = acc;
+        }
+    }
+    free(e); free(u); free(x); free(xh); free(dl);
+    return 0;
+}
+
+int32_t or_get_dpos(const or_model* m) { return m->dpos; }
+
+int or_set_dpos(or_model* m, int32_t dpos) {
+    if (m->c.draft_vocab <= 0 || dpos < 0 || dpos > m->c.max_ctx) return -1;
+    m->dpos = dpos;
+    return 0;
+}
+
 /* ------------------------------------------------------------ state import / export
  * Logical state: position; per GDN layer fp32 S [nv][dv][dk]; per attention
  * layer K codes int8 [pos][nkv][dh], K scales fp16 [pos][nkv][dh/32], V codes
@@ -603,10 +747,10 @@ int or_get_state_gdn(const or_model* m, int layer, double* S) {
 
 int or_set_state_kv(or_model* m, int layer, int32_t npos, const int8_t* kc, const uint16_t* ks,
                     const int8_t* vc, const uint16_t* vs) {
-    if (layer < 0 || layer >= m->c.n_layers || m->L[layer].type != 'A') return -1;
+    or_layer* L = layer_ref(m, layer);
+    if (!L || L->type != 'A') return -1;
     if (npos < 0 || npos > m->c.max_ctx) return -1;
     int64_t n = (int64_t)npos * m->c.attn_kv_heads * m->c.attn_head_dim;
-    or_layer* L = &m->L[layer];
     memcpy(L->kc, kc, n);
     memcpy(L->vc, vc, n);
     memcpy(L->ks, ks, n / 32 * 2);
@@ -614,12 +758,12 @@ int or_set_state_kv(or_model* m, int layer, int32_t npos, const int8_t* kc, cons
     return 0;
 }
 
-int or_get_state_kv(const or_model* m, int layer, int32_t npos, int8_t* kc, uint16_t* ks, int8_t* vc,
+int or_get_state_kv(or_model* m, int layer, int32_t npos, int8_t* kc, uint16_t* ks, int8_t* vc,
                     uint16_t* vs) {
-    if (layer < 0 || layer >= m->c.n_layers || m->L[layer].type != 'A') return -1;
+    const or_layer* L = layer_ref(m, layer);
+    if (!L || L->type != 'A') return -1;
     if (npos < 0 || npos > m->c.max_ctx) return -1;
     int64_t n = (int64_t)npos * m->c.attn_kv_heads * m->c.attn_head_dim;
-    const or_layer* L = &m->L[layer];
     memcpy(kc, L->kc, n);
     memcpy(vc, L->vc, n);
     memcpy(ks, L->ks, n / 32 * 2);

@@ -71,7 +71,10 @@ class BruteModel:
             else:
                 self.kv[l] = []   # list of (kc, ks, vc, vs) per position, each [nkv][...]
         d = s.attn_head_dim
-        if "A" in s.pattern:
+        self.dpos = 0
+        if getattr(s, "draft_vocab", 0) > 0:
+            self.kv[s.n_layers] = []     # the draft head's cache
+        if "A" in s.pattern or getattr(s, "draft_vocab", 0) > 0:
             D = np.diag(weights[(-1, 11)].astype(np.float64))
             self.R = hadamard(d) @ D / np.sqrt(d)           # v' = R v
             self.Rinv = self.R.T                             # orthogonal
@@ -127,17 +130,38 @@ class BruteModel:
             o[i] = a16((self.Rinv @ (pr @ Vr[:, j, :])) * expit(g[i]))
         return self.W(l, 1) @ o.ravel()
 
-    def forward_layers(self, x):
+    def block(self, l, t, x):
         s = self.s
+        xh = a16(rmsnorm(x, self.w[(l, 6)], s.rms_eps))
+        x = x + (self.gdn(l, xh) if t == "G" else self.attn(l, xh))
+        xh = a16(rmsnorm(x, self.w[(l, 7)], s.rms_eps))
+        h = a16(silu(self.W(l, 2) @ xh) * (self.W(l, 3) @ xh))
+        return x + self.W(l, 4) @ h
+
+    def forward_layers(self, x):
         x = np.array(x, np.float64)
-        for l, t in enumerate(s.pattern):
-            xh = a16(rmsnorm(x, self.w[(l, 6)], s.rms_eps))
-            x = x + (self.gdn(l, xh) if t == "G" else self.attn(l, xh))
-            xh = a16(rmsnorm(x, self.w[(l, 7)], s.rms_eps))
-            h = a16(silu(self.W(l, 2) @ xh) * (self.W(l, 3) @ xh))
-            x = x + self.W(l, 4) @ h
+        for l, t in enumerate(self.s.pattern):
+            x = self.block(l, t, x)
         self.pos += 1
         return x
+
+    def draft_step(self, token, h, slot=0):
+        """Draft head on (token, h), weights at layer index n_layers: the
+        concatenation [norm(embedding); norm(h)] through the fuse matrix, one
+        gated-attention block whose cache keeps dpos + slot earlier entries, and
+        the mapped rows of the int8 table (ids ascending) on the normalised
+        output.  -> (output hidden, mapped logits)"""
+        s = self.s
+        D = s.n_layers
+        u = np.concatenate([a16(rmsnorm(self.embed(token), self.w[(D, 13)], s.rms_eps)),
+                            a16(rmsnorm(np.asarray(h, np.float64), self.w[(D, 14)], s.rms_eps))])
+        x = self.W(D, 12) @ u
+        del self.kv[D][self.dpos + slot:]
+        x = self.block(D, "A", x)
+        c, sc = self.w[(-1, 5)]
+        ids = np.sort(np.asarray(self.w[(D, 16)]))
+        z = dequant_i8(c[ids], sc[ids]) @ a16(rmsnorm(x, self.w[(D, 15)], s.rms_eps))
+        return x, z
 
     def embed(self, token):
         c, sc = self.w[(-1, 5)]

@@ -126,6 +126,15 @@ def tokens(n, vocab, seed, stream=workloads.STREAM_PROMPT, i0=0):
     return out
 
 
+def draft_map(shape, seed):
+    """The draft head's vocabulary map: draft_vocab distinct ids drawn uniformly
+    without replacement from [0, vocab) (the ids with the smallest of one
+    Philox u32 key per id, ties broken by id), returned ascending."""
+    keys = u32(shape.vocab, seed, workloads.STREAM_MAP).astype(np.uint64)
+    order = np.argsort((keys << np.uint64(32)) | np.arange(shape.vocab, dtype=np.uint64), kind="stable")
+    return np.sort(order[:shape.draft_vocab]).astype(np.int32)
+
+
 def signs(n, seed, stream):
     out = np.empty(n, dtype=np.int8)
     host().aw4s_signs(_ptr(out), n, seed, stream)

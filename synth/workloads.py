@@ -28,6 +28,7 @@ class Shape:
     rms_eps: float = 1e-6
     max_ctx: int = 4096
     max_verify: int = 4
+    draft_vocab: int = 0    # ids in the draft head's vocabulary map; 0: no draft head
 
     @property
     def n_layers(self):
@@ -42,14 +43,19 @@ class Shape:
 TOY = Shape(hidden=512, ffn=1536, vocab=4096, pattern="GA", gdn_qk_heads=4, gdn_v_heads=4,
             gdn_head_dim=64, attn_q_heads=4, attn_kv_heads=1, attn_head_dim=64, max_ctx=1024)
 
+# the 27B-shape stack with its built-in draft head, whose output projection
+# covers 65,536 of the 248,320 ids (page 5, bs178.com llamAmpere article, point 四)
 FULL_27B = Shape(hidden=5120, ffn=17408, vocab=248320, pattern="GGGA" * 16, gdn_qk_heads=16,
                  gdn_v_heads=32, gdn_head_dim=128, attn_q_heads=24, attn_kv_heads=4,
-                 attn_head_dim=256, max_ctx=16384)
+                 attn_head_dim=256, max_ctx=16384, draft_vocab=65536)
+
+# the toy stack with a draft head over a quarter of its vocabulary
+TOY_MTP = replace(TOY, draft_vocab=1024)
 
 # Single full-size layers (vocab 0: no embedding and no lm_head, the layer runs on
 # hidden vectors).  pattern length = number of independent weight copies.
-GDN_LAYER = replace(FULL_27B, vocab=0, pattern="G", max_ctx=16)
-ATTN_LAYER = replace(FULL_27B, vocab=0, pattern="A", max_ctx=4096 + 512)
+GDN_LAYER = replace(FULL_27B, vocab=0, pattern="G", max_ctx=16, draft_vocab=0)
+ATTN_LAYER = replace(FULL_27B, vocab=0, pattern="A", max_ctx=4096 + 512, draft_vocab=0)
 
 
 def with_(shape, **kw):
@@ -60,8 +66,10 @@ def with_(shape, **kw):
 # tensor kinds (numbering shared by the C ABI, the oracle and this recipe)
 T_MIX_IN, T_MIX_OUT, T_FFN_GATE, T_FFN_UP, T_FFN_DOWN, T_LM_HEAD = 0, 1, 2, 3, 4, 5
 T_NORM_MIX, T_NORM_FFN, T_NORM_GATED, T_A_BIAS, T_NORM_FINAL, T_RHT_SIGNS = 6, 7, 8, 9, 10, 11
+# draft head, all at layer index n_layers (beside its gated-attention layer's kinds 0-4, 6, 7)
+T_DRAFT_FUSE, T_DRAFT_NORM_EMB, T_DRAFT_NORM_HID, T_DRAFT_NORM_OUT, T_DRAFT_MAP = 12, 13, 14, 15, 16
 
-W4, I8, VEC, SIGNS = "w4", "i8", "vec", "signs"
+W4, I8, VEC, SIGNS, MAP = "w4", "i8", "vec", "signs", "map"
 
 WEIGHT_STD = 0.02       # "weights N(0, 0.02)", read as a standard deviation
 A_BIAS = 2.0            # alpha = sigmoid(a + 2): a ~ N(2, 0.5) once x is unit-RMS
@@ -132,8 +140,23 @@ def tensor_specs(s: Shape, norm_jitter=0.0):
     if s.vocab > 0:
         out.append(TensorSpec(-1, T_LM_HEAD, I8, s.vocab, H, [(0, s.vocab, WEIGHT_STD)]))
         out.append(TensorSpec(-1, T_NORM_FINAL, VEC, 1, H, jitter=norm_jitter))
-    if "A" in s.pattern:
+    if "A" in s.pattern or s.draft_vocab > 0:
         out.append(TensorSpec(-1, T_RHT_SIGNS, SIGNS, 1, s.attn_head_dim))
+    if s.draft_vocab > 0:
+        D = s.n_layers
+        rows = mixer_in_rows(s, "A")
+        out.append(TensorSpec(D, T_MIX_IN, W4, rows, H, [(0, rows, WEIGHT_STD)]))
+        out.append(TensorSpec(D, T_MIX_OUT, W4, H, mixer_out_cols(s, "A"), [(0, H, WEIGHT_STD)]))
+        out.append(TensorSpec(D, T_FFN_GATE, W4, s.ffn, H, [(0, s.ffn, WEIGHT_STD)]))
+        out.append(TensorSpec(D, T_FFN_UP, W4, s.ffn, H, [(0, s.ffn, WEIGHT_STD)]))
+        out.append(TensorSpec(D, T_FFN_DOWN, W4, H, s.ffn, [(0, H, WEIGHT_STD)]))
+        out.append(TensorSpec(D, T_NORM_MIX, VEC, 1, H, jitter=norm_jitter))
+        out.append(TensorSpec(D, T_NORM_FFN, VEC, 1, H, jitter=norm_jitter))
+        out.append(TensorSpec(D, T_DRAFT_FUSE, W4, H, 2 * H, [(0, H, WEIGHT_STD)]))
+        out.append(TensorSpec(D, T_DRAFT_NORM_EMB, VEC, 1, H, jitter=norm_jitter))
+        out.append(TensorSpec(D, T_DRAFT_NORM_HID, VEC, 1, H, jitter=norm_jitter))
+        out.append(TensorSpec(D, T_DRAFT_NORM_OUT, VEC, 1, H, jitter=norm_jitter))
+        out.append(TensorSpec(D, T_DRAFT_MAP, MAP, 1, s.draft_vocab))
     return out
 
 
@@ -142,5 +165,6 @@ STREAM_PROMPT = 0x00F00001
 STREAM_HIDDEN = 0x00F00002      # per-step hidden inputs of the single-layer workloads
 STREAM_UNIFORM = 0x00F00003
 STREAM_DRAFT = 0x00F00004
+STREAM_MAP = 0x00F00005         # the draft head's vocabulary map
 STREAM_STATE = 0x00F00100       # + small offsets for the synthetic cache fill
 DRAFT_LOGIT_STD = 1.43          # about 0.02 * sqrt(5120), the spread of random-weight logits

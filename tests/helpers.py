@@ -8,6 +8,8 @@ from synth import workloads as W
 # a tiny hybrid with grouped heads on both mixer types, for brute-force pins
 TINY = W.Shape(hidden=128, ffn=192, vocab=160, pattern="GAGA", gdn_qk_heads=2, gdn_v_heads=4,
                gdn_head_dim=64, attn_q_heads=4, attn_kv_heads=2, attn_head_dim=64, max_ctx=64)
+# the same with a draft head over 40 of the 160 ids
+TINY_MTP = W.with_(TINY, draft_vocab=40)
 
 
 def logical_weights(shape, seed, norm_jitter=0.0):
@@ -21,6 +23,8 @@ def logical_weights(shape, seed, norm_jitter=0.0):
             out[(spec.layer, spec.kind)] = oracle.quant_i8(synth.matrix_rows(spec, seed, 0, spec.rows))
         elif spec.fmt == W.VEC:
             out[(spec.layer, spec.kind)] = synth.vector(spec, seed).astype(np.float64)
+        elif spec.fmt == W.MAP:
+            out[(spec.layer, spec.kind)] = synth.draft_map(shape, seed)
         else:
             out[(spec.layer, spec.kind)] = synth.signs(spec.cols, seed, spec.stream)
     return out
@@ -29,12 +33,14 @@ def logical_weights(shape, seed, norm_jitter=0.0):
 def oracle_from_logical(shape, lw):
     m = oracle.Model(shape)
     for (layer, kind), v in lw.items():
-        if kind in (0, 1, 2, 3, 4):
+        if kind in (0, 1, 2, 3, 4, W.T_DRAFT_FUSE):
             m.load_w4(layer, kind, *v)
         elif kind == 5:
             m.load_i8(*v)
         elif kind == 11:
             m.load_signs(v)
+        elif kind == W.T_DRAFT_MAP:
+            m.set_draft_map(v)
         else:
             m.load_vec(layer, kind, v)
     return m
