@@ -17,7 +17,8 @@ STATUS = {0: "ok", -1: "AW4_E_INVAL", -2: "AW4_E_ARENA", -3: "AW4_E_NODEVICE", -
 
 T_MIX_IN, T_MIX_OUT, T_FFN_GATE, T_FFN_UP, T_FFN_DOWN, T_LM_HEAD = 0, 1, 2, 3, 4, 5
 T_NORM_MIX, T_NORM_FFN, T_NORM_GATED, T_A_BIAS, T_NORM_FINAL, T_RHT_SIGNS = 6, 7, 8, 9, 10, 11
-PHASE_FFN_GATE_UP, PHASE_FFN_DOWN, PHASE_MIX_IN = 0, 1, 2
+T_DRAFT_FUSE, T_DRAFT_NORM_EMB, T_DRAFT_NORM_HID, T_DRAFT_NORM_OUT, T_DRAFT_MAP = 12, 13, 14, 15, 16
+PHASE_FFN_GATE_UP, PHASE_FFN_DOWN, PHASE_MIX_IN, PHASE_HEAD, PHASE_DRAFT_HEAD = 0, 1, 2, 3, 4
 
 _i32, _i64, _u64, _f32, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_float, ctypes.c_void_p
 
@@ -27,7 +28,7 @@ class Config(ctypes.Structure):
                 ("gdn_qk_heads", _i32), ("gdn_v_heads", _i32), ("gdn_head_dim", _i32),
                 ("attn_q_heads", _i32), ("attn_kv_heads", _i32), ("attn_head_dim", _i32),
                 ("group", _i32), ("max_ctx", _i32), ("max_verify", _i32), ("rms_eps", _f32),
-                ("layer_pattern", ctypes.c_char * 128)]
+                ("layer_pattern", ctypes.c_char * 128), ("draft_vocab", _i32)]
 
     @classmethod
     def from_shape(cls, s):
@@ -38,6 +39,7 @@ class Config(ctypes.Structure):
         c.n_layers = len(s.pattern)
         c.rms_eps = float(s.rms_eps)
         c.layer_pattern = s.pattern.encode()
+        c.draft_vocab = int(getattr(s, "draft_vocab", 0))
         return c
 
 
@@ -58,6 +60,7 @@ _SIGS = {
     "aw4_load_tensor": [_vp, _i32, _i32, _vp, _vp],
     "aw4_export_tensor": [_vp, _i32, _i32, _vp, _vp],
     "aw4_set_vector": [_vp, _i32, _i32, _vp, _i32],
+    "aw4_set_draft_map": [_vp, _vp, _i32],
     "aw4_load_weights": [_vp, _vp, _u64],
     "aw4_reset": [_vp],
     "aw4_prefill": [_vp, _vp, _i32, _vp],
@@ -65,10 +68,13 @@ _SIGS = {
     "aw4_decode_greedy": [_vp, _i32, _i32, _vp],
     "aw4_decode_hidden": [_vp, _vp, _vp],
     "aw4_verify_k": [_vp, _vp, _i32, _vp, _vp, _f32, _vp, _vp],
+    "aw4_draft": [_vp, _i32, _i32, _f32, _vp, _vp, _vp, _vp],
     "aw4_read_hidden": [_vp, _vp],
     "aw4_set_graph": [_vp, _i32],
     "aw4_get_pos": [_vp, ctypes.POINTER(_i32)],
     "aw4_set_pos": [_vp, _i32],
+    "aw4_get_draft_pos": [_vp, ctypes.POINTER(_i32)],
+    "aw4_set_draft_pos": [_vp, _i32],
     "aw4_time_phase": [_vp, _i32, _i32, ctypes.POINTER(_f32), ctypes.POINTER(_u64)],
     "aw4_export_state_gdn": [_vp, _i32, _vp],
     "aw4_import_state_gdn": [_vp, _i32, _vp],
@@ -192,6 +198,11 @@ class Model:
         v = np.ascontiguousarray(vals, np.float32)
         self._rc(lib().aw4_set_vector(self.h, layer, kind, _ptr(v), len(v)), "set_vector")
 
+    def set_draft_map(self, ids):
+        import numpy as np
+        v = np.ascontiguousarray(ids, np.int32)
+        self._rc(lib().aw4_set_draft_map(self.h, _ptr(v), len(v)), "set_draft_map")
+
     def load_weights(self, blob: bytes):
         buf = ctypes.create_string_buffer(blob, len(blob))
         self._rc(lib().aw4_load_weights(self.h, buf, len(blob)), "load_weights")
@@ -243,6 +254,28 @@ class Model:
                                     _ptr(uu) if uu is not None else None, float(temperature), _ptr(out),
                                     ctypes.byref(n)), "verify_k")
         return [int(v) for v in out[:n.value]]
+
+    def draft(self, t0, k, temperature=0.0, u=None, q=None, scores=None):
+        """k drafts from the draft head after the last committed position, t0 the
+        token run next.  q: device fp32 tensor [k, vocab] receiving the draft
+        probabilities (temperature > 0); scores: device fp32 tensor [k,
+        draft_vocab] receiving the mapped scores; u: k uniforms."""
+        import numpy as np
+        uu = np.ascontiguousarray(u, np.float32) if u is not None else None
+        out = np.zeros(4, np.int32)
+        self._rc(lib().aw4_draft(self.h, int(t0), int(k), float(temperature), _ptr(uu) if uu is not None else None,
+                                 q.data_ptr() if q is not None else None,
+                                 scores.data_ptr() if scores is not None else None, _ptr(out)), "draft")
+        return [int(v) for v in out[:k]]
+
+    @property
+    def dpos(self):
+        p = _i32()
+        self._rc(lib().aw4_get_draft_pos(self.h, ctypes.byref(p)), "get_draft_pos")
+        return p.value
+
+    def set_dpos(self, p):
+        self._rc(lib().aw4_set_draft_pos(self.h, p), "set_draft_pos")
 
     def decode_hidden(self, x_in, x_out):
         self._rc(lib().aw4_decode_hidden(self.h, x_in.data_ptr(), x_out.data_ptr()), "decode_hidden")

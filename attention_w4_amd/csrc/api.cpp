@@ -94,6 +94,30 @@ struct aw4_model {
     int nhead_blocks = 0;
     int nsplit = 1;
     int32_t host_pos = 0;
+    // draft head (draft_vocab > 0)
+    LayerBufs D;                    // its gated-attention layer; cache in the state region
+    uint32_t* w_fuse = nullptr;     // [H][2H] W4
+    uint16_t* s_fuse = nullptr;
+    float* dn_emb = nullptr;
+    float* dn_hid = nullptr;
+    float* dn_out = nullptr;
+    int32_t* dmap = nullptr;        // [draft_vocab] ascending ids
+    int32_t* drmap = nullptr;       // [vocab] index into dmap or -1
+    float* xd = nullptr;            // [max_verify][H] the draft block's residuals
+    _Float16* ubuf = nullptr;       // [max_verify][2H] its fp16 inputs
+    float* dscore = nullptr;        // [draft_vocab] mapped scores of the current step
+    float* dpv = nullptr;           // head block partials
+    int32_t* dpi = nullptr;
+    float* dzpart = nullptr;        // [draft chunks]
+    int ndhead_blocks = 0;
+    bool map_set = false;
+    int32_t host_dpos = 0;
+    // what the next draft call feeds before its own entry: the hidden rows of
+    // the committed positions (none, the decode residual, or verify rows) and
+    // the tokens that followed them
+    int pend_src = 0;               // 0 nothing to draft from, 1 x, 2 vx rows 0..pend_n
+    int pend_n = 0;
+    int32_t pend_tok[4] = {0, 0, 0, 0};
     uint64_t state_off = 0, state_bytes = 0;   // recurrent states + caches
     bool use_graph = true;
     hipGraphExec_t g_head = nullptr;
@@ -193,7 +217,31 @@ uint64_t plan_layout(const aw4_config* c, aw4_model* m, uint8_t* base) {
         lm_scales = p.take<uint16_t>((uint64_t)c->vocab * (H / 32) * 2);
         norm_final = p.take<float>(H * 4);
     }
-    float* signs = p.take<float>((uint64_t)(has_a ? c->attn_head_dim : 1) * 4);
+    const bool dh = c->draft_vocab > 0;
+    float* signs = p.take<float>((uint64_t)(has_a || dh ? c->attn_head_dim : 1) * 4);
+    LayerBufs D;
+    uint32_t* w_fuse = nullptr;
+    uint16_t* s_fuse = nullptr;
+    float *dn_emb = nullptr, *dn_hid = nullptr, *dn_out = nullptr;
+    int32_t *dmap = nullptr, *drmap = nullptr;
+    if (dh) {
+        D.type = 'A';
+        D.in_rows = mix_in_rows(c, 'A');
+        D.out_cols = mix_out_cols(c, 'A');
+        if (D.in_rows > max_in) max_in = D.in_rows;
+        w4(D.in_rows, H, &D.w_in, &D.s_in);
+        w4(H, D.out_cols, &D.w_out, &D.s_out);
+        w4(2 * F, H, &D.w_gu, &D.s_gu);
+        w4(H, F, &D.w_down, &D.s_down);
+        D.norm_mix = p.take<float>(H * 4);
+        D.norm_ffn = p.take<float>(H * 4);
+        w4(H, 2 * H, &w_fuse, &s_fuse);
+        dn_emb = p.take<float>(H * 4);
+        dn_hid = p.take<float>(H * 4);
+        dn_out = p.take<float>(H * 4);
+        dmap = p.take<int32_t>((uint64_t)c->draft_vocab * 4);
+        drmap = p.take<int32_t>((uint64_t)c->vocab * 4);
+    }
     // recurrent states and caches: one contiguous region, cleared by reset
     p.off = (p.off + 255) & ~uint64_t(255);
     const uint64_t state_off = p.off;
@@ -209,6 +257,13 @@ uint64_t plan_layout(const aw4_config* c, aw4_model* m, uint8_t* base) {
             b.vs = p.take<uint16_t>(n / 32 * 2);
         }
     }
+    if (dh) {
+        const uint64_t n = (uint64_t)c->attn_kv_heads * c->max_ctx * c->attn_head_dim;
+        D.kc = p.take<int8_t>(n);
+        D.ks = p.take<uint16_t>(n / 32 * 2);
+        D.vc = p.take<uint32_t>(n / 32 * 12);
+        D.vs = p.take<uint16_t>(n / 32 * 2);
+    }
     p.off = (p.off + 255) & ~uint64_t(255);
     const uint64_t state_bytes = p.off - state_off;
     Ctl* ctl = p.take<Ctl>(sizeof(Ctl));
@@ -218,10 +273,11 @@ uint64_t plan_layout(const aw4_config* c, aw4_model* m, uint8_t* base) {
     const int64_t hlen = F > (int64_t)c->attn_q_heads * c->attn_head_dim ? F : (int64_t)c->attn_q_heads * c->attn_head_dim;
     // (hlen also sizes the per-token FFN buffers of the verify pass)
     _Float16* hbuf = p.take<_Float16>((uint64_t)hlen * 2);
-    _Float16* abuf = p.take<_Float16>((uint64_t)(has_a ? c->attn_q_heads * c->attn_head_dim : 1) * 2);
+    _Float16* abuf = p.take<_Float16>((uint64_t)(has_a || dh ? c->attn_q_heads * c->attn_head_dim : 1) * 2);
     const int nsplit = nsplit_for(c->max_ctx, c->attn_kv_heads);
     // split partials: one row per (token of a sweep, q head), up to 4 tokens
-    float* part = p.take<float>((uint64_t)(has_a ? kSweepRows * c->attn_q_heads : 1) * nsplit * (c->attn_head_dim + 2) * 4);
+    float* part = p.take<float>((uint64_t)(has_a || dh ? kSweepRows * c->attn_q_heads : 1) * nsplit *
+                                (c->attn_head_dim + 2) * 4);
     float* logits = nullptr;
     float* pv = nullptr;
     int32_t* pi = nullptr;
@@ -239,10 +295,10 @@ uint64_t plan_layout(const aw4_config* c, aw4_model* m, uint8_t* base) {
     float* vproj_a = nullptr;
     for (int l = 0; l < c->n_layers; ++l)
         if (L[l].type == 'G') vproj_g.push_back(p.take<float>((uint64_t)MV * L[l].in_rows * 4));
-    if (has_a) vproj_a = p.take<float>((uint64_t)MV * mix_in_rows(c, 'A') * 4);
+    if (has_a || dh) vproj_a = p.take<float>((uint64_t)MV * mix_in_rows(c, 'A') * 4);
     float* vo = p.take<float>((uint64_t)MV * (has_g ? c->gdn_v_heads * c->gdn_head_dim : 1) * 4);
     _Float16* vh = p.take<_Float16>((uint64_t)MV * hlen * 2);
-    _Float16* va = p.take<_Float16>((uint64_t)MV * (has_a ? c->attn_q_heads * c->attn_head_dim : 1) * 2);
+    _Float16* va = p.take<_Float16>((uint64_t)MV * (has_a || dh ? c->attn_q_heads * c->attn_head_dim : 1) * 2);
     float *vlogits = nullptr, *vpv = nullptr, *vzpart = nullptr, *vwpart = nullptr;
     int32_t* vpi = nullptr;
     if (c->vocab > 0) {
@@ -252,8 +308,36 @@ uint64_t plan_layout(const aw4_config* c, aw4_model* m, uint8_t* base) {
         vzpart = p.take<float>((uint64_t)MV * accept_blocks(c->vocab) * 4);
         vwpart = p.take<float>((uint64_t)MV * accept_blocks(c->vocab) * 4);
     }
+    float *xd = nullptr, *dscore = nullptr, *dpv = nullptr, *dzpart = nullptr;
+    _Float16* ubuf = nullptr;
+    int32_t* dpi = nullptr;
+    int ndhb = 0;
+    if (dh) {
+        xd = p.take<float>((uint64_t)MV * H * 4);
+        ubuf = p.take<_Float16>((uint64_t)MV * 2 * H * 2);
+        dscore = p.take<float>((uint64_t)c->draft_vocab * 4);
+        ndhb = head_blocks(c->draft_vocab);
+        dpv = p.take<float>((uint64_t)ndhb * 4);
+        dpi = p.take<int32_t>((uint64_t)ndhb * 4);
+        dzpart = p.take<float>((uint64_t)draft_chunks(c->draft_vocab) * 4);
+    }
     p.off = (p.off + 255) & ~uint64_t(255);
     if (m) {
+        m->D = D;
+        m->w_fuse = w_fuse;
+        m->s_fuse = s_fuse;
+        m->dn_emb = dn_emb;
+        m->dn_hid = dn_hid;
+        m->dn_out = dn_out;
+        m->dmap = dmap;
+        m->drmap = drmap;
+        m->xd = xd;
+        m->ubuf = ubuf;
+        m->dscore = dscore;
+        m->dpv = dpv;
+        m->dpi = dpi;
+        m->dzpart = dzpart;
+        m->ndhead_blocks = ndhb;
         m->vx = vx;
         m->vproj_g = vproj_g;
         m->vproj_a = vproj_a;
@@ -303,6 +387,11 @@ const char* check_config(const aw4_config* c) {
         if (c->layer_pattern[i] == 'G') g = true;
         else if (c->layer_pattern[i] == 'A') a = true;
         else return "layer_pattern letters must be 'G' or 'A'";
+    }
+    if (c->draft_vocab < 0) return "draft_vocab must be >= 0";
+    if (c->draft_vocab > 0) {
+        if (c->vocab <= 0 || c->draft_vocab > c->vocab) return "draft_vocab must be in [0, vocab]";
+        a = true;   // the draft head's block has the attention layers' shape
     }
     if (g) {
         if (c->gdn_head_dim != 64 && c->gdn_head_dim != 128) return "gdn_head_dim must be 64 or 128";
@@ -365,9 +454,16 @@ int mat_ref(aw4_model* m, int layer, int kind, MatRef* r) {
         r->cols = c->hidden;
         return AW4_OK;
     }
-    if (kind < 0 || kind > 4 || layer < 0 || layer >= c->n_layers) return fail(m, AW4_E_INVAL, "bad layer/kind");
-    LayerBufs& b = m->L[layer];
     const int64_t H = c->hidden, F = c->ffn;
+    const bool draft_layer = c->draft_vocab > 0 && layer == c->n_layers;
+    if (kind == AW4_T_DRAFT_FUSE) {
+        if (!draft_layer) return fail(m, AW4_E_INVAL, "the draft fuse matrix sits at layer n_layers of a draft model");
+        *r = {m->w_fuse, nullptr, m->s_fuse, H, 2 * H, 1};
+        return AW4_OK;
+    }
+    if (kind < 0 || kind > 4 || layer < 0 || (layer >= c->n_layers && !draft_layer))
+        return fail(m, AW4_E_INVAL, "bad layer/kind");
+    LayerBufs& b = draft_layer ? m->D : m->L[layer];
     switch (kind) {
         case AW4_T_MIX_IN: *r = {b.w_in, nullptr, b.s_in, b.in_rows, H, 1}; break;
         case AW4_T_MIX_OUT: *r = {b.w_out, nullptr, b.s_out, H, b.out_cols, 1}; break;
@@ -379,22 +475,27 @@ int mat_ref(aw4_model* m, int layer, int kind, MatRef* r) {
 }
 
 // ---------------------------------------------------------------- step sequence
-int enqueue_layers(aw4_model* m) {
+// One pre-norm block on the single residual x: mixer input projection, the
+// mixer (GDN step, or attention over the cache of committed length *posp with
+// the token appended at *posp + pos_offset), its output projection and the FFN,
+// both added to x.
+int enqueue_block(aw4_model* m, LayerBufs& b, float* x, const int32_t* posp, int pos_offset) {
     const aw4_config* c = &m->cfg;
     hipStream_t s = m->stream;
     const int H = c->hidden, F = c->ffn;
-    for (int l = 0; l < c->n_layers; ++l) {
-        LayerBufs& b = m->L[l];
+    {
         GemvArgs gi{};
         gi.codes = b.w_in;
         gi.scales = b.s_in;
         gi.rows = (int)b.in_rows;
         gi.K = H;
-        gi.x = m->x;
+        gi.x = x;
         gi.nw = b.norm_mix;
         gi.eps = c->rms_eps;
         gi.y = m->proj;
         HIPCHK(m, launch_gemv(PRO_NORM, EPI_STORE, gi, s));
+    }
+    {
         if (b.type == 'G') {
             GdnArgs ga{m->proj, b.a_bias, b.S, m->obuf, c->gdn_qk_heads, c->gdn_v_heads, c->gdn_head_dim, c->rms_eps};
             HIPCHK(m, launch_gdn(ga, s));
@@ -408,10 +509,11 @@ int enqueue_layers(aw4_model* m) {
             go.z = m->proj + 2LL * c->gdn_qk_heads * c->gdn_head_dim + (int64_t)c->gdn_v_heads * c->gdn_head_dim;
             go.gated_d = c->gdn_head_dim;
             go.eps = c->rms_eps;
-            go.y = m->x;
+            go.y = x;
             HIPCHK(m, launch_gemv(PRO_GATED, EPI_RESID, go, s));
         } else {
             AttnArgs aa{};
+            aa.pos_offset = pos_offset;
             aa.nt = 1;
             aa.append = 1;
             aa.proj = m->proj;
@@ -420,7 +522,7 @@ int enqueue_layers(aw4_model* m) {
             aa.vc = b.vc;
             aa.vs = b.vs;
             aa.signs = m->signs;
-            aa.ctl = m->ctl;
+            aa.pos = posp;
             aa.part = m->part;
             aa.prow = kSweepRows * c->attn_q_heads;
             aa.max_ctx = c->max_ctx;
@@ -429,7 +531,7 @@ int enqueue_layers(aw4_model* m) {
             aa.d = c->attn_head_dim;
             aa.nsplit = m->nsplit;
             HIPCHK(m, launch_attn(aa, s));
-            CombineArgs ca{0, 1, 0, m->part, m->proj, m->signs, m->ctl, m->abuf, aa.prow, c->attn_q_heads,
+            CombineArgs ca{pos_offset, 1, 0, m->part, m->proj, m->signs, posp, m->abuf, aa.prow, c->attn_q_heads,
                            c->attn_kv_heads, c->attn_head_dim, m->nsplit};
             HIPCHK(m, launch_combine(ca, s));
             GemvArgs go{};
@@ -438,7 +540,7 @@ int enqueue_layers(aw4_model* m) {
             go.rows = H;
             go.K = (int)b.out_cols;
             go.h = m->abuf;
-            go.y = m->x;
+            go.y = x;
             HIPCHK(m, launch_gemv(PRO_LOADH, EPI_RESID, go, s));
         }
         GemvArgs gf{};
@@ -446,7 +548,7 @@ int enqueue_layers(aw4_model* m) {
         gf.scales = b.s_gu;
         gf.rows = 2 * F;
         gf.K = H;
-        gf.x = m->x;
+        gf.x = x;
         gf.nw = b.norm_ffn;
         gf.eps = c->rms_eps;
         gf.hout = m->hbuf;
@@ -457,8 +559,16 @@ int enqueue_layers(aw4_model* m) {
         gd.rows = H;
         gd.K = F;
         gd.h = m->hbuf;
-        gd.y = m->x;
+        gd.y = x;
         HIPCHK(m, launch_gemv(PRO_LOADH, EPI_RESID, gd, s));
+    }
+    return AW4_OK;
+}
+
+int enqueue_layers(aw4_model* m) {
+    for (int l = 0; l < m->cfg.n_layers; ++l) {
+        int rc = enqueue_block(m, m->L[l], m->x, &m->ctl->pos, 0);
+        if (rc) return rc;
     }
     return AW4_OK;
 }
@@ -490,9 +600,75 @@ int enqueue_phase(aw4_model* m, int phase, int l, uint64_t* bytes) {
             *bytes = w4b(b.in_rows, H) + (uint64_t)H * 8 + (uint64_t)b.in_rows * 4;
             HIPCHK(m, launch_gemv(PRO_NORM, EPI_STORE, g, s));
             break;
+        case AW4_PHASE_HEAD:
+        case AW4_PHASE_DRAFT_HEAD: {
+            // int8 rows (+ fp16 scales) of the full table or of the mapped ids, the
+            // normalised input, one fp32 score per row
+            const bool mapped = phase == AW4_PHASE_DRAFT_HEAD;
+            if (c->vocab <= 0 || (mapped && (c->draft_vocab <= 0 || !m->map_set)))
+                return fail(m, AW4_E_STATE, "no such head");
+            const int rows = mapped ? c->draft_vocab : c->vocab;
+            HeadArgs ha{m->lm_codes, m->lm_scales, mapped ? m->dmap : nullptr, rows, H, m->x,
+                        mapped ? m->dn_out : m->norm_final, c->rms_eps, mapped ? m->dscore : m->logits,
+                        mapped ? m->dpv : m->pv, mapped ? m->dpi : m->pi};
+            *bytes = (uint64_t)rows * (H + H / 16) + (uint64_t)H * 8 + (uint64_t)rows * (mapped ? 8 : 4);
+            HIPCHK(m, launch_head(ha, s));
+            break;
+        }
         default:
             return fail(m, AW4_E_INVAL, "unknown phase");
     }
+    return AW4_OK;
+}
+
+// Gated attention of M tokens at cache positions *posp .. *posp + M - 1 (their
+// projections at proj, rows in_rows apart): all M tokens' K and V are appended
+// first, then sweeps of up to tps tokens read the cache (each token masked to
+// its own position); the o-projection adds into the M residuals at x.
+int enqueue_attn_multi(aw4_model* m, LayerBufs& b, int M, float* x, float* proj, const int32_t* posp) {
+    const aw4_config* c = &m->cfg;
+    hipStream_t s = m->stream;
+    const int H = c->hidden;
+    const int64_t od = (int64_t)c->attn_q_heads * c->attn_head_dim;
+    AttnArgs aa{};
+    aa.nt = M;
+    aa.sproj = b.in_rows;
+    aa.proj = proj;
+    aa.kc = b.kc; aa.ks = b.ks; aa.vc = b.vc; aa.vs = b.vs;
+    aa.signs = m->signs; aa.pos = posp; aa.part = m->part; aa.prow = kSweepRows * c->attn_q_heads;
+    aa.max_ctx = c->max_ctx; aa.nq = c->attn_q_heads; aa.nkv = c->attn_kv_heads;
+    aa.d = c->attn_head_dim; aa.nsplit = m->nsplit;
+    HIPCHK(m, launch_append(aa, s));
+    const int tps = attn_tokens_per_sweep(c->attn_head_dim, c->attn_q_heads, c->attn_kv_heads);
+    for (int t = 0; t < M; t += tps) {
+        aa.pos_offset = t;
+        aa.nt = std::min(tps, M - t);
+        aa.proj = proj + (int64_t)t * b.in_rows;
+        HIPCHK(m, launch_attn(aa, s));
+        CombineArgs ca{t, aa.nt, b.in_rows, m->part, aa.proj, m->signs, posp, m->va + t * od, aa.prow,
+                       c->attn_q_heads, c->attn_kv_heads, c->attn_head_dim, m->nsplit};
+        HIPCHK(m, launch_combine(ca, s));
+    }
+    GemvMultiArgs go{};
+    go.codes = b.w_out; go.scales = b.s_out; go.rows = H; go.K = (int)b.out_cols; go.M = M;
+    go.h = m->va; go.sh = od; go.y = x; go.sy = H;
+    HIPCHK(m, launch_gemv_multi(PRO_LOADH, EPI_RESID, go, s));
+    return AW4_OK;
+}
+
+// FFN of M residuals at x (rows H apart), added into them
+int enqueue_ffn_multi(aw4_model* m, LayerBufs& b, int M, float* x) {
+    const aw4_config* c = &m->cfg;
+    hipStream_t s = m->stream;
+    const int H = c->hidden, F = c->ffn;
+    GemvMultiArgs gf{};
+    gf.codes = b.w_gu; gf.scales = b.s_gu; gf.rows = 2 * F; gf.K = H; gf.M = M;
+    gf.x = x; gf.sx = H; gf.nw = b.norm_ffn; gf.eps = c->rms_eps; gf.hout = m->vh; gf.so = m->hlen;
+    HIPCHK(m, launch_gemv_multi(PRO_NORM, EPI_SWIGLU, gf, s));
+    GemvMultiArgs gd{};
+    gd.codes = b.w_down; gd.scales = b.s_down; gd.rows = H; gd.K = F; gd.M = M;
+    gd.h = m->vh; gd.sh = m->hlen; gd.y = x; gd.sy = H;
+    HIPCHK(m, launch_gemv_multi(PRO_LOADH, EPI_RESID, gd, s));
     return AW4_OK;
 }
 
@@ -502,7 +678,7 @@ int enqueue_phase(aw4_model* m, int phase, int l, uint64_t* bytes) {
 int enqueue_verify(aw4_model* m, int M, int k, const float* dev_q, float temperature) {
     const aw4_config* c = &m->cfg;
     hipStream_t s = m->stream;
-    const int H = c->hidden, F = c->ffn;
+    const int H = c->hidden;
     HIPCHK(m, launch_embed_multi(m->lm_codes, m->lm_scales, H, m->ctl, M, m->vx, s));
     int gi_layer = 0;
     for (int l = 0; l < c->n_layers; ++l) {
@@ -526,41 +702,11 @@ int enqueue_verify(aw4_model* m, int M, int k, const float* dev_q, float tempera
             HIPCHK(m, launch_gemv_multi(PRO_GATED, EPI_RESID, go, s));
             ++gi_layer;
         } else {
-            // all M tokens' K and V first, then sweeps of up to tps tokens over
-            // the cache (each token masked to its own position)
-            const int64_t od = (int64_t)c->attn_q_heads * c->attn_head_dim;
-            AttnArgs aa{};
-            aa.nt = M;
-            aa.sproj = b.in_rows;
-            aa.proj = proj;
-            aa.kc = b.kc; aa.ks = b.ks; aa.vc = b.vc; aa.vs = b.vs;
-            aa.signs = m->signs; aa.ctl = m->ctl; aa.part = m->part; aa.prow = kSweepRows * c->attn_q_heads;
-            aa.max_ctx = c->max_ctx; aa.nq = c->attn_q_heads; aa.nkv = c->attn_kv_heads;
-            aa.d = c->attn_head_dim; aa.nsplit = m->nsplit;
-            HIPCHK(m, launch_append(aa, s));
-            const int tps = attn_tokens_per_sweep(c->attn_head_dim, c->attn_q_heads, c->attn_kv_heads);
-            for (int t = 0; t < M; t += tps) {
-                aa.pos_offset = t;
-                aa.nt = std::min(tps, M - t);
-                aa.proj = proj + (int64_t)t * b.in_rows;
-                HIPCHK(m, launch_attn(aa, s));
-                CombineArgs ca{t, aa.nt, b.in_rows, m->part, aa.proj, m->signs, m->ctl, m->va + t * od, aa.prow,
-                               c->attn_q_heads, c->attn_kv_heads, c->attn_head_dim, m->nsplit};
-                HIPCHK(m, launch_combine(ca, s));
-            }
-            GemvMultiArgs go{};
-            go.codes = b.w_out; go.scales = b.s_out; go.rows = H; go.K = (int)b.out_cols; go.M = M;
-            go.h = m->va; go.sh = od; go.y = m->vx; go.sy = H;
-            HIPCHK(m, launch_gemv_multi(PRO_LOADH, EPI_RESID, go, s));
+            int rc = enqueue_attn_multi(m, b, M, m->vx, proj, &m->ctl->pos);
+            if (rc) return rc;
         }
-        GemvMultiArgs gf{};
-        gf.codes = b.w_gu; gf.scales = b.s_gu; gf.rows = 2 * F; gf.K = H; gf.M = M;
-        gf.x = m->vx; gf.sx = H; gf.nw = b.norm_ffn; gf.eps = c->rms_eps; gf.hout = m->vh; gf.so = m->hlen;
-        HIPCHK(m, launch_gemv_multi(PRO_NORM, EPI_SWIGLU, gf, s));
-        GemvMultiArgs gd{};
-        gd.codes = b.w_down; gd.scales = b.s_down; gd.rows = H; gd.K = F; gd.M = M;
-        gd.h = m->vh; gd.sh = m->hlen; gd.y = m->vx; gd.sy = H;
-        HIPCHK(m, launch_gemv_multi(PRO_LOADH, EPI_RESID, gd, s));
+        int rc = enqueue_ffn_multi(m, b, M, m->vx);
+        if (rc) return rc;
     }
     HeadMultiArgs ha{m->lm_codes, m->lm_scales, c->vocab, c->hidden, M, m->vx, m->norm_final, c->rms_eps,
                      m->vlogits, m->vpv, m->vpi};
@@ -594,13 +740,64 @@ int enqueue_step(aw4_model* m, bool head) {
     int rc = enqueue_layers(m);
     if (rc) return rc;
     if (head) {
-        HeadArgs ha{m->lm_codes, m->lm_scales, c->vocab, c->hidden, m->x, m->norm_final, c->rms_eps,
+        HeadArgs ha{m->lm_codes, m->lm_scales, nullptr, c->vocab, c->hidden, m->x, m->norm_final, c->rms_eps,
                     m->logits, m->pv, m->pi};
         HIPCHK(m, launch_head(ha, s));
         HIPCHK(m, launch_head_final(m->pv, m->pi, m->nhead_blocks, m->ctl, m->ring, m->ring_cap, s));
     } else {
         HIPCHK(m, launch_advance(m->ctl, s));
     }
+    return AW4_OK;
+}
+
+// The draft head's block on M entries (page 5, bs178.com llamAmpere article,
+// point 四; block structure a reading): input from token tok[i] (device) and
+// hidden hin + i sh, the fuse projection into xd rows 0..M-1, then its
+// gated-attention block over its own cache, the entries written at
+// ctl->dpos + pos_offset + i.
+int enqueue_draft_block(aw4_model* m, int M, const int32_t* tok, const float* hin, int64_t sh, int pos_offset) {
+    const aw4_config* c = &m->cfg;
+    hipStream_t s = m->stream;
+    const int H = c->hidden;
+    DraftEmbedArgs de{m->lm_codes, m->lm_scales, tok, hin, sh, m->dn_emb, m->dn_hid, m->ubuf, H, M, c->rms_eps};
+    HIPCHK(m, launch_draft_embed(de, s));
+    if (M == 1) {
+        GemvArgs gf{};
+        gf.codes = m->w_fuse; gf.scales = m->s_fuse; gf.rows = H; gf.K = 2 * H; gf.h = m->ubuf; gf.y = m->xd;
+        HIPCHK(m, launch_gemv(PRO_LOADH, EPI_STORE, gf, s));
+        return enqueue_block(m, m->D, m->xd, &m->ctl->dpos, pos_offset);
+    }
+    if (pos_offset != 0) return fail(m, AW4_E_INVAL, "multi-entry draft steps start at the committed length");
+    LayerBufs& b = m->D;
+    GemvMultiArgs gf{};
+    gf.codes = m->w_fuse; gf.scales = m->s_fuse; gf.rows = H; gf.K = 2 * H; gf.M = M;
+    gf.h = m->ubuf; gf.sh = 2 * H; gf.y = m->xd; gf.sy = H;
+    HIPCHK(m, launch_gemv_multi(PRO_LOADH, EPI_STORE, gf, s));
+    GemvMultiArgs gi{};
+    gi.codes = b.w_in; gi.scales = b.s_in; gi.rows = (int)b.in_rows; gi.K = H; gi.M = M;
+    gi.x = m->xd; gi.sx = H; gi.nw = b.norm_mix; gi.eps = c->rms_eps; gi.y = m->vproj_a; gi.sy = b.in_rows;
+    HIPCHK(m, launch_gemv_multi(PRO_NORM, EPI_STORE, gi, s));
+    int rc = enqueue_attn_multi(m, b, M, m->xd, m->vproj_a, &m->ctl->dpos);
+    if (rc) return rc;
+    return enqueue_ffn_multi(m, b, M, m->xd);
+}
+
+// Mapped scores of xd row `row` (the draft output norm, then the int8 table
+// rows of the map) and the choice of draft j; commit entries are added to the
+// draft cache length once the step's cache reads are done.
+int enqueue_draft_select(aw4_model* m, int row, int j, int commit, float temperature, float* q_row, float* z_row) {
+    const aw4_config* c = &m->cfg;
+    hipStream_t s = m->stream;
+    float* z = z_row ? z_row : m->dscore;
+    HeadArgs ha{m->lm_codes, m->lm_scales, m->dmap, c->draft_vocab, c->hidden, m->xd + (int64_t)row * c->hidden,
+                m->dn_out, c->rms_eps, z, m->dpv, m->dpi};
+    HIPCHK(m, launch_head(ha, s));
+    DraftSelArgs ds{};
+    ds.ctl = m->ctl; ds.z = z; ds.pv = m->dpv; ds.pi = m->dpi; ds.nb = m->ndhead_blocks;
+    ds.map = m->dmap; ds.rmap = m->drmap; ds.Vd = c->draft_vocab; ds.V = c->vocab; ds.j = j; ds.commit = commit;
+    ds.greedy = temperature == 0.f; ds.inv_t = temperature == 0.f ? 1.f : 1.f / temperature;
+    ds.zpart = m->dzpart; ds.q = q_row;
+    HIPCHK(m, launch_draft_select(ds, s));
     return AW4_OK;
 }
 
@@ -637,6 +834,14 @@ void drop_graphs(aw4_model* m) {
 int check_model(aw4_model* m) {
     if (!m) return AW4_E_INVAL;
     return AW4_OK;
+}
+
+// the attention layer whose cache a state call names (n_layers: the draft head's)
+LayerBufs* kv_layer(aw4_model* m, int layer) {
+    if (!m) return nullptr;
+    if (layer >= 0 && layer < m->cfg.n_layers) return m->L[layer].type == 'A' ? &m->L[layer] : nullptr;
+    if (layer == m->cfg.n_layers && m->cfg.draft_vocab > 0) return &m->D;
+    return nullptr;
 }
 
 }  // namespace
@@ -709,7 +914,7 @@ int aw4_tensor_shape(const aw4_model* mc, int32_t layer, int32_t kind, int64_t* 
     aw4_model* m = const_cast<aw4_model*>(mc);
     if (check_model(m) || !rows || !cols) return AW4_E_INVAL;
     const aw4_config* c = &m->cfg;
-    if (kind >= 0 && kind <= 5) {
+    if ((kind >= 0 && kind <= 5) || kind == AW4_T_DRAFT_FUSE) {
         MatRef r;
         int rc = mat_ref(m, layer, kind, &r);
         if (rc) return rc;
@@ -725,6 +930,12 @@ int aw4_tensor_shape(const aw4_model* mc, int32_t layer, int32_t kind, int64_t* 
         if (kind == AW4_T_NORM_MIX || kind == AW4_T_NORM_FFN) n = c->hidden;
         if (kind == AW4_T_NORM_GATED && t == 'G') n = c->gdn_head_dim;
         if (kind == AW4_T_A_BIAS && t == 'G') n = c->gdn_v_heads;
+    }
+    if (c->draft_vocab > 0 && layer == c->n_layers) {
+        if (kind == AW4_T_NORM_MIX || kind == AW4_T_NORM_FFN || kind == AW4_T_DRAFT_NORM_EMB ||
+            kind == AW4_T_DRAFT_NORM_HID || kind == AW4_T_DRAFT_NORM_OUT)
+            n = c->hidden;
+        if (kind == AW4_T_DRAFT_MAP) n = c->draft_vocab;
     }
     if (n < 0) return fail(m, AW4_E_INVAL, "no such tensor");
     *rows = 1;
@@ -801,20 +1012,43 @@ int aw4_set_vector(aw4_model* m, int32_t layer, int32_t kind, const float* vals,
     int64_t rows = 0, cols = 0;
     int rc = aw4_tensor_shape(m, layer, kind, &rows, &cols);
     if (rc) return rc;
-    if (kind < 6 || n != cols) return fail(m, AW4_E_INVAL, "vector length mismatch");
+    if (kind < 6 || kind == AW4_T_DRAFT_FUSE || kind == AW4_T_DRAFT_MAP || n != cols)
+        return fail(m, AW4_E_INVAL, "vector length mismatch");
     float* dst = nullptr;
     if (kind == AW4_T_NORM_FINAL) dst = m->norm_final;
+    else if (kind == AW4_T_DRAFT_NORM_EMB) dst = m->dn_emb;
+    else if (kind == AW4_T_DRAFT_NORM_HID) dst = m->dn_hid;
+    else if (kind == AW4_T_DRAFT_NORM_OUT) dst = m->dn_out;
     else if (kind == AW4_T_RHT_SIGNS) {
         for (int i = 0; i < n; ++i)
             if (vals[i] != 1.0f && vals[i] != -1.0f) return fail(m, AW4_E_INVAL, "rotation signs must be +-1");
         dst = m->signs;
     } else {
-        LayerBufs& b = m->L[layer];
+        LayerBufs& b = layer == m->cfg.n_layers ? m->D : m->L[layer];
         dst = kind == AW4_T_NORM_MIX ? b.norm_mix : kind == AW4_T_NORM_FFN ? b.norm_ffn
               : kind == AW4_T_NORM_GATED ? b.norm_gated : b.a_bias;
     }
     HIPCHK(m, hipStreamSynchronize(m->stream));
     HIPCHK(m, hipMemcpy(dst, vals, (size_t)n * 4, hipMemcpyHostToDevice));
+    return AW4_OK;
+}
+
+int aw4_set_draft_map(aw4_model* m, const int32_t* ids, int32_t n) {
+    if (check_model(m) || !ids) return AW4_E_INVAL;
+    const aw4_config* c = &m->cfg;
+    if (c->draft_vocab <= 0) return fail(m, AW4_E_STATE, "the model has no draft head");
+    if (n != c->draft_vocab) return fail(m, AW4_E_INVAL, "the map must hold draft_vocab ids");
+    std::vector<int32_t> sorted(ids, ids + n);
+    std::sort(sorted.begin(), sorted.end());
+    for (int i = 0; i < n; ++i)
+        if (sorted[i] < 0 || sorted[i] >= c->vocab || (i > 0 && sorted[i] == sorted[i - 1]))
+            return fail(m, AW4_E_INVAL, "map ids must be distinct and in [0, vocab)");
+    std::vector<int32_t> rmap((size_t)c->vocab, -1);
+    for (int i = 0; i < n; ++i) rmap[(size_t)sorted[i]] = i;
+    HIPCHK(m, hipStreamSynchronize(m->stream));
+    HIPCHK(m, hipMemcpy(m->dmap, sorted.data(), (size_t)n * 4, hipMemcpyHostToDevice));
+    HIPCHK(m, hipMemcpy(m->drmap, rmap.data(), rmap.size() * 4, hipMemcpyHostToDevice));
+    m->map_set = true;
     return AW4_OK;
 }
 
@@ -829,7 +1063,7 @@ int aw4_load_weights(aw4_model* m, const void* blob, uint64_t bytes) {
     uint32_t ver;
     memcpy(&ver, p, 4);
     p += 4;
-    if (ver != 1) return fail(m, AW4_E_FORMAT, "unsupported blob version");
+    if (ver != 2) return fail(m, AW4_E_FORMAT, "unsupported blob version");
     aw4_config bc;
     memcpy(&bc, p, sizeof(bc));
     p += sizeof(bc);
@@ -837,7 +1071,7 @@ int aw4_load_weights(aw4_model* m, const void* blob, uint64_t bytes) {
     if (bc.hidden != c->hidden || bc.ffn != c->ffn || bc.vocab != c->vocab || bc.n_layers != c->n_layers ||
         bc.gdn_qk_heads != c->gdn_qk_heads || bc.gdn_v_heads != c->gdn_v_heads || bc.gdn_head_dim != c->gdn_head_dim ||
         bc.attn_q_heads != c->attn_q_heads || bc.attn_kv_heads != c->attn_kv_heads ||
-        bc.attn_head_dim != c->attn_head_dim || bc.group != c->group ||
+        bc.attn_head_dim != c->attn_head_dim || bc.group != c->group || bc.draft_vocab != c->draft_vocab ||
         strncmp(bc.layer_pattern, c->layer_pattern, 128) != 0)
         return fail(m, AW4_E_FORMAT, "blob was made for another config");
     uint32_t count;
@@ -859,7 +1093,12 @@ int aw4_load_weights(aw4_model* m, const void* blob, uint64_t bytes) {
         if (aw4_tensor_shape(m, layer, kind, &er, &ec) || er != rows || ec != cols)
             return fail(m, AW4_E_FORMAT, "tensor shape does not match the config");
         int rc;
-        if (kind <= 5) {
+        if (kind == AW4_T_DRAFT_MAP) {
+            if (nb != (uint64_t)cols * 4) return fail(m, AW4_E_FORMAT, "map payload size mismatch");
+            std::vector<int32_t> v((size_t)cols);
+            memcpy(v.data(), p, (size_t)nb);
+            rc = aw4_set_draft_map(m, v.data(), (int32_t)cols);
+        } else if (kind <= 5 || kind == AW4_T_DRAFT_FUSE) {
             const uint64_t cb = kind == AW4_T_LM_HEAD ? (uint64_t)rows * cols : (uint64_t)rows * cols / 2;
             const uint64_t sb = (uint64_t)rows * (cols / 32) * 2;
             if (nb != cb + sb) return fail(m, AW4_E_FORMAT, "tensor payload size mismatch");
@@ -883,7 +1122,10 @@ int aw4_reset(aw4_model* m) {
     if (check_model(m)) return AW4_E_INVAL;
     HIPCHK(m, launch_fill_zero(m->arena + m->state_off, m->state_bytes, m->stream));
     HIPCHK(m, launch_set_ctl(m->ctl, 0, 0, 0, m->stream));
+    HIPCHK(m, launch_set_dpos(m->ctl, 0, m->stream));
     m->host_pos = 0;
+    m->host_dpos = 0;
+    m->pend_src = 0;
     return AW4_OK;
 }
 
@@ -905,6 +1147,73 @@ int aw4_set_pos(aw4_model* m, int32_t pos) {
     if (pos < 0 || pos > m->cfg.max_ctx) return fail(m, AW4_E_CTX_FULL, "position outside [0, max_ctx]");
     HIPCHK(m, launch_set_ctl(m->ctl, pos, -1, -1, m->stream));
     m->host_pos = pos;
+    m->pend_src = 0;
+    return AW4_OK;
+}
+
+int aw4_get_draft_pos(aw4_model* m, int32_t* dpos) {
+    if (check_model(m) || !dpos) return AW4_E_INVAL;
+    if (m->cfg.draft_vocab <= 0) return fail(m, AW4_E_STATE, "the model has no draft head");
+    *dpos = m->host_dpos;
+    return AW4_OK;
+}
+
+int aw4_set_draft_pos(aw4_model* m, int32_t dpos) {
+    if (check_model(m)) return AW4_E_INVAL;
+    if (m->cfg.draft_vocab <= 0) return fail(m, AW4_E_STATE, "the model has no draft head");
+    if (dpos < 0 || dpos > m->cfg.max_ctx) return fail(m, AW4_E_CTX_FULL, "draft length outside [0, max_ctx]");
+    HIPCHK(m, launch_set_dpos(m->ctl, dpos, m->stream));
+    m->host_dpos = dpos;
+    return AW4_OK;
+}
+
+int aw4_draft(aw4_model* m, int32_t t0, int32_t k, float temperature, const float* host_u, float* dev_q,
+              float* dev_scores, int32_t* host_drafts) {
+    if (check_model(m) || !host_drafts) return AW4_E_INVAL;
+    const aw4_config* c = &m->cfg;
+    if (c->draft_vocab <= 0) return fail(m, AW4_E_STATE, "the model has no draft head");
+    if (!m->map_set) return fail(m, AW4_E_STATE, "no vocabulary map has been set");
+    if (k < 1 || k > 3 || k + 1 > c->max_verify) return fail(m, AW4_E_INVAL, "k must be in [1, min(3, max_verify - 1)]");
+    if (t0 < 0 || t0 >= c->vocab) return fail(m, AW4_E_TOKEN, "token out of range");
+    if (!(temperature >= 0.f) || !std::isfinite(temperature)) return fail(m, AW4_E_INVAL, "temperature must be >= 0");
+    if (temperature > 0.f) {
+        if (!host_u) return fail(m, AW4_E_INVAL, "sampling needs one uniform per draft");
+        for (int i = 0; i < k; ++i)
+            if (!(host_u[i] >= 0.f && host_u[i] < 1.f)) return fail(m, AW4_E_INVAL, "uniforms must lie in [0, 1)");
+    }
+    if (m->pend_src == 0)
+        return fail(m, AW4_E_STATE, "no committed hidden state to draft from (decode, prefill or verify first)");
+    const int M = m->pend_n + 1;
+    if ((int64_t)m->host_dpos + M + (k - 1) > c->max_ctx) return fail(m, AW4_E_CTX_FULL, "draft cache full");
+    int32_t tok[4] = {0, 0, 0, 0};
+    float u[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < m->pend_n; ++i) tok[i] = m->pend_tok[i];
+    tok[M - 1] = t0;
+    for (int i = 0; i < k && temperature > 0.f; ++i) u[i] = host_u[i];
+    const int H = c->hidden;
+    const bool q_out = temperature > 0.f && dev_q;
+    HIPCHK(m, launch_set_draft(m->ctl, tok, u, m->stream));
+    // the pending entries and t0's entry, committed; draft 1 from the last row
+    int rc = enqueue_draft_block(m, M, &m->ctl->dtok[0], m->pend_src == 1 ? m->x : m->vx, H, 0);
+    if (rc) return rc;
+    rc = enqueue_draft_select(m, M - 1, 0, M, temperature, q_out ? dev_q : nullptr, dev_scores);
+    if (rc) return rc;
+    // drafts 2..k from the block's own output and the previous draft, in entries
+    // past the committed length
+    for (int j = 1; j < k; ++j) {
+        rc = enqueue_draft_block(m, 1, &m->ctl->dout[j - 1], m->xd + (j == 1 ? (int64_t)(M - 1) * H : 0), H, j - 1);
+        if (rc) return rc;
+        rc = enqueue_draft_select(m, 0, j, 0, temperature, q_out ? dev_q + (int64_t)j * c->vocab : nullptr,
+                                  dev_scores ? dev_scores + (int64_t)j * c->draft_vocab : nullptr);
+        if (rc) return rc;
+    }
+    int32_t out[4];
+    HIPCHK(m, hipMemcpyAsync(out, &m->ctl->dout[0], 4 * sizeof(int32_t), hipMemcpyDeviceToHost, m->stream));
+    HIPCHK(m, hipStreamSynchronize(m->stream));
+    for (int i = 0; i < k; ++i) host_drafts[i] = out[i];
+    m->host_dpos += M;
+    m->pend_src = 0;
+    m->pend_n = 0;
     return AW4_OK;
 }
 
@@ -914,12 +1223,29 @@ int aw4_prefill(aw4_model* m, const int32_t* tokens, int32_t n, float* dev_logit
     if ((int64_t)m->host_pos + n > m->cfg.max_ctx) return fail(m, AW4_E_CTX_FULL, "prompt exceeds max_ctx");
     for (int i = 0; i < n; ++i)
         if (tokens[i] < 0 || tokens[i] >= m->cfg.vocab) return fail(m, AW4_E_TOKEN, "prompt token out of range");
+    const bool feed = m->cfg.draft_vocab > 0;
+    if (feed && n > 0 && (int64_t)m->host_dpos + n - 1 > m->cfg.max_ctx)
+        return fail(m, AW4_E_CTX_FULL, "prompt exceeds the draft head's cache");
     for (int i = 0; i < n; ++i) {
         HIPCHK(m, launch_set_token(m->ctl, tokens[i], m->stream));
         const bool last = i == n - 1;
         int rc = run_step(m, last && dev_logits != nullptr);
         if (rc) return rc;
         m->host_pos += 1;
+        if (feed && !last) {
+            // the draft head's entry of this position: (its hidden state, the next prompt token)
+            const int32_t tok[4] = {tokens[i + 1], 0, 0, 0};
+            const float u[4] = {0.f, 0.f, 0.f, 0.f};
+            HIPCHK(m, launch_set_draft(m->ctl, tok, u, m->stream));
+            rc = enqueue_draft_block(m, 1, &m->ctl->dtok[0], m->x, m->cfg.hidden, 0);
+            if (rc) return rc;
+            m->host_dpos += 1;
+            HIPCHK(m, launch_set_dpos(m->ctl, m->host_dpos, m->stream));
+        }
+    }
+    if (n > 0) {
+        m->pend_src = 1;
+        m->pend_n = 0;
     }
     if (n > 0 && dev_logits)
         HIPCHK(m, hipMemcpyAsync(dev_logits, m->logits, (size_t)m->cfg.vocab * 4, hipMemcpyDeviceToDevice, m->stream));
@@ -935,6 +1261,8 @@ int aw4_decode_step(aw4_model* m, int32_t token, float* dev_logits, int32_t* hos
     int rc = run_step(m, true);
     if (rc) return rc;
     m->host_pos += 1;
+    m->pend_src = 1;
+    m->pend_n = 0;
     if (dev_logits)
         HIPCHK(m, hipMemcpyAsync(dev_logits, m->logits, (size_t)m->cfg.vocab * 4, hipMemcpyDeviceToDevice, m->stream));
     if (host_argmax) {
@@ -963,6 +1291,8 @@ int aw4_decode_greedy(aw4_model* m, int32_t first_token, int32_t n_steps, int32_
         HIPCHK(m, hipStreamSynchronize(m->stream));
         done += chunk;
         tok = host_out[done - 1];
+        m->pend_src = 1;
+        m->pend_n = 0;
     }
     return AW4_OK;
 }
@@ -1001,6 +1331,11 @@ int aw4_verify_k(aw4_model* m, const int32_t* host_tokens, int32_t k, const floa
     for (int i = 0; i < n_out; ++i) host_out[i] = res[i];
     *host_n_out = n_out;
     m->host_pos += res[6];
+    // the accepted positions' hidden states (verify rows 0 .. n_out - 1) wait for
+    // the next draft call, with the drafts that followed them
+    m->pend_src = 2;
+    m->pend_n = n_out - 1;
+    for (int i = 0; i + 1 < n_out; ++i) m->pend_tok[i] = host_tokens[i + 1];
     return AW4_OK;
 }
 
@@ -1013,6 +1348,7 @@ int aw4_decode_hidden(aw4_model* m, const float* dev_in, float* dev_out) {
     HIPCHK(m, launch_advance(m->ctl, m->stream));
     if (dev_out != m->x) HIPCHK(m, launch_copy_f32(dev_out, m->x, m->cfg.hidden, m->stream));
     m->host_pos += 1;
+    m->pend_src = 0;
     return AW4_OK;
 }
 
@@ -1025,7 +1361,7 @@ int aw4_read_hidden(aw4_model* m, float* host_x) {
 
 int aw4_time_phase(aw4_model* m, int32_t phase, int32_t reps, float* avg_us, uint64_t* bytes_per_launch) {
     if (check_model(m) || reps < 1 || !avg_us || !bytes_per_launch) return AW4_E_INVAL;
-    if (phase < 0 || phase > AW4_PHASE_MIX_IN) return fail(m, AW4_E_INVAL, "unknown phase");
+    if (phase < 0 || phase > AW4_PHASE_DRAFT_HEAD) return fail(m, AW4_E_INVAL, "unknown phase");
     hipEvent_t e0, e1;
     HIPCHK(m, hipEventCreate(&e0));
     HIPCHK(m, hipEventCreate(&e1));
@@ -1075,13 +1411,12 @@ int aw4_import_state_gdn(aw4_model* m, int32_t layer, const float* host_S) {
 
 int aw4_export_state_kv(aw4_model* m, int32_t layer, int32_t npos, int8_t* kc, uint16_t* ks, int8_t* vc,
                         uint16_t* vs) {
-    if (check_model(m) || !kc || !ks || !vc || !vs || layer < 0 || layer >= m->cfg.n_layers ||
-        m->L[layer].type != 'A')
-        return fail(m, AW4_E_INVAL, "not an attention layer");
+    LayerBufs* lb = kv_layer(m, layer);
+    if (check_model(m) || !kc || !ks || !vc || !vs || !lb) return fail(m, AW4_E_INVAL, "not an attention layer");
     const aw4_config* c = &m->cfg;
     if (npos < 0 || npos > c->max_ctx) return fail(m, AW4_E_INVAL, "npos outside [0, max_ctx]");
     const int nkv = c->attn_kv_heads, d = c->attn_head_dim, NG = d / 32, VW = 3 * NG;
-    LayerBufs& b = m->L[layer];
+    LayerBufs& b = *lb;
     HIPCHK(m, hipStreamSynchronize(m->stream));
     std::vector<int8_t> k((size_t)npos * d);
     std::vector<uint16_t> s1((size_t)npos * NG), s2((size_t)npos * NG);
@@ -1109,15 +1444,14 @@ int aw4_export_state_kv(aw4_model* m, int32_t layer, int32_t npos, int8_t* kc, u
 
 int aw4_import_state_kv(aw4_model* m, int32_t layer, int32_t npos, const int8_t* kc, const uint16_t* ks,
                         const int8_t* vc, const uint16_t* vs) {
-    if (check_model(m) || !kc || !ks || !vc || !vs || layer < 0 || layer >= m->cfg.n_layers ||
-        m->L[layer].type != 'A')
-        return fail(m, AW4_E_INVAL, "not an attention layer");
+    LayerBufs* lb = kv_layer(m, layer);
+    if (check_model(m) || !kc || !ks || !vc || !vs || !lb) return fail(m, AW4_E_INVAL, "not an attention layer");
     const aw4_config* c = &m->cfg;
     if (npos < 0 || npos > c->max_ctx) return fail(m, AW4_E_INVAL, "npos outside [0, max_ctx]");
     const int nkv = c->attn_kv_heads, d = c->attn_head_dim, NG = d / 32, VW = 3 * NG;
     for (int64_t i = 0; i < (int64_t)npos * nkv * d; ++i)
         if (vc[i] < -3 || vc[i] > 3) return fail(m, AW4_E_INVAL, "V codes must be in -3..3");
-    LayerBufs& b = m->L[layer];
+    LayerBufs& b = *lb;
     HIPCHK(m, hipStreamSynchronize(m->stream));
     std::vector<int8_t> k((size_t)npos * d);
     std::vector<uint16_t> s1((size_t)npos * NG), s2((size_t)npos * NG);

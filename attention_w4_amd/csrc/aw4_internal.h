@@ -23,8 +23,17 @@ struct Ctl {
     int32_t vn_out;     // tokens emitted (vn_acc + 1)
     int32_t vcommit;    // positions committed (vn_acc + 1)
     int32_t vresid_p;   // 1 when the residual was all zero and p was used
-    int32_t pad[28];
+    // draft head
+    int32_t dpos;       // committed entries of the draft head's cache
+    int32_t dtok[4];    // tokens of the entries a draft call feeds first
+    float du[4];        // one uniform per draft
+    int32_t dout[4];    // drafts (token ids)
+    float dmax;         // largest mapped score of the current draft step
+    float dz;           // its softmax normaliser
+    int32_t darg;       // index into the map of the current draft
+    int32_t pad[16];
 };
+static_assert(sizeof(Ctl) == 256, "control block size");
 
 // W4 GPU layout: codes as dwords [rows][cols/8]; within each dword the eight
 // 4-bit fields (nibble = code + 8) hold elements [0,2,4,6,1,3,5,7] of its
@@ -74,9 +83,10 @@ struct GemvMultiArgs {
 };
 
 struct HeadArgs {
-    const int8_t* codes;      // [V][H]
-    const uint16_t* scales;   // [V][H/32]
-    int32_t V;
+    const int8_t* codes;      // [rows][H]
+    const uint16_t* scales;   // [rows][H/32]
+    const int32_t* map;       // null: output i is row i; else row map[i]
+    int32_t V;                // outputs
     int32_t H;
     const float* x;           // residual [H]
     const float* nw;          // final norm weight [H]
@@ -96,7 +106,7 @@ struct GdnArgs {
 };
 
 struct AttnArgs {
-    int32_t pos_offset;       // the first token sits at ctl->pos + pos_offset
+    int32_t pos_offset;       // the first token sits at *pos + pos_offset
     int32_t nt;               // tokens in this sweep, at consecutive positions
     int32_t append;           // encode and append the (single) token first
     int64_t sproj;            // token m's projections at proj + m * sproj
@@ -106,7 +116,7 @@ struct AttnArgs {
     uint32_t* vc;             // [nkv][max_ctx][3 d/32] 3-bit codes + 4, dims permuted (k_attn.hip)
     uint16_t* vs;             // [nkv][max_ctx][d/32]
     const float* signs;       // [d] +-1
-    const Ctl* ctl;
+    const int32_t* pos;       // device: the cache's committed length (ctl->pos, or ctl->dpos for the draft head)
     float* part;              // [prow][nsplit][d] acc, then [prow][nsplit][2] (m, l); row m nq + head
     int32_t prow;             // rows of part: nq times the most tokens per sweep
     int32_t max_ctx, nq, nkv, d, nsplit;
@@ -119,7 +129,7 @@ struct CombineArgs {
     const float* part;
     const float* proj;
     const float* signs;
-    const Ctl* ctl;
+    const int32_t* pos;
     _Float16* out;            // token m, head h at out + (m nq + h) d
     int32_t prow;
     int32_t nq, nkv, d, nsplit;
@@ -146,6 +156,39 @@ struct AcceptArgs {
     float inv_t;
     float* zpart;             // [k+1][nb]
     float* wpart;             // [k+1][nb]
+};
+
+// Draft head input of M entries: u_m = [fp16(RMSNorm(emb(tok[m])) * nw_emb);
+// fp16(RMSNorm(h_m) * nw_hid)], [M][2H]
+struct DraftEmbedArgs {
+    const int8_t* codes;      // tied int8 table [V][H]
+    const uint16_t* scales;
+    const int32_t* tok;       // device token ids [M]
+    const float* h;           // hidden m at h + m * sh
+    int64_t sh;
+    const float* nw_emb;
+    const float* nw_hid;
+    _Float16* u;              // [M][2H]
+    int32_t H, M;
+    float eps;
+};
+
+// Draft selection from the mapped scores z [Vd] and the head's block partials
+struct DraftSelArgs {
+    Ctl* ctl;
+    const float* z;           // [Vd] mapped scores
+    const float* pv;          // head block partials (best value, best index)
+    const int32_t* pi;
+    int32_t nb;               // head blocks
+    const int32_t* map;       // [Vd] ascending ids
+    const int32_t* rmap;      // [V] index into the map or -1
+    int32_t Vd, V;
+    int32_t j;                // draft index
+    int32_t commit;           // entries to add to ctl->dpos (the first step) or 0
+    int32_t greedy;
+    float inv_t;
+    float* zpart;             // [draft_chunks(Vd)]
+    float* q;                 // [V] draft probabilities of draft j, or null
 };
 
 // ---------------------------------------------------------------- launches
@@ -189,6 +232,11 @@ hipError_t launch_advance(Ctl* ctl, hipStream_t s);
 hipError_t launch_set_ctl(Ctl* ctl, int32_t pos, int32_t token, int32_t nstep, hipStream_t s);
 hipError_t launch_fill_zero(void* p, uint64_t bytes, hipStream_t s);
 hipError_t launch_copy_f32(float* dst, const float* src, int64_t n, hipStream_t s);
+hipError_t launch_draft_embed(const DraftEmbedArgs& a, hipStream_t s);
+hipError_t launch_draft_select(const DraftSelArgs& a, hipStream_t s);
+int draft_chunks(int Vd);
+hipError_t launch_set_draft(Ctl* ctl, const int32_t* tok, const float* u, hipStream_t s);
+hipError_t launch_set_dpos(Ctl* ctl, int32_t dpos, hipStream_t s);
 
 // quantise fp32 rows into the GPU layouts
 hipError_t launch_quant_w4(const float* src, int64_t nrows, int64_t cols, uint32_t* codes, uint16_t* scales,

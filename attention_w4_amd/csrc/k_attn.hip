@@ -46,13 +46,6 @@ constexpr int kTile = 16;                    // positions per wave tile; split l
 
 __device__ __forceinline__ float sigmoidf_(float v) { return 1.0f / (1.0f + __expf(-v)); }
 
-// max over aligned 32-lane segments
-__device__ __forceinline__ float seg32_max(float v) {
-#pragma unroll
-    for (int o = 16; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
-}
-
 __device__ __forceinline__ void split_range(int npos, int nsplit, int& pps, int& used) {
     const int p = (npos + nsplit - 1) / nsplit;
     pps = (p + kTile - 1) / kTile * kTile;
@@ -195,7 +188,7 @@ __global__ __launch_bounds__(512, 1) void k_attn(AttnArgs a) {
     const int split = blockIdx.x, j = blockIdx.y, tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
     const int c = lane & 15, q = lane >> 4;
-    const int pos = a.ctl->pos + a.pos_offset;   // the first token's position
+    const int pos = *a.pos + a.pos_offset;   // the first token's position
     const int nt = NT == 1 ? 1 : a.nt;
     const int npos = pos + nt;
     int pps, used;
@@ -527,7 +520,7 @@ __global__ __launch_bounds__(1024) void k_combine(CombineArgs a) {
     // block i: token i / nq, head i % nq (its slot in the partial rows)
     const int i = blockIdx.x, tid = threadIdx.x;
     const int tm = i / a.nq, hq = i % a.nq;
-    const int pos = a.ctl->pos + a.pos_offset;
+    const int pos = *a.pos + a.pos_offset;
     int pps, used;
     split_range(pos + a.nt, a.nsplit, pps, used);
     const float* base = a.part + (int64_t)i * a.nsplit * D;
@@ -618,13 +611,13 @@ __global__ __launch_bounds__(1024) void k_combine(CombineArgs a) {
     }
 }
 
-// The nt tokens' K and V at positions ctl->pos + pos_offset + m, one wave per
+// The nt tokens' K and V at positions *pos + pos_offset + m, one wave per
 // (kv head, token), before a multi-token sweep reads them.
 template <int D>
 __global__ __launch_bounds__(64) void k_append(AttnArgs a) {
     __shared__ uint8_t vq[D];
     const int j = blockIdx.x, tm = blockIdx.y;
-    const int pos = a.ctl->pos + a.pos_offset + tm;
+    const int pos = *a.pos + a.pos_offset + tm;
     const float* kp = a.proj + (int64_t)tm * a.sproj + 2LL * a.nq * D + (int64_t)j * D;
     encode_append<D>(kp, kp + (int64_t)a.nkv * D, a.signs, a.kc, a.ks, a.vc, a.vs, (int64_t)j * a.max_ctx + pos, vq,
                      threadIdx.x);

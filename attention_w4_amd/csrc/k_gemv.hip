@@ -535,10 +535,11 @@ __global__ __launch_bounds__(256) void k_head_i8(HeadArgs a) {
         const int r0 = pr * 2;
         const bool has1 = (r0 + 1) < a.V;
         const int r1 = has1 ? r0 + 1 : r0;
-        const uint4* c0 = (const uint4*)(a.codes + (int64_t)r0 * H);
-        const uint4* c1 = (const uint4*)(a.codes + (int64_t)r1 * H);
-        const uint16_t* s0 = a.scales + (int64_t)r0 * g_row;
-        const uint16_t* s1 = a.scales + (int64_t)r1 * g_row;
+        const int64_t q0 = a.map ? a.map[r0] : r0, q1 = a.map ? a.map[r1] : r1;
+        const uint4* c0 = (const uint4*)(a.codes + q0 * H);
+        const uint4* c1 = (const uint4*)(a.codes + q1 * H);
+        const uint16_t* s0 = a.scales + q0 * g_row;
+        const uint16_t* s1 = a.scales + q1 * g_row;
         float acc0 = 0.f, acc1 = 0.f;
         for (int c = lane; c < nchunk; c += 64) {
             const uint4 w0 = c0[c], w1 = c1[c];
@@ -588,7 +589,9 @@ __global__ __launch_bounds__(256) void k_head_i8(HeadArgs a) {
 // unrolled by three with the same loads in flight at its entry and at its
 // back edge, so the compiler's wait counts stay exact; a prefetch past the
 // wave's last row reads row 0 instead (an L2 hit, the data is never used).
-template <int H>
+// MAPPED: output i reads table row map[i] (the draft head's id list); the id is
+// fetched with a scalar load, whose wait does not drain the ring's vector loads.
+template <int H, bool MAPPED>
 __global__ __launch_bounds__(256, 2) void k_head_stream(HeadArgs a) {
     constexpr int NC = H / 1024;
     constexpr int GR = H / 32;
@@ -623,8 +626,9 @@ __global__ __launch_bounds__(256, 2) void k_head_stream(HeadArgs a) {
         uint16_t s[NC];
     };
     auto load = [&](Row& b, int row) {
-        const u32x4* cp = (const u32x4*)(a.codes + (int64_t)row * H);
-        const uint16_t* sp = a.scales + (int64_t)row * GR;
+        const int64_t src = MAPPED ? (int64_t)a.map[__builtin_amdgcn_readfirstlane(row)] : row;
+        const u32x4* cp = (const u32x4*)(a.codes + src * H);
+        const uint16_t* sp = a.scales + src * GR;
 #pragma unroll
         for (int i = 0; i < NC; ++i) {
             b.c[i] = __builtin_nontemporal_load(cp + lane + 64 * i);
@@ -1055,7 +1059,7 @@ __device__ __forceinline__ void mfma_prologue(const GemvMultiArgs& a, _Float16* 
 
 template <int PRO, int EPI, int KS, int NST>
 __global__ __launch_bounds__(256, 2) void k_gemv_mfma(GemvMultiArgs a) {
-    constexpr int MAXM = 4, U = kStage, NB = 4 / KS;   // NB row blocks per workgroup
+    constexpr int U = kStage, NB = 4 / KS;   // NB row blocks per workgroup
     typedef _Float16 h8 __attribute__((ext_vector_type(8)));
     typedef float f4 __attribute__((ext_vector_type(4)));
     extern __shared__ __align__(16) unsigned char smem[];
@@ -1356,6 +1360,9 @@ hipError_t launch_stream(int pro, int epi, const GemvArgs& a, hipStream_t s) {
     AW4_STREAM_CASE(PRO_NORM, EPI_SWIGLU)
     AW4_STREAM_CASE(PRO_GATED, EPI_RESID)
     AW4_STREAM_CASE(PRO_LOADH, EPI_RESID)
+    if constexpr (R == 2 && NF == 10) {   // draft-head fuse, K 10240
+        AW4_STREAM_CASE(PRO_LOADH, EPI_STORE)
+    }
 #undef AW4_STREAM_CASE
     return hipErrorInvalidValue;
 }
@@ -1372,6 +1379,7 @@ hipError_t launch_generic(int pro, int epi, const GemvArgs& a, hipStream_t s) {
     AW4_GEMV_CASE(PRO_NORM, EPI_SWIGLU)
     AW4_GEMV_CASE(PRO_GATED, EPI_RESID)
     AW4_GEMV_CASE(PRO_LOADH, EPI_RESID)
+    AW4_GEMV_CASE(PRO_LOADH, EPI_STORE)
 #undef AW4_GEMV_CASE
     return hipErrorInvalidValue;
 }
@@ -1397,6 +1405,7 @@ hipError_t launch_gemv(int pro, int epi, const GemvArgs& a, hipStream_t s) {
         AW4_SHAPE(2, 4)     // K = 4096
         AW4_SHAPE(2, 6)     // K = 6144
         AW4_SHAPE(2, 17)    // K = 17408
+        AW4_SHAPE(2, 10)    // K = 10240 (draft-head fuse)
         AW4_SHAPE(4, 1)     // K = 512
         AW4_SHAPE(4, 3)     // K = 1536
         AW4_SHAPE(8, 1)     // K = 256
@@ -1460,6 +1469,8 @@ bool try_mfma(int pro, int epi, int ks, int nst, const GemvMultiArgs& a, hipStre
     AW4_MFMA(PRO_LOADH, EPI_RESID, 4, 6)    // attention o-projection, K 6144
     AW4_MFMA(PRO_LOADH, EPI_RESID, 4, 17)   // FFN down, K 17408
     AW4_MFMA(PRO_LOADH, EPI_RESID, 2, 34)   // FFN down when one workgroup fills a CU's LDS
+    AW4_MFMA(PRO_LOADH, EPI_STORE, 4, 10)   // draft-head fuse, K 10240
+    AW4_MFMA(PRO_LOADH, EPI_STORE, 4, 1)    // the same on the small stack (K 1024)
     AW4_MFMA(PRO_NORM, EPI_SWIGLU, 2, 1)    // small stack (K 512, 1536, 256)
     AW4_MFMA(PRO_NORM, EPI_STORE, 2, 1)
     AW4_MFMA(PRO_LOADH, EPI_RESID, 2, 3)
@@ -1519,8 +1530,10 @@ hipError_t launch_head_multi(const HeadMultiArgs& a, hipStream_t s) {
 
 hipError_t launch_head(const HeadArgs& a, hipStream_t s) {
     const size_t shm = 64 + (size_t)a.H * 2;
-    if (a.H == 5120)
-        hipLaunchKernelGGL(k_head_stream<5120>, dim3(head_blocks(a.V)), dim3(256), shm, s, a);
+    if (a.H == 5120 && a.map)
+        hipLaunchKernelGGL((k_head_stream<5120, true>), dim3(head_blocks(a.V)), dim3(256), shm, s, a);
+    else if (a.H == 5120)
+        hipLaunchKernelGGL((k_head_stream<5120, false>), dim3(head_blocks(a.V)), dim3(256), shm, s, a);
     else
         hipLaunchKernelGGL(k_head_i8, dim3(head_blocks(a.V)), dim3(256), shm, s, a);
     return hipGetLastError();

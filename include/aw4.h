@@ -17,6 +17,9 @@
  *    multiplied by a random-sign Walsh-Hadamard matrix then 3-bit per 32.
  *  - verify_k checks draft tokens with acceptance probability min(1, p/q) and
  *    residual resampling (page 5, point 四).
+ *  - The model's own draft head proposes those tokens and scores them only over
+ *    a list of token ids, the vocabulary map; the target keeps the full
+ *    vocabulary (page 5, point 四).
  *
  * Conventions for every entry point:
  *  - Returns AW4_OK (0) or a negative AW4_E_* code; no exception crosses the
@@ -55,7 +58,10 @@ extern "C" {
  * gdn_v_heads a multiple of gdn_qk_heads; attention: attn_head_dim in {64, 256},
  * attn_q_heads a multiple of attn_kv_heads, attn_q_heads/attn_kv_heads <= 8;
  * vocab >= 0 (0: no embedding or output head, only aw4_decode_hidden works);
- * max_ctx >= 1; max_verify in [1, 4]; rms_eps > 0. */
+ * max_ctx >= 1; max_verify in [1, 4]; rms_eps > 0; draft_vocab in [0, vocab]
+ * (0: no draft head; otherwise the attention fields must describe a valid
+ * attention layer even when the pattern holds none, since the draft head's
+ * block has that shape). */
 typedef struct aw4_config {
     int32_t hidden;
     int32_t ffn;
@@ -72,6 +78,7 @@ typedef struct aw4_config {
     int32_t max_verify;
     float rms_eps;
     char layer_pattern[128];
+    int32_t draft_vocab;        /* ids in the draft head's vocabulary map */
 } aw4_config;
 
 typedef struct aw4_model aw4_model;
@@ -83,7 +90,14 @@ typedef struct aw4_model aw4_model;
  *   FFN_GATE, FFN_UP [ffn x hidden]; FFN_DOWN [hidden x ffn].
  * Global: LM_HEAD int8 [vocab x hidden] (also the embedding table).
  * Vectors (fp32): NORM_MIX, NORM_FFN [hidden]; NORM_GATED [gdn_head_dim];
- * A_BIAS [gdn_v_heads]; NORM_FINAL [hidden]; RHT_SIGNS [attn_head_dim] (+1/-1). */
+ * A_BIAS [gdn_v_heads]; NORM_FINAL [hidden]; RHT_SIGNS [attn_head_dim] (+1/-1).
+ * Draft head (draft_vocab > 0), all at layer index n_layers: one gated-attention
+ * layer (MIX_IN, MIX_OUT, FFN_*, NORM_MIX, NORM_FFN as above) and
+ *   DRAFT_FUSE      W4 [hidden x 2*hidden], x = W [u_e; u_h] with
+ *                   u_e = RMSNorm(embedding(t)) * DRAFT_NORM_EMB and
+ *                   u_h = RMSNorm(h) * DRAFT_NORM_HID, both in fp16;
+ *   DRAFT_NORM_EMB, DRAFT_NORM_HID, DRAFT_NORM_OUT  vectors [hidden];
+ *   DRAFT_MAP       int32 ids [draft_vocab] (aw4_set_draft_map). */
 enum {
     AW4_T_MIX_IN = 0,
     AW4_T_MIX_OUT = 1,
@@ -96,7 +110,12 @@ enum {
     AW4_T_NORM_GATED = 8,
     AW4_T_A_BIAS = 9,
     AW4_T_NORM_FINAL = 10,
-    AW4_T_RHT_SIGNS = 11
+    AW4_T_RHT_SIGNS = 11,
+    AW4_T_DRAFT_FUSE = 12,
+    AW4_T_DRAFT_NORM_EMB = 13,
+    AW4_T_DRAFT_NORM_HID = 14,
+    AW4_T_DRAFT_NORM_OUT = 15,
+    AW4_T_DRAFT_MAP = 16
 };
 
 /* ----------------------------------------------------------- lifetime */
@@ -147,13 +166,22 @@ int aw4_load_tensor(aw4_model* model, int32_t layer, int32_t kind, const void* h
  * Synchronous. */
 int aw4_export_tensor(aw4_model* model, int32_t layer, int32_t kind, void* host_codes, uint16_t* host_scales);
 
-/* Set a vector kind (6..11) from n host floats.  Synchronous. */
+/* Set a vector kind (6..11, 13..15) from n host floats.  Synchronous. */
 int aw4_set_vector(aw4_model* model, int32_t layer, int32_t kind, const float* host_vals, int32_t n);
+
+/* The draft head's vocabulary map (page 5, point 四: the draft head's output
+ * projection covers only the most useful ids, 65,536 of about 248K in the
+ * pages' model): n == draft_vocab distinct ids in [0, vocab), any order; the
+ * library keeps them ascending, which fixes the order of the mapped scores and
+ * of the draft draw.  Synchronous.  Errors: AW4_E_INVAL, AW4_E_STATE (no draft
+ * head). */
+int aw4_set_draft_map(aw4_model* model, const int32_t* host_ids, int32_t n);
 
 /* Load every tensor from one host blob: "AW4W" magic, uint32 version 1, the
  * aw4_config it was made for, uint32 tensor count, then per tensor
  * {int32 layer, int32 kind, int64 rows, int64 cols, uint64 bytes} followed by
- * the payload (logical codes then scales, or n fp32 values for vectors).
+ * the payload (logical codes then scales, n fp32 values for vectors, or n int32
+ * ids for DRAFT_MAP).  The version is 2 (the config carries draft_vocab).
  * Errors: AW4_E_FORMAT on magic, version, size or config mismatch. */
 int aw4_load_weights(aw4_model* model, const void* host_blob, uint64_t bytes);
 
@@ -164,7 +192,9 @@ int aw4_reset(aw4_model* model);
 
 /* Append n prompt tokens (positions pos..pos+n-1) through every layer.  If
  * dev_logits is not NULL it receives the fp32 logits [vocab] after the last
- * token.  Errors: AW4_E_CTX_FULL, AW4_E_TOKEN, AW4_E_STATE (vocab 0). */
+ * token.  With a draft head, prefill also gives it one cache entry per prompt
+ * position except the last (that position's hidden state and the next prompt
+ * token).  Errors: AW4_E_CTX_FULL, AW4_E_TOKEN, AW4_E_STATE (vocab 0). */
 int aw4_prefill(aw4_model* model, const int32_t* host_tokens, int32_t n, float* dev_logits);
 
 /* One decode step on `token` at the current position: embed, all layers
@@ -196,9 +226,35 @@ int aw4_decode_greedy(aw4_model* model, int32_t first_token, int32_t n_steps, in
  * (*host_n_out = accepted + 1 <= k + 1); the model commits positions pos ..
  * pos + accepted (recurrent states replayed from the committed state, the
  * cache length set), and the last emitted token becomes the next pass's t0.
- * Synchronous.  Errors: AW4_E_INVAL, AW4_E_TOKEN, AW4_E_CTX_FULL, AW4_E_STATE. */
+ * Synchronous.  Errors: AW4_E_INVAL, AW4_E_TOKEN, AW4_E_CTX_FULL, AW4_E_STATE.
+ * The committed positions' hidden states stay on the device for the next
+ * aw4_draft call. */
 int aw4_verify_k(aw4_model* model, const int32_t* host_tokens, int32_t k, const float* dev_q, const float* host_u,
                  float temperature, int32_t* host_out, int32_t* host_n_out);
+
+/* Draft k tokens with the model's draft head (page 5, point 四: depth 3, the
+ * draft head scores only the mapped ids).  t0 is the last emitted token, the
+ * one the next verify_k (or decode step) runs first.  The call first gives the
+ * draft head's cache one entry per position committed since the last draft
+ * call by verify_k (that position's hidden state and the token that followed
+ * it) plus the entry of the last committed position with t0, in one pass
+ * (at most max_verify entries), and draws draft 1 from that last entry; drafts
+ * 2..k come from the draft head's own output and the previous draft, in cache
+ * entries that are not committed.  A plain decode step feeds nothing: its
+ * position is simply absent from the draft cache.
+ * Selection: temperature 0 takes the mapped id with the largest score (lowest
+ * id on ties); temperature T > 0 draws from q = softmax(score / T) over the
+ * mapped ids by inverse CDF in ascending-id order with host_u[j] (k uniforms in
+ * [0, 1)), and dev_q (optional, device, [k][vocab] fp32) receives q with zeros
+ * outside the map: the draft probabilities verify_k takes.  dev_scores
+ * (optional, device, [k][draft_vocab] fp32) receives the mapped scores in
+ * ascending-id order.  host_drafts receives the k ids.  1 <= k <= min(3,
+ * max_verify - 1).  Synchronous.  Errors: AW4_E_INVAL, AW4_E_TOKEN,
+ * AW4_E_CTX_FULL (draft cache), AW4_E_STATE (no draft head, no map, or nothing
+ * committed since the last draft call: reset, set_pos and another aw4_draft
+ * leave no hidden state to draft from). */
+int aw4_draft(aw4_model* model, int32_t t0, int32_t k, float temperature, const float* host_u, float* dev_q,
+              float* dev_scores, int32_t* host_drafts);
 
 /* Layers only, at the current position: dev_x_out = stack(dev_x_in), both
  * fp32 [hidden] device vectors (may alias).  For models without a vocabulary
@@ -222,7 +278,9 @@ int aw4_set_graph(aw4_model* model, int32_t enable);
 enum {
     AW4_PHASE_FFN_GATE_UP = 0,   /* RMSNorm + gate/up W4 GEMV + SwiGLU  */
     AW4_PHASE_FFN_DOWN = 1,      /* down W4 GEMV + residual add          */
-    AW4_PHASE_MIX_IN = 2         /* RMSNorm + mixer input W4 GEMV         */
+    AW4_PHASE_MIX_IN = 2,        /* RMSNorm + mixer input W4 GEMV         */
+    AW4_PHASE_HEAD = 3,          /* final norm + int8 head over the vocab */
+    AW4_PHASE_DRAFT_HEAD = 4     /* draft output norm + int8 head over the mapped ids */
 };
 int aw4_time_phase(aw4_model* model, int32_t phase, int32_t reps, float* avg_us, uint64_t* bytes_per_launch);
 
@@ -233,12 +291,19 @@ int aw4_get_pos(aw4_model* model, int32_t* pos);
 /* Set the position without touching the caches (state import). */
 int aw4_set_pos(aw4_model* model, int32_t pos);
 
+/* Committed entries of the draft head's cache; set it after importing that
+ * cache (layer n_layers of the state calls below).  AW4_E_STATE without a draft
+ * head. */
+int aw4_get_draft_pos(aw4_model* model, int32_t* dpos);
+int aw4_set_draft_pos(aw4_model* model, int32_t dpos);
+
 /* GDN recurrent state of one 'G' layer, fp32 [v_heads][head_dim][head_dim]
  * (row i of a head's matrix maps keys to value dim i).  Synchronous. */
 int aw4_export_state_gdn(aw4_model* model, int32_t layer, float* host_S);
 int aw4_import_state_gdn(aw4_model* model, int32_t layer, const float* host_S);
 
-/* Cache of one 'A' layer, positions [0, npos), logical layout: K codes int8
+/* Cache of one 'A' layer (or, as layer n_layers, of the draft head), entries
+ * [0, npos), logical layout: K codes int8
  * [npos][kv_heads][head_dim], K scales fp16 [npos][kv_heads][head_dim/32],
  * V codes int8 in -3..3 (rotated domain) [npos][kv_heads][head_dim], V scales
  * fp16 [npos][kv_heads][head_dim/32].  Synchronous. */

@@ -77,8 +77,10 @@ class DraftDriver:
         self.last = xs[a]
         return out, a, logits
 
-    def draft(self, t0, k, temperature=0.0, u=None):
-        """-> (k drafts, q [k][vocab] or None, mapped scores [k][draft_vocab])"""
+    def draft(self, t0, k, temperature=0.0, u=None, force=None):
+        """-> (k drafts, q [k][vocab] or None, mapped scores [k][draft_vocab]);
+        force (optional): the tokens fed to drafts 2..k instead of this
+        driver's own earlier drafts (teacher forcing for comparisons)"""
         if self.last is None:
             raise ValueError("no committed hidden state to draft from")
         for h, t in self.pending:
@@ -89,7 +91,7 @@ class DraftDriver:
         drafts, qs, zs = [], [], []
         for j in range(k):
             if j > 0:
-                x, z = self.m.draft_step(drafts[-1], x, j - 1)
+                x, z = self.m.draft_step(drafts[-1] if force is None else force[j - 1], x, j - 1)
             i, qm = select(z, temperature, None if u is None else u[j])
             drafts.append(int(self.map[i]))
             zs.append(z)

@@ -8,7 +8,7 @@ decode step.
 import numpy as np
 
 from . import workloads as W
-from . import dev_matrix_rows, vector, signs
+from . import dev_matrix_rows, draft_map, vector, signs
 
 
 def load_recipe(model, shape, seed, norm_jitter=0.0, chunk_elems=1 << 26):
@@ -25,6 +25,8 @@ def load_recipe(model, shape, seed, norm_jitter=0.0, chunk_elems=1 << 26):
                 model.quantize_tensor(spec.layer, spec.kind, r0, view)
         elif spec.fmt == W.VEC:
             model.set_vector(spec.layer, spec.kind, vector(spec, seed))
+        elif spec.fmt == W.MAP:
+            model.set_draft_map(draft_map(shape, seed))
         else:
             model.set_vector(-1, spec.kind, signs(spec.cols, seed, spec.stream).astype(np.float32))
     model.sync()

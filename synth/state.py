@@ -39,15 +39,19 @@ def kv_state(shape, layer, npos, seed):
     return kc, ks, vc, vs
 
 
-def fill(model, shape, npos, seed, gdn=True, kv=True):
+def fill(model, shape, npos, seed, gdn=True, kv=True, draft=True):
     """Import a synthetic state of npos positions into a model exposing
     import_gdn / import_kv / set_pos (the GPU binding) or set_gdn_state /
-    set_kv / set_pos (the oracle)."""
+    set_kv / set_pos (the oracle).  With a draft head, its cache gets npos - 1
+    entries (one per position whose next token is known) of the same recipe."""
+    put_kv = model.import_kv if hasattr(model, "import_kv") else model.set_kv
     for l, t in enumerate(shape.pattern):
         if t == "G" and gdn:
             S = gdn_state(shape, l, seed)
             (model.import_gdn if hasattr(model, "import_gdn") else model.set_gdn_state)(l, S)
         elif t == "A" and kv:
-            kv = kv_state(shape, l, npos, seed)
-            (model.import_kv if hasattr(model, "import_kv") else model.set_kv)(l, *kv)
+            put_kv(l, *kv_state(shape, l, npos, seed))
+    if getattr(shape, "draft_vocab", 0) > 0 and draft and npos > 0:
+        put_kv(shape.n_layers, *kv_state(shape, shape.n_layers, npos - 1, seed))
+        model.set_dpos(npos - 1)
     model.set_pos(npos)
