@@ -316,7 +316,7 @@ uint64_t plan_layout(const aw4_config* c, aw4_model* m, uint8_t* base) {
         xd = p.take<float>((uint64_t)MV * H * 4);
         ubuf = p.take<_Float16>((uint64_t)MV * 2 * H * 2);
         dscore = p.take<float>((uint64_t)c->draft_vocab * 4);
-        ndhb = head_blocks(c->draft_vocab);
+        ndhb = draft_head_blocks(c->draft_vocab);
         dpv = p.take<float>((uint64_t)ndhb * 4);
         dpi = p.take<int32_t>((uint64_t)ndhb * 4);
         dzpart = p.take<float>((uint64_t)draft_chunks(c->draft_vocab) * 4);
@@ -406,7 +406,8 @@ const char* check_config(const aw4_config* c) {
         const int G = c->attn_q_heads / c->attn_kv_heads;
         if (!(G == 1 || G == 2 || G == 4 || G == 6 || G == 8)) return "attn_q_heads / attn_kv_heads must be 1, 2, 4, 6 or 8";
     }
-    if (c->vocab < 0) return "vocab must be >= 0";
+    if (c->vocab < 0 || c->vocab > (1 << 21)) return "vocab must be in [0, 2097152]";
+    if (c->draft_vocab > 0 && c->hidden > 8192) return "hidden must be <= 8192 with a draft head";
     if (c->max_ctx < 1) return "max_ctx must be >= 1";
     if (c->max_verify < 1 || c->max_verify > 4) return "max_verify must be in [1, 4]";
     if (!(c->rms_eps > 0.f) || !std::isfinite(c->rms_eps)) return "rms_eps must be positive";

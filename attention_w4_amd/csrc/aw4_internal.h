@@ -210,6 +210,7 @@ struct HeadMultiArgs {
 };
 hipError_t launch_head_multi(const HeadMultiArgs& a, hipStream_t s);
 int head_blocks(int V);
+int draft_head_blocks(int V);   // blocks of the mapped head (launch_head with a map)
 hipError_t launch_head_final(const float* pv, const int32_t* pi, int n, Ctl* ctl, int32_t* ring, int ring_cap,
                              hipStream_t s);
 hipError_t launch_gdn(const GdnArgs& a, hipStream_t s);

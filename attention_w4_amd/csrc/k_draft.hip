@@ -11,11 +11,13 @@
 // The block between input and scores runs on the W4 GEMV, attention and head
 // kernels of the target.
 #include "aw4_internal.h"
+#include "block_scan.h"
 
 namespace aw4 {
 namespace {
 
-constexpr int kDraftChunk = 2048;   // map entries per block of the normaliser sums
+constexpr int kDraftChunk = 2048;      // map entries per block of the normaliser sums
+constexpr int kDraftMaxChunks = 1024;  // so up to 2M mapped ids
 
 __device__ __forceinline__ float wsum(float v) {
 #pragma unroll
@@ -28,20 +30,34 @@ __device__ __forceinline__ float half_bits_to_float(uint16_t b) {
 }
 
 // one workgroup per entry m: RMSNorm of the dequantised table row of tok[m]
-// and of h_m, each with its own weight, written side by side as fp16
+// and of h_m, each with its own weight, written side by side as fp16.  Each
+// thread holds its four-value slices in registers, all loaded up front.
+constexpr int kEmbMaxPer = 8;   // hidden sizes up to 8192
+
 __global__ __launch_bounds__(256) void k_draft_embed(DraftEmbedArgs a) {
+    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
     __shared__ float red[2][4];
-    const int m = blockIdx.x, H = a.H;
+    const int m = blockIdx.x, H = a.H, n4 = H / 4;
     const int64_t tok = a.tok[m];
-    const int8_t* cr = a.codes + tok * H;
+    const uint32_t* cr = (const uint32_t*)(a.codes + tok * H);
     const uint16_t* sr = a.scales + tok * (H / 32);
-    const float* h = a.h + (int64_t)m * a.sh;
+    const float4* h = (const float4*)(a.h + (int64_t)m * a.sh);
+    float4 ev[kEmbMaxPer], hv[kEmbMaxPer];
     float se = 0.f, sh = 0.f;
-    for (int k = threadIdx.x; k < H; k += 256) {
-        const float e = (float)cr[k] * half_bits_to_float(sr[k >> 5]);
-        const float v = h[k];
-        se += e * e;
-        sh += v * v;
+#pragma unroll
+    for (int i = 0; i < kEmbMaxPer; ++i) {
+        const int q = threadIdx.x + 256 * i;
+        if (q < n4) {
+            const uint32_t c4 = cr[q];
+            const float sc = half_bits_to_float(sr[q >> 3]);
+            ev[i] = make_float4((float)(int8_t)(c4 & 0xff) * sc, (float)(int8_t)((c4 >> 8) & 0xff) * sc,
+                                (float)(int8_t)((c4 >> 16) & 0xff) * sc, (float)(int8_t)(c4 >> 24) * sc);
+            hv[i] = h[q];
+        } else {
+            ev[i] = hv[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        se += ev[i].x * ev[i].x + ev[i].y * ev[i].y + ev[i].z * ev[i].z + ev[i].w * ev[i].w;
+        sh += hv[i].x * hv[i].x + hv[i].y * hv[i].y + hv[i].z * hv[i].z + hv[i].w * hv[i].w;
     }
     se = wsum(se);
     sh = wsum(sh);
@@ -55,11 +71,20 @@ __global__ __launch_bounds__(256) void k_draft_embed(DraftEmbedArgs a) {
     sh = red[1][0] + red[1][1] + red[1][2] + red[1][3];
     const float re = 1.0f / sqrtf(se / (float)H + a.eps);
     const float rh = 1.0f / sqrtf(sh / (float)H + a.eps);
-    _Float16* u = a.u + (int64_t)m * 2 * H;
-    for (int k = threadIdx.x; k < H; k += 256) {
-        const float e = (float)cr[k] * half_bits_to_float(sr[k >> 5]);
-        u[k] = (_Float16)(e * re * a.nw_emb[k]);
-        u[H + k] = (_Float16)(h[k] * rh * a.nw_hid[k]);
+    h4* ue = (h4*)(a.u + (int64_t)m * 2 * H);
+    h4* uh = (h4*)(a.u + (int64_t)m * 2 * H + H);
+    const float4* we = (const float4*)a.nw_emb;
+    const float4* wh = (const float4*)a.nw_hid;
+#pragma unroll
+    for (int i = 0; i < kEmbMaxPer; ++i) {
+        const int q = threadIdx.x + 256 * i;
+        if (q < n4) {
+            const float4 a4 = we[q], b4 = wh[q];
+            ue[q] = h4{(_Float16)(ev[i].x * re * a4.x), (_Float16)(ev[i].y * re * a4.y),
+                       (_Float16)(ev[i].z * re * a4.z), (_Float16)(ev[i].w * re * a4.w)};
+            uh[q] = h4{(_Float16)(hv[i].x * rh * b4.x), (_Float16)(hv[i].y * rh * b4.y),
+                       (_Float16)(hv[i].z * rh * b4.z), (_Float16)(hv[i].w * rh * b4.w)};
+        }
     }
 }
 
@@ -116,46 +141,32 @@ __global__ __launch_bounds__(256) void k_dsel_z(DraftSelArgs a) {
     if (threadIdx.x == 0) a.zpart[blockIdx.x] = red[0] + red[1] + red[2] + red[3];
 }
 
-// the normaliser (fixed-order sum of the chunks), then the draw: the chunk in
-// which the running sum passes u Z, and the index inside it by a scan
+// the normaliser (sum of the chunk sums), then the draw: the chunk in which
+// the running sum passes u Z, and the index inside it, both by a block-wide
+// scan (block_scan.h)
 __global__ __launch_bounds__(256) void k_dsel_draw(DraftSelArgs a, int nchunks) {
-    __shared__ float s_target, s_base;
-    __shared__ int s_chunk;
+    __shared__ BlockScanLds sl;
+    __shared__ float part[kDraftMaxChunks];
     __shared__ float w[kDraftChunk];
+    __shared__ float s_before;
     Ctl* c = a.ctl;
+    for (int b = threadIdx.x; b < kDraftMaxChunks; b += 256) part[b] = b < nchunks ? a.zpart[b] : 0.f;
+    __syncthreads();
+    const float Z = block_sum_lds<kDraftMaxChunks / 256>(part, nchunks, sl);
+    const float target = c->du[a.j] * Z;
+    const int blk0 = block_inverse_cdf<kDraftMaxChunks / 256>(part, nchunks, 0.f, target, &s_before, sl);
+    const int blk = blk0 < 0 ? 0 : blk0;   // the best entry's weight is 1, so some chunk is nonzero
+    const float base = blk0 < 0 ? 0.f : s_before;
+    __syncthreads();
+    const int i0 = blk * kDraftChunk, i1 = min(a.Vd, i0 + kDraftChunk);
+    for (int i = threadIdx.x; i < kDraftChunk; i += 256) w[i] = i0 + i < i1 ? dweight(a, i0 + i) : 0.f;
+    __syncthreads();
+    const int pick = block_inverse_cdf<kDraftChunk / 256>(w, i1 - i0, base, target, &s_before, sl);
     if (threadIdx.x == 0) {
-        float Z = 0.f;
-        for (int b = 0; b < nchunks; ++b) Z += a.zpart[b];
+        const int idx = pick < 0 ? i0 : i0 + pick;
         c->dz = Z;
-        const float target = c->du[a.j] * Z;
-        float run = 0.f, base = 0.f;
-        int blk = nchunks - 1;
-        for (int b = 0; b < nchunks; ++b) {
-            const float wb = a.zpart[b];
-            if (run + wb > target && wb > 0.f) { blk = b; base = run; break; }
-            run += wb;
-            base = run;
-        }
-        s_target = target;
-        s_base = base;
-        s_chunk = blk;
-    }
-    __syncthreads();
-    const int i0 = s_chunk * kDraftChunk, i1 = min(a.Vd, i0 + kDraftChunk);
-    for (int i = i0 + threadIdx.x; i < i0 + kDraftChunk; i += 256) w[i - i0] = i < i1 ? dweight(a, i) : 0.f;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        float run = s_base;
-        int pick = -1, last_nz = -1;
-        for (int i = i0; i < i1; ++i) {
-            const float wi = w[i - i0];
-            if (wi > 0.f) last_nz = i;
-            run += wi;
-            if (run > s_target && wi > 0.f) { pick = i; break; }
-        }
-        if (pick < 0) pick = last_nz >= 0 ? last_nz : i0;   // rounding at the very end of the mass
-        c->darg = pick;
-        c->dout[a.j] = a.map[pick];
+        c->darg = idx;
+        c->dout[a.j] = a.map[idx];
     }
 }
 
@@ -188,12 +199,13 @@ __global__ void k_set_dpos(Ctl* ctl, int32_t dpos) { ctl->dpos = dpos; }
 int draft_chunks(int Vd) { return (Vd + kDraftChunk - 1) / kDraftChunk; }
 
 hipError_t launch_draft_embed(const DraftEmbedArgs& a, hipStream_t s) {
-    if (a.M < 1 || a.M > 4 || a.H % 32) return hipErrorInvalidValue;
+    if (a.M < 1 || a.M > 4 || a.H % 32 || a.H > 4 * 256 * kEmbMaxPer) return hipErrorInvalidValue;
     hipLaunchKernelGGL(k_draft_embed, dim3(a.M), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
 hipError_t launch_draft_select(const DraftSelArgs& a, hipStream_t s) {
+    if (draft_chunks(a.Vd) > kDraftMaxChunks) return hipErrorInvalidValue;
     hipLaunchKernelGGL(k_dsel_max, dim3(1), dim3(256), 0, s, a);
     if (!a.greedy) {
         const int nc = draft_chunks(a.Vd);

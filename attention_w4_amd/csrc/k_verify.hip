@@ -8,6 +8,7 @@
 // them in parallel, and the accept rule leaves the output distribution equal to
 // the target's; the old exact-match rule is the temperature-0 case).
 #include "aw4_internal.h"
+#include "block_scan.h"
 
 namespace aw4 {
 namespace {
@@ -95,6 +96,7 @@ __global__ __launch_bounds__(256) void k_gdn_multi(GdnMultiArgs a) {
 //   z[j][b]  = sum exp((L_j - max_j) / T)                    (pass 1)
 //   w[j][b]  = sum max(0, p_j - q_j) for j < k, sum p_k      (pass 2)
 constexpr int kAccChunk = 2048;
+constexpr int kAccMaxChunks = 1024;   // vocabularies up to 2M ids
 
 __global__ __launch_bounds__(256) void k_acc_z(AcceptArgs a) {
     __shared__ float red[4];
@@ -140,18 +142,18 @@ __global__ __launch_bounds__(256) void k_acc_w(AcceptArgs a) {
     if (threadIdx.x == 0) a.wpart[j * gridDim.x + b] = red[0] + red[1] + red[2] + red[3];
 }
 
-// Sequential decisions, then the draw: inverse CDF in index order over the
-// chosen distribution: block of the crossing from the block partials, then the
-// exact index inside that block by a fixed-order scan.
+// Sequential decisions (one thread), then the draw: inverse CDF in index order
+// over the chosen distribution, the chunk of the crossing from the chunk
+// masses and the index inside it, both by a block-wide scan (block_scan.h).
 __global__ __launch_bounds__(256) void k_acc_decide(AcceptArgs a, int nb) {
     __shared__ int s_choice;     // distribution to draw from, or -1 (greedy / none)
-    __shared__ float s_target;
-    __shared__ int s_block;
-    __shared__ float s_base;
+    __shared__ BlockScanLds sl;
+    __shared__ float part[kAccMaxChunks];
     __shared__ float chunk[kAccChunk];
+    __shared__ float s_before;
     Ctl* c = a.ctl;
-    const int k = a.k;
-    if (threadIdx.x == 0) {
+    const int k = a.k, tid = threadIdx.x;
+    if (tid == 0) {
         int n_acc = 0;
         int choice = -1;
         bool stop = false;
@@ -175,72 +177,44 @@ __global__ __launch_bounds__(256) void k_acc_decide(AcceptArgs a, int nb) {
         c->vcommit = n_acc + 1;
         if (a.greedy) c->vout[n_acc] = c->vargmax[n_acc];
         s_choice = choice;
-        s_block = -1;
-        if (choice >= 0) {
-            // total mass of the chosen distribution; an all-zero residual falls back to p
-            float tot = 0.f;
-            for (int b = 0; b < nb; ++b) tot += a.wpart[choice * nb + b];
-            c->vresid_p = 0;
-            if (!(tot > 0.f)) c->vresid_p = 1;
-            s_target = c->vu[k] * tot;
-        }
     }
     __syncthreads();
     const int choice = s_choice;
     if (choice < 0) return;
-    const bool use_p = c->vresid_p != 0;
+    const float mx = c->vmax[choice], inv_z = 1.0f / c->vz[choice];
+    for (int b = tid; b < kAccMaxChunks; b += 256) part[b] = b < nb ? a.wpart[choice * nb + b] : 0.f;
+    __syncthreads();
+    float tot = block_sum_lds<kAccMaxChunks / 256>(part, nb, sl);
+    // an all-zero residual falls back to p itself: chunk masses of p
+    const bool use_p = !(tot > 0.f);
     if (use_p) {
-        // residual all zero: draw from p_choice itself; recompute block sums of p
-        if (threadIdx.x == 0) {
-            float tot = 0.f;
-            for (int b = 0; b < nb; ++b) {
-                const int v0 = b * kAccChunk, v1 = min(a.V, v0 + kAccChunk);
-                float bs = 0.f;
-                for (int v = v0; v < v1; ++v)
-                    bs += __expf((a.logits[(int64_t)choice * a.V + v] - c->vmax[choice]) * a.inv_t) / c->vz[choice];
-                a.wpart[choice * nb + b] = bs;
-                tot += bs;
-            }
-            s_target = c->vu[k] * tot;
+        for (int b = tid; b < nb; b += 256) {
+            const int v0 = b * kAccChunk, v1 = min(a.V, v0 + kAccChunk);
+            float bs = 0.f;
+            for (int v = v0; v < v1; ++v) bs += __expf((a.logits[(int64_t)choice * a.V + v] - mx) * a.inv_t) * inv_z;
+            part[b] = bs;
         }
         __syncthreads();
+        tot = block_sum_lds<kAccMaxChunks / 256>(part, nb, sl);
     }
-    if (threadIdx.x == 0) {
-        float run = 0.f;
-        int blk = nb - 1;
-        float base = 0.f;
-        for (int b = 0; b < nb; ++b) {
-            const float w = a.wpart[choice * nb + b];
-            if (run + w > s_target && w > 0.f) { blk = b; base = run; break; }
-            run += w;
-            base = run;
-        }
-        s_block = blk;
-        s_base = base;
-    }
+    if (tid == 0) c->vresid_p = use_p ? 1 : 0;
+    const float target = c->vu[k] * tot;
+    const int blk0 = block_inverse_cdf<kAccMaxChunks / 256>(part, nb, 0.f, target, &s_before, sl);
+    const int blk = blk0 < 0 ? nb - 1 : blk0;
+    const float base = blk0 < 0 ? 0.f : s_before;
     __syncthreads();
-    const int v0 = s_block * kAccChunk, v1 = min(a.V, v0 + kAccChunk);
-    for (int v = v0 + threadIdx.x; v < v0 + kAccChunk; v += 256) {
+    const int v0 = blk * kAccChunk, v1 = min(a.V, v0 + kAccChunk);
+    for (int v = v0 + tid; v < v0 + kAccChunk; v += 256) {
         float w = 0.f;
         if (v < v1) {
-            const float p = __expf((a.logits[(int64_t)choice * a.V + v] - c->vmax[choice]) * a.inv_t) / c->vz[choice];
+            const float p = __expf((a.logits[(int64_t)choice * a.V + v] - mx) * a.inv_t) * inv_z;
             w = (use_p || choice == k) ? p : fmaxf(0.f, p - a.q[(int64_t)choice * a.V + v]);
         }
         chunk[v - v0] = w;
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-        float run = s_base;
-        int pick = -1, last_nz = -1;
-        for (int v = v0; v < v1; ++v) {
-            const float w = chunk[v - v0];
-            if (w > 0.f) last_nz = v;
-            run += w;
-            if (run > s_target && w > 0.f) { pick = v; break; }
-        }
-        if (pick < 0) pick = last_nz >= 0 ? last_nz : v0;   // rounding at the very end of the mass
-        c->vout[c->vn_acc] = pick;
-    }
+    const int pick = block_inverse_cdf<kAccChunk / 256>(chunk, v1 - v0, base, target, &s_before, sl);
+    if (tid == 0) c->vout[c->vn_acc] = pick < 0 ? v0 : v0 + pick;
 }
 
 // per-distribution max and argmax from the head's block partials
@@ -295,6 +269,7 @@ int accept_blocks(int V) { return (V + kAccChunk - 1) / kAccChunk; }
 hipError_t launch_accept(const AcceptArgs& a, const float* head_pv, const int32_t* head_pi, int head_nb,
                          hipStream_t s) {
     const int nb = accept_blocks(a.V);
+    if (nb > kAccMaxChunks) return hipErrorInvalidValue;
     hipLaunchKernelGGL(k_acc_max, dim3(a.k + 1), dim3(256), 0, s, head_pv, head_pi, head_nb, a.ctl);
     if (!a.greedy) {
         hipLaunchKernelGGL(k_acc_z, dim3(nb, a.k + 1), dim3(256), 0, s, a);

@@ -31,7 +31,7 @@ HBM_PEAK_GBS = 8000.0
 # HBM bytes per launch of the gate/up GEMV from the FETCH_SIZE / WRITE_SIZE
 # counter runs recorded in profiles/hbm_traffic_8k_decode.md, valid only for
 # the kernel source whose sha256 prefix is recorded with them.
-GATEUP_TRAFFIC = {"k_gemv_sha256": "e005bcccc8ed1190", "bytes": 101213227}
+GATEUP_TRAFFIC = {"k_gemv_sha256": "517f3a7be23ab92d", "bytes": 101211500}
 
 
 def gateup_traffic():
@@ -76,8 +76,8 @@ def cpu_baseline(ctx, seed):
     from synth import state as SS
     from synth import workloads as W
     full = W.FULL_27B
-    g = W.with_(full, pattern="G", vocab=0, max_ctx=ctx + 8)
-    a = W.with_(full, pattern="A", vocab=full.vocab // 8, max_ctx=ctx + 8)
+    g = W.with_(full, pattern="G", vocab=0, max_ctx=ctx + 8, draft_vocab=0)
+    a = W.with_(full, pattern="A", vocab=full.vocab // 8, max_ctx=ctx + 8, draft_vocab=0)
     og = oracle.from_recipe(g, seed)
     oa = oracle.from_recipe(a, seed)
     SS.fill(og, g, ctx, seed)
@@ -123,7 +123,7 @@ def long_leg(args, torch, A, W, SS, synth):
     from synth.gpu_load import load_recipe
     ctx = args.long_ctx
     k = 3
-    shape = W.with_(W.FULL_27B, max_ctx=ctx + 16 + args.long_steps + (k + 1) * args.verify_passes + 16)
+    shape = W.with_(W.FULL_27B, max_ctx=ctx + 16 + args.long_steps + (k + 1) * (args.verify_passes + args.draft_passes) + 16)
     m = A.Model(shape)
     load_recipe(m, shape, args.seed)
     t0 = time.time()
@@ -180,10 +180,60 @@ def long_leg(args, torch, A, W, SS, synth):
                          "emitted_tok/s": round(emitted / wall, 2),
                          "accepted_per_pass": round(accepted / args.verify_passes, 3),
                          "temperature": 1.0, "draft_q": "softmax of N(0, 1.43^2) logits per slot (synthetic)"}
+    if args.draft_passes:
+        t_last = t if args.verify_passes else int(toks[-1])
+        res["draft_head"] = draft_leg(args, torch, A, m, shape, synth, W, t_last)
     m.close()
     del m
     torch.cuda.empty_cache()
     return res
+
+
+def draft_leg(args, torch, A, m, shape, synth, W, t):
+    """Speculative decoding with the model's own draft head: per pass, three
+    drafts from aw4_draft (temperature 1, q over the 65,536 mapped ids) then one
+    aw4_verify_k pass with that q.  With random weights the draft head and the
+    target are unrelated, so the acceptance rate says nothing about a trained
+    draft head; the timings are what this leg measures.  Also times the draft
+    head's mapped int8 projection against the full output head."""
+    import numpy as np
+    k, P = 3, args.draft_passes
+    V = shape.vocab
+    q = torch.empty(k, V, dtype=torch.float32, device="cuda")
+    du = synth.uniform(k * (P + 1), args.seed, W.STREAM_UNIFORM, i0=1 << 24).reshape(-1, k)
+    uu = synth.uniform((k + 1) * (P + 1), args.seed, W.STREAM_UNIFORM, i0=1 << 25).reshape(-1, k + 1)
+    d = m.draft(t, k, 1.0, du[P], q=q)   # warm-up pass (t: the last emitted token)
+    t = m.verify_k([t] + d, q, uu[P], 1.0)[-1]
+    torch.cuda.synchronize()
+    t_draft = t_verify = 0.0
+    emitted = accepted = 0
+    for p in range(P):
+        t0 = time.perf_counter()
+        d = m.draft(t, k, 1.0, du[p], q=q)
+        t1 = time.perf_counter()
+        out = m.verify_k([t] + d, q, uu[p], 1.0)
+        t2 = time.perf_counter()
+        t_draft += t1 - t0
+        t_verify += t2 - t1
+        emitted += len(out)
+        accepted += len(out) - 1
+        t = out[-1]
+    wall = t_draft + t_verify
+    reps = max(8, args.phase_reps // 4)
+    us_map, b_map = m.time_phase(A.PHASE_DRAFT_HEAD, reps)
+    us_full, b_full = m.time_phase(A.PHASE_HEAD, reps)
+    return {"drafts_per_pass": k, "passes": P, "temperature": 1.0,
+            "passes/s": round(P / wall, 2), "ms_per_pass": round(wall * 1e3 / P, 3),
+            "draft_ms_per_call": round(t_draft * 1e3 / P, 3), "verify_ms_per_pass": round(t_verify * 1e3 / P, 3),
+            "emitted_tok/s": round(emitted / wall, 2), "accepted_per_pass": round(accepted / P, 3),
+            "draft_cache_entries": int(m.dpos),
+            "mapped_head": {"ids": shape.draft_vocab, "avg_us": round(us_map, 2), "bytes": b_map,
+                            "GB/s": round(b_map / (us_map * 1e-6) / 1e9, 1)},
+            "full_head": {"ids": V, "avg_us": round(us_full, 2), "bytes": b_full,
+                          "GB/s": round(b_full / (us_full * 1e-6) / 1e9, 1)},
+            "mapped_over_full_MACs": round(shape.draft_vocab / V, 4),
+            "mapped_over_full_time": round(us_map / us_full, 4),
+            "weights": "random: acceptance is that of an untrained draft head"}
 
 
 def main():
@@ -202,6 +252,8 @@ def main():
                     help="second leg: cached positions of the long-context decode and verify runs (0: skip)")
     ap.add_argument("--long-steps", type=int, default=256, help="timed greedy steps at --long-ctx")
     ap.add_argument("--verify-passes", type=int, default=64, help="timed verify_k passes at --long-ctx (3 drafts)")
+    ap.add_argument("--draft-passes", type=int, default=64,
+                    help="timed draft (aw4_draft, 3 drafts) + verify passes at --long-ctx")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run one plain device copy of this many MiB first (a known-size kernel for counter runs)")
     args = ap.parse_args()

@@ -57,11 +57,11 @@ extern "C" {
  * 'G' (Gated DeltaNet) or 'A' (gated attention); GDN: gdn_head_dim in {64, 128},
  * gdn_v_heads a multiple of gdn_qk_heads; attention: attn_head_dim in {64, 256},
  * attn_q_heads a multiple of attn_kv_heads, attn_q_heads/attn_kv_heads <= 8;
- * vocab >= 0 (0: no embedding or output head, only aw4_decode_hidden works);
+ * vocab in [0, 2097152] (0: no embedding or output head, only aw4_decode_hidden works);
  * max_ctx >= 1; max_verify in [1, 4]; rms_eps > 0; draft_vocab in [0, vocab]
  * (0: no draft head; otherwise the attention fields must describe a valid
  * attention layer even when the pattern holds none, since the draft head's
- * block has that shape). */
+ * block has that shape, and hidden <= 8192). */
 typedef struct aw4_config {
     int32_t hidden;
     int32_t ffn;

@@ -4,7 +4,10 @@ token, aw4_decode_greedy), against the oracle from the same seeded weights and
 the same synthetic 8192-position state.  Greedy tokens must be identical and
 the final hidden state within 1e-2 relative L2.  The oracle is slow at this
 size (about a second per token on the host cores), so the check covers 24
-steps; the smallest top-2 logit margin the oracle sees is reported.
+steps; the smallest top-2 logit margin the oracle sees is reported.  From the
+same state, one decode step and three drafts of the draft head (65,536 mapped
+ids, an 8191-entry synthetic draft cache) are checked the same way: drafts
+identical, mapped scores within 1e-2 relative L2.
 """
 import sys
 import time
@@ -15,6 +18,7 @@ import pytest
 import oracle
 import synth
 from synth import state as SS
+from oracle.draft import DraftDriver
 from synth import workloads as W
 from tests.helpers import rel_l2
 
@@ -50,6 +54,17 @@ def test_full_27b_greedy_from_8k_state():
     SS.fill(gm, shape, CTX, 0)
     emitted = gm.verify_k([first] + [int(t) for t in got[:3]], temperature=0.0)
     vpos = gm.pos
+    # the draft head from the same state: one decode step, then three drafts
+    SS.fill(gm, shape, CTX, 0)
+    t1 = gm.decode_step(first)
+    scores = torch.empty(3, shape.draft_vocab, dtype=torch.float32, device="cuda")
+    drafts = gm.draft(t1, 3, scores=scores)
+    sc = scores.cpu().numpy()
+    # a verify pass of the greedy continuation (all three accepted), then a draft
+    # call that feeds its four entries in one pass
+    emitted2 = gm.verify_k([t1] + [int(t) for t in got[1:4]], temperature=0.0)
+    drafts2 = gm.draft(emitted2[-1], 3, scores=scores)
+    sc2 = scores.cpu().numpy()
     gm.close()
     del gm
     torch.cuda.empty_cache()
@@ -58,6 +73,17 @@ def test_full_27b_greedy_from_8k_state():
     om = oracle.from_recipe(shape, 0)
     SS.fill(om, shape, CTX, 0)
     _say(f"oracle built in {time.time() - t0:.1f} s")
+    t0 = time.time()
+    dd = DraftDriver(om)
+    _, _, t1o = dd.decode(first)
+    dref, _, z = dd.draft(t1o, 3)
+    derr = [rel_l2(sc[j], z[j]) for j in range(3)]
+    out2, _, _ = dd.verify([t1o] + [int(t) for t in got[1:4]], None, None, 0.0)
+    dref2, _, z2 = dd.draft(out2[-1], 3)
+    derr += [rel_l2(sc2[j], z2[j]) for j in range(3)]
+    _say(f"oracle drafts in {time.time() - t0:.1f} s: {dref} then {dref2} (gpu {drafts} then {drafts2}), "
+         f"score rel-L2 {derr}")
+    SS.fill(om, shape, CTX, 0)
     tok, ref, margins = first, [], []
     t0 = time.time()
     for i in range(STEPS):
@@ -72,4 +98,6 @@ def test_full_27b_greedy_from_8k_state():
     _say("verify", emitted, "position", vpos)
     assert list(got) == ref
     assert emitted == ref[:4] and vpos == CTX + 4
+    assert t1 == t1o == ref[0] and drafts == dref and max(derr) < 1e-2
+    assert emitted2 == out2 == ref[1:5] and drafts2 == dref2
     assert rel_l2(xg, x) < 1e-2
