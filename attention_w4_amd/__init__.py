@@ -64,6 +64,7 @@ _SIGS = {
     "aw4_load_weights": [_vp, _vp, _u64],
     "aw4_reset": [_vp],
     "aw4_prefill": [_vp, _vp, _i32, _vp],
+    "aw4_set_prefill_chunk": [_vp, _i32],
     "aw4_decode_step": [_vp, _i32, _vp, _vp],
     "aw4_decode_greedy": [_vp, _i32, _i32, _vp],
     "aw4_decode_hidden": [_vp, _vp, _vp],
@@ -228,6 +229,10 @@ class Model:
         t = np.ascontiguousarray(tokens, np.int32)
         self._rc(lib().aw4_prefill(self.h, _ptr(t), len(t), logits.data_ptr() if logits is not None else None),
                  "prefill")
+
+    def set_prefill_chunk(self, n):
+        """prompt tokens per prefill chunk (0: token by token)"""
+        self._rc(lib().aw4_set_prefill_chunk(self.h, int(n)), "set_prefill_chunk")
 
     def decode_step(self, token, logits=None, want_argmax=True):
         am = _i32()

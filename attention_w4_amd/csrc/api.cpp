@@ -41,6 +41,7 @@ struct LayerBufs {
 };
 
 constexpr int kSweepRows = 4;   // most tokens one attention sweep takes (verify_k has at most 4)
+constexpr int kPrefillMaxChunk = 1024;   // prompt tokens per prefill chunk (buffers sized for it)
 
 struct Plan {
     uint64_t off = 0;
@@ -118,6 +119,21 @@ struct aw4_model {
     int pend_src = 0;               // 0 nothing to draft from, 1 x, 2 vx rows 0..pend_n
     int pend_n = 0;
     int32_t pend_tok[4] = {0, 0, 0, 0};
+    // prefill chunk buffers (C = pchunk_max tokens)
+    int pchunk_max = 0;             // 0: no chunked prefill (shapes the GEMM does not take)
+    int pchunk = 0;                 // current chunk size (aw4_set_prefill_chunk), 0: token by token
+    int32_t* ptok = nullptr;        // [C] token ids
+    int32_t* pnext = nullptr;       // [C] the next token of each (draft head entries)
+    float* px = nullptr;            // [C][H] residuals
+    _Float16* pa = nullptr;         // [C][pa_ld] fp16 GEMM inputs
+    int64_t pa_ld = 0;
+    _Float16* pf = nullptr;         // [C][F] SwiGLU outputs
+    float* pp = nullptr;            // [C][max_in] projections
+    float* po = nullptr;            // [C][nv d] GDN readouts
+    float* pqn = nullptr;           // [C][nqk d]
+    float* pkn = nullptr;
+    float* pab = nullptr;           // [C][nv][2]
+    float* ppart = nullptr;         // attention partials, one split: [C nq][d + 2]
     uint64_t state_off = 0, state_bytes = 0;   // recurrent states + caches
     bool use_graph = true;
     hipGraphExec_t g_head = nullptr;
@@ -308,6 +324,32 @@ uint64_t plan_layout(const aw4_config* c, aw4_model* m, uint8_t* base) {
         vzpart = p.take<float>((uint64_t)MV * accept_blocks(c->vocab) * 4);
         vwpart = p.take<float>((uint64_t)MV * accept_blocks(c->vocab) * 4);
     }
+    // prefill chunk buffers, when every GEMM row length is a multiple of 64
+    const int64_t nvd = (int64_t)c->gdn_v_heads * c->gdn_head_dim, nqd = (int64_t)c->attn_q_heads * c->attn_head_dim;
+    bool gemm_ok = c->vocab > 0 && H % 64 == 0 && F % 64 == 0 && (!has_g || nvd % 64 == 0) &&
+                   (!(has_a || dh) || nqd % 64 == 0);
+    const int C = gemm_ok ? (int)std::min<int64_t>(kPrefillMaxChunk, c->max_ctx) : 0;
+    int32_t *ptok = nullptr, *pnext = nullptr;
+    float *px = nullptr, *pp = nullptr, *po = nullptr, *pqn = nullptr, *pkn = nullptr, *pab = nullptr, *ppart = nullptr;
+    _Float16 *pa = nullptr, *pf = nullptr;
+    int64_t pa_ld = 0;
+    if (C > 0) {
+        pa_ld = std::max<int64_t>(H, std::max(has_g ? nvd : 0, has_a || dh ? nqd : 0));
+        if (dh) pa_ld = std::max<int64_t>(pa_ld, 2 * H);
+        ptok = p.take<int32_t>((uint64_t)C * 4);
+        pnext = p.take<int32_t>((uint64_t)C * 4);
+        px = p.take<float>((uint64_t)C * H * 4);
+        pa = p.take<_Float16>((uint64_t)C * pa_ld * 2);
+        pf = p.take<_Float16>((uint64_t)C * F * 2);
+        pp = p.take<float>((uint64_t)C * max_in * 4);
+        if (has_g) {
+            po = p.take<float>((uint64_t)C * nvd * 4);
+            pqn = p.take<float>((uint64_t)C * c->gdn_qk_heads * c->gdn_head_dim * 4);
+            pkn = p.take<float>((uint64_t)C * c->gdn_qk_heads * c->gdn_head_dim * 4);
+            pab = p.take<float>((uint64_t)C * c->gdn_v_heads * 2 * 4);
+        }
+        if (has_a || dh) ppart = p.take<float>((uint64_t)C * c->attn_q_heads * (c->attn_head_dim + 2) * 4);
+    }
     float *xd = nullptr, *dscore = nullptr, *dpv = nullptr, *dzpart = nullptr;
     _Float16* ubuf = nullptr;
     int32_t* dpi = nullptr;
@@ -323,6 +365,19 @@ uint64_t plan_layout(const aw4_config* c, aw4_model* m, uint8_t* base) {
     }
     p.off = (p.off + 255) & ~uint64_t(255);
     if (m) {
+        m->pchunk_max = m->pchunk = C;
+        m->ptok = ptok;
+        m->pnext = pnext;
+        m->px = px;
+        m->pa = pa;
+        m->pa_ld = pa_ld;
+        m->pf = pf;
+        m->pp = pp;
+        m->po = po;
+        m->pqn = pqn;
+        m->pkn = pkn;
+        m->pab = pab;
+        m->ppart = ppart;
         m->D = D;
         m->w_fuse = w_fuse;
         m->s_fuse = s_fuse;
@@ -802,6 +857,108 @@ int enqueue_draft_select(aw4_model* m, int row, int j, int commit, float tempera
     return AW4_OK;
 }
 
+// ---------------------------------------------------------------- prefill
+// W4 GEMM of the chunk: out = x W^T over T tokens
+int prefill_gemm(aw4_model* m, int epi, const uint32_t* codes, const uint16_t* scales, int64_t N, int64_t K, int T,
+                 const _Float16* x, int64_t ldx, float* y, int64_t ldy, _Float16* hout, int64_t ldo) {
+    GemmArgs g{codes, scales, (int32_t)N, (int32_t)K, T, x, ldx, y, ldy, hout, ldo};
+    HIPCHK(m, launch_gemm_w4(epi, g, m->stream));
+    return AW4_OK;
+}
+
+// The layers `layers[0..nl)` on the T residuals x [T][H] of a prefill chunk,
+// whose tokens sit at cache positions *posp .. *posp + T - 1: per layer the
+// normalised inputs, the mixer input GEMM, the mixer (GDN over the tokens in
+// order, or append + causal attention over the cache), the output GEMM into
+// x, then the FFN (gate/up GEMM with SwiGLU, down GEMM into x).  Every token
+// computes what a decode step computes.
+int enqueue_prefill_layers(aw4_model* m, LayerBufs* layers, int nl, int T, float* x, const int32_t* posp) {
+    const aw4_config* c = &m->cfg;
+    hipStream_t s = m->stream;
+    const int64_t H = c->hidden, F = c->ffn;
+    const int C = m->pchunk_max;
+    int rc;
+    for (int l = 0; l < nl; ++l) {
+        LayerBufs& b = layers[l];
+        HIPCHK(m, launch_norm_rows(x, b.norm_mix, (int)H, c->rms_eps, T, m->pa, m->pa_ld, s));
+        if ((rc = prefill_gemm(m, EPI_STORE, b.w_in, b.s_in, b.in_rows, H, T, m->pa, m->pa_ld, m->pp, b.in_rows,
+                               nullptr, 0)))
+            return rc;
+        if (b.type == 'G') {
+            const int64_t nvd = (int64_t)c->gdn_v_heads * c->gdn_head_dim;
+            GdnPrefillArgs ga{m->pp, b.in_rows, b.a_bias, b.S, m->pqn, m->pkn, m->pab, m->po, nvd,
+                              c->gdn_qk_heads, c->gdn_v_heads, c->gdn_head_dim, T, c->rms_eps};
+            HIPCHK(m, launch_gdn_prefill(ga, b.norm_gated, m->pa, nvd, s));
+            if ((rc = prefill_gemm(m, EPI_RESID, b.w_out, b.s_out, H, nvd, T, m->pa, nvd, x, H, nullptr, 0)))
+                return rc;
+        } else {
+            const int64_t nqd = (int64_t)c->attn_q_heads * c->attn_head_dim;
+            AttnArgs aa{};
+            aa.nt = T;
+            aa.sproj = b.in_rows;
+            aa.proj = m->pp;
+            aa.kc = b.kc; aa.ks = b.ks; aa.vc = b.vc; aa.vs = b.vs;
+            aa.signs = m->signs; aa.pos = posp; aa.part = m->ppart; aa.prow = C * c->attn_q_heads;
+            aa.max_ctx = c->max_ctx; aa.nq = c->attn_q_heads; aa.nkv = c->attn_kv_heads;
+            aa.d = c->attn_head_dim; aa.nsplit = 1;
+            HIPCHK(m, launch_append(aa, s));
+            HIPCHK(m, launch_attn(aa, s));
+            CombineArgs ca{0, T, b.in_rows, m->ppart, m->pp, m->signs, posp, m->pa, aa.prow, c->attn_q_heads,
+                           c->attn_kv_heads, c->attn_head_dim, 1};
+            HIPCHK(m, launch_combine(ca, s));
+            if ((rc = prefill_gemm(m, EPI_RESID, b.w_out, b.s_out, H, nqd, T, m->pa, nqd, x, H, nullptr, 0)))
+                return rc;
+        }
+        HIPCHK(m, launch_norm_rows(x, b.norm_ffn, (int)H, c->rms_eps, T, m->pa, m->pa_ld, s));
+        if ((rc = prefill_gemm(m, EPI_SWIGLU, b.w_gu, b.s_gu, 2 * F, H, T, m->pa, m->pa_ld, nullptr, 0, m->pf, F)))
+            return rc;
+        if ((rc = prefill_gemm(m, EPI_RESID, b.w_down, b.s_down, H, F, T, m->pf, F, x, H, nullptr, 0))) return rc;
+    }
+    return AW4_OK;
+}
+
+// n prompt tokens in chunks: embedding rows, every layer over the chunk, the
+// positions advanced; with a draft head its cache gets the entries of the
+// chunk's positions whose next token is known; the last token's hidden state
+// ends in x (and through the head in logits when asked).
+int enqueue_prefill_chunked(aw4_model* m, const int32_t* tokens, int n, bool want_logits) {
+    const aw4_config* c = &m->cfg;
+    hipStream_t s = m->stream;
+    const int H = c->hidden;
+    const bool feed = c->draft_vocab > 0;
+    for (int i0 = 0; i0 < n; i0 += m->pchunk) {
+        const int T = std::min(m->pchunk, n - i0);
+        const bool last = i0 + T == n;
+        HIPCHK(m, hipMemcpyAsync(m->ptok, tokens + i0, (size_t)T * 4, hipMemcpyHostToDevice, s));
+        HIPCHK(m, launch_embed_rows(m->lm_codes, m->lm_scales, H, m->ptok, T, m->px, s));
+        int rc = enqueue_prefill_layers(m, m->L.data(), c->n_layers, T, m->px, &m->ctl->pos);
+        if (rc) return rc;
+        if (last) HIPCHK(m, launch_copy_f32(m->x, m->px + (int64_t)(T - 1) * H, H, s));
+        const int nf = last ? T - 1 : T;
+        if (feed && nf > 0) {
+            // draft head entries: (hidden of position i0 + t, token i0 + t + 1)
+            HIPCHK(m, hipMemcpyAsync(m->pnext, tokens + i0 + 1, (size_t)nf * 4, hipMemcpyHostToDevice, s));
+            DraftEmbedArgs de{m->lm_codes, m->lm_scales, m->pnext, m->px, H, m->dn_emb, m->dn_hid, m->pa, H, nf,
+                              c->rms_eps};
+            HIPCHK(m, launch_draft_embed(de, s));
+            if ((rc = prefill_gemm(m, EPI_STORE, m->w_fuse, m->s_fuse, H, 2LL * H, nf, m->pa, 2LL * H, m->px, H,
+                                   nullptr, 0)))
+                return rc;
+            if ((rc = enqueue_prefill_layers(m, &m->D, 1, nf, m->px, &m->ctl->dpos))) return rc;
+            m->host_dpos += nf;
+            HIPCHK(m, launch_set_dpos(m->ctl, m->host_dpos, s));
+        }
+        m->host_pos += T;
+        HIPCHK(m, launch_set_ctl(m->ctl, m->host_pos, -1, -1, s));
+    }
+    if (want_logits) {
+        HeadArgs ha{m->lm_codes, m->lm_scales, nullptr, c->vocab, H, m->x, m->norm_final, c->rms_eps, m->logits,
+                    m->pv, m->pi};
+        HIPCHK(m, launch_head(ha, s));
+    }
+    return AW4_OK;
+}
+
 int run_step(aw4_model* m, bool head) {
     if (!m->use_graph) return enqueue_step(m, head);
     hipGraphExec_t* ge = head ? &m->g_head : &m->g_nohead;
@@ -1227,29 +1384,42 @@ int aw4_prefill(aw4_model* m, const int32_t* tokens, int32_t n, float* dev_logit
     const bool feed = m->cfg.draft_vocab > 0;
     if (feed && n > 0 && (int64_t)m->host_dpos + n - 1 > m->cfg.max_ctx)
         return fail(m, AW4_E_CTX_FULL, "prompt exceeds the draft head's cache");
-    for (int i = 0; i < n; ++i) {
-        HIPCHK(m, launch_set_token(m->ctl, tokens[i], m->stream));
-        const bool last = i == n - 1;
-        int rc = run_step(m, last && dev_logits != nullptr);
+    if (n == 0) return AW4_OK;
+    if (m->pchunk > 0) {
+        int rc = enqueue_prefill_chunked(m, tokens, n, dev_logits != nullptr);
         if (rc) return rc;
-        m->host_pos += 1;
-        if (feed && !last) {
-            // the draft head's entry of this position: (its hidden state, the next prompt token)
-            const int32_t tok[4] = {tokens[i + 1], 0, 0, 0};
-            const float u[4] = {0.f, 0.f, 0.f, 0.f};
-            HIPCHK(m, launch_set_draft(m->ctl, tok, u, m->stream));
-            rc = enqueue_draft_block(m, 1, &m->ctl->dtok[0], m->x, m->cfg.hidden, 0);
+    } else {
+        // token by token through the decode step
+        for (int i = 0; i < n; ++i) {
+            HIPCHK(m, launch_set_token(m->ctl, tokens[i], m->stream));
+            const bool last = i == n - 1;
+            int rc = run_step(m, last && dev_logits != nullptr);
             if (rc) return rc;
-            m->host_dpos += 1;
-            HIPCHK(m, launch_set_dpos(m->ctl, m->host_dpos, m->stream));
+            m->host_pos += 1;
+            if (feed && !last) {
+                // the draft head's entry of this position: (its hidden state, the next prompt token)
+                const int32_t tok[4] = {tokens[i + 1], 0, 0, 0};
+                const float u[4] = {0.f, 0.f, 0.f, 0.f};
+                HIPCHK(m, launch_set_draft(m->ctl, tok, u, m->stream));
+                rc = enqueue_draft_block(m, 1, &m->ctl->dtok[0], m->x, m->cfg.hidden, 0);
+                if (rc) return rc;
+                m->host_dpos += 1;
+                HIPCHK(m, launch_set_dpos(m->ctl, m->host_dpos, m->stream));
+            }
         }
     }
-    if (n > 0) {
-        m->pend_src = 1;
-        m->pend_n = 0;
-    }
-    if (n > 0 && dev_logits)
+    m->pend_src = 1;
+    m->pend_n = 0;
+    if (dev_logits)
         HIPCHK(m, hipMemcpyAsync(dev_logits, m->logits, (size_t)m->cfg.vocab * 4, hipMemcpyDeviceToDevice, m->stream));
+    return AW4_OK;
+}
+
+int aw4_set_prefill_chunk(aw4_model* m, int32_t n) {
+    if (check_model(m)) return AW4_E_INVAL;
+    if (n < 0 || n > m->pchunk_max)
+        return fail(m, AW4_E_INVAL, "chunk must be in [0, " + std::to_string(m->pchunk_max) + "]");
+    m->pchunk = n;
     return AW4_OK;
 }
 

@@ -191,6 +191,34 @@ struct DraftSelArgs {
     float* q;                 // [V] draft probabilities of draft j, or null
 };
 
+// W4 GEMM of the prefill: Y[m][n] = sum_k X[m][k] W[n][k] over M tokens
+struct GemmArgs {
+    const uint32_t* codes;   // W4 GPU layout [N][K/8]
+    const uint16_t* scales;  // [N][K/32]
+    int32_t N, K, M;
+    const _Float16* x;       // [M][ldx] fp16 inputs
+    int64_t ldx;
+    float* y;                // STORE / RESID: [M][ldy]
+    int64_t ldy;
+    _Float16* hout;          // SWIGLU: [M][ldo], column n / 2 from rows n, n + 1
+    int64_t ldo;
+};
+
+// Gated DeltaNet over the T tokens of a prefill chunk
+struct GdnPrefillArgs {
+    const float* proj;       // token t's projections at proj + t * sproj
+    int64_t sproj;
+    const float* a_bias;
+    float* S;                // [nv][d][d], read at the start, written at the end
+    float* qn;               // [T][nqk][d] normalised q
+    float* kn;               // [T][nqk][d] normalised k
+    float* ab;               // [T][nv][2] alpha, beta
+    float* o;                // token t's readout at o + t * so
+    int64_t so;
+    int32_t nqk, nv, d, T;
+    float eps;
+};
+
 // ---------------------------------------------------------------- launches
 hipError_t launch_gemv(int pro, int epi, const GemvArgs& a, hipStream_t s);
 int gemv_blocks(int rows);
@@ -238,6 +266,14 @@ hipError_t launch_draft_select(const DraftSelArgs& a, hipStream_t s);
 int draft_chunks(int Vd);
 hipError_t launch_set_draft(Ctl* ctl, const int32_t* tok, const float* u, hipStream_t s);
 hipError_t launch_set_dpos(Ctl* ctl, int32_t dpos, hipStream_t s);
+hipError_t launch_gemm_w4(int epi, const GemmArgs& a, hipStream_t s);
+hipError_t launch_embed_rows(const int8_t* codes, const uint16_t* scales, int H, const int32_t* tok, int T, float* x,
+                             hipStream_t s);
+hipError_t launch_norm_rows(const float* x, const float* w, int K, float eps, int T, _Float16* out, int64_t ldo,
+                            hipStream_t s);
+// normalised q, k and gates, the recurrence, then fp16(RMSNorm(o) w SiLU(z)) into out [T][ldo]
+hipError_t launch_gdn_prefill(const GdnPrefillArgs& a, const float* gated_w, _Float16* out, int64_t ldo,
+                              hipStream_t s);
 
 // quantise fp32 rows into the GPU layouts
 hipError_t launch_quant_w4(const float* src, int64_t nrows, int64_t cols, uint32_t* codes, uint16_t* scales,

@@ -167,7 +167,8 @@ __device__ void encode_append(const float* kp, const float* vp, const float* sig
 
 // NT tokens at consecutive positions share one sweep over the cache: query
 // column c of the score product is token c / G, head c % G (QC = G NT <= 16
-// columns), and token m sees positions up to its own.
+// columns), and token m sees positions up to its own.  Grid z: blocks of NT
+// tokens of a longer run (a prefill chunk), block b taking tokens b NT ...
 template <int D, int G, int NT>
 __global__ __launch_bounds__(512, 1) void k_attn(AttnArgs a) {
     constexpr int NG = D / 32;          // scale groups
@@ -186,10 +187,11 @@ __global__ __launch_bounds__(512, 1) void k_attn(AttnArgs a) {
     __shared__ float mm[kWaves][QC], ll[kWaves][QC];
 
     const int split = blockIdx.x, j = blockIdx.y, tid = threadIdx.x;
+    const int tb0 = blockIdx.z * NT;          // the block's first token in the run
     const int lane = tid & 63, w = tid >> 6;
     const int c = lane & 15, q = lane >> 4;
-    const int pos = *a.pos + a.pos_offset;   // the first token's position
-    const int nt = NT == 1 ? 1 : a.nt;
+    const int pos = *a.pos + a.pos_offset + tb0;   // the block's first token's position
+    const int nt = NT == 1 ? 1 : min(NT, a.nt - tb0);
     const int npos = pos + nt;
     int pps, used;
     split_range(npos, a.nsplit, pps, used);
@@ -283,7 +285,7 @@ __global__ __launch_bounds__(512, 1) void k_attn(AttnArgs a) {
     const int lim = pos + cm;                          // last position column c sees
     h8 qh[NG], ql[NG];
     {
-        const float* qp = a.proj + (int64_t)cm * a.sproj + (int64_t)(j * G + cg) * D + 8 * q;
+        const float* qp = a.proj + (int64_t)(tb0 + cm) * a.sproj + (int64_t)(j * G + cg) * D + 8 * q;
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
             float4 x0 = make_float4(0.f, 0.f, 0.f, 0.f), x1 = x0;
@@ -428,7 +430,7 @@ __global__ __launch_bounds__(512, 1) void k_attn(AttnArgs a) {
 
     // partial rows: column c of kv head j is slot (c / G) nq + j G + c % G
     float* mlp = a.part + (int64_t)a.prow * a.nsplit * D;
-    auto slot_row = [&](int cc) { return (int64_t)((cc / G) * a.nq + j * G + cc % G) * a.nsplit + split; };
+    auto slot_row = [&](int cc) { return (int64_t)((tb0 + cc / G) * a.nq + j * G + cc % G) * a.nsplit + split; };
     if (kOnePass) {
         // every wave posts (m, l, acc) of its columns; lane (c, q) holds column c,
         // dims 16 b + 4 q + rr; then one pass merges the waves per output
@@ -641,14 +643,15 @@ hipError_t launch_append(const AttnArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+// a.nt tokens: one sweep block per attn_tokens_per_sweep tokens (grid z)
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
     const int G = a.nq / a.nkv;
-    if (a.nsplit < 1 || a.nsplit > 256 || a.nt < 1 || a.nt > attn_tokens_per_sweep(a.d, a.nq, a.nkv) ||
-        (a.nt > 1 && a.append) || a.nq * a.nt > a.prow)
+    if (a.nsplit < 1 || a.nsplit > 256 || a.nt < 1 || (a.nt > 1 && a.append) || a.nq * a.nt > a.prow)
         return hipErrorInvalidValue;
-    const dim3 grid(a.nsplit, a.nkv), block(64 * kWaves);
+    const int nn = a.nt == 1 ? 1 : attn_tokens_per_sweep(a.d, a.nq, a.nkv);
+    const dim3 grid(a.nsplit, a.nkv, (a.nt + nn - 1) / nn), block(64 * kWaves);
 #define AW4_ATTN_CASE(DD, GG, NN)                                               \
-    if (a.d == DD && G == GG && (NN == 1 ? a.nt == 1 : a.nt > 1)) {            \
+    if (a.d == DD && G == GG && nn == NN) {                                     \
         hipLaunchKernelGGL((k_attn<DD, GG, NN>), grid, block, 0, s, a);         \
         return hipGetLastError();                                               \
     }

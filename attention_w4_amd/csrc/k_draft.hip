@@ -199,7 +199,7 @@ __global__ void k_set_dpos(Ctl* ctl, int32_t dpos) { ctl->dpos = dpos; }
 int draft_chunks(int Vd) { return (Vd + kDraftChunk - 1) / kDraftChunk; }
 
 hipError_t launch_draft_embed(const DraftEmbedArgs& a, hipStream_t s) {
-    if (a.M < 1 || a.M > 4 || a.H % 32 || a.H > 4 * 256 * kEmbMaxPer) return hipErrorInvalidValue;
+    if (a.M < 1 || a.H % 32 || a.H > 4 * 256 * kEmbMaxPer) return hipErrorInvalidValue;
     hipLaunchKernelGGL(k_draft_embed, dim3(a.M), dim3(256), 0, s, a);
     return hipGetLastError();
 }

@@ -197,6 +197,16 @@ int aw4_reset(aw4_model* model);
  * token).  Errors: AW4_E_CTX_FULL, AW4_E_TOKEN, AW4_E_STATE (vocab 0). */
 int aw4_prefill(aw4_model* model, const int32_t* host_tokens, int32_t n, float* dev_logits);
 
+/* Prompt tokens per prefill chunk.  aw4_prefill runs a prompt in chunks of up
+ * to n tokens: each chunk goes through every layer together (the W4 matrices
+ * read once per chunk on the matrix cores, the GDN recurrence over the
+ * chunk's tokens in order, attention over the cache with causal masks), with
+ * the same per-token arithmetic as a decode step.  n = 0 runs the prompt token
+ * by token through the decode step.  The default and the maximum is
+ * min(1024, max_ctx); shapes whose matrix row lengths are not multiples of 64
+ * have no chunked path (maximum 0).  Errors: AW4_E_INVAL. */
+int aw4_set_prefill_chunk(aw4_model* model, int32_t n);
+
 /* One decode step on `token` at the current position: embed, all layers
  * (appending this position to the caches), final norm, output head, argmax
  * (lowest index on ties).  dev_logits (optional) receives fp32 [vocab];

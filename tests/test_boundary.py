@@ -57,12 +57,20 @@ def test_invalid_configs(kw):
 def test_workspace_bytes_full_model():
     n = A.workspace_bytes(W.FULL_27B)
     # W4 layer weights 12.843 GB + int8 head 1.351 GB (4.5 and 8.5 bits per weight),
-    # GDN state 48 * 2 MiB... plus the KV cache for max_ctx positions
+    # GDN state 48 * 2 MiB... plus the KV cache for max_ctx positions; the draft
+    # head's W4 block and fuse (424.7 M weights), its cache and its id maps; the
+    # prefill chunk buffers for 1024 tokens
     s = W.FULL_27B
-    kv = 16 * s.attn_kv_heads * s.max_ctx * (s.attn_head_dim * (1 + 3 / 8) + 4 * s.attn_head_dim / 32)
-    weights = 14_194_278_400
+    H, F, C = s.hidden, s.ffn, 1024
+    kv_pos = s.attn_kv_heads * (s.attn_head_dim * (1 + 3 / 8) + 4 * s.attn_head_dim / 32)
+    kv = 17 * kv_pos * s.max_ctx
+    weights = 14_194_278_400 + 424_673_280 * 9 // 16 + 4 * (s.draft_vocab + s.vocab)
     state = 48 * s.gdn_v_heads * s.gdn_head_dim ** 2 * 4
-    assert weights + state + kv < n < (weights + state + kv) * 1.02
+    nvd, nqd = s.gdn_v_heads * s.gdn_head_dim, s.attn_q_heads * s.attn_head_dim
+    prefill = C * (4 * H + 2 * 2 * H + 2 * F + 4 * (2 * nqd + 2 * 1024) + 4 * nvd + 8 * s.gdn_qk_heads * s.gdn_head_dim
+                   + 8 * s.gdn_v_heads + 4 * s.attn_q_heads * (s.attn_head_dim + 2))
+    need = weights + state + kv + prefill
+    assert need < n < need * 1.02
 
 
 def test_create_rejects_bad_arena_without_touching_device():

@@ -1,0 +1,184 @@
+"""GPU parity of chunked prefill (aw4_prefill with aw4_set_prefill_chunk)
+against the oracle, which runs the prompt token by token through its decode
+step: the definition of what prefill computes.
+
+Each chunk runs every layer over its tokens together (W4 GEMM on the matrix
+cores, the GDN recurrence over the tokens in order, append + causal attention
+over the cache); the per-token arithmetic is the decode step's, so the final
+hidden state and logits must agree with the oracle to 1e-2 relative L2, the
+greedy continuation must be identical, the recurrent states must agree and the
+cache codes may differ only by one at rounding ties.  Chunk sizes are chosen so
+that chunks end mid-prompt and the last chunk is ragged.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from oracle.draft import DraftDriver
+from synth import workloads as W
+from tests.helpers import TINY, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-2
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def aw4():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import attention_w4_amd as A
+    A.lib()
+    return A
+
+
+def _gpu(A, shape, seed, jitter=0.0):
+    from synth.gpu_load import load_recipe
+    gm = A.Model(shape)
+    load_recipe(gm, shape, seed, jitter)
+    return gm
+
+
+def _check_states(gm, om, shape):
+    for l, t in enumerate(shape.pattern):
+        if t == "G":
+            assert rel_l2(gm.export_gdn(l), om.get_gdn_state(l)) < TOL, l
+        else:
+            gk, ok = gm.export_kv(l, om.pos), om.get_kv(l, om.pos)
+            for a, b in ((gk[0], ok[0]), (gk[2], ok[2])):
+                d = a.astype(int) - b.astype(int)
+                assert np.abs(d).max() <= 1 and (d != 0).mean() < 6e-2, l
+
+
+def _prefill_vs_oracle(A, shape, seed, jitter, n_prompt, chunk, n_greedy):
+    import torch
+    prompt = synth.tokens(n_prompt, shape.vocab, seed)
+    gm = _gpu(A, shape, seed, jitter)
+    gm.set_prefill_chunk(chunk)
+    logits = torch.empty(shape.vocab, dtype=torch.float32, device="cuda")
+    gm.prefill(prompt, logits)
+    xg, lg = gm.read_hidden(), logits.cpu().numpy()
+    om = oracle.from_recipe(shape, seed, jitter)
+    for t in prompt:
+        xo, lo, am = om.decode_token(int(t))
+    _say(f"prompt {n_prompt} in chunks of {chunk}: hidden rel-L2 {rel_l2(xg, xo):.2e}, "
+         f"logits rel-L2 {rel_l2(lg, lo):.2e}")
+    assert gm.pos == om.pos == n_prompt
+    assert rel_l2(xg, xo) < TOL and rel_l2(lg, lo) < TOL
+    assert int(np.argmax(lg)) == am
+    _check_states(gm, om, shape)
+    got = list(gm.decode_greedy(am, n_greedy))
+    ref, tok = [], am
+    for _ in range(n_greedy):
+        _, _, tok = om.decode_token(tok)
+        ref.append(tok)
+    assert got == ref
+    gm.close()
+
+
+@pytest.mark.parametrize("chunk", [128, 1024])
+def test_prefill_toy_matches_oracle(aw4, chunk):
+    _say("case: toy stack prefill, 300 tokens, chunk", chunk)
+    _prefill_vs_oracle(aw4, W.TOY, 0, 0.0, 300, chunk, 32)
+
+
+def test_prefill_tiny_grouped_heads(aw4):
+    _say("case: tiny stack (grouped heads, jittered norms) prefill, 40 tokens, chunk 16")
+    _prefill_vs_oracle(aw4, TINY, 12, 0.2, 40, 16, 8)
+
+
+def test_prefill_chunked_equals_token_by_token(aw4):
+    """The same prompt token by token (chunk 0) and in chunks of 100: the same
+    final state up to rounding order."""
+    _say("case: toy stack prefill, chunks of 100 vs token by token")
+    shape = W.TOY
+    prompt = synth.tokens(257, shape.vocab, 4)
+    res = []
+    for chunk in (0, 100):
+        gm = _gpu(aw4, shape, 4)
+        gm.set_prefill_chunk(chunk)
+        gm.prefill(prompt)
+        res.append((gm.read_hidden(), gm.export_gdn(0), gm.export_kv(1, 257), gm.decode_greedy(7, 16)))
+        gm.close()
+    assert rel_l2(res[1][0], res[0][0]) < 1e-3
+    assert rel_l2(res[1][1], res[0][1]) < 1e-3
+    d = res[1][2][0].astype(int) - res[0][2][0].astype(int)
+    assert np.abs(d).max() <= 1 and (d != 0).mean() < 1e-2
+    assert np.array_equal(res[0][3], res[1][3])
+
+
+def test_prefill_feeds_draft_head(aw4):
+    """Toy stack with a draft head: prefill in chunks of 32 gives the draft
+    head one entry per prompt position but the last, as the oracle's token by
+    token feeding does; the drafts that follow agree."""
+    import torch
+    _say("case: toy stack with draft head, prefill 100 tokens in chunks of 32, then 3 drafts")
+    shape = W.TOY_MTP
+    prompt = synth.tokens(100, shape.vocab, 5)
+    gm = _gpu(aw4, shape, 5, 0.1)
+    gm.set_prefill_chunk(32)
+    logits = torch.empty(shape.vocab, dtype=torch.float32, device="cuda")
+    gm.prefill(prompt, logits)
+    dd = DraftDriver(oracle.from_recipe(shape, 5, 0.1))
+    _, lo, t0 = dd.prefill(prompt)
+    assert gm.dpos == dd.m.dpos == 99
+    assert int(torch.argmax(logits).item()) == t0
+    D = shape.n_layers
+    gk, ok = gm.export_kv(D, 99), dd.m.get_kv(D, 99)
+    for a, b in ((gk[0], ok[0]), (gk[2], ok[2])):
+        d = a.astype(int) - b.astype(int)
+        assert np.abs(d).max() <= 1 and (d != 0).mean() < 6e-2
+    scores = torch.empty(3, shape.draft_vocab, dtype=torch.float32, device="cuda")
+    got = gm.draft(t0, 3, scores=scores)
+    ref, _, z = dd.draft(t0, 3)
+    for j in range(3):
+        assert rel_l2(scores[j].cpu().numpy(), z[j]) < TOL, j
+    assert got == ref
+    gm.close()
+
+
+@pytest.mark.timeout(900)
+def test_prefill_full_size(aw4):
+    """The 27B-shape stack (with its draft head) from a 512-position synthetic
+    state: a 40-token prompt in chunks of 16 (every full-size GEMM shape with
+    ragged token tiles), then three drafts.  From an empty cache the first
+    tokens attend to one or two entries, so a single 3-bit value code at a
+    rounding tie moves their heads by several percent (measured: 2e-1 relative
+    difference after one token between two GPU paths, 4e-3 per attention layer
+    from one flipped code); with 512 cached positions the same flip is diluted."""
+    import torch
+    from synth import state as SS
+    _say("case: full 27B-shape stack, 512-position state, prefill 40 tokens in chunks of 16, then 3 drafts")
+    shape = W.with_(W.FULL_27B, max_ctx=600)
+    prompt = synth.tokens(40, shape.vocab, 6)
+    gm = _gpu(aw4, shape, 6)
+    SS.fill(gm, shape, 512, 6)
+    gm.set_prefill_chunk(16)
+    logits = torch.empty(shape.vocab, dtype=torch.float32, device="cuda")
+    gm.prefill(prompt, logits)
+    xg, lg = gm.read_hidden(), logits.cpu().numpy()
+    assert gm.pos == 552 and gm.dpos == 511 + 39
+    scores = torch.empty(3, shape.draft_vocab, dtype=torch.float32, device="cuda")
+    t0g = int(np.argmax(lg))
+    got = gm.draft(t0g, 3, scores=scores)
+    sc = scores.cpu().numpy()
+    gm.close()
+    del gm
+    torch.cuda.empty_cache()
+    om = oracle.from_recipe(shape, 6)
+    SS.fill(om, shape, 512, 6)
+    dd = DraftDriver(om)
+    xo, lo, t0 = dd.prefill(prompt)
+    ref, _, z = dd.draft(t0, 3)
+    derr = [rel_l2(sc[j], z[j]) for j in range(3)]
+    _say(f"hidden rel-L2 {rel_l2(xg, xo):.2e}, logits rel-L2 {rel_l2(lg, lo):.2e}, draft scores {derr}")
+    assert rel_l2(xg, xo) < TOL and rel_l2(lg, lo) < TOL
+    assert t0g == t0 and got == ref and max(derr) < TOL
