@@ -19,6 +19,7 @@ T_MIX_IN, T_MIX_OUT, T_FFN_GATE, T_FFN_UP, T_FFN_DOWN, T_LM_HEAD = 0, 1, 2, 3, 4
 T_NORM_MIX, T_NORM_FFN, T_NORM_GATED, T_A_BIAS, T_NORM_FINAL, T_RHT_SIGNS = 6, 7, 8, 9, 10, 11
 T_DRAFT_FUSE, T_DRAFT_NORM_EMB, T_DRAFT_NORM_HID, T_DRAFT_NORM_OUT, T_DRAFT_MAP = 12, 13, 14, 15, 16
 PHASE_FFN_GATE_UP, PHASE_FFN_DOWN, PHASE_MIX_IN, PHASE_HEAD, PHASE_DRAFT_HEAD = 0, 1, 2, 3, 4
+PHASE_PREFILL_GATE_UP = 5
 
 _i32, _i64, _u64, _f32, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_float, ctypes.c_void_p
 

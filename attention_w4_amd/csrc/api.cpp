@@ -671,6 +671,15 @@ int enqueue_phase(aw4_model* m, int phase, int l, uint64_t* bytes) {
             HIPCHK(m, launch_head(ha, s));
             break;
         }
+        case AW4_PHASE_PREFILL_GATE_UP: {
+            // the prefill chunk's gate/up GEMM with SwiGLU: 2 M N K flops
+            const int M = m->pchunk_max;
+            if (M <= 0) return fail(m, AW4_E_STATE, "no chunked prefill for this shape");
+            *bytes = 2ULL * M * (2ULL * F) * H;
+            GemmArgs ga{b.w_gu, b.s_gu, 2 * F, H, M, m->pa, m->pa_ld, nullptr, 0, m->pf, F};
+            HIPCHK(m, launch_gemm_w4(EPI_SWIGLU, ga, s));
+            break;
+        }
         default:
             return fail(m, AW4_E_INVAL, "unknown phase");
     }
@@ -1532,7 +1541,7 @@ int aw4_read_hidden(aw4_model* m, float* host_x) {
 
 int aw4_time_phase(aw4_model* m, int32_t phase, int32_t reps, float* avg_us, uint64_t* bytes_per_launch) {
     if (check_model(m) || reps < 1 || !avg_us || !bytes_per_launch) return AW4_E_INVAL;
-    if (phase < 0 || phase > AW4_PHASE_DRAFT_HEAD) return fail(m, AW4_E_INVAL, "unknown phase");
+    if (phase < 0 || phase > AW4_PHASE_PREFILL_GATE_UP) return fail(m, AW4_E_INVAL, "unknown phase");
     hipEvent_t e0, e1;
     HIPCHK(m, hipEventCreate(&e0));
     HIPCHK(m, hipEventCreate(&e1));

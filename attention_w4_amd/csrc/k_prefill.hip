@@ -3,12 +3,13 @@
 // Prefill is the step before decode (the pages time it apart from decode:
 // page 3 "Qwen3.8-27B 實測", the prompt-processing figures of the NVFP4 vLLM
 // and DGX Spark runs, and page 4's note that a 100K-token input takes about
-// two minutes).  Every token computes exactly what a decode step computes (the
-// same fp16 inputs, exact W4 codes, fp32 accumulation, the same KV codec and
-// GDN recurrence); what changes is that the weights are read once per chunk:
-//   - W4 GEMM on the matrix cores: one v_mfma_f32_16x16x32_f16 per 32-value
-//     group on exact codes, the fp16 group scale applied to each row of the
-//     fp32 product, as in the M <= 4 verify kernel, tiled for many tokens;
+// two minutes).  Every token computes what a decode step computes (the same
+// fp16 inputs, fp32 accumulation, the same KV codec and GDN recurrence); what
+// changes is that the weights are read once per chunk:
+//   - W4 GEMM on the matrix cores with exact weights: the fp16 group scale s
+//     splits into s_hi (its top 7 significant bits) and s_lo = s - s_hi (the
+//     rest), code x s_hi and code x s_lo are both exact in fp16, and two
+//     products per group accumulate in place in fp32;
 //   - Gated DeltaNet: the normalised q, k and the gates of all chunk tokens
 //     first, then one workgroup per (v head, 16 state rows) runs the tokens in
 //     order with its rows of S in registers;
@@ -49,16 +50,18 @@ __device__ __forceinline__ float block_sum256(float v, float* red) {
 // Y[m][n] = sum_k X[m][k] W[n][k] over M tokens: a workgroup of four waves
 // covers 128 rows x 128 tokens, each wave 64 x 64 (4 x 4 blocks of 16 x 16).
 // Stages of two 32-value groups: the token tile (fp16), the rows' code dwords
-// and their scales are staged in LDS (double buffered, the next stage loaded
-// into registers while the current one is multiplied).  A operand: the exact
-// codes of 16 rows, lane (c, q) row c, values 8q..8q+7 of the group (one
-// dword, nibble slots [0,2,4,6,1,3,5,7]); B operand: 16 tokens, lane (c, q)
-// token c, the same values.  D lane (c, q) holds rows 4q..4q+3 of token c.
+// and their scales are staged in LDS (double buffered; two register sets hold
+// the next two stages, so a stage's loads have two stages of products to
+// arrive in).  A operands: 16 rows' code x s_hi and code x s_lo, lane (c, q)
+// row c, values 8q..8q+7 of the group (one code dword, nibble slots
+// [0,2,4,6,1,3,5,7], and the row's scale);
+// B operand: 16 tokens, lane (c, q) token c, the same values.  D lane (c, q)
+// holds rows 4q..4q+3 of token c.
 constexpr int kGBK = 64;            // K values per stage (two groups)
 constexpr int kGXP = kGBK + 8;      // padded LDS row of the token tile (halves)
 
 template <int EPI>
-__global__ __launch_bounds__(256, 2) void k_gemm_w4(GemmArgs a) {
+__global__ __launch_bounds__(256, 3) void k_gemm_w4(GemmArgs a) {
     __shared__ __align__(16) _Float16 xs[2][128][kGXP];
     __shared__ __align__(16) uint32_t cs[2][128][8];     // [row][group 0..1][dword 0..3]
     __shared__ __align__(16) uint16_t ss[2][2][128];     // [group][row]
@@ -70,7 +73,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm_w4(GemmArgs a) {
 
     // tiles in XCD order: consecutive workgroups go to the eight XCDs in turn,
     // so the token tiles of one row tile are given to one XCD back to back and
-    // its weights stay in that XCD's L2
+    // its weights stay in that XCD's L2 (measured faster than giving each XCD
+    // one token tile and streaming the weights past it)
     const int ntt = (a.M + 127) / 128, nrt = (a.N + 127) / 128;
     const int b = blockIdx.x, xcd = b & 7, kx = b >> 3;
     const int rt = 8 * (kx / ntt) + xcd, tt = kx % ntt;
@@ -118,7 +122,6 @@ __global__ __launch_bounds__(256, 2) void k_gemm_w4(GemmArgs a) {
     const h2 off_lo = {(_Float16)-1032.0f, (_Float16)-1032.0f};
     const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
     const h2 off_hi = {(_Float16)-72.0f, (_Float16)-72.0f};
-    const f4 zero = {0.f, 0.f, 0.f, 0.f};
 
     auto compute = [&](int buf) {
 #pragma unroll
@@ -136,30 +139,44 @@ __global__ __launch_bounds__(256, 2) void k_gemm_w4(GemmArgs a) {
                 const h2 p1 = __builtin_elementwise_fma(as_h2((w & 0x00F000F0u) | 0x64006400u), sixteenth, off_hi);
                 const h2 p2 = as_h2((w8 & 0x000F000Fu) | 0x64006400u) + off_lo;
                 const h2 p3 = __builtin_elementwise_fma(as_h2((w8 & 0x00F000F0u) | 0x64006400u), sixteenth, off_hi);
-                const h8 av = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-                const uint2 sv = *(const uint2*)&ss[buf][g][r + 4 * q];
-                const float s0 = as_h2(sv.x)[0], s1 = as_h2(sv.x)[1], s2 = as_h2(sv.y)[0], s3 = as_h2(sv.y)[1];
+                // s = s_hi + s_lo, s_hi with 7 significant bits: |code| <= 8 keeps
+                // both products exact in fp16 (s_lo may be subnormal)
+                const uint16_t sb = ss[buf][g][r + c];
+                const _Float16 shi = __builtin_bit_cast(_Float16, (uint16_t)(sb & 0xFFF0u));
+                const _Float16 slo = __builtin_bit_cast(_Float16, sb) - shi;
+                const h2 s2h = {shi, shi}, s2l = {slo, slo};
+                const h2 a0 = p0 * s2h, a1 = p1 * s2h, a2 = p2 * s2h, a3 = p3 * s2h;
+                const h2 b0 = p0 * s2l, b1 = p1 * s2l, b2 = p2 * s2l, b3 = p3 * s2l;
+                const h8 ah = {a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
+                const h8 al = {b0[0], b0[1], b1[0], b1[1], b2[0], b2[1], b3[0], b3[1]};
 #pragma unroll
                 for (int tb = 0; tb < 4; ++tb) {
-                    const f4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv[tb], zero, 0, 0, 0);
-                    acc[rb][tb][0] += s0 * d[0];
-                    acc[rb][tb][1] += s1 * d[1];
-                    acc[rb][tb][2] += s2 * d[2];
-                    acc[rb][tb][3] += s3 * d[3];
+                    acc[rb][tb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bv[tb], acc[rb][tb], 0, 0, 0);
+                    acc[rb][tb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bv[tb], acc[rb][tb], 0, 0, 0);
                 }
             }
         }
     };
 
-    Stage st;
-    gload(st, 0);
-    lstore(st, 0);
+    // unrolled by two so that the register sets keep fixed roles: in the first
+    // half LDS buffer 0 holds stage s and sb stage s + 1, in the second half
+    // buffer 1 holds stage s + 1 and sa stage s + 2.  Loads past the last
+    // stage re-read it (the same straight-line loads every time, so the wait
+    // counts stay exact); only the products of a missing odd stage are skipped.
+    auto sidx = [&](int t) { return t < nstage ? t : nstage - 1; };
+    Stage sa, sb;
+    gload(sa, 0);
+    gload(sb, sidx(1));
+    lstore(sa, 0);
     __syncthreads();
-    for (int s = 0; s < nstage; ++s) {
-        const bool more = s + 1 < nstage;
-        if (more) gload(st, s + 1);
-        compute(s & 1);
-        if (more) lstore(st, (s + 1) & 1);
+    for (int s = 0; s < nstage; s += 2) {
+        gload(sa, sidx(s + 2));
+        compute(0);
+        lstore(sb, 1);
+        __syncthreads();
+        gload(sb, sidx(s + 3));
+        if (s + 1 < nstage) compute(1);
+        lstore(sa, 0);
         __syncthreads();
     }
 

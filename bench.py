@@ -286,13 +286,14 @@ def main():
     load_recipe(m, shape, args.seed)
     t_load = time.time() - t0
     prompt = synth.tokens(args.ctx, shape.vocab, args.seed)
-    t0 = time.time()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
     if args.prompt == "decode":
         m.prefill(prompt[:-1])
     else:
         SS.fill(m, shape, args.ctx - 1, args.seed)
     m.sync()
-    t_prompt = time.time() - t0
+    t_prompt = time.perf_counter() - t0
     first = int(prompt[-1])
     warm = m.decode_greedy(first, args.warmup) if args.warmup else [first]
     tok = int(warm[-1])
@@ -322,6 +323,18 @@ def main():
     for name, ph in (("ffn_down", A.PHASE_FFN_DOWN), ("mixer_in", A.PHASE_MIX_IN)):
         u, b = m.time_phase(ph, args.phase_reps)
         others[name] = {"avg_us": round(u, 2), "bytes": b, "GB/s": round(b / (u * 1e-6) / 1e9, 1)}
+    # prefill: the prompt above through aw4_prefill (chunks of 1024 tokens),
+    # and its dominant kernel, the gate/up W4 GEMM over one chunk, on MFMA
+    prefill = None
+    if args.prompt == "decode":
+        pu, pf = m.time_phase(A.PHASE_PREFILL_GATE_UP, max(4, args.phase_reps // 16))
+        prefill = {"tokens": args.ctx - 1, "s": round(t_prompt, 3), "tok/s": round((args.ctx - 1) / t_prompt, 1),
+                   "chunk": 1024, "note": "also feeds the draft head one entry per prompt position",
+                   "gemm_roofline": {"kernel": "k_gemm_w4 (FFN gate/up + SwiGLU), M 1024 tokens, N 34816, K 5120",
+                                     "bound": "mfma", "achieved": round(pf / (pu * 1e-6) / 1e12, 1),
+                                     "peak": 2500.0, "unit": "TFLOP/s",
+                                     "frac": round(pf / (pu * 1e-6) / 1e12 / 2500.0, 4), "avg_launch_us": round(pu, 2),
+                                     "flops_per_launch": pf}}
 
     out = {
         "metric": "batch-1 decode tok/s (27B-shape W4) + % of HBM roofline, 8K and 262K ctx",
@@ -346,6 +359,7 @@ def main():
                      "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": gateup_traffic(),
                      "avg_launch_us": round(us, 3), "bytes_per_launch": nbytes, "other_kernels": others},
+        "prefill": prefill,
         "setup_s": {"load": round(t_load, 1), "prompt": round(t_prompt, 1)},
         "first_tokens": [int(t) for t in toks[:8]],
     }

@@ -283,14 +283,17 @@ int aw4_set_graph(aw4_model* model, int32_t enable);
  * times, cycling through the layers so that consecutive launches stream
  * different weights, between two HIP events on the model's stream, and
  * returns the average launch-to-launch duration (microseconds) and the
- * algorithmic bytes one launch moves (weights + scales + activations read and
- * written).  Synchronous.  Leaves activations scratch overwritten. */
+ * algorithmic work of one launch: the bytes it moves (weights + scales +
+ * activations read and written) for the decode phases, the flops (2 M N K) for
+ * the prefill GEMM phase.  Synchronous.  Leaves activations scratch
+ * overwritten. */
 enum {
     AW4_PHASE_FFN_GATE_UP = 0,   /* RMSNorm + gate/up W4 GEMV + SwiGLU  */
     AW4_PHASE_FFN_DOWN = 1,      /* down W4 GEMV + residual add          */
     AW4_PHASE_MIX_IN = 2,        /* RMSNorm + mixer input W4 GEMV         */
     AW4_PHASE_HEAD = 3,          /* final norm + int8 head over the vocab */
-    AW4_PHASE_DRAFT_HEAD = 4     /* draft output norm + int8 head over the mapped ids */
+    AW4_PHASE_DRAFT_HEAD = 4,    /* draft output norm + int8 head over the mapped ids */
+    AW4_PHASE_PREFILL_GATE_UP = 5 /* gate/up W4 GEMM + SwiGLU over a full prefill chunk */
 };
 int aw4_time_phase(aw4_model* model, int32_t phase, int32_t reps, float* avg_us, uint64_t* bytes_per_launch);
 
