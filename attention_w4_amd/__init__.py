@@ -29,7 +29,7 @@ class Config(ctypes.Structure):
                 ("gdn_qk_heads", _i32), ("gdn_v_heads", _i32), ("gdn_head_dim", _i32),
                 ("attn_q_heads", _i32), ("attn_kv_heads", _i32), ("attn_head_dim", _i32),
                 ("group", _i32), ("max_ctx", _i32), ("max_verify", _i32), ("rms_eps", _f32),
-                ("layer_pattern", ctypes.c_char * 128), ("draft_vocab", _i32)]
+                ("layer_pattern", ctypes.c_char * 128), ("draft_vocab", _i32), ("max_batch", _i32)]
 
     @classmethod
     def from_shape(cls, s):
@@ -41,6 +41,7 @@ class Config(ctypes.Structure):
         c.rms_eps = float(s.rms_eps)
         c.layer_pattern = s.pattern.encode()
         c.draft_vocab = int(getattr(s, "draft_vocab", 0))
+        c.max_batch = int(getattr(s, "max_batch", 1))
         return c
 
 
@@ -77,6 +78,8 @@ _SIGS = {
     "aw4_set_pos": [_vp, _i32],
     "aw4_get_draft_pos": [_vp, ctypes.POINTER(_i32)],
     "aw4_set_draft_pos": [_vp, _i32],
+    "aw4_select_sequence": [_vp, _i32],
+    "aw4_decode_batch": [_vp, _vp, _i32, _vp],
     "aw4_time_phase": [_vp, _i32, _i32, ctypes.POINTER(_f32), ctypes.POINTER(_u64)],
     "aw4_export_state_gdn": [_vp, _i32, _vp],
     "aw4_import_state_gdn": [_vp, _i32, _vp],
@@ -273,6 +276,17 @@ class Model:
                                  q.data_ptr() if q is not None else None,
                                  scores.data_ptr() if scores is not None else None, _ptr(out)), "draft")
         return [int(v) for v in out[:k]]
+
+    def select_sequence(self, s):
+        self._rc(lib().aw4_select_sequence(self.h, int(s)), "select_sequence")
+
+    def decode_batch(self, tokens):
+        """one greedy step for sequences 0 .. len(tokens) - 1; returns their argmax tokens"""
+        import numpy as np
+        t = np.ascontiguousarray(tokens, np.int32)
+        out = np.zeros(4, np.int32)
+        self._rc(lib().aw4_decode_batch(self.h, _ptr(t), len(t), _ptr(out)), "decode_batch")
+        return [int(v) for v in out[:len(t)]]
 
     @property
     def dpos(self):

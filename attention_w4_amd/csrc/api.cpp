@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <type_traits>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -134,7 +135,13 @@ struct aw4_model {
     float* pkn = nullptr;
     float* pab = nullptr;           // [C][nv][2]
     float* ppart = nullptr;         // attention partials, one split: [C nq][d + 2]
-    uint64_t state_off = 0, state_bytes = 0;   // recurrent states + caches
+    uint64_t state_off = 0, state_bytes = 0;   // recurrent states + caches of one sequence
+    // sequences: max_batch copies of the state region, state_bytes apart; the
+    // single-sequence calls work on sequence `seq` (aw4_select_sequence)
+    int max_batch = 1;
+    int seq = 0;
+    int32_t seq_pos[4] = {0, 0, 0, 0};
+    int32_t seq_dpos[4] = {0, 0, 0, 0};
     bool use_graph = true;
     hipGraphExec_t g_head = nullptr;
     hipGraphExec_t g_nohead = nullptr;
@@ -282,6 +289,8 @@ uint64_t plan_layout(const aw4_config* c, aw4_model* m, uint8_t* base) {
     }
     p.off = (p.off + 255) & ~uint64_t(255);
     const uint64_t state_bytes = p.off - state_off;
+    const int nbatch = c->max_batch > 1 ? c->max_batch : 1;
+    p.off += (uint64_t)(nbatch - 1) * state_bytes;   // the other sequences' copies
     Ctl* ctl = p.take<Ctl>(sizeof(Ctl));
     float* x = p.take<float>(H * 4);
     float* proj = p.take<float>((uint64_t)max_in * 4);
@@ -305,7 +314,7 @@ uint64_t plan_layout(const aw4_config* c, aw4_model* m, uint8_t* base) {
         pi = p.take<int32_t>((uint64_t)nhb * 4);
     }
     int32_t* ring = p.take<int32_t>((uint64_t)kRingCap * 4);
-    const int MV = c->max_verify;
+    const int MV = std::max(c->max_verify, c->max_batch);
     float* vx = p.take<float>((uint64_t)MV * H * 4);
     std::vector<float*> vproj_g;
     float* vproj_a = nullptr;
@@ -426,6 +435,7 @@ uint64_t plan_layout(const aw4_config* c, aw4_model* m, uint8_t* base) {
         m->nsplit = nsplit;
         m->state_off = state_off;
         m->state_bytes = state_bytes;
+        m->max_batch = nbatch;
     }
     return p.off;
 }
@@ -465,6 +475,7 @@ const char* check_config(const aw4_config* c) {
     if (c->draft_vocab > 0 && c->hidden > 8192) return "hidden must be <= 8192 with a draft head";
     if (c->max_ctx < 1) return "max_ctx must be >= 1";
     if (c->max_verify < 1 || c->max_verify > 4) return "max_verify must be in [1, 4]";
+    if (c->max_batch < 0 || c->max_batch > 4) return "max_batch must be in [0, 4]";
     if (!(c->rms_eps > 0.f) || !std::isfinite(c->rms_eps)) return "rms_eps must be positive";
     return nullptr;
 }
@@ -1003,6 +1014,25 @@ int check_model(aw4_model* m) {
     return AW4_OK;
 }
 
+// move every recurrent-state and cache pointer by `delta` sequences
+void shift_state(aw4_model* m, int delta) {
+    const int64_t d = (int64_t)delta * (int64_t)m->state_bytes;
+    auto mv = [d](auto*& ptr) {
+        if (ptr) ptr = (std::remove_reference_t<decltype(*ptr)>*)((char*)ptr + d);
+    };
+    for (LayerBufs& b : m->L) {
+        mv(b.S);
+        mv(b.kc);
+        mv(b.ks);
+        mv(b.vc);
+        mv(b.vs);
+    }
+    mv(m->D.kc);
+    mv(m->D.ks);
+    mv(m->D.vc);
+    mv(m->D.vs);
+}
+
 // the attention layer whose cache a state call names (n_layers: the draft head's)
 LayerBufs* kv_layer(aw4_model* m, int layer) {
     if (!m) return nullptr;
@@ -1230,7 +1260,7 @@ int aw4_load_weights(aw4_model* m, const void* blob, uint64_t bytes) {
     uint32_t ver;
     memcpy(&ver, p, 4);
     p += 4;
-    if (ver != 2) return fail(m, AW4_E_FORMAT, "unsupported blob version");
+    if (ver != 3) return fail(m, AW4_E_FORMAT, "unsupported blob version");
     aw4_config bc;
     memcpy(&bc, p, sizeof(bc));
     p += sizeof(bc);
@@ -1287,12 +1317,13 @@ int aw4_load_weights(aw4_model* m, const void* blob, uint64_t bytes) {
 
 int aw4_reset(aw4_model* m) {
     if (check_model(m)) return AW4_E_INVAL;
-    HIPCHK(m, launch_fill_zero(m->arena + m->state_off, m->state_bytes, m->stream));
+    HIPCHK(m, launch_fill_zero(m->arena + m->state_off, m->state_bytes * (uint64_t)m->max_batch, m->stream));
     HIPCHK(m, launch_set_ctl(m->ctl, 0, 0, 0, m->stream));
     HIPCHK(m, launch_set_dpos(m->ctl, 0, m->stream));
     m->host_pos = 0;
     m->host_dpos = 0;
     m->pend_src = 0;
+    for (int b = 0; b < 4; ++b) m->seq_pos[b] = m->seq_dpos[b] = 0;
     return AW4_OK;
 }
 
@@ -1314,6 +1345,106 @@ int aw4_set_pos(aw4_model* m, int32_t pos) {
     if (pos < 0 || pos > m->cfg.max_ctx) return fail(m, AW4_E_CTX_FULL, "position outside [0, max_ctx]");
     HIPCHK(m, launch_set_ctl(m->ctl, pos, -1, -1, m->stream));
     m->host_pos = pos;
+    m->pend_src = 0;
+    return AW4_OK;
+}
+
+int aw4_select_sequence(aw4_model* m, int32_t s) {
+    if (check_model(m)) return AW4_E_INVAL;
+    if (s < 0 || s >= m->max_batch) return fail(m, AW4_E_INVAL, "sequence outside [0, max_batch)");
+    if (s == m->seq) return AW4_OK;
+    m->seq_pos[m->seq] = m->host_pos;
+    m->seq_dpos[m->seq] = m->host_dpos;
+    shift_state(m, s - m->seq);
+    m->seq = s;
+    m->host_pos = m->seq_pos[s];
+    m->host_dpos = m->seq_dpos[s];
+    HIPCHK(m, launch_set_ctl(m->ctl, m->host_pos, -1, -1, m->stream));
+    HIPCHK(m, launch_set_dpos(m->ctl, m->host_dpos, m->stream));
+    m->pend_src = 0;
+    drop_graphs(m);   // the captured step holds the previous sequence's state pointers
+    return AW4_OK;
+}
+
+int aw4_decode_batch(aw4_model* m, const int32_t* host_tokens, int32_t B, int32_t* host_argmax) {
+    if (check_model(m) || !host_tokens || !host_argmax) return AW4_E_INVAL;
+    const aw4_config* c = &m->cfg;
+    if (c->vocab <= 0) return fail(m, AW4_E_STATE, "decode_batch needs a vocabulary");
+    if (B < 1 || B > m->max_batch) return fail(m, AW4_E_INVAL, "batch must be in [1, max_batch]");
+    m->seq_pos[m->seq] = m->host_pos;
+    int32_t tok[4] = {0, 0, 0, 0}, pos[4] = {0, 0, 0, 0};
+    for (int b = 0; b < B; ++b) {
+        if (host_tokens[b] < 0 || host_tokens[b] >= c->vocab) return fail(m, AW4_E_TOKEN, "token out of range");
+        if (m->seq_pos[b] + 1 > c->max_ctx) return fail(m, AW4_E_CTX_FULL, "context full");
+        tok[b] = host_tokens[b];
+        pos[b] = m->seq_pos[b];
+    }
+    hipStream_t s = m->stream;
+    const int H = c->hidden;
+    const int64_t sb = (int64_t)m->state_bytes;
+    // sequence 0's state pointers (the layers hold the selected sequence's);
+    // the kernels add b * state_bytes for sequence b
+    const int64_t back = -(int64_t)m->seq * sb;
+    auto seq0 = [back](auto* ptr) { return (decltype(ptr))((char*)ptr + back); };
+    int rc = AW4_OK;
+    {
+        HIPCHK(m, launch_set_batch(m->ctl, tok, pos, s));
+        HIPCHK(m, launch_embed_tokens(m->lm_codes, m->lm_scales, H, m->ctl->btok, B, m->vx, s));
+        int gi_layer = 0;
+        for (int l = 0; l < c->n_layers && !rc; ++l) {
+            LayerBufs& b = m->L[l];
+            float* proj = b.type == 'G' ? m->vproj_g[gi_layer] : m->vproj_a;
+            GemvMultiArgs gi{};
+            gi.codes = b.w_in; gi.scales = b.s_in; gi.rows = (int)b.in_rows; gi.K = H; gi.M = B;
+            gi.x = m->vx; gi.sx = H; gi.nw = b.norm_mix; gi.eps = c->rms_eps; gi.y = proj; gi.sy = b.in_rows;
+            HIPCHK(m, launch_gemv_multi(PRO_NORM, EPI_STORE, gi, s));
+            if (b.type == 'G') {
+                const int64_t nvd = (int64_t)c->gdn_v_heads * c->gdn_head_dim;
+                GdnArgs ga{proj, b.a_bias, seq0(b.S), m->vo, c->gdn_qk_heads, c->gdn_v_heads, c->gdn_head_dim,
+                           c->rms_eps, b.in_rows, sb / 4, nvd};
+                HIPCHK(m, launch_gdn_batch(ga, B, s));
+                GemvMultiArgs go{};
+                go.codes = b.w_out; go.scales = b.s_out; go.rows = H; go.K = (int)b.out_cols; go.M = B;
+                go.x = m->vo; go.sx = nvd; go.nw = b.norm_gated;
+                go.z = proj + 2LL * c->gdn_qk_heads * c->gdn_head_dim + nvd;
+                go.sz = b.in_rows; go.gated_d = c->gdn_head_dim; go.eps = c->rms_eps; go.y = m->vx; go.sy = H;
+                HIPCHK(m, launch_gemv_multi(PRO_GATED, EPI_RESID, go, s));
+                ++gi_layer;
+            } else {
+                const int64_t od = (int64_t)c->attn_q_heads * c->attn_head_dim;
+                AttnArgs aa{};
+                aa.nt = B; aa.append = 1; aa.batch = 1; aa.seq_bytes = sb;
+                aa.sproj = b.in_rows; aa.proj = proj;
+                aa.kc = seq0(b.kc); aa.ks = seq0(b.ks); aa.vc = seq0(b.vc); aa.vs = seq0(b.vs);
+                aa.signs = m->signs; aa.pos = m->ctl->bpos; aa.part = m->part; aa.prow = kSweepRows * c->attn_q_heads;
+                aa.max_ctx = c->max_ctx; aa.nq = c->attn_q_heads; aa.nkv = c->attn_kv_heads;
+                aa.d = c->attn_head_dim; aa.nsplit = m->nsplit;
+                HIPCHK(m, launch_attn(aa, s));
+                CombineArgs ca{0, B, b.in_rows, m->part, proj, m->signs, m->ctl->bpos, m->va, aa.prow, c->attn_q_heads,
+                               c->attn_kv_heads, c->attn_head_dim, m->nsplit, 1};
+                HIPCHK(m, launch_combine(ca, s));
+                GemvMultiArgs go{};
+                go.codes = b.w_out; go.scales = b.s_out; go.rows = H; go.K = (int)b.out_cols; go.M = B;
+                go.h = m->va; go.sh = od; go.y = m->vx; go.sy = H;
+                HIPCHK(m, launch_gemv_multi(PRO_LOADH, EPI_RESID, go, s));
+            }
+            rc = enqueue_ffn_multi(m, b, B, m->vx);
+        }
+        if (rc) return rc;
+        HeadMultiArgs ha{m->lm_codes, m->lm_scales, c->vocab, c->hidden, B, m->vx, m->norm_final, c->rms_eps,
+                         m->vlogits, m->vpv, m->vpi};
+        HIPCHK(m, launch_head_multi(ha, s));
+        HIPCHK(m, launch_head_argmax_multi(m->vpv, m->vpi, m->nhead_blocks, B, m->ctl, s));
+    }
+    int32_t am[4];
+    HIPCHK(m, hipMemcpyAsync(am, &m->ctl->vargmax[0], 4 * sizeof(int32_t), hipMemcpyDeviceToHost, s));
+    HIPCHK(m, hipStreamSynchronize(s));
+    for (int b = 0; b < B; ++b) {
+        host_argmax[b] = am[b];
+        m->seq_pos[b] += 1;
+    }
+    m->host_pos = m->seq_pos[m->seq];
+    HIPCHK(m, launch_set_ctl(m->ctl, m->host_pos, -1, -1, s));
     m->pend_src = 0;
     return AW4_OK;
 }

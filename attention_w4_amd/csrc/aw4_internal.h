@@ -31,7 +31,10 @@ struct Ctl {
     float dmax;         // largest mapped score of the current draft step
     float dz;           // its softmax normaliser
     int32_t darg;       // index into the map of the current draft
-    int32_t pad[16];
+    // batch decode: one token per sequence b, each at its own position
+    int32_t btok[4];
+    int32_t bpos[4];
+    int32_t pad[8];
 };
 static_assert(sizeof(Ctl) == 256, "control block size");
 
@@ -103,6 +106,9 @@ struct GdnArgs {
     float* o;                 // [nv*d]
     int32_t nqk, nv, d;
     float eps;
+    // grid z > 1 (batch decode): sequence b's token, state and readout at
+    // proj + b sproj, S + b sstride, o + b so
+    int64_t sproj, sstride, so;
 };
 
 struct AttnArgs {
@@ -118,6 +124,8 @@ struct AttnArgs {
     const float* signs;       // [d] +-1
     const int32_t* pos;       // device: the cache's committed length (ctl->pos, or ctl->dpos for the draft head)
     float* part;              // [prow][nsplit][d] acc, then [prow][nsplit][2] (m, l); row m nq + head
+    int32_t batch;            // 1: grid z is a sequence: its token at pos[z], its cache at + z seq_bytes
+    int64_t seq_bytes;
     int32_t prow;             // rows of part: nq times the most tokens per sweep
     int32_t max_ctx, nq, nkv, d, nsplit;
 };
@@ -133,6 +141,7 @@ struct CombineArgs {
     _Float16* out;            // token m, head h at out + (m nq + h) d
     int32_t prow;
     int32_t nq, nkv, d, nsplit;
+    int32_t batch;            // 1: token m is sequence m's single token at pos[m]
 };
 
 struct GdnMultiArgs {
@@ -242,11 +251,17 @@ int draft_head_blocks(int V);   // blocks of the mapped head (launch_head with a
 hipError_t launch_head_final(const float* pv, const int32_t* pi, int n, Ctl* ctl, int32_t* ring, int ring_cap,
                              hipStream_t s);
 hipError_t launch_gdn(const GdnArgs& a, hipStream_t s);
+hipError_t launch_gdn_batch(const GdnArgs& a, int B, hipStream_t s);
 hipError_t launch_gdn_multi(const GdnMultiArgs& a, hipStream_t s);
 int accept_blocks(int V);
 hipError_t launch_accept(const AcceptArgs& a, const float* head_pv, const int32_t* head_pi, int head_nb,
                          hipStream_t s);
 hipError_t launch_commit_pos(Ctl* ctl, hipStream_t s);
+hipError_t launch_embed_tokens(const int8_t* codes, const uint16_t* scales, int H, const int32_t* tok, int M, float* x,
+                               hipStream_t s);
+hipError_t launch_set_batch(Ctl* ctl, const int32_t* tok, const int32_t* pos, hipStream_t s);
+// per-vector best value and index from the head's block partials into ctl->vmax / vargmax
+hipError_t launch_head_argmax_multi(const float* pv, const int32_t* pi, int nb, int M, Ctl* ctl, hipStream_t s);
 hipError_t launch_embed_multi(const int8_t* codes, const uint16_t* scales, int H, const Ctl* ctl, int M, float* x,
                               hipStream_t s);
 hipError_t launch_set_verify(Ctl* ctl, const int32_t* tok, const float* u, hipStream_t s);

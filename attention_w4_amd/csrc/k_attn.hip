@@ -190,7 +190,14 @@ __global__ __launch_bounds__(512, 1) void k_attn(AttnArgs a) {
     const int tb0 = blockIdx.z * NT;          // the block's first token in the run
     const int lane = tid & 63, w = tid >> 6;
     const int c = lane & 15, q = lane >> 4;
-    const int pos = *a.pos + a.pos_offset + tb0;   // the block's first token's position
+    // the block's first token's position; in a batch each block is a sequence
+    // with its own cache
+    const int pos = a.batch ? a.pos[blockIdx.z] : *a.pos + a.pos_offset + tb0;
+    const int64_t zoff = a.batch ? (int64_t)blockIdx.z * a.seq_bytes : 0;
+    int8_t* const kc = (int8_t*)((char*)a.kc + zoff);
+    uint16_t* const ks = (uint16_t*)((char*)a.ks + zoff);
+    uint32_t* const vc = (uint32_t*)((char*)a.vc + zoff);
+    uint16_t* const vs = (uint16_t*)((char*)a.vs + zoff);
     const int nt = NT == 1 ? 1 : min(NT, a.nt - tb0);
     const int npos = pos + nt;
     int pps, used;
@@ -215,11 +222,11 @@ __global__ __launch_bounds__(512, 1) void k_attn(AttnArgs a) {
     const int ssel = lane >> 5;
     const int sidx = (lane & 31) * HPL;
     const int spp = sidx / NG, sg0 = sidx % NG;
-    const uint16_t* sbase = ssel ? a.vs : a.ks;
+    const uint16_t* sbase = ssel ? vs : ks;
 
     // per-head bases; offsets inside a head fit 32 bits (max_ctx * D < 2^31)
-    const int8_t* khead = a.kc + hbase * D;
-    const uint32_t* vhead = a.vc + hbase * VW;
+    const int8_t* khead = kc + hbase * D;
+    const uint32_t* vhead = vc + hbase * VW;
     const uint16_t* shead = sbase + hbase * NG;
     auto load = [&](int tile0, Raw& r) {
         {
@@ -262,8 +269,8 @@ __global__ __launch_bounds__(512, 1) void k_attn(AttnArgs a) {
     // the new position, so no other wave waits; the writer's own loads of that
     // tile come after its stores in program order.
     auto encode = [&]() {
-        const float* kp = a.proj + 2LL * a.nq * D + (int64_t)j * D;
-        encode_append<D>(kp, kp + (int64_t)a.nkv * D, a.signs, a.kc, a.ks, a.vc, a.vs, hbase + pos, vq, lane);
+        const float* kp = a.proj + (int64_t)tb0 * a.sproj + 2LL * a.nq * D + (int64_t)j * D;
+        encode_append<D>(kp, kp + (int64_t)a.nkv * D, a.signs, kc, ks, vc, vs, hbase + pos, vq, lane);
     };
 
     const int ntiles = (t1 - t0 + kTile - 1) / kTile;
@@ -522,9 +529,9 @@ __global__ __launch_bounds__(1024) void k_combine(CombineArgs a) {
     // block i: token i / nq, head i % nq (its slot in the partial rows)
     const int i = blockIdx.x, tid = threadIdx.x;
     const int tm = i / a.nq, hq = i % a.nq;
-    const int pos = *a.pos + a.pos_offset;
     int pps, used;
-    split_range(pos + a.nt, a.nsplit, pps, used);
+    if (a.batch) split_range(a.pos[tm] + 1, a.nsplit, pps, used);
+    else split_range(*a.pos + a.pos_offset + a.nt, a.nsplit, pps, used);
     const float* base = a.part + (int64_t)i * a.nsplit * D;
     const float* mlp = a.part + (int64_t)a.prow * a.nsplit * D + 2LL * i * a.nsplit;
     // every load is issued before any is used: (m, l) of one split per
@@ -646,9 +653,9 @@ hipError_t launch_append(const AttnArgs& a, hipStream_t s) {
 // a.nt tokens: one sweep block per attn_tokens_per_sweep tokens (grid z)
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
     const int G = a.nq / a.nkv;
-    if (a.nsplit < 1 || a.nsplit > 256 || a.nt < 1 || (a.nt > 1 && a.append) || a.nq * a.nt > a.prow)
+    if (a.nsplit < 1 || a.nsplit > 256 || a.nt < 1 || (a.nt > 1 && a.append && !a.batch) || a.nq * a.nt > a.prow)
         return hipErrorInvalidValue;
-    const int nn = a.nt == 1 ? 1 : attn_tokens_per_sweep(a.d, a.nq, a.nkv);
+    const int nn = a.nt == 1 || a.batch ? 1 : attn_tokens_per_sweep(a.d, a.nq, a.nkv);
     const dim3 grid(a.nsplit, a.nkv, (a.nt + nn - 1) / nn), block(64 * kWaves);
 #define AW4_ATTN_CASE(DD, GG, NN)                                               \
     if (a.d == DD && G == GG && nn == NN) {                                     \

@@ -29,6 +29,10 @@ __global__ __launch_bounds__(256) void k_gdn(GdnArgs a) {
     const int j = h / (a.nv / a.nqk);
     const int row0 = blockIdx.x * ROWS;
     const int tid = threadIdx.x;
+    // batch: sequence blockIdx.z's token, state and readout
+    a.proj += blockIdx.z * a.sproj;
+    a.S += blockIdx.z * a.sstride;
+    a.o += blockIdx.z * a.so;
 
     const float* q = a.proj + (int64_t)j * D;
     const float* k = a.proj + (int64_t)a.nqk * D + (int64_t)j * D;
@@ -91,11 +95,14 @@ __global__ __launch_bounds__(256) void k_gdn(GdnArgs a) {
 
 }  // namespace
 
-hipError_t launch_gdn(const GdnArgs& a, hipStream_t s) {
+hipError_t launch_gdn(const GdnArgs& a, hipStream_t s) { return launch_gdn_batch(a, 1, s); }
+
+hipError_t launch_gdn_batch(const GdnArgs& a, int B, hipStream_t s) {
+    if (B < 1) return hipErrorInvalidValue;
     if (a.d == 128) {
-        hipLaunchKernelGGL(k_gdn<128>, dim3(128 / 16, a.nv), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(k_gdn<128>, dim3(128 / 16, a.nv, B), dim3(256), 0, s, a);
     } else if (a.d == 64) {
-        hipLaunchKernelGGL(k_gdn<64>, dim3(64 / 32, a.nv), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(k_gdn<64>, dim3(64 / 32, a.nv, B), dim3(256), 0, s, a);
     } else {
         return hipErrorInvalidValue;
     }

@@ -33,6 +33,27 @@ __global__ void k_embed_multi(const int8_t* __restrict__ codes, const uint16_t* 
     }
 }
 
+// token rows of a device id array, one workgroup per token
+__global__ void k_embed_tokens(const int8_t* __restrict__ codes, const uint16_t* __restrict__ scales, int H,
+                               const int32_t* tok, float* __restrict__ x) {
+    const int m = blockIdx.x;
+    const int64_t id = tok[m];
+    for (int k = threadIdx.x; k < H; k += blockDim.x)
+        x[(int64_t)m * H + k] = (float)codes[id * H + k] * (float)__builtin_bit_cast(_Float16, scales[id * (H / 32) + k / 32]);
+}
+
+struct BatchIn {
+    int32_t tok[4];
+    int32_t pos[4];
+};
+
+__global__ void k_set_batch(Ctl* ctl, BatchIn in) {
+    for (int i = 0; i < 4; ++i) {
+        ctl->btok[i] = in.tok[i];
+        ctl->bpos[i] = in.pos[i];
+    }
+}
+
 struct VerifyIn {
     int32_t tok[4];
     float u[4];
@@ -130,6 +151,22 @@ hipError_t launch_embed(const int8_t* codes, const uint16_t* scales, int H, cons
 hipError_t launch_embed_multi(const int8_t* codes, const uint16_t* scales, int H, const Ctl* ctl, int M, float* x,
                               hipStream_t s) {
     hipLaunchKernelGGL(k_embed_multi, dim3(grid_for(H)), dim3(256), 0, s, codes, scales, H, ctl, M, x);
+    return hipGetLastError();
+}
+
+hipError_t launch_embed_tokens(const int8_t* codes, const uint16_t* scales, int H, const int32_t* tok, int M, float* x,
+                               hipStream_t s) {
+    hipLaunchKernelGGL(k_embed_tokens, dim3(M), dim3(256), 0, s, codes, scales, H, tok, x);
+    return hipGetLastError();
+}
+
+hipError_t launch_set_batch(Ctl* ctl, const int32_t* tok, const int32_t* pos, hipStream_t s) {
+    BatchIn in;
+    for (int i = 0; i < 4; ++i) {
+        in.tok[i] = tok[i];
+        in.pos[i] = pos[i];
+    }
+    hipLaunchKernelGGL(k_set_batch, dim3(1), dim3(1), 0, s, ctl, in);
     return hipGetLastError();
 }
 

@@ -280,6 +280,12 @@ hipError_t launch_accept(const AcceptArgs& a, const float* head_pv, const int32_
     return hipGetLastError();
 }
 
+hipError_t launch_head_argmax_multi(const float* pv, const int32_t* pi, int nb, int M, Ctl* ctl, hipStream_t s) {
+    if (M < 1 || M > 4) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_acc_max, dim3(M), dim3(256), 0, s, pv, pi, nb, ctl);
+    return hipGetLastError();
+}
+
 hipError_t launch_commit_pos(Ctl* ctl, hipStream_t s) {
     hipLaunchKernelGGL(k_commit_pos, dim3(1), dim3(1), 0, s, ctl);
     return hipGetLastError();

@@ -61,7 +61,7 @@ extern "C" {
  * max_ctx >= 1; max_verify in [1, 4]; rms_eps > 0; draft_vocab in [0, vocab]
  * (0: no draft head; otherwise the attention fields must describe a valid
  * attention layer even when the pattern holds none, since the draft head's
- * block has that shape, and hidden <= 8192). */
+ * block has that shape, and hidden <= 8192); max_batch in [0, 4]. */
 typedef struct aw4_config {
     int32_t hidden;
     int32_t ffn;
@@ -79,6 +79,7 @@ typedef struct aw4_config {
     float rms_eps;
     char layer_pattern[128];
     int32_t draft_vocab;        /* ids in the draft head's vocabulary map */
+    int32_t max_batch;          /* sequences with their own state (0 or 1: one; at most 4) */
 } aw4_config;
 
 typedef struct aw4_model aw4_model;
@@ -181,7 +182,8 @@ int aw4_set_draft_map(aw4_model* model, const int32_t* host_ids, int32_t n);
  * aw4_config it was made for, uint32 tensor count, then per tensor
  * {int32 layer, int32 kind, int64 rows, int64 cols, uint64 bytes} followed by
  * the payload (logical codes then scales, n fp32 values for vectors, or n int32
- * ids for DRAFT_MAP).  The version is 2 (the config carries draft_vocab).
+ * ids for DRAFT_MAP).  The version is 3 (the config carries draft_vocab and
+ * max_batch).
  * Errors: AW4_E_FORMAT on magic, version, size or config mismatch. */
 int aw4_load_weights(aw4_model* model, const void* host_blob, uint64_t bytes);
 
@@ -303,6 +305,23 @@ int aw4_get_pos(aw4_model* model, int32_t* pos);
 
 /* Set the position without touching the caches (state import). */
 int aw4_set_pos(aw4_model* model, int32_t pos);
+
+/* Sequences (max_batch > 1): the model holds max_batch independent sequences,
+ * each with its own recurrent states, caches (the draft head's too) and
+ * position.  Every single-sequence call (prefill, decode, verify, draft, the
+ * state calls, set_pos) works on the selected one (0 at creation); selecting
+ * another keeps each sequence's state.  AW4_E_INVAL outside [0, max_batch). */
+int aw4_select_sequence(aw4_model* model, int32_t s);
+
+/* One decode step for each of sequences 0 .. B-1 (1 <= B <= max_batch) with
+ * one sweep over the weights (page 3 "Qwen3.8-27B 實測": several users served
+ * by one card, four the sweet spot of a 32 GB card): token b runs at sequence
+ * b's position through every layer against that sequence's states and cache,
+ * then the output head; host_argmax receives the B greedy tokens (lowest
+ * index on ties) and each sequence's position advances by one.  The draft
+ * head is not fed.  Synchronous.  Errors: AW4_E_INVAL, AW4_E_TOKEN,
+ * AW4_E_CTX_FULL, AW4_E_STATE (vocab 0). */
+int aw4_decode_batch(aw4_model* model, const int32_t* host_tokens, int32_t B, int32_t* host_argmax);
 
 /* Committed entries of the draft head's cache; set it after importing that
  * cache (layer n_layers of the state calls below).  AW4_E_STATE without a draft

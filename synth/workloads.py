@@ -29,6 +29,7 @@ class Shape:
     max_ctx: int = 4096
     max_verify: int = 4
     draft_vocab: int = 0    # ids in the draft head's vocabulary map; 0: no draft head
+    max_batch: int = 1      # sequences with their own state (batch decode)
 
     @property
     def n_layers(self):
