@@ -145,6 +145,7 @@ struct aw4_model {
     bool use_graph = true;
     hipGraphExec_t g_head = nullptr;
     hipGraphExec_t g_nohead = nullptr;
+    hipGraphExec_t g_batch[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};   // per batch size
     std::string err;
 };
 
@@ -979,6 +980,67 @@ int enqueue_prefill_chunked(aw4_model* m, const int32_t* tokens, int n, bool wan
     return AW4_OK;
 }
 
+// One batch step of sequences 0 .. B-1 (tokens and positions already in
+// ctl->btok / bpos): the M = B projections, per-sequence GDN steps and
+// attention sweeps (grid z), the M = B head and the per-sequence argmax.
+int enqueue_batch_step(aw4_model* m, int B) {
+    const aw4_config* c = &m->cfg;
+    hipStream_t s = m->stream;
+    const int H = c->hidden;
+    const int64_t sb = (int64_t)m->state_bytes;
+    // sequence 0's state pointers (the layers hold the selected sequence's);
+    // the kernels add b * state_bytes for sequence b
+    const int64_t back = -(int64_t)m->seq * sb;
+    auto seq0 = [back](auto* ptr) { return (decltype(ptr))((char*)ptr + back); };
+    HIPCHK(m, launch_embed_tokens(m->lm_codes, m->lm_scales, H, m->ctl->btok, B, m->vx, s));
+    int gi_layer = 0;
+    for (int l = 0; l < c->n_layers; ++l) {
+        LayerBufs& b = m->L[l];
+        float* proj = b.type == 'G' ? m->vproj_g[gi_layer] : m->vproj_a;
+        GemvMultiArgs gi{};
+        gi.codes = b.w_in; gi.scales = b.s_in; gi.rows = (int)b.in_rows; gi.K = H; gi.M = B;
+        gi.x = m->vx; gi.sx = H; gi.nw = b.norm_mix; gi.eps = c->rms_eps; gi.y = proj; gi.sy = b.in_rows;
+        HIPCHK(m, launch_gemv_multi(PRO_NORM, EPI_STORE, gi, s));
+        if (b.type == 'G') {
+            const int64_t nvd = (int64_t)c->gdn_v_heads * c->gdn_head_dim;
+            GdnArgs ga{proj, b.a_bias, seq0(b.S), m->vo, c->gdn_qk_heads, c->gdn_v_heads, c->gdn_head_dim,
+                       c->rms_eps, b.in_rows, sb / 4, nvd};
+            HIPCHK(m, launch_gdn_batch(ga, B, s));
+            GemvMultiArgs go{};
+            go.codes = b.w_out; go.scales = b.s_out; go.rows = H; go.K = (int)b.out_cols; go.M = B;
+            go.x = m->vo; go.sx = nvd; go.nw = b.norm_gated;
+            go.z = proj + 2LL * c->gdn_qk_heads * c->gdn_head_dim + nvd;
+            go.sz = b.in_rows; go.gated_d = c->gdn_head_dim; go.eps = c->rms_eps; go.y = m->vx; go.sy = H;
+            HIPCHK(m, launch_gemv_multi(PRO_GATED, EPI_RESID, go, s));
+            ++gi_layer;
+        } else {
+            const int64_t od = (int64_t)c->attn_q_heads * c->attn_head_dim;
+            AttnArgs aa{};
+            aa.nt = B; aa.append = 1; aa.batch = 1; aa.seq_bytes = sb;
+            aa.sproj = b.in_rows; aa.proj = proj;
+            aa.kc = seq0(b.kc); aa.ks = seq0(b.ks); aa.vc = seq0(b.vc); aa.vs = seq0(b.vs);
+            aa.signs = m->signs; aa.pos = m->ctl->bpos; aa.part = m->part; aa.prow = kSweepRows * c->attn_q_heads;
+            aa.max_ctx = c->max_ctx; aa.nq = c->attn_q_heads; aa.nkv = c->attn_kv_heads;
+            aa.d = c->attn_head_dim; aa.nsplit = m->nsplit;
+            HIPCHK(m, launch_attn(aa, s));
+            CombineArgs ca{0, B, b.in_rows, m->part, proj, m->signs, m->ctl->bpos, m->va, aa.prow, c->attn_q_heads,
+                           c->attn_kv_heads, c->attn_head_dim, m->nsplit, 1};
+            HIPCHK(m, launch_combine(ca, s));
+            GemvMultiArgs go{};
+            go.codes = b.w_out; go.scales = b.s_out; go.rows = H; go.K = (int)b.out_cols; go.M = B;
+            go.h = m->va; go.sh = od; go.y = m->vx; go.sy = H;
+            HIPCHK(m, launch_gemv_multi(PRO_LOADH, EPI_RESID, go, s));
+        }
+        int rc = enqueue_ffn_multi(m, b, B, m->vx);
+        if (rc) return rc;
+    }
+    HeadMultiArgs ha{m->lm_codes, m->lm_scales, c->vocab, c->hidden, B, m->vx, m->norm_final, c->rms_eps,
+                     m->vlogits, m->vpv, m->vpi};
+    HIPCHK(m, launch_head_multi(ha, s));
+    HIPCHK(m, launch_head_argmax_multi(m->vpv, m->vpi, m->nhead_blocks, B, m->ctl, s));
+    return AW4_OK;
+}
+
 int run_step(aw4_model* m, bool head) {
     if (!m->use_graph) return enqueue_step(m, head);
     hipGraphExec_t* ge = head ? &m->g_head : &m->g_nohead;
@@ -1007,6 +1069,10 @@ void drop_graphs(aw4_model* m) {
     if (m->g_head) (void)hipGraphExecDestroy(m->g_head);
     if (m->g_nohead) (void)hipGraphExecDestroy(m->g_nohead);
     m->g_head = m->g_nohead = nullptr;
+    for (hipGraphExec_t& g : m->g_batch) {
+        if (g) (void)hipGraphExecDestroy(g);
+        g = nullptr;
+    }
 }
 
 int check_model(aw4_model* m) {
@@ -1380,61 +1446,32 @@ int aw4_decode_batch(aw4_model* m, const int32_t* host_tokens, int32_t B, int32_
         pos[b] = m->seq_pos[b];
     }
     hipStream_t s = m->stream;
-    const int H = c->hidden;
-    const int64_t sb = (int64_t)m->state_bytes;
-    // sequence 0's state pointers (the layers hold the selected sequence's);
-    // the kernels add b * state_bytes for sequence b
-    const int64_t back = -(int64_t)m->seq * sb;
-    auto seq0 = [back](auto* ptr) { return (decltype(ptr))((char*)ptr + back); };
-    int rc = AW4_OK;
-    {
-        HIPCHK(m, launch_set_batch(m->ctl, tok, pos, s));
-        HIPCHK(m, launch_embed_tokens(m->lm_codes, m->lm_scales, H, m->ctl->btok, B, m->vx, s));
-        int gi_layer = 0;
-        for (int l = 0; l < c->n_layers && !rc; ++l) {
-            LayerBufs& b = m->L[l];
-            float* proj = b.type == 'G' ? m->vproj_g[gi_layer] : m->vproj_a;
-            GemvMultiArgs gi{};
-            gi.codes = b.w_in; gi.scales = b.s_in; gi.rows = (int)b.in_rows; gi.K = H; gi.M = B;
-            gi.x = m->vx; gi.sx = H; gi.nw = b.norm_mix; gi.eps = c->rms_eps; gi.y = proj; gi.sy = b.in_rows;
-            HIPCHK(m, launch_gemv_multi(PRO_NORM, EPI_STORE, gi, s));
-            if (b.type == 'G') {
-                const int64_t nvd = (int64_t)c->gdn_v_heads * c->gdn_head_dim;
-                GdnArgs ga{proj, b.a_bias, seq0(b.S), m->vo, c->gdn_qk_heads, c->gdn_v_heads, c->gdn_head_dim,
-                           c->rms_eps, b.in_rows, sb / 4, nvd};
-                HIPCHK(m, launch_gdn_batch(ga, B, s));
-                GemvMultiArgs go{};
-                go.codes = b.w_out; go.scales = b.s_out; go.rows = H; go.K = (int)b.out_cols; go.M = B;
-                go.x = m->vo; go.sx = nvd; go.nw = b.norm_gated;
-                go.z = proj + 2LL * c->gdn_qk_heads * c->gdn_head_dim + nvd;
-                go.sz = b.in_rows; go.gated_d = c->gdn_head_dim; go.eps = c->rms_eps; go.y = m->vx; go.sy = H;
-                HIPCHK(m, launch_gemv_multi(PRO_GATED, EPI_RESID, go, s));
-                ++gi_layer;
-            } else {
-                const int64_t od = (int64_t)c->attn_q_heads * c->attn_head_dim;
-                AttnArgs aa{};
-                aa.nt = B; aa.append = 1; aa.batch = 1; aa.seq_bytes = sb;
-                aa.sproj = b.in_rows; aa.proj = proj;
-                aa.kc = seq0(b.kc); aa.ks = seq0(b.ks); aa.vc = seq0(b.vc); aa.vs = seq0(b.vs);
-                aa.signs = m->signs; aa.pos = m->ctl->bpos; aa.part = m->part; aa.prow = kSweepRows * c->attn_q_heads;
-                aa.max_ctx = c->max_ctx; aa.nq = c->attn_q_heads; aa.nkv = c->attn_kv_heads;
-                aa.d = c->attn_head_dim; aa.nsplit = m->nsplit;
-                HIPCHK(m, launch_attn(aa, s));
-                CombineArgs ca{0, B, b.in_rows, m->part, proj, m->signs, m->ctl->bpos, m->va, aa.prow, c->attn_q_heads,
-                               c->attn_kv_heads, c->attn_head_dim, m->nsplit, 1};
-                HIPCHK(m, launch_combine(ca, s));
-                GemvMultiArgs go{};
-                go.codes = b.w_out; go.scales = b.s_out; go.rows = H; go.K = (int)b.out_cols; go.M = B;
-                go.h = m->va; go.sh = od; go.y = m->vx; go.sy = H;
-                HIPCHK(m, launch_gemv_multi(PRO_LOADH, EPI_RESID, go, s));
+    // tokens and positions go to the control block; the step itself reads
+    // them there, so one captured graph per batch size serves every call
+    HIPCHK(m, launch_set_batch(m->ctl, tok, pos, s));
+    if (m->use_graph) {
+        hipGraphExec_t* ge = &m->g_batch[B];
+        if (!*ge) {
+            hipGraph_t g = nullptr;
+            HIPCHK(m, hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal));
+            int rc = enqueue_batch_step(m, B);
+            hipError_t e = hipStreamEndCapture(s, &g);
+            if (rc) {
+                if (g) (void)hipGraphDestroy(g);
+                return rc;
             }
-            rc = enqueue_ffn_multi(m, b, B, m->vx);
+            if (e != hipSuccess) return fail(m, AW4_E_HIP, std::string("hipStreamEndCapture: ") + hipGetErrorString(e));
+            e = hipGraphInstantiate(ge, g, nullptr, nullptr, 0);
+            (void)hipGraphDestroy(g);
+            if (e != hipSuccess) {
+                *ge = nullptr;
+                return fail(m, AW4_E_HIP, std::string("hipGraphInstantiate: ") + hipGetErrorString(e));
+            }
         }
+        HIPCHK(m, hipGraphLaunch(*ge, s));
+    } else {
+        int rc = enqueue_batch_step(m, B);
         if (rc) return rc;
-        HeadMultiArgs ha{m->lm_codes, m->lm_scales, c->vocab, c->hidden, B, m->vx, m->norm_final, c->rms_eps,
-                         m->vlogits, m->vpv, m->vpi};
-        HIPCHK(m, launch_head_multi(ha, s));
-        HIPCHK(m, launch_head_argmax_multi(m->vpv, m->vpi, m->nhead_blocks, B, m->ctl, s));
     }
     int32_t am[4];
     HIPCHK(m, hipMemcpyAsync(am, &m->ctl->vargmax[0], 4 * sizeof(int32_t), hipMemcpyDeviceToHost, s));

@@ -236,6 +236,39 @@ def draft_leg(args, torch, A, m, shape, synth, W, t):
             "weights": "random: acceptance is that of an untrained draft head"}
 
 
+def batch_leg(args, torch, m, shape, SS, synth):
+    """Batch decode: B sequences (B = 1..4), each from its own seeded synthetic
+    state of ctx positions, one greedy step each per aw4_decode_batch call;
+    aggregate tok/s over the B sequences."""
+    for b in range(4):
+        m.select_sequence(b)
+        SS.fill(m, shape, args.ctx, args.seed + b)
+    m.select_sequence(0)
+    first = [int(t) for t in synth.tokens(4, shape.vocab, args.seed, i0=1 << 20)]
+    res = {}
+    cur = list(first)
+    for B in (1, 2, 3, 4):
+        m.decode_batch(cur[:B])   # warm-up
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.batch_steps):
+            out = m.decode_batch(cur[:B])
+            cur[:B] = out
+        wall = time.perf_counter() - t0
+        pos = args.ctx
+        state = shape.pattern.count("G") * shape.gdn_v_heads * shape.gdn_head_dim ** 2 * 8
+        kv = shape.pattern.count("A") * shape.attn_kv_heads * (shape.attn_head_dim * 11 // 8 + 16) * (pos + 1)
+        weights = step_bytes(shape, 0) - state - shape.pattern.count("A") * shape.attn_kv_heads * (shape.attn_head_dim * 11 // 8 + 16)
+        nbytes = weights + B * (state + kv)
+        res[f"B{B}"] = {"tok/s": round(B * args.batch_steps / wall, 1),
+                        "ms_per_step": round(wall * 1e3 / args.batch_steps, 3),
+                        "algorithmic_GB_per_step": round(nbytes / 1e9, 3),
+                        "frac_of_8TB/s": round(nbytes / (wall / args.batch_steps) / 1e9 / HBM_PEAK_GBS, 4)}
+    res["note"] = (f"each sequence from its own seeded {args.ctx}-position synthetic state, "
+                   f"{args.batch_steps} steps per batch size, weights read once per step")
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -254,6 +287,7 @@ def main():
     ap.add_argument("--verify-passes", type=int, default=64, help="timed verify_k passes at --long-ctx (3 drafts)")
     ap.add_argument("--draft-passes", type=int, default=64,
                     help="timed draft (aw4_draft, 3 drafts) + verify passes at --long-ctx")
+    ap.add_argument("--batch-steps", type=int, default=64, help="timed aw4_decode_batch steps per batch size 1..4 (0: skip)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run one plain device copy of this many MiB first (a known-size kernel for counter runs)")
     args = ap.parse_args()
@@ -280,7 +314,8 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    shape = W.with_(W.FULL_27B, max_ctx=args.ctx + args.warmup + args.steps + 8)
+    shape = W.with_(W.FULL_27B, max_ctx=max(args.ctx + args.warmup + args.steps, args.ctx + 4 * args.batch_steps) + 8,
+                    max_batch=4 if args.batch_steps else 1)
     t0 = time.time()
     m = A.Model(shape)
     load_recipe(m, shape, args.seed)
@@ -363,6 +398,8 @@ def main():
         "setup_s": {"load": round(t_load, 1), "prompt": round(t_prompt, 1)},
         "first_tokens": [int(t) for t in toks[:8]],
     }
+    if args.batch_steps:
+        out["batch"] = batch_leg(args, torch, m, shape, SS, synth)
     m.close()
     del m
     torch.cuda.empty_cache()
