@@ -292,18 +292,25 @@ __global__ __launch_bounds__(512, 1) void k_attn(AttnArgs a) {
     const int lim = pos + cm;                          // last position column c sees
     h8 qh[NG], ql[NG];
     {
+        // every lane loads (a dead column reads column 0) and all loads are
+        // pinned before the first use: guarded loads were sunk into one branch
+        // and one full memory wait per group
         const float* qp = a.proj + (int64_t)(tb0 + cm) * a.sproj + (int64_t)(j * G + cg) * D + 8 * q;
+        f4 xq[NG][2];
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
-            float4 x0 = make_float4(0.f, 0.f, 0.f, 0.f), x1 = x0;
-            if (qv) {
-                x0 = *(const float4*)(qp + 32 * g);
-                x1 = *(const float4*)(qp + 32 * g + 4);
-            }
-            const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+            xq[g][0] = *(const f4*)(qp + 32 * g);
+            xq[g][1] = *(const f4*)(qp + 32 * g + 4);
+        }
+#pragma unroll
+        for (int g = 0; g < NG; ++g) asm volatile("" : "+v"(xq[g][0]), "+v"(xq[g][1]));
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            const float xs[8] = {xq[g][0][0], xq[g][0][1], xq[g][0][2], xq[g][0][3],
+                                 xq[g][1][0], xq[g][1][1], xq[g][1][2], xq[g][1][3]};
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float v = xs[e] * qscale;
+                const float v = qv ? xs[e] * qscale : 0.f;
                 const _Float16 hi = (_Float16)v;
                 qh[g][e] = hi;
                 ql[g][e] = (_Float16)(v - (float)hi);
@@ -516,11 +523,11 @@ __global__ __launch_bounds__(512, 1) void k_attn(AttnArgs a) {
     }
 }
 
-template <int D>
+// KMAX: split rows per thread, enough for the launch's split count
+template <int D, int KMAX>
 __global__ __launch_bounds__(1024) void k_combine(CombineArgs a) {
     constexpr int LR = D / 4;            // lanes per split row, a float4 each
     constexpr int ROWS = 1024 / LR;      // split rows in flight
-    constexpr int KMAX = 256 / ROWS;     // rows per thread at the largest split count
     constexpr int P = D / 64;            // values per lane in the final transform
     __shared__ float wts[256];
     __shared__ float red[ROWS][D];
@@ -541,13 +548,33 @@ __global__ __launch_bounds__(1024) void k_combine(CombineArgs a) {
         ms = mlp[2 * tid];
         ls = mlp[2 * tid + 1];
     }
+    // the output gate of this head, for the wave that finishes (lane holds
+    // dims P lane .. P lane + P - 1), requested with the rest
+    float gate[P], sgn[P];
+    {
+        const float* gp = a.proj + (int64_t)tm * a.sproj + (int64_t)a.nq * D + (int64_t)hq * D + P * (tid & 63);
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+            gate[j] = gp[j];
+            sgn[j] = a.signs[P * (tid & 63) + j];
+        }
+    }
+    // straight-line loads (a split past `used` re-reads split 0 and is
+    // dropped), pinned before the first use so that none is sunk into a
+    // branch with a wait of its own; KMAX fits the launch's split count, so
+    // few of them are dead
     const int row = tid / LR, e4 = tid % LR;
     f4 pv[KMAX];
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) {
         const int sp = row + k * ROWS;
-        pv[k] = sp < used ? *(const f4*)(base + (int64_t)sp * D + 4 * e4) : f4{0.f, 0.f, 0.f, 0.f};
+        pv[k] = *(const f4*)(base + (int64_t)(sp < used ? sp : 0) * D + 4 * e4);
     }
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) asm volatile("" : "+v"(pv[k]));
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k)
+        if (row + k * ROWS >= used) pv[k] = f4{0.f, 0.f, 0.f, 0.f};
     // split weights exp(m_s - M) and the normaliser
     float M = ms;
 #pragma unroll
@@ -613,9 +640,8 @@ __global__ __launch_bounds__(1024) void k_combine(CombineArgs a) {
 #pragma unroll
         for (int j = 0; j < P; ++j) {
             const int d = P * lane + j;
-            const float o = x[j] * (1.0f / sqrtf((float)D)) * a.signs[d];
-            const float g = a.proj[(int64_t)tm * a.sproj + (int64_t)a.nq * D + (int64_t)hq * D + d];
-            a.out[(int64_t)i * D + d] = (_Float16)(o * sigmoidf_(g));
+            const float o = x[j] * (1.0f / sqrtf((float)D)) * sgn[j];
+            a.out[(int64_t)i * D + d] = (_Float16)(o * sigmoidf_(gate[j]));
         }
     }
 }
@@ -682,9 +708,15 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
     if (a.nsplit < 1 || a.nsplit > 256) return hipErrorInvalidValue;
     if (a.nt < 1 || a.nq * a.nt > a.prow) return hipErrorInvalidValue;
-    if (a.d == 256) hipLaunchKernelGGL(k_combine<256>, dim3(a.nq * a.nt), dim3(1024), 0, s, a);
-    else if (a.d == 64) hipLaunchKernelGGL(k_combine<64>, dim3(a.nq * a.nt), dim3(1024), 0, s, a);
-    else return hipErrorInvalidValue;
+    // split rows per thread: 16 (D = 256) or 64 (D = 64) rows are in flight
+    if (a.d == 256) {
+        if (a.nsplit <= 64) hipLaunchKernelGGL((k_combine<256, 4>), dim3(a.nq * a.nt), dim3(1024), 0, s, a);
+        else hipLaunchKernelGGL((k_combine<256, 16>), dim3(a.nq * a.nt), dim3(1024), 0, s, a);
+    } else if (a.d == 64) {
+        hipLaunchKernelGGL((k_combine<64, 4>), dim3(a.nq * a.nt), dim3(1024), 0, s, a);
+    } else {
+        return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

@@ -40,8 +40,13 @@ __global__ __launch_bounds__(256) void k_gdn(GdnArgs a) {
     const float* av = a.proj + 2LL * a.nqk * D + 2LL * a.nv * D;
     const float* bv = av + a.nv;
 
-    // this thread's slice of the state row, its v and the gate inputs are
-    // requested first: their HBM latency then overlaps the norm reductions
+    // k and q (cache-resident) are requested first and the state row after
+    // them: vector loads retire in issue order, so the norm reductions can
+    // start as soon as k and q arrive while the state's HBM reads are still in
+    // flight.  Threads [0, D) take k, [D, 2D) take q; the others re-read k[0]
+    // and drop it.
+    const int kqi = tid < 2 * D ? tid : 0;
+    float val = kqi < D ? k[kqi] : q[kqi - D];
     const int r = row0 + tid / TPR;
     const int c0 = (tid % TPR) * EPT;
     float* Srow = a.S + ((int64_t)h * D + r) * D + c0;
@@ -49,10 +54,10 @@ __global__ __launch_bounds__(256) void k_gdn(GdnArgs a) {
     const float4 s1 = *(const float4*)(Srow + 4);
     const float vr = v[r];
     const float araw = av[h] + a.a_bias[h], braw = bv[h];
+    asm volatile("" : "+v"(val));   // wait for k and q only
+    if (tid >= 2 * D) val = 0.f;
 
-    // L2 norms of k and q (threads [0, D) take k, [D, 2D) take q)
-    float val = 0.f;
-    if (tid < 2 * D) val = tid < D ? k[tid] : q[tid - D];
+    // L2 norms of k and q
     float ss = val * val;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);

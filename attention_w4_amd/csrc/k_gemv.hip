@@ -300,22 +300,28 @@ struct Prologue<K, PRO_GATED> {
 
 template <int K>
 struct Prologue<K, PRO_LOADH> {
+    typedef uint32_t v4u __attribute__((ext_vector_type(4)));
     static constexpr int N8 = K / 8;
     static constexpr int PER = (N8 + 255) / 256;
-    uint4 v[PER];
+    v4u v[PER];
     __device__ __forceinline__ void load(const GemvArgs& a) {
-        const uint4* src = (const uint4*)a.h;
+        const v4u* src = (const v4u*)a.h;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int idx = threadIdx.x + 256 * i;
             v[i] = src[idx < N8 ? idx : N8 - 1];   // clamped: straight-line loads, stores guarded
         }
+        // pin every load here: otherwise the compiler sinks the loads of a
+        // partial last slice into the guarded stores, one branch and one full
+        // memory wait each (four serial cache round trips at K = 17408)
+#pragma unroll
+        for (int i = 0; i < PER; ++i) asm volatile("" : "+v"(v[i]));
     }
     __device__ __forceinline__ void finish(const GemvArgs&, _Float16* xs, float*) {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int idx = threadIdx.x + 256 * i;
-            if (N8 % 256 == 0 || idx < N8) ((uint4*)xs)[idx] = v[i];
+            if (N8 % 256 == 0 || idx < N8) ((v4u*)xs)[idx] = v[i];
         }
     }
 };
@@ -939,15 +945,32 @@ __device__ __forceinline__ void mfma_prologue(const GemvMultiArgs& a, _Float16* 
     typedef _Float16 h4 __attribute__((ext_vector_type(4)));
     if (PRO == PRO_NORM) {
         constexpr int N4 = K / 4, PER = (N4 + 255) / 256;
-        float4 v[MAXM][PER], w[PER];
+        // straight-line loads (a slice past K or an input past M re-reads a
+        // valid one and is zeroed afterwards), pinned before the first use so
+        // that no load is sunk into a branch with its own full memory wait
+        typedef float f4v __attribute__((ext_vector_type(4)));
+        f4v v[MAXM][PER], w[PER];
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int idx = tid + 256 * i;
-            const bool in = N4 % 256 == 0 || idx < N4;
-            w[i] = in ? ((const float4*)a.nw)[idx] : make_float4(0.f, 0.f, 0.f, 0.f);
+            const int ic = N4 % 256 == 0 || idx < N4 ? idx : N4 - 1;
+            w[i] = ((const f4v*)a.nw)[ic];
+#pragma unroll
+            for (int m = 0; m < MAXM; ++m) v[m][i] = ((const f4v*)(a.x + (m < M ? m : 0) * a.sx))[ic];
+        }
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            asm volatile("" : "+v"(w[i]));
+#pragma unroll
+            for (int m = 0; m < MAXM; ++m) asm volatile("" : "+v"(v[m][i]));
+        }
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int idx = tid + 256 * i;
+            if (N4 % 256 != 0 && idx >= N4) w[i] = f4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int m = 0; m < MAXM; ++m)
-                v[m][i] = in && m < M ? ((const float4*)(a.x + m * a.sx))[idx] : make_float4(0.f, 0.f, 0.f, 0.f);
+                if (m >= M || (N4 % 256 != 0 && idx >= N4)) v[m][i] = f4v{0.f, 0.f, 0.f, 0.f};
         }
         float ss[MAXM];
 #pragma unroll
@@ -982,22 +1005,28 @@ __device__ __forceinline__ void mfma_prologue(const GemvMultiArgs& a, _Float16* 
 #pragma unroll
         for (int m0 = 0; m0 < MAXM; m0 += 2) {
             if (m0 >= M) break;
-            uint4 v[2][PER];
+            typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+            v4u v[2][PER];
 #pragma unroll
             for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
                 for (int i = 0; i < PER; ++i) {
                     const int idx = tid + 256 * i;
                     const int m = m0 + mm < M ? m0 + mm : m0;
-                    v[mm][i] = ((const uint4*)(a.h + m * a.sh))[idx < N8 ? idx : N8 - 1];
+                    v[mm][i] = ((const v4u*)(a.h + m * a.sh))[idx < N8 ? idx : N8 - 1];
                 }
+            // pinned: no load sunk into the guarded stores (one wait each)
+#pragma unroll
+            for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+                for (int i = 0; i < PER; ++i) asm volatile("" : "+v"(v[mm][i]));
 #pragma unroll
             for (int mm = 0; mm < 2; ++mm)
                 if (m0 + mm < M)
 #pragma unroll
                     for (int i = 0; i < PER; ++i) {
                         const int idx = tid + 256 * i;
-                        if (N8 % 256 == 0 || idx < N8) ((uint4*)(xs + (m0 + mm) * K))[idx] = v[mm][i];
+                        if (N8 % 256 == 0 || idx < N8) ((v4u*)(xs + (m0 + mm) * K))[idx] = v[mm][i];
                     }
         }
     } else {
@@ -1333,12 +1362,13 @@ void stream_shape(int K, int& R, int& NF) {
     NF = R * G / 64;
 }
 
-// 4-wave workgroups of a streaming launch over nrb row blocks with at most
-// max_waves waves, unless that would take more than kStreamMaxPer blocks per wave
+// 4-wave workgroups of a streaming launch over nrb row blocks: max_waves waves
+// (or one per block), unless that would take more than kStreamMaxPer blocks per
+// wave.  The per-wave block counts may differ by one: evening them out with
+// fewer waves left part of the chip idle (GDN in-proj: 221 of 256 CUs).
 int stream_grid(int nrb, int max_waves) {
     if (nrb > max_waves * kStreamMaxPer) max_waves = (nrb + kStreamMaxPer - 1) / kStreamMaxPer;
-    const int per = (nrb + max_waves - 1) / max_waves;
-    const int waves = (nrb + per - 1) / per;
+    const int waves = nrb < max_waves ? nrb : max_waves;
     return (waves + 3) / 4;
 }
 
