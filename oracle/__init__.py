@@ -35,7 +35,7 @@ class Cfg(ctypes.Structure):
                 ("gdn_qk_heads", _i32), ("gdn_v_heads", _i32), ("gdn_head_dim", _i32),
                 ("attn_q_heads", _i32), ("attn_kv_heads", _i32), ("attn_head_dim", _i32),
                 ("group", _i32), ("max_ctx", _i32), ("rms_eps", _f64), ("pattern", ctypes.c_char * 128),
-                ("draft_vocab", _i32)]
+                ("draft_vocab", _i32), ("kv_window", _i32)]
 
 
 _lib = None
@@ -64,7 +64,8 @@ def lib():
             "or_load_vec": ([_vp, ctypes.c_int, ctypes.c_int, _vp, ctypes.c_int], ctypes.c_int),
             "or_load_signs": ([_vp, _vp, ctypes.c_int], ctypes.c_int),
             "or_gdn_head_step": ([_vp, _vp, _vp, _vp, _f64, _f64, ctypes.c_int, ctypes.c_int, _vp], None),
-            "or_attend_head": ([_vp, _vp, _vp, _vp, _vp, _i64, _i64, ctypes.c_int, _vp, _vp], None),
+            "or_attend_head": ([_vp, _vp, _vp, _vp, _vp, _i64, _i64, ctypes.c_int, _vp, _vp, _vp, _i64, _i64, _vp],
+                               None),
             "or_kv_encode": ([_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp], None),
             "or_forward_layers": ([_vp, _vp, _vp], ctypes.c_int),
             "or_embed": ([_vp, _i32, _vp], ctypes.c_int),
@@ -73,6 +74,8 @@ def lib():
             "or_get_pos": ([_vp], _i32),
             "or_set_pos": ([_vp, _i32], ctypes.c_int),
             "or_get_last_kv": ([_vp, ctypes.c_int, _vp, _vp], ctypes.c_int),
+            "or_set_state_win": ([_vp, ctypes.c_int, _vp, _vp], ctypes.c_int),
+            "or_get_state_win": ([_vp, ctypes.c_int, _vp, _vp], ctypes.c_int),
             "or_set_state_gdn": ([_vp, ctypes.c_int, _vp], ctypes.c_int),
             "or_get_state_gdn": ([_vp, ctypes.c_int, _vp], ctypes.c_int),
             "or_set_state_kv": ([_vp, ctypes.c_int, _i32, _vp, _vp, _vp, _vp], ctypes.c_int),
@@ -158,15 +161,23 @@ def gdn_head_step(S, k, v, q, alpha, beta):
     return S, o
 
 
-def attend_head(q, kc, ks, vc, vs, signs):
-    """q [d]; kc/vc int8 [npos][d]; ks/vs fp16 bits [npos][d/32]."""
+def attend_head(q, kc, ks, vc, vs, signs, kw=None, vw=None):
+    """q [d]; kc/vc int8 [npos][d]; ks/vs fp16 bits [npos][d/32].  With a window
+    ring kw/vw (fp16 bits [W][d], position t at slot t % W), the last W
+    positions are read from it instead of the codes."""
     q = np.ascontiguousarray(q, np.float64)
     kc, vc = np.ascontiguousarray(kc, np.int8), np.ascontiguousarray(vc, np.int8)
     ks, vs = np.ascontiguousarray(ks, np.uint16), np.ascontiguousarray(vs, np.uint16)
     sg = np.ascontiguousarray(signs, np.int8)
     npos, d = kc.shape
     out = np.zeros(d)
-    lib().or_attend_head(_p(q), _p(kc), _p(ks), _p(vc), _p(vs), npos, d, d, _p(sg), _p(out))
+    if kw is None:
+        lib().or_attend_head(_p(q), _p(kc), _p(ks), _p(vc), _p(vs), npos, d, d, _p(sg), None, None, 0, 0,
+                             _p(out))
+    else:
+        kw, vw = np.ascontiguousarray(kw, np.uint16), np.ascontiguousarray(vw, np.uint16)
+        lib().or_attend_head(_p(q), _p(kc), _p(ks), _p(vc), _p(vs), npos, d, d, _p(sg), _p(kw), _p(vw),
+                             kw.shape[0], d, _p(out))
     return out
 
 
@@ -199,6 +210,7 @@ class Model:
         c.rms_eps = float(shape.rms_eps)
         c.pattern = shape.pattern.encode()
         c.draft_vocab = int(getattr(shape, "draft_vocab", 0))
+        c.kv_window = int(getattr(shape, "kv_window", 0))
         self._cfg = c
         self.h = lib().or_create(ctypes.byref(c))
         if not self.h:
@@ -324,11 +336,26 @@ class Model:
         self._rc(lib().or_get_last_kv(self.h, layer, _p(k), _p(v)), "last_kv")
         return k, v
 
+    def get_win(self, layer):
+        """fp16 window ring (keys, rotated values) [W][nkv][dh] as uint16 bits"""
+        s = self.shape
+        kw = np.zeros((s.kv_window, s.attn_kv_heads, s.attn_head_dim), np.uint16)
+        vw = np.zeros_like(kw)
+        self._rc(lib().or_get_state_win(self.h, layer, _p(kw), _p(vw)), "get_win")
+        return kw, vw
+
+    def set_win(self, layer, kw, vw):
+        kw, vw = (np.ascontiguousarray(a, np.uint16) for a in (kw, vw))
+        self._rc(lib().or_set_state_win(self.h, layer, _p(kw), _p(vw)), "set_win")
+
     def snapshot(self):
-        """recurrent states, caches and position"""
+        """recurrent states, caches (and fp16 windows) and position"""
         st = {"pos": self.pos}
+        win = getattr(self.shape, "kv_window", 0)
         for l, t in enumerate(self.shape.pattern):
             st[l] = self.get_gdn_state(l) if t == "G" else self.get_kv(l, self.pos)
+            if t == "A" and win > 0:
+                st[("win", l)] = self.get_win(l)
         return st
 
     def restore(self, st):
@@ -337,6 +364,8 @@ class Model:
                 self.set_gdn_state(l, st[l].astype(np.float32))
             else:
                 self.set_kv(l, *st[l])
+                if ("win", l) in st:
+                    self.set_win(l, *st[("win", l)])
         self.set_pos(st["pos"])
 
     def get_kv(self, layer, npos):

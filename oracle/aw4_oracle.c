@@ -147,6 +147,7 @@ typedef struct {
     double rms_eps;
     char pattern[128];
     int32_t draft_vocab;    /* rows of the draft head's vocabulary map, 0 = no draft head */
+    int32_t kv_window;      /* recent positions kept at fp16 in the target's caches, 0 = none */
 } or_cfg;
 
 typedef struct { int64_t rows, cols; uint8_t* codes; uint16_t* scales; } or_w4;
@@ -166,6 +167,9 @@ typedef struct {
     uint16_t* vs;
     float* klast;           /* A: fp32 keys of the last appended position [nkv][dh] */
     float* vlast;           /* A: fp32 rotated values of the last appended position */
+    int32_t win;            /* A: recent window W (0: every position from the codes) */
+    uint16_t* kw;           /* A, W > 0: fp16 keys of the last W positions, slot t % W [W][nkv][dh] */
+    uint16_t* vw;           /* A, W > 0: fp16 rotated values, same slots */
 } or_layer;
 
 typedef struct {
@@ -210,7 +214,7 @@ static void w4_alloc(or_w4* w, int64_t rows, int64_t cols) {
     w->scales = (uint16_t*)zalloc((size_t)(rows * (cols / 32) * 2));
 }
 
-static void layer_alloc(const or_cfg* c, or_layer* L, char type) {
+static void layer_alloc(const or_cfg* c, or_layer* L, char type, int32_t win) {
     int64_t H = c->hidden;
     {
         L->type = type;
@@ -234,6 +238,12 @@ static void layer_alloc(const or_cfg* c, or_layer* L, char type) {
             L->vs = (uint16_t*)zalloc(n / 32 * 2);
             L->klast = (float*)zalloc(sizeof(float) * c->attn_kv_heads * c->attn_head_dim);
             L->vlast = (float*)zalloc(sizeof(float) * c->attn_kv_heads * c->attn_head_dim);
+            L->win = win;
+            if (win > 0) {
+                int64_t nw = (int64_t)win * c->attn_kv_heads * c->attn_head_dim;
+                L->kw = (uint16_t*)zalloc(nw * 2);
+                L->vw = (uint16_t*)zalloc(nw * 2);
+            }
         }
     }
 }
@@ -242,6 +252,7 @@ static void layer_free(or_layer* L) {
     for (int i = 0; i < 5; ++i) { free(L->w[i].codes); free(L->w[i].scales); }
     free(L->norm_mix); free(L->norm_ffn); free(L->norm_gated); free(L->a_bias); free(L->S);
     free(L->kc); free(L->ks); free(L->vc); free(L->vs); free(L->klast); free(L->vlast);
+    free(L->kw); free(L->vw);
 }
 
 or_model* or_create(const or_cfg* cfg) {
@@ -249,14 +260,15 @@ or_model* or_create(const or_cfg* cfg) {
     m->c = *cfg;
     const or_cfg* c = &m->c;
     int64_t H = c->hidden;
-    if (c->draft_vocab < 0 || (c->draft_vocab > 0 && (c->vocab <= 0 || c->draft_vocab > c->vocab))) {
+    if (c->draft_vocab < 0 || (c->draft_vocab > 0 && (c->vocab <= 0 || c->draft_vocab > c->vocab)) ||
+        c->kv_window < 0) {
         free(m);
         return NULL;
     }
     m->L = (or_layer*)zalloc(sizeof(or_layer) * (size_t)c->n_layers);
-    for (int l = 0; l < c->n_layers; ++l) layer_alloc(c, &m->L[l], c->pattern[l]);
+    for (int l = 0; l < c->n_layers; ++l) layer_alloc(c, &m->L[l], c->pattern[l], c->kv_window);
     if (c->draft_vocab > 0) {
-        layer_alloc(c, &m->D, 'A');
+        layer_alloc(c, &m->D, 'A', 0);   /* the draft head's cache keeps no fp16 window */
         w4_alloc(&m->fuse, H, 2 * H);
         m->dn_emb = (double*)zalloc(sizeof(double) * H);
         m->dn_hid = (double*)zalloc(sizeof(double) * H);
@@ -476,20 +488,32 @@ static void gdn_mixer(or_model* m, or_layer* L, const double* xh, double* delta)
 
 /* One query head over npos cached positions (stride = elements between
  * consecutive positions of this kv head):
- *   s_t = q . deq(K_t) / sqrt(d),  p = softmax(s),  acc = sum_t p_t deq(V'_t),
- *   out = RHT^-1(acc)   (values are cached in the rotated domain). */
+ *   s_t = q . K~_t / sqrt(d),  p = softmax(s),  acc = sum_t p_t V~'_t,
+ *   out = RHT^-1(acc)   (values are cached in the rotated domain).
+ * K~_t, V~'_t are the dequantised codes, except for the last `win` positions
+ * (win > 0), which are read at fp16 from the window ring kw/vw (position t at
+ * slot t % win, slots wstride elements apart).  The recent-window variant of
+ * the KV cache: page 3 (Qwen3.8-27B 實測), section "RTX 4090 24GB", whose
+ * 130K configuration keeps the last 2,048 tokens at F16 against attention
+ * drift while older positions stay quantised. */
 void or_attend_head(const double* q, const int8_t* kc, const uint16_t* ks, const int8_t* vc,
                     const uint16_t* vs, int64_t npos, int64_t stride, int d, const int8_t* signs,
-                    double* out) {
+                    const uint16_t* kw, const uint16_t* vw, int64_t win, int64_t wstride, double* out) {
     double* s = (double*)malloc(sizeof(double) * (npos > 0 ? npos : 1));
     double* acc = (double*)calloc(d, sizeof(double));
     double scale = 1.0 / sqrt((double)d);
     double mx = -INFINITY;
+    const int64_t w0 = win > 0 ? npos - win : npos;   /* first position read from the window */
     for (int64_t t = 0; t < npos; ++t) {
-        const int8_t* kr = kc + t * stride;
-        const uint16_t* kq = ks + t * stride / 32;
         double dot = 0;
-        for (int e = 0; e < d; ++e) dot += q[e] * ((double)kr[e] * or_f16_to_f64(kq[e / 32]));
+        if (t >= w0) {
+            const uint16_t* kr = kw + (t % win) * wstride;
+            for (int e = 0; e < d; ++e) dot += q[e] * or_f16_to_f64(kr[e]);
+        } else {
+            const int8_t* kr = kc + t * stride;
+            const uint16_t* kq = ks + t * stride / 32;
+            for (int e = 0; e < d; ++e) dot += q[e] * ((double)kr[e] * or_f16_to_f64(kq[e / 32]));
+        }
         s[t] = dot * scale;
         if (s[t] > mx) mx = s[t];
     }
@@ -497,9 +521,14 @@ void or_attend_head(const double* q, const int8_t* kc, const uint16_t* ks, const
     for (int64_t t = 0; t < npos; ++t) { s[t] = exp(s[t] - mx); sum += s[t]; }
     for (int64_t t = 0; t < npos; ++t) {
         double pt = s[t] / sum;
-        const int8_t* vr = vc + t * stride;
-        const uint16_t* vq = vs + t * stride / 32;
-        for (int e = 0; e < d; ++e) acc[e] += pt * ((double)vr[e] * or_f16_to_f64(vq[e / 32]));
+        if (t >= w0) {
+            const uint16_t* vr = vw + (t % win) * wstride;
+            for (int e = 0; e < d; ++e) acc[e] += pt * or_f16_to_f64(vr[e]);
+        } else {
+            const int8_t* vr = vc + t * stride;
+            const uint16_t* vq = vs + t * stride / 32;
+            for (int e = 0; e < d; ++e) acc[e] += pt * ((double)vr[e] * or_f16_to_f64(vq[e / 32]));
+        }
     }
     or_rht_inverse(acc, signs, d, out);
     free(s);
@@ -548,6 +577,14 @@ static void attn_mixer(or_model* m, or_layer* L, int64_t t, const double* xh, do
                      L->vc + base, L->vs + base / 32);
         kv_record(k + (int64_t)j * d, v + (int64_t)j * d, m->signs, d, L->klast + (int64_t)j * d,
                   L->vlast + (int64_t)j * d);
+        if (L->win > 0) {
+            /* the window keeps the fp32 key and rotated value rounded to fp16 */
+            int64_t slot = ((t % L->win) * nkv + j) * d;
+            for (int e = 0; e < d; ++e) {
+                L->kw[slot + e] = or_f32_to_f16(L->klast[(int64_t)j * d + e]);
+                L->vw[slot + e] = or_f32_to_f16(L->vlast[(int64_t)j * d + e]);
+            }
+        }
     }
     double* o = (double*)malloc(sizeof(double) * nq * d);
     int ratio = nq / nkv;
@@ -556,7 +593,8 @@ static void attn_mixer(or_model* m, or_layer* L, int64_t t, const double* xh, do
         int j = i / ratio;
         int64_t off = (int64_t)j * d;
         or_attend_head(q + (int64_t)i * d, L->kc + off, L->ks + off / 32, L->vc + off, L->vs + off / 32,
-                       t + 1, (int64_t)nkv * d, d, m->signs, o + (int64_t)i * d);
+                       t + 1, (int64_t)nkv * d, d, m->signs, L->win > 0 ? L->kw + off : NULL,
+                       L->win > 0 ? L->vw + off : NULL, L->win, (int64_t)nkv * d, o + (int64_t)i * d);
         for (int e = 0; e < d; ++e)
             o[(int64_t)i * d + e] = to_a16(o[(int64_t)i * d + e] * sigmoid(g[(int64_t)i * d + e]));
     }
@@ -768,6 +806,24 @@ int or_get_state_kv(or_model* m, int layer, int32_t npos, int8_t* kc, uint16_t* 
     memcpy(vc, L->vc, n);
     memcpy(ks, L->ks, n / 32 * 2);
     memcpy(vs, L->vs, n / 32 * 2);
+    return 0;
+}
+
+/* The fp16 window ring of an attention layer: keys and rotated values of the
+ * last W positions, position t at slot t % W, [W][nkv][dh] fp16 bits each. */
+int or_set_state_win(or_model* m, int layer, const uint16_t* kw, const uint16_t* vw) {
+    if (layer < 0 || layer >= m->c.n_layers || m->L[layer].type != 'A' || m->L[layer].win <= 0) return -1;
+    int64_t n = (int64_t)m->L[layer].win * m->c.attn_kv_heads * m->c.attn_head_dim;
+    memcpy(m->L[layer].kw, kw, n * 2);
+    memcpy(m->L[layer].vw, vw, n * 2);
+    return 0;
+}
+
+int or_get_state_win(const or_model* m, int layer, uint16_t* kw, uint16_t* vw) {
+    if (layer < 0 || layer >= m->c.n_layers || m->L[layer].type != 'A' || m->L[layer].win <= 0) return -1;
+    int64_t n = (int64_t)m->L[layer].win * m->c.attn_kv_heads * m->c.attn_head_dim;
+    memcpy(kw, m->L[layer].kw, n * 2);
+    memcpy(vw, m->L[layer].vw, n * 2);
     return 0;
 }
 

@@ -69,7 +69,7 @@ class BruteModel:
             if t == "G":
                 self.S[l] = np.zeros((s.gdn_v_heads, s.gdn_head_dim, s.gdn_head_dim))
             else:
-                self.kv[l] = []   # list of (kc, ks, vc, vs) per position, each [nkv][...]
+                self.kv[l] = []   # per position (kc, ks, vc, vs, fp16 k, fp16 rotated v), each [nkv][...]
         d = s.attn_head_dim
         self.dpos = 0
         if getattr(s, "draft_vocab", 0) > 0:
@@ -119,9 +119,15 @@ class BruteModel:
         kc, ks = quant(k, 127)
         vr = (self.R @ v.T).T
         vc, vs = quant(vr, 3)
-        self.kv[l].append((kc, ks, vc, vs))
-        K = np.stack([dequant_i8(e[0], e[1]) for e in self.kv[l]])      # [T][nkv][d]
-        Vr = np.stack([dequant_i8(e[2], e[3]) for e in self.kv[l]])
+        # the fp32 key and rotated value at fp16, for the recent window
+        kh = k.astype(np.float32).astype(np.float16).astype(np.float64)
+        vh = vr.astype(np.float32).astype(np.float16).astype(np.float64)
+        self.kv[l].append((kc, ks, vc, vs, kh, vh))
+        T = len(self.kv[l])
+        win = getattr(s, "kv_window", 0) if l < s.n_layers else 0
+        w0 = T - win if win > 0 else T          # positions w0.. are read at fp16
+        K = np.stack([e[4] if t >= w0 else dequant_i8(e[0], e[1]) for t, e in enumerate(self.kv[l])])
+        Vr = np.stack([e[5] if t >= w0 else dequant_i8(e[2], e[3]) for t, e in enumerate(self.kv[l])])
         o = np.zeros((nq, d))
         for i in range(nq):
             j = i // (nq // nkv)

@@ -30,6 +30,7 @@ class Shape:
     max_verify: int = 4
     draft_vocab: int = 0    # ids in the draft head's vocabulary map; 0: no draft head
     max_batch: int = 1      # sequences with their own state (batch decode)
+    kv_window: int = 0      # recent positions the attention caches also keep at fp16; 0: none
 
     @property
     def n_layers(self):
