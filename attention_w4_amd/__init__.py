@@ -29,7 +29,8 @@ class Config(ctypes.Structure):
                 ("gdn_qk_heads", _i32), ("gdn_v_heads", _i32), ("gdn_head_dim", _i32),
                 ("attn_q_heads", _i32), ("attn_kv_heads", _i32), ("attn_head_dim", _i32),
                 ("group", _i32), ("max_ctx", _i32), ("max_verify", _i32), ("rms_eps", _f32),
-                ("layer_pattern", ctypes.c_char * 128), ("draft_vocab", _i32), ("max_batch", _i32)]
+                ("layer_pattern", ctypes.c_char * 128), ("draft_vocab", _i32), ("max_batch", _i32),
+                ("kv_window", _i32)]
 
     @classmethod
     def from_shape(cls, s):
@@ -42,6 +43,7 @@ class Config(ctypes.Structure):
         c.layer_pattern = s.pattern.encode()
         c.draft_vocab = int(getattr(s, "draft_vocab", 0))
         c.max_batch = int(getattr(s, "max_batch", 1))
+        c.kv_window = int(getattr(s, "kv_window", 0))
         return c
 
 
@@ -85,6 +87,8 @@ _SIGS = {
     "aw4_import_state_gdn": [_vp, _i32, _vp],
     "aw4_export_state_kv": [_vp, _i32, _i32, _vp, _vp, _vp, _vp],
     "aw4_import_state_kv": [_vp, _i32, _i32, _vp, _vp, _vp, _vp],
+    "aw4_export_state_win": [_vp, _i32, _vp, _vp],
+    "aw4_import_state_win": [_vp, _i32, _vp, _vp],
 }
 
 
@@ -343,3 +347,17 @@ class Model:
                 np.ascontiguousarray(vc, np.int8), np.ascontiguousarray(vs, np.uint16)]
         self._rc(lib().aw4_import_state_kv(self.h, layer, arrs[0].shape[0], *[_ptr(a) for a in arrs]),
                  "import_state_kv")
+
+    def export_win(self, layer):
+        """recent-window ring (fp16 bits of keys, rotated values) [W][nkv][dh]"""
+        import numpy as np
+        s = self.shape
+        kw = np.zeros((s.kv_window, s.attn_kv_heads, s.attn_head_dim), np.uint16)
+        vw = np.zeros_like(kw)
+        self._rc(lib().aw4_export_state_win(self.h, layer, _ptr(kw), _ptr(vw)), "export_state_win")
+        return kw, vw
+
+    def import_win(self, layer, kw, vw):
+        import numpy as np
+        kw, vw = (np.ascontiguousarray(a, np.uint16) for a in (kw, vw))
+        self._rc(lib().aw4_import_state_win(self.h, layer, _ptr(kw), _ptr(vw)), "import_state_win")

@@ -39,6 +39,8 @@ struct LayerBufs {
     uint16_t* ks = nullptr;
     uint32_t* vc = nullptr;
     uint16_t* vs = nullptr;
+    _Float16* kw = nullptr;     // recent window (kv_window > 0): fp16 keys [nkv][W][d], slot t % W
+    _Float16* vw = nullptr;     // fp16 rotated values, same slots
 };
 
 constexpr int kSweepRows = 4;   // most tokens one attention sweep takes (verify_k has at most 4)
@@ -95,6 +97,7 @@ struct aw4_model {
     int64_t hlen = 0;
     int nhead_blocks = 0;
     int nsplit = 1;
+    int nsplit_w = 0;               // splits of the recent window's sweep (kv_window > 0)
     int32_t host_pos = 0;
     // draft head (draft_vocab > 0)
     LayerBufs D;                    // its gated-attention layer; cache in the state region
@@ -189,6 +192,13 @@ uint32_t kv_value_field(const uint32_t* rec, int words, int bit) {
     return (uint32_t)(x >> off) & 7u;
 }
 
+// Splits of the recent window's sweep per kv head: about 64 positions each, at
+// most 64 (the window's kernel runs after the main sweep, on its own round).
+int win_splits(int win) {
+    int n = (win + 63) / 64;
+    return n < 1 ? 1 : n > 64 ? 64 : n;
+}
+
 // Splits of the attention grid per kv head: one workgroup per compute unit in
 // one round (256 units on gfx950; aw4_create lowers it to the device's count),
 // never more than there are 16-position tiles of capacity.
@@ -279,6 +289,11 @@ uint64_t plan_layout(const aw4_config* c, aw4_model* m, uint8_t* base) {
             b.ks = p.take<uint16_t>(n / 32 * 2);
             b.vc = p.take<uint32_t>(n / 32 * 12);
             b.vs = p.take<uint16_t>(n / 32 * 2);
+            if (c->kv_window > 0) {
+                const uint64_t nw = (uint64_t)c->attn_kv_heads * c->kv_window * c->attn_head_dim;
+                b.kw = p.take<_Float16>(nw * 2);
+                b.vw = p.take<_Float16>(nw * 2);
+            }
         }
     }
     if (dh) {
@@ -301,8 +316,10 @@ uint64_t plan_layout(const aw4_config* c, aw4_model* m, uint8_t* base) {
     _Float16* hbuf = p.take<_Float16>((uint64_t)hlen * 2);
     _Float16* abuf = p.take<_Float16>((uint64_t)(has_a || dh ? c->attn_q_heads * c->attn_head_dim : 1) * 2);
     const int nsplit = nsplit_for(c->max_ctx, c->attn_kv_heads);
-    // split partials: one row per (token of a sweep, q head), up to 4 tokens
-    float* part = p.take<float>((uint64_t)(has_a || dh ? kSweepRows * c->attn_q_heads : 1) * nsplit *
+    const int nsplit_w = c->kv_window > 0 ? win_splits(c->kv_window) : 0;
+    // split partials: one row per (token of a sweep, q head), up to 4 tokens,
+    // nsplit slots (+ nsplit_w for the recent window) each
+    float* part = p.take<float>((uint64_t)(has_a || dh ? kSweepRows * c->attn_q_heads : 1) * (nsplit + nsplit_w) *
                                 (c->attn_head_dim + 2) * 4);
     float* logits = nullptr;
     float* pv = nullptr;
@@ -434,6 +451,8 @@ uint64_t plan_layout(const aw4_config* c, aw4_model* m, uint8_t* base) {
         m->ring_cap = kRingCap;
         m->nhead_blocks = nhb;
         m->nsplit = nsplit;
+        m->nsplit_w = nsplit_w;
+        if (c->kv_window > 0) m->pchunk_max = m->pchunk = 0;   // prefill runs token by token
         m->state_off = state_off;
         m->state_bytes = state_bytes;
         m->max_batch = nbatch;
@@ -477,6 +496,9 @@ const char* check_config(const aw4_config* c) {
     if (c->max_ctx < 1) return "max_ctx must be >= 1";
     if (c->max_verify < 1 || c->max_verify > 4) return "max_verify must be in [1, 4]";
     if (c->max_batch < 0 || c->max_batch > 4) return "max_batch must be in [0, 4]";
+    if (c->kv_window < 0 || c->kv_window > c->max_ctx) return "kv_window must be in [0, max_ctx]";
+    if (c->kv_window > 0 && (c->max_batch > 1 || c->draft_vocab > 0))
+        return "kv_window needs max_batch <= 1 and no draft head (single-sequence decode only)";
     if (!(c->rms_eps > 0.f) || !std::isfinite(c->rms_eps)) return "rms_eps must be positive";
     return nullptr;
 }
@@ -598,9 +620,20 @@ int enqueue_block(aw4_model* m, LayerBufs& b, float* x, const int32_t* posp, int
             aa.nkv = c->attn_kv_heads;
             aa.d = c->attn_head_dim;
             aa.nsplit = m->nsplit;
+            if (b.kw) {
+                // recent window: the token's codes and fp16 entry first, then
+                // the sweep before the window and the window's own sweep
+                aa.win = c->kv_window;
+                aa.nsplit_w = m->nsplit_w;
+                aa.kw = b.kw;
+                aa.vw = b.vw;
+                aa.append = 0;
+                HIPCHK(m, launch_append(aa, s));
+            }
             HIPCHK(m, launch_attn(aa, s));
+            if (b.kw) HIPCHK(m, launch_attn_win(aa, s));
             CombineArgs ca{pos_offset, 1, 0, m->part, m->proj, m->signs, posp, m->abuf, aa.prow, c->attn_q_heads,
-                           c->attn_kv_heads, c->attn_head_dim, m->nsplit};
+                           c->attn_kv_heads, c->attn_head_dim, m->nsplit, 0, aa.win, aa.nsplit_w};
             HIPCHK(m, launch_combine(ca, s));
             GemvArgs go{};
             go.codes = b.w_out;
@@ -1437,6 +1470,7 @@ int aw4_decode_batch(aw4_model* m, const int32_t* host_tokens, int32_t B, int32_
     const aw4_config* c = &m->cfg;
     if (c->vocab <= 0) return fail(m, AW4_E_STATE, "decode_batch needs a vocabulary");
     if (B < 1 || B > m->max_batch) return fail(m, AW4_E_INVAL, "batch must be in [1, max_batch]");
+    if (c->kv_window > 0) return fail(m, AW4_E_INVAL, "batch decode does not read a recent window");
     m->seq_pos[m->seq] = m->host_pos;
     int32_t tok[4] = {0, 0, 0, 0}, pos[4] = {0, 0, 0, 0};
     for (int b = 0; b < B; ++b) {
@@ -1650,6 +1684,7 @@ int aw4_verify_k(aw4_model* m, const int32_t* host_tokens, int32_t k, const floa
     if (check_model(m) || !host_tokens || !host_out || !host_n_out) return AW4_E_INVAL;
     const aw4_config* c = &m->cfg;
     if (c->vocab <= 0) return fail(m, AW4_E_STATE, "verify_k needs a vocabulary");
+    if (c->kv_window > 0) return fail(m, AW4_E_INVAL, "verify_k does not read a recent window");
     if (k < 0 || k + 1 > c->max_verify) return fail(m, AW4_E_INVAL, "k must be in [0, max_verify - 1]");
     if (!(temperature >= 0.f) || !std::isfinite(temperature)) return fail(m, AW4_E_INVAL, "temperature must be >= 0");
     if (temperature > 0.f && (!host_u || (k > 0 && !dev_q)))
@@ -1827,6 +1862,50 @@ int aw4_import_state_kv(aw4_model* m, int32_t layer, int32_t npos, const int8_t*
         HIPCHK(m, hipMemcpy(b.vc + hb * VW, v.data(), v.size() * 4, hipMemcpyHostToDevice));
     }
     return AW4_OK;
+}
+
+// Recent-window ring of an attention layer in the logical layout [W][nkv][d]
+// (fp16 bits, position t at slot t % W); the library keeps [nkv][W][d].
+static int win_copy(aw4_model* m, int32_t layer, uint16_t* kw, uint16_t* vw, bool to_host) {
+    if (check_model(m) || !kw || !vw) return AW4_E_INVAL;
+    const aw4_config* c = &m->cfg;
+    if (layer < 0 || layer >= c->n_layers || m->L[layer].type != 'A' || !m->L[layer].kw)
+        return fail(m, AW4_E_INVAL, "not an attention layer with a recent window");
+    const int nkv = c->attn_kv_heads, d = c->attn_head_dim, W = c->kv_window;
+    LayerBufs& b = m->L[layer];
+    HIPCHK(m, hipStreamSynchronize(m->stream));
+    std::vector<uint16_t> hk((size_t)nkv * W * d), hv(hk.size());
+    if (to_host) {
+        HIPCHK(m, hipMemcpy(hk.data(), b.kw, hk.size() * 2, hipMemcpyDeviceToHost));
+        HIPCHK(m, hipMemcpy(hv.data(), b.vw, hv.size() * 2, hipMemcpyDeviceToHost));
+    }
+    for (int w = 0; w < W; ++w)
+        for (int j = 0; j < nkv; ++j) {
+            uint16_t* lk = kw + ((int64_t)w * nkv + j) * d;
+            uint16_t* lv = vw + ((int64_t)w * nkv + j) * d;
+            uint16_t* gk = hk.data() + ((int64_t)j * W + w) * d;
+            uint16_t* gv = hv.data() + ((int64_t)j * W + w) * d;
+            if (to_host) {
+                memcpy(lk, gk, (size_t)d * 2);
+                memcpy(lv, gv, (size_t)d * 2);
+            } else {
+                memcpy(gk, lk, (size_t)d * 2);
+                memcpy(gv, lv, (size_t)d * 2);
+            }
+        }
+    if (!to_host) {
+        HIPCHK(m, hipMemcpy(b.kw, hk.data(), hk.size() * 2, hipMemcpyHostToDevice));
+        HIPCHK(m, hipMemcpy(b.vw, hv.data(), hv.size() * 2, hipMemcpyHostToDevice));
+    }
+    return AW4_OK;
+}
+
+int aw4_export_state_win(aw4_model* m, int32_t layer, uint16_t* host_kw, uint16_t* host_vw) {
+    return win_copy(m, layer, host_kw, host_vw, true);
+}
+
+int aw4_import_state_win(aw4_model* m, int32_t layer, const uint16_t* host_kw, const uint16_t* host_vw) {
+    return win_copy(m, layer, const_cast<uint16_t*>(host_kw), const_cast<uint16_t*>(host_vw), false);
 }
 
 }  // extern "C"

@@ -128,6 +128,13 @@ struct AttnArgs {
     int64_t seq_bytes;
     int32_t prow;             // rows of part: nq times the most tokens per sweep
     int32_t max_ctx, nq, nkv, d, nsplit;
+    // recent window (win > 0): positions [npos - win, npos) are read at fp16
+    // from the ring kw/vw ([nkv][win][d], position t at slot t % win) by
+    // k_attn_win into split slots nsplit .. nsplit + nsplit_w - 1 of each
+    // partial row; k_attn covers the positions before the window
+    int32_t win, nsplit_w;
+    _Float16* kw;
+    _Float16* vw;
 };
 
 struct CombineArgs {
@@ -142,6 +149,7 @@ struct CombineArgs {
     int32_t prow;
     int32_t nq, nkv, d, nsplit;
     int32_t batch;            // 1: token m is sequence m's single token at pos[m]
+    int32_t win, nsplit_w;    // recent window (AttnArgs): the window's splits follow the others
 };
 
 struct GdnMultiArgs {
@@ -268,6 +276,7 @@ hipError_t launch_set_verify(Ctl* ctl, const int32_t* tok, const float* u, hipSt
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
 hipError_t launch_append(const AttnArgs& a, hipStream_t s);
 int attn_tokens_per_sweep(int d, int nq, int nkv);
+hipError_t launch_attn_win(const AttnArgs& a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_embed(const int8_t* codes, const uint16_t* scales, int H, const Ctl* ctl, float* x,
                         hipStream_t s);

@@ -74,7 +74,8 @@ __device__ __forceinline__ h8 u8x8_to_h8(uint32_t x0, uint32_t x1) {
 // wave, lane holding dims P lane .. P lane + P - 1; vq is D bytes of LDS.
 template <int D>
 __device__ void encode_append(const float* kp, const float* vp, const float* signs, int8_t* kc, uint16_t* ks,
-                              uint32_t* vc, uint16_t* vs, int64_t prow, uint8_t* vq, int lane) {
+                              uint32_t* vc, uint16_t* vs, int64_t prow, uint8_t* vq, int lane,
+                              _Float16* kwr = nullptr, _Float16* vwr = nullptr) {
     constexpr int NG = D / 32, NB = D / 16, VW = 3 * NG;
     const float qscale = 1.0f / sqrtf((float)D);
     constexpr int P = D / 64;                 // dims per lane: d = P lane + i
@@ -85,6 +86,11 @@ __device__ void encode_append(const float* kp, const float* vp, const float* sig
         kv[i] = kp[P * lane + i];
         v[i] = vp[P * lane + i] * signs[P * lane + i];
     }
+    // recent window (kwr non-null): the fp32 key and, below, the fp32 rotated
+    // value are also kept rounded to fp16
+    if (kwr)
+#pragma unroll
+        for (int i = 0; i < P; ++i) kwr[P * lane + i] = (_Float16)kv[i];
     float am = 0.f;
 #pragma unroll
     for (int i = 0; i < P; ++i) am = fmaxf(am, fabsf(kv[i]));
@@ -131,6 +137,9 @@ __device__ void encode_append(const float* kp, const float* vp, const float* sig
         v[i] *= qscale;   // 1/sqrt(D): a power of two for D = 64, 256
         am = fmaxf(am, fabsf(v[i]));
     }
+    if (vwr)
+#pragma unroll
+        for (int i = 0; i < P; ++i) vwr[P * lane + i] = (_Float16)v[i];
 #pragma unroll
     for (int o = 1; o < GL; o <<= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
     {
@@ -199,7 +208,10 @@ __global__ __launch_bounds__(512, 1) void k_attn(AttnArgs a) {
     uint32_t* const vc = (uint32_t*)((char*)a.vc + zoff);
     uint16_t* const vs = (uint16_t*)((char*)a.vs + zoff);
     const int nt = NT == 1 ? 1 : min(NT, a.nt - tb0);
-    const int npos = pos + nt;
+    // with a recent window (win > 0) this sweep covers only the positions
+    // before it; k_attn_win reads the window
+    const int npos = pos + nt - (a.win > 0 ? a.win : 0);
+    if (npos <= 0) return;
     int pps, used;
     split_range(npos, a.nsplit, pps, used);
     if (split >= used) return;
@@ -443,8 +455,10 @@ __global__ __launch_bounds__(512, 1) void k_attn(AttnArgs a) {
     l += __shfl_xor(l, 32, 64);
 
     // partial rows: column c of kv head j is slot (c / G) nq + j G + c % G
-    float* mlp = a.part + (int64_t)a.prow * a.nsplit * D;
-    auto slot_row = [&](int cc) { return (int64_t)((tb0 + cc / G) * a.nq + j * G + cc % G) * a.nsplit + split; };
+    // partial rows hold nsplit + nsplit_w split slots (the window's last)
+    const int sstride = a.nsplit + a.nsplit_w;
+    float* mlp = a.part + (int64_t)a.prow * sstride * D;
+    auto slot_row = [&](int cc) { return (int64_t)((tb0 + cc / G) * a.nq + j * G + cc % G) * sstride + split; };
     if (kOnePass) {
         // every wave posts (m, l, acc) of its columns; lane (c, q) holds column c,
         // dims 16 b + 4 q + rr; then one pass merges the waves per output
@@ -537,16 +551,25 @@ __global__ __launch_bounds__(1024) void k_combine(CombineArgs a) {
     const int i = blockIdx.x, tid = threadIdx.x;
     const int tm = i / a.nq, hq = i % a.nq;
     int pps, used;
-    if (a.batch) split_range(a.pos[tm] + 1, a.nsplit, pps, used);
-    else split_range(*a.pos + a.pos_offset + a.nt, a.nsplit, pps, used);
-    const float* base = a.part + (int64_t)i * a.nsplit * D;
-    const float* mlp = a.part + (int64_t)a.prow * a.nsplit * D + 2LL * i * a.nsplit;
+    const int npos_all = a.batch ? a.pos[tm] + 1 : *a.pos + a.pos_offset + a.nt;
+    // with a recent window: splits of the positions before it (slots 0 ..
+    // used_q - 1), then the window's splits (slots nsplit ..)
+    const int nq_pos = npos_all - (a.win > 0 ? a.win : 0);
+    int used_q = 0;
+    if (nq_pos > 0) split_range(nq_pos, a.nsplit, pps, used_q);
+    int used_w = 0;
+    if (a.win > 0) split_range(npos_all < a.win ? npos_all : a.win, a.nsplit_w, pps, used_w);
+    used = used_q + used_w;
+    const int sstride = a.nsplit + a.nsplit_w;
+    auto slot = [&](int sp) { return sp < used_q ? sp : a.nsplit + (sp - used_q); };
+    const float* base = a.part + (int64_t)i * sstride * D;
+    const float* mlp = a.part + (int64_t)a.prow * sstride * D + 2LL * i * sstride;
     // every load is issued before any is used: (m, l) of one split per
     // thread, then this thread's slices of the split rows
     float ms = -INFINITY, ls = 0.f;
     if (tid < used) {
-        ms = mlp[2 * tid];
-        ls = mlp[2 * tid + 1];
+        ms = mlp[2 * slot(tid)];
+        ls = mlp[2 * slot(tid) + 1];
     }
     // the output gate of this head, for the wave that finishes (lane holds
     // dims P lane .. P lane + P - 1), requested with the rest
@@ -568,7 +591,7 @@ __global__ __launch_bounds__(1024) void k_combine(CombineArgs a) {
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) {
         const int sp = row + k * ROWS;
-        pv[k] = *(const f4*)(base + (int64_t)(sp < used ? sp : 0) * D + 4 * e4);
+        pv[k] = *(const f4*)(base + (int64_t)(sp < used ? slot(sp) : 0) * D + 4 * e4);
     }
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) asm volatile("" : "+v"(pv[k]));
@@ -654,8 +677,111 @@ __global__ __launch_bounds__(64) void k_append(AttnArgs a) {
     const int j = blockIdx.x, tm = blockIdx.y;
     const int pos = *a.pos + a.pos_offset + tm;
     const float* kp = a.proj + (int64_t)tm * a.sproj + 2LL * a.nq * D + (int64_t)j * D;
+    _Float16 *kwr = nullptr, *vwr = nullptr;
+    if (a.win > 0) {
+        const int64_t wr = ((int64_t)j * a.win + pos % a.win) * D;
+        kwr = a.kw + wr;
+        vwr = a.vw + wr;
+    }
     encode_append<D>(kp, kp + (int64_t)a.nkv * D, a.signs, a.kc, a.ks, a.vc, a.vs, (int64_t)j * a.max_ctx + pos, vq,
-                     threadIdx.x);
+                     threadIdx.x, kwr, vwr);
+}
+
+// The recent window of the single-token decode step: positions
+// [npos - win, npos) of kv head blockIdx.y, read at fp16 from the ring
+// (position t at slot t % win, [nkv][win][D]), split over gridDim.x
+// workgroups whose partial rows go to slots nsplit + split, in the layout the
+// quantised sweep uses, so that k_combine merges both.  Lane l holds dims
+// P l .. P l + P - 1 of the G query heads and of each position's key and value;
+// a wave takes every kWinWaves-th position of the split and keeps an online
+// softmax per head; the waves merge through LDS.
+constexpr int kWinWaves = 8;
+
+template <int D, int G>
+__global__ __launch_bounds__(64 * kWinWaves) void k_attn_win(AttnArgs a) {
+    constexpr int P = D / 64;
+    __shared__ float mo[kWinWaves][G][D];
+    __shared__ float mm[kWinWaves][G], ll[kWinWaves][G];
+    const int split = blockIdx.x, j = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int npos = *a.pos + a.pos_offset + 1;
+    const int wlen = npos < a.win ? npos : a.win;
+    int pps, used;
+    split_range(wlen, a.nsplit_w, pps, used);
+    if (split >= used) return;
+    const int t0 = npos - wlen + split * pps;
+    const int t1 = min(npos, t0 + pps);
+    const float qscale = 1.0f / sqrtf((float)D);
+    float q[G][P];
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int i = 0; i < P; ++i) q[h][i] = a.proj[(int64_t)(j * G + h) * D + P * lane + i] * qscale;
+    const _Float16* kb = a.kw + (int64_t)j * a.win * D + P * lane;
+    const _Float16* vb = a.vw + (int64_t)j * a.win * D + P * lane;
+    float m[G], l[G], acc[G][P];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        m[h] = -INFINITY;
+        l[h] = 0.f;
+#pragma unroll
+        for (int i = 0; i < P; ++i) acc[h][i] = 0.f;
+    }
+    for (int t = t0 + w; t < t1; t += kWinWaves) {
+        const int64_t r = (int64_t)(t % a.win) * D;
+        float kk[P], vv[P];
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            kk[i] = (float)kb[r + i];
+            vv[i] = (float)vb[r + i];
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            float sdot = 0.f;
+#pragma unroll
+            for (int i = 0; i < P; ++i) sdot += q[h][i] * kk[i];
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) sdot += __shfl_xor(sdot, o, 64);
+            const float mn = fmaxf(m[h], sdot);
+            const float corr = __expf(m[h] - mn);   // 0 on the first position (m = -inf)
+            const float pe = __expf(sdot - mn);
+            l[h] = l[h] * corr + pe;
+#pragma unroll
+            for (int i = 0; i < P; ++i) acc[h][i] = acc[h][i] * corr + pe * vv[i];
+            m[h] = mn;
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+#pragma unroll
+        for (int i = 0; i < P; ++i) mo[w][h][P * lane + i] = acc[h][i];
+        if (lane == 0) {
+            mm[w][h] = m[h];
+            ll[w][h] = l[h];
+        }
+    }
+    __syncthreads();
+    const int sstride = a.nsplit + a.nsplit_w;
+    float* mlp = a.part + (int64_t)a.prow * sstride * D;
+    for (int idx = tid; idx < G * D; idx += 64 * kWinWaves) {
+        const int h = idx / D, e = idx % D;
+        float M = mm[0][h];
+#pragma unroll
+        for (int ww = 1; ww < kWinWaves; ++ww) M = fmaxf(M, mm[ww][h]);
+        float L = 0.f, A = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < kWinWaves; ++ww) {
+            const float f = mm[ww][h] == -INFINITY ? 0.f : __expf(mm[ww][h] - M);
+            L += ll[ww][h] * f;
+            A += mo[ww][h][e] * f;
+        }
+        const int64_t row = (int64_t)(j * G + h) * sstride + a.nsplit + split;
+        a.part[row * D + e] = A;
+        if (e == 0) {
+            mlp[2 * row] = M;
+            mlp[2 * row + 1] = L;
+        }
+    }
 }
 
 }  // namespace
@@ -705,12 +831,35 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
     return hipErrorInvalidValue;
 }
 
+hipError_t launch_attn_win(const AttnArgs& a, hipStream_t s) {
+    const int G = a.nq / a.nkv;
+    if (a.win < 1 || a.nsplit_w < 1 || a.nt != 1 || a.batch || a.nq > a.prow || !a.kw || !a.vw)
+        return hipErrorInvalidValue;
+    const dim3 grid(a.nsplit_w, a.nkv), block(64 * kWinWaves);
+#define AW4_WIN_CASE(DD, GG)                                            \
+    if (a.d == DD && G == GG) {                                         \
+        hipLaunchKernelGGL((k_attn_win<DD, GG>), grid, block, 0, s, a); \
+        return hipGetLastError();                                       \
+    }
+    AW4_WIN_CASE(256, 6)
+    AW4_WIN_CASE(256, 4)
+    AW4_WIN_CASE(256, 2)
+    AW4_WIN_CASE(256, 1)
+    AW4_WIN_CASE(64, 4)
+    AW4_WIN_CASE(64, 2)
+    AW4_WIN_CASE(64, 1)
+    AW4_WIN_CASE(64, 6)
+    AW4_WIN_CASE(64, 8)
+#undef AW4_WIN_CASE
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
-    if (a.nsplit < 1 || a.nsplit > 256) return hipErrorInvalidValue;
+    if (a.nsplit < 1 || a.nsplit + a.nsplit_w > 256) return hipErrorInvalidValue;
     if (a.nt < 1 || a.nq * a.nt > a.prow) return hipErrorInvalidValue;
     // split rows per thread: 16 (D = 256) or 64 (D = 64) rows are in flight
     if (a.d == 256) {
-        if (a.nsplit <= 64) hipLaunchKernelGGL((k_combine<256, 4>), dim3(a.nq * a.nt), dim3(1024), 0, s, a);
+        if (a.nsplit + a.nsplit_w <= 64) hipLaunchKernelGGL((k_combine<256, 4>), dim3(a.nq * a.nt), dim3(1024), 0, s, a);
         else hipLaunchKernelGGL((k_combine<256, 16>), dim3(a.nq * a.nt), dim3(1024), 0, s, a);
     } else if (a.d == 64) {
         hipLaunchKernelGGL((k_combine<64, 4>), dim3(a.nq * a.nt), dim3(1024), 0, s, a);

@@ -236,6 +236,55 @@ def draft_leg(args, torch, A, m, shape, synth, W, t):
             "weights": "random: acceptance is that of an untrained draft head"}
 
 
+def window_leg(args, torch, A, W, SS, synth):
+    """Greedy decode with the recent-window KV variant (the last W positions of
+    every attention layer read at fp16, older ones from their codes), from a
+    seeded synthetic state of ctx positions whose ring holds fp16 values, at
+    each context of --window-ctx.  Algorithmic bytes per step: the plain step's
+    bytes with the window's positions counted at 2 x 2 x dh bytes (fp16 key and
+    value) instead of the 384 bytes of their codes and scales, per kv head and
+    attention layer."""
+    from concurrent.futures import ThreadPoolExecutor
+    from synth.gpu_load import load_recipe
+    out = {"window": args.window}
+    for ctx in [int(c) for c in args.window_ctx.split(",") if c]:
+        shape = W.with_(W.FULL_27B, max_ctx=ctx + args.window_steps + 32, draft_vocab=0, kv_window=args.window)
+        m = A.Model(shape)
+        load_recipe(m, shape, args.seed)
+        t0 = time.time()
+        SS.fill(m, shape, ctx - 1, args.seed, kv=False)
+        alayers = [l for l, t in enumerate(shape.pattern) if t == "A"]
+        with ThreadPoolExecutor(4) as ex:
+            for l, kv in zip(alayers, ex.map(lambda l: SS.kv_state(shape, l, ctx - 1, args.seed), alayers)):
+                m.import_kv(l, *kv)
+                m.import_win(l, *SS.win_state(shape, l, args.seed))
+        m.set_pos(ctx - 1)
+        m.sync()
+        t_fill = time.time() - t0
+        first = int(synth.tokens(1, shape.vocab, args.seed + 2)[0])
+        tok = int(m.decode_greedy(first, 8)[-1])
+        pos0 = m.pos
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        m.decode_greedy(tok, args.window_steps)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        d, nkv, na = shape.attn_head_dim, shape.attn_kv_heads, shape.pattern.count("A")
+        nbytes = sum(step_bytes(shape, p) + na * nkv * min(args.window, p + 1) * (4 * d - 384)
+                     for p in range(pos0, pos0 + args.window_steps))
+        out[f"ctx_{ctx}"] = {"tok/s": round(args.window_steps / wall, 2),
+                             "ms_per_step": round(wall * 1e3 / args.window_steps, 4),
+                             "steps": args.window_steps, "ctx_start": int(pos0),
+                             "algorithmic_GB_per_step": round(nbytes / args.window_steps / 1e9, 4),
+                             "frac_of_8TB/s": round(nbytes / wall / 1e9 / HBM_PEAK_GBS, 4),
+                             "setup_fill_s": round(t_fill, 1)}
+        m.close()
+        del m
+        torch.cuda.empty_cache()
+    out["state"] = "seeded synthetic cache, recurrent states and fp16 ring"
+    return out
+
+
 def batch_leg(args, torch, m, shape, SS, synth):
     """Batch decode: B sequences (B = 1..4), each from its own seeded synthetic
     state of ctx positions, one greedy step each per aw4_decode_batch call;
@@ -288,6 +337,10 @@ def main():
     ap.add_argument("--draft-passes", type=int, default=64,
                     help="timed draft (aw4_draft, 3 drafts) + verify passes at --long-ctx")
     ap.add_argument("--batch-steps", type=int, default=64, help="timed aw4_decode_batch steps per batch size 1..4 (0: skip)")
+    ap.add_argument("--window", type=int, default=2048,
+                    help="recent-window leg: positions kept at fp16 per attention layer (0: skip)")
+    ap.add_argument("--window-ctx", default="8192,131072", help="contexts of the recent-window leg")
+    ap.add_argument("--window-steps", type=int, default=128, help="timed greedy steps per window context")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run one plain device copy of this many MiB first (a known-size kernel for counter runs)")
     args = ap.parse_args()
@@ -400,6 +453,8 @@ def main():
     }
     if args.batch_steps:
         out["batch"] = batch_leg(args, torch, m, shape, SS, synth)
+    if args.window:
+        out["kv_window"] = window_leg(args, torch, A, W, SS, synth)
     m.close()
     del m
     torch.cuda.empty_cache()

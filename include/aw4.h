@@ -61,7 +61,19 @@ extern "C" {
  * max_ctx >= 1; max_verify in [1, 4]; rms_eps > 0; draft_vocab in [0, vocab]
  * (0: no draft head; otherwise the attention fields must describe a valid
  * attention layer even when the pattern holds none, since the draft head's
- * block has that shape, and hidden <= 8192); max_batch in [0, 4]. */
+ * block has that shape, and hidden <= 8192); max_batch in [0, 4];
+ * kv_window in [0, max_ctx], and with kv_window > 0 also max_batch <= 1 and
+ * draft_vocab == 0.
+ *
+ * Recent window (kv_window = W > 0; page 3, "Qwen3.8-27B 實測", section
+ * "RTX 4090 24GB": a 130K configuration keeps the last 2,048 tokens at F16
+ * against attention drift).  Every appended position still gets its int8 key
+ * and 3-bit rotated value codes; in addition the fp32 key and the fp32 rotated
+ * value are kept rounded to fp16 in a ring of W slots (position t at slot
+ * t % W).  A decode step at position p reads positions p - W + 1 .. p from the
+ * ring and the older ones from their codes.  Only the single-sequence decode
+ * path reads the window: aw4_prefill runs token by token (no chunks),
+ * aw4_verify_k and aw4_decode_batch return AW4_E_INVAL. */
 typedef struct aw4_config {
     int32_t hidden;
     int32_t ffn;
@@ -80,6 +92,8 @@ typedef struct aw4_config {
     char layer_pattern[128];
     int32_t draft_vocab;        /* ids in the draft head's vocabulary map */
     int32_t max_batch;          /* sequences with their own state (0 or 1: one; at most 4) */
+    int32_t kv_window;          /* recent window: the last kv_window positions of every
+                                   attention layer are read at fp16 (0: none); see below */
 } aw4_config;
 
 typedef struct aw4_model aw4_model;
@@ -343,6 +357,14 @@ int aw4_export_state_kv(aw4_model* model, int32_t layer, int32_t npos, int8_t* h
                         int8_t* host_vc, uint16_t* host_vs);
 int aw4_import_state_kv(aw4_model* model, int32_t layer, int32_t npos, const int8_t* host_kc,
                         const uint16_t* host_ks, const int8_t* host_vc, const uint16_t* host_vs);
+
+/* The recent-window ring of attention layer `layer` (kv_window > 0), in the
+ * logical layout: keys and rotated values as fp16 bits [kv_window][nkv][dh],
+ * position t at slot t % kv_window.  Host buffers of kv_window * nkv * dh
+ * uint16 each, owned by the caller.  Synchronises the model's stream.
+ * AW4_E_INVAL: not an attention layer, or no window configured. */
+int aw4_export_state_win(aw4_model* model, int32_t layer, uint16_t* host_kw, uint16_t* host_vw);
+int aw4_import_state_win(aw4_model* model, int32_t layer, const uint16_t* host_kw, const uint16_t* host_vw);
 
 #ifdef __cplusplus
 }

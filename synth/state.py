@@ -3,7 +3,8 @@
 Used where a long context has to exist without prefilling it token by token
 (8K-262K positions): both the oracle and the GPU model import the same arrays.
 Codes and scales are drawn directly (discretised normals, fp16 bit patterns),
-so no quantiser is involved.  Magnitudes mimic what the decode step writes:
+so no quantiser is involved (the recent-window ring, when the shape has one,
+is fp16 of seeded normals).  Magnitudes mimic what the decode step writes:
 keys ~ N(0, 1.4^2) stored as int8 codes x 0.035, rotated values ~ 1.4 in
 3-bit codes x ~1, recurrent state entries ~ N(0, 0.1^2).
 """
@@ -39,6 +40,15 @@ def kv_state(shape, layer, npos, seed):
     return kc, ks, vc, vs
 
 
+def win_state(shape, layer, seed):
+    """Recent-window ring [W][nkv][d] as fp16 bits: keys ~ N(0, 1.4^2), rotated
+    values ~ N(0, 1), the magnitudes the codes above stand for."""
+    d, nkv, W = shape.attn_head_dim, shape.attn_kv_heads, shape.kv_window
+    kw = normal(W * nkv, d, 1.4, seed, _stream(layer, 5)).astype(np.float16).view(np.uint16)
+    vw = normal(W * nkv, d, 1.0, seed, _stream(layer, 6)).astype(np.float16).view(np.uint16)
+    return kw.reshape(W, nkv, d), vw.reshape(W, nkv, d)
+
+
 def fill(model, shape, npos, seed, gdn=True, kv=True, draft=True):
     """Import a synthetic state of npos positions into a model exposing
     import_gdn / import_kv / set_pos (the GPU binding) or set_gdn_state /
@@ -51,6 +61,8 @@ def fill(model, shape, npos, seed, gdn=True, kv=True, draft=True):
             (model.import_gdn if hasattr(model, "import_gdn") else model.set_gdn_state)(l, S)
         elif t == "A" and kv:
             put_kv(l, *kv_state(shape, l, npos, seed))
+            if getattr(shape, "kv_window", 0) > 0:
+                (model.import_win if hasattr(model, "import_win") else model.set_win)(l, *win_state(shape, l, seed))
     if getattr(shape, "draft_vocab", 0) > 0 and draft and npos > 0:
         put_kv(shape.n_layers, *kv_state(shape, shape.n_layers, npos - 1, seed))
         model.set_dpos(npos - 1)

@@ -36,9 +36,19 @@ def _cfg(shape, **kw):
     return c
 
 
-@pytest.mark.parametrize("shape", [W.TOY, W.FULL_27B, W.GDN_LAYER, W.ATTN_LAYER])
+@pytest.mark.parametrize("shape", [W.TOY, W.FULL_27B, W.GDN_LAYER, W.ATTN_LAYER,
+                                   W.with_(W.TOY, kv_window=16), W.with_(W.FULL_27B, kv_window=2048, draft_vocab=0)])
 def test_valid_configs(shape):
     assert A.lib().aw4_validate_config(ctypes.byref(_cfg(shape))) == 0
+
+
+def test_window_adds_its_ring_to_the_workspace():
+    """kv_window W adds two fp16 rings of W x nkv x dh per attention layer
+    (and W / 64 split slots of partials)"""
+    base = A.workspace_bytes(W.TOY)
+    win = A.workspace_bytes(W.with_(W.TOY, kv_window=64))
+    ring = 2 * 64 * W.TOY.attn_kv_heads * W.TOY.attn_head_dim * 2
+    assert ring <= win - base <= ring + 4096 + 4 * W.TOY.attn_q_heads * (W.TOY.attn_head_dim + 2) * 4
 
 
 @pytest.mark.parametrize("kw", [
@@ -46,6 +56,8 @@ def test_valid_configs(shape):
     dict(gdn_head_dim=96), dict(attn_head_dim=128), dict(attn_q_heads=6, attn_kv_heads=4),
     dict(gdn_v_heads=6, gdn_qk_heads=4), dict(max_verify=5), dict(max_verify=0), dict(rms_eps=0.0),
     dict(vocab=-1), dict(max_ctx=0), dict(attn_q_heads=3, attn_kv_heads=1),
+    dict(kv_window=-1), dict(kv_window=2000), dict(kv_window=16, max_batch=2),
+    dict(kv_window=16, draft_vocab=64),
 ])
 def test_invalid_configs(kw):
     c = _cfg(W.TOY, **kw)
