@@ -621,17 +621,20 @@ int enqueue_block(aw4_model* m, LayerBufs& b, float* x, const int32_t* posp, int
             aa.d = c->attn_head_dim;
             aa.nsplit = m->nsplit;
             if (b.kw) {
-                // recent window: the token's codes and fp16 entry first, then
-                // the sweep before the window and the window's own sweep
+                // recent window: the sweep before the window, then the
+                // window's sweep, which appends the token (codes and fp16
+                // ring entry) first
                 aa.win = c->kv_window;
                 aa.nsplit_w = m->nsplit_w;
                 aa.kw = b.kw;
                 aa.vw = b.vw;
                 aa.append = 0;
-                HIPCHK(m, launch_append(aa, s));
+                HIPCHK(m, launch_attn(aa, s));
+                aa.append = 1;
+                HIPCHK(m, launch_attn_win(aa, s));
+            } else {
+                HIPCHK(m, launch_attn(aa, s));
             }
-            HIPCHK(m, launch_attn(aa, s));
-            if (b.kw) HIPCHK(m, launch_attn_win(aa, s));
             CombineArgs ca{pos_offset, 1, 0, m->part, m->proj, m->signs, posp, m->abuf, aa.prow, c->attn_q_heads,
                            c->attn_kv_heads, c->attn_head_dim, m->nsplit, 0, aa.win, aa.nsplit_w};
             HIPCHK(m, launch_combine(ca, s));

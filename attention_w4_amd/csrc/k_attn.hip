@@ -692,16 +692,37 @@ __global__ __launch_bounds__(64) void k_append(AttnArgs a) {
 // (position t at slot t % win, [nkv][win][D]), split over gridDim.x
 // workgroups whose partial rows go to slots nsplit + split, in the layout the
 // quantised sweep uses, so that k_combine merges both.  Lane l holds dims
-// P l .. P l + P - 1 of the G query heads and of each position's key and value;
-// a wave takes every kWinWaves-th position of the split and keeps an online
-// softmax per head; the waves merge through LDS.
+// P l .. P l + P - 1 of the G query heads and of each position's key and value
+// (a wave's row load is one contiguous 2 D-byte run).  Rounds of
+// kWinWaves x kWinPer positions: each wave requests all of its kWinPer rows
+// before using any, reduces the scores across the wave with DPP moves and
+// keeps an online softmax per head; the waves merge through LDS.
 constexpr int kWinWaves = 8;
+constexpr int kWinPer = 8;
+
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+#define AW4_WDPP(ctrl)                                                                                   \
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), ctrl, 0xF, \
+                                                               0xF, true))
+    AW4_WDPP(0xB1);    // quad_perm [1,0,3,2]
+    AW4_WDPP(0x4E);    // quad_perm [2,3,0,1]
+    AW4_WDPP(0x141);   // row_half_mirror
+    AW4_WDPP(0x140);   // row_mirror
+#undef AW4_WDPP
+    const int iv = __builtin_bit_cast(int, v);
+    return (__builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 0)) +
+            __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 16))) +
+           (__builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 32)) +
+            __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 48)));
+}
 
 template <int D, int G>
 __global__ __launch_bounds__(64 * kWinWaves) void k_attn_win(AttnArgs a) {
     constexpr int P = D / 64;
+    typedef _Float16 hP __attribute__((ext_vector_type(P)));
     __shared__ float mo[kWinWaves][G][D];
     __shared__ float mm[kWinWaves][G], ll[kWinWaves][G];
+    __shared__ uint8_t vq[D];
     const int split = blockIdx.x, j = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int npos = *a.pos + a.pos_offset + 1;
@@ -711,14 +732,23 @@ __global__ __launch_bounds__(64 * kWinWaves) void k_attn_win(AttnArgs a) {
     if (split >= used) return;
     const int t0 = npos - wlen + split * pps;
     const int t1 = min(npos, t0 + pps);
+    // append (a.append): the wave that owns the token's position encodes it
+    // (codes and ring entry) before it reads its rows; no other wave or
+    // workgroup reads that position
+    if (a.append && t1 == npos && w == (npos - 1 - t0) % kWinWaves) {
+        const float* kp = a.proj + 2LL * a.nq * D + (int64_t)j * D;
+        const int64_t wr = ((int64_t)j * a.win + (npos - 1) % a.win) * D;
+        encode_append<D>(kp, kp + (int64_t)a.nkv * D, a.signs, a.kc, a.ks, a.vc, a.vs,
+                         (int64_t)j * a.max_ctx + npos - 1, vq, lane, a.kw + wr, a.vw + wr);
+    }
     const float qscale = 1.0f / sqrtf((float)D);
+    const hP* kb = (const hP*)(a.kw + (int64_t)j * a.win * D) + lane;
+    const hP* vb = (const hP*)(a.vw + (int64_t)j * a.win * D) + lane;
     float q[G][P];
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
         for (int i = 0; i < P; ++i) q[h][i] = a.proj[(int64_t)(j * G + h) * D + P * lane + i] * qscale;
-    const _Float16* kb = a.kw + (int64_t)j * a.win * D + P * lane;
-    const _Float16* vb = a.vw + (int64_t)j * a.win * D + P * lane;
     float m[G], l[G], acc[G][P];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -727,27 +757,45 @@ __global__ __launch_bounds__(64 * kWinWaves) void k_attn_win(AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < P; ++i) acc[h][i] = 0.f;
     }
-    for (int t = t0 + w; t < t1; t += kWinWaves) {
-        const int64_t r = (int64_t)(t % a.win) * D;
-        float kk[P], vv[P];
+    for (int base = t0 + w; base < t1; base += kWinWaves * kWinPer) {
+        // this round's rows, all requested first (a position past the split
+        // re-reads the first one and gets no weight)
+        hP kr[kWinPer], vr[kWinPer];
 #pragma unroll
-        for (int i = 0; i < P; ++i) {
-            kk[i] = (float)kb[r + i];
-            vv[i] = (float)vb[r + i];
+        for (int r = 0; r < kWinPer; ++r) {
+            const int t = base + kWinWaves * r;
+            const int64_t row = (int64_t)((t < t1 ? t : base) % a.win) * (D / P);
+            kr[r] = kb[row];
+            vr[r] = vb[row];
         }
+        // every score of the round first (independent wave reductions), then
+        // one online-softmax update per head
+        float sc[kWinPer][G];
+#pragma unroll
+        for (int r = 0; r < kWinPer; ++r)
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                float sdot = 0.f;
+#pragma unroll
+                for (int i = 0; i < P; ++i) sdot += q[h][i] * (float)kr[r][i];
+                sc[r][h] = base + kWinWaves * r < t1 ? wave_sum_dpp(sdot) : -INFINITY;
+            }
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            float sdot = 0.f;
+            float mn = m[h];
 #pragma unroll
-            for (int i = 0; i < P; ++i) sdot += q[h][i] * kk[i];
+            for (int r = 0; r < kWinPer; ++r) mn = fmaxf(mn, sc[r][h]);
+            const float corr = __expf(m[h] - mn);   // 0 while m = -inf
+            l[h] *= corr;
 #pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) sdot += __shfl_xor(sdot, o, 64);
-            const float mn = fmaxf(m[h], sdot);
-            const float corr = __expf(m[h] - mn);   // 0 on the first position (m = -inf)
-            const float pe = __expf(sdot - mn);
-            l[h] = l[h] * corr + pe;
+            for (int i = 0; i < P; ++i) acc[h][i] *= corr;
 #pragma unroll
-            for (int i = 0; i < P; ++i) acc[h][i] = acc[h][i] * corr + pe * vv[i];
+            for (int r = 0; r < kWinPer; ++r) {
+                const float pe = __expf(sc[r][h] - mn);   // 0 for a dead position
+                l[h] += pe;
+#pragma unroll
+                for (int i = 0; i < P; ++i) acc[h][i] += pe * (float)vr[r][i];
+            }
             m[h] = mn;
         }
     }
@@ -859,7 +907,9 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
     if (a.nt < 1 || a.nq * a.nt > a.prow) return hipErrorInvalidValue;
     // split rows per thread: 16 (D = 256) or 64 (D = 64) rows are in flight
     if (a.d == 256) {
-        if (a.nsplit + a.nsplit_w <= 64) hipLaunchKernelGGL((k_combine<256, 4>), dim3(a.nq * a.nt), dim3(1024), 0, s, a);
+        const int ns = a.nsplit + a.nsplit_w;
+        if (ns <= 64) hipLaunchKernelGGL((k_combine<256, 4>), dim3(a.nq * a.nt), dim3(1024), 0, s, a);
+        else if (ns <= 128) hipLaunchKernelGGL((k_combine<256, 8>), dim3(a.nq * a.nt), dim3(1024), 0, s, a);
         else hipLaunchKernelGGL((k_combine<256, 16>), dim3(a.nq * a.nt), dim3(1024), 0, s, a);
     } else if (a.d == 64) {
         hipLaunchKernelGGL((k_combine<64, 4>), dim3(a.nq * a.nt), dim3(1024), 0, s, a);
