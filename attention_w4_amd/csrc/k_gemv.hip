@@ -339,6 +339,16 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kStreamMaxPer = 10;   // row blocks per wave the pipelined path unrolls
 
+// Two forms of the streaming kernel.  The 27B-shape projections (K = 4096,
+// 5120, 6144: NF = 4, 5, 6) read the input slices from LDS at each use and keep
+// one row block in registers per wave (55-80 VGPRs), so that 4 (NF 4, 6) or 6
+// (NF 5) waves share a SIMD and the wave count, not a deep per-wave pipeline,
+// keeps the loads in flight: measured faster than the register-resident form
+// (2 waves per SIMD, x in registers, a three-deep ring of row blocks) by 2% of
+// a decode step.  Other row lengths keep the register-resident form.
+__host__ __device__ constexpr bool stream_lds_x(int NF) { return NF == 4 || NF == 5 || NF == 6; }
+__host__ __device__ constexpr int stream_simd_waves(int NF) { return NF == 5 ? 6 : stream_lds_x(NF) ? 4 : 2; }
+
 template <int R, int NF>
 struct RowBlock {
     u32x4 c[NF];
@@ -358,13 +368,14 @@ __device__ __forceinline__ void load_block(RowBlock<R, NF>& b, const uint32_t* _
 }
 
 template <int R, int NF, int PRO, int EPI>
-__global__ __launch_bounds__(256, 2) void k_gemv_stream(GemvArgs a) {
+__global__ __launch_bounds__(256, stream_simd_waves(NF)) void k_gemv_stream(GemvArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     float* red = (float*)smem;
     _Float16* xs = (_Float16*)(smem + 64);
     constexpr int G = 64 * NF / R;
     // pipeline the codes across row blocks only while the buffers stay small
-    constexpr bool kPipe = NF <= 8;
+    constexpr bool kPipe = NF <= 8 && !stream_lds_x(NF);
+    constexpr bool kXreg = kPipe;   // the input slices stay in registers
     constexpr int kDepth = 3;
     constexpr int kMaxPer = kStreamMaxPer;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -396,12 +407,12 @@ __global__ __launch_bounds__(256, 2) void k_gemv_stream(GemvArgs a) {
     const uint4* xv = (const uint4*)xs;   // group g: xv[4g .. 4g+3]
     // short rows: this lane's slices of the input stay in registers for every
     // row block (the lane -> group map is the same for all of them)
-    uint4 xr[kPipe ? NF : 1][4];
-    if (kPipe) {
+    uint4 xr[kXreg ? NF : 1][4];
+    if (kXreg) {
 #pragma unroll
         for (int i = 0; i < NF; ++i)
 #pragma unroll
-            for (int k = 0; k < 4; ++k) xr[kPipe ? i : 0][k] = xv[4 * grp_of[i] + k];
+            for (int k = 0; k < 4; ++k) xr[kXreg ? i : 0][k] = xv[4 * grp_of[i] + k];
     }
     const NibK nk;
 
@@ -414,9 +425,9 @@ __global__ __launch_bounds__(256, 2) void k_gemv_stream(GemvArgs a) {
 #pragma unroll
         for (int i = 0; i < NF; ++i) {
             uint4 x0, x1, x2, x3;
-            if (kPipe) {
-                x0 = xr[kPipe ? i : 0][0]; x1 = xr[kPipe ? i : 0][1];
-                x2 = xr[kPipe ? i : 0][2]; x3 = xr[kPipe ? i : 0][3];
+            if (kXreg) {
+                x0 = xr[kXreg ? i : 0][0]; x1 = xr[kXreg ? i : 0][1];
+                x2 = xr[kXreg ? i : 0][2]; x3 = xr[kXreg ? i : 0][3];
             } else {
                 const int g = grp_of[i];
                 x0 = xv[4 * g]; x1 = xv[4 * g + 1]; x2 = xv[4 * g + 2]; x3 = xv[4 * g + 3];
@@ -431,7 +442,7 @@ __global__ __launch_bounds__(256, 2) void k_gemv_stream(GemvArgs a) {
             for (int r = 0; r < R; ++r) acc[r] += row_of[i] == r ? part : 0.f;
             // long rows: split the group loop in two so that the compiler hoists
             // at most half of the LDS reads (16 registers per group)
-            if (!kPipe && i == NF / 2) asm volatile("" ::: "memory");
+            if (!kXreg && i == NF / 2) asm volatile("" ::: "memory");
         }
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[r] = wave_sum_fast(acc[r]);
@@ -1374,10 +1385,11 @@ int stream_grid(int nrb, int max_waves) {
 
 int stream_blocks(int rows, int R, int NF) {
     const int nrb = rows / R;
-    // pipelined shapes: about one workgroup per CU while the ring covers the
-    // rows in at most kStreamMaxPer steps (measured faster than two per CU for
-    // 5-18k rows, and than 8-wave workgroups); the FFN gate/up (17k row
-    // blocks) keeps two per CU
+    // LDS-input form: as many waves as the compiled occupancy holds on 256 CUs
+    // (4 SIMDs each); register-resident form: about one workgroup per CU
+    // while the ring covers the rows in at most kStreamMaxPer steps, two for
+    // more rows; long rows (NF > 8): up to 4096 waves of one block each
+    if (stream_lds_x(NF)) return stream_grid(nrb, 1024 * stream_simd_waves(NF));
     return stream_grid(nrb, NF > 8 ? 4096 : nrb <= 1024 * kStreamMaxPer ? 1024 : 2048);
 }
 

@@ -31,7 +31,7 @@ HBM_PEAK_GBS = 8000.0
 # HBM bytes per launch of the gate/up GEMV from the FETCH_SIZE / WRITE_SIZE
 # counter runs recorded in profiles/hbm_traffic_8k_decode.md, valid only for
 # the kernel source whose sha256 prefix is recorded with them.
-GATEUP_TRAFFIC = {"k_gemv_sha256": "8043a09f9b04bdc9", "bytes": 101212301}
+GATEUP_TRAFFIC = {"k_gemv_sha256": "01c653fb47a7e9d1", "bytes": 100809815}
 
 
 def gateup_traffic():

@@ -297,7 +297,9 @@ int aw4_set_graph(aw4_model* model, int32_t enable);
 
 /* Kernel timing for roofline reports.  Launches one phase of the step `reps`
  * times, cycling through the layers so that consecutive launches stream
- * different weights, between two HIP events on the model's stream, and
+ * different weights, between two HIP events on the model's stream (as one
+ * captured graph when graphs are enabled, as the decode step runs, except
+ * the prefill GEMM phase), and
  * returns the average launch-to-launch duration (microseconds) and the
  * algorithmic work of one launch: the bytes it moves (weights + scales +
  * activations read and written) for the decode phases, the flops (2 M N K) for
