@@ -1474,6 +1474,15 @@ int aw4_decode_batch(aw4_model* m, const int32_t* host_tokens, int32_t B, int32_
     if (c->vocab <= 0) return fail(m, AW4_E_STATE, "decode_batch needs a vocabulary");
     if (B < 1 || B > m->max_batch) return fail(m, AW4_E_INVAL, "batch must be in [1, max_batch]");
     if (c->kv_window > 0) return fail(m, AW4_E_INVAL, "batch decode does not read a recent window");
+    if (B == 1 && m->seq == 0) {
+        // one sequence, the selected one: the single-token step computes the
+        // same thing with the kernels built for one input vector
+        int rc = aw4_decode_step(m, host_tokens[0], nullptr, host_argmax);
+        if (rc) return rc;
+        m->seq_pos[0] = m->host_pos;
+        m->pend_src = 0;
+        return AW4_OK;
+    }
     m->seq_pos[m->seq] = m->host_pos;
     int32_t tok[4] = {0, 0, 0, 0}, pos[4] = {0, 0, 0, 0};
     for (int b = 0; b < B; ++b) {

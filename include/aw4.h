@@ -335,8 +335,10 @@ int aw4_select_sequence(aw4_model* model, int32_t s);
  * b's position through every layer against that sequence's states and cache,
  * then the output head; host_argmax receives the B greedy tokens (lowest
  * index on ties) and each sequence's position advances by one.  The draft
- * head is not fed.  Synchronous.  Errors: AW4_E_INVAL, AW4_E_TOKEN,
- * AW4_E_CTX_FULL, AW4_E_STATE (vocab 0). */
+ * head is not fed.  B = 1 with sequence 0 selected runs the single-token
+ * step (aw4_decode_step), whose kernels are built for one input vector.
+ * Synchronous.  Errors: AW4_E_INVAL, AW4_E_TOKEN, AW4_E_CTX_FULL,
+ * AW4_E_STATE (vocab 0). */
 int aw4_decode_batch(aw4_model* model, const int32_t* host_tokens, int32_t B, int32_t* host_argmax);
 
 /* Committed entries of the draft head's cache; set it after importing that
