@@ -276,10 +276,6 @@ __global__ __launch_bounds__(512, 1) void k_attn(AttnArgs a) {
     // final tile of the range that ends at it.  Only that tile holds the new
     // position, so no other wave waits; the writer's own loads of that tile
     // come after its stores in program order.
-    // The current token is encoded and appended by one wave: the one that
-    // owns the final tile of the range that ends at it.  Only that tile holds
-    // the new position, so no other wave waits; the writer's own loads of that
-    // tile come after its stores in program order.
     auto encode = [&]() {
         const float* kp = a.proj + (int64_t)tb0 * a.sproj + 2LL * a.nq * D + (int64_t)j * D;
         encode_append<D>(kp, kp + (int64_t)a.nkv * D, a.signs, kc, ks, vc, vs, hbase + pos, vq, lane);
