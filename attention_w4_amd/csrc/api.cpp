@@ -1772,6 +1772,52 @@ int aw4_time_phase(aw4_model* m, int32_t phase, int32_t reps, float* avg_us, uin
     // runs them (eager launches of the large grids spent several microseconds
     // each on launch overhead); without graphs, and for the prefill GEMM (1.4 ms
     // a launch), they are launched one by one
+    // The decode GEMV phases are timed in context: each timed launch follows a
+    // launch of the GEMV that precedes it in the decode step (down before
+    // gate/up and before the in-projection, gate/up before down), and a pair
+    // of events inside the graph brackets the timed launch alone.  Back to
+    // back, launches of one kernel ran 10-15% slower than the same kernel
+    // inside the decode step.
+    if (m->use_graph && phase <= AW4_PHASE_MIX_IN) {
+        const int cphase = phase == AW4_PHASE_FFN_DOWN ? AW4_PHASE_FFN_GATE_UP : AW4_PHASE_FFN_DOWN;
+        std::vector<hipEvent_t> ev(2 * (size_t)reps, nullptr);
+        bool ok = true;
+        for (auto& e : ev) ok = ok && hipEventCreate(&e) == hipSuccess;
+        hipGraph_t g = nullptr;
+        hipGraphExec_t gx = nullptr;
+        if (ok) ok = hipStreamBeginCapture(m->stream, hipStreamCaptureModeThreadLocal) == hipSuccess;
+        if (ok) {
+            uint64_t cb = 0;
+            for (int i = 0; i < reps && ok; ++i) {
+                ok = enqueue_phase(m, cphase, (i + L - 1) % L, &cb) == AW4_OK &&
+                     hipEventRecord(ev[2 * i], m->stream) == hipSuccess &&
+                     enqueue_phase(m, phase, i % L, &bytes) == AW4_OK &&
+                     hipEventRecord(ev[2 * i + 1], m->stream) == hipSuccess;
+            }
+            const bool ended = hipStreamEndCapture(m->stream, &g) == hipSuccess;
+            ok = ok && ended && g && hipGraphInstantiate(&gx, g, nullptr, nullptr, 0) == hipSuccess;
+            if (g) (void)hipGraphDestroy(g);
+        }
+        float tot = 0.f;
+        if (ok) ok = hipGraphLaunch(gx, m->stream) == hipSuccess &&   // untimed pass
+                     hipGraphLaunch(gx, m->stream) == hipSuccess && hipStreamSynchronize(m->stream) == hipSuccess;
+        for (int i = 0; i < reps && ok; ++i) {
+            float ms = 0.f;
+            ok = hipEventElapsedTime(&ms, ev[2 * i], ev[2 * i + 1]) == hipSuccess;
+            tot += ms;
+        }
+        if (gx) (void)hipGraphExecDestroy(gx);
+        for (auto& e : ev)
+            if (e) (void)hipEventDestroy(e);
+        (void)hipGetLastError();   // a failed attempt falls back to the timing below
+        if (ok) {
+            (void)hipEventDestroy(e0);
+            (void)hipEventDestroy(e1);
+            *avg_us = tot * 1000.f / (float)reps;
+            *bytes_per_launch = bytes;
+            return AW4_OK;
+        }
+    }
     hipGraphExec_t ge = nullptr;
     if (m->use_graph && phase != AW4_PHASE_PREFILL_GATE_UP) {
         hipGraph_t g = nullptr;

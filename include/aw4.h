@@ -299,7 +299,9 @@ int aw4_set_graph(aw4_model* model, int32_t enable);
  * times, cycling through the layers so that consecutive launches stream
  * different weights, between two HIP events on the model's stream (as one
  * captured graph when graphs are enabled, as the decode step runs, except
- * the prefill GEMM phase), and
+ * the prefill GEMM phase; the three decode GEMV phases are timed in context:
+ * each timed launch follows a launch of the GEMV that precedes it in the
+ * step, with events inside the graph around the timed launch alone), and
  * returns the average launch-to-launch duration (microseconds) and the
  * algorithmic work of one launch: the bytes it moves (weights + scales +
  * activations read and written) for the decode phases, the flops (2 M N K) for
