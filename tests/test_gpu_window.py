@@ -199,3 +199,20 @@ def test_window_rejects_paths_without_it(aw4):
     with pytest.raises(aw4.AW4Error):
         gm.decode_batch([1])
     gm.close()
+
+
+def test_window_graph_equals_eager(aw4):
+    """The decode step with a window, replayed from its captured graph, gives
+    the tokens and hidden state of the same steps launched kernel by kernel."""
+    shape = W.with_(W.TOY, kv_window=12)
+    _say("case: toy stack, window 12, graph vs eager, 24 prompt + 24 greedy")
+    prompt = synth.tokens(24, shape.vocab, 5)
+    out = []
+    for graph in (True, False):
+        gm = _gpu_model(aw4, shape, 5, graph=graph)
+        gm.prefill(prompt[:-1])
+        toks = gm.decode_greedy(int(prompt[-1]), 24)
+        out.append((list(toks), gm.read_hidden()))
+        gm.close()
+    assert out[0][0] == out[1][0]
+    assert np.array_equal(out[0][1], out[1][1])
