@@ -2,7 +2,8 @@
  * aw4.h - C ABI of the MI355X (gfx950) batch-1 decode library for a hybrid
  * Gated DeltaNet / gated-attention language model with 4-bit weights.
  *
- * What the library computes (readings of the pages are listed in the design doc):
+ * What the library computes (where the pages are silent, the plainest reading
+ * is taken and stated where it applies):
  *  - Decode is bandwidth-bound: every token streams all weights from memory
  *    (page 5, bs178.com llamAmpere article, "为什么它真能这么快" point 二;
  *    page 3 "Qwen3.8-27B 實測", section "部署前必知").

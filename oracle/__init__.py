@@ -6,8 +6,9 @@ aw4_oracle.c is compiled with gcc and driven through ctypes here; brute.py is
 an independent numpy implementation for tiny shapes; accept.py holds the
 speculative-decoding acceptance rule.
 
-Precision and formats are described in aw4_oracle.c.  Parity status per
-function is recorded in DESIGN.md ("parity pins").
+Precision and formats are described in aw4_oracle.c.  Each function is
+pinned by CPU tests (tests/test_oracle_*.py) against values the pages and the
+mathematics fix, not against itself.
 """
 import ctypes
 import os

@@ -7,7 +7,7 @@ probability of that token and q the draft head's; the result has exactly the
 target distribution.  The older rule the same passage mentions, keeping a draft
 only when it equals the target's top choice, is the temperature-0 case here.
 
-Readings (DESIGN.md): p_j = softmax(L_j / T); strict "<" against the uniform;
+Readings where the pages are silent: p_j = softmax(L_j / T); strict "<" against the uniform;
 on the first rejection one token is drawn from max(0, p_j - q_j) renormalised
 (from p_j if that is all zero) by inverse CDF in index order with the last
 uniform; if every draft is kept a bonus token is drawn from p_k the same way.

@@ -4,8 +4,8 @@
  * tests, the smoke check and the benchmark's CPU-baseline leg may call it;
  * the product library never does, and the two share no code.
  *
- * What it computes follows the reference pages and the readings recorded in
- * the design doc:
+ * What it computes follows the reference pages, with the plainest reading
+ * taken where they are silent (stated where each applies):
  *  - dense decode, every token runs every layer (page 1, dcwnkz.com estimate,
  *    opening section; page 3 "Qwen3.8-27B 實測", section "部署前必知");
  *  - 48 Gated DeltaNet + 16 full-attention layers (page 3, "部署前必知";

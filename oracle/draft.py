@@ -8,7 +8,7 @@ the full vocabulary.  This module mirrors, on the oracle model, the order in
 which the library feeds the draft head; the arithmetic of one draft step is
 or_draft_step in aw4_oracle.c.
 
-Readings (listed in DESIGN.md):
+Readings where the pages are silent:
   - the draft head's cache gets one entry per committed position r whose next
     token x_{r+1} is known, built from (target hidden h_r, x_{r+1}); prefill
     feeds every prompt position, a verify pass leaves its accepted positions

@@ -4,7 +4,7 @@ Shapes follow the hybrid stack the reference pages discuss (a dense 27B-class
 model with 48 Gated DeltaNet layers and 16 gated-attention layers, vocabulary
 about 248K; page 3 "Qwen3.8-27B 實測", section "部署前必知", and page 5, the
 bs178.com translation of the llamAmpere post, section "为什么它真能这么快"
-point 一).  Sizes the pages leave open are fixed here and listed in the design doc.
+point 一).  Sizes the pages leave open are fixed here.
 
 This module holds no arithmetic of the decode step.
 """
