@@ -99,6 +99,51 @@ def test_codec_brute_agrees():
         assert np.array_equal(np.array(ss, np.uint16), bs.ravel())
 
 
+def _pack_nibbles_by_hand(c):
+    """logical W4 bytes of integer codes [rows][K]: element 2i in the low
+    nibble of byte i, element 2i+1 in the high nibble, nibble = code + 8"""
+    out = np.zeros((c.shape[0], c.shape[1] // 2), np.uint8)
+    for r in range(c.shape[0]):
+        for i in range(c.shape[1] // 2):
+            out[r, i] = ((int(c[r, 2 * i]) + 8) & 15) | (((int(c[r, 2 * i + 1]) + 8) & 15) << 4)
+    return out
+
+
+def test_row_quantisers_index_every_slot():
+    """oracle.quant_w4 / quant_i8 on a 48 x 256 matrix (8 groups per row) equal
+    numpy's group reshape of the same matrix (brute.quant) packed by hand, slot
+    by slot.  Every (row, group) gets its own magnitude, so a scale or a code
+    written at another (row, group) slot changes a value and fails."""
+    rng = np.random.default_rng(7)
+    rows, cols = 48, 256
+    G = cols // 32
+    mag = (1.0 + np.arange(rows * G, dtype=np.float64)).reshape(rows, G) * 1e-3
+    w = rng.uniform(-0.9, 0.9, (rows, cols)) * np.repeat(mag, 32, axis=1)
+    # one element of each group at +-mag: that group's amax, so its scale is known
+    peak = rng.integers(0, 32, (rows, G))
+    for r in range(rows):
+        for g in range(G):
+            w[r, 32 * g + peak[r, g]] = mag[r, g] * (1 if (r + g) % 2 else -1)
+    w = w.astype(np.float32)
+    # every scale distinct: the slot of each one is checked, not just its value
+    bc7, bs7 = brute.quant(w, 7)
+    assert len(np.unique(bs7)) == rows * G
+    codes, scales = oracle.quant_w4(w)
+    assert scales.shape == (rows, G) and codes.shape == (rows, cols // 2)
+    assert np.array_equal(scales, bs7)
+    assert np.array_equal(codes, _pack_nibbles_by_hand(bc7))
+    # the packed codes read back (brute dequant) within half a step of the input
+    deq = brute.dequant_w4(codes, scales)
+    step = np.repeat(brute.f16(bs7), 32, axis=1)
+    assert np.all(np.abs(deq - w) <= 0.5 * step * (1 + 1e-6) + 1e-12)
+    bc127, bs127 = brute.quant(w, 127)
+    c8, s8 = oracle.quant_i8(w)
+    assert np.array_equal(s8, bs127) and np.array_equal(c8, bc127)
+    assert np.all(np.abs(brute.dequant_i8(c8, s8) - w) <= 0.5 * np.repeat(brute.f16(bs127), 32, axis=1) * (1 + 1e-6))
+    # a transposed operand (rows and groups swapped) is not what the oracle wrote
+    assert not np.array_equal(oracle.quant_w4(np.ascontiguousarray(w[::-1]))[1], bs7)
+
+
 def test_w4_packing_hand_worked():
     g = GOLD["w4_packing"]
     codes = np.zeros(32, np.int64)
