@@ -89,6 +89,8 @@ _SIGS = {
     "aw4_import_state_kv": [_vp, _i32, _i32, _vp, _vp, _vp, _vp],
     "aw4_export_state_win": [_vp, _i32, _vp, _vp],
     "aw4_import_state_win": [_vp, _i32, _vp, _vp],
+    "aw4_check_blob": [ctypes.c_void_p, _vp, _u64],
+    "aw4_test_fail_hip_call": [_i32],
 }
 
 
@@ -132,6 +134,25 @@ def workspace_bytes(shape):
 def _ptr(a):
     """host numpy array -> void*"""
     return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _blob_ptr(blob):
+    """(pointer, length) of a bytes-like blob, without a copy"""
+    import numpy as np
+    a = np.frombuffer(blob, np.uint8) if len(blob) else np.zeros(1, np.uint8)
+    return _ptr(a), len(blob), a
+
+
+def check_blob(shape_or_cfg, blob):
+    """aw4_check_blob: 0 for a blob that loads into this config, else the status"""
+    c = shape_or_cfg if isinstance(shape_or_cfg, Config) else Config.from_shape(shape_or_cfg)
+    p, n, _keep = _blob_ptr(blob)
+    return lib().aw4_check_blob(ctypes.byref(c), p, n)
+
+
+def test_fail_hip_call(n):
+    """arm (n >= 1) or disarm (n <= 0) the library's HIP failure injection"""
+    lib().aw4_test_fail_hip_call(int(n))
 
 
 class Model:
@@ -212,9 +233,10 @@ class Model:
         v = np.ascontiguousarray(ids, np.int32)
         self._rc(lib().aw4_set_draft_map(self.h, _ptr(v), len(v)), "set_draft_map")
 
-    def load_weights(self, blob: bytes):
-        buf = ctypes.create_string_buffer(blob, len(blob))
-        self._rc(lib().aw4_load_weights(self.h, buf, len(blob)), "load_weights")
+    def load_weights(self, blob):
+        """blob: bytes-like in the aw4_load_weights format (attention_w4_amd.blob)"""
+        p, n, _keep = _blob_ptr(blob)
+        self._rc(lib().aw4_load_weights(self.h, p, n), "load_weights")
 
     # ---------------------------------------------------------------- decode
     def reset(self):

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 #include <cmath>
 #include <cstdio>
@@ -41,6 +42,14 @@ struct LayerBufs {
     uint16_t* vs = nullptr;
     _Float16* kw = nullptr;     // recent window (kv_window > 0): fp16 keys [nkv][W][d], slot t % W
     _Float16* vw = nullptr;     // fp16 rotated values, same slots
+};
+
+// one tensor of a config and the rows of it that have been set
+struct TensorSlot {
+    int layer = 0, kind = 0;
+    int64_t rows = 0;
+    std::vector<bool> done;
+    int64_t ndone = 0;
 };
 
 constexpr int kSweepRows = 4;   // most tokens one attention sweep takes (verify_k has at most 4)
@@ -145,6 +154,16 @@ struct aw4_model {
     int seq = 0;
     int32_t seq_pos[4] = {0, 0, 0, 0};
     int32_t seq_dpos[4] = {0, 0, 0, 0};
+    // which tensors have been given values (quantize/load/set calls and
+    // aw4_load_weights): the model computes only once every tensor of its
+    // config is complete
+    std::vector<TensorSlot> slots;
+    int slots_missing = 0;
+    // recent window: false for a layer whose ring may hold entries of positions
+    // after the current one (set_pos moved back; aw4_import_state_win refreshes
+    // it); win_imported: the ring was imported since the last decode call, so it
+    // describes whatever position the caller sets next
+    std::vector<bool> win_fresh, win_imported;
     bool use_graph = true;
     hipGraphExec_t g_head = nullptr;
     hipGraphExec_t g_nohead = nullptr;
@@ -161,7 +180,29 @@ int fail(aw4_model* m, int code, const std::string& msg) {
     return code;
 }
 
+// Failure injection for tests of the error path: when armed with n >= 1, the
+// n-th checked HIP call from then on reports hipErrorUnknown (the call itself
+// has run), once.  Calls that open a stream capture are not counted, so an
+// injected failure never leaves a capture open.
+std::atomic<int> g_fail_countdown{0};
+
+hipError_t counted(hipError_t e) {
+    if (e != hipSuccess) return e;
+    int n = g_fail_countdown.load(std::memory_order_relaxed);
+    while (n > 0 && !g_fail_countdown.compare_exchange_weak(n, n - 1, std::memory_order_relaxed)) {
+    }
+    return n == 1 ? hipErrorUnknown : hipSuccess;
+}
+
 #define HIPCHK(m, expr)                                                                        \
+    do {                                                                                       \
+        hipError_t e_ = counted(expr);                                                         \
+        if (e_ != hipSuccess)                                                                  \
+            return fail((m), AW4_E_HIP, std::string(#expr) + ": " + hipGetErrorString(e_));    \
+    } while (0)
+
+// the same without the injection count (calls that begin a stream capture)
+#define HIPCHK_RAW(m, expr)                                                                    \
     do {                                                                                       \
         hipError_t e_ = (expr);                                                                \
         if (e_ != hipSuccess)                                                                  \
@@ -201,12 +242,13 @@ int win_splits(int win) {
 
 // Splits of the attention grid per kv head: one workgroup per compute unit in
 // one round (256 units on gfx950; aw4_create lowers it to the device's count),
-// never more than there are 16-position tiles of capacity.
-int nsplit_for(int max_ctx, int nkv, int cus = 256) {
+// never more than there are 16-position tiles of capacity.  The combine merges
+// at most 256 split slots per row, the recent window's included.
+int nsplit_for(int max_ctx, int nkv, int nsplit_w, int cus = 256) {
     int n = cus / (nkv > 0 ? nkv : 1);
     const int tiles = (max_ctx + 15) / 16;
     if (n > tiles) n = tiles;
-    if (n > 256) n = 256;
+    if (n > 256 - nsplit_w) n = 256 - nsplit_w;
     if (n < 1) n = 1;
     return n;
 }
@@ -315,8 +357,8 @@ uint64_t plan_layout(const aw4_config* c, aw4_model* m, uint8_t* base) {
     // (hlen also sizes the per-token FFN buffers of the verify pass)
     _Float16* hbuf = p.take<_Float16>((uint64_t)hlen * 2);
     _Float16* abuf = p.take<_Float16>((uint64_t)(has_a || dh ? c->attn_q_heads * c->attn_head_dim : 1) * 2);
-    const int nsplit = nsplit_for(c->max_ctx, c->attn_kv_heads);
     const int nsplit_w = c->kv_window > 0 ? win_splits(c->kv_window) : 0;
+    const int nsplit = nsplit_for(c->max_ctx, c->attn_kv_heads, nsplit_w);
     // split partials: one row per (token of a sweep, q head), up to 4 tokens,
     // nsplit slots (+ nsplit_w for the recent window) each
     float* part = p.take<float>((uint64_t)(has_a || dh ? kSweepRows * c->attn_q_heads : 1) * (nsplit + nsplit_w) *
@@ -561,6 +603,228 @@ int mat_ref(aw4_model* m, int layer, int kind, MatRef* r) {
         case AW4_T_FFN_UP: *r = {b.w_gu + H / 8, nullptr, b.s_gu + H / 32, F, H, 2}; break;
         case AW4_T_FFN_DOWN: *r = {b.w_down, nullptr, b.s_down, H, F, 1}; break;
     }
+    return AW4_OK;
+}
+
+// rows x cols of tensor (layer, kind) of config c (vectors: 1 x n); false
+// when the config has no such tensor.  Layer -1 holds the global tensors,
+// layer n_layers the draft head's (draft_vocab > 0).
+bool cfg_tensor_shape(const aw4_config* c, int layer, int kind, int64_t* rows, int64_t* cols) {
+    const int64_t H = c->hidden, F = c->ffn;
+    const bool dl = c->draft_vocab > 0 && layer == c->n_layers;
+    const bool ll = layer >= 0 && layer < c->n_layers;
+    const char t = ll ? c->layer_pattern[layer] : dl ? 'A' : 0;
+    const bool glob = layer == -1;
+    int64_t r = -1, k = -1;
+    switch (kind) {
+        case AW4_T_MIX_IN: if (t) { r = mix_in_rows(c, t); k = H; } break;
+        case AW4_T_MIX_OUT: if (t) { r = H; k = mix_out_cols(c, t); } break;
+        case AW4_T_FFN_GATE:
+        case AW4_T_FFN_UP: if (t) { r = F; k = H; } break;
+        case AW4_T_FFN_DOWN: if (t) { r = H; k = F; } break;
+        case AW4_T_LM_HEAD: if (glob && c->vocab > 0) { r = c->vocab; k = H; } break;
+        case AW4_T_NORM_MIX:
+        case AW4_T_NORM_FFN: if (t) { r = 1; k = H; } break;
+        case AW4_T_NORM_GATED: if (ll && t == 'G') { r = 1; k = c->gdn_head_dim; } break;
+        case AW4_T_A_BIAS: if (ll && t == 'G') { r = 1; k = c->gdn_v_heads; } break;
+        case AW4_T_NORM_FINAL: if (glob && c->vocab > 0) { r = 1; k = H; } break;
+        case AW4_T_RHT_SIGNS:
+            if (glob && (strchr(c->layer_pattern, 'A') || c->draft_vocab > 0)) { r = 1; k = c->attn_head_dim; }
+            break;
+        case AW4_T_DRAFT_FUSE: if (dl) { r = H; k = 2 * H; } break;
+        case AW4_T_DRAFT_NORM_EMB:
+        case AW4_T_DRAFT_NORM_HID:
+        case AW4_T_DRAFT_NORM_OUT: if (dl) { r = 1; k = H; } break;
+        case AW4_T_DRAFT_MAP: if (dl) { r = 1; k = c->draft_vocab; } break;
+        default: break;
+    }
+    if (r < 0) return false;
+    *rows = r;
+    *cols = k;
+    return true;
+}
+
+bool is_matrix_kind(int kind) { return (kind >= AW4_T_MIX_IN && kind <= AW4_T_LM_HEAD) || kind == AW4_T_DRAFT_FUSE; }
+
+// every tensor of the config, none of it set yet
+std::vector<TensorSlot> all_slots(const aw4_config* c) {
+    std::vector<TensorSlot> v;
+    for (int layer = -1; layer <= c->n_layers; ++layer)
+        for (int kind = AW4_T_MIX_IN; kind <= AW4_T_DRAFT_MAP; ++kind) {
+            int64_t r, k;
+            if (!cfg_tensor_shape(c, layer, kind, &r, &k)) continue;
+            TensorSlot t;
+            t.layer = layer;
+            t.kind = kind;
+            t.rows = r;
+            t.done.assign((size_t)r, false);
+            v.push_back(std::move(t));
+        }
+    return v;
+}
+
+// rows [r0, r0 + n) of tensor (layer, kind) now hold values
+void mark_rows(aw4_model* m, int layer, int kind, int64_t r0, int64_t n) {
+    for (TensorSlot& t : m->slots) {
+        if (t.layer != layer || t.kind != kind) continue;
+        const bool was = t.ndone == t.rows;
+        for (int64_t r = r0; r < r0 + n && r < t.rows; ++r)
+            if (!t.done[(size_t)r]) {
+                t.done[(size_t)r] = true;
+                ++t.ndone;
+            }
+        if (!was && t.ndone == t.rows) --m->slots_missing;
+        return;
+    }
+}
+
+// AW4_E_STATE until every tensor of the config has been given values
+int need_weights(aw4_model* m) {
+    if (m->slots_missing == 0) return AW4_OK;
+    for (const TensorSlot& t : m->slots)
+        if (t.ndone < t.rows)
+            return fail(m, AW4_E_STATE, "weights not loaded: tensor (layer " + std::to_string(t.layer) + ", kind " +
+                                            std::to_string(t.kind) + ") has " + std::to_string(t.rows - t.ndone) +
+                                            " of " + std::to_string(t.rows) + " rows unset");
+    return AW4_OK;
+}
+
+// a decode call with a recent window needs rings that hold no position after
+// the current one; the call then writes the rings itself
+int need_fresh_window(aw4_model* m) {
+    for (bool f : m->win_fresh)
+        if (!f)
+            return fail(m, AW4_E_STATE, "the position moved back: import every attention layer's recent-window "
+                                        "ring (aw4_import_state_win) before decoding");
+    m->win_imported.assign(m->win_imported.size(), false);
+    return AW4_OK;
+}
+
+// ---------------------------------------------------------------- weight blob
+// Layout (little-endian): "AW4W", uint32 version 4, the shape fields of the
+// config as int32 (hidden, ffn, vocab, n_layers, gdn_qk_heads, gdn_v_heads,
+// gdn_head_dim, attn_q_heads, attn_kv_heads, attn_head_dim, group,
+// draft_vocab), layer_pattern as 128 bytes (NUL padded), uint32 tensor count,
+// then per tensor int32 layer, int32 kind, int64 rows, int64 cols, uint64
+// payload bytes and the payload: matrices their logical codes then fp16 scale
+// bits, vectors n fp32 values, the draft map n int32 ids.
+constexpr uint32_t kBlobVersion = 4;
+constexpr int kBlobShapeFields = 12;
+constexpr uint64_t kBlobHeader = 4 + 4 + 4 * kBlobShapeFields + 128 + 4;
+
+struct BlobTensor {
+    int32_t layer, kind;
+    int64_t rows, cols;
+    const uint8_t* payload;
+};
+
+void blob_shape_fields(const aw4_config* c, int32_t* f) {
+    const int32_t v[kBlobShapeFields] = {c->hidden, c->ffn, c->vocab, c->n_layers, c->gdn_qk_heads, c->gdn_v_heads,
+                                         c->gdn_head_dim, c->attn_q_heads, c->attn_kv_heads, c->attn_head_dim,
+                                         c->group, c->draft_vocab};
+    memcpy(f, v, sizeof(v));
+}
+
+bool f16_bits_ok(uint16_t b) { return (b & 0x8000u) == 0 && (b & 0x7C00u) != 0x7C00u; }   // finite, not negative
+
+// Checks a blob against config c (pure host: nothing is read beyond
+// [p, p + bytes) and nothing is enqueued).  With apply set, calls it for every
+// tensor of a blob already checked.  AW4_E_FORMAT with *why on the first fault.
+template <class F>
+int walk_blob(const aw4_config* c, const uint8_t* p, uint64_t bytes, std::string* why, F&& apply) {
+    auto bad = [&](const std::string& w) {
+        *why = w;
+        return AW4_E_FORMAT;
+    };
+    const uint8_t* end = p + bytes;
+    auto left = [&]() { return (uint64_t)(end - p); };
+    if (bytes < kBlobHeader) return bad("blob shorter than its header");
+    if (memcmp(p, "AW4W", 4) != 0) return bad("bad magic");
+    uint32_t ver;
+    memcpy(&ver, p + 4, 4);
+    if (ver != kBlobVersion) return bad("unsupported blob version " + std::to_string(ver));
+    int32_t f[kBlobShapeFields], want[kBlobShapeFields];
+    memcpy(f, p + 8, sizeof(f));
+    blob_shape_fields(c, want);
+    static const char* names[kBlobShapeFields] = {"hidden", "ffn", "vocab", "n_layers", "gdn_qk_heads",
+                                                   "gdn_v_heads", "gdn_head_dim", "attn_q_heads", "attn_kv_heads",
+                                                   "attn_head_dim", "group", "draft_vocab"};
+    for (int i = 0; i < kBlobShapeFields; ++i)
+        if (f[i] != want[i])
+            return bad(std::string("blob was made for another config: ") + names[i] + " " + std::to_string(f[i]) +
+                       " != " + std::to_string(want[i]));
+    char pat[129] = {0};
+    memcpy(pat, p + 8 + 4 * kBlobShapeFields, 128);
+    if (strncmp(pat, c->layer_pattern, 128) != 0) return bad("blob was made for another config: layer_pattern");
+    uint32_t count;
+    memcpy(&count, p + kBlobHeader - 4, 4);
+    p += kBlobHeader;
+    std::vector<std::pair<int, int>> seen;
+    for (uint32_t t = 0; t < count; ++t) {
+        if (left() < 32) return bad("truncated tensor header " + std::to_string(t));
+        BlobTensor bt;
+        uint64_t nb;
+        memcpy(&bt.layer, p, 4);
+        memcpy(&bt.kind, p + 4, 4);
+        memcpy(&bt.rows, p + 8, 8);
+        memcpy(&bt.cols, p + 16, 8);
+        memcpy(&nb, p + 24, 8);
+        p += 32;
+        const std::string tn = "tensor (layer " + std::to_string(bt.layer) + ", kind " + std::to_string(bt.kind) + ")";
+        int64_t er = 0, ec = 0;
+        if (!cfg_tensor_shape(c, bt.layer, bt.kind, &er, &ec)) return bad(tn + " is not part of the config");
+        if (er != bt.rows || ec != bt.cols) return bad(tn + " has the wrong shape");
+        for (auto& s2 : seen)
+            if (s2.first == bt.layer && s2.second == bt.kind) return bad(tn + " appears twice");
+        seen.emplace_back(bt.layer, bt.kind);
+        uint64_t want_nb;
+        if (is_matrix_kind(bt.kind))
+            want_nb = (uint64_t)bt.rows * bt.cols / (bt.kind == AW4_T_LM_HEAD ? 1 : 2) + (uint64_t)bt.rows * (bt.cols / 32) * 2;
+        else
+            want_nb = (uint64_t)bt.cols * 4;
+        if (nb != want_nb) return bad(tn + " payload size mismatch");
+        if (left() < nb) return bad(tn + " payload truncated");
+        bt.payload = p;
+        constexpr bool kCheck = std::is_same_v<std::decay_t<F>, std::nullptr_t>;
+        if constexpr (kCheck) {
+            // value checks: codes inside the codec's range, scales finite and
+            // not negative, signs +-1, finite vectors, a valid map
+            if (is_matrix_kind(bt.kind)) {
+                const uint64_t cb = nb - (uint64_t)bt.rows * (bt.cols / 32) * 2;
+                if (bt.kind == AW4_T_LM_HEAD) {
+                    for (uint64_t i = 0; i < cb; ++i)
+                        if (p[i] == 0x80) return bad(tn + " holds int8 code -128 (outside -127..127)");
+                } else {
+                    for (uint64_t i = 0; i < cb; ++i)
+                        if ((p[i] & 15) == 0 || (p[i] >> 4) == 0) return bad(tn + " holds W4 code -8 (outside -7..7)");
+                }
+                for (uint64_t i = cb; i < nb; i += 2) {
+                    uint16_t b;
+                    memcpy(&b, p + i, 2);
+                    if (!f16_bits_ok(b)) return bad(tn + " holds a negative or non-finite scale");
+                }
+            } else if (bt.kind == AW4_T_DRAFT_MAP) {
+                std::vector<int32_t> ids((size_t)bt.cols);
+                memcpy(ids.data(), p, (size_t)nb);
+                std::sort(ids.begin(), ids.end());
+                for (size_t i = 0; i < ids.size(); ++i)
+                    if (ids[i] < 0 || ids[i] >= c->vocab || (i && ids[i] == ids[i - 1]))
+                        return bad(tn + " ids must be distinct and in [0, vocab)");
+            } else {
+                for (int64_t i = 0; i < bt.cols; ++i) {
+                    float v;
+                    memcpy(&v, p + 4 * i, 4);
+                    if (!std::isfinite(v)) return bad(tn + " holds a non-finite value");
+                    if (bt.kind == AW4_T_RHT_SIGNS && v != 1.0f && v != -1.0f) return bad(tn + " signs must be +-1");
+                }
+            }
+        } else {
+            const int rc = apply(bt);
+            if (rc) return rc;
+        }
+        p += nb;
+    }
+    if (p != end) return bad("trailing bytes after the last tensor");
     return AW4_OK;
 }
 
@@ -1082,7 +1346,7 @@ int run_step(aw4_model* m, bool head) {
     hipGraphExec_t* ge = head ? &m->g_head : &m->g_nohead;
     if (!*ge) {
         hipGraph_t g = nullptr;
-        HIPCHK(m, hipStreamBeginCapture(m->stream, hipStreamCaptureModeThreadLocal));
+        HIPCHK_RAW(m, hipStreamBeginCapture(m->stream, hipStreamCaptureModeThreadLocal));
         int rc = enqueue_step(m, head);
         hipError_t e = hipStreamEndCapture(m->stream, &g);
         if (rc) {
@@ -1193,7 +1457,12 @@ int aw4_create(const aw4_config* cfg, void* dev_arena, uint64_t arena_bytes, voi
     m->arena_bytes = arena_bytes;
     m->stream = (hipStream_t)hip_stream;
     plan_layout(cfg, m, m->arena);
-    m->nsplit = nsplit_for(cfg->max_ctx, cfg->attn_kv_heads, prop.multiProcessorCount < 256 ? prop.multiProcessorCount : 256);
+    m->slots = all_slots(cfg);
+    m->slots_missing = (int)m->slots.size();
+    m->win_fresh.assign((size_t)cfg->n_layers, true);
+    m->win_imported.assign((size_t)cfg->n_layers, false);
+    m->nsplit = nsplit_for(cfg->max_ctx, cfg->attn_kv_heads, m->nsplit_w,
+                           prop.multiProcessorCount < 256 ? prop.multiProcessorCount : 256);
     // zero everything once (weights included) so unused tensors are defined
     if (launch_fill_zero(m->arena, need & ~uint64_t(3), m->stream) != hipSuccess) {
         delete m;
@@ -1212,33 +1481,7 @@ void aw4_destroy(aw4_model* m) {
 int aw4_tensor_shape(const aw4_model* mc, int32_t layer, int32_t kind, int64_t* rows, int64_t* cols) {
     aw4_model* m = const_cast<aw4_model*>(mc);
     if (check_model(m) || !rows || !cols) return AW4_E_INVAL;
-    const aw4_config* c = &m->cfg;
-    if ((kind >= 0 && kind <= 5) || kind == AW4_T_DRAFT_FUSE) {
-        MatRef r;
-        int rc = mat_ref(m, layer, kind, &r);
-        if (rc) return rc;
-        *rows = r.rows;
-        *cols = r.cols;
-        return AW4_OK;
-    }
-    int64_t n = -1;
-    if (kind == AW4_T_NORM_FINAL && layer == -1 && c->vocab > 0) n = c->hidden;
-    if (kind == AW4_T_RHT_SIGNS && layer == -1 && strchr(c->layer_pattern, 'A')) n = c->attn_head_dim;
-    if (layer >= 0 && layer < c->n_layers) {
-        const char t = c->layer_pattern[layer];
-        if (kind == AW4_T_NORM_MIX || kind == AW4_T_NORM_FFN) n = c->hidden;
-        if (kind == AW4_T_NORM_GATED && t == 'G') n = c->gdn_head_dim;
-        if (kind == AW4_T_A_BIAS && t == 'G') n = c->gdn_v_heads;
-    }
-    if (c->draft_vocab > 0 && layer == c->n_layers) {
-        if (kind == AW4_T_NORM_MIX || kind == AW4_T_NORM_FFN || kind == AW4_T_DRAFT_NORM_EMB ||
-            kind == AW4_T_DRAFT_NORM_HID || kind == AW4_T_DRAFT_NORM_OUT)
-            n = c->hidden;
-        if (kind == AW4_T_DRAFT_MAP) n = c->draft_vocab;
-    }
-    if (n < 0) return fail(m, AW4_E_INVAL, "no such tensor");
-    *rows = 1;
-    *cols = n;
+    if (!cfg_tensor_shape(&m->cfg, layer, kind, rows, cols)) return fail(m, AW4_E_INVAL, "no such tensor");
     return AW4_OK;
 }
 
@@ -1255,6 +1498,7 @@ int aw4_quantize_tensor(aw4_model* m, int32_t layer, int32_t kind, int64_t row0,
         HIPCHK(m, launch_quant_w4(src, nrows, r.cols, r.w4 + row0 * r.row_stride * (r.cols / 8),
                                   r.scales + row0 * r.row_stride * (r.cols / 32), r.row_stride, m->stream));
     }
+    mark_rows(m, layer, kind, row0, nrows);
     drop_graphs(m);
     return AW4_OK;
 }
@@ -1269,9 +1513,9 @@ int aw4_load_tensor(aw4_model* m, int32_t layer, int32_t kind, const void* host_
     if (r.i8) {
         HIPCHK(m, hipMemcpy(r.i8, host_codes, (size_t)(r.rows * r.cols), hipMemcpyHostToDevice));
         HIPCHK(m, hipMemcpy(r.scales, host_scales, (size_t)(r.rows * G * 2), hipMemcpyHostToDevice));
+        mark_rows(m, layer, kind, 0, r.rows);
         return AW4_OK;
     }
-    std::vector<uint32_t> row(r.cols / 8);
     const uint8_t* src = (const uint8_t*)host_codes;
     // pack on the host, copy row by row into the (possibly interleaved) GPU rows
     std::vector<uint32_t> buf((size_t)(r.rows * (r.cols / 8)));
@@ -1280,6 +1524,7 @@ int aw4_load_tensor(aw4_model* m, int32_t layer, int32_t kind, const void* host_
                           (size_t)(r.cols / 2), (size_t)r.rows, hipMemcpyHostToDevice));
     HIPCHK(m, hipMemcpy2D(r.scales, (size_t)(r.row_stride * G * 2), host_scales, (size_t)(G * 2), (size_t)(G * 2),
                           (size_t)r.rows, hipMemcpyHostToDevice));
+    mark_rows(m, layer, kind, 0, r.rows);
     drop_graphs(m);
     return AW4_OK;
 }
@@ -1329,6 +1574,7 @@ int aw4_set_vector(aw4_model* m, int32_t layer, int32_t kind, const float* vals,
     }
     HIPCHK(m, hipStreamSynchronize(m->stream));
     HIPCHK(m, hipMemcpy(dst, vals, (size_t)n * 4, hipMemcpyHostToDevice));
+    mark_rows(m, layer, kind, 0, 1);
     return AW4_OK;
 }
 
@@ -1348,73 +1594,43 @@ int aw4_set_draft_map(aw4_model* m, const int32_t* ids, int32_t n) {
     HIPCHK(m, hipMemcpy(m->dmap, sorted.data(), (size_t)n * 4, hipMemcpyHostToDevice));
     HIPCHK(m, hipMemcpy(m->drmap, rmap.data(), rmap.size() * 4, hipMemcpyHostToDevice));
     m->map_set = true;
+    mark_rows(m, c->n_layers, AW4_T_DRAFT_MAP, 0, 1);
     return AW4_OK;
 }
 
-int aw4_load_weights(aw4_model* m, const void* blob, uint64_t bytes) {
-    if (check_model(m) || !blob) return AW4_E_INVAL;
-    const uint8_t* p = (const uint8_t*)blob;
-    const uint8_t* end = p + bytes;
-    auto need = [&](uint64_t n) { return (uint64_t)(end - p) >= n; };
-    if (!need(4 + 4 + sizeof(aw4_config) + 4) || memcmp(p, "AW4W", 4) != 0)
-        return fail(m, AW4_E_FORMAT, "bad magic or truncated header");
-    p += 4;
-    uint32_t ver;
-    memcpy(&ver, p, 4);
-    p += 4;
-    if (ver != 3) return fail(m, AW4_E_FORMAT, "unsupported blob version");
-    aw4_config bc;
-    memcpy(&bc, p, sizeof(bc));
-    p += sizeof(bc);
-    const aw4_config* c = &m->cfg;
-    if (bc.hidden != c->hidden || bc.ffn != c->ffn || bc.vocab != c->vocab || bc.n_layers != c->n_layers ||
-        bc.gdn_qk_heads != c->gdn_qk_heads || bc.gdn_v_heads != c->gdn_v_heads || bc.gdn_head_dim != c->gdn_head_dim ||
-        bc.attn_q_heads != c->attn_q_heads || bc.attn_kv_heads != c->attn_kv_heads ||
-        bc.attn_head_dim != c->attn_head_dim || bc.group != c->group || bc.draft_vocab != c->draft_vocab ||
-        strncmp(bc.layer_pattern, c->layer_pattern, 128) != 0)
-        return fail(m, AW4_E_FORMAT, "blob was made for another config");
-    uint32_t count;
-    memcpy(&count, p, 4);
-    p += 4;
-    for (uint32_t t = 0; t < count; ++t) {
-        if (!need(32)) return fail(m, AW4_E_FORMAT, "truncated tensor header");
-        int32_t layer, kind;
-        int64_t rows, cols;
-        uint64_t nb;
-        memcpy(&layer, p, 4);
-        memcpy(&kind, p + 4, 4);
-        memcpy(&rows, p + 8, 8);
-        memcpy(&cols, p + 16, 8);
-        memcpy(&nb, p + 24, 8);
-        p += 32;
-        if (!need(nb)) return fail(m, AW4_E_FORMAT, "truncated tensor payload");
-        int64_t er = 0, ec = 0;
-        if (aw4_tensor_shape(m, layer, kind, &er, &ec) || er != rows || ec != cols)
-            return fail(m, AW4_E_FORMAT, "tensor shape does not match the config");
-        int rc;
-        if (kind == AW4_T_DRAFT_MAP) {
-            if (nb != (uint64_t)cols * 4) return fail(m, AW4_E_FORMAT, "map payload size mismatch");
-            std::vector<int32_t> v((size_t)cols);
-            memcpy(v.data(), p, (size_t)nb);
-            rc = aw4_set_draft_map(m, v.data(), (int32_t)cols);
-        } else if (kind <= 5 || kind == AW4_T_DRAFT_FUSE) {
-            const uint64_t cb = kind == AW4_T_LM_HEAD ? (uint64_t)rows * cols : (uint64_t)rows * cols / 2;
-            const uint64_t sb = (uint64_t)rows * (cols / 32) * 2;
-            if (nb != cb + sb) return fail(m, AW4_E_FORMAT, "tensor payload size mismatch");
-            std::vector<uint16_t> sc((size_t)(sb / 2));
-            memcpy(sc.data(), p + cb, (size_t)sb);
-            rc = aw4_load_tensor(m, layer, kind, p, sc.data());
-        } else {
-            if (nb != (uint64_t)cols * 4) return fail(m, AW4_E_FORMAT, "vector payload size mismatch");
-            std::vector<float> v((size_t)cols);
-            memcpy(v.data(), p, (size_t)nb);
-            rc = aw4_set_vector(m, layer, kind, v.data(), (int32_t)cols);
-        }
-        if (rc) return rc == AW4_E_INVAL ? fail(m, AW4_E_FORMAT, "bad tensor: " + m->err) : rc;
-        p += nb;
-    }
-    if (p != end) return fail(m, AW4_E_FORMAT, "trailing bytes after the last tensor");
+int aw4_test_fail_hip_call(int32_t n) {
+    g_fail_countdown.store(n > 0 ? n : 0, std::memory_order_relaxed);
     return AW4_OK;
+}
+
+int aw4_check_blob(const aw4_config* cfg, const void* blob, uint64_t bytes) {
+    if (check_config(cfg) || (!blob && bytes)) return AW4_E_INVAL;
+    std::string why;
+    return walk_blob(cfg, (const uint8_t*)blob, bytes, &why, nullptr);
+}
+
+int aw4_load_weights(aw4_model* m, const void* blob, uint64_t bytes) {
+    if (check_model(m) || (!blob && bytes)) return AW4_E_INVAL;
+    // the whole blob is checked first: a bad one changes nothing
+    std::string why;
+    if (walk_blob(&m->cfg, (const uint8_t*)blob, bytes, &why, nullptr)) return fail(m, AW4_E_FORMAT, why);
+    int rc = walk_blob(&m->cfg, (const uint8_t*)blob, bytes, &why, [&](const BlobTensor& t) -> int {
+        if (t.kind == AW4_T_DRAFT_MAP) {
+            std::vector<int32_t> v((size_t)t.cols);
+            memcpy(v.data(), t.payload, (size_t)t.cols * 4);
+            return aw4_set_draft_map(m, v.data(), (int32_t)t.cols);
+        }
+        if (is_matrix_kind(t.kind)) {
+            const uint64_t cb = t.kind == AW4_T_LM_HEAD ? (uint64_t)(t.rows * t.cols) : (uint64_t)(t.rows * t.cols / 2);
+            std::vector<uint16_t> sc((size_t)(t.rows * (t.cols / 32)));
+            memcpy(sc.data(), t.payload + cb, sc.size() * 2);
+            return aw4_load_tensor(m, t.layer, t.kind, t.payload, sc.data());
+        }
+        std::vector<float> v((size_t)t.cols);
+        memcpy(v.data(), t.payload, (size_t)t.cols * 4);
+        return aw4_set_vector(m, t.layer, t.kind, v.data(), (int32_t)t.cols);
+    });
+    return rc;
 }
 
 int aw4_reset(aw4_model* m) {
@@ -1426,6 +1642,7 @@ int aw4_reset(aw4_model* m) {
     m->host_dpos = 0;
     m->pend_src = 0;
     for (int b = 0; b < 4; ++b) m->seq_pos[b] = m->seq_dpos[b] = 0;
+    m->win_fresh.assign(m->win_fresh.size(), true);
     return AW4_OK;
 }
 
@@ -1446,6 +1663,10 @@ int aw4_set_pos(aw4_model* m, int32_t pos) {
     if (check_model(m)) return AW4_E_INVAL;
     if (pos < 0 || pos > m->cfg.max_ctx) return fail(m, AW4_E_CTX_FULL, "position outside [0, max_ctx]");
     HIPCHK(m, launch_set_ctl(m->ctl, pos, -1, -1, m->stream));
+    // moving back leaves ring slots holding positions after the new one
+    if (m->cfg.kv_window > 0 && pos < m->host_pos)
+        for (int l = 0; l < m->cfg.n_layers; ++l)
+            if (m->L[l].type == 'A' && !m->win_imported[(size_t)l]) m->win_fresh[(size_t)l] = false;
     m->host_pos = pos;
     m->pend_src = 0;
     return AW4_OK;
@@ -1472,6 +1693,7 @@ int aw4_decode_batch(aw4_model* m, const int32_t* host_tokens, int32_t B, int32_
     if (check_model(m) || !host_tokens || !host_argmax) return AW4_E_INVAL;
     const aw4_config* c = &m->cfg;
     if (c->vocab <= 0) return fail(m, AW4_E_STATE, "decode_batch needs a vocabulary");
+    if (need_weights(m)) return AW4_E_STATE;
     if (B < 1 || B > m->max_batch) return fail(m, AW4_E_INVAL, "batch must be in [1, max_batch]");
     if (c->kv_window > 0) return fail(m, AW4_E_INVAL, "batch decode does not read a recent window");
     if (B == 1 && m->seq == 0) {
@@ -1499,7 +1721,7 @@ int aw4_decode_batch(aw4_model* m, const int32_t* host_tokens, int32_t B, int32_
         hipGraphExec_t* ge = &m->g_batch[B];
         if (!*ge) {
             hipGraph_t g = nullptr;
-            HIPCHK(m, hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal));
+            HIPCHK_RAW(m, hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal));
             int rc = enqueue_batch_step(m, B);
             hipError_t e = hipStreamEndCapture(s, &g);
             if (rc) {
@@ -1554,6 +1776,7 @@ int aw4_draft(aw4_model* m, int32_t t0, int32_t k, float temperature, const floa
     const aw4_config* c = &m->cfg;
     if (c->draft_vocab <= 0) return fail(m, AW4_E_STATE, "the model has no draft head");
     if (!m->map_set) return fail(m, AW4_E_STATE, "no vocabulary map has been set");
+    if (need_weights(m)) return AW4_E_STATE;
     if (k < 1 || k > 3 || k + 1 > c->max_verify) return fail(m, AW4_E_INVAL, "k must be in [1, min(3, max_verify - 1)]");
     if (t0 < 0 || t0 >= c->vocab) return fail(m, AW4_E_TOKEN, "token out of range");
     if (!(temperature >= 0.f) || !std::isfinite(temperature)) return fail(m, AW4_E_INVAL, "temperature must be >= 0");
@@ -1601,6 +1824,7 @@ int aw4_draft(aw4_model* m, int32_t t0, int32_t k, float temperature, const floa
 int aw4_prefill(aw4_model* m, const int32_t* tokens, int32_t n, float* dev_logits) {
     if (check_model(m) || (!tokens && n > 0) || n < 0) return AW4_E_INVAL;
     if (m->cfg.vocab <= 0) return fail(m, AW4_E_STATE, "prefill needs a vocabulary");
+    if (need_weights(m) || need_fresh_window(m)) return AW4_E_STATE;
     if ((int64_t)m->host_pos + n > m->cfg.max_ctx) return fail(m, AW4_E_CTX_FULL, "prompt exceeds max_ctx");
     for (int i = 0; i < n; ++i)
         if (tokens[i] < 0 || tokens[i] >= m->cfg.vocab) return fail(m, AW4_E_TOKEN, "prompt token out of range");
@@ -1649,6 +1873,7 @@ int aw4_set_prefill_chunk(aw4_model* m, int32_t n) {
 int aw4_decode_step(aw4_model* m, int32_t token, float* dev_logits, int32_t* host_argmax) {
     if (check_model(m)) return AW4_E_INVAL;
     if (m->cfg.vocab <= 0) return fail(m, AW4_E_STATE, "decode_step needs a vocabulary");
+    if (need_weights(m) || need_fresh_window(m)) return AW4_E_STATE;
     if (token < 0 || token >= m->cfg.vocab) return fail(m, AW4_E_TOKEN, "token out of range");
     if (m->host_pos + 1 > m->cfg.max_ctx) return fail(m, AW4_E_CTX_FULL, "context full");
     HIPCHK(m, launch_set_token(m->ctl, token, m->stream));
@@ -1669,6 +1894,7 @@ int aw4_decode_step(aw4_model* m, int32_t token, float* dev_logits, int32_t* hos
 int aw4_decode_greedy(aw4_model* m, int32_t first_token, int32_t n_steps, int32_t* host_out) {
     if (check_model(m) || n_steps < 0 || (!host_out && n_steps > 0)) return AW4_E_INVAL;
     if (m->cfg.vocab <= 0) return fail(m, AW4_E_STATE, "decode_greedy needs a vocabulary");
+    if (need_weights(m) || need_fresh_window(m)) return AW4_E_STATE;
     if (first_token < 0 || first_token >= m->cfg.vocab) return fail(m, AW4_E_TOKEN, "token out of range");
     if ((int64_t)m->host_pos + n_steps > m->cfg.max_ctx) return fail(m, AW4_E_CTX_FULL, "context full");
     int done = 0;
@@ -1696,6 +1922,7 @@ int aw4_verify_k(aw4_model* m, const int32_t* host_tokens, int32_t k, const floa
     if (check_model(m) || !host_tokens || !host_out || !host_n_out) return AW4_E_INVAL;
     const aw4_config* c = &m->cfg;
     if (c->vocab <= 0) return fail(m, AW4_E_STATE, "verify_k needs a vocabulary");
+    if (need_weights(m)) return AW4_E_STATE;
     if (c->kv_window > 0) return fail(m, AW4_E_INVAL, "verify_k does not read a recent window");
     if (k < 0 || k + 1 > c->max_verify) return fail(m, AW4_E_INVAL, "k must be in [0, max_verify - 1]");
     if (!(temperature >= 0.f) || !std::isfinite(temperature)) return fail(m, AW4_E_INVAL, "temperature must be >= 0");
@@ -1736,6 +1963,7 @@ int aw4_verify_k(aw4_model* m, const int32_t* host_tokens, int32_t k, const floa
 
 int aw4_decode_hidden(aw4_model* m, const float* dev_in, float* dev_out) {
     if (check_model(m) || !dev_in || !dev_out) return AW4_E_INVAL;
+    if (need_weights(m) || need_fresh_window(m)) return AW4_E_STATE;
     if (m->host_pos + 1 > m->cfg.max_ctx) return fail(m, AW4_E_CTX_FULL, "context full");
     if (dev_in != m->x) HIPCHK(m, launch_copy_f32(m->x, dev_in, m->cfg.hidden, m->stream));
     int rc = enqueue_layers(m);
@@ -1757,6 +1985,7 @@ int aw4_read_hidden(aw4_model* m, float* host_x) {
 int aw4_time_phase(aw4_model* m, int32_t phase, int32_t reps, float* avg_us, uint64_t* bytes_per_launch) {
     if (check_model(m) || reps < 1 || !avg_us || !bytes_per_launch) return AW4_E_INVAL;
     if (phase < 0 || phase > AW4_PHASE_PREFILL_GATE_UP) return fail(m, AW4_E_INVAL, "unknown phase");
+    if (need_weights(m)) return AW4_E_STATE;
     hipEvent_t e0, e1;
     HIPCHK(m, hipEventCreate(&e0));
     HIPCHK(m, hipEventCreate(&e1));
@@ -1821,7 +2050,7 @@ int aw4_time_phase(aw4_model* m, int32_t phase, int32_t reps, float* avg_us, uin
     hipGraphExec_t ge = nullptr;
     if (m->use_graph && phase != AW4_PHASE_PREFILL_GATE_UP) {
         hipGraph_t g = nullptr;
-        HIPCHK(m, hipStreamBeginCapture(m->stream, hipStreamCaptureModeThreadLocal));
+        HIPCHK_RAW(m, hipStreamBeginCapture(m->stream, hipStreamCaptureModeThreadLocal));
         for (int i = 0; i < reps; ++i) {
             int rc = enqueue_phase(m, phase, i % L, &bytes);
             if (rc) {
@@ -1990,7 +2219,12 @@ int aw4_export_state_win(aw4_model* m, int32_t layer, uint16_t* host_kw, uint16_
 }
 
 int aw4_import_state_win(aw4_model* m, int32_t layer, const uint16_t* host_kw, const uint16_t* host_vw) {
-    return win_copy(m, layer, const_cast<uint16_t*>(host_kw), const_cast<uint16_t*>(host_vw), false);
+    int rc = win_copy(m, layer, const_cast<uint16_t*>(host_kw), const_cast<uint16_t*>(host_vw), false);
+    if (rc == AW4_OK) {
+        m->win_fresh[(size_t)layer] = true;
+        m->win_imported[(size_t)layer] = true;
+    }
+    return rc;
 }
 
 }  // extern "C"

@@ -202,11 +202,20 @@ __global__ __launch_bounds__(256) void k_gemv_w4(GemvArgs a) {
 // that the short L2 reads of the input vector are not queued behind the HBM
 // reads of the codes (vector memory counters retire in issue order);
 // finish() reduces and writes the fp16 input vector to LDS.
-template <int K, int PRO>
+// LDS image of the fp16 input.  Flat: element k at k.  Padded: each 32-value
+// group g at 40 g halves (80 bytes), so that lanes reading consecutive groups
+// with 16-byte LDS reads start on different banks (a 64-byte lane stride puts
+// every other lane on the same banks).
+template <bool PAD>
+__host__ __device__ constexpr int xs_at(int k) { return PAD ? (k >> 5) * 40 + (k & 31) : k; }
+template <bool PAD>
+__host__ __device__ constexpr int xs_len(int K) { return PAD ? (K >> 5) * 40 : K; }
+
+template <int K, int PRO, bool PAD = false>
 struct Prologue;
 
-template <int K>
-struct Prologue<K, PRO_NORM> {
+template <int K, bool PAD>
+struct Prologue<K, PRO_NORM, PAD> {
     static constexpr int N4 = K / 4;
     static constexpr int PER = (N4 + 255) / 256;
     float4 v[PER], w[PER];
@@ -242,7 +251,7 @@ struct Prologue<K, PRO_NORM> {
             if (N4 % 256 == 0 || idx < N4) {
                 h4 o = {(_Float16)(v[i].x * r * w[i].x), (_Float16)(v[i].y * r * w[i].y),
                         (_Float16)(v[i].z * r * w[i].z), (_Float16)(v[i].w * r * w[i].w)};
-                ((h4*)xs)[idx] = o;
+                *(h4*)(xs + xs_at<PAD>(4 * idx)) = o;
             }
         }
     }
@@ -251,8 +260,8 @@ struct Prologue<K, PRO_NORM> {
 // gated RMSNorm per head of d values: RMSNorm(o) * w * SiLU(z).  Thread t
 // takes E = K/256 consecutive values; the d/E threads of a head reduce with
 // lane shuffles.
-template <int K>
-struct Prologue<K, PRO_GATED> {
+template <int K, bool PAD>
+struct Prologue<K, PRO_GATED, PAD> {
     static constexpr int E = K >= 256 ? K / 256 : 1;
     static constexpr int V4 = E % 4 == 0 ? E / 4 : 0;   // float4 loads per array when E allows
     float ov[E], zv[E], wv[E];
@@ -292,14 +301,14 @@ struct Prologue<K, PRO_GATED> {
 #pragma unroll
             for (int e = 0; e < E; ++e) {
                 const float silu = zv[e] * sigmoidf_(zv[e]);
-                xs[base + e] = (_Float16)(ov[e] * r * wv[e] * silu);
+                xs[xs_at<PAD>(base + e)] = (_Float16)(ov[e] * r * wv[e] * silu);
             }
         }
     }
 };
 
-template <int K>
-struct Prologue<K, PRO_LOADH> {
+template <int K, bool PAD>
+struct Prologue<K, PRO_LOADH, PAD> {
     typedef uint32_t v4u __attribute__((ext_vector_type(4)));
     static constexpr int N8 = K / 8;
     static constexpr int PER = (N8 + 255) / 256;
@@ -321,7 +330,7 @@ struct Prologue<K, PRO_LOADH> {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int idx = threadIdx.x + 256 * i;
-            if (N8 % 256 == 0 || idx < N8) ((v4u*)xs)[idx] = v[i];
+            if (N8 % 256 == 0 || idx < N8) *(v4u*)(xs + xs_at<PAD>(8 * idx)) = v[i];
         }
     }
 };
@@ -386,7 +395,7 @@ __global__ __launch_bounds__(256, stream_simd_waves(NF)) void k_gemv_stream(Gemv
     // The input vector first, then the weights: issued together, the input's
     // short cache reads queue behind the chip-wide flood of weight requests
     // and every block waits several microseconds for its prologue.
-    Prologue<32 * G, PRO> pro;
+    Prologue<32 * G, PRO, true> pro;
     pro.load(a);
     pro.finish(a, xs, red);
     __syncthreads();
@@ -404,7 +413,7 @@ __global__ __launch_bounds__(256, stream_simd_waves(NF)) void k_gemv_stream(Gemv
         row_of[i] = f / G;
         grp_of[i] = f % G;
     }
-    const uint4* xv = (const uint4*)xs;   // group g: xv[4g .. 4g+3]
+    const uint4* xv = (const uint4*)xs;   // group g: xv[5g .. 5g+3] (padded image)
     // short rows: this lane's slices of the input stay in registers for every
     // row block (the lane -> group map is the same for all of them)
     uint4 xr[kXreg ? NF : 1][4];
@@ -412,7 +421,7 @@ __global__ __launch_bounds__(256, stream_simd_waves(NF)) void k_gemv_stream(Gemv
 #pragma unroll
         for (int i = 0; i < NF; ++i)
 #pragma unroll
-            for (int k = 0; k < 4; ++k) xr[kXreg ? i : 0][k] = xv[4 * grp_of[i] + k];
+            for (int k = 0; k < 4; ++k) xr[kXreg ? i : 0][k] = xv[5 * grp_of[i] + k];
     }
     const NibK nk;
 
@@ -430,7 +439,7 @@ __global__ __launch_bounds__(256, stream_simd_waves(NF)) void k_gemv_stream(Gemv
                 x2 = xr[kXreg ? i : 0][2]; x3 = xr[kXreg ? i : 0][3];
             } else {
                 const int g = grp_of[i];
-                x0 = xv[4 * g]; x1 = xv[4 * g + 1]; x2 = xv[4 * g + 2]; x3 = xv[4 * g + 3];
+                x0 = xv[5 * g]; x1 = xv[5 * g + 1]; x2 = xv[5 * g + 2]; x3 = xv[5 * g + 3];
             }
             float ea = 0.f, eb = 0.f;
             dq_dot8(b.c[i][0], x0, ea, eb, nk);
@@ -949,9 +958,15 @@ constexpr int kStage = 8;
 // norms need one barrier.  NORM: RMSNorm(x_m) * w.  LOADH: fp16 copy (two
 // inputs per round, to bound the registers).  GATED: per head of d values
 // RMSNorm(o) * w * SiLU(z), thread t taking E = K/256 consecutive values.
+// input m's row of the image starts at m (K + kMfmaPad) halves: the 32-byte
+// pad puts the rows of different inputs on different banks for the lanes of a
+// 16-lane row that read the same offset of each
+constexpr int kMfmaPad = 16;
+
 template <int K, int PRO>
 __device__ __forceinline__ void mfma_prologue(const GemvMultiArgs& a, _Float16* xs, float* red) {
     constexpr int MAXM = 4;
+    constexpr int LD = K + kMfmaPad;
     const int M = a.M, tid = threadIdx.x;
     typedef _Float16 h4 __attribute__((ext_vector_type(4)));
     if (PRO == PRO_NORM) {
@@ -1007,7 +1022,7 @@ __device__ __forceinline__ void mfma_prologue(const GemvMultiArgs& a, _Float16* 
                 if (N4 % 256 == 0 || idx < N4) {
                     const h4 o = {(_Float16)(v[m][i].x * r * w[i].x), (_Float16)(v[m][i].y * r * w[i].y),
                                   (_Float16)(v[m][i].z * r * w[i].z), (_Float16)(v[m][i].w * r * w[i].w)};
-                    ((h4*)(xs + m * K))[idx] = o;
+                    ((h4*)(xs + m * LD))[idx] = o;
                 }
             }
         }
@@ -1037,7 +1052,7 @@ __device__ __forceinline__ void mfma_prologue(const GemvMultiArgs& a, _Float16* 
 #pragma unroll
                     for (int i = 0; i < PER; ++i) {
                         const int idx = tid + 256 * i;
-                        if (N8 % 256 == 0 || idx < N8) ((v4u*)(xs + (m0 + mm) * K))[idx] = v[mm][i];
+                        if (N8 % 256 == 0 || idx < N8) ((v4u*)(xs + (m0 + mm) * LD))[idx] = v[mm][i];
                     }
         }
     } else {
@@ -1092,7 +1107,7 @@ __device__ __forceinline__ void mfma_prologue(const GemvMultiArgs& a, _Float16* 
                 if (live && m0 + mm < M)
 #pragma unroll
                     for (int e = 0; e < E; ++e)
-                        xs[(m0 + mm) * K + base + e] =
+                        xs[(m0 + mm) * LD + base + e] =
                             (_Float16)(ov[mm][e] * r * wv[e] * (zv[mm][e] * sigmoidf_(zv[mm][e])));
             }
         }
@@ -1108,7 +1123,7 @@ __global__ __launch_bounds__(256, 2) void k_gemv_mfma(GemvMultiArgs a) {
     float* red = (float*)smem;                        // 16 floats
     _Float16* xs = (_Float16*)(smem + 64);            // [M][K]
     const int K = a.K, G = K / 32, M = a.M, rows = a.rows;
-    f4* part = (f4*)(smem + 64 + (size_t)4 * M * (K / 2));   // [4 waves][64 lanes], KS > 1
+    f4* part = (f4*)(smem + 64 + (size_t)2 * M * (K + kMfmaPad));   // [4 waves][64 lanes], KS > 1
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar branches
     const int c = lane & 15, q = lane >> 4;
@@ -1129,7 +1144,7 @@ __global__ __launch_bounds__(256, 2) void k_gemv_mfma(GemvMultiArgs a) {
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) srow[rr] = a.scales + (int64_t)min(r0 + 4 * q + rr, rows - 1) * G;
     // B operand: input min(c, M - 1) (columns past M are computed and dropped)
-    const _Float16* xrow = xs + min(c, M - 1) * K + 8 * q;
+    const _Float16* xrow = xs + min(c, M - 1) * (K + kMfmaPad) + 8 * q;
 
     struct Stage {
         u32x4 w[U / 4];     // row c, groups g0 + 4h + q (h < U/4), all four dwords
@@ -1398,7 +1413,7 @@ int multi_blocks(int rows, int R, int NF) { return stream_grid(rows / R, NF <= 8
 
 template <int R, int NF>
 hipError_t launch_stream(int pro, int epi, const GemvArgs& a, hipStream_t s) {
-    const size_t shm = 64 + (size_t)a.K * 2;
+    const size_t shm = 64 + (size_t)xs_len<true>(a.K) * 2;
     const dim3 grid(stream_blocks(a.rows, R, NF)), block(256);
 #define AW4_STREAM_CASE(P, E)                                                         \
     if (pro == P && epi == E) {                                                       \
@@ -1494,7 +1509,7 @@ template <int P, int E, int KS, int NST>
 hipError_t launch_mfma(const GemvMultiArgs& a, hipStream_t s) {
     const int nrb = (a.rows + 15) / 16;
     const dim3 grid((nrb + 4 / KS - 1) / (4 / KS)), block(256);
-    const size_t shm = 64 + (size_t)2 * a.M * a.K + (KS > 1 ? 4 * 64 * 16 : 0);
+    const size_t shm = 64 + (size_t)2 * a.M * (a.K + kMfmaPad) + (KS > 1 ? 4 * 64 * 16 : 0);
     if (shm > 65536) {
         hipError_t e = hipFuncSetAttribute((const void*)k_gemv_mfma<P, E, KS, NST>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);

@@ -143,6 +143,13 @@ int aw4_validate_config(const aw4_config* cfg);
  * written to *out_bytes.  Pure host computation. */
 int aw4_workspace_bytes(const aw4_config* cfg, uint64_t* out_bytes);
 
+/* Weights: a new model holds none.  Every call that runs the model (prefill,
+ * decode, verify, draft, batch decode, aw4_decode_hidden, aw4_time_phase)
+ * returns AW4_E_STATE until every tensor of its config (aw4_tensor_shape; the
+ * draft head's and its map included when draft_vocab > 0) has been given values
+ * by aw4_quantize_tensor (all rows, over one or more calls), aw4_load_tensor,
+ * aw4_set_vector, aw4_set_draft_map or aw4_load_weights. */
+
 /* Bind a model to a caller-owned device arena of at least
  * aw4_workspace_bytes() bytes, 256-byte aligned, on the current HIP device,
  * and to hip_stream (a hipStream_t; NULL = the null stream).  The arena stays
@@ -193,13 +200,38 @@ int aw4_set_vector(aw4_model* model, int32_t layer, int32_t kind, const float* h
  * head). */
 int aw4_set_draft_map(aw4_model* model, const int32_t* host_ids, int32_t n);
 
-/* Load every tensor from one host blob: "AW4W" magic, uint32 version 1, the
- * aw4_config it was made for, uint32 tensor count, then per tensor
- * {int32 layer, int32 kind, int64 rows, int64 cols, uint64 bytes} followed by
- * the payload (logical codes then scales, n fp32 values for vectors, or n int32
- * ids for DRAFT_MAP).  The version is 3 (the config carries draft_vocab and
- * max_batch).
- * Errors: AW4_E_FORMAT on magic, version, size or config mismatch. */
+/* Weight blob, the host-side form of a whole model (every weight of the
+ * stack streams from memory once per decoded token, page 5, bs178.com
+ * llamAmpere article, "为什么它真能这么快" point 二, so the weights are loaded
+ * once into device memory and stay there).  Layout, little-endian:
+ *   "AW4W" magic; uint32 version 4;
+ *   int32 x 12: hidden, ffn, vocab, n_layers, gdn_qk_heads, gdn_v_heads,
+ *     gdn_head_dim, attn_q_heads, attn_kv_heads, attn_head_dim, group,
+ *     draft_vocab (the fields that fix tensor shapes; max_ctx, max_verify,
+ *     rms_eps, max_batch and kv_window are run-time choices, not echoed);
+ *   char[128] layer_pattern, NUL padded;
+ *   uint32 tensor count; then per tensor int32 layer, int32 kind, int64 rows,
+ *     int64 cols, uint64 payload bytes, and the payload: a matrix's logical
+ *     codes (the aw4_load_tensor format) then its fp16 scale bits [rows][cols/32];
+ *     a vector's cols fp32 values; DRAFT_MAP's cols int32 ids.
+ * A blob may hold any subset of the config's tensors, each at most once. */
+
+/* Pure host check of a blob against cfg; reads [host_blob, host_blob + bytes)
+ * only and enqueues nothing.  AW4_E_FORMAT on a bad magic or version, a config
+ * echo that differs from cfg, a tensor the config does not have or with the
+ * wrong shape, a duplicated tensor, a payload size that does not match, a
+ * truncated blob or bytes after the last tensor, and on values outside the
+ * formats: W4 code -8 (nibble 0) or int8 code -128 (the codecs use -qmax..qmax),
+ * a negative or non-finite scale, a non-finite vector value, rotation signs other
+ * than +-1, map ids repeated or outside [0, vocab).  AW4_E_INVAL: cfg invalid or
+ * host_blob NULL with bytes > 0. */
+int aw4_check_blob(const aw4_config* cfg, const void* host_blob, uint64_t bytes);
+
+/* Load the tensors of a blob (format above) into the model: the whole blob is
+ * checked first (aw4_check_blob against the model's config), so a bad blob
+ * returns AW4_E_FORMAT and changes nothing; then every tensor is copied and
+ * repacked into the device layout.  Synchronous.  Errors: AW4_E_FORMAT,
+ * AW4_E_INVAL, AW4_E_HIP. */
 int aw4_load_weights(aw4_model* model, const void* host_blob, uint64_t bytes);
 
 /* ----------------------------------------------------------- decode */
@@ -207,11 +239,16 @@ int aw4_load_weights(aw4_model* model, const void* host_blob, uint64_t bytes);
 /* Clear recurrent states and caches; position 0.  Enqueued. */
 int aw4_reset(aw4_model* model);
 
-/* Append n prompt tokens (positions pos..pos+n-1) through every layer.  If
- * dev_logits is not NULL it receives the fp32 logits [vocab] after the last
- * token.  With a draft head, prefill also gives it one cache entry per prompt
- * position except the last (that position's hidden state and the next prompt
- * token).  Errors: AW4_E_CTX_FULL, AW4_E_TOKEN, AW4_E_STATE (vocab 0). */
+/* Append n prompt tokens (positions pos..pos+n-1) through every layer: per
+ * token, what a decode step computes (the pages report prompt processing apart
+ * from generation: page 3 "Qwen3.8-27B 實測" and page 4, jdon.com, where a
+ * 100K-token input takes about two minutes).  host_tokens: n ids in
+ * [0, vocab), read during the call.  If dev_logits (device, fp32 [vocab]) is
+ * not NULL it receives the logits after the last token.  With a draft head,
+ * prefill also gives it one cache entry per prompt position except the last
+ * (that position's hidden state and the next prompt token).  Enqueued.
+ * Errors: AW4_E_INVAL, AW4_E_CTX_FULL, AW4_E_TOKEN, AW4_E_STATE (vocab 0,
+ * weights not complete, or a recent window that must be re-imported). */
 int aw4_prefill(aw4_model* model, const int32_t* host_tokens, int32_t n, float* dev_logits);
 
 /* Prompt tokens per prefill chunk.  aw4_prefill runs a prompt in chunks of up
@@ -224,16 +261,22 @@ int aw4_prefill(aw4_model* model, const int32_t* host_tokens, int32_t n, float* 
  * have no chunked path (maximum 0).  Errors: AW4_E_INVAL. */
 int aw4_set_prefill_chunk(aw4_model* model, int32_t n);
 
-/* One decode step on `token` at the current position: embed, all layers
- * (appending this position to the caches), final norm, output head, argmax
- * (lowest index on ties).  dev_logits (optional) receives fp32 [vocab];
- * host_argmax (optional) receives the argmax after a stream sync; without it
- * the call only enqueues. */
+/* One decode step on `token` at the current position (the single-user,
+ * batch-1 generation step whose speed the pages measure and tie to the bytes
+ * streamed per token: page 5, point 二; page 3 "部署前必知" for the 48 GDN +
+ * 16 attention layers): embed, all layers (appending this position to the
+ * caches), final norm, output head, argmax (lowest index on ties).
+ * dev_logits (optional, device) receives fp32 [vocab]; host_argmax (optional)
+ * receives the argmax after a stream sync; without it the call only enqueues.
+ * Errors: AW4_E_TOKEN, AW4_E_CTX_FULL, AW4_E_STATE (vocab 0, weights not
+ * complete, or a recent window that must be re-imported), AW4_E_HIP. */
 int aw4_decode_step(aw4_model* model, int32_t token, float* dev_logits, int32_t* host_argmax);
 
-/* n greedy steps starting from first_token; each step's argmax feeds the next
- * on the device.  host_tokens_out receives the n generated tokens (one sync at
- * the end).  This is the measured decode loop. */
+/* n greedy steps starting from first_token (page 5, point 二: decode speed is
+ * set by the bytes streamed per token); each step's argmax feeds the next on
+ * the device.  host_tokens_out (host, n int32) receives the n generated tokens
+ * (one sync at the end).  This is the measured decode loop.  Errors as
+ * aw4_decode_step. */
 int aw4_decode_greedy(aw4_model* model, int32_t first_token, int32_t n_steps, int32_t* host_tokens_out);
 
 /* Draft verification (page 5, bs178.com llamAmpere article, point 四: the
@@ -285,7 +328,8 @@ int aw4_draft(aw4_model* model, int32_t t0, int32_t k, float temperature, const 
 
 /* Layers only, at the current position: dev_x_out = stack(dev_x_in), both
  * fp32 [hidden] device vectors (may alias).  For models without a vocabulary
- * (single-layer workloads) and for hidden-state checks.  Enqueued. */
+ * (single-layer workloads) and for hidden-state checks.  Enqueued.  Errors:
+ * AW4_E_CTX_FULL, AW4_E_STATE (weights not complete). */
 int aw4_decode_hidden(aw4_model* model, const float* dev_x_in, float* dev_x_out);
 
 /* Copy the residual vector after the last step's layers (fp32 [hidden]) to the
@@ -322,7 +366,11 @@ int aw4_time_phase(aw4_model* model, int32_t phase, int32_t reps, float* avg_us,
 
 int aw4_get_pos(aw4_model* model, int32_t* pos);
 
-/* Set the position without touching the caches (state import). */
+/* Set the position without touching the caches (state import).  With a
+ * recent window, moving the position back leaves ring slots that hold later
+ * positions: unless every attention layer's ring was imported since the last
+ * decode call, decoding then returns AW4_E_STATE until each ring is imported
+ * again (aw4_import_state_win). */
 int aw4_set_pos(aw4_model* model, int32_t pos);
 
 /* Sequences (max_batch > 1): the model holds max_batch independent sequences,
@@ -372,6 +420,15 @@ int aw4_import_state_kv(aw4_model* model, int32_t layer, int32_t npos, const int
  * AW4_E_INVAL: not an attention layer, or no window configured. */
 int aw4_export_state_win(aw4_model* model, int32_t layer, uint16_t* host_kw, uint16_t* host_vw);
 int aw4_import_state_win(aw4_model* model, int32_t layer, const uint16_t* host_kw, const uint16_t* host_vw);
+
+/* ----------------------------------------------------------- test hook */
+
+/* Error-path testing: with n >= 1, the n-th checked HIP runtime call the
+ * library makes from now on (on any model) is reported as failed, once, and
+ * the entry point that made it returns AW4_E_HIP; the call itself has run.
+ * n <= 0 disarms.  After an AW4_E_HIP the model's device state is undefined
+ * until aw4_reset or a state import.  Not thread-safe across models. */
+int aw4_test_fail_hip_call(int32_t n);
 
 #ifdef __cplusplus
 }

@@ -103,3 +103,133 @@ def test_null_model_calls_are_rejected():
     assert L.aw4_status_string(-6) == b"context full"
     assert L.aw4_last_error(None) == b"null model"
     L.aw4_destroy(None)
+
+
+# ------------------------------------------------------------- weight blob (pure host)
+def _blob_items(shape, seed=3):
+    """(layer, kind, value) of every tensor: the oracle codec's logical codes
+    and scales, fp32 vectors, signs as fp32, the draft map as int32"""
+    import numpy as np
+    from tests.helpers import logical_weights
+    items = []
+    for (layer, kind), v in logical_weights(shape, seed).items():
+        if kind == W.T_RHT_SIGNS:
+            v = np.asarray(v, np.float32)
+        items.append((layer, kind, v))
+    return items
+
+
+@pytest.fixture(scope="module")
+def tiny_blob():
+    from attention_w4_amd import blob
+    from tests.helpers import TINY_MTP
+    return TINY_MTP, blob.write_blob(A.Config.from_shape(TINY_MTP), _blob_items(TINY_MTP))
+
+
+def _records(b):
+    """offsets of every tensor record of a well-formed blob"""
+    import struct
+    from attention_w4_amd import blob
+    off = len(blob.header(A.Config.from_shape(W.TOY), 0))
+    (count,) = struct.unpack_from("<I", b, off - 4)
+    out = []
+    for _ in range(count):
+        layer, kind, rows, cols, nb = struct.unpack_from("<iiqqQ", b, off)
+        out.append((off, layer, kind, rows, cols, nb))
+        off += 32 + nb
+    assert off == len(b)
+    return out
+
+
+def test_blob_checks_clean(tiny_blob):
+    shape, b = tiny_blob
+    assert A.check_blob(shape, b) == 0
+    # any subset of the tensors is a valid blob
+    from attention_w4_amd import blob
+    assert A.check_blob(shape, blob.write_blob(A.Config.from_shape(shape), [])) == 0
+    assert A.check_blob(shape, blob.write_blob(A.Config.from_shape(shape), _blob_items(shape)[:3])) == 0
+
+
+def _set(b, off, fmt, val):
+    import struct
+    bb = bytearray(b)
+    struct.pack_into(fmt, bb, off, val)
+    return bytes(bb)
+
+
+def test_blob_rejects_every_malformation(tiny_blob):
+    import struct
+    shape, b = tiny_blob
+    F = -5
+    recs = _records(b)
+    mat = next(r for r in recs if r[2] == W.T_MIX_IN)
+    vec = next(r for r in recs if r[2] == W.T_NORM_MIX)
+    sig = next(r for r in recs if r[2] == W.T_RHT_SIGNS)
+    mp = next(r for r in recs if r[2] == W.T_DRAFT_MAP)
+    head = next(r for r in recs if r[2] == W.T_LM_HEAD)
+    cases = {
+        "magic": b"AW4X" + b[4:],
+        "version": _set(b, 4, "<I", 3),
+        "echo hidden": _set(b, 8, "<i", shape.hidden + 64),
+        "echo draft_vocab": _set(b, 8 + 4 * 11, "<i", shape.draft_vocab + 1),
+        "echo pattern": b[:56] + b"GAAG" + b[60:],
+        "count too high": _set(b, 184, "<I", len(recs) + 1),
+        "count too low": _set(b, 184, "<I", len(recs) - 1),
+        "truncated header": b[:100],
+        "truncated payload": b[:-1],
+        "trailing byte": b + b"\0",
+        "rows": _set(b, mat[0] + 8, "<q", mat[3] + 1),
+        "cols": _set(b, vec[0] + 16, "<q", vec[4] + 32),
+        "payload bytes": _set(b, vec[0] + 24, "<Q", vec[5] + 4),
+        "kind not in config": _set(b, vec[0] + 4, "<i", W.T_DRAFT_NORM_EMB),   # a draft-head kind at a target layer
+        "layer out of range": _set(b, mat[0], "<i", len(shape.pattern) + 1),
+        "w4 code -8": _set(b, mat[0] + 32 + 5, "<B", 0x80),
+        "int8 code -128": _set(b, head[0] + 32 + 7, "<b", -128),
+        "scale nan": _set(b, mat[0] + 32 + mat[3] * mat[4] // 2 + 2, "<H", 0x7E00),
+        "scale negative": _set(b, mat[0] + 32 + mat[3] * mat[4] // 2, "<H", 0xB800),
+        "vector inf": _set(b, vec[0] + 32 + 8, "<f", float("inf")),
+        "sign not +-1": _set(b, sig[0] + 32, "<f", 0.5),
+        "map id repeated": _set(b, mp[0] + 32 + 4, "<i", struct.unpack_from("<i", b, mp[0] + 32)[0]),
+        "map id out of range": _set(b, mp[0] + 32, "<i", shape.vocab),
+        "duplicate tensor": (b[:184] + struct.pack("<I", len(recs) + 1) + b[188:] +
+                             b[vec[0]:vec[0] + 32 + vec[5]]),
+    }
+    assert vec[1] < len(shape.pattern)
+    for name, bad in cases.items():
+        assert A.check_blob(shape, bad) == F, name
+    assert A.check_blob(W.with_(shape, ffn=shape.ffn + 64), b) == F
+
+
+def test_blob_check_rejects_bad_arguments(tiny_blob):
+    shape, b = tiny_blob
+    L = A.lib()
+    c = A.Config.from_shape(shape)
+    assert L.aw4_check_blob(ctypes.byref(c), None, 16) == -1
+    bad = A.Config.from_shape(shape)
+    bad.group = 16
+    assert A.check_blob(bad, b) == -1
+
+
+def test_blob_writer_round_trips_the_records(tiny_blob):
+    """the records the writer emits carry each tensor's shape and its bytes in
+    order: codes then scales, vectors as fp32"""
+    import numpy as np
+    shape, b = tiny_blob
+    items = _blob_items(shape)
+    recs = _records(b)
+    assert [(r[1], r[2]) for r in recs] == [(l, k) for l, k, _ in items]
+    for (off, layer, kind, rows, cols, nb), (_, _, v) in zip(recs, items):
+        payload = b[off + 32: off + 32 + nb]
+        if kind in (0, 1, 2, 3, 4, 5, 12):
+            codes, scales = v
+            assert rows == scales.shape[0] and cols == scales.shape[1] * 32
+            assert payload == np.ascontiguousarray(codes).tobytes() + np.ascontiguousarray(scales, np.uint16).tobytes()
+        elif kind == W.T_DRAFT_MAP:
+            assert payload == np.asarray(v, np.int32).tobytes()
+        else:
+            assert payload == np.asarray(v, np.float32).tobytes()
+
+
+def test_fault_hook_is_exported():
+    L = A.lib()
+    assert L.aw4_test_fail_hip_call(0) == 0

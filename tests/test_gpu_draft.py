@@ -212,11 +212,12 @@ def test_speculative_greedy_equals_plain_greedy(aw4):
 
 def test_draft_errors(aw4):
     _say("case: draft head error paths, toy stack")
+    from synth.gpu_load import load_recipe
     gm = aw4.Model(SHAPE)
     with pytest.raises(aw4.AW4Error) as e:
         gm.draft(1, 3)
-    assert e.value.code == -8          # no map yet
-    gm.set_draft_map(synth.draft_map(SHAPE, 0))
+    assert e.value.code == -8          # no map (and no weights) yet
+    load_recipe(gm, SHAPE, 0)          # every tensor, the map included
     with pytest.raises(aw4.AW4Error) as e:
         gm.draft(1, 3)
     assert e.value.code == -8          # nothing committed to draft from
