@@ -36,7 +36,7 @@ class Cfg(ctypes.Structure):
                 ("gdn_qk_heads", _i32), ("gdn_v_heads", _i32), ("gdn_head_dim", _i32),
                 ("attn_q_heads", _i32), ("attn_kv_heads", _i32), ("attn_head_dim", _i32),
                 ("group", _i32), ("max_ctx", _i32), ("rms_eps", _f64), ("pattern", ctypes.c_char * 128),
-                ("draft_vocab", _i32), ("kv_window", _i32)]
+                ("draft_vocab", _i32), ("kv_window", _i32), ("kv_format", _i32)]
 
 
 _lib = None
@@ -68,6 +68,11 @@ def lib():
             "or_attend_head": ([_vp, _vp, _vp, _vp, _vp, _i64, _i64, ctypes.c_int, _vp, _vp, _vp, _i64, _i64, _vp],
                                None),
             "or_kv_encode": ([_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp], None),
+            "or_kv_encode_fmt": ([_vp, _vp, _vp, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _vp], None),
+            "or_attend_head_fmt": ([_vp, _vp, _vp, _vp, _vp, _i64, _i64, ctypes.c_int, _vp, _vp, _vp, _i64, _i64,
+                                    ctypes.c_int, _vp], None),
+            "or_lm_level": ([ctypes.c_int], _f64),
+            "or_quant_group_lm": ([_vp, ctypes.c_int, _vp, _vp], None),
             "or_forward_layers": ([_vp, _vp, _vp], ctypes.c_int),
             "or_embed": ([_vp, _i32, _vp], ctypes.c_int),
             "or_head": ([_vp, _vp, _vp, _vp], ctypes.c_int),
@@ -162,10 +167,26 @@ def gdn_head_step(S, k, v, q, alpha, beta):
     return S, o
 
 
-def attend_head(q, kc, ks, vc, vs, signs, kw=None, vw=None):
+def lm_levels():
+    """the Lloyd-Max codebook of the value-cache format 2, ascending (fp16 values)"""
+    return np.array([lib().or_lm_level(c) for c in range(8)])
+
+
+def quant_group_lm(x):
+    """the codebook codec of one group: (scale bits, level indices 0..7)"""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    s = np.zeros(1, np.uint16)
+    c = np.zeros(len(x), np.int8)
+    lib().or_quant_group_lm(_p(x), len(x), _p(s), _p(c))
+    return int(s[0]), c
+
+
+def attend_head(q, kc, ks, vc, vs, signs, kw=None, vw=None, fmt=0):
     """q [d]; kc/vc int8 [npos][d]; ks/vs fp16 bits [npos][d/32].  With a window
     ring kw/vw (fp16 bits [W][d], position t at slot t % W), the last W
-    positions are read from it instead of the codes."""
+    positions are read from it instead of the codes.  fmt: the cache format
+    (0: V codes -3..3 rotated; 1: 4-bit K and V, V not rotated; 2: V codebook
+    indices 0..7 rotated)."""
     q = np.ascontiguousarray(q, np.float64)
     kc, vc = np.ascontiguousarray(kc, np.int8), np.ascontiguousarray(vc, np.int8)
     ks, vs = np.ascontiguousarray(ks, np.uint16), np.ascontiguousarray(vs, np.uint16)
@@ -173,22 +194,22 @@ def attend_head(q, kc, ks, vc, vs, signs, kw=None, vw=None):
     npos, d = kc.shape
     out = np.zeros(d)
     if kw is None:
-        lib().or_attend_head(_p(q), _p(kc), _p(ks), _p(vc), _p(vs), npos, d, d, _p(sg), None, None, 0, 0,
-                             _p(out))
+        lib().or_attend_head_fmt(_p(q), _p(kc), _p(ks), _p(vc), _p(vs), npos, d, d, _p(sg), None, None, 0, 0,
+                                 fmt, _p(out))
     else:
         kw, vw = np.ascontiguousarray(kw, np.uint16), np.ascontiguousarray(vw, np.uint16)
-        lib().or_attend_head(_p(q), _p(kc), _p(ks), _p(vc), _p(vs), npos, d, d, _p(sg), _p(kw), _p(vw),
-                             kw.shape[0], d, _p(out))
+        lib().or_attend_head_fmt(_p(q), _p(kc), _p(ks), _p(vc), _p(vs), npos, d, d, _p(sg), _p(kw), _p(vw),
+                                 kw.shape[0], d, fmt, _p(out))
     return out
 
 
-def kv_encode(k, v, signs):
+def kv_encode(k, v, signs, fmt=0):
     d = len(k)
     k, v = np.ascontiguousarray(k, np.float64), np.ascontiguousarray(v, np.float64)
     sg = np.ascontiguousarray(signs, np.int8)
     kc, vc = np.zeros(d, np.int8), np.zeros(d, np.int8)
     ks, vs = np.zeros(d // 32, np.uint16), np.zeros(d // 32, np.uint16)
-    lib().or_kv_encode(_p(k), _p(v), _p(sg), d, _p(kc), _p(ks), _p(vc), _p(vs))
+    lib().or_kv_encode_fmt(_p(k), _p(v), _p(sg), d, fmt, _p(kc), _p(ks), _p(vc), _p(vs))
     return kc, ks, vc, vs
 
 
@@ -212,6 +233,7 @@ class Model:
         c.pattern = shape.pattern.encode()
         c.draft_vocab = int(getattr(shape, "draft_vocab", 0))
         c.kv_window = int(getattr(shape, "kv_window", 0))
+        c.kv_format = int(getattr(shape, "kv_format", 0))
         self._cfg = c
         self.h = lib().or_create(ctypes.byref(c))
         if not self.h:

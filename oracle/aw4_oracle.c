@@ -87,6 +87,44 @@ void or_quant_group(const float* x, int n, int qmax, uint16_t* s_bits, int8_t* c
     }
 }
 
+/* Lloyd-Max 3-bit codebook for a unit-variance Gaussian (J. Max, "Quantizing
+ * for minimum distortion", IRE Trans. Inf. Theory, 1960, table for N = 8):
+ * output levels +-0.2451, +-0.7560, +-1.3440, +-2.1520, here rounded to fp16.
+ * Randomly rotated coordinates of a vector are close to Gaussian, which is
+ * why a rotated value cache can use it.  Code c in 0..7 indexes the ascending
+ * levels (c < 4 negative). */
+static const double kLmMax[4] = {0.2451, 0.7560, 1.3440, 2.1520};
+
+double or_lm_level(int c) {
+    if (c < 0 || c > 7) return NAN;
+    const double mag = or_f16_to_f64(or_f32_to_f16((float)kLmMax[c < 4 ? 3 - c : c - 4]));
+    return c < 4 ? -mag : mag;
+}
+
+/* Group codec with the Lloyd-Max codebook: s = fp16(sqrt(mean of x^2)) (the
+ * mean square rounded to fp32), t = x / s in fp32, c = the nearest level to t
+ * (the number of midpoints between consecutive levels that t exceeds: a tie
+ * goes to the lower level); s == 0 gives c = 4 (level +0.2451 times 0). */
+void or_quant_group_lm(const float* x, int n, uint16_t* s_bits, int8_t* codes) {
+    double ss = 0.0;
+    for (int i = 0; i < n; ++i) ss += (double)x[i] * (double)x[i];
+    const uint16_t sb = or_f32_to_f16(sqrtf((float)(ss / n)));
+    const float s = (float)or_f16_to_f64(sb);
+    *s_bits = sb;
+    float mid[7];
+    for (int i = 0; i < 7; ++i) mid[i] = (float)(0.5 * (or_lm_level(i) + or_lm_level(i + 1)));
+    for (int i = 0; i < n; ++i) {
+        if (s == 0.0f) { codes[i] = 4; continue; }
+        const float t = x[i] / s;
+        int c = 0;
+        for (int j = 0; j < 7; ++j) c += t > mid[j];
+        codes[i] = (int8_t)c;
+    }
+}
+
+/* value of one cached V code in format fmt (before the scale) */
+static inline double v_level(int fmt, int8_t c) { return fmt == 2 ? or_lm_level(c) : (double)c; }
+
 /* W4 logical format: per row K/2 bytes, element k in the low nibble of byte
  * k/2 when k is even and the high nibble when odd, nibble = code + 8; scales
  * fp16 [rows][K/32]. */
@@ -148,6 +186,8 @@ typedef struct {
     char pattern[128];
     int32_t draft_vocab;    /* rows of the draft head's vocabulary map, 0 = no draft head */
     int32_t kv_window;      /* recent positions kept at fp16 in the target's caches, 0 = none */
+    int32_t kv_format;      /* 0: K int8, V rotated 3-bit uniform; 1: q4_0, K and V 4-bit, V not
+                               rotated; 2: K int8, V rotated 3-bit Lloyd-Max codebook */
 } or_cfg;
 
 typedef struct { int64_t rows, cols; uint8_t* codes; uint16_t* scales; } or_w4;
@@ -260,8 +300,11 @@ or_model* or_create(const or_cfg* cfg) {
     m->c = *cfg;
     const or_cfg* c = &m->c;
     int64_t H = c->hidden;
+    /* the 4-bit and codebook cache formats serve the single-sequence decode
+     * step: no recent window and no draft head with them */
     if (c->draft_vocab < 0 || (c->draft_vocab > 0 && (c->vocab <= 0 || c->draft_vocab > c->vocab)) ||
-        c->kv_window < 0) {
+        c->kv_window < 0 || c->kv_format < 0 || c->kv_format > 2 ||
+        (c->kv_format != 0 && (c->kv_window > 0 || c->draft_vocab > 0))) {
         free(m);
         return NULL;
     }
@@ -496,9 +539,10 @@ static void gdn_mixer(or_model* m, or_layer* L, const double* xh, double* delta)
  * the KV cache: page 3 (Qwen3.8-27B 實測), section "RTX 4090 24GB", whose
  * 130K configuration keeps the last 2,048 tokens at F16 against attention
  * drift while older positions stay quantised. */
-void or_attend_head(const double* q, const int8_t* kc, const uint16_t* ks, const int8_t* vc,
-                    const uint16_t* vs, int64_t npos, int64_t stride, int d, const int8_t* signs,
-                    const uint16_t* kw, const uint16_t* vw, int64_t win, int64_t wstride, double* out) {
+void or_attend_head_fmt(const double* q, const int8_t* kc, const uint16_t* ks, const int8_t* vc,
+                        const uint16_t* vs, int64_t npos, int64_t stride, int d, const int8_t* signs,
+                        const uint16_t* kw, const uint16_t* vw, int64_t win, int64_t wstride, int fmt,
+                        double* out) {
     double* s = (double*)malloc(sizeof(double) * (npos > 0 ? npos : 1));
     double* acc = (double*)calloc(d, sizeof(double));
     double scale = 1.0 / sqrt((double)d);
@@ -527,34 +571,58 @@ void or_attend_head(const double* q, const int8_t* kc, const uint16_t* ks, const
         } else {
             const int8_t* vr = vc + t * stride;
             const uint16_t* vq = vs + t * stride / 32;
-            for (int e = 0; e < d; ++e) acc[e] += pt * ((double)vr[e] * or_f16_to_f64(vq[e / 32]));
+            for (int e = 0; e < d; ++e) acc[e] += pt * (v_level(fmt, vr[e]) * or_f16_to_f64(vq[e / 32]));
         }
     }
-    or_rht_inverse(acc, signs, d, out);
+    /* formats 0 and 2 cache rotated values: undo the rotation once */
+    if (fmt == 1) memcpy(out, acc, sizeof(double) * d);
+    else or_rht_inverse(acc, signs, d, out);
     free(s);
     free(acc);
 }
 
-/* K and V of one kv head into the cache at one position: K int8 per 32 of the
- * fp32 key; V rotated (RHT) then 3-bit per 32; decisions taken in fp32. */
-void or_kv_encode(const double* k, const double* v, const int8_t* signs, int d, int8_t* kc, uint16_t* ks,
-                  int8_t* vc, uint16_t* vs) {
+void or_attend_head(const double* q, const int8_t* kc, const uint16_t* ks, const int8_t* vc,
+                    const uint16_t* vs, int64_t npos, int64_t stride, int d, const int8_t* signs,
+                    const uint16_t* kw, const uint16_t* vw, int64_t win, int64_t wstride, double* out) {
+    or_attend_head_fmt(q, kc, ks, vc, vs, npos, stride, d, signs, kw, vw, win, wstride, 0, out);
+}
+
+/* K and V of one kv head into the cache at one position, decisions taken in
+ * fp32.  Format 0: K int8 per 32 of the fp32 key; V rotated (RHT) then 3-bit
+ * per 32.  Format 1 (q4_0, page 3 "Qwen3.8-27B 實測" and page 4, jdon.com:
+ * both caches at 4 bits for long contexts on small cards): K and V each 4-bit
+ * per 32 with an fp16 scale (the W4 codec), V not rotated.  Format 2: K int8;
+ * V rotated, then the Lloyd-Max codebook per 32. */
+void or_kv_encode_fmt(const double* k, const double* v, const int8_t* signs, int d, int fmt, int8_t* kc,
+                      uint16_t* ks, int8_t* vc, uint16_t* vs) {
     float* tmp = (float*)malloc(sizeof(float) * d);
     double* vr = (double*)malloc(sizeof(double) * d);
     for (int i = 0; i < d; ++i) tmp[i] = (float)k[i];
-    for (int gi = 0; gi < d / 32; ++gi) or_quant_group(tmp + gi * 32, 32, 127, &ks[gi], kc + gi * 32);
-    or_rht_forward(v, signs, d, vr);
+    for (int gi = 0; gi < d / 32; ++gi) or_quant_group(tmp + gi * 32, 32, fmt == 1 ? 7 : 127, &ks[gi], kc + gi * 32);
+    if (fmt == 1) memcpy(vr, v, sizeof(double) * d);
+    else or_rht_forward(v, signs, d, vr);
     for (int i = 0; i < d; ++i) tmp[i] = (float)vr[i];
-    for (int gi = 0; gi < d / 32; ++gi) or_quant_group(tmp + gi * 32, 32, 3, &vs[gi], vc + gi * 32);
+    for (int gi = 0; gi < d / 32; ++gi) {
+        if (fmt == 2) or_quant_group_lm(tmp + gi * 32, 32, &vs[gi], vc + gi * 32);
+        else or_quant_group(tmp + gi * 32, 32, fmt == 1 ? 7 : 3, &vs[gi], vc + gi * 32);
+    }
     free(tmp);
     free(vr);
 }
 
-/* the fp32 key and rotated value the last append quantised (for tie checks) */
-static void kv_record(const double* k, const double* v, const int8_t* signs, int d, float* kl, float* vl) {
+void or_kv_encode(const double* k, const double* v, const int8_t* signs, int d, int8_t* kc, uint16_t* ks,
+                  int8_t* vc, uint16_t* vs) {
+    or_kv_encode_fmt(k, v, signs, d, 0, kc, ks, vc, vs);
+}
+
+/* the fp32 key and (rotated, except in format 1) value the last append
+ * quantised (for tie checks) */
+static void kv_record(const double* k, const double* v, const int8_t* signs, int d, int fmt, float* kl,
+                      float* vl) {
     double* vr = (double*)malloc(sizeof(double) * d);
     for (int i = 0; i < d; ++i) kl[i] = (float)k[i];
-    or_rht_forward(v, signs, d, vr);
+    if (fmt == 1) memcpy(vr, v, sizeof(double) * d);
+    else or_rht_forward(v, signs, d, vr);
     for (int i = 0; i < d; ++i) vl[i] = (float)vr[i];
     free(vr);
 }
@@ -573,9 +641,9 @@ static void attn_mixer(or_model* m, or_layer* L, int64_t t, const double* xh, do
     double* v = k + (int64_t)nkv * d;
     for (int j = 0; j < nkv; ++j) {
         int64_t base = (t * nkv + j) * d;
-        or_kv_encode(k + (int64_t)j * d, v + (int64_t)j * d, m->signs, d, L->kc + base, L->ks + base / 32,
-                     L->vc + base, L->vs + base / 32);
-        kv_record(k + (int64_t)j * d, v + (int64_t)j * d, m->signs, d, L->klast + (int64_t)j * d,
+        or_kv_encode_fmt(k + (int64_t)j * d, v + (int64_t)j * d, m->signs, d, c->kv_format, L->kc + base,
+                         L->ks + base / 32, L->vc + base, L->vs + base / 32);
+        kv_record(k + (int64_t)j * d, v + (int64_t)j * d, m->signs, d, c->kv_format, L->klast + (int64_t)j * d,
                   L->vlast + (int64_t)j * d);
         if (L->win > 0) {
             /* the window keeps the fp32 key and rotated value rounded to fp16 */
@@ -592,9 +660,10 @@ static void attn_mixer(or_model* m, or_layer* L, int64_t t, const double* xh, do
     for (int i = 0; i < nq; ++i) {
         int j = i / ratio;
         int64_t off = (int64_t)j * d;
-        or_attend_head(q + (int64_t)i * d, L->kc + off, L->ks + off / 32, L->vc + off, L->vs + off / 32,
-                       t + 1, (int64_t)nkv * d, d, m->signs, L->win > 0 ? L->kw + off : NULL,
-                       L->win > 0 ? L->vw + off : NULL, L->win, (int64_t)nkv * d, o + (int64_t)i * d);
+        or_attend_head_fmt(q + (int64_t)i * d, L->kc + off, L->ks + off / 32, L->vc + off, L->vs + off / 32,
+                           t + 1, (int64_t)nkv * d, d, m->signs, L->win > 0 ? L->kw + off : NULL,
+                           L->win > 0 ? L->vw + off : NULL, L->win, (int64_t)nkv * d, c->kv_format,
+                           o + (int64_t)i * d);
         for (int e = 0; e < d; ++e)
             o[(int64_t)i * d + e] = to_a16(o[(int64_t)i * d + e] * sigmoid(g[(int64_t)i * d + e]));
     }
@@ -768,7 +837,8 @@ int or_set_dpos(or_model* m, int32_t dpos) {
 /* ------------------------------------------------------------ state import / export
  * Logical state: position; per GDN layer fp32 S [nv][dv][dk]; per attention
  * layer K codes int8 [pos][nkv][dh], K scales fp16 [pos][nkv][dh/32], V codes
- * int8 (-3..3) [pos][nkv][dh], V scales fp16 [pos][nkv][dh/32]. */
+ * int8 [pos][nkv][dh] (format 0: -3..3; format 1: -7..7, keys too; format 2:
+ * level index 0..7), V scales fp16 [pos][nkv][dh/32]. */
 int or_set_state_gdn(or_model* m, int layer, const float* S) {
     if (layer < 0 || layer >= m->c.n_layers || m->L[layer].type != 'G') return -1;
     int64_t n = (int64_t)m->c.gdn_v_heads * m->c.gdn_head_dim * m->c.gdn_head_dim;

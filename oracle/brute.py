@@ -47,6 +47,37 @@ def quant(x, qmax):
     return c.astype(np.int8).reshape(x.shape), s.view(np.uint16)[..., 0]
 
 
+# Max's 8-level Gaussian quantizer (IRE Trans. Inf. Theory, 1960): output
+# level magnitudes, rounded to fp16 for the cache
+LM_MAGNITUDES = (0.2451, 0.7560, 1.3440, 2.1520)
+
+
+def lm_levels():
+    m = np.array(LM_MAGNITUDES, np.float32).astype(np.float16).astype(np.float64)
+    return np.concatenate([-m[::-1], m])
+
+
+def quant_lm(x):
+    """Lloyd-Max group codec along the last axis (groups of 32): scale =
+    fp16(sqrt(mean square)) with the mean square in fp32, code = index of the
+    nearest level to x / scale (the lower one on a tie)"""
+    x = np.asarray(x, np.float32)
+    g = x.reshape(*x.shape[:-1], -1, 32)
+    ms = np.mean(g.astype(np.float64) ** 2, axis=-1, keepdims=True).astype(np.float32)
+    s = np.sqrt(ms).astype(np.float16)
+    sf = s.astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        t = np.where(sf == 0, 0, g / sf).astype(np.float32).astype(np.float64)
+    lv = lm_levels()
+    c = np.argmin(np.abs(t[..., None] - lv), axis=-1)
+    c = np.where(sf == 0, 4, c)
+    return c.astype(np.int8).reshape(x.shape), s.view(np.uint16)[..., 0]
+
+
+def dequant_lm(codes, scales):
+    return lm_levels()[np.asarray(codes, np.int64)] * np.repeat(f16(scales), 32, axis=-1)
+
+
 def rmsnorm(x, w, eps):
     return x / np.sqrt(np.mean(x * x) + eps) * w
 
@@ -116,9 +147,11 @@ class BruteModel:
         g = p[nq * d:2 * nq * d].reshape(nq, d)
         k = p[2 * nq * d:2 * nq * d + nkv * d].reshape(nkv, d)
         v = p[2 * nq * d + nkv * d:].reshape(nkv, d)
-        kc, ks = quant(k, 127)
-        vr = (self.R @ v.T).T
-        vc, vs = quant(vr, 3)
+        fmt = getattr(s, "kv_format", 0)
+        kc, ks = quant(k, 7 if fmt == 1 else 127)
+        vr = v if fmt == 1 else (self.R @ v.T).T       # format 1 keeps values unrotated
+        vc, vs = quant_lm(vr) if fmt == 2 else quant(vr, 7 if fmt == 1 else 3)
+        vdq = dequant_lm if fmt == 2 else dequant_i8
         # the fp32 key and rotated value at fp16, for the recent window
         kh = k.astype(np.float32).astype(np.float16).astype(np.float64)
         vh = vr.astype(np.float32).astype(np.float16).astype(np.float64)
@@ -127,13 +160,14 @@ class BruteModel:
         win = getattr(s, "kv_window", 0) if l < s.n_layers else 0
         w0 = T - win if win > 0 else T          # positions w0.. are read at fp16
         K = np.stack([e[4] if t >= w0 else dequant_i8(e[0], e[1]) for t, e in enumerate(self.kv[l])])
-        Vr = np.stack([e[5] if t >= w0 else dequant_i8(e[2], e[3]) for t, e in enumerate(self.kv[l])])
+        Vr = np.stack([e[5] if t >= w0 else vdq(e[2], e[3]) for t, e in enumerate(self.kv[l])])
         o = np.zeros((nq, d))
         for i in range(nq):
             j = i // (nq // nkv)
             sc = K[:, j, :] @ q[i] / np.sqrt(d)
             pr = softmax(sc)
-            o[i] = a16((self.Rinv @ (pr @ Vr[:, j, :])) * expit(g[i]))
+            acc = pr @ Vr[:, j, :]
+            o[i] = a16((acc if fmt == 1 else self.Rinv @ acc) * expit(g[i]))
         return self.W(l, 1) @ o.ravel()
 
     def block(self, l, t, x):

@@ -31,6 +31,8 @@ class Shape:
     draft_vocab: int = 0    # ids in the draft head's vocabulary map; 0: no draft head
     max_batch: int = 1      # sequences with their own state (batch decode)
     kv_window: int = 0      # recent positions the attention caches also keep at fp16; 0: none
+    kv_format: int = 0      # cache codecs: 0 K int8 + V rotated 3-bit; 1 q4_0 (K, V 4-bit, V not
+                            # rotated); 2 K int8 + V rotated 3-bit Lloyd-Max codebook
 
     @property
     def n_layers(self):
