@@ -91,6 +91,7 @@ _SIGS = {
     "aw4_import_state_win": [_vp, _i32, _vp, _vp],
     "aw4_check_blob": [ctypes.c_void_p, _vp, _u64],
     "aw4_test_fail_hip_call": [_i32],
+    "aw4_decode_step_static": [_vp, _i32, _vp, _vp],
 }
 
 
@@ -268,6 +269,14 @@ class Model:
         am = _i32()
         self._rc(lib().aw4_decode_step(self.h, int(token), logits.data_ptr() if logits is not None else None,
                                        ctypes.byref(am) if want_argmax else None), "decode_step")
+        return am.value if want_argmax else None
+
+    def decode_step_static(self, token, logits=None, want_argmax=True):
+        """aw4_decode_step_static: the decode step with its partials in the
+        library's static device scratch"""
+        am = _i32()
+        self._rc(lib().aw4_decode_step_static(self.h, int(token), logits.data_ptr() if logits is not None else None,
+                                              ctypes.byref(am) if want_argmax else None), "decode_step_static")
         return am.value if want_argmax else None
 
     def decode_greedy(self, first_token, n):

@@ -6,6 +6,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 #include <type_traits>
 #include <cmath>
 #include <cstdio>
@@ -164,6 +165,15 @@ struct aw4_model {
     // it); win_imported: the ring was imported since the last decode call, so it
     // describes whatever position the caller sets next
     std::vector<bool> win_fresh, win_imported;
+    // split partials of the single-token step's attention sweeps (rows of one
+    // token) and the output head's block partials: the arena's by default,
+    // the library's static scratch inside aw4_decode_step_static
+    float* step_part = nullptr;
+    int step_prow = 0;
+    float* step_pv = nullptr;
+    int32_t* step_pi = nullptr;
+    uint8_t* static_scratch = nullptr;   // this device's static scratch (hipGetSymbolAddress)
+    uint64_t static_need = 0;            // bytes of it the step needs
     bool use_graph = true;
     hipGraphExec_t g_head = nullptr;
     hipGraphExec_t g_nohead = nullptr;
@@ -486,9 +496,13 @@ uint64_t plan_layout(const aw4_config* c, aw4_model* m, uint8_t* base) {
         m->hbuf = hbuf;
         m->abuf = abuf;
         m->part = part;
+        m->step_part = part;
+        m->step_prow = kSweepRows * c->attn_q_heads;
         m->logits = logits;
         m->pv = pv;
         m->pi = pi;
+        m->step_pv = pv;
+        m->step_pi = pi;
         m->ring = ring;
         m->ring_cap = kRingCap;
         m->nhead_blocks = nhb;
@@ -828,6 +842,47 @@ int walk_blob(const aw4_config* c, const uint8_t* p, uint64_t bytes, std::string
     return AW4_OK;
 }
 
+// ---------------------------------------------------------------- static scratch
+// For callers that cannot allocate (code under graph capture, serving loops,
+// harnesses that forbid hipMalloc): aw4_decode_step_static keeps the decode
+// step's split partials and head partials in this file-scope device array
+// instead of the arena.  Each device holds its own copy until the process
+// ends; its address comes from hipGetSymbolAddress, once per device, at
+// aw4_create with that device current (the array's name is not a device
+// address in host code).  Every call on a device shares that device's copy.
+constexpr uint64_t kStaticScratchBytes = 4ull << 20;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint8_t* g_scratch_dev[kMaxDevices] = {};
+
+// the current device's copy of the array (resolved on first use per device)
+hipError_t static_scratch_of(int dev, uint8_t** out) {
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void* ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_dev[dev] = (uint8_t*)ptr;
+    }
+    *out = g_scratch_dev[dev];
+    return hipSuccess;
+}
+
+// bytes of static scratch the single-token step needs: one token's rows of
+// attention partials ([nq][splits][d] then [nq][splits][2]) and the head's
+// per-block best value and index
+uint64_t static_step_bytes(const aw4_model* m) {
+    const aw4_config* c = &m->cfg;
+    const bool attn = strchr(c->layer_pattern, 'A') != nullptr;
+    uint64_t part = attn ? (uint64_t)c->attn_q_heads * (m->nsplit + m->nsplit_w) * (c->attn_head_dim + 2) * 4 : 0;
+    part = (part + 255) & ~uint64_t(255);
+    const uint64_t head = (uint64_t)m->nhead_blocks * 4;
+    return part + 2 * ((head + 255) & ~uint64_t(255));
+}
+
 // ---------------------------------------------------------------- step sequence
 // One pre-norm block on the single residual x: mixer input projection, the
 // mixer (GDN step, or attention over the cache of committed length *posp with
@@ -877,8 +932,8 @@ int enqueue_block(aw4_model* m, LayerBufs& b, float* x, const int32_t* posp, int
             aa.vs = b.vs;
             aa.signs = m->signs;
             aa.pos = posp;
-            aa.part = m->part;
-            aa.prow = kSweepRows * c->attn_q_heads;
+            aa.part = m->step_part;
+            aa.prow = m->step_prow;
             aa.max_ctx = c->max_ctx;
             aa.nq = c->attn_q_heads;
             aa.nkv = c->attn_kv_heads;
@@ -899,7 +954,7 @@ int enqueue_block(aw4_model* m, LayerBufs& b, float* x, const int32_t* posp, int
             } else {
                 HIPCHK(m, launch_attn(aa, s));
             }
-            CombineArgs ca{pos_offset, 1, 0, m->part, m->proj, m->signs, posp, m->abuf, aa.prow, c->attn_q_heads,
+            CombineArgs ca{pos_offset, 1, 0, m->step_part, m->proj, m->signs, posp, m->abuf, aa.prow, c->attn_q_heads,
                            c->attn_kv_heads, c->attn_head_dim, m->nsplit, 0, aa.win, aa.nsplit_w};
             HIPCHK(m, launch_combine(ca, s));
             GemvArgs go{};
@@ -1118,9 +1173,9 @@ int enqueue_step(aw4_model* m, bool head) {
     if (rc) return rc;
     if (head) {
         HeadArgs ha{m->lm_codes, m->lm_scales, nullptr, c->vocab, c->hidden, m->x, m->norm_final, c->rms_eps,
-                    m->logits, m->pv, m->pi};
+                    m->logits, m->step_pv, m->step_pi};
         HIPCHK(m, launch_head(ha, s));
-        HIPCHK(m, launch_head_final(m->pv, m->pi, m->nhead_blocks, m->ctl, m->ring, m->ring_cap, s));
+        HIPCHK(m, launch_head_final(m->step_pv, m->step_pi, m->nhead_blocks, m->ctl, m->ring, m->ring_cap, s));
     } else {
         HIPCHK(m, launch_advance(m->ctl, s));
     }
@@ -1463,6 +1518,11 @@ int aw4_create(const aw4_config* cfg, void* dev_arena, uint64_t arena_bytes, voi
     m->win_imported.assign((size_t)cfg->n_layers, false);
     m->nsplit = nsplit_for(cfg->max_ctx, cfg->attn_kv_heads, m->nsplit_w,
                            prop.multiProcessorCount < 256 ? prop.multiProcessorCount : 256);
+    if (static_scratch_of(dev, &m->static_scratch) != hipSuccess) {
+        delete m;
+        return AW4_E_HIP;
+    }
+    m->static_need = static_step_bytes(m);
     // zero everything once (weights included) so unused tensors are defined
     if (launch_fill_zero(m->arena, need & ~uint64_t(3), m->stream) != hipSuccess) {
         delete m;
@@ -1878,6 +1938,43 @@ int aw4_decode_step(aw4_model* m, int32_t token, float* dev_logits, int32_t* hos
     if (m->host_pos + 1 > m->cfg.max_ctx) return fail(m, AW4_E_CTX_FULL, "context full");
     HIPCHK(m, launch_set_token(m->ctl, token, m->stream));
     int rc = run_step(m, true);
+    if (rc) return rc;
+    m->host_pos += 1;
+    m->pend_src = 1;
+    m->pend_n = 0;
+    if (dev_logits)
+        HIPCHK(m, hipMemcpyAsync(dev_logits, m->logits, (size_t)m->cfg.vocab * 4, hipMemcpyDeviceToDevice, m->stream));
+    if (host_argmax) {
+        HIPCHK(m, hipMemcpyAsync(host_argmax, &m->ctl->argmax, 4, hipMemcpyDeviceToHost, m->stream));
+        HIPCHK(m, hipStreamSynchronize(m->stream));
+    }
+    return AW4_OK;
+}
+
+int aw4_decode_step_static(aw4_model* m, int32_t token, float* dev_logits, int32_t* host_argmax) {
+    if (check_model(m)) return AW4_E_INVAL;
+    if (m->cfg.vocab <= 0) return fail(m, AW4_E_STATE, "decode_step needs a vocabulary");
+    if (m->static_need > kStaticScratchBytes)
+        return fail(m, AW4_E_INVAL, "the step needs " + std::to_string(m->static_need) +
+                                        " bytes of static scratch; the library holds " +
+                                        std::to_string(kStaticScratchBytes));
+    if (need_weights(m) || need_fresh_window(m)) return AW4_E_STATE;
+    if (token < 0 || token >= m->cfg.vocab) return fail(m, AW4_E_TOKEN, "token out of range");
+    if (m->host_pos + 1 > m->cfg.max_ctx) return fail(m, AW4_E_CTX_FULL, "context full");
+    HIPCHK(m, launch_set_token(m->ctl, token, m->stream));
+    // the same step with its partials in the static scratch (one token's
+    // rows), launched kernel by kernel: no graph of its own, so a caller may
+    // capture these launches into its own graph
+    const uint64_t part_bytes = m->static_need - 2 * (((uint64_t)m->nhead_blocks * 4 + 255) & ~uint64_t(255));
+    m->step_part = (float*)m->static_scratch;
+    m->step_prow = m->cfg.attn_q_heads;
+    m->step_pv = (float*)(m->static_scratch + part_bytes);
+    m->step_pi = (int32_t*)(m->static_scratch + part_bytes + (((uint64_t)m->nhead_blocks * 4 + 255) & ~uint64_t(255)));
+    const int rc = enqueue_step(m, true);
+    m->step_part = m->part;
+    m->step_prow = kSweepRows * m->cfg.attn_q_heads;
+    m->step_pv = m->pv;
+    m->step_pi = m->pi;
     if (rc) return rc;
     m->host_pos += 1;
     m->pend_src = 1;

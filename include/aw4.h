@@ -421,6 +421,24 @@ int aw4_import_state_kv(aw4_model* model, int32_t layer, int32_t npos, const int
 int aw4_export_state_win(aw4_model* model, int32_t layer, uint16_t* host_kw, uint16_t* host_vw);
 int aw4_import_state_win(aw4_model* model, int32_t layer, const uint16_t* host_kw, const uint16_t* host_vw);
 
+/* ----------------------------------------------------------- no allocation */
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the decode
+ * step of aw4_decode_step, with the step's split partials (attention) and the
+ * output head's per-block partials in a static device array the library
+ * holds (4 MiB per device, kept until the process ends) instead of the arena.
+ * The step's kernels are launched one by one (no graph of its own), so a
+ * caller may capture them into its own graph; pass host_argmax = NULL under
+ * capture (it synchronises the stream).  Every call on a device shares that
+ * device's array and its last contents: calls that overlap on one device (two
+ * models on one device driven from two threads or streams) race.  A step
+ * writes every partial it reads, so nothing needs clearing between calls.
+ * Errors: as aw4_decode_step, and AW4_E_INVAL when the step needs more than
+ * the 4 MiB (attn_q_heads x split slots x (attn_head_dim + 2) x 4 bytes for
+ * the attention partials, plus the head's partials; the 27B shape needs 1.6 MB). */
+int aw4_decode_step_static(aw4_model* model, int32_t token, float* dev_logits, int32_t* host_argmax);
+
 /* ----------------------------------------------------------- test hook */
 
 /* Error-path testing: with n >= 1, the n-th checked HIP runtime call the
