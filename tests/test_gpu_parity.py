@@ -274,13 +274,46 @@ def test_gdn_layer_full_size(aw4):
     assert w < TOL
 
 
-@pytest.mark.parametrize("npos", [0, 4096, 262143])
+def test_gdn_layer_4096_steps(aw4):
+    """The single full-size Gated DeltaNet layer with its FFN for 4096
+    consecutive steps from a zero state (x_t ~ N(0, 1), gates per the recipe),
+    each side on its own state: every step's layer output (output minus input)
+    and the final recurrent state within 1e-2 relative L2."""
+    import torch
+    _say("case: full-size GDN layer, 4096 consecutive steps")
+    shape = W.with_(W.GDN_LAYER, max_ctx=4104)
+    n = 4096
+    gm = _gpu_model(aw4, shape, 7)
+    xin = synth.normal(n, shape.hidden, 1.0, 7, W.STREAM_HIDDEN)
+    xd = torch.from_numpy(np.ascontiguousarray(xin)).cuda()
+    out = torch.empty_like(xd)
+    torch.cuda.synchronize()
+    for t in range(n):
+        gm.decode_hidden(xd[t], out[t])
+    gm.sync()
+    g_out = out.cpu().numpy()
+    g_state = gm.export_gdn(0)
+    gm.close()
+    om = oracle.from_recipe(shape, 7)
+    worst, worst_t = 0.0, -1
+    for t in range(n):
+        xo = om.forward_layers(xin[t].astype(np.float64))
+        e = rel_l2(g_out[t] - xin[t], xo - xin[t])
+        if e > worst:
+            worst, worst_t = e, t
+    es = rel_l2(g_state, om.get_gdn_state(0))
+    _say(f"worst layer-delta rel-L2 {worst:.2e} (step {worst_t}); final state rel-L2 {es:.2e}")
+    assert worst < TOL and es < TOL
+
+
+@pytest.mark.parametrize("npos", [0, 4096, 32767, 131071, 262143])
 def test_attention_layer_full_size(aw4, npos):
     """Full-size gated-attention layer: 24 steps from an empty cache, 4 steps on
-    a 4096-position synthetic cache and 2 steps on a 262,143-position one (the
-    long-context launch: about 32 tiles per wave), teacher-forced."""
+    a 4096-position synthetic cache, 2 steps on 32K and 131K caches and on a
+    262,143-position one (the long-context launch: about 32 tiles per wave),
+    teacher-forced."""
     _say("case: full-size attention layer, cache", npos)
     shape = W.with_(W.ATTN_LAYER, max_ctx=npos + 64)
-    w = _layer_pair(aw4, shape, 5, 24 if npos == 0 else 4 if npos < 100000 else 2, npos=npos)
+    w = _layer_pair(aw4, shape, 5, 24 if npos == 0 else 4 if npos < 8192 else 2, npos=npos)
     _say(f"worst layer-delta rel-L2 {w:.2e}")
     assert w < TOL

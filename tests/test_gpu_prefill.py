@@ -97,9 +97,15 @@ def test_prefill_tiny_grouped_heads(aw4):
 
 def test_prefill_chunked_equals_token_by_token(aw4):
     """The same prompt token by token (chunk 0) and in chunks of 100: the same
-    final state up to rounding (the chunk GEMM multiplies by fp16(code x scale),
-    one rounding of the weight, 2^-12 relative, where the decode kernels keep
-    code and scale apart; measured 1.3e-3 relative on the final hidden state)."""
+    final state up to rounding.  Both paths keep the weights exact (the chunk
+    GEMM multiplies by code x s_hi and code x s_lo, the decode GEMV by code then
+    s), but they sum in fp32 in different orders (32 products per matrix-core
+    step against dot2 chains; one attention split against many), so a cached
+    code whose fp32 value sits at a rounding tie can land on either side, and
+    over 257 positions that are not teacher-forced each such flip moves the
+    later positions a little.  Measured: hidden 4.5e-4, recurrent state 3e-7,
+    0.75% of key codes and 0.02% of value codes one step apart; the bounds are
+    1e-3 and 1%."""
     _say("case: toy stack prefill, chunks of 100 vs token by token")
     shape = W.TOY
     prompt = synth.tokens(257, shape.vocab, 4)
@@ -110,10 +116,16 @@ def test_prefill_chunked_equals_token_by_token(aw4):
         gm.prefill(prompt)
         res.append((gm.read_hidden(), gm.export_gdn(0), gm.export_kv(1, 257), gm.decode_greedy(7, 16)))
         gm.close()
-    assert rel_l2(res[1][0], res[0][0]) < TOL
-    assert rel_l2(res[1][1], res[0][1]) < TOL
-    d = res[1][2][0].astype(int) - res[0][2][0].astype(int)
-    assert np.abs(d).max() <= 1 and (d != 0).mean() < 6e-2
+    eh, es = rel_l2(res[1][0], res[0][0]), rel_l2(res[1][1], res[0][1])
+    dk = res[1][2][0].astype(int) - res[0][2][0].astype(int)
+    dv = res[1][2][2].astype(int) - res[0][2][2].astype(int)
+    first = [int(np.nonzero((dk != 0).reshape(257, -1).any(1) | (dv != 0).reshape(257, -1).any(1))[0][:1].sum())
+             if (dk != 0).any() or (dv != 0).any() else -1]
+    _say(f"chunked vs token by token: hidden {eh:.2e} state {es:.2e} key flips {(dk != 0).mean():.2e} "
+         f"value flips {(dv != 0).mean():.2e} first differing position {first[0]}")
+    assert eh < 1e-3 and es < 1e-3
+    assert np.abs(dk).max() <= 1 and (dk != 0).mean() < 1e-2
+    assert np.abs(dv).max() <= 1 and (dv != 0).mean() < 1e-2
     assert np.array_equal(res[0][3], res[1][3])
 
 
