@@ -30,7 +30,7 @@ class Config(ctypes.Structure):
                 ("attn_q_heads", _i32), ("attn_kv_heads", _i32), ("attn_head_dim", _i32),
                 ("group", _i32), ("max_ctx", _i32), ("max_verify", _i32), ("rms_eps", _f32),
                 ("layer_pattern", ctypes.c_char * 128), ("draft_vocab", _i32), ("max_batch", _i32),
-                ("kv_window", _i32)]
+                ("kv_window", _i32), ("kv_format", _i32)]
 
     @classmethod
     def from_shape(cls, s):
@@ -44,6 +44,7 @@ class Config(ctypes.Structure):
         c.draft_vocab = int(getattr(s, "draft_vocab", 0))
         c.max_batch = int(getattr(s, "max_batch", 1))
         c.kv_window = int(getattr(s, "kv_window", 0))
+        c.kv_format = int(getattr(s, "kv_format", 0))
         return c
 
 
@@ -92,6 +93,7 @@ _SIGS = {
     "aw4_check_blob": [ctypes.c_void_p, _vp, _u64],
     "aw4_test_fail_hip_call": [_i32],
     "aw4_decode_step_static": [_vp, _i32, _vp, _vp],
+    "aw4_time_stream_read": [_vp, _u64, _vp, _vp, _i32, ctypes.POINTER(_f32)],
 }
 
 
@@ -149,6 +151,18 @@ def check_blob(shape_or_cfg, blob):
     c = shape_or_cfg if isinstance(shape_or_cfg, Config) else Config.from_shape(shape_or_cfg)
     p, n, _keep = _blob_ptr(blob)
     return lib().aw4_check_blob(ctypes.byref(c), p, n)
+
+
+def time_stream_read(buf, sink, stream, reps):
+    """aw4_time_stream_read over a device tensor buf (its bytes); sink: a
+    device tensor of at least 8 KB; stream: a torch stream.  -> average us"""
+    us = _f32()
+    nbytes = buf.numel() * buf.element_size() // 16 * 16
+    rc = lib().aw4_time_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), stream.cuda_stream, int(reps),
+                                    ctypes.byref(us))
+    if rc != AW4_OK:
+        raise AW4Error(rc, "aw4_time_stream_read")
+    return us.value
 
 
 def test_fail_hip_call(n):

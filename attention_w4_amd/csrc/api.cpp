@@ -236,11 +236,27 @@ int64_t mix_out_cols(const aw4_config* c, char t) {
 // position's record.
 int kv_key_byte(int e, int d) { return 8 * (d / 32) * ((e & 31) >> 3) + 8 * (e >> 5) + (e & 7); }
 int kv_value_bit(int e, int d) { return 3 * ((d / 16) * (e & 15) + (e >> 4)); }
+// 4-bit keys (kv_format 1): logical dim e = 32 g + 8 q + i is the nibble (code
+// + 8) at slot [0,2,4,6,1,3,5,7][i] of dword q (d/32) + g of the row
+int kv_key_nib_bit(int e, int d) { return 32 * (((e & 31) >> 3) * (d / 32) + (e >> 5)) + 4 * w4_slot(e & 7); }
+// value fields of FB bits: logical dim e's field starts at FB ((d/16)(e % 16) + e / 16)
+int kv_value_bit_fb(int e, int d, int fb) { return fb * ((d / 16) * (e & 15) + (e >> 4)); }
+// codebook indices 0..7 (ascending levels) <-> sign-magnitude fields (bit 2: negative)
+uint32_t lm_field(int c) { return c >= 4 ? (uint32_t)(c - 4) : (uint32_t)(7 - c); }
+int lm_code(uint32_t f) { return (f & 4) ? 7 - (int)f : (int)f + 4; }
+
 uint32_t kv_value_field(const uint32_t* rec, int words, int bit) {
     const int wi = bit >> 5, off = bit & 31;
     uint64_t x = rec[wi];
     if (wi + 1 < words) x |= (uint64_t)rec[wi + 1] << 32;
     return (uint32_t)(x >> off) & 7u;
+}
+
+uint32_t kv_value_field(const uint32_t* rec, int words, int bit, int fb) {
+    const int wi = bit >> 5, off = bit & 31;
+    uint64_t x = rec[wi];
+    if (wi + 1 < words) x |= (uint64_t)rec[wi + 1] << 32;
+    return (uint32_t)(x >> off) & ((1u << fb) - 1u);
 }
 
 // Splits of the recent window's sweep per kv head: about 64 positions each, at
@@ -336,10 +352,12 @@ uint64_t plan_layout(const aw4_config* c, aw4_model* m, uint8_t* base) {
         if (b.type == 'G') {
             b.S = p.take<float>((uint64_t)c->gdn_v_heads * c->gdn_head_dim * c->gdn_head_dim * 4);
         } else {
+            // keys: 1 byte per dim (4-bit cache: half); values: 3 (4) bits per dim
             const uint64_t n = (uint64_t)c->attn_kv_heads * c->max_ctx * c->attn_head_dim;
-            b.kc = p.take<int8_t>(n);
+            const bool q4 = c->kv_format == 1;
+            b.kc = p.take<int8_t>(q4 ? n / 2 : n);
             b.ks = p.take<uint16_t>(n / 32 * 2);
-            b.vc = p.take<uint32_t>(n / 32 * 12);
+            b.vc = p.take<uint32_t>(n / 32 * (q4 ? 16 : 12));
             b.vs = p.take<uint16_t>(n / 32 * 2);
             if (c->kv_window > 0) {
                 const uint64_t nw = (uint64_t)c->attn_kv_heads * c->kv_window * c->attn_head_dim;
@@ -508,7 +526,8 @@ uint64_t plan_layout(const aw4_config* c, aw4_model* m, uint8_t* base) {
         m->nhead_blocks = nhb;
         m->nsplit = nsplit;
         m->nsplit_w = nsplit_w;
-        if (c->kv_window > 0) m->pchunk_max = m->pchunk = 0;   // prefill runs token by token
+        // prefill runs token by token with a recent window or the 4-bit and codebook caches
+        if (c->kv_window > 0 || c->kv_format != 0) m->pchunk_max = m->pchunk = 0;
         m->state_off = state_off;
         m->state_bytes = state_bytes;
         m->max_batch = nbatch;
@@ -555,6 +574,9 @@ const char* check_config(const aw4_config* c) {
     if (c->kv_window < 0 || c->kv_window > c->max_ctx) return "kv_window must be in [0, max_ctx]";
     if (c->kv_window > 0 && (c->max_batch > 1 || c->draft_vocab > 0))
         return "kv_window needs max_batch <= 1 and no draft head (single-sequence decode only)";
+    if (c->kv_format < 0 || c->kv_format > 2) return "kv_format must be 0, 1 or 2";
+    if (c->kv_format != 0 && (c->kv_window > 0 || c->max_batch > 1 || c->draft_vocab > 0))
+        return "kv_format 1 and 2 need no recent window, max_batch <= 1 and no draft head";
     if (!(c->rms_eps > 0.f) || !std::isfinite(c->rms_eps)) return "rms_eps must be positive";
     return nullptr;
 }
@@ -939,6 +961,7 @@ int enqueue_block(aw4_model* m, LayerBufs& b, float* x, const int32_t* posp, int
             aa.nkv = c->attn_kv_heads;
             aa.d = c->attn_head_dim;
             aa.nsplit = m->nsplit;
+            aa.fmt = c->kv_format;
             if (b.kw) {
                 // recent window: the sweep before the window, then the
                 // window's sweep, which appends the token (codes and fp16
@@ -955,7 +978,7 @@ int enqueue_block(aw4_model* m, LayerBufs& b, float* x, const int32_t* posp, int
                 HIPCHK(m, launch_attn(aa, s));
             }
             CombineArgs ca{pos_offset, 1, 0, m->step_part, m->proj, m->signs, posp, m->abuf, aa.prow, c->attn_q_heads,
-                           c->attn_kv_heads, c->attn_head_dim, m->nsplit, 0, aa.win, aa.nsplit_w};
+                           c->attn_kv_heads, c->attn_head_dim, m->nsplit, 0, aa.win, aa.nsplit_w, c->kv_format};
             HIPCHK(m, launch_combine(ca, s));
             GemvArgs go{};
             go.codes = b.w_out;
@@ -2021,6 +2044,7 @@ int aw4_verify_k(aw4_model* m, const int32_t* host_tokens, int32_t k, const floa
     if (c->vocab <= 0) return fail(m, AW4_E_STATE, "verify_k needs a vocabulary");
     if (need_weights(m)) return AW4_E_STATE;
     if (c->kv_window > 0) return fail(m, AW4_E_INVAL, "verify_k does not read a recent window");
+    if (c->kv_format != 0) return fail(m, AW4_E_INVAL, "verify_k reads the int8 / 3-bit cache only (kv_format 0)");
     if (k < 0 || k + 1 > c->max_verify) return fail(m, AW4_E_INVAL, "k must be in [0, max_verify - 1]");
     if (!(temperature >= 0.f) || !std::isfinite(temperature)) return fail(m, AW4_E_INVAL, "temperature must be >= 0");
     if (temperature > 0.f && (!host_u || (k > 0 && !dev_q)))
@@ -2209,25 +2233,35 @@ int aw4_export_state_kv(aw4_model* m, int32_t layer, int32_t npos, int8_t* kc, u
     if (check_model(m) || !kc || !ks || !vc || !vs || !lb) return fail(m, AW4_E_INVAL, "not an attention layer");
     const aw4_config* c = &m->cfg;
     if (npos < 0 || npos > c->max_ctx) return fail(m, AW4_E_INVAL, "npos outside [0, max_ctx]");
-    const int nkv = c->attn_kv_heads, d = c->attn_head_dim, NG = d / 32, VW = 3 * NG;
+    const int nkv = c->attn_kv_heads, d = c->attn_head_dim, NG = d / 32;
+    const int fmt = layer == c->n_layers ? 0 : c->kv_format;   // the draft head's cache is format 0
+    const int FB = fmt == 1 ? 4 : 3, VW = FB * NG, KR = fmt == 1 ? d / 2 : d;
     LayerBufs& b = *lb;
     HIPCHK(m, hipStreamSynchronize(m->stream));
-    std::vector<int8_t> k((size_t)npos * d);
+    std::vector<int8_t> k((size_t)npos * KR);
     std::vector<uint16_t> s1((size_t)npos * NG), s2((size_t)npos * NG);
     std::vector<uint32_t> v((size_t)npos * VW + 1);
     for (int j = 0; j < nkv && npos > 0; ++j) {
         const int64_t hb = (int64_t)j * c->max_ctx;
-        HIPCHK(m, hipMemcpy(k.data(), b.kc + hb * d, (size_t)npos * d, hipMemcpyDeviceToHost));
+        HIPCHK(m, hipMemcpy(k.data(), b.kc + hb * KR, (size_t)npos * KR, hipMemcpyDeviceToHost));
         HIPCHK(m, hipMemcpy(s1.data(), b.ks + hb * NG, s1.size() * 2, hipMemcpyDeviceToHost));
         HIPCHK(m, hipMemcpy(s2.data(), b.vs + hb * NG, s2.size() * 2, hipMemcpyDeviceToHost));
         HIPCHK(m, hipMemcpy(v.data(), b.vc + hb * VW, (size_t)npos * VW * 4, hipMemcpyDeviceToHost));
         for (int t = 0; t < npos; ++t) {
             const int64_t lo = ((int64_t)t * nkv + j);
-            const int8_t* kr = k.data() + (size_t)t * d;
+            const int8_t* kr = k.data() + (size_t)t * KR;
             const uint32_t* rec = v.data() + (size_t)t * VW;
             for (int e = 0; e < d; ++e) {
-                kc[lo * d + e] = (int8_t)((int)(uint8_t)kr[kv_key_byte(e, d)] - 128);
-                vc[lo * d + e] = (int8_t)((int)kv_value_field(rec, VW, kv_value_bit(e, d)) - 4);
+                if (fmt == 1) {
+                    const int kb = kv_key_nib_bit(e, d);
+                    kc[lo * d + e] = (int8_t)((int)((((const uint32_t*)kr)[kb >> 5] >> (kb & 31)) & 15u) - 8);
+                    const uint32_t f = kv_value_field(rec, VW, kv_value_bit_fb(e, d, 4), 4);
+                    vc[lo * d + e] = (int8_t)((int)f - 8);
+                } else {
+                    kc[lo * d + e] = (int8_t)((int)(uint8_t)kr[kv_key_byte(e, d)] - 128);
+                    const uint32_t f = kv_value_field(rec, VW, kv_value_bit(e, d));
+                    vc[lo * d + e] = (int8_t)(fmt == 2 ? lm_code(f) : (int)f - 4);
+                }
             }
             memcpy(ks + lo * NG, s1.data() + (size_t)t * NG, (size_t)NG * 2);
             memcpy(vs + lo * NG, s2.data() + (size_t)t * NG, (size_t)NG * 2);
@@ -2242,32 +2276,49 @@ int aw4_import_state_kv(aw4_model* m, int32_t layer, int32_t npos, const int8_t*
     if (check_model(m) || !kc || !ks || !vc || !vs || !lb) return fail(m, AW4_E_INVAL, "not an attention layer");
     const aw4_config* c = &m->cfg;
     if (npos < 0 || npos > c->max_ctx) return fail(m, AW4_E_INVAL, "npos outside [0, max_ctx]");
-    const int nkv = c->attn_kv_heads, d = c->attn_head_dim, NG = d / 32, VW = 3 * NG;
-    for (int64_t i = 0; i < (int64_t)npos * nkv * d; ++i)
-        if (vc[i] < -3 || vc[i] > 3) return fail(m, AW4_E_INVAL, "V codes must be in -3..3");
+    const int nkv = c->attn_kv_heads, d = c->attn_head_dim, NG = d / 32;
+    const int fmt = layer == c->n_layers ? 0 : c->kv_format;   // the draft head's cache is format 0
+    const int FB = fmt == 1 ? 4 : 3, VW = FB * NG, KR = fmt == 1 ? d / 2 : d;
+    const int vlo = fmt == 1 ? -7 : fmt == 2 ? 0 : -3, vhi = fmt == 1 ? 7 : fmt == 2 ? 7 : 3;
+    for (int64_t i = 0; i < (int64_t)npos * nkv * d; ++i) {
+        if (vc[i] < vlo || vc[i] > vhi)
+            return fail(m, AW4_E_INVAL, "V codes must be in " + std::to_string(vlo) + ".." + std::to_string(vhi));
+        if (fmt == 1 && (kc[i] < -7 || kc[i] > 7)) return fail(m, AW4_E_INVAL, "K codes must be in -7..7");
+    }
     LayerBufs& b = *lb;
     HIPCHK(m, hipStreamSynchronize(m->stream));
-    std::vector<int8_t> k((size_t)npos * d);
+    std::vector<int8_t> k((size_t)npos * KR);
     std::vector<uint16_t> s1((size_t)npos * NG), s2((size_t)npos * NG);
     std::vector<uint32_t> v((size_t)npos * VW);
     for (int j = 0; j < nkv && npos > 0; ++j) {
         std::fill(v.begin(), v.end(), 0u);
+        std::fill(k.begin(), k.end(), (int8_t)0);
         for (int t = 0; t < npos; ++t) {
             const int64_t lo = ((int64_t)t * nkv + j);
-            int8_t* kr = k.data() + (size_t)t * d;
+            int8_t* kr = k.data() + (size_t)t * KR;
             uint32_t* rec = v.data() + (size_t)t * VW;
             for (int e = 0; e < d; ++e) {
-                kr[kv_key_byte(e, d)] = (int8_t)(uint8_t)((int)kc[lo * d + e] + 128);
-                const uint32_t n = (uint32_t)(vc[lo * d + e] + 4) & 7u;
-                const int bit = kv_value_bit(e, d), wi = bit >> 5, off = bit & 31;
+                uint32_t n;
+                int bit;
+                if (fmt == 1) {
+                    const int kb = kv_key_nib_bit(e, d);
+                    ((uint32_t*)kr)[kb >> 5] |= ((uint32_t)(kc[lo * d + e] + 8) & 15u) << (kb & 31);
+                    n = (uint32_t)(vc[lo * d + e] + 8) & 15u;
+                    bit = kv_value_bit_fb(e, d, 4);
+                } else {
+                    kr[kv_key_byte(e, d)] = (int8_t)(uint8_t)((int)kc[lo * d + e] + 128);
+                    n = fmt == 2 ? lm_field(vc[lo * d + e]) : (uint32_t)(vc[lo * d + e] + 4) & 7u;
+                    bit = kv_value_bit(e, d);
+                }
+                const int wi = bit >> 5, off = bit & 31;
                 rec[wi] |= n << off;
-                if (off > 29) rec[wi + 1] |= n >> (32 - off);
+                if (off > 32 - FB) rec[wi + 1] |= n >> (32 - off);
             }
             memcpy(s1.data() + (size_t)t * NG, ks + lo * NG, (size_t)NG * 2);
             memcpy(s2.data() + (size_t)t * NG, vs + lo * NG, (size_t)NG * 2);
         }
         const int64_t hb = (int64_t)j * c->max_ctx;
-        HIPCHK(m, hipMemcpy(b.kc + hb * d, k.data(), k.size(), hipMemcpyHostToDevice));
+        HIPCHK(m, hipMemcpy(b.kc + hb * KR, k.data(), k.size(), hipMemcpyHostToDevice));
         HIPCHK(m, hipMemcpy(b.ks + hb * NG, s1.data(), s1.size() * 2, hipMemcpyHostToDevice));
         HIPCHK(m, hipMemcpy(b.vs + hb * NG, s2.data(), s2.size() * 2, hipMemcpyHostToDevice));
         HIPCHK(m, hipMemcpy(b.vc + hb * VW, v.data(), v.size() * 4, hipMemcpyHostToDevice));

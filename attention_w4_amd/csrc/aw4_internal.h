@@ -135,6 +135,7 @@ struct AttnArgs {
     int32_t win, nsplit_w;
     _Float16* kw;
     _Float16* vw;
+    int32_t fmt;              // cache format (k_attn.hip): 0 int8 K + rotated 3-bit V, 1 q4_0, 2 codebook V
 };
 
 struct CombineArgs {
@@ -150,6 +151,7 @@ struct CombineArgs {
     int32_t nq, nkv, d, nsplit;
     int32_t batch;            // 1: token m is sequence m's single token at pos[m]
     int32_t win, nsplit_w;    // recent window (AttnArgs): the window's splits follow the others
+    int32_t fmt;              // cache format: 1 keeps values unrotated
 };
 
 struct GdnMultiArgs {
@@ -285,6 +287,8 @@ hipError_t launch_advance(Ctl* ctl, hipStream_t s);
 hipError_t launch_set_ctl(Ctl* ctl, int32_t pos, int32_t token, int32_t nstep, hipStream_t s);
 hipError_t launch_fill_zero(void* p, uint64_t bytes, hipStream_t s);
 hipError_t launch_copy_f32(float* dst, const float* src, int64_t n, hipStream_t s);
+// plain streaming read of bytes (a multiple of 16) by nblocks workgroups; sink [nblocks]
+hipError_t launch_stream_read(const void* src, uint64_t bytes, uint32_t* sink, int nblocks, hipStream_t s);
 hipError_t launch_draft_embed(const DraftEmbedArgs& a, hipStream_t s);
 hipError_t launch_draft_select(const DraftSelArgs& a, hipStream_t s);
 int draft_chunks(int Vd);

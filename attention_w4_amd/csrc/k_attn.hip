@@ -57,6 +57,55 @@ __device__ __forceinline__ int k_byte(int d) {
     return 8 * (D / 32) * ((d & 31) >> 3) + 8 * (d >> 5) + (d & 7);
 }
 
+// Cache formats.  0: keys int8, values rotated then 3-bit codes -3..3 (field
+// code + 4).  1 (q4_0: page 3 "Qwen3.8-27B 實測", section "RTX 5090 32GB", and
+// page 4, jdon.com, on 262K contexts): keys and values 4-bit codes -7..7 per 32
+// with an fp16 scale, values not rotated; a key row holds, per lane quarter q,
+// one dword per scale group g (dword q NG + g) whose nibbles (code + 8) carry
+// dims 32 g + 8 q + e in the slot order [0,2,4,6,1,3,5,7]; value fields are
+// 4-bit (code + 8).  2: keys int8; values rotated, then the index of the
+// nearest level of the 8-level Lloyd-Max Gaussian codebook, stored as a 3-bit
+// sign (bit 2, set for the four negative levels) and magnitude (bits 0-1) field.
+template <int FMT>
+struct KvFmt {
+    static constexpr int KB = FMT == 1 ? 4 : 8;       // key bits
+    static constexpr int FB = FMT == 1 ? 4 : 3;       // value field bits
+    static constexpr bool ROT = FMT != 1;             // values cached in the rotated domain
+    static constexpr int KQMAX = FMT == 1 ? 7 : 127;
+};
+
+// Lloyd-Max codebook magnitudes (J. Max 1960, 8 levels for a unit Gaussian) as
+// fp16: 0.2451, 0.7560, 1.3440, 2.1520, in the byte order a v_perm_b32 table
+// needs (magnitude m at bytes 2 m, 2 m + 1 of the 8-byte pair hi:lo)
+__device__ __forceinline__ void lm_table(uint32_t& lo, uint32_t& hi) {
+    const _Float16 m0 = (_Float16)0.2451f, m1 = (_Float16)0.7560f, m2 = (_Float16)1.3440f, m3 = (_Float16)2.1520f;
+    lo = (uint32_t)__builtin_bit_cast(uint16_t, m0) | ((uint32_t)__builtin_bit_cast(uint16_t, m1) << 16);
+    hi = (uint32_t)__builtin_bit_cast(uint16_t, m2) | ((uint32_t)__builtin_bit_cast(uint16_t, m3) << 16);
+}
+
+// two sign-magnitude codebook fields (bits 0-2 and 16-18 of x) -> the two fp16 levels
+__device__ __forceinline__ h2 lm_pair(uint32_t x, uint32_t tlo, uint32_t thi) {
+    const uint32_t mag = x & 0x00030003u;
+    const uint32_t sel = mag * 0x0202u + 0x01000100u;   // 2 m and 2 m + 1 in each half
+    const uint32_t v = __builtin_amdgcn_perm(thi, tlo, sel);
+    return __builtin_bit_cast(h2, v ^ ((x & 0x00040004u) << 13));
+}
+
+// eight 4-bit key fields of one dword (slot order [0,2,4,6,1,3,5,7], nibble =
+// code + 8) -> the eight exact fp16 codes
+__device__ __forceinline__ h8 nib8_to_h8(uint32_t w) {
+    const h2 off_lo = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+    const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+    const h2 off_hi = {(_Float16)-72.0f, (_Float16)-72.0f};
+    const uint32_t w8 = w >> 8;
+    const h2 p0 = __builtin_bit_cast(h2, (w & 0x000F000Fu) | 0x64006400u) + off_lo;
+    const h2 p1 = __builtin_elementwise_fma(__builtin_bit_cast(h2, (w & 0x00F000F0u) | 0x64006400u), sixteenth, off_hi);
+    const h2 p2 = __builtin_bit_cast(h2, (w8 & 0x000F000Fu) | 0x64006400u) + off_lo;
+    const h2 p3 = __builtin_elementwise_fma(__builtin_bit_cast(h2, (w8 & 0x00F000F0u) | 0x64006400u), sixteenth, off_hi);
+    const h8 r = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+    return r;
+}
+
 // eight offset-binary bytes u = b + 128 (little endian in x0, x1) -> the eight
 // exact fp16 values b: 0x6400 | u is the half 1024 + u
 __device__ __forceinline__ h8 u8x8_to_h8(uint32_t x0, uint32_t x1) {
@@ -72,11 +121,12 @@ __device__ __forceinline__ h8 u8x8_to_h8(uint32_t x0, uint32_t x1) {
 // Encode one token (quantise K; sign flip, fast Walsh-Hadamard transform,
 // quantise V) and write it at cache row prow (kv-head base + position): one
 // wave, lane holding dims P lane .. P lane + P - 1; vq is D bytes of LDS.
-template <int D>
+template <int D, int FMT = 0>
 __device__ void encode_append(const float* kp, const float* vp, const float* signs, int8_t* kc, uint16_t* ks,
                               uint32_t* vc, uint16_t* vs, int64_t prow, uint8_t* vq, int lane,
                               _Float16* kwr = nullptr, _Float16* vwr = nullptr) {
-    constexpr int NG = D / 32, NB = D / 16, VW = 3 * NG;
+    typedef KvFmt<FMT> F;
+    constexpr int NG = D / 32, NB = D / 16, VW = F::FB * D / 32;
     const float qscale = 1.0f / sqrtf((float)D);
     constexpr int P = D / 64;                 // dims per lane: d = P lane + i
     constexpr int GL = 32 / P;                // lanes per scale group
@@ -84,7 +134,7 @@ __device__ void encode_append(const float* kp, const float* vp, const float* sig
 #pragma unroll
     for (int i = 0; i < P; ++i) {
         kv[i] = kp[P * lane + i];
-        v[i] = vp[P * lane + i] * signs[P * lane + i];
+        v[i] = F::ROT ? vp[P * lane + i] * signs[P * lane + i] : vp[P * lane + i];
     }
     // recent window (kwr non-null): the fp32 key and, below, the fp32 rotated
     // value are also kept rounded to fp16
@@ -96,7 +146,7 @@ __device__ void encode_append(const float* kp, const float* vp, const float* sig
     for (int i = 0; i < P; ++i) am = fmaxf(am, fabsf(kv[i]));
 #pragma unroll
     for (int o = 1; o < GL; o <<= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
-    {
+    if (F::KB == 8) {
         const _Float16 sh = (_Float16)(am / 127.0f);
         const float sc = (float)sh;
         uint32_t packed = 0;
@@ -110,10 +160,31 @@ __device__ void encode_append(const float* kp, const float* vp, const float* sig
         if (P == 4) *(uint32_t*)(kc + prow * D + k_byte<D>(P * lane)) = packed;
         else kc[prow * D + k_byte<D>(lane)] = (int8_t)(uint8_t)packed;
         if (lane % GL == 0) ks[prow * NG + lane / GL] = __builtin_bit_cast(uint16_t, sh);
+    } else {
+        // 4-bit keys: dim 32 g + 8 q + e goes to nibble slot [0,2,4,6,1,3,5,7][e]
+        // of dword q NG + g; the 8 / P lanes sharing a dword merge their nibbles
+        const _Float16 sh = (_Float16)(am / 7.0f);
+        const float sc = (float)sh;
+        uint32_t part = 0;
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            float cd = sc == 0.f ? 0.f : rintf(kv[i] / sc);
+            cd = fminf(fmaxf(cd, -7.f), 7.f);
+            const int d = P * lane + i, e = d & 7;
+            part |= (uint32_t)((int)cd + 8) << (4 * w4_slot(e));
+        }
+#pragma unroll
+        for (int o = 1; o < 8 / P; o <<= 1) part |= __shfl_xor(part, o, 64);
+        const int d0 = P * lane;
+        if ((d0 & 7) == 0) {
+            const int g = d0 >> 5, qq = (d0 & 31) >> 3;
+            ((uint32_t*)kc)[prow * (D / 8) + qq * NG + g] = part;
+        }
+        if (lane % GL == 0) ks[prow * NG + lane / GL] = __builtin_bit_cast(uint16_t, sh);
     }
     // Sylvester transform, stage by stage in the order of the index bits
 #pragma unroll
-    for (int hh = 1; hh < D; hh <<= 1) {
+    for (int hh = 1; hh < D && F::ROT; hh <<= 1) {
         if (hh < P) {
 #pragma unroll
             for (int i = 0; i < P; ++i)
@@ -132,24 +203,50 @@ __device__ void encode_append(const float* kp, const float* vp, const float* sig
         }
     }
     am = 0.f;
+    float ss = 0.f;
 #pragma unroll
     for (int i = 0; i < P; ++i) {
-        v[i] *= qscale;   // 1/sqrt(D): a power of two for D = 64, 256
+        if (F::ROT) v[i] *= qscale;   // 1/sqrt(D): a power of two for D = 64, 256
         am = fmaxf(am, fabsf(v[i]));
+        ss += v[i] * v[i];
     }
     if (vwr)
 #pragma unroll
         for (int i = 0; i < P; ++i) vwr[P * lane + i] = (_Float16)v[i];
 #pragma unroll
-    for (int o = 1; o < GL; o <<= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
-    {
-        const _Float16 sh = (_Float16)(am / 3.0f);
+    for (int o = 1; o < GL; o <<= 1) {
+        am = fmaxf(am, __shfl_xor(am, o, 64));
+        ss += __shfl_xor(ss, o, 64);
+    }
+    if (FMT == 2) {
+        // codebook: scale fp16(root mean square), the nearest level of v / s
+        // (ties to the lower level) as a sign-magnitude field
+        const _Float16 sh = (_Float16)sqrtf(ss / 32.0f);
+        const float sc = (float)sh;
+        const float l0 = (float)(_Float16)0.2451f, l1 = (float)(_Float16)0.7560f, l2 = (float)(_Float16)1.3440f,
+                    l3 = (float)(_Float16)2.1520f;
+        const float m01 = 0.5f * (l0 + l1), m12 = 0.5f * (l1 + l2), m23 = 0.5f * (l2 + l3);
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            int f = 0;   // sc == 0: level +0.2451 x 0
+            if (sc != 0.f) {
+                const float t = v[i] / sc;
+                const int c = (t > -m23) + (t > -m12) + (t > -m01) + (t > 0.f) + (t > m01) + (t > m12) + (t > m23);
+                f = c >= 4 ? c - 4 : 7 - c;
+            }
+            vq[P * lane + i] = (uint8_t)f;
+        }
+        if (lane % GL == 0) vs[prow * NG + lane / GL] = __builtin_bit_cast(uint16_t, sh);
+    } else {
+        constexpr float vq_max = FMT == 1 ? 7.0f : 3.0f;
+        constexpr int vq_off = FMT == 1 ? 8 : 4;
+        const _Float16 sh = (_Float16)(am / vq_max);
         const float sc = (float)sh;
 #pragma unroll
         for (int i = 0; i < P; ++i) {
             float cd = sc == 0.f ? 0.f : rintf(v[i] / sc);
-            cd = fminf(fmaxf(cd, -3.f), 3.f);
-            vq[P * lane + i] = (uint8_t)((int)cd + 4);
+            cd = fminf(fmaxf(cd, -vq_max), vq_max);
+            vq[P * lane + i] = (uint8_t)((int)cd + vq_off);
         }
         if (lane % GL == 0) vs[prow * NG + lane / GL] = __builtin_bit_cast(uint16_t, sh);
     }
@@ -157,16 +254,16 @@ __device__ void encode_append(const float* kp, const float* vp, const float* sig
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     if (lane < VW) {
-        // word lane of the record: 3-bit slots f = NB (d % 16) + d / 16 overlapping its bits
+        // word lane of the record: FB-bit fields f = NB (d % 16) + d / 16 overlapping its bits
         uint32_t word = 0;
         const int lo = 32 * lane;
-        const int f0 = lo / 3 > 0 ? lo / 3 - 1 : 0;
-        const int f1 = min(D - 1, (lo + 31) / 3);
+        const int f0 = lo / F::FB > 0 ? lo / F::FB - 1 : 0;
+        const int f1 = min(D - 1, (lo + 31) / F::FB);
         for (int f = f0; f <= f1; ++f) {
             const int d = 16 * (f % NB) + f / NB;
             const uint32_t n = vq[d];
-            const int sft = 3 * f - lo;
-            if (sft >= 32 || sft <= -3) continue;
+            const int sft = F::FB * f - lo;
+            if (sft >= 32 || sft <= -F::FB) continue;
             word |= sft >= 0 ? n << sft : n >> (-sft);
         }
         vc[prow * VW + lane] = word;
@@ -178,12 +275,15 @@ __device__ void encode_append(const float* kp, const float* vp, const float* sig
 // column c of the score product is token c / G, head c % G (QC = G NT <= 16
 // columns), and token m sees positions up to its own.  Grid z: blocks of NT
 // tokens of a longer run (a prefill chunk), block b taking tokens b NT ...
-template <int D, int G, int NT>
+template <int D, int G, int NT, int FMT = 0>
 __global__ __launch_bounds__(512, 1) void k_attn(AttnArgs a) {
+    typedef KvFmt<FMT> F;
     constexpr int NG = D / 32;          // scale groups
     constexpr int NB = D / 16;          // 16-dim blocks of the value product
-    constexpr int VW = 3 * NG;          // 32-bit words per value record
-    constexpr int VB = 3 * NB;          // value bits per lane slot
+    constexpr int VW = F::FB * NG;      // 32-bit words per value record
+    constexpr int VB = F::FB * NB;      // value bits per lane slot
+    constexpr int KROW = D * F::KB / 8; // key bytes per position
+    constexpr int KW = NG * F::KB / 4;  // key dwords a lane loads per position (its quarter)
     constexpr int HPL = NG / 2;         // staged scale halves per lane (NG >= 2)
     constexpr int QC = G * NT;          // query columns
     static_assert(G >= 1 && QC <= 16 && NG >= 2, "shape");
@@ -222,7 +322,7 @@ __global__ __launch_bounds__(512, 1) void k_attn(AttnArgs a) {
 
     // raw words of one tile for this lane
     struct Raw {
-        uint4 k[NG / 2];           // key bytes of position tile0 + c, quarter q
+        uint32_t k[KW];            // key codes of position tile0 + c, quarter q
         uint32_t vlo[4], vhi[4];   // value words of positions tile0 + 4 q + r
         uint32_t sc[2];            // HPL staged scale halves
         bool sv;                   // their position is inside the range
@@ -237,15 +337,26 @@ __global__ __launch_bounds__(512, 1) void k_attn(AttnArgs a) {
     const uint16_t* sbase = ssel ? vs : ks;
 
     // per-head bases; offsets inside a head fit 32 bits (max_ctx * D < 2^31)
-    const int8_t* khead = kc + hbase * D;
+    const int8_t* khead = kc + hbase * KROW;
     const uint32_t* vhead = vc + hbase * VW;
     const uint16_t* shead = sbase + hbase * NG;
     auto load = [&](int tile0, Raw& r) {
         {
             const int p = min(tile0 + c, t1 - 1);
-            const uint4* kp = (const uint4*)(khead + (p * D + 8 * NG * q));
+            const uint32_t* kp = (const uint32_t*)(khead + (p * KROW + 4 * KW * q));
+            if (KW % 4 == 0) {
 #pragma unroll
-            for (int i = 0; i < NG / 2; ++i) r.k[i] = kp[i];
+                for (int i = 0; i < KW / 4; ++i) {
+                    const uint4 x = ((const uint4*)kp)[i];
+                    r.k[4 * i] = x.x; r.k[4 * i + 1] = x.y; r.k[4 * i + 2] = x.z; r.k[4 * i + 3] = x.w;
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < KW / 2; ++i) {
+                    const uint2 x = ((const uint2*)kp)[i];
+                    r.k[2 * i] = x.x; r.k[2 * i + 1] = x.y;
+                }
+            }
         }
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
@@ -278,7 +389,7 @@ __global__ __launch_bounds__(512, 1) void k_attn(AttnArgs a) {
     // come after its stores in program order.
     auto encode = [&]() {
         const float* kp = a.proj + (int64_t)tb0 * a.sproj + 2LL * a.nq * D + (int64_t)j * D;
-        encode_append<D>(kp, kp + (int64_t)a.nkv * D, a.signs, kc, ks, vc, vs, hbase + pos, vq, lane);
+        encode_append<D, FMT>(kp, kp + (int64_t)a.nkv * D, a.signs, kc, ks, vc, vs, hbase + pos, vq, lane);
     };
 
     const int ntiles = (t1 - t0 + kTile - 1) / kTile;
@@ -346,8 +457,7 @@ __global__ __launch_bounds__(512, 1) void k_attn(AttnArgs a) {
         float s[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
-            const uint4 kw = r.k[g >> 1];
-            const h8 kf = (g & 1) ? u8x8_to_h8(kw.z, kw.w) : u8x8_to_h8(kw.x, kw.y);
+            const h8 kf = F::KB == 4 ? nib8_to_h8(r.k[g]) : u8x8_to_h8(r.k[2 * g], r.k[2 * g + 1]);
             f4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qh[g], (f4{0.f, 0.f, 0.f, 0.f}), 0, 0, 0);
             d = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, ql[g], d, 0, 0, 0);
             const f4 ks = *(const f4*)&stile[w][0][g][4 * q];
@@ -381,25 +491,37 @@ __global__ __launch_bounds__(512, 1) void k_attn(AttnArgs a) {
         // the lo part carries the residual) so that the product keeps fp32
         // accuracy; the codes themselves are exact halves.  The lane's value slot
         // of position rr holds dims c + 16 b at bits 3 b.
-        uint32_t lo32[4], mid[4];
+        uint32_t lo32[4], mid[4], hi32[4];
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
             const uint64_t win = ((((uint64_t)r.vhi[rr]) << 32) | r.vlo[rr]) >> vsh;
             lo32[rr] = (uint32_t)win;
             mid[rr] = (uint32_t)(win >> 16);
+            hi32[rr] = (uint32_t)(win >> 32);
         }
-        // fields of positions (0, 1) and (2, 3) five at a time: the low 16 bits
-        // of each position's shifted slot side by side in one word
+        // 3-bit fields of positions (0, 1) and (2, 3) five at a time: the low
+        // 16 bits of each position's shifted slot side by side in one word;
+        // 4-bit fields four at a time, from each 16-bit quarter of the slot
         uint32_t zc[2][4];
 #pragma unroll
         for (int pr = 0; pr < 2; ++pr) {
             const int ra = 2 * pr, rb = 2 * pr + 1;
-            zc[pr][0] = __builtin_amdgcn_perm(lo32[rb], lo32[ra], 0x05040100u);               // fields 0..4
-            if (NB > 5) zc[pr][1] = __builtin_amdgcn_perm(lo32[rb] >> 15, lo32[ra] >> 15, 0x05040100u);  // 5..9
-            if (NB > 10) zc[pr][2] = __builtin_amdgcn_perm(mid[rb] >> 14, mid[ra] >> 14, 0x05040100u);  // 10..14
-            if (NB > 15) zc[pr][3] = __builtin_amdgcn_perm(mid[rb] >> 29, mid[ra] >> 29, 0x05040100u);  // 15
+            if (F::FB == 4) {
+                zc[pr][0] = __builtin_amdgcn_perm(lo32[rb], lo32[ra], 0x05040100u);                 // fields 0..3
+                if (NB > 4) zc[pr][1] = __builtin_amdgcn_perm(lo32[rb], lo32[ra], 0x07060302u);     // 4..7
+                if (NB > 8) zc[pr][2] = __builtin_amdgcn_perm(hi32[rb], hi32[ra], 0x05040100u);     // 8..11
+                if (NB > 12) zc[pr][3] = __builtin_amdgcn_perm(hi32[rb], hi32[ra], 0x07060302u);    // 12..15
+            } else {
+                zc[pr][0] = __builtin_amdgcn_perm(lo32[rb], lo32[ra], 0x05040100u);               // fields 0..4
+                if (NB > 5) zc[pr][1] = __builtin_amdgcn_perm(lo32[rb] >> 15, lo32[ra] >> 15, 0x05040100u);  // 5..9
+                if (NB > 10) zc[pr][2] = __builtin_amdgcn_perm(mid[rb] >> 14, mid[ra] >> 14, 0x05040100u);  // 10..14
+                if (NB > 15) zc[pr][3] = __builtin_amdgcn_perm(mid[rb] >> 29, mid[ra] >> 29, 0x05040100u);  // 15
+            }
         }
+        uint32_t lmt_lo = 0, lmt_hi = 0;
+        if (FMT == 2) lm_table(lmt_lo, lmt_hi);
         const h2 bias = {(_Float16)-1028.f, (_Float16)-1028.f};
+        const h2 bias4 = {(_Float16)-1032.f, (_Float16)-1032.f};
         // (x & mask) | 0x6400 halves in one v_and_or_b32: the mask in an SGPR and
         // the constant in a VGPR (a gfx9 VOP3 takes no literal operands)
         uint32_t m7, h64;
@@ -422,9 +544,20 @@ __global__ __launch_bounds__(512, 1) void k_attn(AttnArgs a) {
 #pragma unroll
             for (int bb = 0; bb < 2; ++bb) {
                 const int b = 2 * g + bb;
-                const int ch = b / 5, sh3 = 3 * (b % 5);
-                const h2 v01 = __builtin_bit_cast(h2, ((zc[0][ch] >> sh3) & m7) | h64) + bias;
-                const h2 v23 = __builtin_bit_cast(h2, ((zc[1][ch] >> sh3) & m7) | h64) + bias;
+                h2 v01, v23;
+                if (F::FB == 4) {
+                    const int ch = b / 4, sh4 = 4 * (b % 4);
+                    v01 = __builtin_bit_cast(h2, ((zc[0][ch] >> sh4) & 0x000F000Fu) | 0x64006400u) + bias4;
+                    v23 = __builtin_bit_cast(h2, ((zc[1][ch] >> sh4) & 0x000F000Fu) | 0x64006400u) + bias4;
+                } else if (FMT == 2) {
+                    const int ch = b / 5, sh3 = 3 * (b % 5);
+                    v01 = lm_pair(zc[0][ch] >> sh3, lmt_lo, lmt_hi);
+                    v23 = lm_pair(zc[1][ch] >> sh3, lmt_lo, lmt_hi);
+                } else {
+                    const int ch = b / 5, sh3 = 3 * (b % 5);
+                    v01 = __builtin_bit_cast(h2, ((zc[0][ch] >> sh3) & m7) | h64) + bias;
+                    v23 = __builtin_bit_cast(h2, ((zc[1][ch] >> sh3) & m7) | h64) + bias;
+                }
                 const h4 va = {v01[0], v01[1], v23[0], v23[1]};
                 o[b] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, phi, o[b], 0, 0, 0);
                 o[b] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, plo, o[b], 0, 0, 0);
@@ -533,8 +666,9 @@ __global__ __launch_bounds__(512, 1) void k_attn(AttnArgs a) {
     }
 }
 
-// KMAX: split rows per thread, enough for the launch's split count
-template <int D, int KMAX>
+// KMAX: split rows per thread, enough for the launch's split count; ROT: the
+// values were cached in the rotated domain, so the merged row is rotated back
+template <int D, int KMAX, bool ROT = true>
 __global__ __launch_bounds__(1024) void k_combine(CombineArgs a) {
     constexpr int LR = D / 4;            // lanes per split row, a float4 each
     constexpr int ROWS = 1024 / LR;      // split rows in flight
@@ -630,7 +764,14 @@ __global__ __launch_bounds__(1024) void k_combine(CombineArgs a) {
         v[tid] = t / L;
     }
     __syncthreads();
-    if (tid < 64) {
+    if (!ROT && tid < 64) {
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+            const int d = P * tid + j;
+            a.out[(int64_t)i * D + d] = (_Float16)(v[d] * sigmoidf_(gate[j]));
+        }
+    }
+    if (ROT && tid < 64) {
         // undo the rotation in one wave: Sylvester transform stage by stage in
         // the order of the index bits, lane holds d = P lane + j
         const int lane = tid;
@@ -838,7 +979,7 @@ int attn_tokens_per_sweep(int d, int nq, int nkv) {
 }
 
 hipError_t launch_append(const AttnArgs& a, hipStream_t s) {
-    if (a.nt < 1) return hipErrorInvalidValue;
+    if (a.nt < 1 || a.fmt != 0) return hipErrorInvalidValue;
     const dim3 grid(a.nkv, a.nt), block(64);
     if (a.d == 256) hipLaunchKernelGGL(k_append<256>, grid, block, 0, s, a);
     else if (a.d == 64) hipLaunchKernelGGL(k_append<64>, grid, block, 0, s, a);
@@ -853,6 +994,22 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
         return hipErrorInvalidValue;
     const int nn = a.nt == 1 || a.batch ? 1 : attn_tokens_per_sweep(a.d, a.nq, a.nkv);
     const dim3 grid(a.nsplit, a.nkv, (a.nt + nn - 1) / nn), block(64 * kWaves);
+    if (a.fmt != 0) {
+        // the 4-bit and codebook caches: single-token sweeps of one sequence
+        if (a.nt != 1 || a.batch || a.win > 0) return hipErrorInvalidValue;
+#define AW4_ATTN_FMT(DD, GG)                                                                  \
+        if (a.d == DD && G == GG) {                                                           \
+            if (a.fmt == 1) hipLaunchKernelGGL((k_attn<DD, GG, 1, 1>), grid, block, 0, s, a); \
+            else if (a.fmt == 2) hipLaunchKernelGGL((k_attn<DD, GG, 1, 2>), grid, block, 0, s, a); \
+            else return hipErrorInvalidValue;                                                 \
+            return hipGetLastError();                                                         \
+        }
+        AW4_ATTN_FMT(256, 6)
+        AW4_ATTN_FMT(64, 4)
+        AW4_ATTN_FMT(64, 2)
+#undef AW4_ATTN_FMT
+        return hipErrorInvalidValue;
+    }
 #define AW4_ATTN_CASE(DD, GG, NN)                                               \
     if (a.d == DD && G == GG && nn == NN) {                                     \
         hipLaunchKernelGGL((k_attn<DD, GG, NN>), grid, block, 0, s, a);         \
@@ -877,7 +1034,7 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
 
 hipError_t launch_attn_win(const AttnArgs& a, hipStream_t s) {
     const int G = a.nq / a.nkv;
-    if (a.win < 1 || a.nsplit_w < 1 || a.nt != 1 || a.batch || a.nq > a.prow || !a.kw || !a.vw)
+    if (a.win < 1 || a.nsplit_w < 1 || a.nt != 1 || a.batch || a.nq > a.prow || !a.kw || !a.vw || a.fmt != 0)
         return hipErrorInvalidValue;
     const dim3 grid(a.nsplit_w, a.nkv), block(64 * kWinWaves);
 #define AW4_WIN_CASE(DD, GG)                                            \
@@ -902,13 +1059,21 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
     if (a.nsplit < 1 || a.nsplit + a.nsplit_w > 256) return hipErrorInvalidValue;
     if (a.nt < 1 || a.nq * a.nt > a.prow) return hipErrorInvalidValue;
     // split rows per thread: 16 (D = 256) or 64 (D = 64) rows are in flight
-    if (a.d == 256) {
-        const int ns = a.nsplit + a.nsplit_w;
-        if (ns <= 64) hipLaunchKernelGGL((k_combine<256, 4>), dim3(a.nq * a.nt), dim3(1024), 0, s, a);
-        else if (ns <= 128) hipLaunchKernelGGL((k_combine<256, 8>), dim3(a.nq * a.nt), dim3(1024), 0, s, a);
-        else hipLaunchKernelGGL((k_combine<256, 16>), dim3(a.nq * a.nt), dim3(1024), 0, s, a);
+    const int ns = a.nsplit + a.nsplit_w;
+    const dim3 grid(a.nq * a.nt), block(1024);
+    if (a.d == 256 && a.fmt == 1) {
+        // values cached unrotated
+        if (ns <= 64) hipLaunchKernelGGL((k_combine<256, 4, false>), grid, block, 0, s, a);
+        else if (ns <= 128) hipLaunchKernelGGL((k_combine<256, 8, false>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((k_combine<256, 16, false>), grid, block, 0, s, a);
+    } else if (a.d == 256) {
+        if (ns <= 64) hipLaunchKernelGGL((k_combine<256, 4>), grid, block, 0, s, a);
+        else if (ns <= 128) hipLaunchKernelGGL((k_combine<256, 8>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((k_combine<256, 16>), grid, block, 0, s, a);
+    } else if (a.d == 64 && a.fmt == 1) {
+        hipLaunchKernelGGL((k_combine<64, 4, false>), grid, block, 0, s, a);
     } else if (a.d == 64) {
-        hipLaunchKernelGGL((k_combine<64, 4>), dim3(a.nq * a.nt), dim3(1024), 0, s, a);
+        hipLaunchKernelGGL((k_combine<64, 4>), grid, block, 0, s, a);
     } else {
         return hipErrorInvalidValue;
     }

@@ -7,6 +7,7 @@
 // in fp32 and round-to-nearest-even, codes clamp(rint(w / s), -qmax, qmax),
 // all codes 0 when s rounds to 0.
 #include "aw4_internal.h"
+#include "../../include/aw4.h"
 
 namespace aw4 {
 namespace {
@@ -84,6 +85,30 @@ __global__ void k_fill_zero(uint32_t* p, uint64_t n) {
 __global__ void k_copy_f32(float* dst, const float* src, int64_t n) {
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
         dst[i] = src[i];
+}
+
+// Plain streaming read for bandwidth reports: each thread reads 16-byte words
+// with a grid-wide stride (every wave load covers 1 KB of contiguous memory)
+// and folds them into one word, written per workgroup so nothing is dropped.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(256) void k_stream_read(const u32x4_t* __restrict__ src, uint64_t n16, uint32_t* sink) {
+    uint32_t acc = 0;
+    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+    uint64_t i = blockIdx.x * (uint64_t)blockDim.x + threadIdx.x;
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+        const u32x4_t a = __builtin_nontemporal_load(src + i);
+        const u32x4_t b = __builtin_nontemporal_load(src + i + stride);
+        const u32x4_t c = __builtin_nontemporal_load(src + i + 2 * stride);
+        const u32x4_t d = __builtin_nontemporal_load(src + i + 3 * stride);
+        const u32x4_t e = a ^ b ^ c ^ d;
+        acc ^= e[0] ^ e[1] ^ e[2] ^ e[3];
+    }
+    for (; i < n16; i += stride) {
+        const u32x4_t a = __builtin_nontemporal_load(src + i);
+        acc ^= a[0] ^ a[1] ^ a[2] ^ a[3];
+    }
+    for (int o = 32; o >= 1; o >>= 1) acc ^= __shfl_xor(acc, o, 64);
+    if ((threadIdx.x & 63) == 0) atomicXor(&sink[blockIdx.x], acc);
 }
 
 __device__ __forceinline__ void quant_group32(const float* w, int qmax, int* c, uint16_t* sbits) {
@@ -203,6 +228,12 @@ hipError_t launch_fill_zero(void* p, uint64_t bytes, hipStream_t s) {
     return hipGetLastError();
 }
 
+hipError_t launch_stream_read(const void* src, uint64_t bytes, uint32_t* sink, int nblocks, hipStream_t s) {
+    if (bytes % 16 || nblocks < 1) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_stream_read, dim3(nblocks), dim3(256), 0, s, (const u32x4_t*)src, bytes / 16, sink);
+    return hipGetLastError();
+}
+
 hipError_t launch_copy_f32(float* dst, const float* src, int64_t n, hipStream_t s) {
     hipLaunchKernelGGL(k_copy_f32, dim3(grid_for(n)), dim3(256), 0, s, dst, src, n);
     return hipGetLastError();
@@ -223,3 +254,32 @@ hipError_t launch_quant_i8(const float* src, int64_t nrows, int64_t cols, int8_t
 }
 
 }  // namespace aw4
+
+// Streaming-read bandwidth of the device (the reference point beside the 8 TB/s
+// peak in bandwidth reports): reps launches of k_stream_read over bytes at
+// dev_src between two events on hip_stream, after one untimed launch; the
+// average launch duration in microseconds.  dev_sink: at least 8 KB of device
+// memory (one word per workgroup, 2048 workgroups: 8 per compute unit).
+extern "C" int aw4_time_stream_read(const void* dev_src, uint64_t bytes, void* dev_sink, void* hip_stream, int32_t reps,
+                                    float* avg_us) {
+    if (!dev_src || !dev_sink || !avg_us || reps < 1 || bytes < 16 || bytes % 16) return AW4_E_INVAL;
+    hipStream_t s = (hipStream_t)hip_stream;
+    constexpr int kBlocks = 2048;
+    hipEvent_t e0, e1;
+    if (hipEventCreate(&e0) != hipSuccess) return AW4_E_HIP;
+    if (hipEventCreate(&e1) != hipSuccess) {
+        (void)hipEventDestroy(e0);
+        return AW4_E_HIP;
+    }
+    bool ok = aw4::launch_stream_read(dev_src, bytes, (uint32_t*)dev_sink, kBlocks, s) == hipSuccess;
+    ok = ok && hipEventRecord(e0, s) == hipSuccess;
+    for (int i = 0; ok && i < reps; ++i) ok = aw4::launch_stream_read(dev_src, bytes, (uint32_t*)dev_sink, kBlocks, s) == hipSuccess;
+    ok = ok && hipEventRecord(e1, s) == hipSuccess && hipEventSynchronize(e1) == hipSuccess;
+    float ms = 0.f;
+    ok = ok && hipEventElapsedTime(&ms, e0, e1) == hipSuccess;
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    if (!ok) return AW4_E_HIP;
+    *avg_us = ms * 1000.f / (float)reps;
+    return AW4_OK;
+}

@@ -60,10 +60,17 @@ def step_bytes(shape, pos):
     ng = shape.pattern.count("G")
     na = shape.pattern.count("A")
     b += ng * shape.gdn_v_heads * shape.gdn_head_dim ** 2 * 4 * 2   # state read + write
-    d = shape.attn_head_dim
-    kv_pos = shape.attn_kv_heads * (d + d * 3 // 8 + 2 * (d // 32) * 2)
-    b += na * kv_pos * (pos + 1)                                # cache read incl. the new entry
+    b += na * kv_bytes_per_pos(shape) * (pos + 1)               # cache read incl. the new entry
     return b
+
+
+def kv_bytes_per_pos(shape):
+    """cache bytes of one position of one attention layer, all kv heads: key
+    codes, value codes and the two fp16 scales per 32 dims (format 1 stores 4-bit
+    keys and values, formats 0 and 2 int8 keys and 3-bit values)"""
+    d = shape.attn_head_dim
+    codes = d // 2 + d // 2 if getattr(shape, "kv_format", 0) == 1 else d + d * 3 // 8
+    return shape.attn_kv_heads * (codes + 2 * (d // 32) * 2)
 
 
 def cpu_baseline(ctx, seed):
@@ -110,6 +117,23 @@ def cpu_baseline(ctx, seed):
             "sample": (f"fp64 C oracle: 1 GDN layer step ({tg:.3f} s) and 1 attention layer step ({ta:.3f} s) at "
                        f"{ctx} cached positions, int8 head over vocab/8 ({th / 8:.3f} s); median of 3; "
                        f"scaled to 48 + 16 layers + full head = {per_token:.2f} s/token")}
+
+
+def stream_probe(torch, A, sizes=((1 << 30, 20), (100_000_000 // 16 * 16, 100))):
+    """Measured streaming-read bandwidth of the box: a plain device read
+    (aw4_time_stream_read: 16-byte non-temporal loads, every wave load 1 KB
+    contiguous) of 1 GiB and of 100 MB, average over reps launches."""
+    out = {}
+    sink = torch.zeros(2048, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    for nbytes, reps in sizes:
+        buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        us = A.time_stream_read(buf, sink, stream, reps)
+        out["read_1GiB" if nbytes == 1 << 30 else f"read_{nbytes // 1_000_000}MB"] = {
+            "bytes": nbytes, "avg_us": round(us, 2), "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1)}
+        del buf
+    torch.cuda.empty_cache()
+    return out
 
 
 def long_leg(args, torch, A, W, SS, synth):
@@ -285,6 +309,53 @@ def window_leg(args, torch, A, W, SS, synth):
     return out
 
 
+def kvformat_leg(args, torch, A, W, SS, synth):
+    """Greedy decode at a long context with the other cache codecs: format 1
+    (q4_0, keys and values 4-bit, values not rotated) and format 2 (int8 keys,
+    values rotated then coded with the Lloyd-Max codebook), each from a seeded
+    synthetic state in its format.  Algorithmic bytes count the format's cache
+    bytes per position."""
+    from concurrent.futures import ThreadPoolExecutor
+    from synth.gpu_load import load_recipe
+    out = {}
+    ctx = args.kvformat_ctx
+    for fmt in (1, 2):
+        shape = W.with_(W.FULL_27B, max_ctx=ctx + args.kvformat_steps + 32, draft_vocab=0, kv_format=fmt)
+        m = A.Model(shape)
+        load_recipe(m, shape, args.seed)
+        t0 = time.time()
+        SS.fill(m, shape, ctx - 1, args.seed, kv=False)
+        alayers = [l for l, t in enumerate(shape.pattern) if t == "A"]
+        with ThreadPoolExecutor(4) as ex:
+            for l, kv in zip(alayers, ex.map(lambda l: SS.kv_state(shape, l, ctx - 1, args.seed), alayers)):
+                m.import_kv(l, *kv)
+        m.set_pos(ctx - 1)
+        m.sync()
+        t_fill = time.time() - t0
+        tok = int(m.decode_greedy(int(synth.tokens(1, shape.vocab, args.seed + 3)[0]), 8)[-1])
+        pos0 = m.pos
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        m.decode_greedy(tok, args.kvformat_steps)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        nbytes = sum(step_bytes(shape, p) for p in range(pos0, pos0 + args.kvformat_steps))
+        out[f"format_{fmt}"] = {"codec": "q4_0: K and V 4-bit, V not rotated" if fmt == 1 else
+                                "K int8, V rotated + 3-bit Lloyd-Max codebook",
+                                "tok/s": round(args.kvformat_steps / wall, 2),
+                                "ms_per_step": round(wall * 1e3 / args.kvformat_steps, 4),
+                                "steps": args.kvformat_steps, "ctx_start": int(pos0),
+                                "cache_bytes_per_position": kv_bytes_per_pos(shape) * len(alayers),
+                                "algorithmic_GB_per_step": round(nbytes / args.kvformat_steps / 1e9, 4),
+                                "frac_of_8TB/s": round(nbytes / wall / 1e9 / HBM_PEAK_GBS, 4),
+                                "setup_fill_s": round(t_fill, 1)}
+        m.close()
+        del m
+        torch.cuda.empty_cache()
+    out["state"] = "seeded synthetic cache and recurrent states in each format"
+    return out
+
+
 def batch_leg(args, torch, m, shape, SS, synth):
     """Batch decode: B sequences (B = 1..4), each from its own seeded synthetic
     state of ctx positions, one greedy step each per aw4_decode_batch call;
@@ -306,8 +377,8 @@ def batch_leg(args, torch, m, shape, SS, synth):
         wall = time.perf_counter() - t0
         pos = args.ctx
         state = shape.pattern.count("G") * shape.gdn_v_heads * shape.gdn_head_dim ** 2 * 8
-        kv = shape.pattern.count("A") * shape.attn_kv_heads * (shape.attn_head_dim * 11 // 8 + 16) * (pos + 1)
-        weights = step_bytes(shape, 0) - state - shape.pattern.count("A") * shape.attn_kv_heads * (shape.attn_head_dim * 11 // 8 + 16)
+        kv = shape.pattern.count("A") * kv_bytes_per_pos(shape) * (pos + 1)
+        weights = step_bytes(shape, 0) - state - shape.pattern.count("A") * kv_bytes_per_pos(shape)
         nbytes = weights + B * (state + kv)
         res[f"B{B}"] = {"tok/s": round(B * args.batch_steps / wall, 1),
                         "ms_per_step": round(wall * 1e3 / args.batch_steps, 3),
@@ -341,6 +412,9 @@ def main():
                     help="recent-window leg: positions kept at fp16 per attention layer (0: skip)")
     ap.add_argument("--window-ctx", default="8192,131072", help="contexts of the recent-window leg")
     ap.add_argument("--window-steps", type=int, default=128, help="timed greedy steps per window context")
+    ap.add_argument("--kvformat-ctx", type=int, default=262144,
+                    help="cached positions of the q4_0 and codebook cache legs (0: skip)")
+    ap.add_argument("--kvformat-steps", type=int, default=128, help="timed greedy steps per cache format")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run one plain device copy of this many MiB first (a known-size kernel for counter runs)")
     args = ap.parse_args()
@@ -407,6 +481,8 @@ def main():
     # weight bytes are FFN, gate/up alone 46% of the step)
     us, nbytes = m.time_phase(A.PHASE_FFN_GATE_UP, args.phase_reps)
     ach = nbytes / (us * 1e-6) / 1e9
+    probe = stream_probe(torch, A)
+    probe_gbs = probe["read_1GiB"]["GB/s"]
     others = {}
     for name, ph in (("ffn_down", A.PHASE_FFN_DOWN), ("mixer_in", A.PHASE_MIX_IN)):
         u, b = m.time_phase(ph, args.phase_reps)
@@ -442,10 +518,12 @@ def main():
                    "ctx_start": int(pos0), "prompt": args.prompt, "global_batch": 1},
         "hbm": {"algorithmic_GB_per_step": round(total_bytes / args.steps / 1e9, 4),
                 "achieved_GB/s": round(gbs, 1), "frac_of_8TB/s": round(gbs / HBM_PEAK_GBS, 4),
-                "gpu_event_ms": round(gpu_ms, 3)},
+                "frac_of_measured_read": round(gbs / probe_gbs, 4), "gpu_event_ms": round(gpu_ms, 3),
+                "measured_read_probe": probe},
         "roofline": {"kernel": "k_gemv_stream (RMSNorm + FFN gate/up W4 GEMV + SwiGLU), K=5120, 34816 rows",
                      "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": gateup_traffic(),
+                     "frac": round(ach / HBM_PEAK_GBS, 4), "frac_of_measured_read": round(ach / probe_gbs, 4),
+                     "traffic": gateup_traffic(),
                      "avg_launch_us": round(us, 3), "bytes_per_launch": nbytes, "other_kernels": others},
         "prefill": prefill,
         "setup_s": {"load": round(t_load, 1), "prompt": round(t_prompt, 1)},
@@ -460,6 +538,8 @@ def main():
     torch.cuda.empty_cache()
     if args.long_ctx:
         out["ctx_262k" if args.long_ctx == 262144 else f"ctx_{args.long_ctx}"] = long_leg(args, torch, A, W, SS, synth)
+    if args.kvformat_ctx:
+        out["kv_formats"] = kvformat_leg(args, torch, A, W, SS, synth)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.ctx, args.seed)
     print(json.dumps(out), flush=True)

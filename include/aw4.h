@@ -74,7 +74,22 @@ extern "C" {
  * t % W).  A decode step at position p reads positions p - W + 1 .. p from the
  * ring and the older ones from their codes.  Only the single-sequence decode
  * path reads the window: aw4_prefill runs token by token (no chunks),
- * aw4_verify_k and aw4_decode_batch return AW4_E_INVAL. */
+ * aw4_verify_k and aw4_decode_batch return AW4_E_INVAL.
+ *
+ * KV-cache codecs (kv_format).  0: keys int8 per 32 with an fp16 scale, values
+ * rotated by the random-sign Walsh-Hadamard transform then 3-bit codes -3..3 per
+ * 32 (page 5, bs178.com llamAmpere article, "为什么它真能这么快" point 三).
+ * 1, q4_0 (page 3, "Qwen3.8-27B 實測", section "RTX 5090 32GB：可以四人", runs
+ * 131K with both caches at q4_0; page 4, jdon.com, on fitting 262K into 24 GB):
+ * keys and values each 4-bit codes -7..7 per 32 with an fp16 scale (the W4
+ * weight codec), values not rotated.  2: keys int8; values rotated, then per 32
+ * the index 0..7 of the nearest level of the 8-level Lloyd-Max codebook of a
+ * unit Gaussian (J. Max 1960: +-0.2451, +-0.7560, +-1.3440, +-2.1520, as fp16),
+ * scaled by fp16 of the group's root mean square, ties to the lower level.
+ * Formats 1 and 2 serve the single-sequence decode step: they need kv_window 0,
+ * max_batch <= 1 and draft_vocab 0; aw4_prefill runs token by token and
+ * aw4_verify_k returns AW4_E_INVAL.  The state calls use the logical codes of
+ * the format (format 1: K and V -7..7; format 2: V indices 0..7). */
 typedef struct aw4_config {
     int32_t hidden;
     int32_t ffn;
@@ -95,6 +110,7 @@ typedef struct aw4_config {
     int32_t max_batch;          /* sequences with their own state (0 or 1: one; at most 4) */
     int32_t kv_window;          /* recent window: the last kv_window positions of every
                                    attention layer are read at fp16 (0: none); see below */
+    int32_t kv_format;          /* KV-cache codecs (0, 1 or 2); see below */
 } aw4_config;
 
 typedef struct aw4_model aw4_model;
@@ -361,6 +377,16 @@ enum {
     AW4_PHASE_PREFILL_GATE_UP = 5 /* gate/up W4 GEMM + SwiGLU over a full prefill chunk */
 };
 int aw4_time_phase(aw4_model* model, int32_t phase, int32_t reps, float* avg_us, uint64_t* bytes_per_launch);
+
+/* Streaming-read bandwidth of the device, the measured reference beside the
+ * 8 TB/s peak in bandwidth reports: reps launches of a plain read kernel
+ * (16-byte non-temporal loads, 2048 workgroups, every wave load 1 KB of
+ * contiguous memory) over bytes (a multiple of 16) at dev_src, timed between
+ * two HIP events on hip_stream after one untimed launch; *avg_us receives the
+ * average launch duration.  dev_sink: at least 8 KB of device memory the
+ * kernel writes.  Synchronous.  Errors: AW4_E_INVAL, AW4_E_HIP. */
+int aw4_time_stream_read(const void* dev_src, uint64_t bytes, void* dev_sink, void* hip_stream, int32_t reps,
+                         float* avg_us);
 
 /* ----------------------------------------------------------- state */
 

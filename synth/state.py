@@ -30,13 +30,33 @@ def gdn_state(shape, layer, seed):
         shape.gdn_v_heads, shape.gdn_head_dim, shape.gdn_head_dim)
 
 
+# the 4-bit cache (format 1): code std ~ 2.8 (keys and values of std 1.4 at scale 0.5)
+Q4_SPREAD256 = 720
+Q4_SCALE_BITS = 0x3800          # fp16 0.5
+
+
 def kv_state(shape, layer, npos, seed):
+    """Logical cache codes and scales of npos positions in the shape's cache
+    format: format 0 int8 keys and 3-bit values (-3..3); format 1 4-bit keys
+    and values (-7..7); format 2 int8 keys and codebook indices 0..7 (from
+    discretised normals folded onto the eight levels)."""
     d, nkv = shape.attn_head_dim, shape.attn_kv_heads
+    fmt = getattr(shape, "kv_format", 0)
     n = npos * nkv * d
-    kc = codes(n, K_SPREAD256, 127, seed, _stream(layer, 1)).reshape(npos, nkv, d)
-    vc = codes(n, V_SPREAD256, 3, seed, _stream(layer, 2)).reshape(npos, nkv, d)
-    ks = scale_bits(n // 32, K_SCALE_BITS, seed, _stream(layer, 3)).reshape(npos, nkv, d // 32)
-    vs = scale_bits(n // 32, V_SCALE_BITS, seed, _stream(layer, 4)).reshape(npos, nkv, d // 32)
+    if fmt == 1:
+        kc = codes(n, Q4_SPREAD256, 7, seed, _stream(layer, 1)).reshape(npos, nkv, d)
+        vc = codes(n, Q4_SPREAD256, 7, seed, _stream(layer, 2)).reshape(npos, nkv, d)
+        kb, vb = Q4_SCALE_BITS, Q4_SCALE_BITS
+    else:
+        kc = codes(n, K_SPREAD256, 127, seed, _stream(layer, 1)).reshape(npos, nkv, d)
+        kb, vb = K_SCALE_BITS, V_SCALE_BITS
+        if fmt == 2:
+            a = codes(n, V_SPREAD256, 7, seed, _stream(layer, 2))
+            vc = np.where(a >= 0, np.minimum(a, 3) + 4, np.maximum(a, -4) + 4).astype(np.int8).reshape(npos, nkv, d)
+        else:
+            vc = codes(n, V_SPREAD256, 3, seed, _stream(layer, 2)).reshape(npos, nkv, d)
+    ks = scale_bits(n // 32, kb, seed, _stream(layer, 3)).reshape(npos, nkv, d // 32)
+    vs = scale_bits(n // 32, vb, seed, _stream(layer, 4)).reshape(npos, nkv, d // 32)
     return kc, ks, vc, vs
 
 

@@ -37,7 +37,8 @@ def _cfg(shape, **kw):
 
 
 @pytest.mark.parametrize("shape", [W.TOY, W.FULL_27B, W.GDN_LAYER, W.ATTN_LAYER,
-                                   W.with_(W.TOY, kv_window=16), W.with_(W.FULL_27B, kv_window=2048, draft_vocab=0)])
+                                   W.with_(W.TOY, kv_window=16), W.with_(W.FULL_27B, kv_window=2048, draft_vocab=0),
+                                   W.with_(W.TOY, kv_format=1), W.with_(W.FULL_27B, kv_format=2, draft_vocab=0)])
 def test_valid_configs(shape):
     assert A.lib().aw4_validate_config(ctypes.byref(_cfg(shape))) == 0
 
@@ -58,12 +59,26 @@ def test_window_adds_its_ring_to_the_workspace():
     dict(vocab=-1), dict(max_ctx=0), dict(attn_q_heads=3, attn_kv_heads=1),
     dict(kv_window=-1), dict(kv_window=2000), dict(kv_window=16, max_batch=2),
     dict(kv_window=16, draft_vocab=64),
+    dict(kv_format=3), dict(kv_format=-1), dict(kv_format=1, kv_window=16), dict(kv_format=2, max_batch=2),
+    dict(kv_format=1, draft_vocab=64),
 ])
 def test_invalid_configs(kw):
     c = _cfg(W.TOY, **kw)
     assert A.lib().aw4_validate_config(ctypes.byref(c)) == -1
     out = ctypes.c_uint64()
     assert A.lib().aw4_workspace_bytes(ctypes.byref(c), ctypes.byref(out)) == -1
+
+
+def test_cache_formats_size_the_workspace():
+    """per attention layer, kv head and position: format 0 and 2 hold a key row
+    of d bytes and a value record of 3 d / 8 bytes, format 1 (q4_0) d / 2 bytes
+    each; the scales are the same"""
+    s = W.with_(W.ATTN_LAYER, draft_vocab=0)
+    n = s.attn_kv_heads * s.max_ctx
+    d = s.attn_head_dim
+    b0, b1, b2 = (A.workspace_bytes(W.with_(s, kv_format=f)) for f in (0, 1, 2))
+    assert b2 == b0
+    assert abs((b0 - b1) - n * (d + 3 * d // 8 - d // 2 - d // 2)) <= 4096
 
 
 def test_workspace_bytes_full_model():
