@@ -1255,6 +1255,150 @@ __global__ __launch_bounds__(256, 2) void k_gemv_mfma(GemvMultiArgs a) {
     }
 }
 
+// int8 head over M <= 4 vectors on the matrix cores (row length H, a compile-
+// time multiple of 256).  A wave takes blocks of 16 rows; per 64-byte span of
+// a row (64 codes), lane (c, q) loads bytes 16 q .. 16 q + 15 of row c, and a
+// 4 x 4 transpose across the lane rows (two 32-lane and two 16-lane swaps)
+// leaves word j of lane row q = codes 16 j + 4 q .. + 3, the A operand of
+// v_mfma_f32_16x16x16_f16 j (exact codes as fp16); the B operand is input c
+// at the same four positions, from LDS.  Two products make a 32-code group,
+// whose fp16 scale then multiplies each of the lane's four rows.  Stages of
+// two spans (four groups) run two ahead in a ring of three register sets,
+// unrolled by three so that no copy moves a set.
+// Results: logits [M][V] and per-workgroup best value and index per vector
+// (lowest index on ties), gridDim.x partials per vector as k_head_multi.
+template <int H>
+__global__ __launch_bounds__(256, 2) void k_head_mfma(HeadMultiArgs a) {
+    constexpr int MAXM = 4, GR = H / 32, NSP = H / 64, SPS = 2, NST = NSP / SPS;   // spans per stage, stages per row block
+    static_assert(NSP % SPS == 0, "row length");
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+    extern __shared__ __align__(16) unsigned char smem[];
+    float* red = (float*)smem;
+    _Float16* xs = (_Float16*)(smem + 64);   // [M][H + kMfmaPad]
+    __shared__ float bv_s[MAXM][4];
+    __shared__ int bi_s[MAXM][4];
+    {
+        GemvMultiArgs g{};
+        g.K = H;
+        g.M = a.M;
+        g.x = a.x;
+        g.sx = H;
+        g.nw = a.nw;
+        g.eps = a.eps;
+        mfma_prologue<H, PRO_NORM>(g, xs, red);
+    }
+    __syncthreads();
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int c = lane & 15, q = lane >> 4;
+    const int M = a.M, V = a.V;
+    const int nrb = (V + 15) / 16;
+    const _Float16* xrow = xs + min(c, M - 1) * (H + kMfmaPad) + 4 * q;
+    const h2 off = {(_Float16)1152.0f, (_Float16)1152.0f};
+    float best = -INFINITY;
+    int besti = 0x7fffffff;
+    struct Stage {
+        u32x4 w[SPS];       // row c: span bytes 16 q .. 16 q + 15 of each span
+        uint2 s[4];         // rows 4 q + rr: fp16 scales of the stage's 4 groups
+    };
+    for (int rb = blockIdx.x * 4 + wave; rb < nrb; rb += gridDim.x * 4) {
+        const int r0 = rb * 16;
+        const u32x4* arow = (const u32x4*)(a.codes + (int64_t)min(r0 + c, V - 1) * H) + q;
+        const uint16_t* srow[4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) srow[rr] = a.scales + (int64_t)min(r0 + 4 * q + rr, V - 1) * GR;
+        auto load = [&](Stage& st, int sidx) {
+#pragma unroll
+            for (int h = 0; h < SPS; ++h) st.w[h] = __builtin_nontemporal_load(arow + 4 * (sidx * SPS + h));
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) st.s[rr] = *(const uint2*)(srow[rr] + 4 * sidx);
+        };
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        const f4 zero = {0.f, 0.f, 0.f, 0.f};
+        auto compute = [&](const Stage& st, int sidx) {
+#pragma unroll
+            for (int h = 0; h < SPS; ++h) {
+                const int k0 = 64 * (sidx * SPS + h);
+                uint2 xb[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) xb[j] = *(const uint2*)(xrow + k0 + 16 * j);
+                const auto ab = __builtin_amdgcn_permlane32_swap(st.w[h][0], st.w[h][2], false, false);
+                const auto cd = __builtin_amdgcn_permlane32_swap(st.w[h][1], st.w[h][3], false, false);
+                const auto t01 = __builtin_amdgcn_permlane16_swap(ab[0], cd[0], false, false);
+                const auto t23 = __builtin_amdgcn_permlane16_swap(ab[1], cd[1], false, false);
+                const uint32_t wd[4] = {t01[0], t01[1], t23[0], t23[1]};
+                f4 d[2];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t b = wd[j] ^ 0x80808080u;
+                    const h2 p01 = as_h2(__builtin_amdgcn_perm(0x64646464u, b, 0x04010400u)) - off;
+                    const h2 p23 = as_h2(__builtin_amdgcn_perm(0x64646464u, b, 0x04030402u)) - off;
+                    const h4 av = {p01[0], p01[1], p23[0], p23[1]};
+                    d[j >> 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, __builtin_bit_cast(h4, xb[j]),
+                                                                     (j & 1) ? d[j >> 1] : zero, 0, 0, 0);
+                }
+                // groups 2 h and 2 h + 1 of the stage: scale halves of words h
+#pragma unroll
+                for (int gg = 0; gg < 2; ++gg)
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) {
+                        const uint32_t sw = h == 0 ? st.s[rr].x : st.s[rr].y;
+                        acc[rr] += (float)as_h2(sw)[gg] * d[gg][rr];
+                    }
+            }
+        };
+        // loads past the last stage re-read it, so every step issues the same ones
+        Stage ring[3];
+        load(ring[0], 0);
+        load(ring[1], min(1, NST - 1));
+        for (int sidx = 0;; sidx += 3) {
+            load(ring[2], min(sidx + 2, NST - 1));
+            asm volatile("" ::: "memory");
+            compute(ring[0], sidx);
+            if (sidx + 1 >= NST) break;
+            load(ring[0], min(sidx + 3, NST - 1));
+            asm volatile("" ::: "memory");
+            compute(ring[1], sidx + 1);
+            if (sidx + 2 >= NST) break;
+            load(ring[1], min(sidx + 4, NST - 1));
+            asm volatile("" ::: "memory");
+            compute(ring[2], sidx + 2);
+            if (sidx + 3 >= NST) break;
+        }
+        if (c < M) {
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int row = r0 + 4 * q + rr;
+                if (row < V) {
+                    if (a.logits) a.logits[(int64_t)c * V + row] = acc[rr];
+                    if (better(acc[rr], row, best, besti)) { best = acc[rr]; besti = row; }
+                }
+            }
+        }
+    }
+    // per vector (lane column c): best over the four lane rows, then the waves
+#pragma unroll
+    for (int o = 16; o <= 32; o <<= 1) {
+        const float ov = __shfl_xor(best, o, 64);
+        const int oi = __shfl_xor(besti, o, 64);
+        if (better(ov, oi, best, besti)) { best = ov; besti = oi; }
+    }
+    if (q == 0 && c < M) {
+        bv_s[c][wave] = best;
+        bi_s[c][wave] = besti;
+    }
+    __syncthreads();
+    if (threadIdx.x < M) {
+        const int m = threadIdx.x;
+        float b = bv_s[m][0];
+        int bi = bi_s[m][0];
+        for (int w = 1; w < 4; ++w)
+            if (better(bv_s[m][w], bi_s[m][w], b, bi)) { b = bv_s[m][w]; bi = bi_s[m][w]; }
+        a.part_val[m * gridDim.x + blockIdx.x] = b;
+        a.part_idx[m * gridDim.x + blockIdx.x] = bi;
+    }
+}
+
 // int8 head over M vectors (per-vector logits and per-block argmax partials)
 __global__ __launch_bounds__(256) void k_head_multi(HeadMultiArgs a) {
     constexpr int MAXM = 4;
@@ -1583,6 +1727,19 @@ hipError_t launch_gemv_multi(int pro, int epi, const GemvMultiArgs& a, hipStream
 
 hipError_t launch_head_multi(const HeadMultiArgs& a, hipStream_t s) {
     if (a.M < 1 || a.M > 4) return hipErrorInvalidValue;
+    if (a.H == 5120 || a.H == 512) {
+        // the matrix-core form (27B and toy widths); one partial per workgroup
+        // and vector as below, head_blocks(V) workgroups
+        const size_t shm = 64 + (size_t)2 * a.M * (a.H + kMfmaPad);
+        const void* fn = a.H == 5120 ? (const void*)k_head_mfma<5120> : (const void*)k_head_mfma<512>;
+        if (shm > 65536) {
+            hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+            if (e != hipSuccess) return e;
+        }
+        if (a.H == 5120) hipLaunchKernelGGL(k_head_mfma<5120>, dim3(head_blocks(a.V)), dim3(256), shm, s, a);
+        else hipLaunchKernelGGL(k_head_mfma<512>, dim3(head_blocks(a.V)), dim3(256), shm, s, a);
+        return hipGetLastError();
+    }
     const size_t shm = 64 + (size_t)a.H * 2 * (size_t)a.M;
     if (shm > 65536) {
         hipError_t e = hipFuncSetAttribute((const void*)k_head_multi, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);

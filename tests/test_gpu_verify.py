@@ -187,3 +187,62 @@ def test_verify_acceptance_distribution_chi2(aw4):
     _say(f"chi2 p-value {stat.pvalue:.3f}")
     assert stat.pvalue > 1e-3
     gm.close()
+
+
+@pytest.mark.parametrize("temperature", [0.0, 1.0])
+def test_verify_at_262k_positions(aw4, temperature):
+    """One full-size gated-attention layer with a 4096-id head on a seeded
+    262,143-position synthetic cache: a verify pass of three drafts (the
+    two-token sweeps over the whole cache) against the oracle's, from the same
+    state: emitted tokens (at temperature 1: except at a decision boundary),
+    committed position and the appended cache entries."""
+    import torch
+    from synth import state as SS
+    from synth.gpu_load import load_recipe
+    npos = 262143
+    shape = W.with_(W.ATTN_LAYER, vocab=4096, max_ctx=npos + 16)
+    _say("case: verify at 262,143 cached positions, one attention layer, T =", temperature)
+    gm = aw4.Model(shape)
+    load_recipe(gm, shape, 21)
+    om = oracle.from_recipe(shape, 21)
+    SS.fill(om, shape, npos, 21)
+    SS.fill(gm, shape, npos, 21)
+    t0 = int(synth.tokens(1, shape.vocab, 21, i0=npos)[0])
+    k = 3
+    if temperature == 0.0:
+        snap = om.snapshot()
+        drafts, t = [], t0
+        for _ in range(k):
+            _, _, t = om.decode_token(t)
+            drafts.append(t)
+        om.restore(snap)
+        drafts[2] = (drafts[2] + 1) % shape.vocab      # the third draft is wrong
+        q = u = None
+        qd = None
+    else:
+        q, drafts = _synthetic_q(shape.vocab, k, 21, 0)
+        u = synth.uniform(k + 1, 21, W.STREAM_UNIFORM, i0=77)
+        qd = torch.from_numpy(q).cuda()
+    tokens = [t0] + drafts
+    got = gm.verify_k(tokens, qd, u, temperature)
+    ref, a, L = oracle_verify(om, tokens, None if q is None else q.astype(np.float64), u, temperature)
+    _say(f"gpu {got} oracle {ref} (drafts {drafts})")
+    if temperature == 0.0:
+        assert got == ref and len(ref) == 3
+    elif got != ref:
+        # differing only where the oracle's own decision sits at its boundary
+        j = next(i for i in range(min(len(got), len(ref))) if got[i] != ref[i])
+        p = softmax_t(L[j], 1.0)
+        if j < k and abs(u[j] - min(1.0, p[drafts[j]] / q[j][drafts[j]])) < 1e-4:
+            pass
+        else:
+            w = np.maximum(p - q[j], 0.0) if j < k else p
+            c = np.cumsum(w) / w.sum()
+            assert abs(c[min(got[j], ref[j])] - u[k]) < 1e-4, (got, ref)
+    if got == ref:
+        assert gm.pos == om.pos
+        gk, ok = gm.export_kv(0, om.pos), om.get_kv(0, om.pos)
+        for x, y in ((gk[0], ok[0]), (gk[2], ok[2])):
+            d = x[npos:].astype(int) - y[npos:].astype(int)
+            assert np.abs(d).max() <= 1 and (d != 0).mean() < 6e-2
+    gm.close()
