@@ -87,23 +87,29 @@ __global__ void k_copy_f32(float* dst, const float* src, int64_t n) {
         dst[i] = src[i];
 }
 
-// Plain streaming read for bandwidth reports: each thread reads 16-byte words
-// with a grid-wide stride (every wave load covers 1 KB of contiguous memory)
-// and folds them into one word, written per workgroup so nothing is dropped.
+// Plain streaming read for bandwidth reports: workgroup b reads the b-th
+// contiguous chunk of per 16-byte words, eight 4 KB workgroup loads in flight
+// (16-byte non-temporal loads, every wave load 1 KB contiguous), folds them
+// into one word and writes it per workgroup so nothing is dropped.  Of the
+// forms measured on the device (grid-wide stride with 2048 workgroups; chunks
+// with 512 to 4096 workgroups; plain or non-temporal loads) this one, at 512
+// workgroups, reads fastest.
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-__global__ __launch_bounds__(256) void k_stream_read(const u32x4_t* __restrict__ src, uint64_t n16, uint32_t* sink) {
+__global__ __launch_bounds__(256) void k_stream_read(const u32x4_t* __restrict__ src, uint64_t n16, uint64_t per,
+                                                     uint32_t* sink) {
+    constexpr int U = 8;
     uint32_t acc = 0;
-    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
-    uint64_t i = blockIdx.x * (uint64_t)blockDim.x + threadIdx.x;
-    for (; i + 3 * stride < n16; i += 4 * stride) {
-        const u32x4_t a = __builtin_nontemporal_load(src + i);
-        const u32x4_t b = __builtin_nontemporal_load(src + i + stride);
-        const u32x4_t c = __builtin_nontemporal_load(src + i + 2 * stride);
-        const u32x4_t d = __builtin_nontemporal_load(src + i + 3 * stride);
-        const u32x4_t e = a ^ b ^ c ^ d;
-        acc ^= e[0] ^ e[1] ^ e[2] ^ e[3];
+    const uint64_t beg = blockIdx.x * per;
+    const uint64_t end = beg + per < n16 ? beg + per : n16;
+    uint64_t i = beg + threadIdx.x;
+    for (; i + (U - 1) * 256 < end; i += U * 256) {
+        u32x4_t v[U];
+#pragma unroll
+        for (int j = 0; j < U; ++j) v[j] = __builtin_nontemporal_load(src + i + j * 256);
+#pragma unroll
+        for (int j = 0; j < U; ++j) acc ^= v[j][0] ^ v[j][1] ^ v[j][2] ^ v[j][3];
     }
-    for (; i < n16; i += stride) {
+    for (; i < end; i += 256) {
         const u32x4_t a = __builtin_nontemporal_load(src + i);
         acc ^= a[0] ^ a[1] ^ a[2] ^ a[3];
     }
@@ -230,7 +236,10 @@ hipError_t launch_fill_zero(void* p, uint64_t bytes, hipStream_t s) {
 
 hipError_t launch_stream_read(const void* src, uint64_t bytes, uint32_t* sink, int nblocks, hipStream_t s) {
     if (bytes % 16 || nblocks < 1) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_stream_read, dim3(nblocks), dim3(256), 0, s, (const u32x4_t*)src, bytes / 16, sink);
+    const uint64_t n16 = bytes / 16;
+    // chunks of whole 256-word workgroup loads that cover the range
+    const uint64_t per = ((n16 + nblocks - 1) / nblocks + 255) / 256 * 256;
+    hipLaunchKernelGGL(k_stream_read, dim3(nblocks), dim3(256), 0, s, (const u32x4_t*)src, n16, per, sink);
     return hipGetLastError();
 }
 
@@ -259,12 +268,12 @@ hipError_t launch_quant_i8(const float* src, int64_t nrows, int64_t cols, int8_t
 // peak in bandwidth reports): reps launches of k_stream_read over bytes at
 // dev_src between two events on hip_stream, after one untimed launch; the
 // average launch duration in microseconds.  dev_sink: at least 8 KB of device
-// memory (one word per workgroup, 2048 workgroups: 8 per compute unit).
+// memory (one word per workgroup, 512 workgroups: 2 per compute unit).
 extern "C" int aw4_time_stream_read(const void* dev_src, uint64_t bytes, void* dev_sink, void* hip_stream, int32_t reps,
                                     float* avg_us) {
     if (!dev_src || !dev_sink || !avg_us || reps < 1 || bytes < 16 || bytes % 16) return AW4_E_INVAL;
     hipStream_t s = (hipStream_t)hip_stream;
-    constexpr int kBlocks = 2048;
+    constexpr int kBlocks = 512;
     hipEvent_t e0, e1;
     if (hipEventCreate(&e0) != hipSuccess) return AW4_E_HIP;
     if (hipEventCreate(&e1) != hipSuccess) {

@@ -120,9 +120,10 @@ def cpu_baseline(ctx, seed):
 
 
 def stream_probe(torch, A, sizes=((1 << 30, 20), (100_000_000 // 16 * 16, 100))):
-    """Measured streaming-read bandwidth of the box: a plain device read
-    (aw4_time_stream_read: 16-byte non-temporal loads, every wave load 1 KB
-    contiguous) of 1 GiB and of 100 MB, average over reps launches."""
+    """Measured streaming-read bandwidth of the device: a plain read
+    (aw4_time_stream_read: 512 workgroups over contiguous chunks, 16-byte
+    non-temporal loads, eight 4 KB loads in flight per workgroup) of 1 GiB and
+    of 100 MB, average over reps launches."""
     out = {}
     sink = torch.zeros(2048, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()

@@ -379,12 +379,12 @@ enum {
 int aw4_time_phase(aw4_model* model, int32_t phase, int32_t reps, float* avg_us, uint64_t* bytes_per_launch);
 
 /* Streaming-read bandwidth of the device, the measured reference beside the
- * 8 TB/s peak in bandwidth reports: reps launches of a plain read kernel
- * (16-byte non-temporal loads, 2048 workgroups, every wave load 1 KB of
- * contiguous memory) over bytes (a multiple of 16) at dev_src, timed between
- * two HIP events on hip_stream after one untimed launch; *avg_us receives the
- * average launch duration.  dev_sink: at least 8 KB of device memory the
- * kernel writes.  Synchronous.  Errors: AW4_E_INVAL, AW4_E_HIP. */
+ * 8 TB/s peak in bandwidth reports: reps launches of a plain read kernel (512
+ * workgroups, each reading one contiguous chunk with eight 4 KB workgroup loads
+ * of 16-byte non-temporal words in flight) over bytes (a multiple of 16) at
+ * dev_src, timed between two HIP events on hip_stream after one untimed launch;
+ * *avg_us receives the average launch duration.  dev_sink: at least 8 KB of
+ * device memory the kernel writes.  Synchronous.  Errors: AW4_E_INVAL, AW4_E_HIP. */
 int aw4_time_stream_read(const void* dev_src, uint64_t bytes, void* dev_sink, void* hip_stream, int32_t reps,
                          float* avg_us);
 
