@@ -252,8 +252,9 @@ struct HeadMultiArgs {
     const float* nw;
     float eps;
     float* logits;         // [M][V]
-    float* part_val;       // [M][nblocks]
+    float* part_val;       // [M][nparts]
     int32_t* part_idx;
+    int32_t nparts;        // partial slots per vector (set by launch_head_multi: head_blocks(V))
 };
 hipError_t launch_head_multi(const HeadMultiArgs& a, hipStream_t s);
 int head_blocks(int V);

@@ -12,6 +12,8 @@
 // The input vector is produced by a fused prologue (RMSNorm, gated RMSNorm or
 // a plain fp16 load) and the result leaves through a fused epilogue (store,
 // residual add, SwiGLU of an interleaved gate/up pair).
+#include <mutex>
+
 #include "aw4_internal.h"
 
 #include <algorithm>
@@ -1132,126 +1134,136 @@ __global__ __launch_bounds__(256, 2) void k_gemv_mfma(GemvMultiArgs a) {
     __syncthreads();
 
     const int nrb = (rows + 15) / 16;
-    const int blk = blockIdx.x * NB + wave / KS;
-    const bool live = blk < nrb;                       // uniform over the KS waves of a block
-    const int gbeg = (wave % KS) * (NST * U);   // NST stages of U groups per wave
-    const int r0 = blk * 16;
-    // codes: lane (c, q) loads row c's group g + q whole (16 bytes) and four
-    // lane-row swaps hand each lane its dword of every group (see compute);
-    // the four result rows, clamped into the matrix
-    const u32x4* arow = (const u32x4*)(a.codes + (int64_t)min(r0 + c, rows - 1) * G * 4) + q;
-    const uint16_t* srow[4];
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) srow[rr] = a.scales + (int64_t)min(r0 + 4 * q + rr, rows - 1) * G;
     // B operand: input min(c, M - 1) (columns past M are computed and dropped)
     const _Float16* xrow = xs + min(c, M - 1) * (K + kMfmaPad) + 8 * q;
-
-    struct Stage {
-        u32x4 w[U / 4];     // row c, groups g0 + 4h + q (h < U/4), all four dwords
-        uint4 s[4];         // fp16 scales of groups g0 .. g0 + U - 1, rows 4q .. 4q + 3
-    };
-    auto load = [&](Stage& st, int sidx) {
-        const int g0 = gbeg + sidx * U;
-#pragma unroll
-        for (int h = 0; h < U / 4; ++h) st.w[h] = __builtin_nontemporal_load(arow + g0 + 4 * h);
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) st.s[rr] = *(const uint4*)(srow[rr] + g0);
-    };
     const NibK nk;
     const h2 off_lo = {(_Float16)-1032.0f, (_Float16)-1032.0f};
     const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
     const h2 off_hi = {(_Float16)-72.0f, (_Float16)-72.0f};
     const f4 zero = {0.f, 0.f, 0.f, 0.f};
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    auto compute = [&](const Stage& st, int sidx) {
-        const int g0 = gbeg + sidx * U;
-        // the stage's input fragments first (LDS latency once per stage), then
-        // the products back to back, then the scales
-        uint4 xb[U];
-#pragma unroll
-        for (int j = 0; j < U; ++j) xb[j] = *(const uint4*)(xrow + 32 * (g0 + j));
-        asm volatile("" ::: "memory");   // issued together, before the products
-        // 4 x 4 transpose across the lane rows (16 lanes each): lane row t
-        // holds dwords 0..3 of group g0 + 4h + t; after two 32-lane and two
-        // 16-lane swaps, word j of lane row q is dword q of group g0 + 4h + j
-        uint32_t wd[U];
-#pragma unroll
-        for (int h = 0; h < U / 4; ++h) {
-            const auto ab = __builtin_amdgcn_permlane32_swap(st.w[h][0], st.w[h][2], false, false);
-            const auto cd = __builtin_amdgcn_permlane32_swap(st.w[h][1], st.w[h][3], false, false);
-            const auto t01 = __builtin_amdgcn_permlane16_swap(ab[0], cd[0], false, false);
-            const auto t23 = __builtin_amdgcn_permlane16_swap(ab[1], cd[1], false, false);
-            wd[4 * h] = t01[0];
-            wd[4 * h + 1] = t01[1];
-            wd[4 * h + 2] = t23[0];
-            wd[4 * h + 3] = t23[1];
-        }
-        f4 d[U];
-#pragma unroll
-        for (int j = 0; j < U; ++j) {
-            // exact codes: lo slots 1024 + n - 1032, hi slots (1024 + 16 n) / 16 - 72
-            const uint32_t w = wd[j], w8 = w >> 8;
-            const h2 p0 = as_h2((w & nk.lo) | nk.e) + off_lo;
-            const h2 p1 = __builtin_elementwise_fma(as_h2((w & nk.hi) | nk.e), sixteenth, off_hi);
-            const h2 p2 = as_h2((w8 & nk.lo) | nk.e) + off_lo;
-            const h2 p3 = __builtin_elementwise_fma(as_h2((w8 & nk.hi) | nk.e), sixteenth, off_hi);
-            const h8 av = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-            d[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(h8, xb[j]), zero, 0, 0, 0);
-        }
-#pragma unroll
-        for (int j = 0; j < U; ++j)
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const uint32_t sw = (j >> 1) == 0 ? st.s[rr].x : (j >> 1) == 1 ? st.s[rr].y
-                                  : (j >> 1) == 2 ? st.s[rr].z : st.s[rr].w;
-                acc[rr] += (float)as_h2(sw)[j & 1] * d[j][rr];
-            }
+    struct Stage {
+        u32x4 w[U / 4];     // row c, groups g0 + 4h + q (h < U/4), all four dwords
+        uint4 s[4];         // fp16 scales of groups g0 .. g0 + U - 1, rows 4q .. 4q + 3
     };
-    if (live) {
-        // three register sets used in turn, each refilled right after use, in
-        // straight-line code (a loop header would merge the wait counts); loads
-        // past the last stage re-read it so every step issues the same ones
-        Stage ring[3];
-        load(ring[0], 0);
-        load(ring[1], NST > 1 ? 1 : 0);
+    const int gbeg = (wave % KS) * (NST * U);   // NST stages of U groups per wave
+    // persistent: workgroup units (NB row blocks each) in turn, so that a
+    // launch of one round of resident workgroups covers every row block
+    const int nunits = (nrb + NB - 1) / NB;
+    for (int unit = blockIdx.x; unit < nunits; unit += gridDim.x) {
+        const int blk = unit * NB + wave / KS;
+        const bool live = blk < nrb;                       // uniform over the KS waves of a block
+        const int r0 = blk * 16;
+        // codes: lane (c, q) loads row c's group g + q whole (16 bytes) and four
+        // lane-row swaps hand each lane its dword of every group (see compute);
+        // the four result rows, clamped into the matrix
+        const u32x4* arow = (const u32x4*)(a.codes + (int64_t)min(r0 + c, rows - 1) * G * 4) + q;
+        const uint16_t* srow[4];
 #pragma unroll
-        for (int sidx = 0; sidx < NST; ++sidx) {
-            load(ring[(sidx + 2) % 3], sidx + 2 < NST ? sidx + 2 : NST - 1);
-            asm volatile("" ::: "memory");   // keep each stage's loads in their place
-            compute(ring[sidx % 3], sidx);
-        }
-    }
-    if (KS > 1) {
-        part[wave * 64 + lane] = f4{acc[0], acc[1], acc[2], acc[3]};
-        __syncthreads();
-        if (wave % KS != 0) return;
+        for (int rr = 0; rr < 4; ++rr) srow[rr] = a.scales + (int64_t)min(r0 + 4 * q + rr, rows - 1) * G;
+        auto load = [&](Stage& st, int sidx) {
+            const int g0 = gbeg + sidx * U;
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) acc[rr] = 0.f;
+            for (int h = 0; h < U / 4; ++h) st.w[h] = __builtin_nontemporal_load(arow + g0 + 4 * h);
 #pragma unroll
-        for (int t = 0; t < KS; ++t) {
-            const f4 v = part[(wave + t) * 64 + lane];
+            for (int rr = 0; rr < 4; ++rr) st.s[rr] = *(const uint4*)(srow[rr] + g0);
+        };
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        auto compute = [&](const Stage& st, int sidx) {
+            const int g0 = gbeg + sidx * U;
+            // the stage's input fragments first (LDS latency once per stage), then
+            // the products back to back, then the scales
+            uint4 xb[U];
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) acc[rr] += v[rr];
-        }
-    }
-    if (!live || c >= M) return;
-    const int rb = r0 + 4 * q;
-    if (EPI == EPI_STORE) {
+            for (int j = 0; j < U; ++j) xb[j] = *(const uint4*)(xrow + 32 * (g0 + j));
+            asm volatile("" ::: "memory");   // issued together, before the products
+            // 4 x 4 transpose across the lane rows (16 lanes each): lane row t
+            // holds dwords 0..3 of group g0 + 4h + t; after two 32-lane and two
+            // 16-lane swaps, word j of lane row q is dword q of group g0 + 4h + j
+            uint32_t wd[U];
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-            if (rb + rr < rows) a.y[c * a.sy + rb + rr] = acc[rr];
-    } else if (EPI == EPI_RESID) {
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-            if (rb + rr < rows) a.y[c * a.sy + rb + rr] += acc[rr];
-    } else {
-        // interleaved gate/up rows: (4q, 4q + 1) and (4q + 2, 4q + 3)
-#pragma unroll
-        for (int rr = 0; rr < 4; rr += 2)
-            if (rb + rr + 1 < rows) {
-                const float gg = acc[rr];
-                a.hout[c * a.so + ((rb + rr) >> 1)] = (_Float16)(gg * sigmoidf_(gg) * acc[rr + 1]);
+            for (int h = 0; h < U / 4; ++h) {
+                const auto ab = __builtin_amdgcn_permlane32_swap(st.w[h][0], st.w[h][2], false, false);
+                const auto cd = __builtin_amdgcn_permlane32_swap(st.w[h][1], st.w[h][3], false, false);
+                const auto t01 = __builtin_amdgcn_permlane16_swap(ab[0], cd[0], false, false);
+                const auto t23 = __builtin_amdgcn_permlane16_swap(ab[1], cd[1], false, false);
+                wd[4 * h] = t01[0];
+                wd[4 * h + 1] = t01[1];
+                wd[4 * h + 2] = t23[0];
+                wd[4 * h + 3] = t23[1];
             }
+            f4 d[U];
+#pragma unroll
+            for (int j = 0; j < U; ++j) {
+                // exact codes: lo slots 1024 + n - 1032, hi slots (1024 + 16 n) / 16 - 72
+                const uint32_t w = wd[j], w8 = w >> 8;
+                const h2 p0 = as_h2((w & nk.lo) | nk.e) + off_lo;
+                const h2 p1 = __builtin_elementwise_fma(as_h2((w & nk.hi) | nk.e), sixteenth, off_hi);
+                const h2 p2 = as_h2((w8 & nk.lo) | nk.e) + off_lo;
+                const h2 p3 = __builtin_elementwise_fma(as_h2((w8 & nk.hi) | nk.e), sixteenth, off_hi);
+                const h8 av = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+                d[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(h8, xb[j]), zero, 0, 0, 0);
+            }
+#pragma unroll
+            for (int j = 0; j < U; ++j)
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const uint32_t sw = (j >> 1) == 0 ? st.s[rr].x : (j >> 1) == 1 ? st.s[rr].y
+                                      : (j >> 1) == 2 ? st.s[rr].z : st.s[rr].w;
+                    acc[rr] += (float)as_h2(sw)[j & 1] * d[j][rr];
+                }
+        };
+        if (live) {
+            // three register sets used in turn, each refilled right after use, in
+            // straight-line code (a loop header would merge the wait counts); loads
+            // past the last stage re-read it so every step issues the same ones
+            Stage ring[3];
+            load(ring[0], 0);
+            load(ring[1], NST > 1 ? 1 : 0);
+#pragma unroll
+            for (int sidx = 0; sidx < NST; ++sidx) {
+                load(ring[(sidx + 2) % 3], sidx + 2 < NST ? sidx + 2 : NST - 1);
+                asm volatile("" ::: "memory");   // keep each stage's loads in their place
+                compute(ring[sidx % 3], sidx);
+            }
+        }
+        bool out = live && c < M;
+        if (KS > 1) {
+            part[wave * 64 + lane] = f4{acc[0], acc[1], acc[2], acc[3]};
+            __syncthreads();
+            if (wave % KS == 0) {
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) acc[rr] = 0.f;
+#pragma unroll
+                for (int t = 0; t < KS; ++t) {
+                    const f4 v = part[(wave + t) * 64 + lane];
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) acc[rr] += v[rr];
+                }
+            } else {
+                out = false;
+            }
+            __syncthreads();   // part[] is reused by the next unit
+        }
+        if (out) {
+            const int rb = r0 + 4 * q;
+            if (EPI == EPI_STORE) {
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr)
+                    if (rb + rr < rows) a.y[c * a.sy + rb + rr] = acc[rr];
+            } else if (EPI == EPI_RESID) {
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr)
+                    if (rb + rr < rows) a.y[c * a.sy + rb + rr] += acc[rr];
+            } else {
+                // interleaved gate/up rows: (4q, 4q + 1) and (4q + 2, 4q + 3)
+#pragma unroll
+                for (int rr = 0; rr < 4; rr += 2)
+                    if (rb + rr + 1 < rows) {
+                        const float gg = acc[rr];
+                        a.hout[c * a.so + ((rb + rr) >> 1)] = (_Float16)(gg * sigmoidf_(gg) * acc[rr + 1]);
+                    }
+            }
+        }
     }
 }
 
@@ -1266,7 +1278,8 @@ __global__ __launch_bounds__(256, 2) void k_gemv_mfma(GemvMultiArgs a) {
 // two spans (four groups) run two ahead in a ring of three register sets,
 // unrolled by three so that no copy moves a set.
 // Results: logits [M][V] and per-workgroup best value and index per vector
-// (lowest index on ties), gridDim.x partials per vector as k_head_multi.
+// (lowest index on ties), a.nparts partial slots per vector as k_head_multi
+// (slots past the grid hold -inf).
 template <int H>
 __global__ __launch_bounds__(256, 2) void k_head_mfma(HeadMultiArgs a) {
     constexpr int MAXM = 4, GR = H / 32, NSP = H / 64, SPS = 2, NST = NSP / SPS;   // spans per stage, stages per row block
@@ -1394,8 +1407,13 @@ __global__ __launch_bounds__(256, 2) void k_head_mfma(HeadMultiArgs a) {
         int bi = bi_s[m][0];
         for (int w = 1; w < 4; ++w)
             if (better(bv_s[m][w], bi_s[m][w], b, bi)) { b = bv_s[m][w]; bi = bi_s[m][w]; }
-        a.part_val[m * gridDim.x + blockIdx.x] = b;
-        a.part_idx[m * gridDim.x + blockIdx.x] = bi;
+        a.part_val[m * a.nparts + blockIdx.x] = b;
+        a.part_idx[m * a.nparts + blockIdx.x] = bi;
+        // slots past the grid: empty (never better than a real partial)
+        for (int p = blockIdx.x + gridDim.x; p < a.nparts; p += gridDim.x) {
+            a.part_val[m * a.nparts + p] = -INFINITY;
+            a.part_idx[m * a.nparts + p] = 0x7fffffff;
+        }
     }
 }
 
@@ -1514,6 +1532,28 @@ int gemv_blocks(int rows) {
 }
 
 int head_blocks(int V) { return gemv_blocks(V); }
+
+// workgroups of 256 threads of fn with shm bytes of dynamic LDS that the
+// current device holds at once (0 if the runtime cannot tell); cached per
+// (kernel, LDS size)
+int resident_blocks(const void* fn, size_t shm) {
+    struct Entry { const void* fn; size_t shm; int dev, n; };
+    static Entry cache[64];
+    static int ncache = 0;
+    static std::mutex mu;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < ncache; ++i)
+        if (cache[i].fn == fn && cache[i].shm == shm && cache[i].dev == dev) return cache[i].n;
+    int cus = 0, nb = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, 256, shm) != hipSuccess)
+        return 0;
+    const int n = nb * cus;
+    if (ncache < 64) cache[ncache++] = Entry{fn, shm, dev, n};
+    return n;
+}
 
 // the mapped head over its shorter id list: one round of two workgroups per
 // CU (measured 57 us for 65,536 rows against 65 us at the 1024 workgroups of
@@ -1652,13 +1692,17 @@ namespace {
 template <int P, int E, int KS, int NST>
 hipError_t launch_mfma(const GemvMultiArgs& a, hipStream_t s) {
     const int nrb = (a.rows + 15) / 16;
-    const dim3 grid((nrb + 4 / KS - 1) / (4 / KS)), block(256);
+    const int nunits = (nrb + 4 / KS - 1) / (4 / KS);
     const size_t shm = 64 + (size_t)2 * a.M * (a.K + kMfmaPad) + (KS > 1 ? 4 * 64 * 16 : 0);
+    const void* fn = (const void*)k_gemv_mfma<P, E, KS, NST>;
     if (shm > 65536) {
-        hipError_t e = hipFuncSetAttribute((const void*)k_gemv_mfma<P, E, KS, NST>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
         if (e != hipSuccess) return e;
     }
+    // one round of resident workgroups, each taking units in turn: a partial
+    // second round ran on a mostly idle chip
+    const int res = resident_blocks(fn, shm);
+    const dim3 grid(res > 0 && res < nunits ? res : nunits), block(256);
     hipLaunchKernelGGL((k_gemv_mfma<P, E, KS, NST>), grid, block, shm, s, a);
     return hipGetLastError();
 }
@@ -1736,8 +1780,14 @@ hipError_t launch_head_multi(const HeadMultiArgs& a, hipStream_t s) {
             hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
             if (e != hipSuccess) return e;
         }
-        if (a.H == 5120) hipLaunchKernelGGL(k_head_mfma<5120>, dim3(head_blocks(a.V)), dim3(256), shm, s, a);
-        else hipLaunchKernelGGL(k_head_mfma<512>, dim3(head_blocks(a.V)), dim3(256), shm, s, a);
+        // one round of resident workgroups (a partial second round ran on a
+        // mostly idle chip); partial slots past the grid are filled empty
+        HeadMultiArgs b = a;
+        b.nparts = head_blocks(a.V);
+        const int res = resident_blocks(fn, shm);
+        const dim3 grid(res > 0 && res < b.nparts ? res : b.nparts);
+        if (a.H == 5120) hipLaunchKernelGGL(k_head_mfma<5120>, grid, dim3(256), shm, s, b);
+        else hipLaunchKernelGGL(k_head_mfma<512>, grid, dim3(256), shm, s, b);
         return hipGetLastError();
     }
     const size_t shm = 64 + (size_t)a.H * 2 * (size_t)a.M;
