@@ -1143,7 +1143,7 @@ __global__ __launch_bounds__(256, 2) void k_gemv_mfma(GemvMultiArgs a) {
     const f4 zero = {0.f, 0.f, 0.f, 0.f};
     struct Stage {
         u32x4 w[U / 4];     // row c, groups g0 + 4h + q (h < U/4), all four dwords
-        uint4 s[4];         // fp16 scales of groups g0 .. g0 + U - 1, rows 4q .. 4q + 3
+        uint4 s;            // row c: fp16 scales of groups g0 .. g0 + U - 1
     };
     const int gbeg = (wave % KS) * (NST * U);   // NST stages of U groups per wave
     // persistent: workgroup units (NB row blocks each) in turn, so that a
@@ -1153,19 +1153,16 @@ __global__ __launch_bounds__(256, 2) void k_gemv_mfma(GemvMultiArgs a) {
         const int blk = unit * NB + wave / KS;
         const bool live = blk < nrb;                       // uniform over the KS waves of a block
         const int r0 = blk * 16;
+        const int row = min(r0 + c, rows - 1);
         // codes: lane (c, q) loads row c's group g + q whole (16 bytes) and four
-        // lane-row swaps hand each lane its dword of every group (see compute);
-        // the four result rows, clamped into the matrix
-        const u32x4* arow = (const u32x4*)(a.codes + (int64_t)min(r0 + c, rows - 1) * G * 4) + q;
-        const uint16_t* srow[4];
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) srow[rr] = a.scales + (int64_t)min(r0 + 4 * q + rr, rows - 1) * G;
+        // lane-row swaps hand each lane its dword of every group (see compute)
+        const u32x4* arow = (const u32x4*)(a.codes + (int64_t)row * G * 4) + q;
+        const uint16_t* srow = a.scales + (int64_t)row * G;
         auto load = [&](Stage& st, int sidx) {
             const int g0 = gbeg + sidx * U;
 #pragma unroll
-            for (int h = 0; h < U / 4; ++h) st.w[h] = __builtin_nontemporal_load(arow + g0 + 4 * h);
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) st.s[rr] = *(const uint4*)(srow[rr] + g0);
+            for (int h = 0; h < U / 4; ++h) st.w[h] = arow[g0 + 4 * h];   // plain loads: see the head below
+            st.s = *(const uint4*)(srow + g0);
         };
         float acc[4] = {0.f, 0.f, 0.f, 0.f};
         auto compute = [&](const Stage& st, int sidx) {
@@ -1201,32 +1198,34 @@ __global__ __launch_bounds__(256, 2) void k_gemv_mfma(GemvMultiArgs a) {
                 const h2 p2 = as_h2((w8 & nk.lo) | nk.e) + off_lo;
                 const h2 p3 = __builtin_elementwise_fma(as_h2((w8 & nk.hi) | nk.e), sixteenth, off_hi);
                 const h8 av = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-                d[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(h8, xb[j]), zero, 0, 0, 0);
+                // D = X W^T: lane (c, q) gets inputs 4 q .. 4 q + 3 at row c
+                d[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, xb[j]), av, zero, 0, 0, 0);
             }
 #pragma unroll
-            for (int j = 0; j < U; ++j)
+            for (int j = 0; j < U; ++j) {
+                const uint32_t sw = (j >> 1) == 0 ? st.s.x : (j >> 1) == 1 ? st.s.y : (j >> 1) == 2 ? st.s.z : st.s.w;
+                const float sc = (float)as_h2(sw)[j & 1];
 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    const uint32_t sw = (j >> 1) == 0 ? st.s[rr].x : (j >> 1) == 1 ? st.s[rr].y
-                                      : (j >> 1) == 2 ? st.s[rr].z : st.s[rr].w;
-                    acc[rr] += (float)as_h2(sw)[j & 1] * d[j][rr];
-                }
+                for (int rr = 0; rr < 4; ++rr) acc[rr] += sc * d[j][rr];
+            }
         };
         if (live) {
-            // three register sets used in turn, each refilled right after use, in
+            // RING register sets used in turn, each refilled right after use, in
             // straight-line code (a loop header would merge the wait counts); loads
             // past the last stage re-read it so every step issues the same ones
-            Stage ring[3];
-            load(ring[0], 0);
-            load(ring[1], NST > 1 ? 1 : 0);
+            constexpr int RING = 5;
+            Stage ring[RING];
+#pragma unroll
+            for (int k = 0; k < RING - 1; ++k) load(ring[k], k < NST ? k : NST - 1);
 #pragma unroll
             for (int sidx = 0; sidx < NST; ++sidx) {
-                load(ring[(sidx + 2) % 3], sidx + 2 < NST ? sidx + 2 : NST - 1);
+                load(ring[(sidx + RING - 1) % RING], sidx + RING - 1 < NST ? sidx + RING - 1 : NST - 1);
                 asm volatile("" ::: "memory");   // keep each stage's loads in their place
-                compute(ring[sidx % 3], sidx);
+                compute(ring[sidx % RING], sidx);
             }
         }
-        bool out = live && c < M;
+        // lane (c, q): inputs 4 q + rr at row r0 + c (M <= 4: the q = 0 lanes)
+        bool out = live && q == 0;
         if (KS > 1) {
             part[wave * 64 + lane] = f4{acc[0], acc[1], acc[2], acc[3]};
             __syncthreads();
@@ -1244,25 +1243,27 @@ __global__ __launch_bounds__(256, 2) void k_gemv_mfma(GemvMultiArgs a) {
             }
             __syncthreads();   // part[] is reused by the next unit
         }
-        if (out) {
-            const int rb = r0 + 4 * q;
-            if (EPI == EPI_STORE) {
+        if (EPI == EPI_SWIGLU) {
+            // interleaved gate/up rows: even lane c holds gate row r0 + c, the
+            // next lane its up row
+            float up[4];
 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr)
-                    if (rb + rr < rows) a.y[c * a.sy + rb + rr] = acc[rr];
-            } else if (EPI == EPI_RESID) {
+            for (int rr = 0; rr < 4; ++rr) up[rr] = __shfl_down(acc[rr], 1, 64);
+            if (out && (c & 1) == 0 && r0 + c + 1 < rows) {
 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr)
-                    if (rb + rr < rows) a.y[c * a.sy + rb + rr] += acc[rr];
-            } else {
-                // interleaved gate/up rows: (4q, 4q + 1) and (4q + 2, 4q + 3)
-#pragma unroll
-                for (int rr = 0; rr < 4; rr += 2)
-                    if (rb + rr + 1 < rows) {
-                        const float gg = acc[rr];
-                        a.hout[c * a.so + ((rb + rr) >> 1)] = (_Float16)(gg * sigmoidf_(gg) * acc[rr + 1]);
+                for (int m = 0; m < 4; ++m)
+                    if (m < M) {
+                        const float gg = acc[m];
+                        a.hout[m * a.so + ((r0 + c) >> 1)] = (_Float16)(gg * sigmoidf_(gg) * up[m]);
                     }
             }
+        } else if (out && r0 + c < rows) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                if (m < M) {
+                    if (EPI == EPI_STORE) a.y[m * a.sy + r0 + c] = acc[m];
+                    else a.y[m * a.sy + r0 + c] += acc[m];
+                }
         }
     }
 }
@@ -1271,18 +1272,23 @@ __global__ __launch_bounds__(256, 2) void k_gemv_mfma(GemvMultiArgs a) {
 // time multiple of 256).  A wave takes blocks of 16 rows; per 64-byte span of
 // a row (64 codes), lane (c, q) loads bytes 16 q .. 16 q + 15 of row c, and a
 // 4 x 4 transpose across the lane rows (two 32-lane and two 16-lane swaps)
-// leaves word j of lane row q = codes 16 j + 4 q .. + 3, the A operand of
-// v_mfma_f32_16x16x16_f16 j (exact codes as fp16); the B operand is input c
-// at the same four positions, from LDS.  Two products make a 32-code group,
-// whose fp16 scale then multiplies each of the lane's four rows.  Stages of
-// two spans (four groups) run two ahead in a ring of three register sets,
-// unrolled by three so that no copy moves a set.
+// leaves word j of lane row q = codes 16 j + 4 q .. + 3 of row c: the B
+// operand of v_mfma_f32_16x16x16_f16 j (exact codes as fp16); the A operand
+// is input c at the same four positions, from LDS.  The product D = X W^T
+// gives lane (c, q) the logits of inputs 4 q .. 4 q + 3 at row c, so a lane
+// needs only its own row's fp16 group scales.  Stages of two spans (four
+// groups) run four ahead in a ring of five register sets, unrolled by five so
+// that no copy moves a set.  Each load instruction takes 64 bytes of each of
+// 16 rows; plain loads serve that pattern faster than non-temporal ones (head
+// 394 -> 297 us, M = 4 FFN gate/up 32.3 -> 27.9 us, with the same HBM bytes
+// fetched), in this kernel and in k_gemv_mfma.
 // Results: logits [M][V] and per-workgroup best value and index per vector
 // (lowest index on ties), a.nparts partial slots per vector as k_head_multi
 // (slots past the grid hold -inf).
 template <int H>
 __global__ __launch_bounds__(256, 2) void k_head_mfma(HeadMultiArgs a) {
     constexpr int MAXM = 4, GR = H / 32, NSP = H / 64, SPS = 2, NST = NSP / SPS;   // spans per stage, stages per row block
+    constexpr int RING = 5;
     static_assert(NSP % SPS == 0, "row length");
     typedef float f4 __attribute__((ext_vector_type(4)));
     typedef _Float16 h4 __attribute__((ext_vector_type(4)));
@@ -1308,23 +1314,21 @@ __global__ __launch_bounds__(256, 2) void k_head_mfma(HeadMultiArgs a) {
     const int nrb = (V + 15) / 16;
     const _Float16* xrow = xs + min(c, M - 1) * (H + kMfmaPad) + 4 * q;
     const h2 off = {(_Float16)1152.0f, (_Float16)1152.0f};
-    float best = -INFINITY;
-    int besti = 0x7fffffff;
+    float best[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    int besti[4] = {0x7fffffff, 0x7fffffff, 0x7fffffff, 0x7fffffff};
     struct Stage {
         u32x4 w[SPS];       // row c: span bytes 16 q .. 16 q + 15 of each span
-        uint2 s[4];         // rows 4 q + rr: fp16 scales of the stage's 4 groups
+        uint2 s;            // row c: fp16 scales of the stage's 4 groups
     };
     for (int rb = blockIdx.x * 4 + wave; rb < nrb; rb += gridDim.x * 4) {
         const int r0 = rb * 16;
-        const u32x4* arow = (const u32x4*)(a.codes + (int64_t)min(r0 + c, V - 1) * H) + q;
-        const uint16_t* srow[4];
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) srow[rr] = a.scales + (int64_t)min(r0 + 4 * q + rr, V - 1) * GR;
+        const int row = min(r0 + c, V - 1);
+        const u32x4* arow = (const u32x4*)(a.codes + (int64_t)row * H) + q;
+        const uint16_t* srow = a.scales + (int64_t)row * GR;
         auto load = [&](Stage& st, int sidx) {
 #pragma unroll
-            for (int h = 0; h < SPS; ++h) st.w[h] = __builtin_nontemporal_load(arow + 4 * (sidx * SPS + h));
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) st.s[rr] = *(const uint2*)(srow[rr] + 4 * sidx);
+            for (int h = 0; h < SPS; ++h) st.w[h] = arow[4 * (sidx * SPS + h)];
+            st.s = *(const uint2*)(srow + 4 * sidx);
         };
         float acc[4] = {0.f, 0.f, 0.f, 0.f};
         const f4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -1346,59 +1350,58 @@ __global__ __launch_bounds__(256, 2) void k_head_mfma(HeadMultiArgs a) {
                     const uint32_t b = wd[j] ^ 0x80808080u;
                     const h2 p01 = as_h2(__builtin_amdgcn_perm(0x64646464u, b, 0x04010400u)) - off;
                     const h2 p23 = as_h2(__builtin_amdgcn_perm(0x64646464u, b, 0x04030402u)) - off;
-                    const h4 av = {p01[0], p01[1], p23[0], p23[1]};
-                    d[j >> 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, __builtin_bit_cast(h4, xb[j]),
+                    const h4 wv = {p01[0], p01[1], p23[0], p23[1]};
+                    d[j >> 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(h4, xb[j]), wv,
                                                                      (j & 1) ? d[j >> 1] : zero, 0, 0, 0);
                 }
-                // groups 2 h and 2 h + 1 of the stage: scale halves of words h
+                // groups 2 h and 2 h + 1 of the stage: this row's scales
+                const h2 sc = as_h2(h == 0 ? st.s.x : st.s.y);
 #pragma unroll
                 for (int gg = 0; gg < 2; ++gg)
 #pragma unroll
-                    for (int rr = 0; rr < 4; ++rr) {
-                        const uint32_t sw = h == 0 ? st.s[rr].x : st.s[rr].y;
-                        acc[rr] += (float)as_h2(sw)[gg] * d[gg][rr];
-                    }
+                    for (int rr = 0; rr < 4; ++rr) acc[rr] += (float)sc[gg] * d[gg][rr];
             }
         };
         // loads past the last stage re-read it, so every step issues the same ones
-        Stage ring[3];
-        load(ring[0], 0);
-        load(ring[1], min(1, NST - 1));
-        for (int sidx = 0;; sidx += 3) {
-            load(ring[2], min(sidx + 2, NST - 1));
-            asm volatile("" ::: "memory");
-            compute(ring[0], sidx);
-            if (sidx + 1 >= NST) break;
-            load(ring[0], min(sidx + 3, NST - 1));
-            asm volatile("" ::: "memory");
-            compute(ring[1], sidx + 1);
-            if (sidx + 2 >= NST) break;
-            load(ring[1], min(sidx + 4, NST - 1));
-            asm volatile("" ::: "memory");
-            compute(ring[2], sidx + 2);
-            if (sidx + 3 >= NST) break;
-        }
-        if (c < M) {
+        Stage ring[RING];
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int row = r0 + 4 * q + rr;
-                if (row < V) {
-                    if (a.logits) a.logits[(int64_t)c * V + row] = acc[rr];
-                    if (better(acc[rr], row, best, besti)) { best = acc[rr]; besti = row; }
-                }
+        for (int k = 0; k < RING - 1; ++k) load(ring[k], min(k, NST - 1));
+        for (int sidx = 0;; sidx += RING) {
+#pragma unroll
+            for (int k = 0; k < RING; ++k) {
+                load(ring[(k + RING - 1) % RING], min(sidx + k + RING - 1, NST - 1));
+                asm volatile("" ::: "memory");
+                compute(ring[k], sidx + k);
+                if (sidx + k + 1 >= NST) break;
+            }
+            if (sidx + RING >= NST) break;
+        }
+        // lane (c, q): inputs 4 q + rr at row r0 + c
+        const int rowv = r0 + c;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int m = 4 * q + rr;
+            if (m < M && rowv < V) {
+                if (a.logits) a.logits[(int64_t)m * V + rowv] = acc[rr];
+                if (better(acc[rr], rowv, best[rr], besti[rr])) { best[rr] = acc[rr]; besti[rr] = rowv; }
             }
         }
     }
-    // per vector (lane column c): best over the four lane rows, then the waves
+    // per input (lanes q = 0, slot rr): best over the 16 rows of the lane row, then the waves
 #pragma unroll
-    for (int o = 16; o <= 32; o <<= 1) {
-        const float ov = __shfl_xor(best, o, 64);
-        const int oi = __shfl_xor(besti, o, 64);
-        if (better(ov, oi, best, besti)) { best = ov; besti = oi; }
-    }
-    if (q == 0 && c < M) {
-        bv_s[c][wave] = best;
-        bi_s[c][wave] = besti;
+    for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+        for (int o = 1; o <= 8; o <<= 1) {
+            const float ov = __shfl_xor(best[rr], o, 64);
+            const int oi = __shfl_xor(besti[rr], o, 64);
+            if (better(ov, oi, best[rr], besti[rr])) { best[rr] = ov; besti[rr] = oi; }
+        }
+    if (lane == 0) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            bv_s[rr][wave] = best[rr];
+            bi_s[rr][wave] = besti[rr];
+        }
     }
     __syncthreads();
     if (threadIdx.x < M) {
