@@ -73,10 +73,12 @@ def kv_bytes_per_pos(shape):
     return shape.attn_kv_heads * (codes + 2 * (d // 32) * 2)
 
 
-def cpu_baseline(ctx, seed):
+def cpu_baseline(ctx, seed, long_ctx=0):
     """Oracle on a bounded sample: one GDN layer step and one attention layer
     step at `ctx` cached positions (synthetic state), and the int8 head over a
-    1/8 slice of the vocabulary; scaled to one full token."""
+    1/8 slice of the vocabulary; scaled to one full token.  With long_ctx, also
+    one attention layer step at long_ctx cached positions, scaled the same way
+    (the GDN layers and the head do not depend on the context)."""
     import numpy as np
     import oracle
     import synth
@@ -110,13 +112,31 @@ def cpu_baseline(ctx, seed):
 
     tg, ta = med(step_g), med(step_a)
     th = med(lambda: oa.head(x)) * 8
-    per_token = full.pattern.count("G") * tg + full.pattern.count("A") * ta + th
+    ng, na = full.pattern.count("G"), full.pattern.count("A")
+    per_token = ng * tg + na * ta + th
     cores = len(os.sched_getaffinity(0))
     threads = int(os.environ.get("OMP_NUM_THREADS", cores))
-    return {"value": round(1.0 / per_token, 4), "unit": "tok/s", "cores": min(cores, threads), "kind": "oracle",
-            "sample": (f"fp64 C oracle: 1 GDN layer step ({tg:.3f} s) and 1 attention layer step ({ta:.3f} s) at "
-                       f"{ctx} cached positions, int8 head over vocab/8 ({th / 8:.3f} s); median of 3; "
-                       f"scaled to 48 + 16 layers + full head = {per_token:.2f} s/token")}
+    out = {"value": round(1.0 / per_token, 4), "unit": "tok/s", "cores": min(cores, threads), "kind": "oracle",
+           "sample": (f"fp64 C oracle: 1 GDN layer step ({tg:.3f} s) and 1 attention layer step ({ta:.3f} s) at "
+                      f"{ctx} cached positions, int8 head over vocab/8 ({th / 8:.3f} s); median of 3; "
+                      f"scaled to 48 + 16 layers + full head = {per_token:.2f} s/token")}
+    if long_ctx:
+        del oa
+        al = W.with_(full, pattern="A", vocab=0, max_ctx=long_ctx + 8, draft_vocab=0)
+        ol = oracle.from_recipe(al, seed)
+        SS.fill(ol, al, long_ctx, seed)
+
+        def step_l():
+            ol.set_pos(long_ctx)
+            ol.forward_layers(x)
+
+        tl = med(step_l)
+        per_long = ng * tg + na * tl + th
+        out["ctx_" + ("262k" if long_ctx == 262144 else str(long_ctx))] = {
+            "value": round(1.0 / per_long, 4), "unit": "tok/s",
+            "sample": (f"1 attention layer step at {long_ctx} cached positions ({tl:.3f} s, median of 3) with the "
+                       f"GDN layer and head times above; scaled to {per_long:.2f} s/token")}
+    return out
 
 
 def stream_probe(torch, A, sizes=((1 << 30, 20), (100_000_000 // 16 * 16, 100))):
@@ -542,7 +562,7 @@ def main():
     if args.kvformat_ctx:
         out["kv_formats"] = kvformat_leg(args, torch, A, W, SS, synth)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(args.ctx, args.seed)
+        out["cpu_baseline"] = cpu_baseline(args.ctx, args.seed, args.long_ctx)
     print(json.dumps(out), flush=True)
 
 
