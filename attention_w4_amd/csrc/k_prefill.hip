@@ -92,27 +92,30 @@ __global__ __launch_bounds__(256, 3) void k_gemm_w4(GemmArgs a) {
         const int L = tid + 256 * i;
         xbase[i] = a.x + (int64_t)min(m0 + (L >> 3), a.M - 1) * a.ldx + 8 * (L & 7);
     }
-    struct Stage {
-        uint4 x[4];
-        uint4 cw;
-        uint16_t sc;
-    };
-    auto gload = [&](Stage& st, int s) {
-        const int k0 = s * kGBK;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) st.x[i] = *(const uint4*)(xbase[i] + k0);
-        st.cw = cbase[2 * s];
-        st.sc = sbase[2 * s];
-    };
-    auto lstore = [&](const Stage& st, int buf) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int L = tid + 256 * i;
-            *(uint4*)&xs[buf][L >> 3][8 * (L & 7)] = st.x[i];
-        }
-        *(uint4*)&cs[buf][tid >> 1][4 * sg] = st.cw;
-        ss[buf][sg][tid >> 1] = st.sc;
-    };
+    // two register sets for the stages in flight (plain named values: a
+    // struct passed to the loaders by reference was kept on the stack, 176
+    // bytes of scratch traffic per lane per stage pair)
+    uint4 xa0, xa1, xa2, xa3, ca, xb0, xb1, xb2, xb3, cb;
+    uint16_t sca, scb;
+#define AW4_GLOAD(X0, X1, X2, X3, CW, SC, S)                       \
+    {                                                              \
+        const int k0_ = (S) * kGBK;                                \
+        X0 = *(const uint4*)(xbase[0] + k0_);                      \
+        X1 = *(const uint4*)(xbase[1] + k0_);                      \
+        X2 = *(const uint4*)(xbase[2] + k0_);                      \
+        X3 = *(const uint4*)(xbase[3] + k0_);                      \
+        CW = cbase[2 * (S)];                                       \
+        SC = sbase[2 * (S)];                                       \
+    }
+#define AW4_LSTORE(X0, X1, X2, X3, CW, SC, BUF)                    \
+    {                                                              \
+        *(uint4*)&xs[BUF][tid >> 3][8 * (tid & 7)] = X0;           \
+        *(uint4*)&xs[BUF][(tid + 256) >> 3][8 * (tid & 7)] = X1;   \
+        *(uint4*)&xs[BUF][(tid + 512) >> 3][8 * (tid & 7)] = X2;   \
+        *(uint4*)&xs[BUF][(tid + 768) >> 3][8 * (tid & 7)] = X3;   \
+        *(uint4*)&cs[BUF][tid >> 1][4 * sg] = CW;                  \
+        ss[BUF][sg][tid >> 1] = SC;                                \
+    }
 
     f4 acc[4][4];
 #pragma unroll
@@ -164,21 +167,22 @@ __global__ __launch_bounds__(256, 3) void k_gemm_w4(GemmArgs a) {
     // stage re-read it (the same straight-line loads every time, so the wait
     // counts stay exact); only the products of a missing odd stage are skipped.
     auto sidx = [&](int t) { return t < nstage ? t : nstage - 1; };
-    Stage sa, sb;
-    gload(sa, 0);
-    gload(sb, sidx(1));
-    lstore(sa, 0);
+    AW4_GLOAD(xa0, xa1, xa2, xa3, ca, sca, 0)
+    AW4_GLOAD(xb0, xb1, xb2, xb3, cb, scb, sidx(1))
+    AW4_LSTORE(xa0, xa1, xa2, xa3, ca, sca, 0)
     __syncthreads();
     for (int s = 0; s < nstage; s += 2) {
-        gload(sa, sidx(s + 2));
+        AW4_GLOAD(xa0, xa1, xa2, xa3, ca, sca, sidx(s + 2))
         compute(0);
-        lstore(sb, 1);
+        AW4_LSTORE(xb0, xb1, xb2, xb3, cb, scb, 1)
         __syncthreads();
-        gload(sb, sidx(s + 3));
+        AW4_GLOAD(xb0, xb1, xb2, xb3, cb, scb, sidx(s + 3))
         if (s + 1 < nstage) compute(1);
-        lstore(sa, 0);
+        AW4_LSTORE(xa0, xa1, xa2, xa3, ca, sca, 0)
         __syncthreads();
     }
+#undef AW4_GLOAD
+#undef AW4_LSTORE
 
     // epilogue: lane (c, q) of block (rb, tb) holds rows 4q..4q+3 of token c
 #pragma unroll
