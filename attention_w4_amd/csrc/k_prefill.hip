@@ -6,10 +6,10 @@
 // two minutes).  Every token computes what a decode step computes (the same
 // fp16 inputs, fp32 accumulation, the same KV codec and GDN recurrence); what
 // changes is that the weights are read once per chunk:
-//   - W4 GEMM on the matrix cores with exact weights: the fp16 group scale s
-//     splits into s_hi (its top 7 significant bits) and s_lo = s - s_hi (the
-//     rest), code x s_hi and code x s_lo are both exact in fp16, and two
-//     products per group accumulate in place in fp32;
+//   - W4 GEMM on the matrix cores with exact weights: one product per 32-value
+//     group of exact codes against the fp16 inputs (exact products, fp32
+//     sums), then the row's fp16 group scale applied in fp32, as the decode
+//     GEMV does;
 //   - Gated DeltaNet: the normalised q, k and the gates of all chunk tokens
 //     first, then one workgroup per (v head, 16 state rows) runs the tokens in
 //     order with its rows of S in registers;
@@ -52,16 +52,16 @@ __device__ __forceinline__ float block_sum256(float v, float* red) {
 // Stages of two 32-value groups: the token tile (fp16), the rows' code dwords
 // and their scales are staged in LDS (double buffered; two register sets hold
 // the next two stages, so a stage's loads have two stages of products to
-// arrive in).  A operands: 16 rows' code x s_hi and code x s_lo, lane (c, q)
-// row c, values 8q..8q+7 of the group (one code dword, nibble slots
-// [0,2,4,6,1,3,5,7], and the row's scale);
+// arrive in).  A operand: 16 rows' exact codes, lane (c, q) row c, values
+// 8q..8q+7 of the group (one code dword, nibble slots [0,2,4,6,1,3,5,7]);
 // B operand: 16 tokens, lane (c, q) token c, the same values.  D lane (c, q)
-// holds rows 4q..4q+3 of token c.
+// holds rows 4q..4q+3 of token c, which take their rows' scales before they
+// are added to the accumulators.
 constexpr int kGBK = 64;            // K values per stage (two groups)
 constexpr int kGXP = kGBK + 8;      // padded LDS row of the token tile (halves)
 
 template <int EPI>
-__global__ __launch_bounds__(256, 3) void k_gemm_w4(GemmArgs a) {
+__global__ __launch_bounds__(256, 2) void k_gemm_w4(GemmArgs a) {
     __shared__ __align__(16) _Float16 xs[2][128][kGXP];
     __shared__ __align__(16) uint32_t cs[2][128][8];     // [row][group 0..1][dword 0..3]
     __shared__ __align__(16) uint16_t ss[2][2][128];     // [group][row]
@@ -125,6 +125,7 @@ __global__ __launch_bounds__(256, 3) void k_gemm_w4(GemmArgs a) {
     const h2 off_lo = {(_Float16)-1032.0f, (_Float16)-1032.0f};
     const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
     const h2 off_hi = {(_Float16)-72.0f, (_Float16)-72.0f};
+    const f4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
     auto compute = [&](int buf) {
 #pragma unroll
@@ -142,20 +143,17 @@ __global__ __launch_bounds__(256, 3) void k_gemm_w4(GemmArgs a) {
                 const h2 p1 = __builtin_elementwise_fma(as_h2((w & 0x00F000F0u) | 0x64006400u), sixteenth, off_hi);
                 const h2 p2 = as_h2((w8 & 0x000F000Fu) | 0x64006400u) + off_lo;
                 const h2 p3 = __builtin_elementwise_fma(as_h2((w8 & 0x00F000F0u) | 0x64006400u), sixteenth, off_hi);
-                // s = s_hi + s_lo, s_hi with 7 significant bits: |code| <= 8 keeps
-                // both products exact in fp16 (s_lo may be subnormal)
-                const uint16_t sb = ss[buf][g][r + c];
-                const _Float16 shi = __builtin_bit_cast(_Float16, (uint16_t)(sb & 0xFFF0u));
-                const _Float16 slo = __builtin_bit_cast(_Float16, sb) - shi;
-                const h2 s2h = {shi, shi}, s2l = {slo, slo};
-                const h2 a0 = p0 * s2h, a1 = p1 * s2h, a2 = p2 * s2h, a3 = p3 * s2h;
-                const h2 b0 = p0 * s2l, b1 = p1 * s2l, b2 = p2 * s2l, b3 = p3 * s2l;
-                const h8 ah = {a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
-                const h8 al = {b0[0], b0[1], b1[0], b1[1], b2[0], b2[1], b3[0], b3[1]};
+                const h8 av = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+                // fp16 scales of the four rows this lane's results belong to
+                // (rows r + 4q .. r + 4q + 3), applied in fp32 after the product
+                const uint2 sv = *(const uint2*)&ss[buf][g][r + 4 * q];
+                const float s4[4] = {(float)as_h2(sv.x)[0], (float)as_h2(sv.x)[1], (float)as_h2(sv.y)[0],
+                                     (float)as_h2(sv.y)[1]};
 #pragma unroll
                 for (int tb = 0; tb < 4; ++tb) {
-                    acc[rb][tb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bv[tb], acc[rb][tb], 0, 0, 0);
-                    acc[rb][tb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bv[tb], acc[rb][tb], 0, 0, 0);
+                    const f4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv[tb], zero4, 0, 0, 0);
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) acc[rb][tb][rr] = __builtin_fmaf(s4[rr], d[rr], acc[rb][tb][rr]);
                 }
             }
         }
