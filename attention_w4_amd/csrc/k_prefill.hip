@@ -58,6 +58,13 @@ __device__ __forceinline__ float block_sum256(float v, float* red) {
 // holds rows 4q..4q+3 of token c, which take their rows' scales before they
 // are added to the accumulators.
 constexpr int kGBK = 64;            // K values per stage (two groups)
+// LDS position of code dword d of row R: d ^ cswz(R) within the row's 8
+// dwords.  A wave reads dword 4 g + q of rows r + c (c < 16) for one group g;
+// unswizzled, 16 rows 32 bytes apart fill only 16 of the 32 banks (4-way
+// conflicts); XOR with 0, 1, 4 or 5 by (R >> 2) & 3 spreads them over all 32
+// (2-way, the least for 256 bytes).  The row's two 16-byte halves swap for
+// 4 and 5, its dword pairs for 1 and 5.
+__device__ __forceinline__ int cswz(int R) { return ((R >> 2) & 1) | (((R >> 3) & 1) << 2); }
 constexpr int kGXP = kGBK + 8;      // padded LDS row of the token tile (halves)
 
 template <int EPI>
@@ -113,7 +120,11 @@ __global__ __launch_bounds__(256, 2) void k_gemm_w4(GemmArgs a) {
         *(uint4*)&xs[BUF][(tid + 256) >> 3][8 * (tid & 7)] = X1;   \
         *(uint4*)&xs[BUF][(tid + 512) >> 3][8 * (tid & 7)] = X2;   \
         *(uint4*)&xs[BUF][(tid + 768) >> 3][8 * (tid & 7)] = X3;   \
-        *(uint4*)&cs[BUF][tid >> 1][4 * sg] = CW;                  \
+        {                                                          \
+            const int sw_ = cswz(tid >> 1);                        \
+            *(uint4*)&cs[BUF][tid >> 1][4 * (sg ^ (sw_ >> 2))] =   \
+                (sw_ & 1) ? uint4{CW.y, CW.x, CW.w, CW.z} : CW;    \
+        }                                                          \
         ss[BUF][sg][tid >> 1] = SC;                                \
     }
 
@@ -138,7 +149,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_w4(GemmArgs a) {
             for (int rb = 0; rb < 4; ++rb) {
                 const int r = 64 * wr + 16 * rb;
                 // exact codes: lo slots 1024 + n - 1032, hi slots (1024 + 16 n) / 16 - 72
-                const uint32_t w = cs[buf][r + c][4 * g + q], w8 = w >> 8;
+                const uint32_t w = cs[buf][r + c][(4 * g + q) ^ cswz(c)], w8 = w >> 8;
                 const h2 p0 = as_h2((w & 0x000F000Fu) | 0x64006400u) + off_lo;
                 const h2 p1 = __builtin_elementwise_fma(as_h2((w & 0x00F000F0u) | 0x64006400u), sixteenth, off_hi);
                 const h2 p2 = as_h2((w8 & 0x000F000Fu) | 0x64006400u) + off_lo;
