@@ -11,6 +11,7 @@ cache codes may differ only by one at rounding ties.  Chunk sizes are chosen so
 that chunks end mid-prompt and the last chunk is ragged.
 """
 import sys
+import time
 
 import numpy as np
 import pytest
@@ -97,14 +98,14 @@ def test_prefill_tiny_grouped_heads(aw4):
 
 def test_prefill_chunked_equals_token_by_token(aw4):
     """The same prompt token by token (chunk 0) and in chunks of 100: the same
-    final state up to rounding.  Both paths keep the weights exact (the chunk
-    GEMM multiplies by code x s_hi and code x s_lo, the decode GEMV by code then
-    s), but they sum in fp32 in different orders (32 products per matrix-core
-    step against dot2 chains; one attention split against many), so a cached
-    code whose fp32 value sits at a rounding tie can land on either side, and
-    over 257 positions that are not teacher-forced each such flip moves the
-    later positions a little.  Measured: hidden 4.5e-4, recurrent state 3e-7,
-    0.75% of key codes and 0.02% of value codes one step apart; the bounds are
+    final state up to rounding.  Both paths keep the weights exact (products
+    of exact codes and fp16 inputs, the group scale applied to the fp32 sum),
+    but they sum in fp32 in different orders (32 products per matrix-core step
+    against dot2 chains; one attention split against many), so a cached code
+    whose fp32 value sits at a rounding tie can land on either side, and over
+    257 positions that are not teacher-forced each such flip moves the later
+    positions a little.  Measured: hidden 4.0e-4, recurrent state 1.7e-7,
+    0.5% of key codes and 0.01% of value codes one step apart; the bounds are
     1e-3 and 1%."""
     _say("case: toy stack prefill, chunks of 100 vs token by token")
     shape = W.TOY
@@ -196,3 +197,74 @@ def test_prefill_full_size(aw4):
     _say(f"hidden rel-L2 {rel_l2(xg, xo):.2e}, logits rel-L2 {rel_l2(lg, lo):.2e}, draft scores {derr}")
     assert rel_l2(xg, xo) < TOL and rel_l2(lg, lo) < TOL
     assert t0g == t0 and got == ref and max(derr) < TOL
+
+
+def _deq_keys(kc, ks, n):
+    """dequantised keys [n][nkv * d] from logical codes and fp16 scale bits"""
+    sc = ks.view(np.float16).astype(np.float64)
+    return (kc.astype(np.float64).reshape(n, -1, 32) * sc.reshape(n, -1, 1)).reshape(n, -1)
+
+
+@pytest.mark.timeout(600)
+def test_prefill_8k_full_size_chunked_vs_decode(aw4):
+    """The benchmark's prompt path at full size: the 8191-token random prompt
+    of the 8K workload through aw4_prefill in chunks of 1024 against the same
+    prompt through the decode step token by token (the path the oracle checks
+    step by step), each from a fresh model.
+
+    The two sum in different orders, so cached codes at rounding ties land on
+    either side (the toy test above).  At the first positions of a prompt a
+    layer's attention returns nearly one position's value, stored as 3-bit
+    codes, so one value-code flip there moves that output by a whole
+    quantisation step, and the deeper layers carry it on: measured, the
+    per-position difference of the dequantised keys is 3.6e-3 (median) in the
+    first attention layer and 1.0e-2 in the last, where position 0 differs by
+    23% and positions past 1024 by 1% on average.  The bounds: logits and
+    final hidden state within 1e-2 relative L2 (measured 6.2e-3); the first
+    GDN layer's state within 1e-5 (3.9e-7) and the last one's within 3e-2
+    (8.7e-3); the first attention layer's codes at most one step apart, under
+    5% of key codes (3.9%) and 1% of value codes (0.09%); the median
+    per-position key difference of the last attention layer under 2e-2; the
+    same next token unless the top-2 logit margin is below 0.05."""
+    import torch
+    shape = W.with_(W.FULL_27B, max_ctx=8192 + 32, draft_vocab=0)
+    prompt = synth.tokens(8192, shape.vocab, 0)
+    n = len(prompt) - 1
+    g_layers = [l for l, t in enumerate(shape.pattern) if t == "G"]
+    a_layers = [l for l, t in enumerate(shape.pattern) if t == "A"]
+    res = []
+    for chunk in (1024, 0):
+        _say(f"case: full-size prefill of {n} tokens, chunk {chunk}")
+        t0 = time.time()
+        gm = _gpu(aw4, shape, 0)
+        gm.set_prefill_chunk(chunk)
+        lo = torch.empty(shape.vocab, dtype=torch.float32, device="cuda")
+        gm.prefill(prompt[:-1], lo)
+        gm.sync()
+        _say(f"  prefill {time.time() - t0:.1f} s")
+        res.append({"lo": lo.cpu().numpy().astype(np.float64), "x": gm.read_hidden(),
+                    "S": [gm.export_gdn(l) for l in (g_layers[0], g_layers[-1])],
+                    "kv": [gm.export_kv(l, n) for l in (a_layers[0], a_layers[-1])]})
+        gm.close()
+        del gm
+        torch.cuda.empty_cache()
+    c, d = res
+    el, ex = rel_l2(c["lo"], d["lo"]), rel_l2(c["x"], d["x"])
+    es = [rel_l2(a, b) for a, b in zip(c["S"], d["S"])]
+    (kc1, ks1, vc1, _), (kc0, ks0, vc0, _) = c["kv"][0], d["kv"][0]
+    dk, dv = kc1.astype(int) - kc0.astype(int), vc1.astype(int) - vc0.astype(int)
+    kl1, kl0 = _deq_keys(c["kv"][1][0], c["kv"][1][1], n), _deq_keys(d["kv"][1][0], d["kv"][1][1], n)
+    prel = np.linalg.norm(kl1 - kl0, axis=1) / np.linalg.norm(kl0, axis=1)
+    top = np.argsort(-d["lo"])[:2]
+    margin = float(d["lo"][top[0]] - d["lo"][top[1]])
+    _say(f"chunked vs token by token at full size: logits {el:.2e} hidden {ex:.2e}; GDN states first "
+         f"{es[0]:.2e} last {es[1]:.2e}; first attention layer: key flips {(dk != 0).mean():.2e}, value flips "
+         f"{(dv != 0).mean():.2e}, max steps {np.abs(dk).max()} {np.abs(dv).max()}; last attention layer "
+         f"per-position key difference median {np.median(prel):.2e}, position 0 {prel[0]:.2e}; next token "
+         f"{int(np.argmax(c['lo']))} vs {int(top[0])} (margin {margin:.3f})")
+    assert el < 1e-2 and ex < 1e-2
+    assert es[0] < 1e-5 and es[1] < 3e-2
+    assert np.abs(dk).max() <= 1 and np.abs(dv).max() <= 1
+    assert (dk != 0).mean() < 5e-2 and (dv != 0).mean() < 1e-2
+    assert np.median(prel) < 2e-2
+    assert int(np.argmax(c["lo"])) == int(top[0]) or margin < 0.05
