@@ -1718,8 +1718,8 @@ bool try_mfma(int pro, int epi, int ks, int nst, const GemvMultiArgs& a, hipStre
         err = launch_mfma<P, E, KS, NST>(a, s);              \
         return true;                                         \
     }
-    AW4_MFMA(PRO_NORM, EPI_SWIGLU, 2, 10)   // FFN gate/up, K 5120
-    AW4_MFMA(PRO_NORM, EPI_STORE, 2, 10)    // mixer in-projections, K 5120
+    AW4_MFMA(PRO_NORM, EPI_SWIGLU, 4, 5)    // FFN gate/up, K 5120
+    AW4_MFMA(PRO_NORM, EPI_STORE, 4, 5)     // mixer in-projections, K 5120
     AW4_MFMA(PRO_GATED, EPI_RESID, 4, 4)    // GDN out-projection, K 4096
     AW4_MFMA(PRO_LOADH, EPI_RESID, 4, 6)    // attention o-projection, K 6144
     AW4_MFMA(PRO_LOADH, EPI_RESID, 4, 17)   // FFN down, K 17408
@@ -1749,8 +1749,11 @@ hipError_t launch_gemv_multi(int pro, int epi, const GemvMultiArgs& a, hipStream
         const int nrb = (a.rows + 15) / 16;
         // at least two waves per row block: with one, the stage offsets are
         // compile-time constants and the compiler merges the ring's loads
-        // until the registers spill
-        int ks = nrb <= 512 && G % (4 * kStage) == 0 ? 4 : G % (2 * kStage) == 0 ? 2 : 1;
+        // until the registers spill.  Four where the groups allow it: the
+        // resident workgroups take row blocks in turn, and the finer unit
+        // evens out their counts (2176 gate/up row blocks in units of two
+        // over 768 workgroups left a 41% tail)
+        int ks = G % (4 * kStage) == 0 ? 4 : G % (2 * kStage) == 0 ? 2 : 1;
         // an input image above half the LDS leaves one workgroup per CU: then
         // two waves per row block keep the grid within one round of CUs
         if (ks == 4 && (size_t)2 * a.M * a.K > 80 * 1024) ks = 2;
