@@ -55,6 +55,7 @@ struct TensorSlot {
 
 constexpr int kSweepRows = 4;   // most tokens one attention sweep takes (verify_k has at most 4)
 constexpr int kPrefillMaxChunk = 1024;   // prompt tokens per prefill chunk (buffers sized for it)
+constexpr int kGemmSplitSlots = 512;     // split-K partial tiles of the chunk GEMM (64 KB each)
 
 struct Plan {
     uint64_t off = 0;
@@ -148,6 +149,7 @@ struct aw4_model {
     float* pkn = nullptr;
     float* pab = nullptr;           // [C][nv][2]
     float* ppart = nullptr;         // attention partials, one split: [C nq][d + 2]
+    float* gpart = nullptr;         // chunk GEMM split-K partial tiles [kGemmSplitSlots][128 x 128]
     uint64_t state_off = 0, state_bytes = 0;   // recurrent states + caches of one sequence
     // sequences: max_batch copies of the state region, state_bytes apart; the
     // single-sequence calls work on sequence `seq` (aw4_select_sequence)
@@ -428,6 +430,7 @@ uint64_t plan_layout(const aw4_config* c, aw4_model* m, uint8_t* base) {
     const int C = gemm_ok ? (int)std::min<int64_t>(kPrefillMaxChunk, c->max_ctx) : 0;
     int32_t *ptok = nullptr, *pnext = nullptr;
     float *px = nullptr, *pp = nullptr, *po = nullptr, *pqn = nullptr, *pkn = nullptr, *pab = nullptr, *ppart = nullptr;
+    float* gpart = nullptr;
     _Float16 *pa = nullptr, *pf = nullptr;
     int64_t pa_ld = 0;
     if (C > 0) {
@@ -446,6 +449,7 @@ uint64_t plan_layout(const aw4_config* c, aw4_model* m, uint8_t* base) {
             pab = p.take<float>((uint64_t)C * c->gdn_v_heads * 2 * 4);
         }
         if (has_a || dh) ppart = p.take<float>((uint64_t)C * c->attn_q_heads * (c->attn_head_dim + 2) * 4);
+        gpart = p.take<float>((uint64_t)kGemmSplitSlots * 128 * 128 * 4);
     }
     float *xd = nullptr, *dscore = nullptr, *dpv = nullptr, *dzpart = nullptr;
     _Float16* ubuf = nullptr;
@@ -475,6 +479,7 @@ uint64_t plan_layout(const aw4_config* c, aw4_model* m, uint8_t* base) {
         m->pkn = pkn;
         m->pab = pab;
         m->ppart = ppart;
+        m->gpart = gpart;
         m->D = D;
         m->w_fuse = w_fuse;
         m->s_fuse = s_fuse;
@@ -1066,7 +1071,8 @@ int enqueue_phase(aw4_model* m, int phase, int l, uint64_t* bytes) {
             const int M = m->pchunk_max;
             if (M <= 0) return fail(m, AW4_E_STATE, "no chunked prefill for this shape");
             *bytes = 2ULL * M * (2ULL * F) * H;
-            GemmArgs ga{b.w_gu, b.s_gu, 2 * F, H, M, m->pa, m->pa_ld, nullptr, 0, m->pf, F};
+            GemmArgs ga{b.w_gu, b.s_gu, 2 * F, H, M, m->pa, m->pa_ld, nullptr, 0, m->pf, F,
+                        m->gpart, kGemmSplitSlots, 0, 0};
             HIPCHK(m, launch_gemm_w4(EPI_SWIGLU, ga, s));
             break;
         }
@@ -1260,7 +1266,8 @@ int enqueue_draft_select(aw4_model* m, int row, int j, int commit, float tempera
 // W4 GEMM of the chunk: out = x W^T over T tokens
 int prefill_gemm(aw4_model* m, int epi, const uint32_t* codes, const uint16_t* scales, int64_t N, int64_t K, int T,
                  const _Float16* x, int64_t ldx, float* y, int64_t ldy, _Float16* hout, int64_t ldo) {
-    GemmArgs g{codes, scales, (int32_t)N, (int32_t)K, T, x, ldx, y, ldy, hout, ldo};
+    GemmArgs g{codes, scales, (int32_t)N, (int32_t)K, T, x, ldx, y, ldy, hout, ldo, m->gpart, kGemmSplitSlots,
+               0, 0};
     HIPCHK(m, launch_gemm_w4(epi, g, m->stream));
     return AW4_OK;
 }

@@ -221,6 +221,13 @@ struct GemmArgs {
     int64_t ldy;
     _Float16* hout;          // SWIGLU: [M][ldo], column n / 2 from rows n, n + 1
     int64_t ldo;
+    // split-K of the last, partial round of tiles (null part: no split): each
+    // split writes its 128 x 128 fp32 partial tile to a slot of part
+    // (part_slots slots); a second kernel adds a tile's splits in split order
+    // and runs the epilogue
+    float* part;
+    int32_t part_slots;
+    int32_t nfull, nsplit;   // set by the launcher: units [0, nfull) are whole tiles
 };
 
 // Gated DeltaNet over the T tokens of a prefill chunk
@@ -258,6 +265,8 @@ struct HeadMultiArgs {
 };
 hipError_t launch_head_multi(const HeadMultiArgs& a, hipStream_t s);
 int head_blocks(int V);
+// workgroups of 256 threads of fn (shm bytes of dynamic LDS) resident at once
+int resident_blocks(const void* fn, size_t shm);
 int draft_head_blocks(int V);   // blocks of the mapped head (launch_head with a map)
 hipError_t launch_head_final(const float* pv, const int32_t* pi, int n, Ctl* ctl, int32_t* ring, int ring_cap,
                              hipStream_t s);

@@ -17,6 +17,8 @@
 //     one sweep block per few tokens of the chunk.
 #include "aw4_internal.h"
 
+#include <algorithm>
+
 namespace aw4 {
 namespace {
 
@@ -67,6 +69,51 @@ constexpr int kGBK = 64;            // K values per stage (two groups)
 __device__ __forceinline__ int cswz(int R) { return ((R >> 2) & 1) | (((R >> 3) & 1) << 2); }
 constexpr int kGXP = kGBK + 8;      // padded LDS row of the token tile (halves)
 
+// tile (rt, tt) of unit b: consecutive units go to the eight XCDs in turn, so
+// the token tiles of one row tile run on one XCD back to back and its weights
+// stay in that XCD's L2 (measured faster than giving each XCD one token tile
+// and streaming the weights past it, and than XCD pairs taking two token
+// tiles each, by 1-4%)
+__device__ __forceinline__ void gemm_tile(int b, int ntt, int& rt, int& tt) {
+    const int xcd = b & 7, kx = b >> 3;
+    rt = 8 * (kx / ntt) + xcd;
+    tt = kx % ntt;
+}
+
+// GEMM epilogue: lane (c, q) of wave (wr, wt) holds, in acc[rb][tb], rows
+// n0 + 64 wr + 16 rb + 4q .. + 3 of token m0 + 64 wt + 16 tb + c
+template <int EPI>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const f4 (&acc)[4][4], int m0, int n0, int wr, int wt,
+                                              int c, int q) {
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+        const int m = m0 + 64 * wt + 16 * tb + c;
+        if (m >= a.M) continue;
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+            const int n = n0 + 64 * wr + 16 * rb + 4 * q;
+            const f4 v = acc[rb][tb];
+            if (EPI == EPI_SWIGLU) {
+                // interleaved gate/up rows: (n, n + 1) and (n + 2, n + 3)
+#pragma unroll
+                for (int rr = 0; rr < 4; rr += 2)
+                    if (n + rr + 1 < a.N)
+                        a.hout[(int64_t)m * a.ldo + ((n + rr) >> 1)] = (_Float16)(v[rr] * sigmoid_rcp(v[rr]) * v[rr + 1]);
+            } else {
+                float* y = a.y + (int64_t)m * a.ldy + n;
+                if (n + 3 < a.N && (a.ldy & 3) == 0) {
+                    f4* y4 = (f4*)y;
+                    *y4 = EPI == EPI_RESID ? *y4 + v : v;
+                } else {
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr)
+                        if (n + rr < a.N) y[rr] = EPI == EPI_RESID ? y[rr] + v[rr] : v[rr];
+                }
+            }
+        }
+    }
+}
+
 template <int EPI>
 __global__ __launch_bounds__(256, 2) void k_gemm_w4(GemmArgs a) {
     __shared__ __align__(16) _Float16 xs[2][128][kGXP];
@@ -78,13 +125,21 @@ __global__ __launch_bounds__(256, 2) void k_gemm_w4(GemmArgs a) {
     const int wr = wave & 1, wt = wave >> 1;             // the wave's row and token halves
     const int G = a.K / 32, nstage = a.K / kGBK;
 
-    // tiles in XCD order: consecutive workgroups go to the eight XCDs in turn,
-    // so the token tiles of one row tile are given to one XCD back to back and
-    // its weights stay in that XCD's L2 (measured faster than giving each XCD
-    // one token tile and streaming the weights past it)
+    // tiles in XCD order (gemm_tile).  Units past a.nfull are the splits of
+    // the last tiles: split sp of tile a.nfull + x + 8 j (x < 8) is unit
+    // a.nfull + x + 8 (j S + sp), so that the S splits of a tile run on its
+    // XCD; split sp takes the stages [sp nstage / S, (sp + 1) nstage / S).
     const int ntt = (a.M + 127) / 128, nrt = (a.N + 127) / 128;
-    const int b = blockIdx.x, xcd = b & 7, kx = b >> 3;
-    const int rt = 8 * (kx / ntt) + xcd, tt = kx % ntt;
+    int b = blockIdx.x, split = -1, st0 = 0, st1 = nstage;
+    if (b >= a.nfull) {
+        const int S = a.nsplit, j = b - a.nfull, grp = j >> 3;
+        split = grp % S;
+        b = a.nfull + (j & 7) + 8 * (grp / S);
+        st0 = split * nstage / S;
+        st1 = (split + 1) * nstage / S;
+    }
+    int rt, tt;
+    gemm_tile(b, ntt, rt, tt);
     if (rt >= nrt) return;
     const int n0 = rt * 128, m0 = tt * 128;
 
@@ -138,34 +193,52 @@ __global__ __launch_bounds__(256, 2) void k_gemm_w4(GemmArgs a) {
     const h2 off_hi = {(_Float16)-72.0f, (_Float16)-72.0f};
     const f4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
+    // the fp16 exponent bits of the code slots, in a register: (w & mask) | it
+    // is then one v_and_or_b32 (with both as literals it takes two)
+    uint32_t k6400;
+    asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(k6400));
+
+    // Eight (group, row block) steps per stage, software-pipelined: step t's
+    // four products are issued before step t - 1's results take their
+    // scales, so the FMAs wait on products issued a step earlier instead of
+    // the ones just issued.
     auto compute = [&](int buf) {
+        h8 bv[2][4];
 #pragma unroll
-        for (int g = 0; g < 2; ++g) {
-            h8 bv[4];
+        for (int g = 0; g < 2; ++g)
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb)
-                bv[tb] = *(const h8*)&xs[buf][64 * wt + 16 * tb + c][32 * g + 8 * q];
+                bv[g][tb] = *(const h8*)&xs[buf][64 * wt + 16 * tb + c][32 * g + 8 * q];
+        f4 d[2][4];
+        uint2 sv[2];
 #pragma unroll
-            for (int rb = 0; rb < 4; ++rb) {
-                const int r = 64 * wr + 16 * rb;
+        for (int t = 0; t <= 8; ++t) {
+            if (t < 8) {
+                const int g = t >> 2, r = 64 * wr + 16 * (t & 3);
                 // exact codes: lo slots 1024 + n - 1032, hi slots (1024 + 16 n) / 16 - 72
                 const uint32_t w = cs[buf][r + c][(4 * g + q) ^ cswz(c)], w8 = w >> 8;
-                const h2 p0 = as_h2((w & 0x000F000Fu) | 0x64006400u) + off_lo;
-                const h2 p1 = __builtin_elementwise_fma(as_h2((w & 0x00F000F0u) | 0x64006400u), sixteenth, off_hi);
-                const h2 p2 = as_h2((w8 & 0x000F000Fu) | 0x64006400u) + off_lo;
-                const h2 p3 = __builtin_elementwise_fma(as_h2((w8 & 0x00F000F0u) | 0x64006400u), sixteenth, off_hi);
+                const h2 p0 = as_h2((w & 0x000F000Fu) | k6400) + off_lo;
+                const h2 p1 = __builtin_elementwise_fma(as_h2((w & 0x00F000F0u) | k6400), sixteenth, off_hi);
+                const h2 p2 = as_h2((w8 & 0x000F000Fu) | k6400) + off_lo;
+                const h2 p3 = __builtin_elementwise_fma(as_h2((w8 & 0x00F000F0u) | k6400), sixteenth, off_hi);
                 const h8 av = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
                 // fp16 scales of the four rows this lane's results belong to
                 // (rows r + 4q .. r + 4q + 3), applied in fp32 after the product
-                const uint2 sv = *(const uint2*)&ss[buf][g][r + 4 * q];
-                const float s4[4] = {(float)as_h2(sv.x)[0], (float)as_h2(sv.x)[1], (float)as_h2(sv.y)[0],
-                                     (float)as_h2(sv.y)[1]};
+                sv[t & 1] = *(const uint2*)&ss[buf][g][r + 4 * q];
 #pragma unroll
-                for (int tb = 0; tb < 4; ++tb) {
-                    const f4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv[tb], zero4, 0, 0, 0);
+                for (int tb = 0; tb < 4; ++tb)
+                    d[t & 1][tb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv[g][tb], zero4, 0, 0, 0);
+            }
+            if (t > 0) {
+                const int u = t - 1, rb = u & 3;
+                const uint2 s2 = sv[u & 1];
+                const float s4[4] = {(float)as_h2(s2.x)[0], (float)as_h2(s2.x)[1], (float)as_h2(s2.y)[0],
+                                     (float)as_h2(s2.y)[1]};
 #pragma unroll
-                    for (int rr = 0; rr < 4; ++rr) acc[rb][tb][rr] = __builtin_fmaf(s4[rr], d[rr], acc[rb][tb][rr]);
-                }
+                for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr)
+                        acc[rb][tb][rr] = __builtin_fmaf(s4[rr], d[u & 1][tb][rr], acc[rb][tb][rr]);
             }
         }
     };
@@ -175,52 +248,60 @@ __global__ __launch_bounds__(256, 2) void k_gemm_w4(GemmArgs a) {
     // buffer 1 holds stage s + 1 and sa stage s + 2.  Loads past the last
     // stage re-read it (the same straight-line loads every time, so the wait
     // counts stay exact); only the products of a missing odd stage are skipped.
-    auto sidx = [&](int t) { return t < nstage ? t : nstage - 1; };
-    AW4_GLOAD(xa0, xa1, xa2, xa3, ca, sca, 0)
+    const int nst = st1 - st0;
+    auto sidx = [&](int t) { return st0 + (t < nst ? t : nst - 1); };
+    AW4_GLOAD(xa0, xa1, xa2, xa3, ca, sca, st0)
     AW4_GLOAD(xb0, xb1, xb2, xb3, cb, scb, sidx(1))
     AW4_LSTORE(xa0, xa1, xa2, xa3, ca, sca, 0)
     __syncthreads();
-    for (int s = 0; s < nstage; s += 2) {
+    for (int s = 0; s < nst; s += 2) {
         AW4_GLOAD(xa0, xa1, xa2, xa3, ca, sca, sidx(s + 2))
         compute(0);
         AW4_LSTORE(xb0, xb1, xb2, xb3, cb, scb, 1)
         __syncthreads();
         AW4_GLOAD(xb0, xb1, xb2, xb3, cb, scb, sidx(s + 3))
-        if (s + 1 < nstage) compute(1);
+        if (s + 1 < nst) compute(1);
         AW4_LSTORE(xa0, xa1, xa2, xa3, ca, sca, 0)
         __syncthreads();
     }
 #undef AW4_GLOAD
 #undef AW4_LSTORE
 
-    // epilogue: lane (c, q) of block (rb, tb) holds rows 4q..4q+3 of token c
+    if (split >= 0) {
+        // this split's partial tile, in the lanes' own order; k_gemm_combine
+        // adds the splits and runs the epilogue after the launch
+        f4* part = (f4*)a.part + ((int64_t)(b - a.nfull) * a.nsplit + split) * 4096 + wave * 1024 + lane;
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-        const int m = m0 + 64 * wt + 16 * tb + c;
-        if (m >= a.M) continue;
+        for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-            const int n = n0 + 64 * wr + 16 * rb + 4 * q;
-            const f4 v = acc[rb][tb];
-            if (EPI == EPI_SWIGLU) {
-                // interleaved gate/up rows: (n, n + 1) and (n + 2, n + 3)
-#pragma unroll
-                for (int rr = 0; rr < 4; rr += 2)
-                    if (n + rr + 1 < a.N)
-                        a.hout[(int64_t)m * a.ldo + ((n + rr) >> 1)] = (_Float16)(v[rr] * sigmoid_rcp(v[rr]) * v[rr + 1]);
-            } else {
-                float* y = a.y + (int64_t)m * a.ldy + n;
-                if (n + 3 < a.N && (a.ldy & 3) == 0) {
-                    f4* y4 = (f4*)y;
-                    *y4 = EPI == EPI_RESID ? *y4 + v : v;
-                } else {
-#pragma unroll
-                    for (int rr = 0; rr < 4; ++rr)
-                        if (n + rr < a.N) y[rr] = EPI == EPI_RESID ? y[rr] + v[rr] : v[rr];
-                }
-            }
-        }
+            for (int tb = 0; tb < 4; ++tb) part[64 * (4 * rb + tb)] = acc[rb][tb];
+        return;
     }
+    gemm_epilogue<EPI>(a, acc, m0, n0, wr, wt, c, q);
+}
+
+// The split tiles of a k_gemm_w4 launch: one workgroup per tile, the same
+// lane layout; the splits' partials added in split order, then the epilogue.
+template <int EPI>
+__global__ __launch_bounds__(256) void k_gemm_combine(GemmArgs a) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int c = lane & 15, q = lane >> 4, wr = wave & 1, wt = wave >> 1;
+    const int b = a.nfull + blockIdx.x, ntt = (a.M + 127) / 128, nrt = (a.N + 127) / 128;
+    int rt, tt;
+    gemm_tile(b, ntt, rt, tt);
+    if (rt >= nrt) return;
+    const f4* part = (const f4*)a.part + (int64_t)blockIdx.x * a.nsplit * 4096 + wave * 1024 + lane;
+    f4 acc[4][4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) acc[rb][tb] = part[64 * (4 * rb + tb)];
+    for (int sp = 1; sp < a.nsplit; ++sp)
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) acc[rb][tb] += part[sp * 4096 + 64 * (4 * rb + tb)];
+    gemm_epilogue<EPI>(a, acc, tt * 128, rt * 128, wr, wt, c, q);
 }
 
 // ------------------------------------------------------------------ row kernels
@@ -354,14 +435,44 @@ __global__ __launch_bounds__(256) void k_gated_rows(GdnPrefillArgs a, const floa
 
 }  // namespace
 
-hipError_t launch_gemm_w4(int epi, const GemmArgs& a, hipStream_t s) {
-    if (a.M < 1 || a.N < 1 || a.K % kGBK || a.K < kGBK) return hipErrorInvalidValue;
+// Tiles in rounds of the resident workgroups (P); when the last round is at
+// most half full, its tiles are split S = P / tail ways along K (at most 8,
+// at least one stage per split, at most a.part_slots partial tiles), so that
+// it takes one round of 1/S-length units instead of a whole tile time on a
+// partly idle chip (FFN gate/up at 1024 tokens: 2176 tiles on 512 slots,
+// 4.25 rounds of work in 5); k_gemm_combine then adds the splits.
+hipError_t launch_gemm_w4(int epi, const GemmArgs& a0, hipStream_t s) {
+    if (a0.M < 1 || a0.N < 1 || a0.K % kGBK || a0.K < kGBK) return hipErrorInvalidValue;
+    const void* fn = epi == EPI_STORE ? (const void*)k_gemm_w4<EPI_STORE>
+                   : epi == EPI_RESID ? (const void*)k_gemm_w4<EPI_RESID>
+                   : epi == EPI_SWIGLU ? (const void*)k_gemm_w4<EPI_SWIGLU> : nullptr;
+    if (!fn) return hipErrorInvalidValue;
+    GemmArgs a = a0;
     const int ntt = (a.M + 127) / 128, nrt = (a.N + 127) / 128;
-    const dim3 grid(8 * ntt * ((nrt + 7) / 8)), block(256);
+    const int T = 8 * ntt * ((nrt + 7) / 8), nstage = a.K / kGBK;
+    a.nfull = T;
+    a.nsplit = 1;
+    const int P = a.part ? resident_blocks(fn, 0) : 0;
+    if (P >= 8 && P % 8 == 0 && T > P) {
+        const int tail = T % P;
+        int S = tail ? P / tail : 0;
+        S = std::min(S, std::min(8, nstage));
+        if (tail && (int64_t)tail * S > a.part_slots) S = a.part_slots / tail;
+        if (S >= 2) {
+            a.nfull = T - tail;
+            a.nsplit = S;
+        }
+    }
+    const dim3 grid(a.nfull + (T - a.nfull) * a.nsplit), block(256);
     if (epi == EPI_STORE) hipLaunchKernelGGL(k_gemm_w4<EPI_STORE>, grid, block, 0, s, a);
     else if (epi == EPI_RESID) hipLaunchKernelGGL(k_gemm_w4<EPI_RESID>, grid, block, 0, s, a);
-    else if (epi == EPI_SWIGLU) hipLaunchKernelGGL(k_gemm_w4<EPI_SWIGLU>, grid, block, 0, s, a);
-    else return hipErrorInvalidValue;
+    else hipLaunchKernelGGL(k_gemm_w4<EPI_SWIGLU>, grid, block, 0, s, a);
+    if (a.nsplit > 1) {
+        const dim3 cg(T - a.nfull);
+        if (epi == EPI_STORE) hipLaunchKernelGGL(k_gemm_combine<EPI_STORE>, cg, block, 0, s, a);
+        else if (epi == EPI_RESID) hipLaunchKernelGGL(k_gemm_combine<EPI_RESID>, cg, block, 0, s, a);
+        else hipLaunchKernelGGL(k_gemm_combine<EPI_SWIGLU>, cg, block, 0, s, a);
+    }
     return hipGetLastError();
 }
 

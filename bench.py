@@ -512,7 +512,7 @@ def main():
     # and its dominant kernel, the gate/up W4 GEMM over one chunk, on MFMA
     prefill = None
     if args.prompt == "decode":
-        pu, pf = m.time_phase(A.PHASE_PREFILL_GATE_UP, max(4, args.phase_reps // 16))
+        pu, pf = m.time_phase(A.PHASE_PREFILL_GATE_UP, max(16, args.phase_reps // 2))
         prefill = {"tokens": args.ctx - 1, "s": round(t_prompt, 3), "tok/s": round((args.ctx - 1) / t_prompt, 1),
                    "chunk": 1024, "note": "also feeds the draft head one entry per prompt position",
                    "gemm_roofline": {"kernel": "k_gemm_w4 (FFN gate/up + SwiGLU), M 1024 tokens, N 34816, K 5120",

@@ -91,6 +91,17 @@ def test_prefill_toy_matches_oracle(aw4, chunk):
     _prefill_vs_oracle(aw4, W.TOY, 0, 0.0, 300, chunk, 32)
 
 
+def test_prefill_split_gemm_tail(aw4):
+    """A toy stack with a 36,864-wide FFN: at 128 tokens its gate/up GEMM has
+    576 tiles of 128 rows x 128 tokens, one full round of 512 resident
+    workgroups and 64 left over, which run split eight ways along K (each
+    split a partial tile, the last to arrive adds them in split order).  Both
+    chunks (128 tokens, then 2) take that path; the result must match the
+    oracle's token-by-token decode as every other prefill does."""
+    _say("case: toy stack with FFN 36864 (split-K tail of the gate/up GEMM), 130 tokens, chunk 128")
+    _prefill_vs_oracle(aw4, W.with_(W.TOY, ffn=36864), 5, 0.1, 130, 128, 8)
+
+
 def test_prefill_tiny_grouped_heads(aw4):
     _say("case: tiny stack (grouped heads, jittered norms) prefill, 40 tokens, chunk 16")
     _prefill_vs_oracle(aw4, TINY, 12, 0.2, 40, 16, 8)
