@@ -1276,19 +1276,22 @@ __global__ __launch_bounds__(256, 2) void k_gemv_mfma(GemvMultiArgs a) {
 // operand of v_mfma_f32_16x16x16_f16 j (exact codes as fp16); the A operand
 // is input c at the same four positions, from LDS.  The product D = X W^T
 // gives lane (c, q) the logits of inputs 4 q .. 4 q + 3 at row c, so a lane
-// needs only its own row's fp16 group scales.  Stages of two spans (four
-// groups) run four ahead in a ring of five register sets, unrolled by five so
-// that no copy moves a set.  Each load instruction takes 64 bytes of each of
-// 16 rows; plain loads serve that pattern faster than non-temporal ones (head
-// 394 -> 297 us, M = 4 FFN gate/up 32.3 -> 27.9 us, with the same HBM bytes
-// fetched), in this kernel and in k_gemv_mfma.
+// needs only its own row's fp16 group scales.  Stages of SPS spans (2 SPS
+// groups) run RING - 1 ahead in a ring of RING register sets, unrolled by RING
+// so that no copy moves a set.  Each load instruction takes 64 bytes of each
+// of 16 rows; plain loads serve that pattern faster than non-temporal ones
+// (head 394 -> 297 us, M = 4 FFN gate/up 32.3 -> 27.9 us, with the same HBM
+// bytes fetched), in this kernel and in k_gemv_mfma.  At the 27B width a
+// stage takes 512 bytes of each row, one stage ahead (SPS 8, RING 2): longer
+// runs per row than 128 bytes four stages ahead (SPS 2, RING 5), 299 -> 257
+// us for the same bytes in flight (SPS 4: 272 us, SPS 16 or 20: 272, 300 us;
+// three waves per SIMD at SPS 8: 259 us).
 // Results: logits [M][V] and per-workgroup best value and index per vector
 // (lowest index on ties), a.nparts partial slots per vector as k_head_multi
 // (slots past the grid hold -inf).
-template <int H>
+template <int H, int SPS, int RING>
 __global__ __launch_bounds__(256, 2) void k_head_mfma(HeadMultiArgs a) {
-    constexpr int MAXM = 4, GR = H / 32, NSP = H / 64, SPS = 2, NST = NSP / SPS;   // spans per stage, stages per row block
-    constexpr int RING = 5;
+    constexpr int MAXM = 4, GR = H / 32, NSP = H / 64, NST = NSP / SPS;   // spans per stage, stages per row block
     static_assert(NSP % SPS == 0, "row length");
     typedef float f4 __attribute__((ext_vector_type(4)));
     typedef _Float16 h4 __attribute__((ext_vector_type(4)));
@@ -1318,7 +1321,7 @@ __global__ __launch_bounds__(256, 2) void k_head_mfma(HeadMultiArgs a) {
     int besti[4] = {0x7fffffff, 0x7fffffff, 0x7fffffff, 0x7fffffff};
     struct Stage {
         u32x4 w[SPS];       // row c: span bytes 16 q .. 16 q + 15 of each span
-        uint2 s;            // row c: fp16 scales of the stage's 4 groups
+        uint32_t s[SPS];    // row c: fp16 scales of the stage's 2 SPS groups
     };
     for (int rb = blockIdx.x * 4 + wave; rb < nrb; rb += gridDim.x * 4) {
         const int r0 = rb * 16;
@@ -1328,7 +1331,9 @@ __global__ __launch_bounds__(256, 2) void k_head_mfma(HeadMultiArgs a) {
         auto load = [&](Stage& st, int sidx) {
 #pragma unroll
             for (int h = 0; h < SPS; ++h) st.w[h] = arow[4 * (sidx * SPS + h)];
-            st.s = *(const uint2*)(srow + 4 * sidx);
+            const uint32_t* sp = (const uint32_t*)(srow + 2 * SPS * sidx);
+#pragma unroll
+            for (int h = 0; h < SPS; ++h) st.s[h] = sp[h];
         };
         float acc[4] = {0.f, 0.f, 0.f, 0.f};
         const f4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -1355,7 +1360,7 @@ __global__ __launch_bounds__(256, 2) void k_head_mfma(HeadMultiArgs a) {
                                                                      (j & 1) ? d[j >> 1] : zero, 0, 0, 0);
                 }
                 // groups 2 h and 2 h + 1 of the stage: this row's scales
-                const h2 sc = as_h2(h == 0 ? st.s.x : st.s.y);
+                const h2 sc = as_h2(st.s[h]);
 #pragma unroll
                 for (int gg = 0; gg < 2; ++gg)
 #pragma unroll
@@ -1781,7 +1786,7 @@ hipError_t launch_head_multi(const HeadMultiArgs& a, hipStream_t s) {
         // the matrix-core form (27B and toy widths); one partial per workgroup
         // and vector as below, head_blocks(V) workgroups
         const size_t shm = 64 + (size_t)2 * a.M * (a.H + kMfmaPad);
-        const void* fn = a.H == 5120 ? (const void*)k_head_mfma<5120> : (const void*)k_head_mfma<512>;
+        const void* fn = a.H == 5120 ? (const void*)k_head_mfma<5120, 8, 2> : (const void*)k_head_mfma<512, 2, 5>;
         if (shm > 65536) {
             hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
             if (e != hipSuccess) return e;
@@ -1792,8 +1797,8 @@ hipError_t launch_head_multi(const HeadMultiArgs& a, hipStream_t s) {
         b.nparts = head_blocks(a.V);
         const int res = resident_blocks(fn, shm);
         const dim3 grid(res > 0 && res < b.nparts ? res : b.nparts);
-        if (a.H == 5120) hipLaunchKernelGGL(k_head_mfma<5120>, grid, dim3(256), shm, s, b);
-        else hipLaunchKernelGGL(k_head_mfma<512>, grid, dim3(256), shm, s, b);
+        if (a.H == 5120) hipLaunchKernelGGL((k_head_mfma<5120, 8, 2>), grid, dim3(256), shm, s, b);
+        else hipLaunchKernelGGL((k_head_mfma<512, 2, 5>), grid, dim3(256), shm, s, b);
         return hipGetLastError();
     }
     const size_t shm = 64 + (size_t)a.H * 2 * (size_t)a.M;
