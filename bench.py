@@ -31,7 +31,7 @@ HBM_PEAK_GBS = 8000.0
 # HBM bytes per launch of the gate/up GEMV from the FETCH_SIZE / WRITE_SIZE
 # counter runs recorded in profiles/hbm_traffic_8k_decode.md, valid only for
 # the kernel source whose sha256 prefix is recorded with them.
-GATEUP_TRAFFIC = {"k_gemv_sha256": "49892bb6464cb10b", "bytes": 100812263}
+GATEUP_TRAFFIC = {"k_gemv_sha256": "c5ad4ccaf7ce5010", "bytes": 100812527}
 
 
 def gateup_traffic():
