@@ -360,10 +360,22 @@ __global__ __launch_bounds__(256) void k_gdn_seq(GdnPrefillArgs a) {
     constexpr int EPT = 8;
     constexpr int TPR = D / EPT;
     constexpr int ROWS = 256 / TPR;
+    // the chunk's inputs are staged in LDS TB tokens at a time (double
+    // buffered, the next block's loads in flight while the current one runs):
+    // with the inputs read from global memory one token ahead, every step
+    // waited for a cache round trip
+    constexpr int TB = 32;
+    constexpr int KQ4 = TB * 2 * D / 4 / 256;   // float4 of k and q per thread per block
+    constexpr int NVT = TB * ROWS / 256;         // v values per thread per block
+    static_assert(KQ4 * 256 * 4 == TB * 2 * D && NVT * 256 == TB * ROWS, "staging shape");
+    __shared__ __align__(16) float kq_s[2][TB][2][D];   // [buf][token][k, q][dim]
+    __shared__ float v_s[2][TB][ROWS];
+    __shared__ float ab_s[2][TB][2];
+    const int tid = threadIdx.x;
     const int h = blockIdx.y;
     const int j = h / (a.nv / a.nqk);
-    const int r = blockIdx.x * ROWS + threadIdx.x / TPR;
-    const int c0 = (threadIdx.x % TPR) * EPT;
+    const int row0 = blockIdx.x * ROWS, rl = tid / TPR, r = row0 + rl;
+    const int c0 = (tid % TPR) * EPT;
     float* Srow = a.S + ((int64_t)h * D + r) * D + c0;
     float s[8];
     {
@@ -371,45 +383,70 @@ __global__ __launch_bounds__(256) void k_gdn_seq(GdnPrefillArgs a) {
         s[0] = s0.x; s[1] = s0.y; s[2] = s0.z; s[3] = s0.w;
         s[4] = s1.x; s[5] = s1.y; s[6] = s1.z; s[7] = s1.w;
     }
-    struct In {
-        float4 k0, k1, q0, q1;
-        float v, al, be;
-    };
-    auto load = [&](In& in, int t) {
-        const float* kp = a.kn + ((int64_t)t * a.nqk + j) * D + c0;
-        const float* qp = a.qn + ((int64_t)t * a.nqk + j) * D + c0;
-        in.k0 = *(const float4*)kp;
-        in.k1 = *(const float4*)(kp + 4);
-        in.q0 = *(const float4*)qp;
-        in.q1 = *(const float4*)(qp + 4);
-        in.v = a.proj[(int64_t)t * a.sproj + 2LL * a.nqk * D + (int64_t)h * D + r];
-        const float2 g = *(const float2*)(a.ab + ((int64_t)t * a.nv + h) * 2);
-        in.al = g.x;
-        in.be = g.y;
-    };
-    In cur, nxt;
-    load(cur, 0);
-    for (int t = 0; t < a.T; ++t) {
-        if (t + 1 < a.T) load(nxt, t + 1);
-        const float kk[8] = {cur.k0.x, cur.k0.y, cur.k0.z, cur.k0.w, cur.k1.x, cur.k1.y, cur.k1.z, cur.k1.w};
-        const float qq[8] = {cur.q0.x, cur.q0.y, cur.q0.z, cur.q0.w, cur.q1.x, cur.q1.y, cur.q1.z, cur.q1.w};
-        float u = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) u += s[e] * kk[e];
-#pragma unroll
-        for (int o = TPR / 2; o >= 1; o >>= 1) u += __shfl_xor(u, o, 64);
-        const float delta = cur.be * (cur.v - cur.al * u);
-        float oo = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            s[e] = cur.al * s[e] + delta * kk[e];
-            oo += s[e] * qq[e];
-        }
-#pragma unroll
-        for (int o = TPR / 2; o >= 1; o >>= 1) oo += __shfl_xor(oo, o, 64);
-        if ((threadIdx.x % TPR) == 0) a.o[(int64_t)t * a.so + (int64_t)h * D + r] = oo;
-        cur = nxt;
+    // staged values in named registers (arrays captured by reference in a
+    // lambda were kept on the stack)
+    f4 rk[KQ4];
+    float rv[NVT], rab = 0.f;
+#define AW4_GDN_STAGE(BLK)                                                                                 \
+    {                                                                                                      \
+        /* tokens past the chunk re-read its last token (never used) */                                   \
+        _Pragma("unroll") for (int i = 0; i < KQ4; ++i) {                                                  \
+            const int idx = tid + 256 * i, tt = idx / (D / 2), rem = idx % (D / 2);                        \
+            const int t = min((BLK) * TB + tt, a.T - 1);                                                   \
+            const float* src = (rem < D / 4 ? a.kn : a.qn) + ((int64_t)t * a.nqk + j) * D + 4 * (rem % (D / 4)); \
+            rk[i] = *(const f4*)src;                                                                       \
+        }                                                                                                  \
+        _Pragma("unroll") for (int i = 0; i < NVT; ++i) {                                                  \
+            const int idx = tid + 256 * i, tt = idx / ROWS;                                                \
+            const int t = min((BLK) * TB + tt, a.T - 1);                                                   \
+            rv[i] = a.proj[(int64_t)t * a.sproj + 2LL * a.nqk * D + (int64_t)h * D + row0 + idx % ROWS];  \
+        }                                                                                                  \
+        if (tid < 2 * TB) {                                                                                \
+            const int t = min((BLK) * TB + tid / 2, a.T - 1);                                              \
+            rab = a.ab[((int64_t)t * a.nv + h) * 2 + (tid & 1)];                                           \
+        }                                                                                                  \
     }
+#define AW4_GDN_PUT(BUF)                                                                                   \
+    {                                                                                                      \
+        _Pragma("unroll") for (int i = 0; i < KQ4; ++i) ((f4*)&kq_s[BUF][0][0][0])[tid + 256 * i] = rk[i]; \
+        _Pragma("unroll") for (int i = 0; i < NVT; ++i)(&v_s[BUF][0][0])[tid + 256 * i] = rv[i];          \
+        if (tid < 2 * TB) (&ab_s[BUF][0][0])[tid] = rab;                                                   \
+    }
+    const int nblk = (a.T + TB - 1) / TB;
+    AW4_GDN_STAGE(0)
+    AW4_GDN_PUT(0)
+    __syncthreads();
+    for (int blk = 0; blk < nblk; ++blk) {
+        const int buf = blk & 1;
+        if (blk + 1 < nblk) AW4_GDN_STAGE(blk + 1)
+        const int tn = min(TB, a.T - blk * TB);
+        for (int tt = 0; tt < tn; ++tt) {
+            const float4 k0 = *(const float4*)&kq_s[buf][tt][0][c0], k1 = *(const float4*)&kq_s[buf][tt][0][c0 + 4];
+            const float4 q0 = *(const float4*)&kq_s[buf][tt][1][c0], q1 = *(const float4*)&kq_s[buf][tt][1][c0 + 4];
+            const float v = v_s[buf][tt][rl], al = ab_s[buf][tt][0], be = ab_s[buf][tt][1];
+            const float kk[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+            const float qq[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+            float u = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) u += s[e] * kk[e];
+#pragma unroll
+            for (int o = TPR / 2; o >= 1; o >>= 1) u += __shfl_xor(u, o, 64);
+            const float delta = be * (v - al * u);
+            float oo = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                s[e] = al * s[e] + delta * kk[e];
+                oo += s[e] * qq[e];
+            }
+#pragma unroll
+            for (int o = TPR / 2; o >= 1; o >>= 1) oo += __shfl_xor(oo, o, 64);
+            if ((tid % TPR) == 0) a.o[(int64_t)(blk * TB + tt) * a.so + (int64_t)h * D + r] = oo;
+        }
+        if (blk + 1 < nblk) AW4_GDN_PUT(buf ^ 1)
+        __syncthreads();
+    }
+#undef AW4_GDN_STAGE
+#undef AW4_GDN_PUT
     *(float4*)Srow = make_float4(s[0], s[1], s[2], s[3]);
     *(float4*)(Srow + 4) = make_float4(s[4], s[5], s[6], s[7]);
 }
