@@ -954,10 +954,6 @@ __global__ __launch_bounds__(256, 2) void k_gemv_multi(GemvMultiArgs a) {
 // split its groups, adding their partial sums through LDS.  Loads run two
 // stages of kStage groups ahead in a ring of three register sets.
 constexpr int kStage = 8;
-// register ring of the multi-input kernel (stages in flight + 1), and the units
-// per workgroup whose results wait in LDS while the ring runs on across them
-constexpr int kMfmaRing = 5, kMfmaDefer = 4;
-__host__ __device__ constexpr bool mfma_carried(int nst) { return nst % kMfmaRing == 0; }
 
 // The M input vectors as fp16 [M][K] in LDS for a compile-time K: every load
 // of every input is issued before any is used (one memory round trip), and the
@@ -1153,71 +1149,86 @@ __global__ __launch_bounds__(256, 2) void k_gemv_mfma(GemvMultiArgs a) {
     // persistent: workgroup units (NB row blocks each) in turn, so that a
     // launch of one round of resident workgroups covers every row block
     const int nunits = (nrb + NB - 1) / NB;
-    // codes: lane (c, q) loads row c's group g + q whole (16 bytes) and four
-    // lane-row swaps hand each lane its dword of every group (see compute).
-    // Rows past the matrix, and units past the last, re-read its last row
-    // (valid memory; the sums are never stored).
-    auto rows_of = [&](int unit, const u32x4*& arow, const uint16_t*& srow) {
-        const int row = min((unit * NB + wave / KS) * 16 + c, rows - 1);
-        arow = (const u32x4*)(a.codes + (int64_t)row * G * 4) + q;
-        srow = a.scales + (int64_t)row * G;
-    };
-    auto load = [&](Stage& st, const u32x4* arow, const uint16_t* srow, int sidx) {
-        const int g0 = gbeg + sidx * U;
+    for (int unit = blockIdx.x; unit < nunits; unit += gridDim.x) {
+        const int blk = unit * NB + wave / KS;
+        const bool live = blk < nrb;                       // uniform over the KS waves of a block
+        const int r0 = blk * 16;
+        const int row = min(r0 + c, rows - 1);
+        // codes: lane (c, q) loads row c's group g + q whole (16 bytes) and four
+        // lane-row swaps hand each lane its dword of every group (see compute)
+        const u32x4* arow = (const u32x4*)(a.codes + (int64_t)row * G * 4) + q;
+        const uint16_t* srow = a.scales + (int64_t)row * G;
+        auto load = [&](Stage& st, int sidx) {
+            const int g0 = gbeg + sidx * U;
 #pragma unroll
-        for (int h = 0; h < U / 4; ++h) st.w[h] = arow[g0 + 4 * h];   // plain loads: see the head below
-        st.s = *(const uint4*)(srow + g0);
-    };
-    auto compute = [&](const Stage& st, int sidx, float* acc) {
-        const int g0 = gbeg + sidx * U;
-        // the stage's input fragments first (LDS latency once per stage), then
-        // the products back to back, then the scales
-        uint4 xb[U];
+            for (int h = 0; h < U / 4; ++h) st.w[h] = arow[g0 + 4 * h];   // plain loads: see the head below
+            st.s = *(const uint4*)(srow + g0);
+        };
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        auto compute = [&](const Stage& st, int sidx) {
+            const int g0 = gbeg + sidx * U;
+            // the stage's input fragments first (LDS latency once per stage), then
+            // the products back to back, then the scales
+            uint4 xb[U];
 #pragma unroll
-        for (int j = 0; j < U; ++j) xb[j] = *(const uint4*)(xrow + 32 * (g0 + j));
-        asm volatile("" ::: "memory");   // issued together, before the products
-        // 4 x 4 transpose across the lane rows (16 lanes each): lane row t
-        // holds dwords 0..3 of group g0 + 4h + t; after two 32-lane and two
-        // 16-lane swaps, word j of lane row q is dword q of group g0 + 4h + j
-        uint32_t wd[U];
+            for (int j = 0; j < U; ++j) xb[j] = *(const uint4*)(xrow + 32 * (g0 + j));
+            asm volatile("" ::: "memory");   // issued together, before the products
+            // 4 x 4 transpose across the lane rows (16 lanes each): lane row t
+            // holds dwords 0..3 of group g0 + 4h + t; after two 32-lane and two
+            // 16-lane swaps, word j of lane row q is dword q of group g0 + 4h + j
+            uint32_t wd[U];
 #pragma unroll
-        for (int h = 0; h < U / 4; ++h) {
-            const auto ab = __builtin_amdgcn_permlane32_swap(st.w[h][0], st.w[h][2], false, false);
-            const auto cd = __builtin_amdgcn_permlane32_swap(st.w[h][1], st.w[h][3], false, false);
-            const auto t01 = __builtin_amdgcn_permlane16_swap(ab[0], cd[0], false, false);
-            const auto t23 = __builtin_amdgcn_permlane16_swap(ab[1], cd[1], false, false);
-            wd[4 * h] = t01[0];
-            wd[4 * h + 1] = t01[1];
-            wd[4 * h + 2] = t23[0];
-            wd[4 * h + 3] = t23[1];
+            for (int h = 0; h < U / 4; ++h) {
+                const auto ab = __builtin_amdgcn_permlane32_swap(st.w[h][0], st.w[h][2], false, false);
+                const auto cd = __builtin_amdgcn_permlane32_swap(st.w[h][1], st.w[h][3], false, false);
+                const auto t01 = __builtin_amdgcn_permlane16_swap(ab[0], cd[0], false, false);
+                const auto t23 = __builtin_amdgcn_permlane16_swap(ab[1], cd[1], false, false);
+                wd[4 * h] = t01[0];
+                wd[4 * h + 1] = t01[1];
+                wd[4 * h + 2] = t23[0];
+                wd[4 * h + 3] = t23[1];
+            }
+            f4 d[U];
+#pragma unroll
+            for (int j = 0; j < U; ++j) {
+                // exact codes: lo slots 1024 + n - 1032, hi slots (1024 + 16 n) / 16 - 72
+                const uint32_t w = wd[j], w8 = w >> 8;
+                const h2 p0 = as_h2((w & nk.lo) | nk.e) + off_lo;
+                const h2 p1 = __builtin_elementwise_fma(as_h2((w & nk.hi) | nk.e), sixteenth, off_hi);
+                const h2 p2 = as_h2((w8 & nk.lo) | nk.e) + off_lo;
+                const h2 p3 = __builtin_elementwise_fma(as_h2((w8 & nk.hi) | nk.e), sixteenth, off_hi);
+                const h8 av = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+                // D = X W^T: lane (c, q) gets inputs 4 q .. 4 q + 3 at row c
+                d[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, xb[j]), av, zero, 0, 0, 0);
+            }
+#pragma unroll
+            for (int j = 0; j < U; ++j) {
+                const uint32_t sw = (j >> 1) == 0 ? st.s.x : (j >> 1) == 1 ? st.s.y : (j >> 1) == 2 ? st.s.z : st.s.w;
+                const float sc = (float)as_h2(sw)[j & 1];
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) acc[rr] += sc * d[j][rr];
+            }
+        };
+        if (live) {
+            // RING register sets used in turn, each refilled right after use, in
+            // straight-line code (a loop header would merge the wait counts); loads
+            // past the last stage re-read it so every step issues the same ones
+            constexpr int RING = 5;
+            Stage ring[RING];
+#pragma unroll
+            for (int k = 0; k < RING - 1; ++k) load(ring[k], k < NST ? k : NST - 1);
+#pragma unroll
+            for (int sidx = 0; sidx < NST; ++sidx) {
+                load(ring[(sidx + RING - 1) % RING], sidx + RING - 1 < NST ? sidx + RING - 1 : NST - 1);
+                asm volatile("" ::: "memory");   // keep each stage's loads in their place
+                compute(ring[sidx % RING], sidx);
+            }
         }
-        f4 d[U];
-#pragma unroll
-        for (int j = 0; j < U; ++j) {
-            // exact codes: lo slots 1024 + n - 1032, hi slots (1024 + 16 n) / 16 - 72
-            const uint32_t w = wd[j], w8 = w >> 8;
-            const h2 p0 = as_h2((w & nk.lo) | nk.e) + off_lo;
-            const h2 p1 = __builtin_elementwise_fma(as_h2((w & nk.hi) | nk.e), sixteenth, off_hi);
-            const h2 p2 = as_h2((w8 & nk.lo) | nk.e) + off_lo;
-            const h2 p3 = __builtin_elementwise_fma(as_h2((w8 & nk.hi) | nk.e), sixteenth, off_hi);
-            const h8 av = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-            // D = X W^T: lane (c, q) gets inputs 4 q .. 4 q + 3 at row c
-            d[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, xb[j]), av, zero, 0, 0, 0);
-        }
-#pragma unroll
-        for (int j = 0; j < U; ++j) {
-            const uint32_t sw = (j >> 1) == 0 ? st.s.x : (j >> 1) == 1 ? st.s.y : (j >> 1) == 2 ? st.s.z : st.s.w;
-            const float sc = (float)as_h2(sw)[j & 1];
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) acc[rr] += sc * d[j][rr];
-        }
-    };
-    // the KS waves of a row block add their partial sums through LDS; the
-    // barriers wait for LDS only, so the loads in flight keep flowing
-    auto reduce = [&](float* acc) {
+        // lane (c, q): inputs 4 q + rr at row r0 + c (M <= 4: the q = 0 lanes)
+        bool out = live && q == 0;
         if (KS > 1) {
             part[wave * 64 + lane] = f4{acc[0], acc[1], acc[2], acc[3]};
-            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            __syncthreads();
             if (wave % KS == 0) {
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) acc[rr] = 0.f;
@@ -1227,114 +1238,33 @@ __global__ __launch_bounds__(256, 2) void k_gemv_mfma(GemvMultiArgs a) {
 #pragma unroll
                     for (int rr = 0; rr < 4; ++rr) acc[rr] += v[rr];
                 }
+            } else {
+                out = false;
             }
-            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // part[] is reused by the next unit
+            __syncthreads();   // part[] is reused by the next unit
         }
-    };
-    // lane (c, 0) of a block's first wave: v holds inputs 0..3 at row 16 blk + c,
-    // up the next lane's (interleaved gate/up rows: even lane c holds gate row
-    // 16 blk + c, the next lane its up row)
-    auto epilogue = [&](int blk, const f4& v, const f4& up) {
-        const int r0 = blk * 16;
-        if (blk >= nrb) return;
         if (EPI == EPI_SWIGLU) {
-            if ((c & 1) == 0 && r0 + c + 1 < rows) {
+            // interleaved gate/up rows: even lane c holds gate row r0 + c, the
+            // next lane its up row
+            float up[4];
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) up[rr] = __shfl_down(acc[rr], 1, 64);
+            if (out && (c & 1) == 0 && r0 + c + 1 < rows) {
 #pragma unroll
                 for (int m = 0; m < 4; ++m)
-                    if (m < M) a.hout[m * a.so + ((r0 + c) >> 1)] = (_Float16)(v[m] * sigmoidf_(v[m]) * up[m]);
+                    if (m < M) {
+                        const float gg = acc[m];
+                        a.hout[m * a.so + ((r0 + c) >> 1)] = (_Float16)(gg * sigmoidf_(gg) * up[m]);
+                    }
             }
-        } else if (r0 + c < rows) {
+        } else if (out && r0 + c < rows) {
 #pragma unroll
             for (int m = 0; m < 4; ++m)
                 if (m < M) {
-                    if (EPI == EPI_STORE) a.y[m * a.sy + r0 + c] = v[m];
-                    else a.y[m * a.sy + r0 + c] += v[m];
+                    if (EPI == EPI_STORE) a.y[m * a.sy + r0 + c] = acc[m];
+                    else a.y[m * a.sy + r0 + c] += acc[m];
                 }
         }
-    };
-    // lane (c, q): inputs 4 q + rr at row r0 + c (M <= 4: the q = 0 lanes)
-    const bool outw = KS == 1 || wave % KS == 0;
-    int unit = blockIdx.x;
-    if constexpr (mfma_carried(NST)) {
-        // Up to kMfmaDefer units per workgroup with the register ring carried
-        // across them: the next unit's first stages load while this one
-        // finishes.  The units are straight-line code (a loop would copy the
-        // ring's registers at its header and wait there for every load in
-        // flight), and their results wait in LDS until the last one is done:
-        // no global access but the ring's loads sits among them (a store, or
-        // the read-modify-write of a residual, would be waited for, and every
-        // load issued before it with it).
-        f4* res = part + (KS > 1 ? 4 * 64 : 0);   // [kMfmaDefer][NB][16]
-        int done = 0;
-        if (unit < nunits) {
-            const u32x4* arow;
-            const uint16_t* srow;
-            rows_of(unit, arow, srow);
-            Stage ring[kMfmaRing];
-#pragma unroll
-            for (int k = 0; k < kMfmaRing - 1; ++k) {
-                load(ring[k], arow, srow, k);
-                asm volatile("" ::: "memory");   // stage order: the first stage's scales before later codes
-            }
-#pragma unroll
-            for (int u = 0; u < kMfmaDefer; ++u) {
-                if (unit >= nunits) break;
-                const u32x4* anext;
-                const uint16_t* snext;
-                rows_of(unit + gridDim.x, anext, snext);
-                float acc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int sidx = 0; sidx < NST; ++sidx) {
-                    const int ls = sidx + kMfmaRing - 1;   // ring slot ls % kMfmaRing: NST is a multiple of the ring
-                    if (ls < NST) load(ring[ls % kMfmaRing], arow, srow, ls);
-                    else load(ring[ls % kMfmaRing], anext, snext, ls - NST);
-                    asm volatile("" ::: "memory");   // keep each stage's loads in their place
-                    compute(ring[sidx % kMfmaRing], sidx, acc);
-                }
-                arow = anext;
-                srow = snext;
-                reduce(acc);
-                if (outw && q == 0) res[(u * NB + wave / KS) * 16 + c] = f4{acc[0], acc[1], acc[2], acc[3]};
-                unit += gridDim.x;
-                done = u + 1;
-            }
-        }
-        // each writing wave reads back its own entries
-        if (outw && q == 0)
-            for (int i = 0; i < done; ++i) {
-                const f4* r = res + (i * NB + wave / KS) * 16;
-                epilogue((blockIdx.x + i * gridDim.x) * NB + wave / KS, r[c], r[c < 15 ? c + 1 : c]);
-            }
-    }
-    // units the carried ring does not cover (other stage counts, or more units
-    // per workgroup than it holds, which the launch avoids): the ring restarts
-    // at each unit
-    for (; unit < nunits; unit += gridDim.x) {
-        float acc[4] = {0.f, 0.f, 0.f, 0.f};
-        if (unit * NB + wave / KS < nrb) {   // uniform over the KS waves of a block
-            const u32x4* arow;
-            const uint16_t* srow;
-            rows_of(unit, arow, srow);
-            // kMfmaRing register sets used in turn, each refilled right after use,
-            // in straight-line code; loads past the last stage re-read it so
-            // every step issues the same ones
-            Stage ring[kMfmaRing];
-#pragma unroll
-            for (int k = 0; k < kMfmaRing - 1; ++k) load(ring[k], arow, srow, k < NST ? k : NST - 1);
-#pragma unroll
-            for (int sidx = 0; sidx < NST; ++sidx) {
-                const int ls = sidx + kMfmaRing - 1;
-                load(ring[ls % kMfmaRing], arow, srow, ls < NST ? ls : NST - 1);
-                asm volatile("" ::: "memory");   // keep each stage's loads in their place
-                compute(ring[sidx % kMfmaRing], sidx, acc);
-            }
-        }
-        reduce(acc);
-        const f4 v = {acc[0], acc[1], acc[2], acc[3]};
-        f4 up;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) up[rr] = __shfl_down(acc[rr], 1, 64);
-        if (outw && q == 0) epilogue(unit * NB + wave / KS, v, up);
     }
 }
 
@@ -1771,10 +1701,7 @@ template <int P, int E, int KS, int NST>
 hipError_t launch_mfma(const GemvMultiArgs& a, hipStream_t s) {
     const int nrb = (a.rows + 15) / 16;
     const int nunits = (nrb + 4 / KS - 1) / (4 / KS);
-    // LDS: the input image, the KS-wave partial sums, and with the carried
-    // ring the results of up to kMfmaDefer units
-    const size_t shm = 64 + (size_t)2 * a.M * (a.K + kMfmaPad) + (KS > 1 ? 4 * 64 * 16 : 0) +
-                       (mfma_carried(NST) ? (size_t)kMfmaDefer * (4 / KS) * 16 * 16 : 0);
+    const size_t shm = 64 + (size_t)2 * a.M * (a.K + kMfmaPad) + (KS > 1 ? 4 * 64 * 16 : 0);
     const void* fn = (const void*)k_gemv_mfma<P, E, KS, NST>;
     if (shm > 65536) {
         hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
@@ -1783,10 +1710,7 @@ hipError_t launch_mfma(const GemvMultiArgs& a, hipStream_t s) {
     // one round of resident workgroups, each taking units in turn: a partial
     // second round ran on a mostly idle chip
     const int res = resident_blocks(fn, shm);
-    int nb = res > 0 && res < nunits ? res : nunits;
-    // the carried ring holds kMfmaDefer units per workgroup
-    if (mfma_carried(NST)) nb = std::max(nb, (nunits + kMfmaDefer - 1) / kMfmaDefer);
-    const dim3 grid(nb), block(256);
+    const dim3 grid(res > 0 && res < nunits ? res : nunits), block(256);
     hipLaunchKernelGGL((k_gemv_mfma<P, E, KS, NST>), grid, block, shm, s, a);
     return hipGetLastError();
 }
@@ -1827,6 +1751,7 @@ hipError_t launch_gemv_multi(int pro, int epi, const GemvMultiArgs& a, hipStream
     if (pro == PRO_GATED && (a.gated_d <= 0 || a.K % a.gated_d)) return hipErrorInvalidValue;
     const int G = a.K / 32;
     if (a.K % 32 == 0 && G % kStage == 0 && a.rows >= 1) {
+        const int nrb = (a.rows + 15) / 16;
         // at least two waves per row block: with one, the stage offsets are
         // compile-time constants and the compiler merges the ring's loads
         // until the registers spill.  Four where the groups allow it: the
