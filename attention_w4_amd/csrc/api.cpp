@@ -1084,8 +1084,9 @@ int enqueue_phase(aw4_model* m, int phase, int l, uint64_t* bytes) {
 
 // Gated attention of M tokens at cache positions *posp .. *posp + M - 1 (their
 // projections at proj, rows in_rows apart): all M tokens' K and V are appended
-// first, then sweeps of up to tps tokens read the cache (each token masked to
-// its own position); the o-projection adds into the M residuals at x.
+// first, then one launch of sweeps of up to tps tokens each (grid z) reads the
+// cache (each token masked to its own position) and one combine merges all M;
+// the o-projection adds into the M residuals at x.
 int enqueue_attn_multi(aw4_model* m, LayerBufs& b, int M, float* x, float* proj, const int32_t* posp) {
     const aw4_config* c = &m->cfg;
     hipStream_t s = m->stream;
@@ -1100,16 +1101,11 @@ int enqueue_attn_multi(aw4_model* m, LayerBufs& b, int M, float* x, float* proj,
     aa.max_ctx = c->max_ctx; aa.nq = c->attn_q_heads; aa.nkv = c->attn_kv_heads;
     aa.d = c->attn_head_dim; aa.nsplit = m->nsplit;
     HIPCHK(m, launch_append(aa, s));
-    const int tps = attn_tokens_per_sweep(c->attn_head_dim, c->attn_q_heads, c->attn_kv_heads);
-    for (int t = 0; t < M; t += tps) {
-        aa.pos_offset = t;
-        aa.nt = std::min(tps, M - t);
-        aa.proj = proj + (int64_t)t * b.in_rows;
-        HIPCHK(m, launch_attn(aa, s));
-        CombineArgs ca{t, aa.nt, b.in_rows, m->part, aa.proj, m->signs, posp, m->va + t * od, aa.prow,
-                       c->attn_q_heads, c->attn_kv_heads, c->attn_head_dim, m->nsplit};
-        HIPCHK(m, launch_combine(ca, s));
-    }
+    aa.zfast = M > attn_tokens_per_sweep(c->attn_head_dim, c->attn_q_heads, c->attn_kv_heads) ? 1 : 0;
+    HIPCHK(m, launch_attn(aa, s));
+    CombineArgs ca{0, M, b.in_rows, m->part, proj, m->signs, posp, m->va, aa.prow,
+                   c->attn_q_heads, c->attn_kv_heads, c->attn_head_dim, m->nsplit};
+    HIPCHK(m, launch_combine(ca, s));
     GemvMultiArgs go{};
     go.codes = b.w_out; go.scales = b.s_out; go.rows = H; go.K = (int)b.out_cols; go.M = M;
     go.h = m->va; go.sh = od; go.y = x; go.sy = H;

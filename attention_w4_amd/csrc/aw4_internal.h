@@ -136,6 +136,7 @@ struct AttnArgs {
     _Float16* kw;
     _Float16* vw;
     int32_t fmt;              // cache format (k_attn.hip): 0 int8 K + rotated 3-bit V, 1 q4_0, 2 codebook V
+    int32_t zfast;            // several token blocks of one sequence: blocks of a split adjacent in dispatch order
 };
 
 struct CombineArgs {

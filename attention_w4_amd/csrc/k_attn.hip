@@ -295,8 +295,24 @@ __global__ __launch_bounds__(512, 1) void k_attn(AttnArgs a) {
     __shared__ float mo[kOnePass ? kWaves : 4][QC][D];  // wave results
     __shared__ float mm[kWaves][QC], ll[kWaves][QC];
 
-    const int split = blockIdx.x, j = blockIdx.y, tid = threadIdx.x;
-    const int tb0 = blockIdx.z * NT;          // the block's first token in the run
+    const int j = blockIdx.y, tid = threadIdx.x;
+    // split and token block: grid (split, kv head, block), or with zfast the
+    // nz token blocks of a split next to each other in x, and with two blocks
+    // and whole groups of 8 splits eight apart, so that both run at the same
+    // time on one XCD (workgroups are dealt to the 8 XCDs in turn) and the
+    // later block's cache reads find the earlier one's lines in its L2
+    int split = blockIdx.x, zb = blockIdx.z;
+    if (NT > 1 && a.zfast) {
+        const int nz = (a.nt + NT - 1) / NT, b = blockIdx.x;
+        if (nz == 2 && a.nsplit % 8 == 0) {
+            zb = (b >> 3) & 1;
+            split = ((b >> 4) << 3) | (b & 7);
+        } else {
+            zb = b % nz;
+            split = b / nz;
+        }
+    }
+    const int tb0 = zb * NT;                  // the block's first token in the run
     const int lane = tid & 63, w = tid >> 6;
     const int c = lane & 15, q = lane >> 4;
     // the block's first token's position; in a batch each block is a sequence
@@ -993,7 +1009,9 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
     if (a.nsplit < 1 || a.nsplit > 256 || a.nt < 1 || (a.nt > 1 && a.append && !a.batch) || a.nq * a.nt > a.prow)
         return hipErrorInvalidValue;
     const int nn = a.nt == 1 || a.batch ? 1 : attn_tokens_per_sweep(a.d, a.nq, a.nkv);
-    const dim3 grid(a.nsplit, a.nkv, (a.nt + nn - 1) / nn), block(64 * kWaves);
+    const int nz = (a.nt + nn - 1) / nn;
+    if (a.zfast && (a.batch || nn == 1 || a.append)) return hipErrorInvalidValue;
+    const dim3 grid(a.zfast ? a.nsplit * nz : a.nsplit, a.nkv, a.zfast ? 1 : nz), block(64 * kWaves);
     if (a.fmt != 0) {
         // the 4-bit and codebook caches: single-token sweeps of one sequence
         if (a.nt != 1 || a.batch || a.win > 0) return hipErrorInvalidValue;
