@@ -1173,17 +1173,27 @@ int enqueue_verify(aw4_model* m, int M, int k, const float* dev_q, float tempera
     ac.greedy = temperature == 0.f; ac.inv_t = temperature == 0.f ? 1.f : 1.f / temperature;
     ac.zpart = m->vzpart; ac.wpart = m->vwpart;
     HIPCHK(m, launch_accept(ac, m->vpv, m->vpi, m->nhead_blocks, s));
-    // commit: replay the accepted prefix into the GDN states, advance the position
+    // commit: replay the accepted prefix into the GDN states (every layer's in
+    // one launch, up to kMaxReplayLayers at a time), advance the position
+    GdnReplayArgs rp{};
     gi_layer = 0;
     for (int l = 0; l < c->n_layers; ++l) {
         LayerBufs& b = m->L[l];
         if (b.type != 'G') continue;
-        GdnMultiArgs ga{};
-        ga.proj = m->vproj_g[gi_layer++]; ga.sproj = b.in_rows; ga.a_bias = b.a_bias; ga.S = b.S; ga.o = nullptr;
-        ga.so = 0; ga.nqk = c->gdn_qk_heads; ga.nv = c->gdn_v_heads; ga.d = c->gdn_head_dim; ga.M = M;
-        ga.eps = c->rms_eps; ga.replay = 1; ga.commit_n = &m->ctl->vcommit;
-        HIPCHK(m, launch_gdn_multi(ga, s));
+        if (rp.nlayers == 0) {
+            GdnMultiArgs& ga = rp.a;
+            ga.sproj = b.in_rows; ga.o = nullptr; ga.so = 0; ga.nqk = c->gdn_qk_heads; ga.nv = c->gdn_v_heads;
+            ga.d = c->gdn_head_dim; ga.M = M; ga.eps = c->rms_eps; ga.replay = 1; ga.commit_n = &m->ctl->vcommit;
+        }
+        rp.proj[rp.nlayers] = m->vproj_g[gi_layer++];
+        rp.a_bias[rp.nlayers] = b.a_bias;
+        rp.S[rp.nlayers] = b.S;
+        if (++rp.nlayers == kMaxReplayLayers) {
+            HIPCHK(m, launch_gdn_replay(rp, s));
+            rp.nlayers = 0;
+        }
     }
+    if (rp.nlayers > 0) HIPCHK(m, launch_gdn_replay(rp, s));
     HIPCHK(m, launch_commit_pos(m->ctl, s));
     return AW4_OK;
 }

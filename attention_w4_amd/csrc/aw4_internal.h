@@ -168,6 +168,17 @@ struct GdnMultiArgs {
     const int32_t* commit_n;
 };
 
+// the replay of up to kMaxReplayLayers GDN layers in one launch: common
+// fields in a (replay = 1, commit_n set), per-layer inputs and states
+constexpr int kMaxReplayLayers = 64;
+struct GdnReplayArgs {
+    GdnMultiArgs a;
+    int32_t nlayers;
+    const float* proj[kMaxReplayLayers];
+    const float* a_bias[kMaxReplayLayers];
+    float* S[kMaxReplayLayers];
+};
+
 struct AcceptArgs {
     Ctl* ctl;
     const float* logits;      // [k+1][V]
@@ -274,6 +285,7 @@ hipError_t launch_head_final(const float* pv, const int32_t* pi, int n, Ctl* ctl
 hipError_t launch_gdn(const GdnArgs& a, hipStream_t s);
 hipError_t launch_gdn_batch(const GdnArgs& a, int B, hipStream_t s);
 hipError_t launch_gdn_multi(const GdnMultiArgs& a, hipStream_t s);
+hipError_t launch_gdn_replay(const GdnReplayArgs& r, hipStream_t s);
 int accept_blocks(int V);
 hipError_t launch_accept(const AcceptArgs& a, const float* head_pv, const int32_t* head_pi, int head_nb,
                          hipStream_t s);

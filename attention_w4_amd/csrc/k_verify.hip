@@ -25,15 +25,14 @@ __device__ __forceinline__ float wsum(float v) {
 // commit_n < 0.  With commit_n >= 0 (the replay) the first n steps are applied
 // and S written back, no readout.
 template <int D>
-__global__ __launch_bounds__(256) void k_gdn_multi(GdnMultiArgs a) {
+__device__ __forceinline__ void gdn_multi_block(const GdnMultiArgs& a, int bx, int h) {
     constexpr int EPT = 8;
     constexpr int TPR = D / EPT;
     constexpr int ROWS = 256 / TPR;
     __shared__ float kq[4][2][D];
     __shared__ float red[4][2][4];
-    const int h = blockIdx.y;
     const int j = h / (a.nv / a.nqk);
-    const int row0 = blockIdx.x * ROWS;
+    const int row0 = bx * ROWS;
     const int tid = threadIdx.x, wave = tid >> 6;
     const int nsteps = a.replay ? *a.commit_n : a.M;
 
@@ -89,6 +88,23 @@ __global__ __launch_bounds__(256) void k_gdn_multi(GdnMultiArgs a) {
         *(float4*)Srow = make_float4(s[0], s[1], s[2], s[3]);
         *(float4*)(Srow + 4) = make_float4(s[4], s[5], s[6], s[7]);
     }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void k_gdn_multi(GdnMultiArgs a) {
+    gdn_multi_block<D>(a, blockIdx.x, blockIdx.y);
+}
+
+// The replay of every GDN layer in one launch (grid z: layer): the layers'
+// replays are independent of each other once the accepted count is known.
+template <int D>
+__global__ __launch_bounds__(256) void k_gdn_replay(GdnReplayArgs r) {
+    GdnMultiArgs a = r.a;
+    const int l = blockIdx.z;
+    a.proj = r.proj[l];
+    a.a_bias = r.a_bias[l];
+    a.S = r.S[l];
+    gdn_multi_block<D>(a, blockIdx.x, blockIdx.y);
 }
 
 // ----------------------------------------------------------------- acceptance
@@ -260,6 +276,16 @@ hipError_t launch_gdn_multi(const GdnMultiArgs& a, hipStream_t s) {
     if (a.M < 1 || a.M > 4) return hipErrorInvalidValue;
     if (a.d == 128) hipLaunchKernelGGL(k_gdn_multi<128>, dim3(128 / 16, a.nv), dim3(256), 0, s, a);
     else if (a.d == 64) hipLaunchKernelGGL(k_gdn_multi<64>, dim3(64 / 32, a.nv), dim3(256), 0, s, a);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_gdn_replay(const GdnReplayArgs& r, hipStream_t s) {
+    const GdnMultiArgs& a = r.a;
+    if (a.M < 1 || a.M > 4 || !a.replay || !a.commit_n || r.nlayers < 1 || r.nlayers > kMaxReplayLayers)
+        return hipErrorInvalidValue;
+    if (a.d == 128) hipLaunchKernelGGL(k_gdn_replay<128>, dim3(128 / 16, a.nv, r.nlayers), dim3(256), 0, s, r);
+    else if (a.d == 64) hipLaunchKernelGGL(k_gdn_replay<64>, dim3(64 / 32, a.nv, r.nlayers), dim3(256), 0, s, r);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }
