@@ -325,8 +325,10 @@ __global__ __launch_bounds__(512, 1) void k_attn(AttnArgs a) {
     uint16_t* const vs = (uint16_t*)((char*)a.vs + zoff);
     const int nt = NT == 1 ? 1 : min(NT, a.nt - tb0);
     // with a recent window (win > 0) this sweep covers only the positions
-    // before it; k_attn_win reads the window
-    const int npos = pos + nt - (a.win > 0 ? a.win : 0);
+    // before it; k_attn_win reads the window.  With zfast one combine merges
+    // every token of the run, so every block splits the positions up to the
+    // run's end (the combine's partition) and masks those after its tokens.
+    const int npos = (NT > 1 && a.zfast ? *a.pos + a.pos_offset + a.nt : pos + nt) - (a.win > 0 ? a.win : 0);
     if (npos <= 0) return;
     int pps, used;
     split_range(npos, a.nsplit, pps, used);

@@ -189,20 +189,24 @@ def test_verify_acceptance_distribution_chi2(aw4):
     gm.close()
 
 
-@pytest.mark.parametrize("temperature,k", [(0.0, 3), (1.0, 3), (0.0, 2)])
-def test_verify_at_262k_positions(aw4, temperature, k):
+@pytest.mark.parametrize("temperature,k,npos", [(0.0, 3, 262143), (1.0, 3, 262143), (0.0, 2, 262143),
+                                                 (0.0, 3, 4093), (1.0, 3, 4093)])
+def test_verify_at_262k_positions(aw4, temperature, k, npos):
     """One full-size gated-attention layer with a 4096-id head on a seeded
-    262,143-position synthetic cache: a verify pass of k drafts (the two-token
-    sweeps over the whole cache, both token blocks of a split in one launch;
-    with two drafts the second block holds one token) against the oracle's,
-    from the same state: emitted tokens (at temperature 1: except at a
-    decision boundary), committed position and the appended cache entries."""
+    synthetic cache of npos positions: a verify pass of k drafts (the two-token
+    sweeps over the whole cache, both token blocks of a split in one launch
+    and one combine; with two drafts the second block holds one token)
+    against the oracle's, from the same state: emitted tokens (at temperature
+    1: except at a decision boundary), committed position and the appended
+    cache entries.  At 4,093 positions the first block's own end (4,095) and
+    the run's (4,097) split the cache differently (64 splits of 64 positions
+    against 52 of 80): the blocks must use the run's partition, the one the
+    combine merges."""
     import torch
     from synth import state as SS
     from synth.gpu_load import load_recipe
-    npos = 262143
     shape = W.with_(W.ATTN_LAYER, vocab=4096, max_ctx=npos + 16)
-    _say("case: verify at 262,143 cached positions, one attention layer, T =", temperature, "drafts", k)
+    _say("case: verify at", npos, "cached positions, one attention layer, T =", temperature, "drafts", k)
     gm = aw4.Model(shape)
     load_recipe(gm, shape, 21)
     om = oracle.from_recipe(shape, 21)
