@@ -36,23 +36,38 @@ __device__ __forceinline__ void gdn_multi_block(const GdnMultiArgs& a, int bx, i
     const int tid = threadIdx.x, wave = tid >> 6;
     const int nsteps = a.replay ? *a.commit_n : a.M;
 
-    for (int m = 0; m < nsteps; ++m) {
-        const float* proj = a.proj + m * a.sproj;
-        float val = 0.f;
-        if (tid < 2 * D) val = tid < D ? proj[a.nqk * D + j * D + tid] : proj[j * D + tid - D];
-        float ss = wsum(val * val);
+    // k and q of every step at once (threads [0, D) take k, [D, 2D) q): the
+    // loads are issued together, and one barrier serves all the norms
+    float val[4];
+    {
+        const int tq = tid < 2 * D ? tid : 0;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const float* proj = a.proj + (m < nsteps ? m : 0) * a.sproj;
+            const float v = tq < D ? proj[a.nqk * D + j * D + tq] : proj[j * D + tq - D];
+            val[m] = m < nsteps && tid < 2 * D ? v : 0.f;
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        if (m >= nsteps) break;
+        const float ss = wsum(val[m] * val[m]);
         if ((tid & 63) == 0) red[m][0][wave] = ss;
-        __syncthreads();
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        if (m >= nsteps) break;
         constexpr int WPV = D / 64;
         float ssk = 0.f, ssq = 0.f;
 #pragma unroll
         for (int w = 0; w < WPV; ++w) { ssk += red[m][0][w]; ssq += red[m][0][WPV + w]; }
         if (tid < 2 * D) {
             const float r = 1.0f / sqrtf((tid < D ? ssk : ssq) + a.eps);
-            kq[m][tid < D ? 0 : 1][tid < D ? tid : tid - D] = val * r;
+            kq[m][tid < D ? 0 : 1][tid < D ? tid : tid - D] = val[m] * r;
         }
-        __syncthreads();
     }
+    __syncthreads();
 
     const int r = row0 + tid / TPR;
     const int c0 = (tid % TPR) * EPT;
