@@ -54,7 +54,7 @@ extern "C" {
 #define AW4_E_STATE (-8)       /* call not valid in the model's current state */
 
 /* Model shape.  Requirements (else AW4_E_INVAL): hidden, ffn multiples of 64;
- * group == 32; n_layers in [1, 128], layer_pattern holds n_layers letters
+ * group == 32; n_layers in [1, 127], layer_pattern holds n_layers letters
  * 'G' (Gated DeltaNet) or 'A' (gated attention); GDN: gdn_head_dim in {64, 128},
  * gdn_v_heads a multiple of gdn_qk_heads; attention: attn_head_dim in {64, 256},
  * attn_q_heads a multiple of attn_kv_heads, attn_q_heads/attn_kv_heads <= 8;

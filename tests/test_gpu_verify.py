@@ -59,26 +59,45 @@ def _import(gm, om, shape):
     gm.set_pos(om.pos)
 
 
-def _check_commit(gm, om, shape, pos0):
+def _check_commit(gm, om, shape, pos0, gdn_tol=1e-3):
+    """returns each GDN layer's relative L2 state error"""
     assert gm.pos == om.pos
+    errs = {}
     for l, t in enumerate(shape.pattern):
         if t == "G":
-            assert rel_l2(gm.export_gdn(l), om.get_gdn_state(l)) < 1e-3, l
+            errs[l] = rel_l2(gm.export_gdn(l), om.get_gdn_state(l))
+            assert errs[l] < gdn_tol, (l, errs[l])
         else:
             gk, ok = gm.export_kv(l, om.pos), om.get_kv(l, om.pos)
             for a, b in ((gk[0], ok[0]), (gk[2], ok[2])):
                 d = a[pos0:].astype(int) - b[pos0:].astype(int)
                 assert np.abs(d).max() <= 1 and (d != 0).mean() < 6e-2
+    return errs
 
 
-@pytest.mark.parametrize("shape_name", ["TINY", "TOY"])
+@pytest.mark.parametrize("shape_name", ["TINY", "TOY", "TINY_DEEP"])
 def test_verify_greedy_equals_greedy_decode(aw4, shape_name):
-    shape = TINY if shape_name == "TINY" else W.TOY
+    """Greedy verify passes against the oracle's: emitted tokens, and after
+    each commit the position, every GDN layer's state and the appended cache
+    entries.  TINY_DEEP stacks 66 GDN layers, more than one launch of the
+    commit's replay covers (64 layers), so the replay takes two.  Its states
+    are held to 5e-2 relative L2 instead of 1e-3, and each to a tenth of how
+    far the oracle's state moved over the pass: the fp16 activations drift
+    from the fp64 oracle with depth, alike on the decode and the verify path
+    (after three accepted drafts from one imported state: decode steps 1.5e-3
+    at the 11th GDN layer and 7.0e-3 at the 66th, the verify pass 1.3e-3 and
+    5.9e-3).  Measured over these ten passes, the last six GDN layers, the two
+    from the second replay launch among them, are off by 1.7e-3 to 2.5e-2
+    while their states move by 0.42 to 1.0 of their norm, so a launch that
+    skipped or misplaced a layer fails by far.  The two attention layers come
+    first, so their cache codes see the shallow inputs the usual code bound
+    was set for."""
+    shape = {"TINY": TINY, "TOY": W.TOY, "TINY_DEEP": W.with_(TINY, pattern="AA" + "G" * 66)}[shape_name]
     _say("case: verify_k greedy", shape_name)
-    om, gm, prompt = _pair(aw4, shape, 2, 24, 0.1 if shape_name == "TINY" else 0.0)
+    om, gm, prompt = _pair(aw4, shape, 2, 24, 0.0 if shape_name == "TOY" else 0.1)
     rng = np.random.default_rng(0)
     t0 = int(prompt[-1])
-    total_acc = 0
+    total_acc, worst = 0, 0.0
     for p in range(10):
         k = [3, 2, 1, 0, 3, 3, 2, 3, 1, 3][p]
         # drafts: the oracle's own greedy continuation, with one wrong token on some passes
@@ -94,13 +113,20 @@ def test_verify_greedy_equals_greedy_decode(aw4, shape_name):
         tokens = [t0] + chain
         _import(gm, om, shape)
         pos0 = om.pos
+        deep = shape_name == "TINY_DEEP"
+        pre = {l: om.get_gdn_state(l).copy() for l, t in enumerate(shape.pattern) if deep and t == "G"}
         ref, a, _ = oracle_verify(om, tokens, None, None, 0.0)
         got = gm.verify_k(tokens, temperature=0.0)
         assert got == ref, (p, tokens, got, ref)
-        _check_commit(gm, om, shape, pos0)
+        errs = _check_commit(gm, om, shape, pos0, 5e-2 if deep else 1e-3)
+        if deep:
+            # each state is ten times nearer the oracle's than to where it started
+            for l in errs:
+                assert errs[l] < 0.1 * rel_l2(pre[l], om.get_gdn_state(l)), (p, l)
+        worst = max(worst, max(errs.values()))
         total_acc += a
         t0 = ref[-1]
-    _say("accepted drafts", total_acc)
+    _say("accepted drafts", total_acc, "largest GDN state error", worst)
     assert total_acc > 5
     gm.close()
 
