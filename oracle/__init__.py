@@ -84,6 +84,7 @@ def lib():
             "or_get_state_win": ([_vp, ctypes.c_int, _vp, _vp], ctypes.c_int),
             "or_set_state_gdn": ([_vp, ctypes.c_int, _vp], ctypes.c_int),
             "or_get_state_gdn": ([_vp, ctypes.c_int, _vp], ctypes.c_int),
+            "or_set_state_gdn64": ([_vp, ctypes.c_int, _vp], ctypes.c_int),
             "or_set_state_kv": ([_vp, ctypes.c_int, _i32, _vp, _vp, _vp, _vp], ctypes.c_int),
             "or_set_draft_map": ([_vp, _vp, _i32], ctypes.c_int),
             "or_get_draft_map": ([_vp, _vp], ctypes.c_int),
@@ -384,7 +385,8 @@ class Model:
     def restore(self, st):
         for l, t in enumerate(self.shape.pattern):
             if t == "G":
-                self.set_gdn_state(l, st[l].astype(np.float32))
+                S = np.ascontiguousarray(st[l], np.float64)
+                self._rc(lib().or_set_state_gdn64(self.h, l, _p(S)), "restore")
             else:
                 self.set_kv(l, *st[l])
                 if ("win", l) in st:

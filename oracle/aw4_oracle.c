@@ -846,6 +846,15 @@ int or_set_state_gdn(or_model* m, int layer, const float* S) {
     return 0;
 }
 
+/* the state at full precision: a verify pass puts back exactly the state it
+ * saved before running the drafts */
+int or_set_state_gdn64(or_model* m, int layer, const double* S) {
+    if (layer < 0 || layer >= m->c.n_layers || m->L[layer].type != 'G') return -1;
+    int64_t n = (int64_t)m->c.gdn_v_heads * m->c.gdn_head_dim * m->c.gdn_head_dim;
+    memcpy(m->L[layer].S, S, sizeof(double) * n);
+    return 0;
+}
+
 int or_get_state_gdn(const or_model* m, int layer, double* S) {
     if (layer < 0 || layer >= m->c.n_layers || m->L[layer].type != 'G') return -1;
     int64_t n = (int64_t)m->c.gdn_v_heads * m->c.gdn_head_dim * m->c.gdn_head_dim;

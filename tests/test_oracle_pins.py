@@ -403,3 +403,44 @@ def test_inverse_cdf_index_order():
     assert inverse_cdf(w, 0.7499) == 3
     assert inverse_cdf(w, 0.75) == 4
     assert inverse_cdf(w, 0.9999) == 4
+
+
+@pytest.mark.parametrize("wrong", [None, 0, 2])
+def test_verify_commit_equals_decoding_the_accepted_prefix(wrong):
+    """A verify pass commits what decoding the accepted prefix one token at a
+    time gives (the acceptance rule keeps the target's own tokens; the rejected
+    drafts leave no trace): from the same state, the position, every GDN
+    state, every cache entry and the next token's logits equal those of a model
+    that decoded t0 .. d_a alone.  Greedy drafts with none, the first or the
+    third made wrong (a = 3, 0, 2)."""
+    from oracle.accept import verify
+    from tests.helpers import TINY, logical_weights, oracle_from_logical
+    lw = logical_weights(TINY, seed=31, norm_jitter=0.1)
+    om, ref = oracle_from_logical(TINY, lw), oracle_from_logical(TINY, lw)
+    prompt = synth.tokens(9, TINY.vocab, 31)
+    for t in prompt[:-1]:
+        om.decode_token(int(t))
+        ref.decode_token(int(t))
+    t0 = int(prompt[-1])
+    snap = om.snapshot()
+    chain, t = [], t0
+    for _ in range(3):
+        _, _, t = om.decode_token(t)
+        chain.append(int(t))
+    om.restore(snap)
+    if wrong is not None:
+        chain[wrong] = (chain[wrong] + 1) % TINY.vocab
+    out, a, _ = verify(om, [t0] + chain, None, None, 0.0)
+    assert a == (3 if wrong is None else wrong)
+    for t in [t0] + chain[:a]:
+        ref.decode_token(t)
+    assert om.pos == ref.pos
+    for l, kind in enumerate(TINY.pattern):
+        if kind == "G":
+            assert np.array_equal(om.get_gdn_state(l), ref.get_gdn_state(l)), l
+        else:
+            for x, y in zip(om.get_kv(l, om.pos), ref.get_kv(l, ref.pos)):
+                assert np.array_equal(x, y), l
+    _, L1, _ = om.decode_token(out[-1])
+    _, L2, _ = ref.decode_token(out[-1])
+    assert np.array_equal(L1, L2)
